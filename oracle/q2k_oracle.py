@@ -1,0 +1,338 @@
+"""CPU oracle for the Q2_K quantised decode path.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the bench's CPU
+baseline may import this module. The product path (the HIP library and its
+Python binding) never calls it, and this module imports nothing from the
+product package. It is plain, slow and written to be checked by eye against
+the definitions below.
+
+What it computes, and where each definition comes from (the pages are the
+rustdoc source views of the metrale engine: ``engram_v41/apply.rs``,
+``engram_v41.rs``, ``attn_v41/decode.rs`` and ``moe_v41/init.rs``):
+
+* Q2_K super-block, 84 bytes per 256 weights: ``engram_v41.rs``,
+  ``const ENGRAM_ROW_BYTES`` and the ``EngramLayerWeights::wkv_q2k`` doc ("as
+  the GGUF ships it", 84 bytes against 512 in bf16). The pages give only the
+  size; the byte layout is GGUF's Q2_K record (16 scale bytes whose low
+  nibble is the sub-block scale and high nibble the sub-block min, 64 bytes
+  of 2-bit quants, fp16 ``d``, fp16 ``dmin``). Element ``128h + 32j + l``
+  takes bits ``2j..2j+1`` of ``qs[32h + l]`` and sub-block ``8h + 2j + (l>=16)``;
+  its value is ``d*sc*q - dmin*m``.
+* q8_1 activation rows: ``moe_v41/init.rs`` (``kquant_q8_1_rows_bytes``,
+  the ``kquant_q8_1_rows_bf16`` kernel) and ``attn_v41/decode.rs``
+  (``q_kv_projections``: one q8_1 quantisation shared by two Q2_K matrices).
+  32-wide blocks, scale ``amax/127``, round to nearest.
+* The Q2_K x q8_1 product (``kquant_mmvq_q2_k_w``, ``mmvq_q2k_pair_w``,
+  ``kquant_mmvq_q2_k_experts_w*``): ``y[t, n] = sum_e W[n, e] * a[t, e]`` with
+  ``W`` the dequantised weights and ``a = d8 * xq`` the dequantised
+  activations, accumulated here in fp64.
+* Row dequantisation to bf16 (``dequant_q2_k_to_bf16``,
+  ``EngramV41::rows_from_q2k``).
+* SwiGLU then q8_1 re-quantisation (``kquant_swiglu_q8_1_rows_bf16``).
+* The engram gate (``engram_v41_gate``; module doc step 4 "normalised dot of
+  stream against key, signed-sqrt sigmoid, h += gate * value"; ``qk`` is
+  ``q_weight * k_weight``).
+
+Readings taken where the pages are silent (each is listed in the design
+notes): q8_1 rounds half away from zero after a correctly rounded f32
+division and keeps an f32 scale plus per-16 integer sums; the dequantised
+value is formed in f32 and rounded to bf16 to nearest-even; the gate
+RMS-normalises both vectors with ``eps`` inside each root, divides the
+weighted dot by ``sqrt(dim)``, and takes the keys of streams ``0..hc-1``
+before the one shared value in each ``kv`` row. The gate formula is that
+reading: parity unpinned by the pages' own numbers (they print none); it is
+pinned by the closed forms in the oracle tests.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK_BYTES = 84          # engram_v41.rs: const ENGRAM_ROW_BYTES
+BLOCK_WEIGHTS = 256
+Q8_BLOCK = 32
+
+
+# ----------------------------------------------------------------------------
+# Scalar formats
+# ----------------------------------------------------------------------------
+
+def fp16_bits_to_f64(bits) -> np.ndarray:
+    """IEEE binary16 decode from the bit fields (sign, 5-bit exponent with bias
+    15, 10-bit fraction; exponent 0 is subnormal, 31 is inf/NaN)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    normal = sign * (1.0 + f / 1024.0) * np.exp2(e.astype(np.float64) - 15.0)
+    sub = sign * (f / 1024.0) * 2.0 ** -14
+    special = np.where(f == 0, sign * np.inf, np.nan)
+    return np.where(e == 0, sub, np.where(e == 31, special, normal))
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """bf16 is the top half of an f32: shift the 16 bits into place."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+    return (b << 16).view(np.float32)
+
+
+def f32_to_bf16_bits_rne(x) -> np.ndarray:
+    """Round f32 to bf16, to nearest with ties to even, returning bits.
+
+    Keep the top 16 bits; round up when the dropped 16 bits exceed half, or
+    equal half with an odd kept part. NaN keeps a quiet NaN pattern.
+    """
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    kept = u >> 16
+    dropped = u & 0xFFFF
+    up = (dropped > 0x8000) | ((dropped == 0x8000) & ((kept & 1) == 1))
+    out = (kept + up.astype(np.uint64)) & 0xFFFF
+    isnan = np.isnan(np.asarray(x, dtype=np.float32))
+    out = np.where(isnan, (kept | 0x40), out)
+    return out.astype(np.uint16)
+
+
+def round_half_away(v32) -> np.ndarray:
+    """Round an f32 value to the nearest integer, halves away from zero.
+
+    |v| + 0.5 is exact in fp64 for any f32 v of magnitude below 2**52, so the
+    floor sees the true value.
+    """
+    v = np.asarray(v32, dtype=np.float32).astype(np.float64)
+    return np.sign(v) * np.floor(np.abs(v) + 0.5)
+
+
+# ----------------------------------------------------------------------------
+# Q2_K blocks (GGUF layout; size from engram_v41.rs ENGRAM_ROW_BYTES)
+# ----------------------------------------------------------------------------
+
+def q2k_fields(blocks: np.ndarray):
+    """Split ``uint8 [..., 84]`` blocks into (sc, m, q, d, dmin).
+
+    sc, m: int64 [..., 16] sub-block scale and min nibbles.
+    q:     int64 [..., 256] the 2-bit quant of each element, element order.
+    d, dmin: fp64 [...] super-block scales (fp16 bit patterns decoded).
+    """
+    blocks = np.asarray(blocks, dtype=np.uint8)
+    assert blocks.shape[-1] == BLOCK_BYTES
+    scales = blocks[..., 0:16].astype(np.int64)
+    qs = blocks[..., 16:80].astype(np.int64)
+    sc = scales & 0xF
+    m = scales >> 4
+    lead = blocks.shape[:-1]
+    q = np.zeros(lead + (BLOCK_WEIGHTS,), dtype=np.int64)
+    # element 128h + 32j + l takes bits 2j..2j+1 of qs[32h + l]
+    for h in range(2):
+        for j in range(4):
+            for_l = qs[..., 32 * h: 32 * h + 32]
+            q[..., 128 * h + 32 * j: 128 * h + 32 * j + 32] = (for_l >> (2 * j)) & 3
+    d_bits = blocks[..., 80].astype(np.uint16) | (blocks[..., 81].astype(np.uint16) << 8)
+    dmin_bits = blocks[..., 82].astype(np.uint16) | (blocks[..., 83].astype(np.uint16) << 8)
+    return sc, m, q, fp16_bits_to_f64(d_bits), fp16_bits_to_f64(dmin_bits)
+
+
+def subblock_of_element() -> np.ndarray:
+    """Sub-block index of each element 128h + 32j + l: 8h + 2j + (l >= 16)."""
+    e = np.arange(BLOCK_WEIGHTS)
+    h, j, l = e // 128, (e % 128) // 32, e % 32
+    return 8 * h + 2 * j + (l >= 16).astype(np.int64)
+
+
+def q2k_dequant_f64(blocks: np.ndarray) -> np.ndarray:
+    """Exact weight values d*sc*q - dmin*m in fp64, shape [..., 256].
+
+    Each product has at most 17 significant bits, so both products and (for
+    fp16 scales of ordinary range) their difference are exact in fp64.
+    """
+    sc, m, q, d, dmin = q2k_fields(blocks)
+    sb = subblock_of_element()
+    return (d[..., None] * sc[..., sb] * q) - (dmin[..., None] * m[..., sb])
+
+
+def q2k_matrix_f64(w: np.ndarray) -> np.ndarray:
+    """Dequantise a Q2_K matrix ``[n, k/256, 84]`` to fp64 ``[n, k]``."""
+    n, nb = w.shape[0], w.shape[1]
+    return q2k_dequant_f64(w).reshape(n, nb * BLOCK_WEIGHTS)
+
+
+def q2k_dequant_bf16_bits(blocks: np.ndarray) -> np.ndarray:
+    """``dequant_q2_k_to_bf16`` (engram_v41.rs, EngramV41::rows_from_q2k):
+    the value formed in f32 (d*sc*q and dmin*m are exact in f32, the
+    subtraction rounds once), then rounded to bf16 to nearest-even."""
+    sc, m, q, d, dmin = q2k_fields(blocks)
+    sb = subblock_of_element()
+    d32 = d.astype(np.float32)[..., None]
+    dmin32 = dmin.astype(np.float32)[..., None]
+    a = d32 * (sc[..., sb] * q).astype(np.float32)
+    b = dmin32 * m[..., sb].astype(np.float32)
+    v = (a - b).astype(np.float32)
+    return f32_to_bf16_bits_rne(v)
+
+
+def dequant_rows_bf16_bits(table: np.ndarray, ids) -> np.ndarray:
+    """Gather table rows by id, then dequantise each (one block per row).
+
+    ``table``: uint8 [n_table_rows, 84] (or [n_table_rows, 1, 84]).
+    ``ids``: int sequence, or None for rows 0..n-1 in order.
+    Returns uint16 bf16 bits [n_rows, 256].
+    """
+    t = np.asarray(table, dtype=np.uint8).reshape(-1, BLOCK_BYTES)
+    rows = t if ids is None else t[np.asarray(ids, dtype=np.int64)]
+    return q2k_dequant_bf16_bits(rows)
+
+
+# ----------------------------------------------------------------------------
+# q8_1 activation rows
+# ----------------------------------------------------------------------------
+
+def q8_1_quantize(x_f32: np.ndarray):
+    """q8_1 of rows ``[m, k]`` (exact f32 values, e.g. from bf16).
+
+    Per 32-wide block: amax = max |x|, d = amax / 127 (f32, correctly rounded),
+    xq = round(x / d) with the f32 quotient rounded half away from zero, and
+    xq = 0 when amax = 0. Also returns the integer sum of each 16-wide half.
+
+    Returns (xq int64 [m, k], d f32 [m, k/32], s int64 [m, k/16]).
+    """
+    x = np.asarray(x_f32, dtype=np.float32)
+    m, k = x.shape
+    assert k % Q8_BLOCK == 0
+    xb = x.reshape(m, k // Q8_BLOCK, Q8_BLOCK)
+    amax = np.max(np.abs(xb), axis=-1).astype(np.float32)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(d > 0, d, np.float32(1.0)).astype(np.float32)
+    quot = (xb / safe[..., None]).astype(np.float32)
+    xq = np.clip(round_half_away(quot), -127, 127).astype(np.int64)
+    xq = np.where((d > 0)[..., None], xq, 0)
+    xq = xq.reshape(m, k)
+    s = xq.reshape(m, k // 16, 16).sum(axis=-1)
+    return xq, d, s
+
+
+def q8_1_from_bf16_bits(x_bits: np.ndarray):
+    """q8_1 of bf16 rows given as bit patterns."""
+    return q8_1_quantize(bf16_bits_to_f32(x_bits))
+
+
+def q8_1_dequant_f64(xq: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """a[t, e] = d[t, e // 32] * xq[t, e], exact in fp64."""
+    m, k = xq.shape
+    return d.astype(np.float64).repeat(Q8_BLOCK, axis=1) * xq.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Q2_K x q8_1 products
+# ----------------------------------------------------------------------------
+
+def mmvq(w: np.ndarray, xq: np.ndarray, d8: np.ndarray) -> np.ndarray:
+    """y[t, n] = sum_e W[n, e] * d8[t, e//32] * xq[t, e] in fp64 (dense route).
+
+    ``w``: uint8 [n, k/256, 84]; ``xq``: int [m, k]; ``d8``: f32 [m, k/32].
+    Returns fp64 [m, n].
+    """
+    wf = q2k_matrix_f64(w)
+    a = q8_1_dequant_f64(xq, d8)
+    return a @ wf.T
+
+
+def block_dots(w: np.ndarray, xq: np.ndarray):
+    """Integer sums per (token t, row n, q8 block c of the row):
+
+    I = sum over the 32 elements e of block c of sc(e) * q(e) * xq(e)
+    M = sum over the same elements of m(e) * xq(e)
+
+    where sc(e), m(e) are the scale and min nibbles of e's 16-wide sub-block.
+    Returns (I, M) int64 [m, n, k/32].
+    """
+    sc, mn, q, _, _ = q2k_fields(w)          # [n, nb, 16], [n, nb, 256]
+    sb = subblock_of_element()
+    n, nb = w.shape[0], w.shape[1]
+    wsq = (sc[..., sb] * q).reshape(n, nb * BLOCK_WEIGHTS)     # [n, k]
+    wm = mn[..., sb].reshape(n, nb * BLOCK_WEIGHTS)
+    mt, k = xq.shape
+    nq8 = k // Q8_BLOCK
+    I = np.einsum("nce,tce->tnc", wsq.reshape(n, nq8, Q8_BLOCK),
+                  xq.reshape(mt, nq8, Q8_BLOCK).astype(np.int64))
+    M = np.einsum("nce,tce->tnc", wm.reshape(n, nq8, Q8_BLOCK),
+                  xq.reshape(mt, nq8, Q8_BLOCK).astype(np.int64))
+    return I, M
+
+
+def mmvq_from_block_dots(w: np.ndarray, I: np.ndarray, M: np.ndarray, d8: np.ndarray):
+    """The integer route: y[t, n] = sum_b sum_c d8[t, 8b+c] * (d_b * I - dmin_b * M),
+    in fp64. Equal to ``mmvq`` up to fp64 rounding."""
+    _, _, _, d, dmin = q2k_fields(w)         # [n, nb]
+    n, nb = d.shape
+    d_e = np.repeat(d, 8, axis=1)            # per q8 block of the row
+    dmin_e = np.repeat(dmin, 8, axis=1)
+    inner = d_e[None] * I.astype(np.float64) - dmin_e[None] * M.astype(np.float64)
+    return np.einsum("tnc,tc->tn", inner, d8.astype(np.float64))
+
+
+def mmvq_pair(wa, wb, xq, d8):
+    """``mmvq_q2k_pair_w`` (attn_v41/decode.rs, q_kv_projections): two
+    matrices against the same q8_1 rows."""
+    return mmvq(wa, xq, d8), mmvq(wb, xq, d8)
+
+
+def mmvq_experts(matrices_by_id, xq, d8, x_per_id: bool):
+    """Expert-batch product (``kquant_mmvq_q2_k_experts_w*``, moe_v41/init.rs):
+    ``matrices_by_id[i]`` is the Q2_K matrix of the i-th selected id; the input
+    is shared (``x_per_id`` False) or the i-th group of ``m`` rows.
+    Returns fp64 [n_ids, m, n] in id-list order."""
+    outs = []
+    m_per = xq.shape[0] if not x_per_id else xq.shape[0] // len(matrices_by_id)
+    for i, w in enumerate(matrices_by_id):
+        if x_per_id:
+            sl = slice(i * m_per, (i + 1) * m_per)
+            outs.append(mmvq(w, xq[sl], d8[sl]))
+        else:
+            outs.append(mmvq(w, xq, d8))
+    return np.stack(outs)
+
+
+# ----------------------------------------------------------------------------
+# SwiGLU and the engram gate
+# ----------------------------------------------------------------------------
+
+def swiglu_bf16_bits(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """bf16 SwiGLU of the gate/up outputs (``kquant_swiglu_q8_1_rows_bf16``):
+    silu(g) * u = g / (1 + exp(-g)) * u in fp64, rounded to f32 and then to
+    bf16, nearest-even both times."""
+    g64 = np.asarray(g, dtype=np.float64)
+    u64 = np.asarray(u, dtype=np.float64)
+    h = g64 / (1.0 + np.exp(-g64)) * u64
+    return f32_to_bf16_bits_rne(h.astype(np.float32))
+
+
+def engram_gate(h: np.ndarray, kv: np.ndarray, qk: np.ndarray, eps: float) -> np.ndarray:
+    """Engram gate (engram_v41.rs module doc, step 4; ``engram_v41_gate`` in
+    engram_v41/apply.rs with arguments streams, kv, qk, dim, hc, eps).
+
+    For token t and stream j, with key k_j = kv[t, j*dim:(j+1)*dim] and value
+    v = kv[t, hc*dim:(hc+1)*dim]:
+        rms(x) = sqrt(mean(x^2) + eps)
+        s = sum_i qk[j, i] * h[t, j, i] * k_j[i] / (rms(h[t, j]) * rms(k_j) * sqrt(dim))
+        g = 1 / (1 + exp(-sign(s) * sqrt(|s|)))
+        h[t, j, :] += g * v
+    Returns the updated stream in fp64; the input is not modified.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    qk = np.asarray(qk, dtype=np.float64)
+    T, hc, dim = h.shape
+    out = h.copy()
+    for t in range(T):
+        v = kv[t, hc * dim:(hc + 1) * dim]
+        for j in range(hc):
+            x = h[t, j]
+            k = kv[t, j * dim:(j + 1) * dim]
+            rx = math.sqrt(float(np.mean(x * x)) + eps)
+            rk = math.sqrt(float(np.mean(k * k)) + eps)
+            s = float(np.sum(qk[j] * x * k)) / (rx * rk * math.sqrt(dim))
+            sg = math.copysign(math.sqrt(abs(s)), s) if s != 0.0 else 0.0
+            g = 1.0 / (1.0 + math.exp(-sg))
+            out[t, j] = x + g * v
+    return out

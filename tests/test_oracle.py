@@ -1,0 +1,450 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself
+(hand-derived values, closed forms, library routines, an exact-rational
+route, brute force on tiny inputs). CPU only."""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import q2k_oracle as orc
+from q2_quantized_decode_amd import synthetic as syn
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- formats ---
+
+def test_fp16_decode_all_patterns_match_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = orc.fp16_bits_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    both_nan = np.isnan(mine) & np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.array_equal(mine[~both_nan], ref[~both_nan])
+
+
+def test_bf16_rne_matches_torch_conversion():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32),
+        (rng.standard_normal(20000) * 1e30).astype(np.float32),
+        (rng.standard_normal(20000) * 1e-30).astype(np.float32),
+        # exact ties: low 16 bits = 0x8000 with odd and even kept parts
+        (np.arange(1, 5000, dtype=np.uint32) << 16 | 0x8000).view(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38], dtype=np.float32),
+    ])
+    mine = orc.f32_to_bf16_bits_rne(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+def test_round_half_away_literals():
+    v = np.array([0.5, -0.5, 1.5, 2.5, -2.5, 63.5, -63.5, 0.49999997, 126.5, 3.0, -0.0],
+                 dtype=np.float32)
+    assert orc.round_half_away(v).tolist() == [1, -1, 2, 3, -3, 64, -64, 0, 127, 3, 0]
+
+
+# ------------------------------------------------------------- Q2_K decode ---
+
+def _load_hand_blocks():
+    recs = {}
+    with open(os.path.join(GOLDEN, "q2k_hand_blocks.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            name, hexbytes, pairs = (p.strip() for p in line.split("|"))
+            blk = np.frombuffer(bytes.fromhex(hexbytes), dtype=np.uint8)
+            exp = {int(a): float(b) for a, b in (p.split("=") for p in pairs.split())}
+            recs[name] = (blk, exp)
+    return recs
+
+
+def test_hand_blocks_literal_values():
+    recs = _load_hand_blocks()
+    assert set(recs) == {"block_e4", "block_sparse"}
+    for name, (blk, exp) in recs.items():
+        assert blk.size == 84
+        vals = orc.q2k_dequant_f64(blk[None])[0]
+        for e, v in exp.items():
+            assert vals[e] == v, (name, e, vals[e], v)
+    # block_sparse has exactly three nonzero elements
+    blk, _ = recs["block_sparse"]
+    vals = orc.q2k_dequant_f64(blk[None])[0]
+    assert np.count_nonzero(vals) == 3
+
+
+def test_block_size_is_84_bytes():
+    # engram_v41.rs: ENGRAM_ROW_BYTES = 84; 84 bytes per 256 weights vs 512 in bf16
+    assert orc.BLOCK_BYTES == 84
+    assert orc.BLOCK_WEIGHTS * 2 == 512
+
+
+def test_all_zero_quants_give_minus_dmin_times_min():
+    rng = np.random.default_rng(3)
+    blk = syn.q2k_blocks(rng, 5, 3)
+    blk[..., 16:80] = 0
+    vals = orc.q2k_dequant_f64(blk)
+    for r in range(5):
+        for b in range(3):
+            dmin = float(blk[r, b, 82:84].view(np.float16)[0])
+            mins = blk[r, b, 0:16] >> 4
+            for e in range(256):
+                assert vals[r, b, e] == -dmin * float(mins[e // 16])
+
+
+def test_zero_scales_give_positive_zero():
+    rng = np.random.default_rng(4)
+    blk = syn.q2k_blocks(rng, 2, 2)
+    blk[..., 80:84] = 0
+    bits = orc.q2k_dequant_bf16_bits(blk)
+    assert np.all(bits == 0)
+
+
+def test_layout_bijection_bit_pairs_and_nibbles():
+    base = np.zeros((1, 84), dtype=np.uint8)
+    base[0, 0:16] = 0x11            # sc = 1, m = 1 everywhere
+    base[0, 80:82] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
+    base[0, 82:84] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
+    ref = orc.q2k_dequant_f64(base)[0]
+    seen = set()
+    for byte in range(64):
+        for plane in range(4):
+            blk = base.copy()
+            blk[0, 16 + byte] = 1 << (2 * plane)
+            diff = np.nonzero(orc.q2k_dequant_f64(blk)[0] != ref)[0]
+            assert diff.size == 1
+            e = int(diff[0])
+            # by hand: byte 32h + l, plane j -> element 128h + 32j + l
+            h, l = divmod(byte, 32)
+            assert e == 128 * h + 32 * plane + l
+            seen.add(e)
+    assert seen == set(range(256))
+    for s in range(16):
+        for hi in (False, True):
+            blk = base.copy()
+            blk[0, 16:80] = 0xFF   # q = 3 so the scale nibble matters too
+            ref2 = orc.q2k_dequant_f64(blk)[0]
+            blk[0, s] = 0x12 if not hi else 0x21
+            diff = np.nonzero(orc.q2k_dequant_f64(blk)[0] != ref2)[0]
+            assert diff.tolist() == list(range(16 * s, 16 * s + 16))
+
+
+def test_dequant_bf16_rounding_hand_cases():
+    def block(d_bits, dmin_bits, sc, m, qbyte):
+        b = np.zeros((1, 84), dtype=np.uint8)
+        b[0, 0:16] = (m << 4) | sc
+        b[0, 16:80] = qbyte
+        b[0, 80] = d_bits & 0xFF
+        b[0, 81] = d_bits >> 8
+        b[0, 82] = dmin_bits & 0xFF
+        b[0, 83] = dmin_bits >> 8
+        return b
+    # d = 1 + 2^-10 (0x3C01), sc*q = 15*3: 45.0439453125 -> bf16 45.0 (0x4234)
+    bits = orc.q2k_dequant_bf16_bits(block(0x3C01, 0x0000, 15, 0, 0xFF))[0]
+    assert int(bits[0]) == 0x4234
+    # d = 1, sc*q = 45, dmin = -0.125, m = 1: 45.125 is a tie -> even 45.0
+    bits = orc.q2k_dequant_bf16_bits(block(0x3C00, 0xB000, 15, 1, 0xFF))[0]
+    assert int(bits[0]) == 0x4234
+    # dmin = -0.375, m = 1: 45.375 ties between 45.25 (odd) and 45.5 (even)
+    bits = orc.q2k_dequant_bf16_bits(block(0x3C00, 0xB600, 15, 1, 0xFF))[0]
+    assert int(bits[0]) == 0x4236
+    # q = 0, dmin = 0.5, m = 3: -1.5 exactly (0xBFC0)
+    bits = orc.q2k_dequant_bf16_bits(block(0x3C00, 0x3800, 15, 3, 0x00))[0]
+    assert int(bits[0]) == 0xBFC0
+
+
+# ---------------------------------------------------------------- q8_1 -------
+
+def _f32_round_fraction(fr: Fraction) -> Fraction:
+    """Round a rational to the nearest f32 value, ties to even (exact route)."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)
+    scale = Fraction(2) ** (23 - e)
+    v = a * scale
+    fl = v.numerator // v.denominator
+    rem = v - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * Fraction(fl) / scale
+
+
+def _q8_exact(xrow):
+    """q8_1 of one 32-block by exact rationals: d = f32(amax/127), then each
+    quotient f32(x/d) rounded half away from zero."""
+    xs = [Fraction(float(v)) for v in xrow]
+    amax = max(abs(v) for v in xs)
+    d = _f32_round_fraction(amax / 127)
+    if d == 0:
+        return [0] * len(xs), d
+    out = []
+    for v in xs:
+        q = _f32_round_fraction(v / d)
+        mag = abs(q)
+        r = int(mag + Fraction(1, 2))     # floor(|q| + 1/2)
+        out.append(r if q >= 0 else -r)
+    return out, d
+
+
+def test_q8_1_against_exact_rational_route():
+    rng = np.random.default_rng(11)
+    blocks = syn.bf16_normal(rng, (300, 32), outlier_frac=0.05)
+    x = orc.bf16_bits_to_f32(blocks)
+    # tie-constructed blocks: an element equal to amax/2, amax/2 * odd/127 ...
+    ties = []
+    for amax in (0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 20.0):
+        row = np.zeros(32, dtype=np.float32)
+        row[0] = amax
+        row[1] = amax / 2
+        row[2] = -amax / 2
+        row[3] = amax * 3 / 254
+        row[4] = -amax * 5 / 254
+        ties.append(row)
+    x = np.concatenate([x, np.stack(ties)]).astype(np.float32)
+    x = orc.bf16_bits_to_f32(syn.f32_to_bf16_bits_torch(x))    # stay on bf16 values
+    xq, d, s = orc.q8_1_quantize(x)
+    for i in range(x.shape[0]):
+        exp_q, exp_d = _q8_exact(x[i])
+        assert Fraction(float(d[i, 0])) == exp_d
+        assert xq[i].tolist() == exp_q, i
+        assert s[i, 0] == sum(exp_q[:16]) and s[i, 1] == sum(exp_q[16:])
+
+
+def test_q8_1_special_cases():
+    x = np.zeros((4, 32), dtype=np.float32)
+    x[1, 7] = 0.75
+    x[2, 3] = -2.5
+    x[3] = np.arange(-16, 16, dtype=np.float32) * 4      # amax = 64 ... see below
+    x[3, 31] = 127.0                                      # amax = 127 -> d = 1
+    xq, d, _ = orc.q8_1_quantize(x)
+    assert np.all(xq[0] == 0) and d[0, 0] == 0
+    assert xq[1, 7] == 127 and np.count_nonzero(xq[1]) == 1
+    assert d[1, 0] == np.float32(0.75) / np.float32(127)
+    assert xq[2, 3] == -127
+    assert d[3, 0] == 1.0 and np.array_equal(xq[3], x[3].astype(np.int64))
+    # amax = 1 with an element at exactly 1/2: the f32 quotient is 63.5 -> 64
+    t = np.zeros((1, 32), dtype=np.float32)
+    t[0, 0], t[0, 1], t[0, 2] = 1.0, 0.5, -0.5
+    xq, d, _ = orc.q8_1_quantize(t)
+    assert np.float32(0.5) / d[0, 0] == np.float32(63.5)
+    assert xq[0, 1] == 64 and xq[0, 2] == -64
+
+
+# ----------------------------------------------------------- GEMV routes ----
+
+def _brute_force_y(w, x_bits):
+    """Element by element from the raw bytes, in plain Python loops."""
+    n, nb = w.shape[0], w.shape[1]
+    m, k = x_bits.shape
+    xf = orc.bf16_bits_to_f32(x_bits)
+    xq, d8, _ = orc.q8_1_quantize(xf)
+    y = [[0.0] * n for _ in range(m)]
+    for t in range(m):
+        for r in range(n):
+            acc = 0.0
+            for b in range(nb):
+                blk = w[r, b]
+                d = float(np.frombuffer(bytes(blk[80:82]), np.float16)[0])
+                dmin = float(np.frombuffer(bytes(blk[82:84]), np.float16)[0])
+                for h in range(2):
+                    for j in range(4):
+                        for l in range(32):
+                            q = (int(blk[16 + 32 * h + l]) >> (2 * j)) & 3
+                            sb = 8 * h + 2 * j + (1 if l >= 16 else 0)
+                            sc = int(blk[sb]) & 15
+                            mn = int(blk[sb]) >> 4
+                            e = 256 * b + 128 * h + 32 * j + l
+                            wv = d * sc * q - dmin * mn
+                            acc += wv * float(d8[t, e // 32]) * int(xq[t, e])
+            y[t][r] = acc
+    return np.array(y)
+
+
+@pytest.mark.parametrize("n,k,m", [(3, 256, 1), (2, 512, 3), (4, 256, 8)])
+def test_mmvq_brute_force_tiny(n, k, m):
+    case = syn.single_gemv_case(n=n, k=k, m=m, seed=99 + n + k + m)
+    xq, d8, _ = orc.q8_1_from_bf16_bits(case.x_bits)
+    y = orc.mmvq(case.w, xq, d8)
+    yb = _brute_force_y(case.w, case.x_bits)
+    assert np.allclose(y, yb, rtol=1e-12, atol=1e-12)
+
+
+def test_integer_route_matches_dense_route():
+    case = syn.single_gemv_case(n=64, k=1024, m=4, seed=5)
+    xq, d8, _ = orc.q8_1_from_bf16_bits(case.x_bits)
+    I, M = orc.block_dots(case.w, xq)
+    assert np.abs(I).max() <= 32 * 45 * 127 and np.abs(M).max() <= 32 * 15 * 127
+    y1 = orc.mmvq(case.w, xq, d8)
+    y2 = orc.mmvq_from_block_dots(case.w, I, M, d8)
+    assert np.allclose(y1, y2, rtol=1e-12, atol=1e-12)
+
+
+def test_block_dots_brute_force():
+    case = syn.single_gemv_case(n=2, k=512, m=2, seed=6)
+    xq, _, _ = orc.q8_1_from_bf16_bits(case.x_bits)
+    I, M = orc.block_dots(case.w, xq)
+    for t in range(2):
+        for r in range(2):
+            for c in range(16):
+                si = sm = 0
+                for l in range(32):
+                    e = 32 * c + l
+                    b, eb = divmod(e, 256)
+                    h, rest = divmod(eb, 128)
+                    j, ll = divmod(rest, 32)
+                    blk = case.w[r, b]
+                    q = (int(blk[16 + 32 * h + ll]) >> (2 * j)) & 3
+                    sb = 8 * h + 2 * j + (ll >= 16)
+                    si += (int(blk[sb]) & 15) * q * int(xq[t, e])
+                    sm += (int(blk[sb]) >> 4) * int(xq[t, e])
+                assert I[t, r, c] == si and M[t, r, c] == sm
+
+
+def _const_matrix(n, nb, scale_byte, q_byte, d_bits, dmin_bits):
+    w = np.zeros((n, nb, 84), dtype=np.uint8)
+    w[..., 0:16] = scale_byte
+    w[..., 16:80] = q_byte
+    w[..., 80], w[..., 81] = d_bits & 0xFF, d_bits >> 8
+    w[..., 82], w[..., 83] = dmin_bits & 0xFF, dmin_bits >> 8
+    return w
+
+
+def test_mmvq_closed_forms():
+    k = 512
+    # W = 3 everywhere (q = 3, sc = 1, m = 0, d = 1); x = 127 -> d8 = 1, xq = 127
+    w = _const_matrix(2, 2, 0x01, 0xFF, 0x3C00, 0x0000)
+    xq = np.full((1, k), 127, dtype=np.int64)
+    d8 = np.ones((1, k // 32), dtype=np.float32)
+    assert orc.mmvq(w, xq, d8).tolist() == [[195072.0, 195072.0]]      # 3*127*512
+    # W = 2*1 - 1*3 = -1 (q = 1, sc = 2, m = 3, d = dmin = 1)
+    w = _const_matrix(1, 2, 0x32, 0x55, 0x3C00, 0x3C00)
+    assert orc.mmvq(w, xq, d8).tolist() == [[-65024.0]]                # -127*512
+    alt = np.tile(np.array([127, -127], dtype=np.int64), k // 2)[None]
+    assert orc.mmvq(w, alt, d8).tolist() == [[0.0]]
+    # through the quantiser: integer inputs whose blocks all hold 127 keep d8 = 1
+    rng = np.random.default_rng(21)
+    xs = rng.integers(-126, 127, size=k).astype(np.float32)
+    xs[::32] = 127.0
+    xq2, d82, _ = orc.q8_1_quantize(xs[None])
+    assert np.all(d82 == 1.0) and np.array_equal(xq2[0], xs.astype(np.int64))
+
+
+def test_mmvq_linearity_under_power_of_two_scaling():
+    case = syn.single_gemv_case(n=16, k=512, m=2, seed=8)
+    x = orc.bf16_bits_to_f32(case.x_bits)
+    xq1, d1, _ = orc.q8_1_quantize(x)
+    xq2, d2, _ = orc.q8_1_quantize((x * np.float32(2.0)).astype(np.float32))
+    assert np.array_equal(xq1, xq2) and np.array_equal(d2, d1 * np.float32(2))
+    assert np.array_equal(orc.mmvq(case.w, xq2, d2), 2.0 * orc.mmvq(case.w, xq1, d1))
+
+
+def test_pair_and_experts_compose_single():
+    pc = syn.attention_pair_case(m=2, na=8, nb=4, k=512)
+    xq, d8, _ = orc.q8_1_from_bf16_bits(pc.x_bits)
+    ya, yb = orc.mmvq_pair(pc.wa, pc.wb, xq, d8)
+    assert np.array_equal(ya, orc.mmvq(pc.wa, xq, d8))
+    assert np.array_equal(yb, orc.mmvq(pc.wb, xq, d8))
+    ys = orc.mmvq_experts([pc.wa, pc.wa[::-1].copy()], xq, d8, x_per_id=False)
+    assert ys.shape == (2, 2, 8)
+    assert np.array_equal(ys[0], ya) and np.array_equal(ys[1], ya[:, ::-1])
+    # one input group of m rows per id
+    yp = orc.mmvq_experts([pc.wb, pc.wb], np.concatenate([xq, xq[::-1]]),
+                          np.concatenate([d8, d8[::-1]]), x_per_id=True)
+    assert np.array_equal(yp[0], yb) and np.array_equal(yp[1], yb[::-1])
+
+
+# ----------------------------------------------------------- SwiGLU / gate --
+
+def test_swiglu_against_torch_silu():
+    rng = np.random.default_rng(12)
+    g = (rng.standard_normal((4, 256)) * 3).astype(np.float32)
+    u = rng.standard_normal((4, 256)).astype(np.float32)
+    mine = orc.swiglu_bf16_bits(g, u)
+    tg = torch.from_numpy(g.astype(np.float64))
+    ref = (torch.nn.functional.silu(tg) * torch.from_numpy(u.astype(np.float64)))
+    ref_bits = ref.to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref_bits)
+    # silu(0) = 0: the product is a signed zero
+    assert np.all((orc.swiglu_bf16_bits(np.zeros(8, np.float32), u[0, :8]) & 0x7FFF) == 0)
+
+
+def test_gate_value_zero_leaves_stream():
+    h, kv, qk, eps = syn.gate_case(1, 2, 3, 64)
+    kv[:, 3 * 64:] = 0.0
+    assert np.array_equal(orc.engram_gate(h, kv, qk, eps), h.astype(np.float64))
+
+
+def test_gate_orthogonal_key_gives_half():
+    dim, hc = 64, 2
+    h = np.zeros((1, hc, dim), np.float32)
+    kv = np.zeros((1, (hc + 1) * dim), np.float32)
+    h[0, :, : dim // 2] = 1.0                   # support on the first half
+    kv[0, 0: dim // 2] = 0.0
+    kv[0, dim // 2: dim] = 2.0                  # key 0 on the second half
+    kv[0, dim + dim // 2: 2 * dim] = -3.0       # key 1 on the second half
+    kv[0, hc * dim:] = np.arange(dim, dtype=np.float32)
+    qk = np.ones((hc, dim), np.float32)
+    out = orc.engram_gate(h, kv, qk, 1e-6)
+    v = np.arange(dim, dtype=np.float64)
+    for j in range(hc):
+        assert np.array_equal(out[0, j], h[0, j] + 0.5 * v)
+
+
+def test_gate_constant_vectors_closed_form():
+    # eps = 0, h = a, k = b, qk = 1: s = dim*a*b / (|a| |b| sqrt(dim)) = +-sqrt(dim)
+    dim = 16
+    h = np.full((1, 2, dim), 3.0, np.float32)
+    h[0, 1] = -0.25
+    kv = np.zeros((1, 3 * dim), np.float32)
+    kv[0, :dim] = 2.0
+    kv[0, dim:2 * dim] = 5.0
+    kv[0, 2 * dim:] = 1.0
+    qk = np.ones((2, dim), np.float32)
+    out = orc.engram_gate(h, kv, qk, 0.0)
+    sig2 = 0.8807970779778823       # 1 / (1 + e^-2): s = 4, sqrt(s) = 2
+    assert np.allclose(out[0, 0], 3.0 + sig2, rtol=0, atol=1e-15)
+    assert np.allclose(out[0, 1], -0.25 + (1 - sig2), rtol=0, atol=1e-15)
+
+
+def test_gate_sign_flip_gives_complement():
+    h, kv, qk, eps = syn.gate_case(2, 1, 4, 128)
+    out1 = orc.engram_gate(h, kv, qk, eps)
+    kv2 = kv.copy()
+    kv2[:, : 4 * 128] *= -1.0
+    out2 = orc.engram_gate(h, kv2, qk, eps)
+    v = kv[0, 4 * 128:].astype(np.float64)
+    g1 = (out1[0] - h[0]) / v
+    g2 = (out2[0] - h[0]) / v
+    assert np.allclose(g1 + g2, 1.0, atol=1e-12)
+
+
+def test_gate_stream_uses_its_own_key():
+    h, kv, qk, eps = syn.gate_case(3, 1, 2, 32)
+    h[0, 1] = h[0, 0]
+    qk[1] = qk[0]
+    kv[0, 32:64] = kv[0, 0:32]
+    out = orc.engram_gate(h, kv, qk, eps)
+    assert np.array_equal(out[0, 0], out[0, 1])
+    kv[0, 32:64] *= -1
+    out = orc.engram_gate(h, kv, qk, eps)
+    assert not np.array_equal(out[0, 0], out[0, 1])
+
+
+def test_dequant_rows_gathers_by_id():
+    rng = np.random.default_rng(13)
+    table = syn.q2k_blocks(rng, 100, 1)
+    ids = np.array([7, 0, 99, 7], dtype=np.int64)
+    got = orc.dequant_rows_bf16_bits(table, ids)
+    for i, r in enumerate(ids):
+        assert np.array_equal(got[i], orc.q2k_dequant_bf16_bits(table[r])[0])
+    assert np.array_equal(orc.dequant_rows_bf16_bits(table[:3], None),
+                          orc.q2k_dequant_bf16_bits(table[:3, 0]))
