@@ -1,0 +1,289 @@
+"""Benchmark: Q2_K mmvq achieved HBM GB/s on one MI355X.
+
+Workload: the large batched-verify matrix, Q2_K [32768, 7168] (28
+super-blocks per row, 77 070 336 bytes), seeded synthetic weights and bf16
+activations ~ N(0,1) with 5% +-20 outliers. One step is the whole decode hot
+path for that matrix: q8_1 quantisation of the bf16 token(s), then the
+Q2_K x q8_1 product. The headline runs m = 1; m = 8 is reported beside it.
+
+Method:
+* Inputs are resident in HBM before timing. The weights are replicated 16
+  times (1.23 GB, over four times the 256 MB Infinity Cache) and step i reads
+  copy i % 16, so every step streams its matrix from HBM.
+* The steps are captured once into a HIP graph (16 steps, one per copy) and
+  the graph is replayed; W warm-up steps, then K timed steps between two
+  device synchronisations (wall clock).
+* Roofline of the dominant kernel (q2k_mmvq): a second graph holds only the
+  16 products; HIP events on the launching stream bracket its replays, and
+  achieved = algorithmic bytes per launch / average launch time.
+* CPU baseline: the CPU oracle timed on a bounded sample of rows of the
+  same matrix and token (about ten seconds of host work).
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Q2_K mmvq achieved HBM GB/s (% of peak) at m=1 and m=8, 1x MI355X"
+PEAK_GBS = 8000.0          # MI355X HBM3E
+N, K = 32768, 7168
+COPIES = 16
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_large_verify_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "q2_quantized_decode_amd", "csrc", f)
+                  for f in ("mmvq.hip", "q2k_device.h")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def mmvq_bytes(m: int) -> int:
+    """Algorithmic bytes of one product launch: weights + q8_1 rows + f32 out."""
+    return N * (K // 256) * 84 + m * K * 5 // 4 + 4 * m * N
+
+
+def q8_bytes(m: int) -> int:
+    """Algorithmic bytes of one q8_1 launch: bf16 in + q8_1 rows out."""
+    return 2 * m * K + m * K * 5 // 4
+
+
+def measured_traffic(m: int):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or
+    None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    v = rec.get(f"m{m}_bytes_per_launch")
+    return float(v) if v is not None else None
+
+
+def cpu_baseline(case, rows: int):
+    from oracle import q2k_oracle as orc
+
+    xq, d8, _ = orc.q8_1_from_bf16_bits(case.x_bits[:1])
+    w = case.w[:rows]
+    c0 = time.process_time()
+    t0 = time.perf_counter()
+    orc.mmvq(w, xq, d8)
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    gbs = w.nbytes / wall / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"first {rows} of {N} rows of the [32768, 7168] Q2_K matrix, m=1, "
+                      f"{w.nbytes} weight bytes in {wall:.2f} s (fp64 dense oracle)"}
+
+
+def run(args):
+    import torch
+
+    import q2_quantized_decode_amd as q2
+    from q2_quantized_decode_amd import synthetic as syn
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (HIP device)")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q2.lib()
+
+    case = syn.large_verify_case(m=8)
+    w0 = torch.from_numpy(case.w.reshape(-1)).to(dev)
+    copies = [w0] + [w0.clone() for _ in range(COPIES - 1)]
+    x8 = syn.bf16_bits_to_tensor(case.x_bits).to(dev)
+
+    results = {}
+    for m in (1, 8):
+        x = x8[:m].contiguous()
+        xq = torch.empty(q2.q8_1_rows_bytes(m, K), dtype=torch.uint8, device=dev)
+        y = torch.empty((m, N), dtype=torch.float32, device=dev)
+        stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+
+        def step(i):
+            q2.q8_1_rows(x, out=xq)
+            q2.q2k_mmvq(copies[i % COPIES], xq, N, K, m, out=y)
+
+        def product(i):
+            q2.q2k_mmvq(copies[i % COPIES], xq, N, K, m, out=y)
+
+        with torch.cuda.stream(stream):
+            for i in range(COPIES):          # eager warm-up (and first launches)
+                step(i)
+        torch.cuda.synchronize()
+
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step, stream=stream):
+            for i in range(COPIES):
+                step(i)
+        g_prod = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_prod, stream=stream):
+            for i in range(COPIES):
+                product(i)
+        torch.cuda.synchronize()
+
+        # exactly args.steps timed steps: whole 16-step replays, then the rest
+        reps, rem = divmod(args.steps, COPIES)
+        g_rem = None
+        if rem:
+            g_rem = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_rem, stream=stream):
+                for i in range(rem):
+                    step(i)
+        wreps = max(1, -(-args.warmup // COPIES))
+        with torch.cuda.stream(stream):
+            for _ in range(wreps):
+                g_step.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g_step.replay()
+            if g_rem is not None:
+                g_rem.replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+
+            # dominant kernel alone, bracketed by events on this stream
+            for _ in range(wreps):
+                g_prod.replay()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            preps = max(1, reps)
+            ev0.record(stream)
+            for _ in range(preps):
+                g_prod.replay()
+            ev1.record(stream)
+            ev1.synchronize()
+        steps = args.steps
+        step_s = (t1 - t0) / steps
+        launch_s = ev0.elapsed_time(ev1) / 1e3 / (preps * COPIES)
+        step_bytes = mmvq_bytes(m) + q8_bytes(m)
+        # parity re-check on the benchmarked buffers (sampled rows)
+        y_host = y.cpu().numpy()
+        results[m] = dict(step_s=step_s, launch_s=launch_s, steps=steps, y=y_host,
+                          step_gbs=step_bytes / step_s / 1e9,
+                          achieved=mmvq_bytes(m) / launch_s / 1e9)
+
+    # parity of the benchmarked output (the last step read copy 15 of the
+    # same bytes) on sampled rows against the oracle
+    from oracle import q2k_oracle as orc
+    rows = np.sort(syn.rng_for(17).choice(N, 64, replace=False))
+    for m in (1, 8):
+        xq_o, d8_o, _ = orc.q8_1_from_bf16_bits(case.x_bits[:m])
+        ref = orc.mmvq(case.w[rows], xq_o, d8_o)
+        got = results[m]["y"][:, rows].astype(np.float64)
+        if not np.all(np.abs(got - ref) <= 1e-4 + 2e-3 * np.abs(ref)):
+            raise SystemExit(f"bench parity failed at m={m}")
+
+    r1, r8 = results[1], results[8]
+    wreps_all = max(1, -(-args.warmup // COPIES))
+    line = {
+        "metric": METRIC,
+        "value": round(r1["step_gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": r1["steps"],
+        "warmup": wreps_all * COPIES,
+        "ms_per_step": round(r1["step_s"] * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "large batched verify, Q2_K [32768, 7168] x q8_1, m=1 "
+                               "(step = q8_1 quantisation + product)",
+                   "n": N, "k": K, "m": 1, "weight_copies": COPIES,
+                   "pct_of_peak": round(100 * r1["step_gbs"] / PEAK_GBS, 2),
+                   "tokens_per_s": round(1 / r1["step_s"], 1)},
+        "roofline": {"bound": "hbm", "achieved": round(r1["achieved"], 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(r1["achieved"] / PEAK_GBS, 4),
+                     "traffic": measured_traffic(1),
+                     "kernel": "q2k_mmvq (mmvq_narrow_kernel<1>)",
+                     "bytes_per_launch": mmvq_bytes(1),
+                     "us_per_launch": round(r1["launch_s"] * 1e6, 3)},
+        "m8": {"value": round(r8["step_gbs"], 1), "unit": "GB/s",
+               "ms_per_step": round(r8["step_s"] * 1e3, 5),
+               "pct_of_peak": round(100 * r8["step_gbs"] / PEAK_GBS, 2),
+               "tokens_per_s": round(8 / r8["step_s"], 1),
+               "roofline": {"bound": "hbm", "achieved": round(r8["achieved"], 1),
+                            "peak": PEAK_GBS, "unit": "GB/s",
+                            "frac": round(r8["achieved"] / PEAK_GBS, 4),
+                            "traffic": measured_traffic(8),
+                            "bytes_per_launch": mmvq_bytes(8),
+                            "us_per_launch": round(r8["launch_s"] * 1e6, 3)}},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+def pmc_calibration(args):
+    """For counter runs: a plain device copy of known size, then a few
+    products at m = 1 and m = 8 on distinct weight copies."""
+    import torch
+
+    import q2_quantized_decode_amd as q2
+    from q2_quantized_decode_amd import synthetic as syn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    case = syn.large_verify_case(m=8)
+    w0 = torch.from_numpy(case.w.reshape(-1)).to(dev)
+    copies = [w0] + [w0.clone() for _ in range(7)]
+    x8 = syn.bf16_bits_to_tensor(case.x_bits).to(dev)
+    for m in (1, 8):
+        x = x8[:m].contiguous()
+        xq = q2.q8_1_rows(x)
+        y = torch.empty((m, N), dtype=torch.float32, device=dev)
+        for i in range(8):
+            q2.q2k_mmvq(copies[i], xq, N, K, m, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 2 * src.numel(), "copies": 4, "mmvq_launches_per_m": 8}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3200)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--cpu-rows", type=int, default=12288)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--pmc-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        raise SystemExit(2)
+    if args.pmc_calibration:
+        pmc_calibration(args)
+    else:
+        run(args)
+
+
+if __name__ == "__main__":
+    main()

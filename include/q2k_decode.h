@@ -1,0 +1,191 @@
+/*
+ * q2k_decode.h - C ABI of the MI355X (gfx950) Q2_K quantised decode library
+ * (libq2kdecode.so).
+ *
+ * The operations are the single-token (m <= 8) decode path of a 2-bit
+ * k-quant model as the metrale engine pages describe it:
+ *   - q8_1 quantisation of bf16 activation rows   (moe_v41/init.rs: the
+ *     kquant_q8_1_rows_bf16 kernel and kquant_q8_1_rows_bytes sizing;
+ *     attn_v41/decode.rs, q_kv_projections: one quantisation for two matrices)
+ *   - the Q2_K x q8_1 matrix-vector product, single / shared-input pair /
+ *     expert-id batch (kquant_mmvq_q2_k_w, mmvq_q2k_pair_w,
+ *     kquant_mmvq_q2_k_experts_w*)
+ *   - fused bf16 SwiGLU + q8_1 re-quantisation (kquant_swiglu_q8_1_rows_bf16)
+ *   - engram Q2_K row gather + dequantisation to bf16 (engram_v41.rs,
+ *     EngramV41::rows_from_q2k and its dequant_q2_k_to_bf16 launch)
+ *   - the engram gate (engram_v41/apply.rs, the engram_v41_gate launch;
+ *     engram_v41.rs module doc, step 4)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers named *_dev, and every tensor argument, are DEVICE pointers on the
+ * current HIP device; `bases` in q2k_mmvq_experts is a HOST array of device
+ * pointers. `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream). The caller owns every buffer and the stream. The library never
+ * allocates, frees or synchronises: each call only enqueues kernels on
+ * `stream` and returns, so every call may be captured in a HIP graph.
+ *
+ * Every argument check runs on the host before any HIP call, in release
+ * builds too. Return values: Q2K_OK (0) or a negative Q2K_E* code;
+ * q2k_last_error() then gives a message (thread-local, valid until the next
+ * failing call on that thread). Data errors that only the device can see
+ * (an expert id or a table row id out of range) write NaN into the affected
+ * output rows and store 1 into *err_flag_dev when that pointer is non-NULL;
+ * the flag is never cleared by the library.
+ *
+ * Q2_K weights are GGUF Q2_K super-blocks, unchanged: 84 bytes per 256
+ * weights (engram_v41.rs, const ENGRAM_ROW_BYTES and the
+ * EngramLayerWeights::wkv_q2k doc), laid out scales[16] (low nibble = scale,
+ * high nibble = min), qs[64] (2-bit quants; element 128h+32j+l is bits
+ * 2j..2j+1 of qs[32h+l], sub-block 8h+2j+(l>=16)), fp16 d, fp16 dmin. A
+ * matrix [n, k] is n rows of k/256 consecutive blocks (row-major, no
+ * padding); its base must be 4-byte aligned.
+ *
+ * q8_1 activation rows use this library's own layout, sized by
+ * q8_1_rows_bytes(): per row of k values, k int8 quants, then k/32 f32 block
+ * scales, then k/16 int16 sums of each 16 quants. Treat it as opaque.
+ */
+#ifndef Q2K_DECODE_H
+#define Q2K_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define Q2K_API __attribute__((visibility("default")))
+#else
+#define Q2K_API
+#endif
+
+#define Q2K_ABI_VERSION 1
+
+#define Q2K_OK 0
+#define Q2K_EINVAL (-1)   /* NULL pointer, or pointers that must not overlap do */
+#define Q2K_ESHAPE (-2)   /* k % 256 != 0, m outside 1..8, n <= 0, hc outside 1..4, ... */
+#define Q2K_ESPACE (-3)   /* an output or workspace is smaller than required */
+#define Q2K_EALIGN (-4)   /* a pointer or stride is not aligned as documented */
+#define Q2K_ELAUNCH (-5)  /* the HIP launch itself failed (hipGetLastError) */
+#define Q2K_EDEVICE (-6)  /* no usable HIP device for the query the call needs */
+
+/* Largest token count of the product entry points (the pages take the
+ * Q2_K route for m <= 8 only: attn_v41/decode.rs, q_kv_projections). */
+#define Q2K_MAX_M 8
+
+/* Version of this ABI (Q2K_ABI_VERSION). */
+Q2K_API int32_t q2k_abi_version(void);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+Q2K_API const char* q2k_last_error(void);
+
+/* Bytes of `m` q8_1 rows of `k` values (cf. kquant_q8_1_rows_bytes in
+ * moe_v41/init.rs): m * k * 5 / 4. Returns 0 when m < 1 or k is not a
+ * positive multiple of 256. */
+Q2K_API size_t q8_1_rows_bytes(int32_t m, int32_t k);
+
+/* q8_1 quantisation of bf16 rows (kquant_q8_1_rows_bf16, moe_v41/init.rs;
+ * used once per input in attn_v41/decode.rs q_kv_projections).
+ *   x_bf16_dev : bf16 [m, k], row i at x + i * x_row_stride elements;
+ *                16-byte aligned base, x_row_stride % 8 == 0, >= k.
+ *   xq_dev     : output, q8_1_rows_bytes(m, k) bytes (xq_bytes must be at
+ *                least that), 16-byte aligned.
+ *   m >= 1 rows, k % 256 == 0.
+ * Per 32-wide block: amax = max|x|, d = amax/127 (correctly rounded f32
+ * division), q = round-half-away(x/d) in -127..127 (0 when amax == 0). */
+Q2K_API int32_t q8_1_rows(const void* x_bf16_dev, int64_t x_row_stride, void* xq_dev,
+                  size_t xq_bytes, int32_t m, int32_t k, void* stream);
+
+/* Q2_K x q8_1 product, one matrix (kquant_mmvq_q2_k_w, moe_v41/init.rs;
+ * the engram wkv projection of engram_v41/apply.rs).
+ *   w_dev  : Q2_K [n, k], 4-byte aligned.
+ *   xq_dev : q8_1 rows [m, k] from q8_1_rows, 16-byte aligned.
+ *   y_dev  : f32 [m, n] (row t at y + t*n), 4-byte aligned; must not
+ *            overlap w or xq.
+ *   1 <= m <= 8, n >= 1, k % 256 == 0.
+ * y[t][r] = sum over the row's blocks b and q8 blocks c of
+ *           d8[t][c] * (d_b * I - dmin_b * M), I and M exact int32 sums. */
+Q2K_API int32_t q2k_mmvq(const void* w_dev, const void* xq_dev, float* y_dev,
+                 int32_t n, int32_t k, int32_t m, void* stream);
+
+/* Two Q2_K matrices that read the same q8_1 rows, in one launch
+ * (mmvq_q2k_pair_w via kquant_mmvq_pair_w, attn_v41/decode.rs
+ * q_kv_projections: wq_a and wkv). ya_dev f32 [m, na], yb_dev f32 [m, nb];
+ * each as in q2k_mmvq; the two outputs must not overlap. */
+Q2K_API int32_t q2k_mmvq_pair(const void* wa_dev, float* ya_dev, int32_t na,
+                      const void* wb_dev, float* yb_dev, int32_t nb,
+                      const void* xq_dev, int32_t k, int32_t m, void* stream);
+
+/* Expert-id batch (kquant_mmvq_q2_k_experts_w*, moe_v41/init.rs: gate and
+ * up run as one batch of 2*ne matrices, up read at gate_out + ne*inter).
+ *   bases      : HOST array of n_bases (1..4) device pointers; base j holds
+ *                n_experts Q2_K matrices [n, k], expert e at
+ *                bases[j] + e * expert_stride_bytes (stride >= n*k/256*84,
+ *                multiple of 4).
+ *   ids_dev    : int32 [n_ids] expert ids (device); 1 <= n_ids <= 64.
+ *   xq_dev     : x_per_id == 0: q8_1 rows [m, k] shared by every matrix;
+ *                x_per_id == 1: q8_1 rows [n_ids * m, k], id i reads rows
+ *                i*m .. i*m+m-1.
+ *   y_dev      : f32 [n_bases, n_ids, m, n], in id-list order.
+ *   err_flag_dev : nullable int32; an id outside [0, n_experts) NaN-fills
+ *                its outputs and stores 1 here.
+ * Only the selected experts' matrices are read. */
+Q2K_API int32_t q2k_mmvq_experts(const void* const* bases, int32_t n_bases,
+                         int64_t expert_stride_bytes, int32_t n_experts,
+                         const int32_t* ids_dev, int32_t n_ids,
+                         const void* xq_dev, int32_t x_per_id, float* y_dev,
+                         int32_t n, int32_t k, int32_t m,
+                         int32_t* err_flag_dev, void* stream);
+
+/* Fused bf16 SwiGLU and q8_1 re-quantisation
+ * (kquant_swiglu_q8_1_rows_bf16, moe_v41/init.rs).
+ *   g_dev, u_dev : f32 [rows, k] contiguous (gate and up outputs).
+ *   h_bf16_dev   : nullable bf16 [rows, k]; receives h when non-NULL.
+ *   hq_dev       : q8_1 rows [rows, k], hq_bytes >= q8_1_rows_bytes(rows, k).
+ * h = bf16_rne(silu(g) * u) with silu(g) = g / (1 + exp(-g)) in f32, then
+ * hq = q8_1 of h exactly as q8_1_rows would quantise it. */
+Q2K_API int32_t swiglu_q8_1_rows(const float* g_dev, const float* u_dev, void* h_bf16_dev,
+                         void* hq_dev, size_t hq_bytes, int32_t rows, int32_t k,
+                         void* stream);
+
+/* Engram row gather and dequantisation to bf16 (engram_v41.rs,
+ * EngramV41::rows_from_q2k, dequant_q2_k_to_bf16): one Q2_K block per
+ * 256-wide row.
+ *   table_dev    : n_table_rows Q2_K blocks (84 bytes each), 4-byte aligned.
+ *   ids_dev      : nullable int64 [n_rows]; NULL reads rows 0..n_rows-1.
+ *   out_bf16_dev : bf16 [n_rows, 256].
+ *   err_flag_dev : nullable; an id outside [0, n_table_rows) NaN-fills its
+ *                  row and stores 1 here.
+ * out = bf16_rne(d*sc*q - dmin*m) with the value formed in f32. */
+Q2K_API int32_t q2k_dequant_rows(const void* table_dev, int64_t n_table_rows,
+                         const int64_t* ids_dev, int32_t n_rows, void* out_bf16_dev,
+                         int32_t* err_flag_dev, void* stream);
+
+/* Engram gate, in place on the f32 stream (engram_v41/apply.rs: grid
+ * [T, hc], arguments streams, kv, qk, dim, hc, eps; engram_v41.rs module doc
+ * step 4).
+ *   h_dev  : f32 [t, hc, dim], updated in place.
+ *   kv_dev : f32 [t, (hc+1)*dim]: the keys of streams 0..hc-1, then the one
+ *            shared value; must not overlap h.
+ *   qk_dev : f32 [hc, dim], the product q_weight * k_weight.
+ *   1 <= hc <= 4, dim >= 1, t >= 1.
+ * For each (t, j): s = sum(qk*h*k) / (rms(h)*rms(k)*sqrt(dim)) with
+ * rms(x) = sqrt(mean(x^2) + eps); g = sigmoid(sign(s)*sqrt|s|);
+ * h += g * value. */
+Q2K_API int32_t engram_gate(float* h_dev, const float* kv_dev, const float* qk_dev,
+                    int32_t t, int32_t hc, int32_t dim, float eps, void* stream);
+
+/* Integer stage of q2k_mmvq, exported for exact checking (same device
+ * code): out_dev int32 [m, n, k/32, 2] receives, per token t, row r and
+ * q8 block c, I = sum sc*q*xq and M = sum m*xq over the block's 32 values.
+ * Arguments as in q2k_mmvq. */
+Q2K_API int32_t q2k_block_dots(const void* w_dev, const void* xq_dev, int32_t* out_dev,
+                       int32_t n, int32_t k, int32_t m, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q2K_DECODE_H */

@@ -1,1 +1,218 @@
-"""Q2_K quantised decode for AMD MI355X (gfx950)."""
+"""Q2_K quantised decode for AMD MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libq2kdecode.so`` (declared in
+``include/q2k_decode.h``). Each function has the name of its C entry point
+and only marshals arguments: torch tensors in, device pointers and the
+current HIP stream out. Every step runs in the library's HIP kernels; there
+is no CPU fallback. A missing library raises on first use.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq2kdecode.so")
+
+Q2K_OK = 0
+ERROR_NAMES = {-1: "Q2K_EINVAL", -2: "Q2K_ESHAPE", -3: "Q2K_ESPACE", -4: "Q2K_EALIGN",
+               -5: "Q2K_ELAUNCH", -6: "Q2K_EDEVICE"}
+MAX_M = 8
+BLOCK_BYTES = 84
+BLOCK_WEIGHTS = 256
+
+# (name, restype, argtypes) of every exported symbol of the header.
+_VP, _I32, _I64, _SZ, _F32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                              ctypes.c_float)
+SIGNATURES = {
+    "q2k_abi_version": (_I32, []),
+    "q2k_last_error": (ctypes.c_char_p, []),
+    "q8_1_rows_bytes": (_SZ, [_I32, _I32]),
+    "q8_1_rows": (_I32, [_VP, _I64, _VP, _SZ, _I32, _I32, _VP]),
+    "q2k_mmvq": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
+    "q2k_mmvq_pair": (_I32, [_VP, _VP, _I32, _VP, _VP, _I32, _VP, _I32, _I32, _VP]),
+    "q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP, _I32,
+                                _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP]),
+    "swiglu_q8_1_rows": (_I32, [_VP, _VP, _VP, _VP, _SZ, _I32, _I32, _VP]),
+    "q2k_dequant_rows": (_I32, [_VP, _I64, _VP, _I32, _VP, _VP, _VP]),
+    "engram_gate": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _F32, _VP]),
+    "q2k_block_dots": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class Q2KError(RuntimeError):
+    """A non-zero status from the library, with its code and message."""
+
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn}: {ERROR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libq2kdecode.so (built in-tree); raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m q2_quantized_decode_amd.build`"
+                " (hipcc, gfx950). There is no CPU fallback.")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn: str, code: int) -> None:
+    if code != Q2K_OK:
+        msg = lib().q2k_last_error()
+        raise Q2KError(fn, code, msg.decode() if msg else "")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (cuda) tensor, got {t.device}")
+    return t.data_ptr()
+
+
+def _contig(t: torch.Tensor, name: str) -> int:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return _dev(t, name)
+
+
+def q2k_abi_version() -> int:
+    return int(lib().q2k_abi_version())
+
+
+def q8_1_rows_bytes(m: int, k: int) -> int:
+    return int(lib().q8_1_rows_bytes(m, k))
+
+
+def q8_1_rows(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q8_1 rows of a bf16 [m, k] tensor (row stride any multiple of 8)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a bf16 [m, k] tensor with unit column stride")
+    m, k = x.shape
+    need = q8_1_rows_bytes(m, k)
+    if out is None:
+        out = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check("q8_1_rows", lib().q8_1_rows(_dev(x, "x"), x.stride(0), _contig(out, "out"),
+                                        out.numel(), m, k, _stream()))
+    return out
+
+
+def q2k_mmvq(w: torch.Tensor, xq: torch.Tensor, n: int, k: int, m: int,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """f32 [m, n] = Q2_K w [n, k] times q8_1 rows xq [m, k]."""
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _check("q2k_mmvq", lib().q2k_mmvq(_contig(w, "w"), _contig(xq, "xq"), _contig(out, "out"),
+                                      n, k, m, _stream()))
+    return out
+
+
+def q2k_mmvq_pair(wa: torch.Tensor, na: int, wb: torch.Tensor, nb: int, xq: torch.Tensor,
+                  k: int, m: int, ya: Optional[torch.Tensor] = None,
+                  yb: Optional[torch.Tensor] = None):
+    """Two Q2_K matrices against the same q8_1 rows, one launch."""
+    if ya is None:
+        ya = torch.empty((m, na), dtype=torch.float32, device=wa.device)
+    if yb is None:
+        yb = torch.empty((m, nb), dtype=torch.float32, device=wb.device)
+    _check("q2k_mmvq_pair", lib().q2k_mmvq_pair(
+        _contig(wa, "wa"), _contig(ya, "ya"), na, _contig(wb, "wb"), _contig(yb, "yb"), nb,
+        _contig(xq, "xq"), k, m, _stream()))
+    return ya, yb
+
+
+def q2k_mmvq_experts(bases: Sequence[torch.Tensor], expert_stride_bytes: int, n_experts: int,
+                     ids: torch.Tensor, xq: torch.Tensor, x_per_id: bool, n: int, k: int,
+                     m: int, out: Optional[torch.Tensor] = None,
+                     err_flag: Optional[torch.Tensor] = None,
+                     base_ptrs: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """f32 [n_bases, n_ids, m, n] for the expert ids in ``ids`` (int32, device).
+
+    ``bases`` are the expert sets (expert e at byte e * expert_stride_bytes);
+    ``base_ptrs`` may give explicit device addresses inside them instead."""
+    if ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    n_ids = ids.numel()
+    ptrs = list(base_ptrs) if base_ptrs is not None else [_contig(b, "base") for b in bases]
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    if out is None:
+        out = torch.empty((len(ptrs), n_ids, m, n), dtype=torch.float32, device=ids.device)
+    flag = 0 if err_flag is None else _contig(err_flag, "err_flag")
+    _check("q2k_mmvq_experts", lib().q2k_mmvq_experts(
+        arr, len(ptrs), expert_stride_bytes, n_experts, _contig(ids, "ids"), n_ids,
+        _contig(xq, "xq"), 1 if x_per_id else 0, _contig(out, "out"), n, k, m, flag or None,
+        _stream()))
+    return out
+
+
+def swiglu_q8_1_rows(g: torch.Tensor, u: torch.Tensor, h: Optional[torch.Tensor] = None,
+                     hq: Optional[torch.Tensor] = None, want_h: bool = True):
+    """h = bf16(silu(g) * u) and its q8_1 rows; g, u f32 [rows, k]."""
+    if g.dtype != torch.float32 or u.dtype != torch.float32 or g.shape != u.shape or g.dim() != 2:
+        raise ValueError("g and u must be f32 [rows, k] of one shape")
+    rows, k = g.shape
+    if h is None and want_h:
+        h = torch.empty((rows, k), dtype=torch.bfloat16, device=g.device)
+    need = q8_1_rows_bytes(rows, k)
+    if hq is None:
+        hq = torch.empty(max(need, 16), dtype=torch.uint8, device=g.device)
+    hp = _contig(h, "h") if h is not None else None
+    _check("swiglu_q8_1_rows", lib().swiglu_q8_1_rows(
+        _contig(g, "g"), _contig(u, "u"), hp, _contig(hq, "hq"), hq.numel(), rows, k, _stream()))
+    return h, hq
+
+
+def q2k_dequant_rows(table: torch.Tensor, n_table_rows: int, ids: Optional[torch.Tensor],
+                     n_rows: int, out: Optional[torch.Tensor] = None,
+                     err_flag: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [n_rows, 256] rows of a Q2_K table, gathered by int64 ``ids``."""
+    if ids is not None and ids.dtype != torch.int64:
+        raise ValueError("ids must be int64")
+    if out is None:
+        out = torch.empty((n_rows, BLOCK_WEIGHTS), dtype=torch.bfloat16, device=table.device)
+    idp = _contig(ids, "ids") if ids is not None else None
+    flag = _contig(err_flag, "err_flag") if err_flag is not None else None
+    _check("q2k_dequant_rows", lib().q2k_dequant_rows(
+        _contig(table, "table"), n_table_rows, idp, n_rows, _contig(out, "out"), flag, _stream()))
+    return out
+
+
+def engram_gate(h: torch.Tensor, kv: torch.Tensor, qk: torch.Tensor, eps: float) -> torch.Tensor:
+    """In place on the f32 stream h [t, hc, dim]; kv f32 [t, (hc+1)*dim]; qk [hc, dim]."""
+    if h.dtype != torch.float32 or kv.dtype != torch.float32 or qk.dtype != torch.float32:
+        raise ValueError("h, kv and qk must be f32")
+    if h.dim() != 3:
+        raise ValueError("h must be [t, hc, dim]")
+    t, hc, dim = h.shape
+    _check("engram_gate", lib().engram_gate(_contig(h, "h"), _contig(kv, "kv"), _contig(qk, "qk"),
+                                            t, hc, dim, float(eps), _stream()))
+    return h
+
+
+def q2k_block_dots(w: torch.Tensor, xq: torch.Tensor, n: int, k: int, m: int,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int32 [m, n, k/32, 2]: the exact (I, M) sums of q2k_mmvq's integer stage."""
+    if out is None:
+        out = torch.empty((m, n, k // 32, 2), dtype=torch.int32, device=w.device)
+    _check("q2k_block_dots", lib().q2k_block_dots(_contig(w, "w"), _contig(xq, "xq"),
+                                                  _contig(out, "out"), n, k, m, _stream()))
+    return out

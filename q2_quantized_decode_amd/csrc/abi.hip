@@ -1,0 +1,279 @@
+// extern "C" entry points of libq2kdecode.so (declared in q2k_decode.h).
+//
+// Every argument check runs here, on the host, before any HIP call (the
+// pages refuse bad shapes "before any launch": engram_v41/apply.rs module
+// invariants, moe_v41/init.rs MoeV41::new, attn_v41/decode.rs m <= 8), and
+// in release builds too. Kernels are only enqueued on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/q2k_decode.h"
+#include "q2k_device.h"
+#include "q2k_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(Q2K_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return Q2K_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+size_t q2k_matrix_bytes(int64_t n, int64_t k) { return (size_t)n * (size_t)(k / 256) * 84; }
+
+int32_t check_k(const char* fn, int32_t k) {
+  if (k <= 0 || k % 256 != 0)
+    return fail(Q2K_ESHAPE, "%s: k = %d is not a positive multiple of 256 (Q2_K super-blocks)", fn, k);
+  return Q2K_OK;
+}
+
+int32_t check_m(const char* fn, int32_t m) {
+  if (m < 1 || m > Q2K_MAX_M)
+    return fail(Q2K_ESHAPE, "%s: m = %d outside 1..%d", fn, m, Q2K_MAX_M);
+  return Q2K_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t q2k_abi_version(void) { return Q2K_ABI_VERSION; }
+
+const char* q2k_last_error(void) { return g_err; }
+
+size_t q8_1_rows_bytes(int32_t m, int32_t k) {
+  if (m < 1 || k <= 0 || k % 256 != 0) return 0;
+  return (size_t)m * q2k::q8_row_bytes(k);
+}
+
+int32_t q8_1_rows(const void* x_bf16_dev, int64_t x_row_stride, void* xq_dev, size_t xq_bytes,
+                  int32_t m, int32_t k, void* stream) {
+  const char* fn = "q8_1_rows";
+  if (!x_bf16_dev || !xq_dev) return fail(Q2K_EINVAL, "%s: null pointer", fn);
+  if (m < 1) return fail(Q2K_ESHAPE, "%s: m = %d < 1", fn, m);
+  if (int32_t r = check_k(fn, k)) return r;
+  if (x_row_stride < k) return fail(Q2K_ESHAPE, "%s: row stride %lld < k = %d", fn, (long long)x_row_stride, k);
+  if (!aligned(x_bf16_dev, 16) || x_row_stride % 8 != 0)
+    return fail(Q2K_EALIGN, "%s: x must be 16-byte aligned with a row stride that is a multiple of 8", fn);
+  if (!aligned(xq_dev, 16)) return fail(Q2K_EALIGN, "%s: xq must be 16-byte aligned", fn);
+  const size_t need = q8_1_rows_bytes(m, k);
+  if (xq_bytes < need) return fail(Q2K_ESPACE, "%s: xq holds %zu bytes, %zu needed", fn, xq_bytes, need);
+  const size_t xbytes = ((size_t)(m - 1) * x_row_stride + k) * 2;
+  if (overlap(x_bf16_dev, xbytes, xq_dev, need)) return fail(Q2K_EINVAL, "%s: x and xq overlap", fn);
+  return launched(q2k::launch_q8_1_rows(x_bf16_dev, x_row_stride, xq_dev, m, k, (hipStream_t)stream), fn);
+}
+
+static int32_t check_matrix(const char* fn, const char* name, const void* w, int32_t n) {
+  if (!w) return fail(Q2K_EINVAL, "%s: %s is null", fn, name);
+  if (n < 1) return fail(Q2K_ESHAPE, "%s: %s has n = %d rows", fn, name, n);
+  if (!aligned(w, 4)) return fail(Q2K_EALIGN, "%s: %s must be 4-byte aligned", fn, name);
+  return Q2K_OK;
+}
+
+static int32_t check_out(const char* fn, const char* name, const void* y) {
+  if (!y) return fail(Q2K_EINVAL, "%s: %s is null", fn, name);
+  if (!aligned(y, 4)) return fail(Q2K_EALIGN, "%s: %s must be 4-byte aligned", fn, name);
+  return Q2K_OK;
+}
+
+int32_t q2k_mmvq(const void* w_dev, const void* xq_dev, float* y_dev, int32_t n, int32_t k,
+                 int32_t m, void* stream) {
+  const char* fn = "q2k_mmvq";
+  if (int32_t r = check_matrix(fn, "w", w_dev, n)) return r;
+  if (int32_t r = check_out(fn, "y", y_dev)) return r;
+  if (!xq_dev) return fail(Q2K_EINVAL, "%s: xq is null", fn);
+  if (int32_t r = check_k(fn, k)) return r;
+  if (int32_t r = check_m(fn, m)) return r;
+  if (!aligned(xq_dev, 16)) return fail(Q2K_EALIGN, "%s: xq must be 16-byte aligned", fn);
+  const size_t ybytes = (size_t)m * n * 4;
+  if (overlap(y_dev, ybytes, w_dev, q2k_matrix_bytes(n, k)) ||
+      overlap(y_dev, ybytes, xq_dev, q8_1_rows_bytes(m, k)))
+    return fail(Q2K_EINVAL, "%s: y overlaps an input", fn);
+  q2k::MmvqLaunch a{};
+  a.w[0] = w_dev;
+  a.y[0] = y_dev;
+  a.n[0] = n;
+  a.njobs = 1;
+  a.xq = xq_dev;
+  a.k = k;
+  a.m = m;
+  return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
+}
+
+int32_t q2k_mmvq_pair(const void* wa_dev, float* ya_dev, int32_t na, const void* wb_dev,
+                      float* yb_dev, int32_t nb, const void* xq_dev, int32_t k, int32_t m,
+                      void* stream) {
+  const char* fn = "q2k_mmvq_pair";
+  if (int32_t r = check_matrix(fn, "wa", wa_dev, na)) return r;
+  if (int32_t r = check_matrix(fn, "wb", wb_dev, nb)) return r;
+  if (int32_t r = check_out(fn, "ya", ya_dev)) return r;
+  if (int32_t r = check_out(fn, "yb", yb_dev)) return r;
+  if (!xq_dev) return fail(Q2K_EINVAL, "%s: xq is null", fn);
+  if (int32_t r = check_k(fn, k)) return r;
+  if (int32_t r = check_m(fn, m)) return r;
+  if (!aligned(xq_dev, 16)) return fail(Q2K_EALIGN, "%s: xq must be 16-byte aligned", fn);
+  const size_t ya_bytes = (size_t)m * na * 4, yb_bytes = (size_t)m * nb * 4;
+  if (overlap(ya_dev, ya_bytes, yb_dev, yb_bytes)) return fail(Q2K_EINVAL, "%s: ya and yb overlap", fn);
+  const size_t xqb = q8_1_rows_bytes(m, k);
+  if (overlap(ya_dev, ya_bytes, wa_dev, q2k_matrix_bytes(na, k)) ||
+      overlap(ya_dev, ya_bytes, wb_dev, q2k_matrix_bytes(nb, k)) ||
+      overlap(yb_dev, yb_bytes, wa_dev, q2k_matrix_bytes(na, k)) ||
+      overlap(yb_dev, yb_bytes, wb_dev, q2k_matrix_bytes(nb, k)) ||
+      overlap(ya_dev, ya_bytes, xq_dev, xqb) || overlap(yb_dev, yb_bytes, xq_dev, xqb))
+    return fail(Q2K_EINVAL, "%s: an output overlaps an input", fn);
+  q2k::MmvqLaunch a{};
+  a.w[0] = wa_dev;
+  a.y[0] = ya_dev;
+  a.n[0] = na;
+  a.w[1] = wb_dev;
+  a.y[1] = yb_dev;
+  a.n[1] = nb;
+  a.njobs = 2;
+  a.xq = xq_dev;
+  a.k = k;
+  a.m = m;
+  return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
+}
+
+int32_t q2k_mmvq_experts(const void* const* bases, int32_t n_bases, int64_t expert_stride_bytes,
+                         int32_t n_experts, const int32_t* ids_dev, int32_t n_ids,
+                         const void* xq_dev, int32_t x_per_id, float* y_dev, int32_t n, int32_t k,
+                         int32_t m, int32_t* err_flag_dev, void* stream) {
+  const char* fn = "q2k_mmvq_experts";
+  if (!bases) return fail(Q2K_EINVAL, "%s: bases is null", fn);
+  if (n_bases < 1 || n_bases > q2k::kMaxExpertBases)
+    return fail(Q2K_ESHAPE, "%s: n_bases = %d outside 1..%d", fn, n_bases, q2k::kMaxExpertBases);
+  for (int i = 0; i < n_bases; ++i)
+    if (int32_t r = check_matrix(fn, "bases[i]", bases[i], n)) return r;
+  if (!ids_dev || !xq_dev) return fail(Q2K_EINVAL, "%s: null pointer", fn);
+  if (int32_t r = check_out(fn, "y", y_dev)) return r;
+  if (int32_t r = check_k(fn, k)) return r;
+  if (int32_t r = check_m(fn, m)) return r;
+  if (n_experts < 1) return fail(Q2K_ESHAPE, "%s: n_experts = %d < 1", fn, n_experts);
+  if (n_ids < 1 || n_ids > 64) return fail(Q2K_ESHAPE, "%s: n_ids = %d outside 1..64", fn, n_ids);
+  if (x_per_id != 0 && x_per_id != 1) return fail(Q2K_ESHAPE, "%s: x_per_id = %d", fn, x_per_id);
+  const size_t mat = q2k_matrix_bytes(n, k);
+  if (expert_stride_bytes < (int64_t)mat)
+    return fail(Q2K_ESHAPE, "%s: expert stride %lld < matrix size %zu", fn, (long long)expert_stride_bytes, mat);
+  if (expert_stride_bytes % 4 != 0) return fail(Q2K_EALIGN, "%s: expert stride must be a multiple of 4", fn);
+  if (!aligned(xq_dev, 16)) return fail(Q2K_EALIGN, "%s: xq must be 16-byte aligned", fn);
+  if (!aligned(ids_dev, 4)) return fail(Q2K_EALIGN, "%s: ids must be 4-byte aligned", fn);
+  if ((int64_t)n_bases * n_ids * m * (int64_t)n > (int64_t)1 << 31)
+    return fail(Q2K_ESHAPE, "%s: output larger than 2^31 values", fn);
+  const size_t ybytes = (size_t)n_bases * n_ids * m * n * 4;
+  const size_t set_bytes = (size_t)expert_stride_bytes * (size_t)(n_experts - 1) + mat;
+  for (int i = 0; i < n_bases; ++i)
+    if (overlap(y_dev, ybytes, bases[i], set_bytes)) return fail(Q2K_EINVAL, "%s: y overlaps a base", fn);
+  if (overlap(y_dev, ybytes, xq_dev, q8_1_rows_bytes(x_per_id ? n_ids * m : m, k)))
+    return fail(Q2K_EINVAL, "%s: y overlaps xq", fn);
+  q2k::MmvqLaunch a{};
+  for (int i = 0; i < n_bases; ++i) a.w[i] = bases[i];
+  a.y[0] = y_dev;
+  a.n[0] = n;
+  a.njobs = n_bases;
+  a.xq = xq_dev;
+  a.ids = ids_dev;
+  a.n_ids = n_ids;
+  a.n_experts = n_experts;
+  a.x_per_id = x_per_id;
+  a.expert_stride = expert_stride_bytes;
+  a.err_flag = err_flag_dev;
+  a.k = k;
+  a.m = m;
+  return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
+}
+
+int32_t swiglu_q8_1_rows(const float* g_dev, const float* u_dev, void* h_bf16_dev, void* hq_dev,
+                         size_t hq_bytes, int32_t rows, int32_t k, void* stream) {
+  const char* fn = "swiglu_q8_1_rows";
+  if (!g_dev || !u_dev || !hq_dev) return fail(Q2K_EINVAL, "%s: null pointer", fn);
+  if (rows < 1) return fail(Q2K_ESHAPE, "%s: rows = %d < 1", fn, rows);
+  if (int32_t r = check_k(fn, k)) return r;
+  if (!aligned(g_dev, 16) || !aligned(u_dev, 16) || !aligned(hq_dev, 16) ||
+      (h_bf16_dev && !aligned(h_bf16_dev, 16)))
+    return fail(Q2K_EALIGN, "%s: g, u, h and hq must be 16-byte aligned", fn);
+  const size_t need = q8_1_rows_bytes(rows, k);
+  if (hq_bytes < need) return fail(Q2K_ESPACE, "%s: hq holds %zu bytes, %zu needed", fn, hq_bytes, need);
+  const size_t fb = (size_t)rows * k * 4, hb = (size_t)rows * k * 2;
+  if (overlap(hq_dev, need, g_dev, fb) || overlap(hq_dev, need, u_dev, fb) ||
+      (h_bf16_dev && (overlap(h_bf16_dev, hb, g_dev, fb) || overlap(h_bf16_dev, hb, u_dev, fb) ||
+                      overlap(h_bf16_dev, hb, hq_dev, need))))
+    return fail(Q2K_EINVAL, "%s: an output overlaps an input or the other output", fn);
+  return launched(q2k::launch_swiglu_q8_1_rows(g_dev, u_dev, h_bf16_dev, hq_dev, rows, k,
+                                               (hipStream_t)stream), fn);
+}
+
+int32_t q2k_dequant_rows(const void* table_dev, int64_t n_table_rows, const int64_t* ids_dev,
+                         int32_t n_rows, void* out_bf16_dev, int32_t* err_flag_dev, void* stream) {
+  const char* fn = "q2k_dequant_rows";
+  if (!table_dev || !out_bf16_dev) return fail(Q2K_EINVAL, "%s: null pointer", fn);
+  if (n_rows < 1) return fail(Q2K_ESHAPE, "%s: n_rows = %d < 1", fn, n_rows);
+  if (n_table_rows < 1) return fail(Q2K_ESHAPE, "%s: empty table", fn);
+  if (!ids_dev && n_rows > n_table_rows)
+    return fail(Q2K_ESPACE, "%s: %d contiguous rows from a %lld-row table", fn, n_rows, (long long)n_table_rows);
+  if (!aligned(table_dev, 4) || !aligned(out_bf16_dev, 8) || (ids_dev && !aligned(ids_dev, 8)))
+    return fail(Q2K_EALIGN, "%s: table must be 4-byte, out and ids 8-byte aligned", fn);
+  if (overlap(out_bf16_dev, (size_t)n_rows * 512, table_dev, (size_t)n_table_rows * 84))
+    return fail(Q2K_EINVAL, "%s: out overlaps the table", fn);
+  return launched(q2k::launch_dequant_rows(table_dev, n_table_rows, ids_dev, n_rows, out_bf16_dev,
+                                           err_flag_dev, (hipStream_t)stream), fn);
+}
+
+int32_t engram_gate(float* h_dev, const float* kv_dev, const float* qk_dev, int32_t t, int32_t hc,
+                    int32_t dim, float eps, void* stream) {
+  const char* fn = "engram_gate";
+  if (!h_dev || !kv_dev || !qk_dev) return fail(Q2K_EINVAL, "%s: null pointer", fn);
+  if (hc < 1 || hc > 4) return fail(Q2K_ESHAPE, "%s: hc = %d outside 1..4", fn, hc);
+  if (dim < 1) return fail(Q2K_ESHAPE, "%s: dim = %d < 1", fn, dim);
+  if (t < 1 || t > 65535) return fail(Q2K_ESHAPE, "%s: t = %d outside 1..65535", fn, t);
+  if (!(eps >= 0.0f)) return fail(Q2K_ESHAPE, "%s: eps must be >= 0", fn);
+  if (!aligned(h_dev, 4) || !aligned(kv_dev, 4) || !aligned(qk_dev, 4))
+    return fail(Q2K_EALIGN, "%s: pointers must be 4-byte aligned", fn);
+  const size_t hb = (size_t)t * hc * dim * 4;
+  if (overlap(h_dev, hb, kv_dev, (size_t)t * (hc + 1) * dim * 4) ||
+      overlap(h_dev, hb, qk_dev, (size_t)hc * dim * 4))
+    return fail(Q2K_EINVAL, "%s: h overlaps kv or qk", fn);
+  return launched(q2k::launch_engram_gate(h_dev, kv_dev, qk_dev, t, hc, dim, eps, (hipStream_t)stream), fn);
+}
+
+int32_t q2k_block_dots(const void* w_dev, const void* xq_dev, int32_t* out_dev, int32_t n,
+                       int32_t k, int32_t m, void* stream) {
+  const char* fn = "q2k_block_dots";
+  if (int32_t r = check_matrix(fn, "w", w_dev, n)) return r;
+  if (!xq_dev || !out_dev) return fail(Q2K_EINVAL, "%s: null pointer", fn);
+  if (int32_t r = check_k(fn, k)) return r;
+  if (int32_t r = check_m(fn, m)) return r;
+  if (!aligned(xq_dev, 16) || !aligned(out_dev, 16))
+    return fail(Q2K_EALIGN, "%s: xq and out must be 16-byte aligned", fn);
+  if ((int64_t)m * n * (k / 32) * 2 > (int64_t)1 << 31)
+    return fail(Q2K_ESHAPE, "%s: output larger than 2^31 values", fn);
+  q2k::MmvqLaunch a{};
+  a.w[0] = w_dev;
+  a.n[0] = n;
+  a.njobs = 1;
+  a.xq = xq_dev;
+  a.dots = out_dev;
+  a.k = k;
+  a.m = m;
+  return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

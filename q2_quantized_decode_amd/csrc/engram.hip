@@ -1,0 +1,110 @@
+// Engram row gather + Q2_K dequantisation to bf16, and the engram gate.
+//
+// Rows (engram_v41.rs, EngramV41::rows_from_q2k and its dequant_q2_k_to_bf16
+// launch): each table row is one 256-wide Q2_K block. The pages gather the
+// blocks on the host and upload them; here the row ids are read on the
+// device, so the table stays resident in HBM and only ids cross PCIe.
+// One wave per row, four elements per lane, one 8-byte bf16 store per lane.
+//
+// Gate (engram_v41/apply.rs, engram_v41_gate with grid [T, hc]; engram_v41.rs
+// module doc step 4): one 256-thread workgroup per (token, stream) forms
+// three sums over dim in a fixed order, then updates the stream in place.
+#include "q2k_device.h"
+#include "q2k_launch.h"
+
+namespace q2k {
+
+__global__ __launch_bounds__(256) void dequant_rows_kernel(const uint8_t* __restrict__ table,
+                                                           int64_t n_table_rows,
+                                                           const int64_t* __restrict__ ids,
+                                                           int n_rows, uint16_t* __restrict__ out,
+                                                           int32_t* err_flag) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t id = ids ? ids[row] : row;
+  uint16_t* o = out + (int64_t)row * kBlockWeights + 4 * lane;
+  if (id < 0 || id >= n_table_rows) {
+    *reinterpret_cast<u32x2*>(o) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+    if (lane == 0 && err_flag != nullptr) *err_flag = 1;
+    return;
+  }
+  const uint8_t* blk = table + id * kBlockBytes;
+  const int e = 4 * lane;            // elements e .. e+3 share h, j and sub-block
+  const int h = e >> 7;
+  const int j = (e >> 5) & 3;
+  const int l = e & 31;
+  const uint32_t qw = *reinterpret_cast<const uint32_t*>(blk + 16 + 32 * h + l) >> (2 * j);
+  const uint32_t sb = blk[e >> 4];
+  const uint32_t dd = *reinterpret_cast<const uint32_t*>(blk + 80);
+  const float d = fp16_bits_to_f32(dd & 0xffffu);
+  const float dmin = fp16_bits_to_f32(dd >> 16);
+  const float mterm = dmin * (float)(sb >> 4);   // exact: <= 15 significant bits
+  uint32_t bits[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t q = (qw >> (8 * i)) & 3u;
+    // d * (sc*q) is exact in f32, so the subtraction is the only rounding,
+    // whether or not it is fused.
+    const float v = d * (float)((sb & 15u) * q) - mterm;
+    bits[i] = f32_to_bf16_bits(v);
+  }
+  *reinterpret_cast<u32x2*>(o) = u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+}
+
+__device__ __forceinline__ float block_sum_256(float v, float* lds) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds[wave] = v;
+  __syncthreads();
+  return (lds[0] + lds[1]) + (lds[2] + lds[3]);
+}
+
+__global__ __launch_bounds__(256) void engram_gate_kernel(float* __restrict__ h,
+                                                          const float* __restrict__ kv,
+                                                          const float* __restrict__ qk, int hc,
+                                                          int dim, float eps) {
+  __shared__ float lds[4];
+  const int t = blockIdx.x;
+  const int j = blockIdx.y;
+  float* hs = h + ((int64_t)t * hc + j) * dim;
+  const float* key = kv + (int64_t)t * (hc + 1) * dim + (int64_t)j * dim;
+  const float* val = kv + (int64_t)t * (hc + 1) * dim + (int64_t)hc * dim;
+  const float* w = qk + (int64_t)j * dim;
+  float shh = 0.0f, skk = 0.0f, sqk = 0.0f;
+  for (int i = threadIdx.x; i < dim; i += 256) {
+    const float x = hs[i];
+    const float kk = key[i];
+    shh = fmaf(x, x, shh);
+    skk = fmaf(kk, kk, skk);
+    sqk = fmaf(w[i] * x, kk, sqk);
+  }
+  shh = block_sum_256(shh, lds);
+  skk = block_sum_256(skk, lds);
+  sqk = block_sum_256(sqk, lds);
+  const float rh = sqrtf(shh / (float)dim + eps);
+  const float rk = sqrtf(skk / (float)dim + eps);
+  const float s = sqk / (rh * rk * sqrtf((float)dim));
+  const float sg = copysignf(sqrtf(fabsf(s)), s);
+  const float g = 1.0f / (1.0f + expf(-sg));
+  for (int i = threadIdx.x; i < dim; i += 256) hs[i] = fmaf(g, val[i], hs[i]);
+}
+
+hipError_t launch_dequant_rows(const void* table, int64_t n_table_rows, const int64_t* ids,
+                               int n_rows, void* out, int32_t* err_flag, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((n_rows + 3) / 4);
+  hipLaunchKernelGGL(dequant_rows_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(table), n_table_rows, ids, n_rows,
+                     static_cast<uint16_t*>(out), err_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_engram_gate(float* h, const float* kv, const float* qk, int t, int hc, int dim,
+                              float eps, hipStream_t stream) {
+  hipLaunchKernelGGL(engram_gate_kernel, dim3((unsigned)t, (unsigned)hc), dim3(256), 0, stream, h,
+                     kv, qk, hc, dim, eps);
+  return hipGetLastError();
+}
+
+}  // namespace q2k

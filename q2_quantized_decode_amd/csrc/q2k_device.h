@@ -1,0 +1,57 @@
+// Device-side helpers shared by the gfx950 kernels of libq2kdecode.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q2k {
+
+constexpr int kBlockBytes = 84;     // GGUF Q2_K super-block (engram_v41.rs ENGRAM_ROW_BYTES)
+constexpr int kBlockWeights = 256;
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// Same vectors with only 4-byte alignment: Q2_K blocks are 84 bytes, so a
+// field inside one is dword aligned but not 8/16-byte aligned.
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// q8_1 row layout of this library: k int8 quants, k/32 f32 scales, k/16
+// int16 sums of 16 quants.
+__host__ __device__ constexpr size_t q8_row_bytes(int k) { return (size_t)k * 5 / 4; }
+__host__ __device__ constexpr size_t q8_scale_offset(int k) { return (size_t)k; }
+__host__ __device__ constexpr size_t q8_sum_offset(int k) { return (size_t)k + (size_t)k / 8; }
+
+// Load through an explicit global (address space 1) pointer, so the access
+// is a global_load with an SGPR base rather than a flat load.
+template <typename T>
+__device__ __forceinline__ T gload(const void* p) {
+  return *(const __attribute__((address_space(1))) T*)(p);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// f32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float fp16_bits_to_f32(uint32_t h) {
+  _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
+  return (float)v;
+}
+
+// Signed 4 x int8 dot product accumulated into c (v_dot4c_i32_i8).
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+__device__ __forceinline__ float quiet_nan() { return __uint_as_float(0x7fc00000u); }
+
+}  // namespace q2k

@@ -1,0 +1,45 @@
+// Internal launchers behind the C ABI. Arguments are validated by the ABI
+// layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q2k {
+
+// Up to this many matrices in one plain (non-expert) product launch.
+constexpr int kMaxPlainJobs = 4;
+constexpr int kMaxExpertBases = 4;
+
+struct MmvqLaunch {
+  // Plain mode (ids == nullptr): job j multiplies w[j] [n[j], k] by xq.
+  // Expert mode (ids != nullptr): job base*n_ids + i multiplies the matrix
+  // w[base] + ids[i] * expert_stride by xq (shared) or by the i-th group of
+  // m rows of xq (x_per_id), writing y[0] + (base*n_ids + i) * m * n[0].
+  const void* w[kMaxPlainJobs];
+  float* y[kMaxPlainJobs];
+  int32_t n[kMaxPlainJobs];
+  int32_t njobs;
+  const void* xq;
+  const int32_t* ids;
+  int32_t n_ids;
+  int32_t n_experts;
+  int32_t x_per_id;
+  int64_t expert_stride;
+  int32_t* err_flag;
+  int32_t* dots;   // non-null: write the int32 (I, M) block sums instead of y (plain, one job)
+  int32_t k;
+  int32_t m;
+};
+
+hipError_t launch_q8_1_rows(const void* x, int64_t stride, void* xq, int m, int k,
+                            hipStream_t stream);
+hipError_t launch_swiglu_q8_1_rows(const float* g, const float* u, void* h, void* hq, int rows,
+                                   int k, hipStream_t stream);
+hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream);
+hipError_t launch_dequant_rows(const void* table, int64_t n_table_rows, const int64_t* ids,
+                               int n_rows, void* out, int32_t* err_flag, hipStream_t stream);
+hipError_t launch_engram_gate(float* h, const float* kv, const float* qk, int t, int hc, int dim,
+                              float eps, hipStream_t stream);
+
+}  // namespace q2k

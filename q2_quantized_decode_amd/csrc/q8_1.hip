@@ -1,0 +1,143 @@
+// q8_1 activation rows and the fused bf16 SwiGLU + q8_1 re-quantisation.
+//
+// q8_1 (moe_v41/init.rs: kquant_q8_1_rows_bf16; attn_v41/decode.rs,
+// q_kv_projections): each 32-wide block of a row gets d = amax / 127 and
+// int8 quants round(x / d). This library stores d as f32 and, for the Q2_K
+// min term, the integer sum of every 16 quants.
+//
+// Launch shape: one lane per 8 consecutive values (one 16-byte bf16 load),
+// four lanes per 32-block; the block's amax and the 16-wide sums are
+// combined across those lanes with shuffles. The quantiser is latency bound
+// (at most a few tens of thousands of values per call), so the only goal is
+// one pass with coalesced 16-byte loads.
+#include "q2k_device.h"
+#include "q2k_launch.h"
+
+namespace q2k {
+
+// Quantise the 8 values v (elements e0..e0+7 of one row) and store them.
+// Lanes 4i..4i+3 of the wave must hold one 32-block; all lanes call this.
+__device__ __forceinline__ void q8_1_store8(const float v[8], uint8_t* row, int e0, int k,
+                                            bool active) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+  a = fmaxf(a, __shfl_xor(a, 1));
+  a = fmaxf(a, __shfl_xor(a, 2));
+  // Correctly rounded f32 division (no fast-math reciprocal).
+  const float d = a / 127.0f;
+  int q[8];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int qi = 0;
+    if (d > 0.0f) {
+      float r = roundf(v[i] / d);   // halves away from zero
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+      qi = (int)r;
+    }
+    q[i] = qi;
+    s += qi;
+  }
+  s += __shfl_xor(s, 1);   // lanes (4i, 4i+1) and (4i+2, 4i+3): one 16-wide half each
+  if (!active) return;
+  uint32_t lo = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
+                ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
+  uint32_t hi = (uint32_t)(q[4] & 0xff) | ((uint32_t)(q[5] & 0xff) << 8) |
+                ((uint32_t)(q[6] & 0xff) << 16) | ((uint32_t)(q[7] & 0xff) << 24);
+  *reinterpret_cast<u32x2*>(row + e0) = u32x2{lo, hi};
+  const int lane = threadIdx.x & 63;
+  if ((lane & 3) == 0)
+    *reinterpret_cast<float*>(row + q8_scale_offset(k) + (size_t)(e0 / 32) * 4) = d;
+  if ((lane & 1) == 0)
+    *reinterpret_cast<int16_t*>(row + q8_sum_offset(k) + (size_t)(e0 / 16) * 2) = (int16_t)s;
+}
+
+__global__ __launch_bounds__(256) void q8_1_rows_kernel(const uint16_t* __restrict__ x,
+                                                        int64_t stride, uint8_t* __restrict__ xq,
+                                                        int m, int k) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_row = k / 8;
+  const int64_t total = (int64_t)m * per_row;
+  const bool active = gid < total;
+  const int64_t row = active ? gid / per_row : 0;
+  const int e0 = active ? (int)(gid - row * per_row) * 8 : 0;
+  float v[8];
+  if (active) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(x + row * stride + e0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_bits_to_f32(raw[i] & 0xffffu);
+      v[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  q8_1_store8(v, xq + row * q8_row_bytes(k), e0, k, active);
+}
+
+// h = bf16(silu(g) * u), then q8_1 of h. silu(g) = g / (1 + exp(-g)), in f32.
+__global__ __launch_bounds__(256) void swiglu_q8_1_rows_kernel(const float* __restrict__ g,
+                                                               const float* __restrict__ u,
+                                                               uint16_t* __restrict__ h_out,
+                                                               uint8_t* __restrict__ hq,
+                                                               int rows, int k) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_row = k / 8;
+  const int64_t total = (int64_t)rows * per_row;
+  const bool active = gid < total;
+  const int64_t row = active ? gid / per_row : 0;
+  const int e0 = active ? (int)(gid - row * per_row) * 8 : 0;
+  float v[8];
+  uint32_t hb[8];
+  if (active) {
+    const size_t off = (size_t)row * k + e0;
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(g + off);
+    const f32x4 g1 = *reinterpret_cast<const f32x4*>(g + off + 4);
+    const f32x4 u0 = *reinterpret_cast<const f32x4*>(u + off);
+    const f32x4 u1 = *reinterpret_cast<const f32x4*>(u + off + 4);
+    const float gg[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+    const float uu[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // silu(g) = g * sigmoid(g), with exp taken of -|g| so it cannot
+      // overflow: sigmoid = 1/(1+e) for g >= 0 and e/(1+e) for g < 0.
+      const float e = expf(-fabsf(gg[i]));
+      const float sig = gg[i] >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
+      const float silu = gg[i] * sig;
+      hb[i] = f32_to_bf16_bits(silu * uu[i]);
+      v[i] = bf16_bits_to_f32(hb[i]);
+    }
+    if (h_out != nullptr) {
+      u32x4 packed;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed[i] = hb[2 * i] | (hb[2 * i + 1] << 16);
+      *reinterpret_cast<u32x4*>(h_out + off) = packed;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  q8_1_store8(v, hq + row * q8_row_bytes(k), e0, k, active);
+}
+
+hipError_t launch_q8_1_rows(const void* x, int64_t stride, void* xq, int m, int k,
+                            hipStream_t stream) {
+  const int64_t lanes = (int64_t)m * (k / 8);
+  const int64_t blocks = (lanes + 255) / 256;
+  hipLaunchKernelGGL(q8_1_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), stride, static_cast<uint8_t*>(xq), m, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_q8_1_rows(const float* g, const float* u, void* h, void* hq, int rows,
+                                   int k, hipStream_t stream) {
+  const int64_t lanes = (int64_t)rows * (k / 8);
+  const int64_t blocks = (lanes + 255) / 256;
+  hipLaunchKernelGGL(swiglu_q8_1_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g, u,
+                     static_cast<uint16_t*>(h), static_cast<uint8_t*>(hq), rows, k);
+  return hipGetLastError();
+}
+
+}  // namespace q2k

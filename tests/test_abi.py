@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+
+The pointers passed here are never dereferenced: every call below fails
+validation, which runs before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import q2_quantized_decode_amd as q2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q2k_decode.h")
+
+EINVAL, ESHAPE, ESPACE, EALIGN = -1, -2, -3, -4
+P = 0x7f0000000000          # a 256-byte aligned fake device address
+Q = 0x7f0001000000
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"Q2K_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return q2.lib()
+
+
+def test_header_symbols_exported(L):
+    names = _declared()
+    assert set(names) == set(q2.SIGNATURES), names
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_version_and_sizes(L):
+    assert L.q2k_abi_version() == 1
+    assert L.q8_1_rows_bytes(1, 1024) == 1280
+    assert L.q8_1_rows_bytes(8, 7168) == 8 * 8960
+    assert L.q8_1_rows_bytes(0, 1024) == 0
+    assert L.q8_1_rows_bytes(1, 100) == 0
+    assert L.q8_1_rows_bytes(1, -256) == 0
+
+
+def _err(L):
+    return L.q2k_last_error().decode()
+
+
+def test_q8_1_rows_validation(L):
+    assert L.q8_1_rows(None, 1024, P, 1280, 1, 1024, None) == EINVAL
+    assert L.q8_1_rows(P, 1024, Q, 1280, 1, 1000, None) == ESHAPE
+    assert "multiple of 256" in _err(L)
+    assert L.q8_1_rows(P, 1024, Q, 1280, 0, 1024, None) == ESHAPE
+    assert L.q8_1_rows(P, 512, Q, 1280, 1, 1024, None) == ESHAPE       # stride < k
+    assert L.q8_1_rows(P + 2, 1024, Q, 1280, 1, 1024, None) == EALIGN
+    assert L.q8_1_rows(P, 1028, Q, 2560, 2, 1024, None) == EALIGN     # stride % 8
+    assert L.q8_1_rows(P, 1024, Q, 1279, 1, 1024, None) == ESPACE
+    assert L.q8_1_rows(P, 1024, P + 16, 1280, 1, 1024, None) == EINVAL  # overlap
+
+
+def test_mmvq_validation(L):
+    assert L.q2k_mmvq(None, Q, P, 256, 1024, 1, None) == EINVAL
+    assert L.q2k_mmvq(P, Q, 0x100, 256, 1000, 1, None) == ESHAPE
+    assert L.q2k_mmvq(P, Q, 0x100, 256, 1024, 9, None) == ESHAPE
+    assert "1..8" in _err(L)
+    assert L.q2k_mmvq(P, Q, 0x100, 256, 1024, 0, None) == ESHAPE
+    assert L.q2k_mmvq(P, Q, 0x100, 0, 1024, 1, None) == ESHAPE
+    assert L.q2k_mmvq(P + 2, Q, 0x100, 256, 1024, 1, None) == EALIGN
+    assert L.q2k_mmvq(P, Q + 4, 0x100, 256, 1024, 1, None) == EALIGN
+    assert L.q2k_mmvq(P, Q, P + 100, 256, 1024, 1, None) == EINVAL    # y inside w
+
+
+def test_pair_validation(L):
+    assert L.q2k_mmvq_pair(P, 0x100, 1024, None, 0x10000, 512, Q, 4096, 1, None) == EINVAL
+    assert L.q2k_mmvq_pair(P, 0x100, 1024, P, 0x200, 512, Q, 4096, 1, None) == EINVAL  # ya/yb overlap
+    assert L.q2k_mmvq_pair(P, 0x100, 1024, P, 0x100000, 512, Q, 4096, 9, None) == ESHAPE
+
+
+def test_experts_validation(L):
+    arr = (ctypes.c_void_p * 2)(P, Q)
+    ok = dict(stride=1024 * 16 * 84, n_experts=4, ids=0x200000, n_ids=8, xq=0x300000,
+              y=0x400000, n=1024, k=4096, m=1)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.q2k_mmvq_experts(arr, kw.get("n_bases", 2), a["stride"], a["n_experts"],
+                                  a["ids"], a["n_ids"], a["xq"], kw.get("x_per_id", 0), a["y"],
+                                  a["n"], a["k"], a["m"], None, None)
+    assert call(n_bases=0) == ESHAPE
+    assert call(n_bases=5) == ESHAPE
+    assert call(stride=100) == ESHAPE
+    assert call(stride=1024 * 16 * 84 + 2) == EALIGN
+    assert call(n_ids=0) == ESHAPE
+    assert call(n_ids=65) == ESHAPE
+    assert call(x_per_id=2) == ESHAPE
+    assert call(ids=0) == EINVAL
+    assert call(k=4000) == ESHAPE
+    assert call(n_experts=0) == ESHAPE
+    assert L.q2k_mmvq_experts(None, 1, ok["stride"], 4, 0x200000, 8, 0x300000, 0, 0x400000,
+                              1024, 4096, 1, None, None) == EINVAL
+
+
+def test_swiglu_dequant_gate_dots_validation(L):
+    assert L.swiglu_q8_1_rows(P, Q, None, 0x10000000, 100, 8, 2048, None) == ESPACE
+    assert L.swiglu_q8_1_rows(P, Q, None, 0x10000000, 8 * 2560, 8, 2000, None) == ESHAPE
+    assert L.swiglu_q8_1_rows(P + 4, Q, None, 0x10000000, 8 * 2560, 8, 2048, None) == EALIGN
+    assert L.swiglu_q8_1_rows(None, Q, None, 0x10000000, 8 * 2560, 8, 2048, None) == EINVAL
+    assert L.q2k_dequant_rows(None, 10, None, 8, Q, None, None) == EINVAL
+    assert L.q2k_dequant_rows(P, 4, None, 8, Q, None, None) == ESPACE
+    assert L.q2k_dequant_rows(P, 10, None, 0, Q, None, None) == ESHAPE
+    assert L.q2k_dequant_rows(P + 2, 10, None, 8, Q, None, None) == EALIGN
+    assert L.engram_gate(P, Q, 0x10000000, 1, 5, 4096, 1e-6, None) == ESHAPE
+    assert L.engram_gate(P, Q, 0x10000000, 1, 0, 4096, 1e-6, None) == ESHAPE
+    assert "1..4" in _err(L)
+    assert L.engram_gate(P, Q, 0x10000000, 0, 4, 4096, 1e-6, None) == ESHAPE
+    assert L.engram_gate(P, P + 64, 0x10000000, 1, 4, 4096, 1e-6, None) == EINVAL
+    assert L.engram_gate(P, Q, 0x10000000, 1, 4, 4096, -1.0, None) == ESHAPE
+    assert L.q2k_block_dots(P, Q, 0x10000000, 256, 1024, 9, None) == ESHAPE
+    assert L.q2k_block_dots(P, Q, 0x10000004, 256, 1024, 1, None) == EALIGN
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros((1, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        q2.q8_1_rows(x)

@@ -1,0 +1,422 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: q8_1 bytes, integer block sums and dequantised bf16 rows bit-exact;
+f32 products and the gated stream within |gpu - ref| <= 1e-4 + 2e-3 |ref|
+elementwise; the bf16 SwiGLU value within one bf16 ulp (the GPU forms it in
+f32, the oracle in fp64), with its q8_1 bytes bit-exact from the GPU's own h.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import q2_quantized_decode_amd as q2
+from oracle import q2k_oracle as orc
+from q2_quantized_decode_amd import synthetic as syn
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 1e-4, 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    q2.lib()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    return syn.bf16_bits_to_tensor(bits).cuda()
+
+
+def split_q8(buf: np.ndarray, m: int, k: int):
+    """Unpack the library's q8_1 rows (layout stated in the header)."""
+    rb = k * 5 // 4
+    rows = buf[: m * rb].reshape(m, rb)
+    xq = rows[:, :k].view(np.int8).astype(np.int64)
+    d = rows[:, k:k + k // 8].copy().view(np.float32)
+    s = rows[:, k + k // 8:k + k // 4].copy().view(np.int16).astype(np.int64)
+    return xq, d, s
+
+
+def assert_q8_equal(buf_dev: torch.Tensor, x_bits: np.ndarray):
+    m, k = x_bits.shape
+    xq, d, s = split_q8(buf_dev.cpu().numpy(), m, k)
+    oq, od, os_ = orc.q8_1_from_bf16_bits(x_bits)
+    assert np.array_equal(d.view(np.uint32), od.view(np.uint32)), "q8_1 scales differ"
+    assert np.array_equal(xq, oq), "q8_1 quants differ"
+    assert np.array_equal(s, os_), "q8_1 half sums differ"
+    return oq, od
+
+
+def bf16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in bf16 steps (+0 and -0 are the same point)."""
+    def key(bits):
+        v = bits.astype(np.int64)
+        return np.where(v & 0x8000, -(v & 0x7FFF), v)
+    return np.abs(key(a) - key(b))
+
+
+def assert_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    excess = np.abs(got - ref) - (ATOL + RTOL * np.abs(ref))
+    i = int(np.argmax(excess))
+    assert excess.flat[i] <= 0, (f"{what}: element {np.unravel_index(i, got.shape)} "
+                                 f"gpu {got.flat[i]!r} ref {ref.flat[i]!r}")
+
+
+# ----------------------------------------------------------------- q8_1 -----
+
+@pytest.mark.parametrize("m,k,seed,outliers", [
+    (1, 1024, 1000, 0.0), (8, 7168, 1004, 0.05), (3, 256, 5, 0.0), (5, 4096, 6, 0.2),
+    (64, 2048, 7, 0.05)])
+def test_q8_1_rows_bit_exact(m, k, seed, outliers):
+    x = syn.bf16_normal(syn.rng_for(seed, m, k), (m, k), outlier_frac=outliers)
+    assert_q8_equal(q2.q8_1_rows(bf16_dev(x)), x)
+
+
+def test_q8_1_rows_strided_and_special_blocks():
+    k = 512
+    rng = syn.rng_for(77)
+    x = syn.bf16_normal(rng, (4, k)).astype(np.uint16)
+    f = orc.bf16_bits_to_f32(x).copy()
+    f[0, 0:32] = 0.0                                 # all-zero block
+    f[1, 32:64] = 0.0
+    f[1, 40] = -3.0                                  # single nonzero
+    f[2, 64:96] = np.float32(1.0)                    # ties: elements at amax / 2
+    f[2, 65] = 0.5
+    f[2, 66] = -0.5
+    f[3, 96:128] = np.arange(-16, 16, dtype=np.float32) * 4
+    f[3, 127] = 127.0                                # d = 1
+    x = syn.f32_to_bf16_bits_torch(f)
+    big = np.zeros((4, k + 64), dtype=np.uint16)     # rows 576 apart (stride % 8 == 0)
+    big[:, :k] = x
+    xt = bf16_dev(big)[:, :k]
+    assert xt.stride(0) == k + 64
+    assert_q8_equal(q2.q8_1_rows(xt), x)
+
+
+def test_q8_1_rows_tiny_blocks_keep_subnormal_scales():
+    # amax at the bottom of the bf16 normal range: d = amax / 127 is subnormal in f32
+    k = 256
+    f = np.zeros((1, k), dtype=np.float32)
+    f[0, :32] = np.float32(2.0 ** -126) * np.arange(1, 33, dtype=np.float32) / 32
+    f[0, 32:64] = np.float32(2.0 ** -120)
+    x = syn.f32_to_bf16_bits_torch(f)
+    assert_q8_equal(q2.q8_1_rows(bf16_dev(x)), x)
+
+
+# ---------------------------------------------------------------- mmvq ------
+
+SHAPES = [
+    (256, 1024, 1), (1, 256, 1), (3, 256, 8), (37, 512, 2), (1000, 2048, 1), (333, 4096, 3),
+    (130, 7168, 1), (130, 7168, 8), (77, 1792, 5), (10, 8448, 1), (9, 9216, 4), (257, 1024, 7),
+    (64, 2560, 6),
+]
+
+
+@pytest.mark.parametrize("n,k,m", SHAPES)
+def test_mmvq_and_block_dots(n, k, m):
+    case = syn.single_gemv_case(n=n, k=k, m=m, seed=n * 31 + k + m)
+    w = dev(case.w.reshape(-1))
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits))
+    oq, od = assert_q8_equal(xq, case.x_bits)
+    y = q2.q2k_mmvq(w, xq, n, k, m)
+    dots = q2.q2k_block_dots(w, xq, n, k, m)
+    torch.cuda.synchronize()
+    I, M = orc.block_dots(case.w, oq)
+    got = dots.cpu().numpy().astype(np.int64)
+    assert np.array_equal(got[..., 0], I), "I sums differ"
+    assert np.array_equal(got[..., 1], M), "M sums differ"
+    assert_close(y.cpu().numpy(), orc.mmvq(case.w, oq, od), f"mmvq n={n} k={k} m={m}")
+
+
+def test_mmvq_single_gemv_workload():
+    """256 x 1024 (4 super-blocks) Q2_K against one bf16 token."""
+    case = syn.single_gemv_case()
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits))
+    oq, od = assert_q8_equal(xq, case.x_bits)
+    y = q2.q2k_mmvq(dev(case.w.reshape(-1)), xq, 256, 1024, 1)
+    assert_close(y.cpu().numpy(), orc.mmvq(case.w, oq, od), "single gemv")
+
+
+def test_mmvq_exact_closed_form():
+    # W = 3 (q = 3, sc = 1, m = 0, d = 1); x = 127 everywhere: d8 = 1, y = 3*127*k exactly
+    n, k = 96, 2048
+    w = np.zeros((n, k // 256, 84), dtype=np.uint8)
+    w[..., 0:16] = 0x01
+    w[..., 16:80] = 0xFF
+    w[..., 81] = 0x3C
+    x = syn.f32_to_bf16_bits_torch(np.full((2, k), 127.0, np.float32))
+    y = q2.q2k_mmvq(dev(w.reshape(-1)), q2.q8_1_rows(bf16_dev(x)), n, k, 2)
+    assert np.all(y.cpu().numpy() == 3 * 127 * k)
+
+
+def test_mmvq_deterministic_and_stride_independent():
+    case = syn.single_gemv_case(n=2048, k=4096, m=4, seed=42)
+    w = dev(case.w.reshape(-1))
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits))
+    a = q2.q2k_mmvq(w, xq, 2048, 4096, 4).cpu().numpy()
+    b = q2.q2k_mmvq(w, xq, 2048, 4096, 4).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # the first 1000 rows alone give the same bytes as inside the bigger launch
+    c = q2.q2k_mmvq(w[: 1000 * 16 * 84], xq, 1000, 4096, 4).cpu().numpy()
+    assert np.array_equal(c.view(np.uint32), a[:, :1000].view(np.uint32))
+
+
+# ---------------------------------------------------------------- pair ------
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_pair_attention_inputs(m):
+    """x [m, 4096] quantised once, wq_a [1024, 4096] and wkv [512, 4096]."""
+    pc = syn.attention_pair_case(m)
+    xq = q2.q8_1_rows(bf16_dev(pc.x_bits))
+    oq, od = assert_q8_equal(xq, pc.x_bits)
+    wa, wb = dev(pc.wa.reshape(-1)), dev(pc.wb.reshape(-1))
+    ya, yb = q2.q2k_mmvq_pair(wa, pc.na, wb, pc.nb, xq, pc.k, m)
+    ra, rb = orc.mmvq_pair(pc.wa, pc.wb, oq, od)
+    assert_close(ya.cpu().numpy(), ra, "pair a")
+    assert_close(yb.cpu().numpy(), rb, "pair b")
+    sa = q2.q2k_mmvq(wa, xq, pc.na, pc.k, m).cpu().numpy()
+    sb = q2.q2k_mmvq(wb, xq, pc.nb, pc.k, m).cpu().numpy()
+    assert np.array_equal(sa.view(np.uint32), ya.cpu().numpy().view(np.uint32))
+    assert np.array_equal(sb.view(np.uint32), yb.cpu().numpy().view(np.uint32))
+
+
+def test_pair_ragged():
+    pc = syn.attention_pair_case(3, seed=9, na=37, nb=5, k=1280)
+    xq = q2.q8_1_rows(bf16_dev(pc.x_bits))
+    oq, od = assert_q8_equal(xq, pc.x_bits)
+    ya, yb = q2.q2k_mmvq_pair(dev(pc.wa.reshape(-1)), 37, dev(pc.wb.reshape(-1)), 5, xq, 1280, 3)
+    ra, rb = orc.mmvq_pair(pc.wa, pc.wb, oq, od)
+    assert_close(ya.cpu().numpy(), ra, "ragged pair a")
+    assert_close(yb.cpu().numpy(), rb, "ragged pair b")
+
+
+# -------------------------------------------------------------- experts -----
+
+POISON = 0x7E   # every byte 0x7E: d = dmin = fp16 0x7E7E, a NaN
+
+
+def _expert_set(case, kind, n_rows, n_blocks):
+    """Resident set of all experts of one kind: unselected experts are
+    poisoned (NaN scales), the selected ones hold their seeded matrices."""
+    per = n_rows * n_blocks * 84
+    buf = torch.full((case.n_experts * per,), POISON, dtype=torch.uint8, device="cuda")
+    for e in case.ids.tolist():
+        buf[e * per:(e + 1) * per] = dev(case.expert_matrix(e, kind).reshape(-1))
+    return buf, per
+
+
+@pytest.fixture(scope="module")
+def expert_batch():
+    case = syn.expert_batch_case()
+    gate, per_gu = _expert_set(case, "gate", case.inter, case.dim // 256)
+    up, _ = _expert_set(case, "up", case.inter, case.dim // 256)
+    down, per_d = _expert_set(case, "down", case.dim, case.inter // 256)
+    return case, gate, up, down, per_gu, per_d
+
+
+def test_expert_batch_stagewise(expert_batch):
+    """Gate/up over 8 of 256 experts, bf16 SwiGLU + q8_1, down: [8, 4096]."""
+    case, gate, up, down, per_gu, per_d = expert_batch
+    ids = dev(case.ids)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits))
+    oq, od = assert_q8_equal(xq, case.x_bits)
+    gu = q2.q2k_mmvq_experts([gate, up], per_gu, case.n_experts, ids, xq, False,
+                             case.inter, case.dim, 1, err_flag=flag)
+    gu_h = gu.cpu().numpy()
+    for bi, kind in enumerate(("gate", "up")):
+        mats = [case.expert_matrix(e, kind) for e in case.ids.tolist()]
+        ref = orc.mmvq_experts(mats, oq, od, x_per_id=False)
+        assert_close(gu_h[bi], ref, kind)
+    g = gu[0].reshape(len(case.ids), case.inter).contiguous()
+    u = gu[1].reshape(len(case.ids), case.inter).contiguous()
+    h, hq = q2.swiglu_q8_1_rows(g, u)
+    h_bits = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref_h = orc.swiglu_bf16_bits(g.cpu().numpy(), u.cpu().numpy())
+    assert bf16_ulp_distance(h_bits, ref_h).max() <= 1, "SwiGLU more than one bf16 ulp off"
+    hq_o, hd_o = assert_q8_equal(hq, h_bits)
+    yd = q2.q2k_mmvq_experts([down], per_d, case.n_experts, ids, hq, True, case.dim,
+                             case.inter, 1, err_flag=flag)
+    mats = [case.expert_matrix(e, "down") for e in case.ids.tolist()]
+    ref_d = orc.mmvq_experts(mats, hq_o, hd_o, x_per_id=True)
+    assert_close(yd.cpu().numpy()[0], ref_d, "down")
+    assert int(flag.item()) == 0
+    # experts == per-expert singles, bit for bit
+    for i, e in enumerate(case.ids.tolist()):
+        s = q2.q2k_mmvq(down[e * per_d:(e + 1) * per_d], hq[i * q2.q8_1_rows_bytes(1, 2048):],
+                        case.dim, case.inter, 1).cpu().numpy()
+        assert np.array_equal(s.view(np.uint32), yd.cpu().numpy()[0, i].view(np.uint32))
+
+
+def test_expert_bad_id_flags_and_nans(expert_batch):
+    case, gate, up, down, per_gu, per_d = expert_batch
+    ids = dev(np.array([case.ids[0], 300, -1, case.ids[1]], dtype=np.int32))
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits))
+    y = q2.q2k_mmvq_experts([gate], per_gu, case.n_experts, ids, xq, False, case.inter,
+                            case.dim, 1, err_flag=flag).cpu().numpy()
+    assert int(flag.item()) == 1
+    assert np.all(np.isnan(y[0, 1])) and np.all(np.isnan(y[0, 2]))
+    assert np.all(np.isfinite(y[0, 0])) and np.all(np.isfinite(y[0, 3]))
+
+
+def test_experts_multi_token_shared_and_per_id():
+    rng = syn.rng_for(55)
+    n, k, m, n_exp = 200, 1024, 3, 6
+    mats = [syn.q2k_blocks(rng, n, k // 256) for _ in range(n_exp)]
+    stride = n * (k // 256) * 84 + 4            # padded stride
+    buf = np.zeros(n_exp * stride, dtype=np.uint8)
+    for e in range(n_exp):
+        buf[e * stride:e * stride + mats[e].size] = mats[e].reshape(-1)
+    ids_np = np.array([5, 0, 3], dtype=np.int32)
+    x = syn.bf16_normal(rng, (len(ids_np) * m, k))
+    xq = q2.q8_1_rows(bf16_dev(x))
+    oq, od = assert_q8_equal(xq, x)
+    y = q2.q2k_mmvq_experts([dev(buf)], stride, n_exp, dev(ids_np), xq, True, n, k, m).cpu().numpy()
+    ref = orc.mmvq_experts([mats[i] for i in ids_np], oq, od, x_per_id=True)
+    assert_close(y[0], ref, "per-id experts")
+    ys = q2.q2k_mmvq_experts([dev(buf)], stride, n_exp, dev(ids_np), xq, False, n, k, m).cpu().numpy()
+    refs = orc.mmvq_experts([mats[i] for i in ids_np], oq[:m], od[:m], x_per_id=False)
+    assert_close(ys[0], refs, "shared-input experts")
+
+
+# --------------------------------------------------------------- engram -----
+
+@pytest.fixture(scope="module")
+def engram():
+    return syn.engram_step_case()
+
+
+def test_dequant_rows_bit_exact(engram):
+    table = dev(engram.table.reshape(-1))
+    ids = dev(engram.ids)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = q2.q2k_dequant_rows(table, engram.table.shape[0], ids, len(engram.ids), err_flag=flag)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, orc.dequant_rows_bf16_bits(engram.table, engram.ids))
+    assert int(flag.item()) == 0
+    many = dev(syn.rng_for(3).integers(0, engram.table.shape[0], size=4099, dtype=np.int64))
+    out = q2.q2k_dequant_rows(table, engram.table.shape[0], many, 4099)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, orc.dequant_rows_bf16_bits(engram.table, many.cpu().numpy()))
+    out = q2.q2k_dequant_rows(table, engram.table.shape[0], None, 13)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, orc.dequant_rows_bf16_bits(engram.table[:13], None))
+
+
+def test_dequant_rows_hand_blocks_and_bad_ids():
+    table = np.zeros((3, 84), dtype=np.uint8)
+    table[0, 0:16] = [((15 - s) << 4) | s for s in range(16)]
+    table[0, 16:80] = 0xE4
+    table[0, 80:84] = [0x00, 0x3C, 0x00, 0x38]
+    table[1, 0:16] = 0x1F                           # sc = 15, m = 1
+    table[1, 16:80] = 0xFF
+    table[1, 80:84] = [0x00, 0x3C, 0x00, 0xB0]     # 45 - (-0.125) = 45.125: a tie
+    table[2, 80:84] = [0x00, 0x00, 0x00, 0x00]
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids = dev(np.array([0, 1, 2, 3, -7], dtype=np.int64))
+    out = q2.q2k_dequant_rows(dev(table.reshape(-1)), 3, ids, 5, err_flag=flag)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got[:3], orc.dequant_rows_bf16_bits(table, [0, 1, 2]))
+    assert got[1, 0] == 0x4234 and np.all(got[2] == 0)
+    assert np.all(got[3:] == 0x7FC0) and int(flag.item()) == 1
+
+
+@pytest.mark.parametrize("t,hc,dim", [(1, 4, 4096), (2, 1, 4096), (3, 3, 1000), (1, 2, 7), (4, 4, 256)])
+def test_engram_gate(t, hc, dim):
+    h, kv, qk, eps = syn.gate_case(11, t, hc, dim)
+    hd = dev(h)
+    q2.engram_gate(hd, dev(kv), dev(qk), eps)
+    assert_close(hd.cpu().numpy(), orc.engram_gate(h, kv, qk, eps), f"gate {t},{hc},{dim}")
+
+
+def test_engram_gate_closed_forms():
+    dim = 64
+    h = np.zeros((1, 2, dim), np.float32)
+    h[0, :, :32] = 1.0
+    kv = np.zeros((1, 3 * dim), np.float32)
+    kv[0, 32:64] = 2.0
+    kv[0, 96:128] = -3.0
+    kv[0, 128:] = np.arange(dim, dtype=np.float32)
+    qk = np.ones((2, dim), np.float32)
+    hd = dev(h)
+    q2.engram_gate(hd, dev(kv), dev(qk), 1e-6)
+    expect = h + 0.5 * np.arange(dim, dtype=np.float32)      # s = 0 -> g = 1/2
+    assert np.array_equal(hd.cpu().numpy(), expect)
+    kv[0, 128:] = 0.0
+    hd = dev(h)
+    q2.engram_gate(hd, dev(kv), dev(qk), 1e-6)
+    assert np.array_equal(hd.cpu().numpy(), h)                # v = 0: unchanged
+
+
+def test_engram_step(engram):
+    """Row gather [8 x 256] -> [1, 2048] -> q8_1 -> wkv [20480, 2048] -> gate on [1, 4, 4096]."""
+    e = engram
+    table = dev(e.table.reshape(-1))
+    rows = q2.q2k_dequant_rows(table, e.table.shape[0], dev(e.ids), e.cols)
+    rows_bits = rows.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref_rows = orc.dequant_rows_bf16_bits(e.table, e.ids)
+    assert np.array_equal(rows_bits, ref_rows)
+    x = rows.view(1, e.cols * 256)
+    xq = q2.q8_1_rows(x)
+    oq, od = assert_q8_equal(xq, ref_rows.reshape(1, -1))
+    n_out = e.dim * (e.hc + 1)
+    kv = q2.q2k_mmvq(dev(e.wkv.reshape(-1)), xq, n_out, e.cols * 256, 1)
+    ref_kv = orc.mmvq(e.wkv, oq, od)
+    assert_close(kv.cpu().numpy(), ref_kv, "wkv")
+    hd = dev(e.h)
+    q2.engram_gate(hd, kv, dev(e.qk), e.eps)
+    kv_h = kv.cpu().numpy()
+    assert_close(hd.cpu().numpy(), orc.engram_gate(e.h, kv_h, e.qk, e.eps), "gate (stage)")
+    assert_close(hd.cpu().numpy(), orc.engram_gate(e.h, ref_kv, e.qk, e.eps), "gate (end to end)")
+
+
+# ------------------------------------------------------- full-size verify ---
+
+@pytest.fixture(scope="module")
+def large():
+    case = syn.large_verify_case(m=8)
+    return case, dev(case.w.reshape(-1))
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_large_verify_sampled(large, m):
+    """[32768, 7168] Q2_K against m bf16 tokens with 5% +-20 outliers, in the
+    launch configuration the benchmark times; sampled rows vs the oracle."""
+    case, w = large
+    x = case.x_bits[:m]
+    xq = q2.q8_1_rows(bf16_dev(x))
+    oq, od = assert_q8_equal(xq, x)
+    y = q2.q2k_mmvq(w, xq, case.n, case.k, m).cpu().numpy()
+    rows = np.unique(np.concatenate([
+        np.arange(0, 64), np.arange(case.n - 64, case.n),
+        syn.rng_for(4, m).choice(case.n, 384, replace=False)]))
+    ref = orc.mmvq(case.w[rows], oq, od)
+    assert_close(y[:, rows], ref, f"large m={m}")
+    assert np.all(np.isfinite(y))
+
+
+def test_swiglu_extreme_gates():
+    """Gate values where exp(-g) overflows f32 (g < -88.7) and the far tails."""
+    k = 256
+    g = np.linspace(-120.0, 120.0, 2 * k, dtype=np.float32).reshape(2, k)
+    g[0, :8] = [-1e30, -200.0, -103.9, -88.8, -88.7, -87.0, 0.0, -0.0]
+    u = np.full((2, k), 1.5, np.float32)
+    u[1] = -3.25
+    h, hq = q2.swiglu_q8_1_rows(dev(g), dev(u))
+    h_bits = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert bf16_ulp_distance(h_bits, orc.swiglu_bf16_bits(g, u)).max() <= 1
+    assert_q8_equal(hq, h_bits)
