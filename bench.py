@@ -218,7 +218,7 @@ def run(args):
         "roofline": {"bound": "hbm", "achieved": round(r1["achieved"], 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(r1["achieved"] / PEAK_GBS, 4),
                      "traffic": measured_traffic(1),
-                     "kernel": "q2k_mmvq (mmvq_narrow_kernel<1>)",
+                     "kernel": "q2k_mmvq (mmvq_m1_kernel)",
                      "bytes_per_launch": mmvq_bytes(1),
                      "us_per_launch": round(r1["launch_s"] * 1e6, 3)},
         "m8": {"value": round(r8["step_gbs"], 1), "unit": "GB/s",

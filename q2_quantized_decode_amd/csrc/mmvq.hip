@@ -51,6 +51,7 @@ struct MmvqParams {
   int32_t waves_per_job;             // expert mode
   int32_t total_waves;
   int32_t chunk;                     // row steps per wave
+  int32_t interleave;                // 1: a job's waves take its steps round-robin
   int32_t k;
   int32_t gs_log2;                   // lanes per row group = 1 << gs_log2
 };
@@ -63,6 +64,7 @@ struct WaveJob {
   int n;
   int it;              // first row step
   int it_end;          // end of the run
+  int stride;          // distance between the wave's consecutive steps
   bool bad;            // expert id out of range
 };
 
@@ -91,8 +93,22 @@ __device__ __forceinline__ WaveJob resolve_wave(const MmvqParams& p, int wave, i
     J.xq = p.x_per_id ? p.xq + (int64_t)i * M * (int64_t)q8_row_bytes(p.k) : p.xq;
   }
   const int iters = (J.n + P - 1) / P;
-  J.it = lw * p.chunk;
-  J.it_end = min(J.it + p.chunk, iters);
+  if (p.interleave) {
+    int waves_of_job;
+    if (p.ids == nullptr) {
+      const int j = (wave >= p.wave_end[0]) + (wave >= p.wave_end[1]) + (wave >= p.wave_end[2]);
+      waves_of_job = p.wave_end[j] - (j > 0 ? p.wave_end[j - 1] : 0);
+    } else {
+      waves_of_job = p.waves_per_job;
+    }
+    J.it = lw;
+    J.it_end = iters;
+    J.stride = waves_of_job;
+  } else {
+    J.it = lw * p.chunk;
+    J.it_end = min(J.it + p.chunk, iters);
+    J.stride = 1;
+  }
   return J;
 }
 
@@ -150,17 +166,31 @@ __device__ __forceinline__ AHalf zero_ahalf() {
   return a;
 }
 
-// Exact integer sums of the lane's four q8 blocks c = 8b + 4h + j:
-// I[j] = sum sc*q*xq, Mv[j] = sum m*xq.
-__device__ __forceinline__ void half_block_dots(const WHalf& w, const AHalf& a, int I[4],
-                                                int Mv[4]) {
+// sdot4 that starts a chain: v_dot4_i32_i8 with an inline zero accumulator
+// (the accumulating v_dot4c form would need a v_mov to clear it first).
+__device__ __forceinline__ int sdot4_first(uint32_t a, uint32_t b) {
+  int r;
+  asm volatile("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Integer sums of the lane's four q8 blocks c = 8b + 4h + j:
+// I4[j] = sum sc*q*xq and Mv[j] = sum m*xq, except that I4[1] and I4[3]
+// come out multiplied by 4 (planes 1 and 3 are masked in place, q*4 < 128,
+// instead of being shifted down; every term is then a multiple of 4).
+__device__ __forceinline__ void half_block_dots_x4(const WHalf& w, const AHalf& a, int I4[4],
+                                                   int Mv[4]) {
   const uint32_t q[8] = {w.q0[0], w.q0[1], w.q0[2], w.q0[3], w.q1[0], w.q1[1], w.q1[2], w.q1[3]};
   int D[4][2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    int d0 = 0, d1 = 0, d2 = 0, d3 = 0;
+    const uint32_t v0 = q[4 * s], v04 = v0 >> 4;
+    int d0 = sdot4_first(v0 & 0x03030303u, a.x[0 + s][0]);
+    int d1 = sdot4_first(v0 & 0x0C0C0C0Cu, a.x[2 + s][0]);
+    int d2 = sdot4_first(v04 & 0x03030303u, a.x[4 + s][0]);
+    int d3 = sdot4_first(v04 & 0x0C0C0C0Cu, a.x[6 + s][0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 1; i < 4; ++i) {
       const uint32_t v = q[4 * s + i];
       const uint32_t v4 = v >> 4;
       d0 = sdot4(v & 0x03030303u, a.x[0 + s][i], d0);
@@ -169,23 +199,34 @@ __device__ __forceinline__ void half_block_dots(const WHalf& w, const AHalf& a, 
       d3 = sdot4(v4 & 0x0C0C0C0Cu, a.x[6 + s][i], d3);
     }
     D[0][s] = d0;
-    D[1][s] = d1 >> 2;   // exact: every term is a multiple of 4
+    D[1][s] = d1;
     D[2][s] = d2;
-    D[3][s] = d3 >> 2;
+    D[3][s] = d3;
   }
+  // Scale bytes scales[8h + 2j + s]: low nibble sc, high nibble m.
+  const uint32_t scn[2] = {w.sc[0] & 0x0F0F0F0Fu, w.sc[1] & 0x0F0F0F0Fu};
+  const uint32_t mn[2] = {(w.sc[0] >> 4) & 0x0F0F0F0Fu, (w.sc[1] >> 4) & 0x0F0F0F0Fu};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t scw = (j < 2) ? w.sc[0] : w.sc[1];
     const int sh = (j & 1) * 16;
-    const uint32_t b0 = (scw >> sh) & 0xffu;
-    const uint32_t b1 = (scw >> (sh + 8)) & 0xffu;
-    // Every factor fits in 24 signed bits (|D| <= 16*3*127, |S| <= 16*127),
+    const int sc0 = (int)((scn[j >> 1] >> sh) & 0xffu), sc1 = (int)((scn[j >> 1] >> (sh + 8)) & 0xffu);
+    const int m0 = (int)((mn[j >> 1] >> sh) & 0xffu), m1 = (int)((mn[j >> 1] >> (sh + 8)) & 0xffu);
+    // Every factor fits in 24 signed bits (|D| <= 16*12*127, |S| <= 16*127),
     // so the full-rate 24-bit multiplies are exact.
-    I[j] = __mul24((int)(b0 & 15u), D[j][0]) + __mul24((int)(b1 & 15u), D[j][1]);
+    I4[j] = __mul24(sc0, D[j][0]) + __mul24(sc1, D[j][1]);
     const int s0 = (int)(int16_t)(a.s[j] & 0xffffu);
     const int s1 = (int)(int16_t)(a.s[j] >> 16);
-    Mv[j] = __mul24((int)(b0 >> 4), s0) + __mul24((int)(b1 >> 4), s1);
+    Mv[j] = __mul24(m0, s0) + __mul24(m1, s1);
   }
+}
+
+// Exact integer sums I[j] = sum sc*q*xq, Mv[j] = sum m*xq of the lane's four
+// q8 blocks (the x4 of planes 1 and 3 shifted out: exact).
+__device__ __forceinline__ void half_block_dots(const WHalf& w, const AHalf& a, int I[4],
+                                                int Mv[4]) {
+  half_block_dots_x4(w, a, I, Mv);
+  I[1] >>= 2;
+  I[3] >>= 2;
 }
 
 // The lane's contribution d * sum_j d8_j I_j - dmin * sum_j d8_j M_j, in
@@ -222,13 +263,300 @@ __device__ __forceinline__ void store_dots(int32_t* dots, const WHalf& w, const 
   *reinterpret_cast<u32x4*>(o + 4) = u32x4{(uint32_t)I[2], (uint32_t)Mv[2], (uint32_t)I[3], (uint32_t)Mv[3]};
 }
 
+// ---------------------------------------------------------------------------
+// Cross-lane helpers on fp64 values (moved as two dwords).
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// DPP controls: the partner of lane l differs from l in bit OFF (and, for
+// the mirrors, in the bits below it): 8 -> row_mirror (l ^ 15 within 16),
+// 4 -> row_half_mirror (l ^ 7 within 8), 2 / 1 -> quad_perm.
+template <int OFF> struct DppPartner;
+template <> struct DppPartner<8> { static constexpr int ctrl = 0x140; };
+template <> struct DppPartner<4> { static constexpr int ctrl = 0x141; };
+template <> struct DppPartner<2> { static constexpr int ctrl = 0x4E; };   // [2,3,0,1]
+template <> struct DppPartner<1> { static constexpr int ctrl = 0xB1; };   // [1,0,3,2]
+
+__device__ __forceinline__ uint64_t bits64(double v) { return __builtin_bit_cast(uint64_t, v); }
+__device__ __forceinline__ double from_bits(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// One halving level of a transposed reduction: lanes whose bit OFF is 0 end
+// with X summed over the lane pair, the others with Y summed over the pair.
+template <int OFF>
+__device__ __forceinline__ double halve(double x, double y, int lane) {
+  if constexpr (OFF == 32) {
+    // swaps lanes 32..63 of the first operand with lanes 0..31 of the second
+    const uint64_t bx = bits64(x), by = bits64(y);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)bx, (uint32_t)by, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(bx >> 32), (uint32_t)(by >> 32),
+                                                     false, false);
+    return from_bits(lo[0], hi[0]) + from_bits(lo[1], hi[1]);
+  } else if constexpr (OFF == 16) {
+    // swaps the odd 16-lane rows of the first operand with the even rows of the second
+    const uint64_t bx = bits64(x), by = bits64(y);
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)bx, (uint32_t)by, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(bx >> 32), (uint32_t)(by >> 32),
+                                                     false, false);
+    return from_bits(lo[0], hi[0]) + from_bits(lo[1], hi[1]);
+  } else {
+    const bool up = (lane & OFF) != 0;
+    const double send = up ? x : y;
+    const double keep = up ? y : x;
+    return keep + dpp_f64<DppPartner<OFF>::ctrl>(send);
+  }
+}
+
+// Sum eight per-lane values a[0..7] over groups of GS = 1 << GSL lanes
+// (GS >= 8) at once: three halving levels leave lane l holding the group
+// total of slot (l & (GS-1)) >> (GSL-3), the remaining levels finish the sum.
+template <int GSL>
+__device__ __forceinline__ double reduce8(const double a[8], int lane) {
+  constexpr int GS = 1 << GSL;
+  double b4[4], b2[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b4[i] = halve<GS / 2>(a[i], a[i + 4], lane);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) b2[i] = halve<GS / 4>(b4[i], b4[i + 2], lane);
+  double v = halve<GS / 8>(b2[0], b2[1], lane);
+  if constexpr (GS / 16 >= 1) v += dpp_f64<DppPartner<(GS >= 64 ? 4 : GS / 16)>::ctrl>(v);
+  if constexpr (GS / 32 >= 1) v += dpp_f64<DppPartner<(GS >= 64 ? 2 : GS / 32)>::ctrl>(v);
+  if constexpr (GS / 64 >= 1) v += dpp_f64<DppPartner<1>::ctrl>(v);
+  return v;
+}
+
+// d*sum_j d8_j I_j - dmin*sum_j d8_j M_j for one lane, fp64 (exact terms).
+// dq holds d8_j with the x4 of planes 1 and 3 folded in (d8/4 is exact).
+__device__ __forceinline__ double half_block_value_m1(const WHalf& w, const AHalf& a,
+                                                      const double dq[4], const double dm[4]) {
+  int I4[4], Mv[4];
+  half_block_dots_x4(w, a, I4, Mv);
+  double fI = 0.0, fM = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    fI = fma(dq[j], (double)I4[j], fI);
+    fM = fma(dm[j], (double)Mv[j], fM);
+  }
+  const double d = (double)fp16_bits_to_f32(w.dd & 0xffffu);
+  const double dmin = (double)fp16_bits_to_f32(w.dd >> 16);
+  return d * fI - dmin * fM;
+}
+
+// Weight fields of one lane at fixed 32-bit byte offsets from a uniform
+// (SGPR) base, so the loads use the scalar-base + vector-offset form.
+struct LaneOffsets {
+  uint32_t q;    // qs[32h]
+  uint32_t sc;   // scales[8h]
+  uint32_t dd;   // d, dmin
+};
+
+// The empty asm makes each offset an opaque 32-bit VGPR value, so the
+// compiler keeps "uniform base + 32-bit offset" instead of reassociating the
+// sum into per-step 64-bit vector address arithmetic.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ LaneOffsets lane_offsets(uint32_t blk_off, int h) {
+  return LaneOffsets{opaque(blk_off + 16u + 32u * (uint32_t)h), opaque(blk_off + 8u * (uint32_t)h),
+                     opaque(blk_off + 80u)};
+}
+
+__device__ __forceinline__ WHalf load_whalf_at(const uint8_t* base, const LaneOffsets& o) {
+  WHalf r;
+  r.q0 = gload<u32x4_a4>(base + o.q);
+  r.q1 = gload<u32x4_a4>(base + o.q + 16u);
+  r.sc = gload<u32x2_a4>(base + o.sc);
+  r.dd = gload<uint32_t>(base + o.dd);
+  return r;
+}
+
+// Per-wave LDS staging area for one row step (at most 64 half blocks, i.e.
+// 2688 bytes, rounded up to three 1 KB wave-wide 16-byte loads).
+constexpr int kStageBytes = 3072;
+
+// One token, rows of at most 64 half blocks and at least 8 lanes per row
+// (k from 1024 to 8192). Each wave owns a run of CH row steps (CH a multiple
+// of 8, known at compile time), either consecutive or interleaved with the
+// other runs of the matrix (stride S) so that the waves sweep the matrix
+// together. Per step:
+//  * the step's bytes (P whole rows, contiguous) arrive by three wave-wide
+//    coalesced 16-byte loads into a ring of R register sets;
+//  * the wave writes them to its own LDS area and each lane reads back its
+//    half block's fields (32 quant bytes, 8 scale bytes, d/dmin);
+//  * activations stay in VGPRs for the whole run; sums of eight consecutive
+//    steps are reduced together.
+// A full run is straight-line code (exact hardware wait counters); staging
+// of step s + 1 overlaps the arithmetic of step s. Runs cut short by the end
+// of the matrix take a guarded path with direct per-lane loads.
+template <int GSL, int R, int CH, bool STAGED>
+__global__ __launch_bounds__(256) void mmvq_m1_kernel(const MmvqParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[STAGED ? 4 : 1][STAGED ? kStageBytes : 16];
+  constexpr int GS = 1 << GSL;
+  constexpr int P = 64 >> GSL;
+  constexpr int V = 8;
+  static_assert(CH % V == 0 && R >= 2, "run and ring shapes");
+  const int lane = threadIdx.x & 63;
+  const int wiw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int g8 = gridDim.x >> 3;
+  const int wg = blockIdx.x;
+  const int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 + wiw;
+  if (wave >= p.total_waves) return;
+  const WaveJob J = resolve_wave<1>(p, wave, P);
+  if (J.it >= J.it_end) return;
+
+  const int k = p.k;
+  const int nb = k >> 8;
+  const int hb = lane & (GS - 1);
+  const int prow = lane >> GSL;
+  const bool hb_ok = hb < 2 * nb;
+  const int hbc = hb_ok ? hb : 0;     // idle lanes read a valid half block
+  const int b = hbc >> 1;
+  const int h = hbc & 1;
+  const uint32_t rowbytes = (uint32_t)nb * kBlockBytes;
+  const uint32_t step_bytes = (uint32_t)P * rowbytes;
+  const int slot = (lane & (GS - 1)) >> (GSL - 3);
+  const bool writer = (lane & ((GS >> 3) - 1)) == 0;
+
+  // The run's steps are J.it + st * S, st = 0..CH-1.
+  const int S = J.stride;
+  const size_t run_stride = (size_t)S * step_bytes;
+  const uint8_t* wrun = J.w + (size_t)J.it * step_bytes;
+  const int last_step = J.it + (CH - 1) * S;
+  const bool full = last_step < J.it_end && (last_step + 1) * P <= J.n;
+
+  // Activations first: the first step waits for them and ring slot 0 only.
+  const AHalf act = load_ahalf(J.xq, k, b, h);
+  double dq[4], dm[4];
+
+  if (full && !STAGED) {
+    // Direct path: each lane loads its own half block's fields.
+    const LaneOffsets off = lane_offsets((uint32_t)prow * rowbytes + (uint32_t)b * kBlockBytes, h);
+    WHalf ws[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ws[r] = load_whalf_at(wrun + (size_t)r * run_stride, off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dm[j] = (double)act.d8[j];
+      dq[j] = (j & 1) ? 0.25 * dm[j] : dm[j];
+    }
+#pragma unroll
+    for (int g = 0; g < CH / V; ++g) {
+      double acc[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int st = g * V + v;                      // step within the run
+        const double t = half_block_value_m1(ws[v % R], act, dq, dm);
+        if (st + R < CH) ws[v % R] = load_whalf_at(wrun + (size_t)(st + R) * run_stride, off);
+        acc[v] = hb_ok ? t : 0.0;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const double tot = reduce8<GSL>(acc, lane);
+      if (writer) J.y[(J.it + (g * V + slot) * S) * P + prow] = J.bad ? quiet_nan() : (float)tot;
+    }
+  } else if (full) {
+    // Staged path. Chunk i of a step is bytes [16 (64 i + lane), +16), clamped to end
+    // inside the step (duplicates re-read and re-write identical bytes).
+    const uint32_t c0 = opaque(min(16u * (uint32_t)lane, step_bytes - 16u));
+    const uint32_t c1 = opaque(min(16u * (uint32_t)(64 + lane), step_bytes - 16u));
+    const uint32_t c2 = opaque(min(16u * (uint32_t)(128 + lane), step_bytes - 16u));
+    uint8_t* lds = stage[STAGED ? wiw : 0];
+    const uint32_t fo = (uint32_t)prow * rowbytes + (uint32_t)b * kBlockBytes;
+    u32x4 raw[R][3];
+    auto fetch = [&](int r, int st) {
+      const uint8_t* base = wrun + (size_t)st * run_stride;
+      raw[r][0] = gload<u32x4_a4>(base + c0);
+      raw[r][1] = gload<u32x4_a4>(base + c1);
+      raw[r][2] = gload<u32x4_a4>(base + c2);
+    };
+    auto stage_step = [&](int r) -> WHalf {
+      *reinterpret_cast<u32x4_a4*>(lds + c0) = raw[r][0];
+      *reinterpret_cast<u32x4_a4*>(lds + c1) = raw[r][1];
+      *reinterpret_cast<u32x4_a4*>(lds + c2) = raw[r][2];
+      WHalf w;
+      w.q0 = *reinterpret_cast<const u32x4_a4*>(lds + fo + 16 + 32 * h);
+      w.q1 = *reinterpret_cast<const u32x4_a4*>(lds + fo + 32 + 32 * h);
+      w.sc = *reinterpret_cast<const u32x2_a4*>(lds + fo + 8 * h);
+      w.dd = *reinterpret_cast<const uint32_t*>(lds + fo + 80);
+      return w;
+    };
+#pragma unroll
+    for (int r = 0; r < R; ++r) fetch(r, r);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dm[j] = (double)act.d8[j];
+      dq[j] = (j & 1) ? 0.25 * dm[j] : dm[j];
+    }
+    WHalf wcur = stage_step(0);
+    if (R < CH) fetch(0, R);
+#pragma unroll
+    for (int g = 0; g < CH / V; ++g) {
+      double acc[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int st = g * V + v;                      // step within the run
+        WHalf wnext = wcur;
+        if (st + 1 < CH) {
+          wnext = stage_step((st + 1) % R);
+          if (st + 1 + R < CH) fetch((st + 1) % R, st + 1 + R);
+        }
+        const double t = half_block_value_m1(wcur, act, dq, dm);
+        acc[v] = hb_ok ? t : 0.0;
+        wcur = wnext;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const double tot = reduce8<GSL>(acc, lane);
+      if (writer) J.y[(J.it + (g * V + slot) * S) * P + prow] = J.bad ? quiet_nan() : (float)tot;
+    }
+  } else {
+    // Guarded path: one direct load per step, rows past n read the step's
+    // first row instead.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dm[j] = (double)act.d8[j];
+      dq[j] = (j & 1) ? 0.25 * dm[j] : dm[j];
+    }
+    const LaneOffsets off = lane_offsets((uint32_t)prow * rowbytes + (uint32_t)b * kBlockBytes, h);
+    const LaneOffsets first = lane_offsets((uint32_t)b * kBlockBytes, h);
+    for (int g0 = J.it; g0 < J.it_end; g0 += V * S) {
+      double acc[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int step = g0 + v * S;
+        double val = 0.0;
+        if (step < J.it_end) {
+          const bool in = step * P + prow < J.n;
+          const WHalf w = load_whalf_at(J.w + (size_t)step * step_bytes, in ? off : first);
+          const double t = half_block_value_m1(w, act, dq, dm);
+          val = (hb_ok && in) ? t : 0.0;
+        }
+        acc[v] = val;
+      }
+      const double tot = reduce8<GSL>(acc, lane);
+      const int step = g0 + slot * S;
+      const int row = step * P + prow;
+      if (writer && step < J.it_end && row < J.n) J.y[row] = J.bad ? quiet_nan() : (float)tot;
+    }
+  }
+  if (J.bad && lane == 0 && p.err_flag != nullptr) *p.err_flag = 1;
+}
+
 // Narrow rows (2 * k/256 <= 64 half blocks): one half block per lane.
 template <int M, bool CACHE, int DEPTH, bool DOTS>
 __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
   const int lane = threadIdx.x & 63;
   const int g8 = gridDim.x >> 3;
   const int wg = blockIdx.x;
-  const int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 + (threadIdx.x >> 6);
+  const int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 +
+                   __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (wave >= p.total_waves) return;
 
   const int k = p.k;
@@ -250,20 +578,21 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
   WHalf ws[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
-    const int row = (J.it + d) * P + prow;
-    ws[d] = (J.it + d < J.it_end && hb_ok && row < J.n) ? load_whalf(wlane + row * rowbytes, h)
-                                                        : zero_whalf();
+    const int st = J.it + d * J.stride;
+    const int row = st * P + prow;
+    ws[d] = (st < J.it_end && hb_ok && row < J.n) ? load_whalf(wlane + row * rowbytes, h)
+                                                 : zero_whalf();
   }
   AHalf act;
   if constexpr (CACHE) act = hb_ok ? load_ahalf(J.xq, k, b, h) : zero_ahalf();
 
-  for (int base = J.it; base < J.it_end; base += DEPTH) {
+  for (int base = J.it; base < J.it_end; base += DEPTH * J.stride) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
-      const int cur = base + d;
+      const int cur = base + d * J.stride;
       if (cur < J.it_end) {
         const WHalf w = ws[d];
-        const int nxt = cur + DEPTH;
+        const int nxt = cur + DEPTH * J.stride;
         const int nrow = nxt * P + prow;
         ws[d] = (nxt < J.it_end && hb_ok && nrow < J.n) ? load_whalf(wlane + nrow * rowbytes, h)
                                                         : zero_whalf();
@@ -299,14 +628,15 @@ __global__ __launch_bounds__(256) void mmvq_wide_kernel(const MmvqParams p) {
   const int lane = threadIdx.x & 63;
   const int g8 = gridDim.x >> 3;
   const int wg = blockIdx.x;
-  const int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 + (threadIdx.x >> 6);
+  const int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 +
+                   __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (wave >= p.total_waves) return;
   const int k = p.k;
   const int nb = k >> 8;
   const size_t rowbytes = (size_t)nb * kBlockBytes;
   const size_t rb = q8_row_bytes(k);
   const WaveJob J = resolve_wave<M>(p, wave, 1);
-  for (int row = J.it; row < J.it_end; ++row) {
+  for (int row = J.it; row < J.it_end; row += J.stride) {
     double part[M];
 #pragma unroll
     for (int t = 0; t < M; ++t) part[t] = 0.0;
@@ -339,6 +669,12 @@ namespace {
 struct Tuning {
   int waves_per_cu = 16;
   int depth = 2;
+  bool fast_m1 = true;
+  int interleave = 1;
+  int ring = 4;
+  int run = 0;       // m = 1 run length override (8, 16, 32); 0 = from waves_per_cu
+  bool staged = false;
+  int m1_waves_per_cu = 4;
 };
 
 const Tuning& tuning() {
@@ -349,6 +685,21 @@ const Tuning& tuning() {
       const int v = atoi(s);
       if (v >= 1 && v <= 64) t.waves_per_cu = v;
     }
+    if (const char* s = getenv("Q2K_MMVQ_GENERIC_M1")) t.fast_m1 = atoi(s) == 0;
+    if (const char* s = getenv("Q2K_MMVQ_INTERLEAVE")) t.interleave = atoi(s) != 0;
+    if (const char* s = getenv("Q2K_MMVQ_STAGED")) t.staged = atoi(s) != 0;
+    if (const char* s = getenv("Q2K_MMVQ_M1_WAVES_PER_CU")) {
+      const int v = atoi(s);
+      if (v >= 1 && v <= 64) t.m1_waves_per_cu = v;
+    }
+    if (const char* s = getenv("Q2K_MMVQ_RUN")) {
+      const int v = atoi(s);
+      if (v == 8 || v == 16 || v == 32) t.run = v;
+    }
+    if (const char* s = getenv("Q2K_MMVQ_RING")) {
+      const int v = atoi(s);
+      if (v == 2 || v == 4 || v == 8) t.ring = v;
+    }
     if (const char* s = getenv("Q2K_MMVQ_DEPTH")) {
       const int v = atoi(s);
       if (v == 1 || v == 2 || v == 4) t.depth = v;
@@ -356,6 +707,8 @@ const Tuning& tuning() {
   });
   return t;
 }
+
+bool fast_m1() { return tuning().fast_m1; }
 
 int cu_count() {
   static int counts[64];
@@ -372,6 +725,38 @@ int cu_count() {
 
 template <int M>
 void dispatch_narrow(const MmvqParams& p, dim3 grid, bool dots, int depth, hipStream_t s) {
+  if (M == 1 && !dots && p.gs_log2 >= 3 && fast_m1()) {
+    const int ring = tuning().ring;
+    const int ch = p.chunk;
+    const bool staged = tuning().staged;
+#define Q2K_M1(G, R, C)                                                                   \
+  do {                                                                                    \
+    if (staged) hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, true>), grid, dim3(256), 0, s, p); \
+    else hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, false>), grid, dim3(256), 0, s, p);       \
+  } while (0)
+#define Q2K_M1_CH(G, R)                          \
+  do {                                           \
+    if (ch == 8) Q2K_M1(G, R, 8);                \
+    else if (ch == 16) Q2K_M1(G, R, 16);         \
+    else Q2K_M1(G, R, 32);                       \
+  } while (0)
+#define Q2K_M1_RING(G)                           \
+  do {                                           \
+    if (ring == 2) Q2K_M1_CH(G, 2);              \
+    else if (ring == 8) Q2K_M1_CH(G, 8);         \
+    else Q2K_M1_CH(G, 4);                        \
+  } while (0)
+    switch (p.gs_log2) {
+      case 3: Q2K_M1_RING(3); return;
+      case 4: Q2K_M1_RING(4); return;
+      case 5: Q2K_M1_RING(5); return;
+      default: Q2K_M1_RING(6); return;
+    }
+#undef Q2K_M1_RING
+#undef Q2K_M1_CH
+#undef Q2K_M1_RING
+#undef Q2K_M1
+  }
   if (dots) {
     hipLaunchKernelGGL((mmvq_narrow_kernel<M, false, 1, true>), grid, dim3(256), 0, s, p);
   } else if (M == 1) {
@@ -442,8 +827,15 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   }
   if (total_iters == 0) return hipSuccess;
   const Tuning& tu = tuning();
-  const int64_t target_waves = (int64_t)cu_count() * tu.waves_per_cu;
-  const int64_t chunk = (total_iters + target_waves - 1) / target_waves;
+  const bool m1_path = a.m == 1 && a.dots == nullptr && !wide && gs_log2 >= 3 && tu.fast_m1;
+  const int64_t target_waves =
+      (int64_t)cu_count() * (m1_path ? tu.m1_waves_per_cu : tu.waves_per_cu);
+  int64_t chunk = (total_iters + target_waves - 1) / target_waves;
+  if (m1_path) {
+    // runs of 8, 16 or 32 steps (compile-time run lengths of the m = 1 kernel)
+    chunk = chunk <= 8 ? 8 : chunk <= 16 ? 16 : 32;
+    if (tu.run > 0) chunk = tu.run;
+  }
   p.chunk = (int)chunk;
   int64_t total_waves = 0;
   if (a.ids == nullptr) {
@@ -456,6 +848,7 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
     total_waves = (int64_t)p.waves_per_job * n_jobs;
   }
   p.total_waves = (int)total_waves;
+  p.interleave = tu.interleave;
   int64_t groups = (total_waves + 3) / 4;
   groups = (groups + 7) / 8 * 8;
   const dim3 grid((unsigned)groups);
