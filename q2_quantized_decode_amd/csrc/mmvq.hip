@@ -674,6 +674,7 @@ struct Tuning {
   int ring = 4;
   int run = 0;       // m = 1 run length override (8, 16, 32); 0 = from waves_per_cu
   bool staged = false;
+  bool mfma = true;
   int m1_waves_per_cu = 4;
 };
 
@@ -688,6 +689,7 @@ const Tuning& tuning() {
     if (const char* s = getenv("Q2K_MMVQ_GENERIC_M1")) t.fast_m1 = atoi(s) == 0;
     if (const char* s = getenv("Q2K_MMVQ_INTERLEAVE")) t.interleave = atoi(s) != 0;
     if (const char* s = getenv("Q2K_MMVQ_STAGED")) t.staged = atoi(s) != 0;
+    if (const char* s = getenv("Q2K_MMVQ_NO_MFMA")) t.mfma = atoi(s) == 0;
     if (const char* s = getenv("Q2K_MMVQ_M1_WAVES_PER_CU")) {
       const int v = atoi(s);
       if (v >= 1 && v <= 64) t.m1_waves_per_cu = v;
@@ -782,6 +784,7 @@ void dispatch_wide(const MmvqParams& p, dim3 grid, bool dots, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
+  if (tuning().mfma && mfma_preferred(a)) return launch_mmvq_mfma(a, stream);
   MmvqParams p{};
   const int nb = a.k / kBlockWeights;
   const int lanes = 2 * nb;

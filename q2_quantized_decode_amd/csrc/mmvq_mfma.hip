@@ -1,0 +1,477 @@
+// Q2_K x q8_1 product for 2..8 tokens on the CDNA4 matrix cores.
+//
+// The GGUF Q2_K super-block and the q8_1 block dot it is multiplied with are
+// those of the llama.cpp k-quant pages (block_q2_K layout; the q2_K x q8_1
+// vector dot). With 8 tokens the packed-dot formulation spends two int8 dot
+// instructions per 4 weights on the vector ALUs; here the integer block sums
+// go through v_mfma_i32_16x16x64_i8 and the min term through
+// v_mfma_f64_16x16x4f64, so the vector ALUs only unpack the 2-bit weights and
+// scale the per-block integer results.
+//
+// * Tile: one wave computes 16 weight rows x 8 token slots over a range of
+//   super-blocks, one 256-weight super-block b at a time. Weights are the B
+//   operand: lane (g = lane/16, j = lane%16) loads only its own row r0 + j
+//   (16 bytes of qs, 8 scale bytes, d/dmin), 28 bytes per super-block.
+// * I term (exact int32): plane p = 0..3 of a super-block is one MFMA with
+//   K = 64 weights; K-group g holds the 16 weights 128(g>>1) + 32p + 16(g&1)
+//   + 0..15, i.e. qs bytes 16g..16g+15, bits 2p..2p+1, all in sub-block
+//   s = 8(g>>1) + 2p + (g&1), so B = sc_s * q (<= 45, a v_perm_b32 lookup of
+//   q in {0, sc, 2sc, 3sc}). The A operand (activations) is block diagonal:
+//   A-row a = token (a&7), half (a>>3) carries that token's quants of q8
+//   block 4(a>>3) + p in the two K-groups of that half and zeros elsewhere,
+//   so the output (A-row, weight row) is exactly I = sum sc*q*xq of one
+//   (token, q8 block, row). Each I is scaled by its d8 in fp64 and each
+//   super-block's sum by the row's d.
+// * M term: sum_s dmin*m_s * (d8*S)_s, four fp64 MFMAs per super-block
+//   (K = 4 sub-blocks each: MFMA i, k-index g is sub-block 8(g>>1) + 2i +
+//   (g&1), the scale byte a lane already holds), B = dmin*m (exact), A =
+//   d8*S of the activations (exact), accumulated in the MFMA accumulators.
+//   Its A-rows are arranged so that its output lands on the same lane and
+//   register as the I output of the same token.
+// * Activations of the workgroup's matrix (8 token slots of quants, d8 and
+//   d8*S in fp64, plus an all-zero slot) are staged once in LDS; the waves of
+//   a workgroup take eight consecutive tiles of one matrix.
+//
+// A workgroup is sixteen waves: two per tile, each taking half of the row,
+// their sums combined through LDS in a fixed order. Four waves per SIMD hide
+// the dependency chains of one tile better than whole-row waves with deeper
+// software pipelining did (measured).
+#include <stdlib.h>
+
+#include "q2k_device.h"
+#include "q2k_launch.h"
+
+namespace q2k {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+constexpr int kSlots = 8;              // token slots of a tile (m <= 8; unused slots are zero)
+constexpr int kTabSlots = kSlots + 1;  // plus one all-zero slot
+constexpr int kTilesPerWg = 8;
+constexpr uint32_t kMfmaMaxLds = 160 * 1024;
+constexpr int kThreads = 2 * kTilesPerWg * kWave;   // two waves per tile
+// The second-half waves hand 4 fp64 partial sums per lane of their tile's
+// lanes g < 2 to the first-half waves.
+constexpr uint32_t kXchgBytes = kTilesPerWg * 32 * 4 * 8;
+
+struct MfmaParams {
+  const uint8_t* w[kMaxPlainJobs];   // plain: job matrices; expert mode: the bases
+  float* y[kMaxPlainJobs];
+  int32_t n[kMaxPlainJobs];
+  int32_t wg_end[kMaxPlainJobs];     // plain mode: exclusive prefix of workgroups per job
+  const uint8_t* xq;
+  const int32_t* ids;                // expert mode when non-null
+  int32_t n_ids;
+  int32_t n_experts;
+  int32_t x_per_id;
+  int64_t expert_stride;
+  int32_t* err_flag;
+  int32_t wgs_per_job;               // expert mode
+  int32_t total_wgs;
+  int32_t m;
+};
+
+// LDS layout (bytes) for row length k:
+//   quants  [kTabSlots][k + 16]   slot stride padded by 16 bytes so the eight
+//                                 token slots fall on different banks
+//   d8      [k/32][kSlots] fp64   block-major: a lane's four tokens are adjacent
+//   d8*S    [k/16][kTabSlots] fp64
+__host__ __device__ constexpr uint32_t q_stride(int k) { return (uint32_t)k + 16u; }
+__host__ __device__ constexpr uint32_t lds_d8_off(int k) { return kTabSlots * q_stride(k); }
+__host__ __device__ constexpr uint32_t lds_at_off(int k) {
+  return lds_d8_off(k) + (uint32_t)(k / 32) * kSlots * 8u;
+}
+__host__ __device__ constexpr uint32_t lds_bytes(int k) {
+  return lds_at_off(k) + (uint32_t)(k / 16) * kTabSlots * 8u;
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_load(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const T*>(base + off);
+}
+
+__device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// sc * 0x030201 as one full-rate 24-bit multiply. Written as asm because the
+// compiler otherwise merges the following shift into a 32-bit constant and
+// emits the quarter-rate v_mul_lo_u32.
+__device__ __forceinline__ uint32_t mul_u24_030201(uint32_t sc) {
+  uint32_t r;
+  asm("v_mul_u32_u24_e32 %0, 0x30201, %1" : "=v"(r) : "v"(sc));
+  return r;
+}
+
+// Weight fields of one lane for one super-block.
+struct Blk {
+  u32x4 qs;     // qs[16g .. 16g + 15]
+  u32x2 sc;     // scales[8(g>>1) .. 8(g>>1) + 7]
+  uint32_t dd;  // d (low half), dmin (high half)
+};
+
+struct BlkOffsets {
+  uint32_t q, s, d;
+};
+
+__device__ __forceinline__ Blk load_blk(const uint8_t* base, const BlkOffsets& o) {
+  Blk x;
+  x.qs = gload<u32x4_a4>(base + o.q);
+  x.sc = gload<u32x2_a4>(base + o.s);
+  x.dd = gload<uint32_t>(base + o.d);
+  return x;
+}
+
+// The matrix, output and activations of one workgroup.
+struct Job {
+  const uint8_t* W;
+  float* Y;
+  const uint8_t* X;
+  int n;
+  int lwg;   // workgroup index within the job
+  bool bad;  // expert id out of range: outputs NaN, error flag set
+};
+
+__device__ __forceinline__ Job resolve_job(const MfmaParams& p, int wgi, size_t rb) {
+  Job J;
+  J.bad = false;
+  if (p.ids == nullptr) {
+    const int j = (wgi >= p.wg_end[0]) + (wgi >= p.wg_end[1]) + (wgi >= p.wg_end[2]);
+    J.lwg = wgi - (j > 0 ? p.wg_end[j - 1] : 0);
+    J.W = p.w[j];
+    J.Y = p.y[j];
+    J.n = p.n[j];
+    J.X = p.xq;
+  } else {
+    const int j = wgi / p.wgs_per_job;
+    J.lwg = wgi - j * p.wgs_per_job;
+    const int base = j / p.n_ids;
+    const int i = j - base * p.n_ids;
+    const int id = p.ids[i];
+    J.bad = id < 0 || id >= p.n_experts;
+    J.W = p.w[base] + (int64_t)(J.bad ? 0 : id) * p.expert_stride;
+    J.n = p.n[0];
+    J.Y = p.y[0] + (int64_t)j * p.m * J.n;
+    J.X = p.x_per_id ? p.xq + (int64_t)i * p.m * (int64_t)rb : p.xq;
+  }
+  return J;
+}
+
+// Stage the activations of m tokens (k wide) in LDS. Every load is issued
+// before the first LDS store, so the staging costs one memory latency.
+template <int k, int THREADS>
+__device__ __forceinline__ void stage_activations(uint8_t* lds, const uint8_t* X, int m) {
+  static_assert(kSlots * (k / 128) <= THREADS, "one scale group per thread");
+  const size_t rb = q8_row_bytes(k);
+  const int tid = threadIdx.x;
+  constexpr int QC = k / 16;  // 16-byte quant chunks per token
+  constexpr int QIT = (kSlots * QC + THREADS - 1) / THREADS;
+  u32x4 qv[QIT];
+#pragma unroll
+  for (int it = 0; it < QIT; ++it) {
+    const int idx = tid + it * THREADS;
+    const int t = idx / QC, e = idx - (idx / QC) * QC;
+    qv[it] = u32x4{0, 0, 0, 0};
+    if (idx < kSlots * QC && t < m) qv[it] = gload<u32x4>(X + (size_t)t * rb + 16 * e);
+  }
+  // Scales and half-block sums: thread (token t2, group c4) takes q8 blocks
+  // 4c4..4c4+3, i.e. sub-blocks 8c4..8c4+7.
+  constexpr int C4 = k / 128;
+  const int t2 = tid / C4, c4 = tid - (tid / C4) * C4;
+  const bool sv_ok = tid < kSlots * C4 && t2 < m;
+  f32x4 d8v = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 sv = u32x4{0, 0, 0, 0};
+  if (sv_ok) {
+    d8v = gload<f32x4>(X + (size_t)t2 * rb + q8_scale_offset(k) + 16 * c4);
+    sv = gload<u32x4>(X + (size_t)t2 * rb + q8_sum_offset(k) + 16 * c4);
+  }
+#pragma unroll
+  for (int it = 0; it < QIT; ++it) {
+    const int idx = tid + it * THREADS;
+    const int t = idx / QC, e = idx - (idx / QC) * QC;
+    if (idx < kSlots * QC) *reinterpret_cast<u32x4*>(lds + t * q_stride(k) + 16 * e) = qv[it];
+  }
+  for (int e = tid; e < QC; e += THREADS)
+    *reinterpret_cast<u32x4*>(lds + kSlots * q_stride(k) + 16 * e) = u32x4{0, 0, 0, 0};
+  if (tid < kSlots * C4) {
+    double* d8t = reinterpret_cast<double*>(lds + lds_d8_off(k));
+    double* at = reinterpret_cast<double*>(lds + lds_at_off(k));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d8t[(4 * c4 + i) * kSlots + t2] = (double)d8v[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int16_t sum = (int16_t)(sv[j >> 1] >> (16 * (j & 1)));
+      at[(8 * c4 + j) * kTabSlots + t2] = (double)d8v[j >> 1] * (double)sum;
+    }
+  }
+  for (int s2 = tid; s2 < k / 16; s2 += THREADS)
+    reinterpret_cast<double*>(lds + lds_at_off(k))[s2 * kTabSlots + kSlots] = 0.0;
+}
+
+// Workgroup barrier that orders LDS only: weight loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Per-lane constants of a tile.
+struct Lane {
+  int g, j16;
+  uint32_t a_base;    // I-term A operand (activation quants)
+  uint32_t d8_base;   // d8 of the lane's four outputs
+  uint32_t at_base;   // M-term A operand (d8*S)
+  uint32_t sc_shift;  // 8 * (g & 1)
+};
+
+template <int k>
+__device__ __forceinline__ Lane lane_consts() {
+  Lane L;
+  const int lane = threadIdx.x & 63;
+  L.g = lane >> 4;
+  L.j16 = lane & 15;
+  const int g = L.g, j16 = L.j16;
+  // I-term A: A-row j16 = token (j16 & 7), half (j16 >> 3); K-group g is
+  // non-zero only in its own half.
+  const uint32_t a_slot = ((g >> 1) == (j16 >> 3)) ? (uint32_t)(j16 & 7) : (uint32_t)kSlots;
+  L.a_base = opaque_v(a_slot * q_stride(k) + 128u * (g >> 1) + 16u * (g & 1));
+  // d8 of the lane's four outputs: tokens 4(g&1) + 0..3 of q8 block 8b + 4(g>>1) + p.
+  L.d8_base = opaque_v(lds_d8_off(k) + 8u * (kSlots * 4u * (g >> 1) + 4u * (g & 1)));
+  // M-term A: A-row a = j16 carries token 4(a&1) + (a>>2) when (a&3) < 2,
+  // otherwise zeros; k-index g is sub-block 8(g>>1) + 2i + (g&1).
+  const uint32_t m_slot = (j16 & 3) < 2 ? (uint32_t)(4 * (j16 & 1) + (j16 >> 2)) : (uint32_t)kSlots;
+  L.at_base = opaque_v(lds_at_off(k) + 8u * ((8u * (g >> 1) + (g & 1)) * kTabSlots + m_slot));
+  L.sc_shift = 8u * (g & 1);
+  return L;
+}
+
+// B operand of plane pl: sc * q of the lane's 16 weights.
+__device__ __forceinline__ v4i plane_weights(const u32x4& qs, uint32_t sw, int pl) {
+  const uint32_t sc = (sw >> (16 * (pl & 1))) & 15u;
+  const uint32_t table = mul_u24_030201(sc) << 8;  // bytes 0, sc, 2sc, 3sc
+  v4i wq;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) wq[w] = (int)__builtin_amdgcn_perm(0u, table, (qs[w] >> (2 * pl)) & 0x03030303u);
+  return wq;
+}
+
+// Final sums of a tile: lanes g and g ^ 2 hold the two q8 halves of the same
+// tokens; the M term sits on lanes g < 2. Gives the row value of token
+// 4g + i on lanes g < 2.
+__device__ __forceinline__ void tile_sums(const double* yI, const v4d& accM, double* yv) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) yv[i] = yI[i] + __shfl_xor(yI[i], 32) - accM[i];
+}
+
+__device__ __forceinline__ void store_tile(const Job& J, int m, int r0, const Lane& L, const double* yv) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int token = 4 * L.g + i;
+    const int row = r0 + L.j16;
+    if (L.g < 2 && token < m && row < J.n) J.Y[(int64_t)token * J.n + row] = J.bad ? quiet_nan() : (float)yv[i];
+  }
+}
+
+}  // namespace
+
+// Sixteen waves per workgroup: wave w takes tile w & 7 over super-blocks
+// [(w >> 3) NB/2, ((w >> 3) + 1) NB/2). Four waves per SIMD hide the
+// latencies that one tile's dependency chains leave; the second-half sums are
+// added to the first half's through LDS in a fixed order, so the result does
+// not depend on timing.
+template <int NB, int R>
+__global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const MfmaParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int k = NB * kBlockWeights;
+  constexpr int NBH = NB / 2;
+  static_assert(NB % 2 == 0, "row split in two halves");
+  constexpr uint32_t rowbytes = (uint32_t)NB * kBlockBytes;
+  const int g8 = gridDim.x >> 3;
+  const int wgi = (blockIdx.x & 7) * g8 + (blockIdx.x >> 3);   // XCD-major workgroup index
+  if (wgi >= p.total_wgs) return;                              // whole workgroup
+  const int m = p.m;
+  const Job J = resolve_job(p, wgi, q8_row_bytes(k));
+
+  const int wiw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int tw = wiw & (kTilesPerWg - 1);
+  const int kh = wiw >> 3;
+  const int tiles = (J.n + 15) >> 4;
+  const int tile_raw = J.lwg * kTilesPerWg + tw;
+  const bool active = tile_raw < tiles;                        // wave-uniform
+  const int r0 = (active ? tile_raw : tiles - 1) * 16;
+  const Lane L = lane_consts<k>();
+  const uint32_t lrow = (uint32_t)(min(r0 + L.j16, J.n - 1) - r0);
+  const int b0 = kh * NBH;
+  const uint8_t* Wt = J.W + (size_t)r0 * rowbytes + (size_t)b0 * kBlockBytes;
+  const BlkOffsets off{opaque_v(lrow * rowbytes + 16u + 16u * L.g), opaque_v(lrow * rowbytes + 8u * (L.g >> 1)),
+                       opaque_v(lrow * rowbytes + 80u)};
+  Blk ring[R];
+#pragma unroll
+  for (int b = 0; b < R; ++b)
+    if (b < NBH) ring[b] = load_blk(Wt + b * kBlockBytes, off);
+
+  stage_activations<k, kThreads>(lds, J.X, m);
+  lds_barrier();
+
+  double yv[4] = {0.0, 0.0, 0.0, 0.0};
+  if (active) {
+    // Two M accumulators (MFMAs i = 0,2 and 1,3) halve the fp64 MFMA
+    // dependency chain.
+    v4d accM0 = v4d{0.0, 0.0, 0.0, 0.0}, accM1 = v4d{0.0, 0.0, 0.0, 0.0};
+    double yI[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int bb = 0; bb < NBH; ++bb) {
+      const int b = b0 + bb;   // super-block index within the row (LDS operands)
+      const Blk cur = ring[bb % R];
+      if (bb + R < NBH) ring[bb % R] = load_blk(Wt + (bb + R) * kBlockBytes, off);
+
+      const uint32_t sw0 = cur.sc[0] >> L.sc_shift, sw1 = cur.sc[1] >> L.sc_shift;
+      const double dmin = (double)fp16_bits_to_f32(cur.dd >> 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t mb = ((i < 2 ? sw0 : sw1) >> (16 * (i & 1) + 4)) & 15u;
+        const double am = lds_load<double>(lds, L.at_base + 8u * kTabSlots * (16u * b + 2u * i));
+        if (i & 1)
+          accM1 = __builtin_amdgcn_mfma_f64_16x16x4f64(am, dmin * (double)mb, accM1, 0, 0, 0);
+        else
+          accM0 = __builtin_amdgcn_mfma_f64_16x16x4f64(am, dmin * (double)mb, accM0, 0, 0, 0);
+      }
+      double accI[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int pl = 0; pl < 4; ++pl) {
+        const v4i aq = lds_load<v4i>(lds, L.a_base + 256u * b + 32u * pl);
+        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, plane_weights(cur.qs, pl < 2 ? sw0 : sw1, pl),
+                                                            v4i{0, 0, 0, 0}, 0, 0, 0);
+        const v4d d8 = lds_load<v4d>(lds, L.d8_base + 8u * kSlots * (8u * b + pl));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accI[i] = fma(d8[i], (double)c[i], accI[i]);
+      }
+      const double d = (double)fp16_bits_to_f32(cur.dd & 0xffffu);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) yI[i] = fma(d, accI[i], yI[i]);
+      // Pin the running sums here: otherwise every super-block's epilogue is
+      // sunk to the final store, keeping all MFMA results live.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(yI[i]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    tile_sums(yI, accM0 + accM1, yv);
+  }
+
+  // Second half -> LDS -> first half. The exchange area follows the tables.
+  double* xchg = reinterpret_cast<double*>(lds + lds_bytes(k));
+  const int slot = (tw * 32 + (int)(threadIdx.x & 31)) * 4;
+  if (kh == 1 && active && L.g < 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xchg[slot + i] = yv[i];
+  }
+  lds_barrier();
+  if (kh == 0 && active) {
+    if (L.g < 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) yv[i] += xchg[slot + i];
+    }
+    store_tile(J, m, r0, L, yv);
+  }
+  if (J.bad && threadIdx.x == 0 && p.err_flag != nullptr) *p.err_flag = 1;
+}
+
+namespace {
+
+constexpr int kRing = 2;
+
+int nb_slot(int nb) {
+  switch (nb) {
+    case 4: return 0;
+    case 8: return 1;
+    case 16: return 2;
+    case 28: return 3;
+    default: return -1;
+  }
+}
+
+template <int NB>
+hipError_t launch_nb(const MfmaParams& p, dim3 gd, size_t shm, hipStream_t stream) {
+  // More than 64 KB of dynamic LDS must be allowed explicitly, once per
+  // device and kernel.
+  static bool set_for[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!set_for[dev]) {
+    const hipError_t e = hipFuncSetAttribute((const void*)mmvq_mfma_kernel<NB, kRing>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaMaxLds);
+    if (e != hipSuccess) return e;
+    set_for[dev] = true;
+  }
+  hipLaunchKernelGGL((mmvq_mfma_kernel<NB, kRing>), gd, dim3(kThreads), shm, stream, p);
+  return hipGetLastError();
+}
+
+int64_t workgroups(const MmvqLaunch& a) {
+  const int tile_rows = 16 * kTilesPerWg;
+  if (a.ids != nullptr) return (int64_t)((a.n[0] + tile_rows - 1) / tile_rows) * a.njobs * a.n_ids;
+  int64_t total = 0;
+  for (int j = 0; j < a.njobs; ++j) total += (a.n[j] + tile_rows - 1) / tile_rows;
+  return total;
+}
+
+}  // namespace
+
+bool mfma_supports(int k) {
+  return nb_slot(k / kBlockWeights) >= 0 && lds_bytes(k) + kXchgBytes <= kMfmaMaxLds;
+}
+
+bool mfma_preferred(const MmvqLaunch& a) {
+  // One workgroup per CU at a time (LDS): below a quarter of the chip the
+  // packed-dot kernels, which spread a row over more waves, are faster.
+  return a.m >= 2 && a.dots == nullptr && mfma_supports(a.k) && workgroups(a) >= 64;
+}
+
+hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream) {
+  const int nb = a.k / kBlockWeights;
+  const int which = nb_slot(nb);
+  if (which < 0) return hipErrorInvalidValue;
+  MfmaParams p{};
+  for (int j = 0; j < kMaxPlainJobs; ++j) {
+    p.w[j] = static_cast<const uint8_t*>(a.w[j]);
+    p.y[j] = a.y[j];
+    p.n[j] = a.n[j];
+  }
+  p.xq = static_cast<const uint8_t*>(a.xq);
+  p.ids = a.ids;
+  p.n_ids = a.n_ids;
+  p.n_experts = a.n_experts;
+  p.x_per_id = a.x_per_id;
+  p.expert_stride = a.expert_stride;
+  p.err_flag = a.err_flag;
+  p.m = a.m;
+
+  // Eight consecutive 16-row tiles per workgroup.
+  const int tile_rows = 16 * kTilesPerWg;
+  int64_t total_wgs = 0;
+  if (a.ids == nullptr) {
+    for (int j = 0; j < kMaxPlainJobs; ++j) {
+      if (j < a.njobs) total_wgs += (a.n[j] + tile_rows - 1) / tile_rows;
+      p.wg_end[j] = (int)total_wgs;
+    }
+  } else {
+    p.wgs_per_job = (a.n[0] + tile_rows - 1) / tile_rows;
+    total_wgs = (int64_t)p.wgs_per_job * a.njobs * a.n_ids;
+  }
+  if (total_wgs == 0) return hipSuccess;
+  p.total_wgs = (int)total_wgs;
+  const dim3 gd((unsigned)((total_wgs + 7) / 8 * 8));
+  const size_t shm = lds_bytes(a.k) + kXchgBytes;
+  switch (which) {
+    case 0: return launch_nb<4>(p, gd, shm, stream);
+    case 1: return launch_nb<8>(p, gd, shm, stream);
+    case 2: return launch_nb<16>(p, gd, shm, stream);
+    default: return launch_nb<28>(p, gd, shm, stream);
+  }
+}
+
+}  // namespace q2k

@@ -37,6 +37,11 @@ hipError_t launch_q8_1_rows(const void* x, int64_t stride, void* xq, int m, int 
 hipError_t launch_swiglu_q8_1_rows(const float* g, const float* u, void* h, void* hq, int rows,
                                    int k, hipStream_t stream);
 hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream);
+// 2..8 tokens on the matrix cores, rows of 4, 8, 16 or 28 super-blocks.
+hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream);
+bool mfma_supports(int k);
+// True when the matrix-core kernel is the faster choice for this launch.
+bool mfma_preferred(const MmvqLaunch& a);
 hipError_t launch_dequant_rows(const void* table, int64_t n_table_rows, const int64_t* ids,
                                int n_rows, void* out, int32_t* err_flag, hipStream_t stream);
 hipError_t launch_engram_gate(float* h, const float* kv, const float* qk, int t, int hc, int dim,

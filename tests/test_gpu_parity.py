@@ -174,6 +174,97 @@ def test_mmvq_deterministic_and_stride_independent():
     assert np.array_equal(c.view(np.uint32), a[:, :1000].view(np.uint32))
 
 
+# ------------------------------------------------- matrix-core path ---------
+# 2..8 tokens against matrices of at least 64 workgroups of 128 rows (8192
+# rows) with 4, 8, 16 or 28 super-blocks per row run on the matrix cores.
+
+MFMA_ROWS = 8192 + 5     # 65 workgroups, the last tile ragged
+
+
+def _sample_rows(n, seed, extra=256):
+    """Both ends, every tile boundary of one workgroup, and random rows."""
+    rows = [np.arange(0, 160), np.arange(n - 160, n), syn.rng_for(seed).choice(n, extra, replace=False)]
+    return np.unique(np.concatenate(rows))
+
+
+@pytest.mark.parametrize("k,m", [(1024, 2), (1024, 8), (2048, 3), (4096, 5), (4096, 8), (7168, 4)])
+def test_mfma_mmvq(k, m):
+    n = MFMA_ROWS
+    case = syn.single_gemv_case(n=n, k=k, m=m, seed=7000 + k + m)
+    w = dev(case.w.reshape(-1))
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits))
+    oq, od = assert_q8_equal(xq, case.x_bits)
+    y = q2.q2k_mmvq(w, xq, n, k, m).cpu().numpy()
+    rows = np.arange(n) if k == 1024 else _sample_rows(n, k + m)
+    assert_close(y[:, rows], orc.mmvq(case.w[rows], oq, od), f"mfma n={n} k={k} m={m}")
+    again = q2.q2k_mmvq(w, xq, n, k, m).cpu().numpy()
+    assert np.array_equal(again.view(np.uint32), y.view(np.uint32)), "not deterministic"
+
+
+def _constant_blocks(n, k, scale_byte, qs_byte, d_bits, dmin_bits):
+    w = np.zeros((n, k // 256, 84), dtype=np.uint8)
+    w[..., 0:16] = scale_byte
+    w[..., 16:80] = qs_byte
+    w[..., 80:82] = np.frombuffer(np.uint16(d_bits).tobytes(), np.uint8)
+    w[..., 82:84] = np.frombuffer(np.uint16(dmin_bits).tobytes(), np.uint8)
+    return w
+
+
+@pytest.mark.parametrize("k", [1024, 7168])
+def test_mfma_closed_forms(k):
+    """x = 127 everywhere (d8 = 1, every half sum 16*127). I term: q = 3,
+    sc = 1, d = 1, m = 0 gives 3*127*k. M term: sc = 0, m = 5, dmin = 1
+    gives -5*127*k."""
+    n, m = MFMA_ROWS, 6
+    x = syn.f32_to_bf16_bits_torch(np.full((m, k), 127.0, np.float32))
+    xq = q2.q8_1_rows(bf16_dev(x))
+    w_i = _constant_blocks(n, k, 0x01, 0xFF, 0x3C00, 0x0000)
+    y = q2.q2k_mmvq(dev(w_i.reshape(-1)), xq, n, k, m).cpu().numpy()
+    assert np.all(y == 3 * 127 * k)
+    w_m = _constant_blocks(n, k, 0x50, 0xFF, 0x0000, 0x3C00)
+    y = q2.q2k_mmvq(dev(w_m.reshape(-1)), xq, n, k, m).cpu().numpy()
+    assert np.all(y == -5 * 127 * k)
+
+
+def test_mfma_pair():
+    pc = syn.attention_pair_case(4, seed=77, na=4096 + 7, nb=4096 + 100, k=2048)
+    xq = q2.q8_1_rows(bf16_dev(pc.x_bits))
+    oq, od = assert_q8_equal(xq, pc.x_bits)
+    ya, yb = q2.q2k_mmvq_pair(dev(pc.wa.reshape(-1)), pc.na, dev(pc.wb.reshape(-1)), pc.nb, xq, pc.k, 4)
+    ra = orc.mmvq(pc.wa[_sample_rows(pc.na, 1)], oq, od)
+    rb = orc.mmvq(pc.wb[_sample_rows(pc.nb, 2)], oq, od)
+    assert_close(ya.cpu().numpy()[:, _sample_rows(pc.na, 1)], ra, "mfma pair a")
+    assert_close(yb.cpu().numpy()[:, _sample_rows(pc.nb, 2)], rb, "mfma pair b")
+
+
+@pytest.mark.parametrize("x_per_id", [False, True])
+def test_mfma_experts(x_per_id):
+    """Gate/up-shaped experts (2048 rows) over 8 ids and two bases: 256
+    workgroups; one id out of range gives NaN rows and the flag."""
+    rng = syn.rng_for(56, int(x_per_id))
+    n, k, m, n_exp = 2048, 1024, 3, 10
+    mats = [[syn.q2k_blocks(rng, n, k // 256) for _ in range(n_exp)] for _ in range(2)]
+    stride = n * (k // 256) * 84
+    bases = [dev(np.concatenate([mt.reshape(-1) for mt in mats[b]])) for b in range(2)]
+    ids_np = np.array([3, 9, 0, 12, 5, 1, 7, 2], dtype=np.int32)   # 12 is out of range
+    x = syn.bf16_normal(rng, ((len(ids_np) if x_per_id else 1) * m, k))
+    xq = q2.q8_1_rows(bf16_dev(x))
+    oq, od = assert_q8_equal(xq, x)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = q2.q2k_mmvq_experts(bases, stride, n_exp, dev(ids_np), xq, x_per_id, n, k, m,
+                            err_flag=flag).cpu().numpy()
+    assert int(flag.item()) == 1
+    rows = _sample_rows(n, 3, extra=128)
+    for b in range(2):
+        for i, e in enumerate(ids_np.tolist()):
+            if e >= n_exp:
+                assert np.all(np.isnan(y[b, i]))
+                continue
+            xs = slice(i * m, (i + 1) * m) if x_per_id else slice(0, m)
+            ref = orc.mmvq(mats[b][e][rows], oq[xs], od[xs])
+            assert_close(y[b, i][:, rows], ref, f"mfma expert base={b} id={e}")
+
+
 # ---------------------------------------------------------------- pair ------
 
 @pytest.mark.parametrize("m", [1, 4, 8])
@@ -392,7 +483,7 @@ def large():
     return case, dev(case.w.reshape(-1))
 
 
-@pytest.mark.parametrize("m", [1, 8])
+@pytest.mark.parametrize("m", [1, 3, 8])
 def test_large_verify_sampled(large, m):
     """[32768, 7168] Q2_K against m bf16 tokens with 5% +-20 outliers, in the
     launch configuration the benchmark times; sampled rows vs the oracle."""
