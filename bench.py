@@ -17,7 +17,7 @@ Method:
   16 products; HIP events on the launching stream bracket its replays, and
   achieved = algorithmic bytes per launch / average launch time.
 * CPU baseline: the CPU oracle timed on a bounded sample of rows of the
-  same matrix and token (about ten seconds of host work).
+  same matrix and token (about twelve seconds of host work).
 
 Prints one JSON line.
 """
@@ -42,15 +42,18 @@ PEAK_GBS = 8000.0          # MI355X HBM3E
 N, K = 32768, 7168
 COPIES = 16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_large_verify_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "q2_quantized_decode_amd", "csrc", f)
-                  for f in ("mmvq.hip", "q2k_device.h")]
+CSRC = os.path.join(ROOT, "q2_quantized_decode_amd", "csrc")
+# The product kernel that runs at each m on this matrix, and its sources.
+KERNELS = {1: ("mmvq_m1_kernel", ("mmvq.hip", "q2k_device.h")),
+           8: ("mmvq_mfma_kernel", ("mmvq_mfma.hip", "q2k_device.h"))}
+COPY_BYTES = 256 << 20     # size of the calibration copy
 
 
-def kernel_hash() -> str:
+def kernel_hash(m: int) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    for f in KERNELS[m][1]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -72,27 +75,37 @@ def measured_traffic(m: int):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_hash") != kernel_hash():
+    r = rec.get(f"m{m}")
+    if not r or r.get("kernel_hash") != kernel_hash(m):
         return None
-    v = rec.get(f"m{m}_bytes_per_launch")
-    return float(v) if v is not None else None
+    return float(r["bytes_per_launch"])
 
 
-def cpu_baseline(case, rows: int):
+def cpu_baseline(case, seconds: float, chunk: int = 4096):
+    """The oracle's m = 1 product over consecutive row chunks of the matrix
+    (wrapping around) until about `seconds` of wall time have passed."""
     from oracle import q2k_oracle as orc
 
     xq, d8, _ = orc.q8_1_from_bf16_bits(case.x_bits[:1])
-    w = case.w[:rows]
+    done_bytes = 0
+    chunks = 0
     c0 = time.process_time()
     t0 = time.perf_counter()
-    orc.mmvq(w, xq, d8)
-    wall = time.perf_counter() - t0
+    while True:
+        r0 = (chunks * chunk) % N
+        w = case.w[r0:r0 + chunk]
+        orc.mmvq(w, xq, d8)
+        done_bytes += w.nbytes
+        chunks += 1
+        wall = time.perf_counter() - t0
+        if wall >= seconds:
+            break
     cpu = time.process_time() - c0
-    gbs = w.nbytes / wall / 1e9
-    return {"value": round(gbs, 6), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
-            "sample": f"first {rows} of {N} rows of the [32768, 7168] Q2_K matrix, m=1, "
-                      f"{w.nbytes} weight bytes in {wall:.2f} s (fp64 dense oracle)"}
+    return {"value": round(done_bytes / wall / 1e9, 6), "unit": "GB/s",
+            "cores": max(1, round(cpu / wall)), "kind": "oracle",
+            "sample": f"{chunks} chunks of {chunk} rows of the [32768, 7168] Q2_K matrix "
+                      f"(rows taken in order, wrapping), m=1: {done_bytes} weight bytes in "
+                      f"{wall:.1f} s, fp64 dense oracle"}
 
 
 def run(args):
@@ -218,7 +231,7 @@ def run(args):
         "roofline": {"bound": "hbm", "achieved": round(r1["achieved"], 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(r1["achieved"] / PEAK_GBS, 4),
                      "traffic": measured_traffic(1),
-                     "kernel": "q2k_mmvq (mmvq_m1_kernel)",
+                     "kernel": f"q2k_mmvq ({KERNELS[1][0]})",
                      "bytes_per_launch": mmvq_bytes(1),
                      "us_per_launch": round(r1["launch_s"] * 1e6, 3)},
         "m8": {"value": round(r8["step_gbs"], 1), "unit": "GB/s",
@@ -229,11 +242,12 @@ def run(args):
                             "peak": PEAK_GBS, "unit": "GB/s",
                             "frac": round(r8["achieved"] / PEAK_GBS, 4),
                             "traffic": measured_traffic(8),
+                            "kernel": f"q2k_mmvq ({KERNELS[8][0]})",
                             "bytes_per_launch": mmvq_bytes(8),
                             "us_per_launch": round(r8["launch_s"] * 1e6, 3)}},
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
@@ -247,15 +261,15 @@ def pmc_calibration(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    for _ in range(4):
-        dst.copy_(src)
-    torch.cuda.synchronize()
     case = syn.large_verify_case(m=8)
     w0 = torch.from_numpy(case.w.reshape(-1)).to(dev)
     copies = [w0] + [w0.clone() for _ in range(7)]
     x8 = syn.bf16_bits_to_tensor(case.x_bits).to(dev)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
     for m in (1, 8):
         x = x8[:m].contiguous()
         xq = q2.q8_1_rows(x)
@@ -263,7 +277,56 @@ def pmc_calibration(args):
         for i in range(8):
             q2.q2k_mmvq(copies[i], xq, N, K, m, out=y)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": 2 * src.numel(), "copies": 4, "mmvq_launches_per_m": 8}))
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 4, "mmvq_launches_per_m": 8}))
+
+
+def _pmc_rows(path: str, counter: str):
+    import csv
+    with open(path, newline="") as f:
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(f)
+                if r["Counter_Name"] == counter]
+
+
+def traffic_from(fetch_csv: str, write_csv: str, out: str):
+    """HBM bytes per product launch from two rocprofv3 --pmc runs of
+    --pmc-calibration (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch). Each
+    counter is scaled by the factor that makes it read COPY_BYTES for the
+    calibration copies (read COPY_BYTES, write COPY_BYTES)."""
+    rec = {"commands": [
+        "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d <out>/pmc_fetch -o f "
+        "--output-format csv -- python3 /root/repo/bench.py --pmc-calibration",
+        "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d <out>/pmc_write -o w "
+        "--output-format csv -- python3 /root/repo/bench.py --pmc-calibration",
+        "python3 bench.py --traffic-from <out>/pmc_fetch/f_counter_collection.csv "
+        "<out>/pmc_write/w_counter_collection.csv"],
+        "calibration": f"four device copies of {COPY_BYTES} bytes (read {COPY_BYTES}, write "
+                       f"{COPY_BYTES}); each counter is scaled by COPY_BYTES / its copy reading"}
+    scaled = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_rows(path, counter)
+        # the four COPY_BYTES copies are the largest copy dispatches
+        copies = sorted(v for name, v in rows if "opy" in name)[-4:]
+        if len(copies) < 4:
+            raise SystemExit(f"{path}: calibration copies not found")
+        factor = COPY_BYTES / (1024.0 * float(np.median(copies)))
+        rec[f"{counter}_factor"] = round(factor, 4)
+        for m, (kname, _) in KERNELS.items():
+            vals = [v for name, v in rows if kname in name]
+            if not vals:
+                raise SystemExit(f"{path}: no {kname} dispatches")
+            scaled.setdefault(m, {})[counter] = 1024.0 * factor * float(np.mean(vals))
+    for m, (kname, _) in KERNELS.items():
+        tot = scaled[m]["FETCH_SIZE"] + scaled[m]["WRITE_SIZE"]
+        rec[f"m{m}"] = {"kernel": kname, "kernel_hash": kernel_hash(m),
+                        "fetch_bytes": round(scaled[m]["FETCH_SIZE"]),
+                        "write_bytes": round(scaled[m]["WRITE_SIZE"]),
+                        "bytes_per_launch": round(tot),
+                        "algorithmic_bytes": mmvq_bytes(m),
+                        "ratio_to_algorithmic": round(tot / mmvq_bytes(m), 4)}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def main():
@@ -271,10 +334,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3200)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--cpu-rows", type=int, default=12288)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--pmc-calibration", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic record from two counter runs and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from, TRAFFIC_FILE)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

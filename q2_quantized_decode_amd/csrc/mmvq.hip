@@ -387,16 +387,19 @@ constexpr int kStageBytes = 3072;
 // (k from 1024 to 8192). Each wave owns a run of CH row steps (CH a multiple
 // of 8, known at compile time), either consecutive or interleaved with the
 // other runs of the matrix (stride S) so that the waves sweep the matrix
-// together. Per step:
-//  * the step's bytes (P whole rows, contiguous) arrive by three wave-wide
-//    coalesced 16-byte loads into a ring of R register sets;
-//  * the wave writes them to its own LDS area and each lane reads back its
-//    half block's fields (32 quant bytes, 8 scale bytes, d/dmin);
-//  * activations stay in VGPRs for the whole run; sums of eight consecutive
-//    steps are reduced together.
-// A full run is straight-line code (exact hardware wait counters); staging
-// of step s + 1 overlaps the arithmetic of step s. Runs cut short by the end
-// of the matrix take a guarded path with direct per-lane loads.
+// together. A step is P whole rows (contiguous bytes); lane l works on half
+// block l % GS of row l / GS. Per step:
+//  * direct path (default): each lane loads its half block's fields (32
+//    quant bytes, 8 scale bytes, d/dmin) into a ring of R register sets, R
+//    steps ahead of the arithmetic;
+//  * staged path (STAGED): the step arrives by three wave-wide coalesced
+//    16-byte loads, goes through the wave's own LDS area, and each lane reads
+//    its fields back (measured slower: LDS bank conflicts on the field reads);
+//  * the activations stay in VGPRs for the whole run; the sums of eight
+//    consecutive steps are reduced together (one transposed butterfly).
+// A full run is straight-line code, so the hardware wait counters are exact
+// and no wait drains the ring. Runs cut short by the end of the matrix take
+// a guarded path with one direct load per step.
 template <int GSL, int R, int CH, bool STAGED>
 __global__ __launch_bounds__(256) void mmvq_m1_kernel(const MmvqParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[STAGED ? 4 : 1][STAGED ? kStageBytes : 16];
