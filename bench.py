@@ -108,6 +108,54 @@ def cpu_baseline(case, seconds: float, chunk: int = 4096):
                       f"{wall:.1f} s, fp64 dense oracle"}
 
 
+def bench_grouped(torch, q2, syn, dev, copies_n: int = 64):
+    """The grouped-input product (wo_a shape: 8 groups x 1024 rows, 2048-wide
+    slices of a 16384-wide input) at m = 1 and m = 8 over rotating weight
+    copies, timed with HIP events around graph replays of 16 launches."""
+    out = {}
+    gc = syn.grouped_case(8)
+    w0 = torch.from_numpy(gc.w.reshape(-1)).to(dev)
+    copies = [w0] + [w0.clone() for _ in range(copies_n - 1)]
+    x8 = syn.bf16_bits_to_tensor(gc.x_bits).to(dev)
+    wbytes = w0.numel()
+    for m in (1, 8):
+        xq = q2.q8_1_rows(x8[:m].contiguous())
+        y = torch.empty((m, gc.groups * gc.rows), dtype=torch.float32, device=dev)
+        stream = torch.cuda.Stream()
+        graphs = []
+        torch.cuda.synchronize()
+        for c0 in range(0, copies_n, 16):
+            with torch.cuda.stream(stream):
+                for i in range(16):
+                    q2.q2k_mmvq_grouped(copies[c0 + i], xq, gc.groups, gc.rows, gc.k, m, out=y)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(16):
+                    q2.q2k_mmvq_grouped(copies[c0 + i], xq, gc.groups, gc.rows, gc.k, m, out=y)
+            graphs.append(g)
+        reps = 20
+        with torch.cuda.stream(stream):
+            for g in graphs:
+                g.replay()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(reps):
+                for g in graphs:
+                    g.replay()
+            ev1.record(stream)
+            ev1.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / (reps * copies_n)
+        nbytes = wbytes + q2.q8_1_rows_bytes(m, gc.groups * gc.k) + 4 * m * gc.groups * gc.rows
+        out[f"m{m}"] = {"us_per_launch": round(us, 3), "bytes_per_launch": nbytes,
+                        "achieved": round(nbytes / us / 1e3, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                        "frac": round(nbytes / us / 1e3 / PEAK_GBS, 4)}
+    out["workload"] = ("grouped-input wo_a product, Q2_K [8192, 2048] in 8 groups of 1024 rows "
+                       f"over 2048-wide slices of x [m, 16384], {copies_n} rotating copies")
+    return out
+
+
 def run(args):
     import torch
 
@@ -246,6 +294,9 @@ def run(args):
                             "bytes_per_launch": mmvq_bytes(8),
                             "us_per_launch": round(r8["launch_s"] * 1e6, 3)}},
     }
+    del copies
+    torch.cuda.synchronize()
+    line["grouped"] = bench_grouped(torch, q2, syn, dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -61,7 +61,7 @@ extern "C" {
 #define Q2K_API
 #endif
 
-#define Q2K_ABI_VERSION 1
+#define Q2K_ABI_VERSION 2
 
 #define Q2K_OK 0
 #define Q2K_EINVAL (-1)   /* NULL pointer, or pointers that must not overlap do */
@@ -138,6 +138,23 @@ Q2K_API int32_t q2k_mmvq_experts(const void* const* bases, int32_t n_bases,
                          const void* xq_dev, int32_t x_per_id, float* y_dev,
                          int32_t n, int32_t k, int32_t m,
                          int32_t* err_flag_dev, void* stream);
+
+/* Grouped-input product: the Q2_K route of the attention output projection
+ * wo_a (attn_v41/decode.rs, the grouped wo_a step of the decode body, taken
+ * when wo_a is Q2_K and m <= 8), where output row g*o_rank + r is the dot of
+ * wo_a's row with the g-th column slice o_g of the attention output.
+ *   w_dev          : Q2_K [groups * rows_per_group, k]; rows g*R .. g*R+R-1
+ *                    (R = rows_per_group) belong to group g.
+ *   xq_dev         : q8_1 rows [m, groups * k] (q8_1_rows of the whole input
+ *                    rows); group g reads elements g*k .. g*k+k-1 of each.
+ *   y_dev          : f32 [m, groups * R] (token-major):
+ *                    y[t][g*R + r] = sum_e W[g*R + r][e] * x[t][g*k + e].
+ *   groups >= 1, rows_per_group >= 1, k % 256 == 0, 1 <= m <= Q2K_MAX_M,
+ *   groups * R, groups * k < 2^31. Q2K_ESHAPE otherwise; Q2K_EINVAL for
+ *   null pointers or y overlapping w or xq; Q2K_EALIGN as q2k_mmvq. */
+Q2K_API int32_t q2k_mmvq_grouped(const void* w_dev, const void* xq_dev, float* y_dev,
+                         int32_t groups, int32_t rows_per_group, int32_t k, int32_t m,
+                         void* stream);
 
 /* Fused bf16 SwiGLU and q8_1 re-quantisation
  * (kquant_swiglu_q8_1_rows_bf16, moe_v41/init.rs).

@@ -23,7 +23,8 @@ rustdoc source views of the metrale engine: ``engram_v41/apply.rs``,
   (``q_kv_projections``: one q8_1 quantisation shared by two Q2_K matrices).
   32-wide blocks, scale ``amax/127``, round to nearest.
 * The Q2_K x q8_1 product (``kquant_mmvq_q2_k_w``, ``mmvq_q2k_pair_w``,
-  ``kquant_mmvq_q2_k_experts_w*``): ``y[t, n] = sum_e W[n, e] * a[t, e]`` with
+  ``kquant_mmvq_q2_k_experts_w*``, and the grouped ``wo_a`` step of
+  ``attn_v41/decode.rs``): ``y[t, n] = sum_e W[n, e] * a[t, e]`` with
   ``W`` the dequantised weights and ``a = d8 * xq`` the dequantised
   activations, accumulated here in fp64.
 * Row dequantisation to bf16 (``dequant_q2_k_to_bf16``,
@@ -291,6 +292,30 @@ def mmvq_experts(matrices_by_id, xq, d8, x_per_id: bool):
         else:
             outs.append(mmvq(w, xq, d8))
     return np.stack(outs)
+
+
+def mmvq_grouped(w: np.ndarray, xq: np.ndarray, d8: np.ndarray, groups: int) -> np.ndarray:
+    """Grouped-input product, the Q2_K route of the attention output
+    projection ``wo_a`` (attn_v41/decode.rs, decode body: output column
+    ``g*o_rank + r`` is the dot of row ``g*o_rank + r`` of ``wo_a`` with the
+    g-th column slice ``o_g`` of the attention output).
+
+    ``w``: uint8 [groups*R, k/256, 84]; ``xq``: int [m, groups*k] and ``d8``:
+    f32 [m, groups*k/32] (the q8_1 rows of the whole attention output).
+    Returns fp64 [m, groups*R]: y[t, g*R + r] = sum_e W[g*R + r, e] *
+    a[t, g*k + e], ``a = d8 * xq``."""
+    n_total, nb = w.shape[0], w.shape[1]
+    if n_total % groups:
+        raise ValueError("rows must split evenly into groups")
+    rows, k = n_total // groups, 256 * nb
+    if xq.shape[1] != groups * k:
+        raise ValueError("activation width must be groups * k")
+    wf = q2k_matrix_f64(w)
+    a = q8_1_dequant_f64(xq, d8)
+    y = np.empty((a.shape[0], n_total), dtype=np.float64)
+    for g in range(groups):
+        y[:, g * rows:(g + 1) * rows] = a[:, g * k:(g + 1) * k] @ wf[g * rows:(g + 1) * rows].T
+    return y
 
 
 # ----------------------------------------------------------------------------

@@ -37,6 +37,7 @@ SIGNATURES = {
     "q2k_mmvq_pair": (_I32, [_VP, _VP, _I32, _VP, _VP, _I32, _VP, _I32, _I32, _VP]),
     "q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP, _I32,
                                 _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP]),
+    "q2k_mmvq_grouped": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP]),
     "swiglu_q8_1_rows": (_I32, [_VP, _VP, _VP, _VP, _SZ, _I32, _I32, _VP]),
     "q2k_dequant_rows": (_I32, [_VP, _I64, _VP, _I32, _VP, _VP, _VP]),
     "engram_gate": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _F32, _VP]),
@@ -160,6 +161,18 @@ def q2k_mmvq_experts(bases: Sequence[torch.Tensor], expert_stride_bytes: int, n_
     _check("q2k_mmvq_experts", lib().q2k_mmvq_experts(
         arr, len(ptrs), expert_stride_bytes, n_experts, _contig(ids, "ids"), n_ids,
         _contig(xq, "xq"), 1 if x_per_id else 0, _contig(out, "out"), n, k, m, flag or None,
+        _stream()))
+    return out
+
+
+def q2k_mmvq_grouped(w: torch.Tensor, xq: torch.Tensor, groups: int, rows_per_group: int, k: int,
+                     m: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """f32 [m, groups * rows_per_group]: row g*R + r of ``w`` against elements
+    g*k .. g*k+k-1 of each q8_1 row (rows of width groups * k)."""
+    if out is None:
+        out = torch.empty((m, groups * rows_per_group), dtype=torch.float32, device=w.device)
+    _check("q2k_mmvq_grouped", lib().q2k_mmvq_grouped(
+        _contig(w, "w"), _contig(xq, "xq"), _contig(out, "out"), groups, rows_per_group, k, m,
         _stream()))
     return out
 

@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+#include <stdint.h>
 
 #include "../../include/q2k_decode.h"
 #include "q2k_device.h"
@@ -196,6 +197,40 @@ int32_t q2k_mmvq_experts(const void* const* bases, int32_t n_bases, int64_t expe
   a.x_per_id = x_per_id;
   a.expert_stride = expert_stride_bytes;
   a.err_flag = err_flag_dev;
+  a.k = k;
+  a.m = m;
+  return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
+}
+
+int32_t q2k_mmvq_grouped(const void* w_dev, const void* xq_dev, float* y_dev, int32_t groups,
+                         int32_t rows_per_group, int32_t k, int32_t m, void* stream) {
+  const char* fn = "q2k_mmvq_grouped";
+  if (groups < 1) return fail(Q2K_ESHAPE, "%s: groups = %d < 1", fn, groups);
+  if (rows_per_group < 1) return fail(Q2K_ESHAPE, "%s: rows_per_group = %d < 1", fn, rows_per_group);
+  if (int32_t r = check_k(fn, k)) return r;
+  if (int32_t r = check_m(fn, m)) return r;
+  const int64_t n_total = (int64_t)groups * rows_per_group;
+  const int64_t k_total = (int64_t)groups * k;
+  if (n_total > INT32_MAX || k_total > INT32_MAX)
+    return fail(Q2K_ESHAPE, "%s: groups * rows_per_group or groups * k exceeds 2^31 - 1", fn);
+  if ((int64_t)m * n_total > (int64_t)1 << 31) return fail(Q2K_ESHAPE, "%s: output larger than 2^31 values", fn);
+  if (int32_t r = check_matrix(fn, "w", w_dev, (int32_t)n_total)) return r;
+  if (int32_t r = check_out(fn, "y", y_dev)) return r;
+  if (!xq_dev) return fail(Q2K_EINVAL, "%s: xq is null", fn);
+  if (!aligned(xq_dev, 16)) return fail(Q2K_EALIGN, "%s: xq must be 16-byte aligned", fn);
+  const size_t ybytes = (size_t)m * (size_t)n_total * 4;
+  if (overlap(y_dev, ybytes, w_dev, q2k_matrix_bytes(n_total, k)) ||
+      overlap(y_dev, ybytes, xq_dev, q8_1_rows_bytes(m, (int32_t)k_total)))
+    return fail(Q2K_EINVAL, "%s: y overlaps an input", fn);
+  q2k::MmvqLaunch a{};
+  a.w[0] = w_dev;
+  a.y[0] = y_dev;
+  a.n[0] = rows_per_group;
+  a.njobs = 1;
+  a.xq = xq_dev;
+  a.groups = groups;
+  a.n_ids = groups;
+  a.expert_stride = (int64_t)q2k_matrix_bytes(rows_per_group, k);
   a.k = k;
   a.m = m;
   return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);

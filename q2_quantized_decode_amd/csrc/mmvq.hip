@@ -42,13 +42,14 @@ struct MmvqParams {
   int32_t wave_end[kMaxPlainJobs];   // plain mode: exclusive prefix of waves per job
   const uint8_t* xq;
   const int32_t* ids;                // expert mode when non-null
-  int32_t n_ids;
+  int32_t n_ids;                     // expert mode: ids; grouped mode: groups
   int32_t n_experts;
   int32_t x_per_id;
   int64_t expert_stride;
   int32_t* err_flag;
   int32_t* dots;
-  int32_t waves_per_job;             // expert mode
+  int32_t groups;                    // grouped mode when > 0
+  int32_t waves_per_job;             // expert and grouped modes
   int32_t total_waves;
   int32_t chunk;                     // row steps per wave
   int32_t interleave;                // 1: a job's waves take its steps round-robin
@@ -59,9 +60,10 @@ struct MmvqParams {
 // The matrix one wave works on, and its run of row steps.
 struct WaveJob {
   const uint8_t* w;    // row 0 of the matrix
-  float* y;            // [m, n] output of the matrix
-  const uint8_t* xq;   // q8_1 rows read by the matrix
+  float* y;            // output row 0 of the matrix; token t at y + t * ldy
+  XView x;             // q8_1 activations read by the matrix
   int n;
+  int ldy;
   int it;              // first row step
   int it_end;          // end of the run
   int stride;          // distance between the wave's consecutive steps
@@ -72,14 +74,24 @@ template <int M>
 __device__ __forceinline__ WaveJob resolve_wave(const MmvqParams& p, int wave, int P) {
   WaveJob J;
   int lw;
-  if (p.ids == nullptr) {
+  if (p.ids == nullptr && p.groups == 0) {
     const int j = (wave >= p.wave_end[0]) + (wave >= p.wave_end[1]) + (wave >= p.wave_end[2]);
     lw = wave - (j > 0 ? p.wave_end[j - 1] : 0);
     J.w = p.w[j];
     J.y = p.y[j];
     J.n = p.n[j];
-    J.xq = p.xq;
+    J.ldy = J.n;
+    J.x = xview(p.xq, p.k, 0);
     J.bad = false;
+  } else if (p.groups > 0) {
+    const int g = wave / p.waves_per_job;
+    lw = wave - g * p.waves_per_job;
+    J.bad = false;
+    J.w = p.w[0] + (int64_t)g * p.expert_stride;
+    J.n = p.n[0];
+    J.ldy = p.groups * p.n[0];
+    J.y = p.y[0] + (int64_t)g * p.n[0];
+    J.x = xview(p.xq, p.groups * p.k, g * p.k);
   } else {
     const int j = wave / p.waves_per_job;
     lw = wave - j * p.waves_per_job;
@@ -89,13 +101,14 @@ __device__ __forceinline__ WaveJob resolve_wave(const MmvqParams& p, int wave, i
     J.bad = id < 0 || id >= p.n_experts;
     J.w = p.w[base] + (int64_t)(J.bad ? 0 : id) * p.expert_stride;
     J.n = p.n[0];
+    J.ldy = J.n;
     J.y = p.y[0] + (int64_t)j * M * p.n[0];
-    J.xq = p.x_per_id ? p.xq + (int64_t)i * M * (int64_t)q8_row_bytes(p.k) : p.xq;
+    J.x = xview(p.x_per_id ? p.xq + (int64_t)i * M * (int64_t)q8_row_bytes(p.k) : p.xq, p.k, 0);
   }
   const int iters = (J.n + P - 1) / P;
   if (p.interleave) {
     int waves_of_job;
-    if (p.ids == nullptr) {
+    if (p.ids == nullptr && p.groups == 0) {
       const int j = (wave >= p.wave_end[0]) + (wave >= p.wave_end[1]) + (wave >= p.wave_end[2]);
       waves_of_job = p.wave_end[j] - (j > 0 ? p.wave_end[j - 1] : 0);
     } else {
@@ -147,13 +160,14 @@ struct AHalf {
   u32x4 s;
 };
 
-__device__ __forceinline__ AHalf load_ahalf(const uint8_t* row, int k, int b, int h) {
+__device__ __forceinline__ AHalf load_ahalf(const XView& x, int t, int b, int h) {
   AHalf a;
-  const uint8_t* xb = row + 256 * b + 128 * h;
+  const int64_t to = (int64_t)t * x.stride;
+  const uint8_t* xb = x.q + to + 256 * b + 128 * h;
 #pragma unroll
   for (int i = 0; i < 8; ++i) a.x[i] = gload<u32x4>(xb + 16 * i);
-  a.d8 = gload<f32x4>(row + q8_scale_offset(k) + (size_t)(8 * b + 4 * h) * 4);
-  a.s = gload<u32x4>(row + q8_sum_offset(k) + (size_t)(16 * b + 8 * h) * 2);
+  a.d8 = gload<f32x4>(x.s + to + (size_t)(8 * b + 4 * h) * 4);
+  a.s = gload<u32x4>(x.m + to + (size_t)(16 * b + 8 * h) * 2);
   return a;
 }
 
@@ -437,7 +451,7 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const MmvqParams p) {
   const bool full = last_step < J.it_end && (last_step + 1) * P <= J.n;
 
   // Activations first: the first step waits for them and ring slot 0 only.
-  const AHalf act = load_ahalf(J.xq, k, b, h);
+  const AHalf act = load_ahalf(J.x, 0, b, h);
   double dq[4], dm[4];
 
   if (full && !STAGED) {
@@ -572,7 +586,6 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
   const int b = hb >> 1;
   const int h = hb & 1;
   const size_t rowbytes = (size_t)nb * kBlockBytes;
-  const size_t rb = q8_row_bytes(k);
 
   const WaveJob J = resolve_wave<M>(p, wave, P);
   if (J.it >= J.it_end) return;
@@ -587,7 +600,7 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
                                                  : zero_whalf();
   }
   AHalf act;
-  if constexpr (CACHE) act = hb_ok ? load_ahalf(J.xq, k, b, h) : zero_ahalf();
+  if constexpr (CACHE) act = hb_ok ? load_ahalf(J.x, 0, b, h) : zero_ahalf();
 
   for (int base = J.it; base < J.it_end; base += DEPTH * J.stride) {
 #pragma unroll
@@ -607,7 +620,7 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
           if constexpr (CACHE) {
             a = act;
           } else {
-            a = hb_ok ? load_ahalf(J.xq + t * rb, k, b, h) : zero_ahalf();
+            a = hb_ok ? load_ahalf(J.x, t, b, h) : zero_ahalf();
           }
           if constexpr (DOTS) {
             if (live) store_dots(p.dots, w, a, t, J.n, row, k, b, h);
@@ -615,7 +628,7 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
             double part = live ? half_block_value(w, a) : 0.0;
             part = group_sum(part, gs);
             if (hb == 0 && row < J.n)
-              J.y[(int64_t)t * J.n + row] = J.bad ? quiet_nan() : (float)part;
+              J.y[(int64_t)t * J.ldy + row] = J.bad ? quiet_nan() : (float)part;
           }
         }
       }
@@ -637,7 +650,6 @@ __global__ __launch_bounds__(256) void mmvq_wide_kernel(const MmvqParams p) {
   const int k = p.k;
   const int nb = k >> 8;
   const size_t rowbytes = (size_t)nb * kBlockBytes;
-  const size_t rb = q8_row_bytes(k);
   const WaveJob J = resolve_wave<M>(p, wave, 1);
   for (int row = J.it; row < J.it_end; row += J.stride) {
     double part[M];
@@ -648,7 +660,7 @@ __global__ __launch_bounds__(256) void mmvq_wide_kernel(const MmvqParams p) {
       const WHalf w = load_whalf(J.w + row * rowbytes + b * kBlockBytes, h);
 #pragma unroll
       for (int t = 0; t < M; ++t) {
-        const AHalf a = load_ahalf(J.xq + t * rb, k, b, h);
+        const AHalf a = load_ahalf(J.x, t, b, h);
         if constexpr (DOTS) {
           store_dots(p.dots, w, a, t, J.n, row, k, b, h);
         } else {
@@ -660,7 +672,7 @@ __global__ __launch_bounds__(256) void mmvq_wide_kernel(const MmvqParams p) {
 #pragma unroll
       for (int t = 0; t < M; ++t) {
         const double v = group_sum(part[t], 64);
-        if (lane == 0) J.y[(int64_t)t * J.n + row] = J.bad ? quiet_nan() : (float)v;
+        if (lane == 0) J.y[(int64_t)t * J.ldy + row] = J.bad ? quiet_nan() : (float)v;
       }
     }
   }
@@ -813,16 +825,17 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   p.expert_stride = a.expert_stride;
   p.err_flag = a.err_flag;
   p.dots = a.dots;
+  p.groups = a.groups;
   p.k = a.k;
   p.gs_log2 = gs_log2;
 
   // Row steps per job, then a run length that spreads them over about
   // waves_per_cu waves per CU, then whole runs per job (no run straddles
   // two matrices, so each wave resolves its matrix once).
-  const int n_jobs = a.ids == nullptr ? a.njobs : a.njobs * a.n_ids;
+  const int n_jobs = uniform_jobs(a) ? a.njobs * a.n_ids : a.njobs;
   int64_t total_iters = 0;
   int64_t iters_of[kMaxPlainJobs] = {0, 0, 0, 0};
-  if (a.ids == nullptr) {
+  if (!uniform_jobs(a)) {
     for (int j = 0; j < a.njobs; ++j) {
       iters_of[j] = (a.n[j] + P - 1) / P;
       total_iters += iters_of[j];
@@ -844,7 +857,7 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   }
   p.chunk = (int)chunk;
   int64_t total_waves = 0;
-  if (a.ids == nullptr) {
+  if (!uniform_jobs(a)) {
     for (int j = 0; j < kMaxPlainJobs; ++j) {
       total_waves += j < a.njobs ? (iters_of[j] + chunk - 1) / chunk : 0;
       p.wave_end[j] = (int)total_waves;

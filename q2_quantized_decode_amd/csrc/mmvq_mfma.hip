@@ -64,12 +64,13 @@ struct MfmaParams {
   int32_t wg_end[kMaxPlainJobs];     // plain mode: exclusive prefix of workgroups per job
   const uint8_t* xq;
   const int32_t* ids;                // expert mode when non-null
-  int32_t n_ids;
+  int32_t n_ids;                     // expert mode: ids; grouped mode: groups
   int32_t n_experts;
   int32_t x_per_id;
   int64_t expert_stride;
   int32_t* err_flag;
-  int32_t wgs_per_job;               // expert mode
+  int32_t groups;                    // grouped mode when > 0
+  int32_t wgs_per_job;               // expert and grouped modes
   int32_t total_wgs;
   int32_t m;
 };
@@ -129,23 +130,34 @@ __device__ __forceinline__ Blk load_blk(const uint8_t* base, const BlkOffsets& o
 // The matrix, output and activations of one workgroup.
 struct Job {
   const uint8_t* W;
-  float* Y;
-  const uint8_t* X;
+  float* Y;    // output row 0; token t at Y + t * ldy
+  XView X;
   int n;
-  int lwg;   // workgroup index within the job
-  bool bad;  // expert id out of range: outputs NaN, error flag set
+  int ldy;
+  int lwg;     // workgroup index within the job
+  bool bad;    // expert id out of range: outputs NaN, error flag set
 };
 
-__device__ __forceinline__ Job resolve_job(const MfmaParams& p, int wgi, size_t rb) {
+template <int k>
+__device__ __forceinline__ Job resolve_job(const MfmaParams& p, int wgi) {
   Job J;
   J.bad = false;
-  if (p.ids == nullptr) {
+  if (p.ids == nullptr && p.groups == 0) {
     const int j = (wgi >= p.wg_end[0]) + (wgi >= p.wg_end[1]) + (wgi >= p.wg_end[2]);
     J.lwg = wgi - (j > 0 ? p.wg_end[j - 1] : 0);
     J.W = p.w[j];
     J.Y = p.y[j];
     J.n = p.n[j];
-    J.X = p.xq;
+    J.ldy = J.n;
+    J.X = xview(p.xq, k, 0);
+  } else if (p.groups > 0) {
+    const int g = wgi / p.wgs_per_job;
+    J.lwg = wgi - g * p.wgs_per_job;
+    J.W = p.w[0] + (int64_t)g * p.expert_stride;
+    J.n = p.n[0];
+    J.ldy = p.groups * p.n[0];
+    J.Y = p.y[0] + (int64_t)g * p.n[0];
+    J.X = xview(p.xq, p.groups * k, g * k);
   } else {
     const int j = wgi / p.wgs_per_job;
     J.lwg = wgi - j * p.wgs_per_job;
@@ -155,8 +167,9 @@ __device__ __forceinline__ Job resolve_job(const MfmaParams& p, int wgi, size_t 
     J.bad = id < 0 || id >= p.n_experts;
     J.W = p.w[base] + (int64_t)(J.bad ? 0 : id) * p.expert_stride;
     J.n = p.n[0];
+    J.ldy = J.n;
     J.Y = p.y[0] + (int64_t)j * p.m * J.n;
-    J.X = p.x_per_id ? p.xq + (int64_t)i * p.m * (int64_t)rb : p.xq;
+    J.X = xview(p.x_per_id ? p.xq + (int64_t)i * p.m * (int64_t)q8_row_bytes(k) : p.xq, k, 0);
   }
   return J;
 }
@@ -164,9 +177,8 @@ __device__ __forceinline__ Job resolve_job(const MfmaParams& p, int wgi, size_t 
 // Stage the activations of m tokens (k wide) in LDS. Every load is issued
 // before the first LDS store, so the staging costs one memory latency.
 template <int k, int THREADS>
-__device__ __forceinline__ void stage_activations(uint8_t* lds, const uint8_t* X, int m) {
+__device__ __forceinline__ void stage_activations(uint8_t* lds, const XView& X, int m) {
   static_assert(kSlots * (k / 128) <= THREADS, "one scale group per thread");
-  const size_t rb = q8_row_bytes(k);
   const int tid = threadIdx.x;
   constexpr int QC = k / 16;  // 16-byte quant chunks per token
   constexpr int QIT = (kSlots * QC + THREADS - 1) / THREADS;
@@ -176,7 +188,7 @@ __device__ __forceinline__ void stage_activations(uint8_t* lds, const uint8_t* X
     const int idx = tid + it * THREADS;
     const int t = idx / QC, e = idx - (idx / QC) * QC;
     qv[it] = u32x4{0, 0, 0, 0};
-    if (idx < kSlots * QC && t < m) qv[it] = gload<u32x4>(X + (size_t)t * rb + 16 * e);
+    if (idx < kSlots * QC && t < m) qv[it] = gload<u32x4>(X.q + t * X.stride + 16 * e);
   }
   // Scales and half-block sums: thread (token t2, group c4) takes q8 blocks
   // 4c4..4c4+3, i.e. sub-blocks 8c4..8c4+7.
@@ -186,8 +198,8 @@ __device__ __forceinline__ void stage_activations(uint8_t* lds, const uint8_t* X
   f32x4 d8v = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 sv = u32x4{0, 0, 0, 0};
   if (sv_ok) {
-    d8v = gload<f32x4>(X + (size_t)t2 * rb + q8_scale_offset(k) + 16 * c4);
-    sv = gload<u32x4>(X + (size_t)t2 * rb + q8_sum_offset(k) + 16 * c4);
+    d8v = gload<f32x4>(X.s + t2 * X.stride + 16 * c4);
+    sv = gload<u32x4>(X.m + t2 * X.stride + 16 * c4);
   }
 #pragma unroll
   for (int it = 0; it < QIT; ++it) {
@@ -272,7 +284,7 @@ __device__ __forceinline__ void store_tile(const Job& J, int m, int r0, const La
   for (int i = 0; i < 4; ++i) {
     const int token = 4 * L.g + i;
     const int row = r0 + L.j16;
-    if (L.g < 2 && token < m && row < J.n) J.Y[(int64_t)token * J.n + row] = J.bad ? quiet_nan() : (float)yv[i];
+    if (L.g < 2 && token < m && row < J.n) J.Y[(int64_t)token * J.ldy + row] = J.bad ? quiet_nan() : (float)yv[i];
   }
 }
 
@@ -294,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const MfmaParams p)
   const int wgi = (blockIdx.x & 7) * g8 + (blockIdx.x >> 3);   // XCD-major workgroup index
   if (wgi >= p.total_wgs) return;                              // whole workgroup
   const int m = p.m;
-  const Job J = resolve_job(p, wgi, q8_row_bytes(k));
+  const Job J = resolve_job<k>(p, wgi);
 
   const int wiw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int tw = wiw & (kTilesPerWg - 1);
@@ -413,7 +425,7 @@ hipError_t launch_nb(const MfmaParams& p, dim3 gd, size_t shm, hipStream_t strea
 
 int64_t workgroups(const MmvqLaunch& a) {
   const int tile_rows = 16 * kTilesPerWg;
-  if (a.ids != nullptr) return (int64_t)((a.n[0] + tile_rows - 1) / tile_rows) * a.njobs * a.n_ids;
+  if (uniform_jobs(a)) return (int64_t)((a.n[0] + tile_rows - 1) / tile_rows) * a.njobs * a.n_ids;
   int64_t total = 0;
   for (int j = 0; j < a.njobs; ++j) total += (a.n[j] + tile_rows - 1) / tile_rows;
   return total;
@@ -448,12 +460,13 @@ hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream) {
   p.x_per_id = a.x_per_id;
   p.expert_stride = a.expert_stride;
   p.err_flag = a.err_flag;
+  p.groups = a.groups;
   p.m = a.m;
 
   // Eight consecutive 16-row tiles per workgroup.
   const int tile_rows = 16 * kTilesPerWg;
   int64_t total_wgs = 0;
-  if (a.ids == nullptr) {
+  if (!uniform_jobs(a)) {
     for (int j = 0; j < kMaxPlainJobs; ++j) {
       if (j < a.njobs) total_wgs += (a.n[j] + tile_rows - 1) / tile_rows;
       p.wg_end[j] = (int)total_wgs;

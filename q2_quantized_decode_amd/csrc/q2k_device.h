@@ -25,6 +25,23 @@ __host__ __device__ constexpr size_t q8_row_bytes(int k) { return (size_t)k * 5 
 __host__ __device__ constexpr size_t q8_scale_offset(int k) { return (size_t)k; }
 __host__ __device__ constexpr size_t q8_sum_offset(int k) { return (size_t)k + (size_t)k / 8; }
 
+// Where a product reads its q8_1 activations: the quants, block scales and
+// half sums of token 0, and the byte distance between tokens. A whole row of
+// K values starting at `row` has its fields at row, row + K and row + 9K/8;
+// the sub-row of that row starting at element e0 (a multiple of 256) has the
+// same layout shifted by e0 quant bytes and e0/8 scale and sum bytes.
+struct XView {
+  const uint8_t* q;
+  const uint8_t* s;
+  const uint8_t* m;
+  int64_t stride;
+};
+
+__host__ __device__ inline XView xview(const uint8_t* row, int K, int e0) {
+  return XView{row + e0, row + q8_scale_offset(K) + e0 / 8, row + q8_sum_offset(K) + e0 / 8,
+               (int64_t)q8_row_bytes(K)};
+}
+
 // Load through an explicit global (address space 1) pointer, so the access
 // is a global_load with an SGPR base rather than a flat load.
 template <typename T>

@@ -12,10 +12,15 @@ constexpr int kMaxPlainJobs = 4;
 constexpr int kMaxExpertBases = 4;
 
 struct MmvqLaunch {
-  // Plain mode (ids == nullptr): job j multiplies w[j] [n[j], k] by xq.
+  // Plain mode (ids == nullptr, groups == 0): job j multiplies w[j] [n[j], k]
+  // by xq.
   // Expert mode (ids != nullptr): job base*n_ids + i multiplies the matrix
   // w[base] + ids[i] * expert_stride by xq (shared) or by the i-th group of
   // m rows of xq (x_per_id), writing y[0] + (base*n_ids + i) * m * n[0].
+  // Grouped mode (groups > 0): job g multiplies rows g*n[0] .. g*n[0]+n[0]-1
+  // of w[0] (expert_stride = n[0] row bytes apart) by elements g*k .. g*k+k-1
+  // of each q8_1 row of width groups*k, writing y[0][t, g*n[0] + r] (output
+  // rows groups*n[0] apart); n_ids == groups, njobs == 1.
   const void* w[kMaxPlainJobs];
   float* y[kMaxPlainJobs];
   int32_t n[kMaxPlainJobs];
@@ -28,9 +33,13 @@ struct MmvqLaunch {
   int64_t expert_stride;
   int32_t* err_flag;
   int32_t* dots;   // non-null: write the int32 (I, M) block sums instead of y (plain, one job)
+  int32_t groups;  // grouped mode when > 0
   int32_t k;
   int32_t m;
 };
+
+// Expert and grouped launches are n_jobs equal-sized jobs.
+inline bool uniform_jobs(const MmvqLaunch& a) { return a.ids != nullptr || a.groups > 0; }
 
 hipError_t launch_q8_1_rows(const void* x, int64_t stride, void* xq, int m, int k,
                             hipStream_t stream);

@@ -124,6 +124,28 @@ def attention_pair_case(m: int, seed: int = 1002, na: int = 1024, nb: int = 512,
 
 
 @dataclass
+class GroupedCase:
+    """Grouped-input product: x [m, groups*k] (the attention output), w
+    [groups*rows, k] (wo_a), output [m, groups*rows]."""
+    w: np.ndarray          # uint8 [groups*rows, k/256, 84]
+    x_bits: np.ndarray     # uint16 [m, groups*k]
+    groups: int
+    rows: int
+    k: int
+    m: int
+
+
+def grouped_case(m: int, seed: int = 1005, groups: int = 8, rows: int = 1024,
+                 k: int = 2048) -> GroupedCase:
+    """wo_a-shaped grouped product (the pages give no group sizes): 8 groups
+    of 1024 rows over 2048-wide slices of a [m, 16384] input ~ N(0,1)."""
+    rng = rng_for(seed, m)
+    w = q2k_blocks(rng, groups * rows, k // Q2K_BLOCK_WEIGHTS)
+    x = bf16_normal(rng, (m, groups * k))
+    return GroupedCase(w=w, x_bits=x, groups=groups, rows=rows, k=k, m=m)
+
+
+@dataclass
 class ExpertCase:
     """Routed-expert decode batch over a resident expert set."""
     n_experts: int

@@ -38,7 +38,7 @@ def test_header_symbols_exported(L):
 
 
 def test_version_and_sizes(L):
-    assert L.q2k_abi_version() == 1
+    assert L.q2k_abi_version() == 2
     assert L.q8_1_rows_bytes(1, 1024) == 1280
     assert L.q8_1_rows_bytes(8, 7168) == 8 * 8960
     assert L.q8_1_rows_bytes(0, 1024) == 0
@@ -78,6 +78,21 @@ def test_pair_validation(L):
     assert L.q2k_mmvq_pair(P, 0x100, 1024, None, 0x10000, 512, Q, 4096, 1, None) == EINVAL
     assert L.q2k_mmvq_pair(P, 0x100, 1024, P, 0x200, 512, Q, 4096, 1, None) == EINVAL  # ya/yb overlap
     assert L.q2k_mmvq_pair(P, 0x100, 1024, P, 0x100000, 512, Q, 4096, 9, None) == ESHAPE
+
+
+def test_grouped_validation(L):
+    # w at P: 8 x 1024 rows of 2048 (5.5 MB); xq at Q; y far above both
+    y = 0x40000000
+    assert L.q2k_mmvq_grouped(P, Q, y, 0, 1024, 2048, 4, None) == ESHAPE
+    assert L.q2k_mmvq_grouped(P, Q, y, 8, 0, 2048, 4, None) == ESHAPE
+    assert L.q2k_mmvq_grouped(P, Q, y, 8, 1024, 2000, 4, None) == ESHAPE
+    assert L.q2k_mmvq_grouped(P, Q, y, 8, 1024, 2048, 9, None) == ESHAPE
+    assert L.q2k_mmvq_grouped(P, Q, y, 1 << 16, 1 << 16, 2048, 1, None) == ESHAPE   # rows >= 2^31
+    assert L.q2k_mmvq_grouped(None, Q, y, 8, 1024, 2048, 4, None) == EINVAL
+    assert L.q2k_mmvq_grouped(P, None, y, 8, 1024, 2048, 4, None) == EINVAL
+    assert L.q2k_mmvq_grouped(P + 2, Q, y, 8, 1024, 2048, 4, None) == EALIGN
+    assert L.q2k_mmvq_grouped(P, Q + 4, y, 8, 1024, 2048, 4, None) == EALIGN
+    assert L.q2k_mmvq_grouped(P, Q, P + 64, 8, 1024, 2048, 4, None) == EINVAL    # y inside w
 
 
 def test_experts_validation(L):

@@ -294,6 +294,37 @@ def test_pair_ragged():
     assert_close(yb.cpu().numpy(), rb, "ragged pair b")
 
 
+# -------------------------------------------------------------- grouped -----
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_grouped_wo_a(m):
+    """8 groups of 1024 rows over 2048-wide slices of x [m, 16384]: the m = 1
+    kernel at m = 1, the matrix cores above (64 workgroups)."""
+    gc = syn.grouped_case(m)
+    xq = q2.q8_1_rows(bf16_dev(gc.x_bits))
+    oq, od = assert_q8_equal(xq, gc.x_bits)
+    y = q2.q2k_mmvq_grouped(dev(gc.w.reshape(-1)), xq, gc.groups, gc.rows, gc.k, m).cpu().numpy()
+    assert_close(y, orc.mmvq_grouped(gc.w, oq, od, gc.groups), f"grouped m={m}")
+
+
+@pytest.mark.parametrize("groups,rows,k,m", [(3, 37, 1280, 3), (5, 16, 256, 1), (2, 130, 9216, 2)])
+def test_grouped_ragged_equals_slices(groups, rows, k, m):
+    """Small and ragged groups (packed-dot kernels, k > 8192 on the wide one):
+    the oracle, and bit-for-bit the plain product of each group's rows with
+    the q8_1 rows of its slice (the kernels' sums do not depend on the grid)."""
+    gc = syn.grouped_case(m, seed=60 + groups, groups=groups, rows=rows, k=k)
+    w = dev(gc.w.reshape(-1))
+    xq = q2.q8_1_rows(bf16_dev(gc.x_bits))
+    oq, od = assert_q8_equal(xq, gc.x_bits)
+    y = q2.q2k_mmvq_grouped(w, xq, groups, rows, k, m).cpu().numpy()
+    assert_close(y, orc.mmvq_grouped(gc.w, oq, od, groups), "grouped ragged")
+    per = rows * (k // 256) * 84
+    for g in range(groups):
+        xs = q2.q8_1_rows(bf16_dev(np.ascontiguousarray(gc.x_bits[:, g * k:(g + 1) * k])))
+        ys = q2.q2k_mmvq(w[g * per:(g + 1) * per], xs, rows, k, m).cpu().numpy()
+        assert np.array_equal(ys.view(np.uint32), y[:, g * rows:(g + 1) * rows].view(np.uint32))
+
+
 # -------------------------------------------------------------- experts -----
 
 POISON = 0x7E   # every byte 0x7E: d = dmin = fp16 0x7E7E, a NaN

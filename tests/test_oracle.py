@@ -362,6 +362,38 @@ def test_pair_and_experts_compose_single():
     assert np.array_equal(yp[0], yb) and np.array_equal(yp[1], yb[::-1])
 
 
+@pytest.mark.parametrize("groups,rows,k,m", [(3, 2, 256, 2), (2, 3, 512, 1)])
+def test_grouped_brute_force_tiny(groups, rows, k, m):
+    """Row g*R + r against elements g*k .. of each input row, element by
+    element from the raw bytes (the brute-force route of one matrix applied to
+    the group's slice)."""
+    gc = syn.grouped_case(m, seed=31 + groups + k, groups=groups, rows=rows, k=k)
+    xq, d8, _ = orc.q8_1_from_bf16_bits(gc.x_bits)
+    y = orc.mmvq_grouped(gc.w, xq, d8, groups)
+    assert y.shape == (m, groups * rows)
+    for g in range(groups):
+        yb = _brute_force_y(gc.w[g * rows:(g + 1) * rows], gc.x_bits[:, g * k:(g + 1) * k])
+        assert np.allclose(y[:, g * rows:(g + 1) * rows], yb, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_closed_forms():
+    """One group equals the plain product; with W = 3 everywhere and x = 127
+    only in slice g0 (zero elsewhere), rows of group g0 are 3*127*k and every
+    other row is exactly 0."""
+    gc = syn.grouped_case(2, seed=40, groups=1, rows=5, k=512)
+    xq, d8, _ = orc.q8_1_from_bf16_bits(gc.x_bits)
+    assert np.array_equal(orc.mmvq_grouped(gc.w, xq, d8, 1), orc.mmvq(gc.w, xq, d8))
+    groups, rows, k, g0 = 4, 3, 256, 2
+    w = _const_matrix(groups * rows, k // 256, 0x01, 0xFF, 0x3C00, 0x0000)
+    x = np.zeros((1, groups * k), dtype=np.float32)
+    x[0, g0 * k:(g0 + 1) * k] = 127.0
+    xq, d8, _ = orc.q8_1_quantize(x)
+    y = orc.mmvq_grouped(w, xq, d8, groups)
+    want = np.zeros((1, groups * rows))
+    want[0, g0 * rows:(g0 + 1) * rows] = 3 * 127 * k
+    assert np.array_equal(y, want)
+
+
 # ----------------------------------------------------------- SwiGLU / gate --
 
 def test_swiglu_against_torch_silu():
