@@ -156,6 +156,81 @@ def bench_grouped(torch, q2, syn, dev, copies_n: int = 64):
     return out
 
 
+def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
+    """The engram step on the device, one token per step: n-gram hash (2
+    hashed layers, 3-grams, 4 heads = 8 row ids), gather + dequantisation of
+    8 table rows (500 000-row table), q8_1 of the [1, 2048] row, the wkv
+    product [20480, 2048] (80 rotating copies, 1.1 GB) and the gate on
+    [1, 4, 4096]; graphs of 16 steps, HIP events around the replays. The hash
+    alone is timed the same way, for one decode token and a 4096-token
+    prefill."""
+    e = syn.engram_step_case()
+    hc = syn.engram_hash_case(seqlen=4096)
+    tm, mu, pr, of = (torch.from_numpy(a).to(dev) for a in
+                      (hc.token_map, hc.multipliers, hc.primes, hc.offsets))
+    cache = torch.zeros(8192, dtype=torch.int64, device=dev)
+    toks = torch.from_numpy(hc.tokens).to(dev)
+    table = torch.from_numpy(e.table.reshape(-1)).to(dev)
+    w0 = torch.from_numpy(e.wkv.reshape(-1)).to(dev)
+    copies = [w0] + [w0.clone() for _ in range(copies_n - 1)]
+    h = torch.from_numpy(e.h).to(dev)
+    qk = torch.from_numpy(e.qk).to(dev)
+    ids = torch.empty((2, 1, 8), dtype=torch.int64, device=dev)
+    rows = torch.empty((8, 256), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty(q2.q8_1_rows_bytes(1, 2048), dtype=torch.uint8, device=dev)
+    n_out = e.dim * (e.hc + 1)
+    kv = torch.empty((1, n_out), dtype=torch.float32, device=dev)
+    # prefill positions 0..4095 once so the decode steps see a real look-back
+    q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks, 0)
+
+    def step(i):
+        q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks[i % 64:i % 64 + 1], 4096 + (i % 64), out=ids)
+        q2.q2k_dequant_rows(table, 500000, ids[1].reshape(-1), 8, out=rows)
+        q2.q8_1_rows(rows.view(1, 2048), out=xq)
+        q2.q2k_mmvq(copies[i % copies_n], xq, n_out, 2048, 1, out=kv)
+        q2.engram_gate(h, kv, qk, e.eps)
+
+    def timed(fn, launches, reps=20):
+        stream = torch.cuda.Stream()
+        graphs = []
+        torch.cuda.synchronize()
+        for c0 in range(0, launches, 16):
+            with torch.cuda.stream(stream):
+                for i in range(16):
+                    fn(c0 + i)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(16):
+                    fn(c0 + i)
+            graphs.append(g)
+        with torch.cuda.stream(stream):
+            for g in graphs:
+                g.replay()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(reps):
+                for g in graphs:
+                    g.replay()
+            ev1.record(stream)
+            ev1.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / (reps * launches)
+
+    us_step = timed(step, copies_n)
+    us_hash1 = timed(lambda i: q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks[i % 64:i % 64 + 1],
+                                              4096 + (i % 64), out=ids), 16)
+    pre = torch.empty((2, 4096, 8), dtype=torch.int64, device=dev)
+    us_pre = timed(lambda i: q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks, 0, out=pre), 16)
+    wkv_bytes = w0.numel()
+    return {"workload": "engram step, one token: hash -> 8-row gather -> q8_1 -> wkv Q2_K "
+                        "[20480, 2048] -> gate [1, 4, 4096]; 80 rotating wkv copies",
+            "us_per_step": round(us_step, 3), "tokens_per_s": round(1e6 / us_step, 1),
+            "wkv_bytes": wkv_bytes,
+            "wkv_gbs_at_step_time": round(wkv_bytes / us_step / 1e3, 1),
+            "hash_decode_us": round(us_hash1, 3), "hash_prefill_4096_us": round(us_pre, 3)}
+
+
 def run(args):
     import torch
 
@@ -297,6 +372,7 @@ def run(args):
     del copies
     torch.cuda.synchronize()
     line["grouped"] = bench_grouped(torch, q2, syn, dev)
+    line["engram_step"] = bench_engram(torch, q2, syn, dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -194,6 +194,41 @@ Q2K_API int32_t q2k_dequant_rows(const void* table_dev, int64_t n_table_rows,
 Q2K_API int32_t engram_gate(float* h_dev, const float* kv_dev, const float* qk_dev,
                     int32_t t, int32_t hc, int32_t dim, float eps, void* stream);
 
+/* Engram n-gram hash: the row ids each hashed layer gathers (engram_v41.rs,
+ * EngramHasher::hash and EngramHasher::layer_row_ids; the tables are
+ * EngramHashTables). The pages run it on the host; here it runs on the
+ * device next to the table.
+ *   token_map_dev    : int64 [vocab] compressed id per token id, -1 = unmapped.
+ *   multipliers_dev  : int64 [n_layers, max_ngram].
+ *   primes_dev       : int64 [n_layers, max_ngram - 1, n_heads], each > 0.
+ *   offsets_dev      : int64 [n_layers, (max_ngram - 1) * n_heads].
+ *   cache_dev        : int64 [cache_len], the sequence's compressed ids by
+ *                      position (the hasher state). Positions < start_pos are
+ *                      read; positions start_pos .. start_pos+seqlen-1 are
+ *                      written. Zero it for a new sequence.
+ *   ids_dev          : int32 [seqlen] token ids at positions start_pos.. .
+ *   out_dev          : int64 [n_layers][seqlen][cols], cols = (max_ngram-1) *
+ *                      n_heads: layer l's ids are one contiguous [seqlen, cols]
+ *                      array (token-major, as layer_row_ids orders them), ready
+ *                      for q2k_dequant_rows.
+ * Row id (s, l, (i-1)*n_heads + h) for position p = start_pos + s: window
+ * tokens tok[j] = compressed id of position p - j (position 0 when p < j),
+ * pad_id from the first j with p < j or an unmapped id on; rolling =
+ * tok[0]*mult[l][0], then rolling ^= tok[i]*mult[l][i] (64-bit wrapping);
+ * id = (rolling mod primes[l][i-1][h], in [0, prime)) + offsets[l][col].
+ * A token id outside [0, vocab) (the pages refuse the call) or a prime <= 0
+ * writes -1 for every row id whose window reads it and stores 1 into the
+ * nullable *err_flag_dev. Q2K_ESHAPE: vocab < 1, n_layers outside 1..64,
+ * max_ngram outside 2..8, n_heads outside 1..64, seqlen < 1, positions past
+ * cache_len; Q2K_EINVAL: null pointers, out or cache overlapping an input;
+ * Q2K_EALIGN: 64-bit arrays not 8-byte aligned, ids not 4-byte aligned. */
+Q2K_API int32_t engram_hash(const int64_t* token_map_dev, int64_t vocab,
+                         const int64_t* multipliers_dev, const int64_t* primes_dev,
+                         const int64_t* offsets_dev, int32_t n_layers, int32_t max_ngram,
+                         int32_t n_heads, int64_t pad_id, int64_t* cache_dev, int64_t cache_len,
+                         const int32_t* ids_dev, int32_t seqlen, int64_t start_pos,
+                         int64_t* out_dev, int32_t* err_flag_dev, void* stream);
+
 /* Integer stage of q2k_mmvq, exported for exact checking (same device
  * code): out_dev int32 [m, n, k/32, 2] receives, per token t, row r and
  * q8 block c, I = sum sc*q*xq and M = sum m*xq over the block's 32 values.

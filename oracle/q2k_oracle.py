@@ -30,6 +30,9 @@ rustdoc source views of the metrale engine: ``engram_v41/apply.rs``,
 * Row dequantisation to bf16 (``dequant_q2_k_to_bf16``,
   ``EngramV41::rows_from_q2k``).
 * SwiGLU then q8_1 re-quantisation (``kquant_swiglu_q8_1_rows_bf16``).
+* The engram n-gram hash (``EngramHasher::hash``): window of compressed
+  token ids, rolling xor of wrapping products, Euclidean remainder by a
+  prime per head, plus an offset per column.
 * The engram gate (``engram_v41_gate``; module doc step 4 "normalised dot of
   stream against key, signed-sqrt sigmoid, h += gate * value"; ``qk`` is
   ``q_weight * k_weight``).
@@ -316,6 +319,73 @@ def mmvq_grouped(w: np.ndarray, xq: np.ndarray, d8: np.ndarray, groups: int) -> 
     for g in range(groups):
         y[:, g * rows:(g + 1) * rows] = a[:, g * k:(g + 1) * k] @ wf[g * rows:(g + 1) * rows].T
     return y
+
+
+# ----------------------------------------------------------------------------
+# Engram n-gram hash (integers only)
+# ----------------------------------------------------------------------------
+
+_U64 = (1 << 64) - 1
+
+
+def _as_i64(v: int) -> int:
+    """Two's-complement reading of the low 64 bits of a Python int."""
+    v &= _U64
+    return v - (1 << 64) if v >> 63 else v
+
+
+def engram_hash(token_map, multipliers, primes, offsets, pad_id: int, n_heads: int,
+                cache, input_ids, start_pos: int):
+    """The engram n-gram hash of one sequence (engram_v41.rs,
+    ``EngramHasher::hash``), in plain Python integers with explicit 64-bit
+    wrap-around.
+
+    ``token_map``: compressed id per vocabulary id (-1 = unmapped);
+    ``multipliers[l][i]`` (i < max_ngram); ``primes[l][i-1][h]``;
+    ``offsets[l][(i-1)*n_heads + h]``; ``cache``: compressed ids of the
+    positions already seen (at least ``start_pos + len(input_ids)`` long; its
+    entries from ``start_pos`` on are overwritten here).
+
+    Steps, for each new token s at position pos = start_pos + s:
+      1. cache[pos] = token_map[id] (an id outside the map is an error);
+      2. window tokens tok[i] = cache[pos - i] for i < max_ngram, except that
+         from the first i with pos < i or cache[pos - i] == -1 on, every
+         tok[i] is pad_id;
+      3. per hashed layer l: rolling = tok[0]*mult[l][0], then for i >= 1
+         rolling ^= tok[i]*mult[l][i] (64-bit wrapping products) and, for each
+         head h, row id = (rolling mod primes[l][i-1][h], in [0, prime)) +
+         offsets[l][(i-1)*n_heads + h].
+    Returns (ids [seqlen][n_layers][(max_ngram-1)*n_heads] as Python ints,
+    the updated cache)."""
+    cache = list(cache)
+    n_layers = len(multipliers)
+    ng = len(multipliers[0])
+    cols = (ng - 1) * n_heads
+    for s, tid in enumerate(input_ids):
+        if not 0 <= tid < len(token_map):
+            raise ValueError(f"token {tid} outside token_map")
+        cache[start_pos + s] = token_map[tid]
+    out = []
+    for s in range(len(input_ids)):
+        pos = start_pos + s
+        tok = []
+        blocked = False
+        for i in range(ng):
+            src = cache[max(pos - i, 0)]
+            blocked = blocked or pos < i or src == -1
+            tok.append(pad_id if blocked else src)
+        per_layer = []
+        for l in range(n_layers):
+            row = [0] * cols
+            rolling = _as_i64(tok[0] * multipliers[l][0])
+            for i in range(1, ng):
+                rolling = _as_i64(rolling ^ _as_i64(tok[i] * multipliers[l][i]))
+                for h in range(n_heads):
+                    p = primes[l][i - 1][h]
+                    row[(i - 1) * n_heads + h] = _as_i64(rolling % p + offsets[l][(i - 1) * n_heads + h])
+            per_layer.append(row)
+        out.append(per_layer)
+    return out, cache
 
 
 # ----------------------------------------------------------------------------

@@ -42,6 +42,8 @@ SIGNATURES = {
     "q2k_dequant_rows": (_I32, [_VP, _I64, _VP, _I32, _VP, _VP, _VP]),
     "engram_gate": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _F32, _VP]),
     "q2k_block_dots": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
+    "engram_hash": (_I32, [_VP, _I64, _VP, _VP, _VP, _I32, _I32, _I32, _I64, _VP, _I64, _VP, _I32,
+                           _I64, _VP, _VP, _VP]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -219,6 +221,33 @@ def engram_gate(h: torch.Tensor, kv: torch.Tensor, qk: torch.Tensor, eps: float)
     _check("engram_gate", lib().engram_gate(_contig(h, "h"), _contig(kv, "kv"), _contig(qk, "qk"),
                                             t, hc, dim, float(eps), _stream()))
     return h
+
+
+def engram_hash(token_map: torch.Tensor, multipliers: torch.Tensor, primes: torch.Tensor,
+                offsets: torch.Tensor, pad_id: int, cache: torch.Tensor, ids: torch.Tensor,
+                start_pos: int, out: Optional[torch.Tensor] = None,
+                err_flag: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int64 [n_layers, seqlen, (max_ngram-1)*n_heads] engram row ids for the
+    int32 token ids at positions start_pos.. (the int64 ``cache`` is updated)."""
+    for name, t in (("token_map", token_map), ("multipliers", multipliers), ("primes", primes),
+                    ("offsets", offsets), ("cache", cache)):
+        if t.dtype != torch.int64:
+            raise ValueError(f"{name} must be int64")
+    if ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    n_layers, max_ngram = multipliers.shape
+    n_heads = primes.shape[-1]
+    cols = (max_ngram - 1) * n_heads
+    seqlen = ids.numel()
+    if out is None:
+        out = torch.empty((n_layers, seqlen, cols), dtype=torch.int64, device=ids.device)
+    flag = 0 if err_flag is None else _contig(err_flag, "err_flag")
+    _check("engram_hash", lib().engram_hash(
+        _contig(token_map, "token_map"), token_map.numel(), _contig(multipliers, "multipliers"),
+        _contig(primes, "primes"), _contig(offsets, "offsets"), n_layers, max_ngram, n_heads,
+        pad_id, _contig(cache, "cache"), cache.numel(), _contig(ids, "ids"), seqlen, start_pos,
+        _contig(out, "out"), flag or None, _stream()))
+    return out
 
 
 def q2k_block_dots(w: torch.Tensor, xq: torch.Tensor, n: int, k: int, m: int,

@@ -289,6 +289,42 @@ int32_t engram_gate(float* h_dev, const float* kv_dev, const float* qk_dev, int3
   return launched(q2k::launch_engram_gate(h_dev, kv_dev, qk_dev, t, hc, dim, eps, (hipStream_t)stream), fn);
 }
 
+int32_t engram_hash(const int64_t* token_map_dev, int64_t vocab, const int64_t* multipliers_dev,
+                    const int64_t* primes_dev, const int64_t* offsets_dev, int32_t n_layers,
+                    int32_t max_ngram, int32_t n_heads, int64_t pad_id, int64_t* cache_dev,
+                    int64_t cache_len, const int32_t* ids_dev, int32_t seqlen, int64_t start_pos,
+                    int64_t* out_dev, int32_t* err_flag_dev, void* stream) {
+  const char* fn = "engram_hash";
+  if (!token_map_dev || !multipliers_dev || !primes_dev || !offsets_dev || !cache_dev || !ids_dev ||
+      !out_dev)
+    return fail(Q2K_EINVAL, "%s: null pointer", fn);
+  if (vocab < 1) return fail(Q2K_ESHAPE, "%s: vocab = %lld < 1", fn, (long long)vocab);
+  if (n_layers < 1 || n_layers > 64) return fail(Q2K_ESHAPE, "%s: n_layers = %d outside 1..64", fn, n_layers);
+  if (max_ngram < 2 || max_ngram > 8) return fail(Q2K_ESHAPE, "%s: max_ngram = %d outside 2..8", fn, max_ngram);
+  if (n_heads < 1 || n_heads > 64) return fail(Q2K_ESHAPE, "%s: n_heads = %d outside 1..64", fn, n_heads);
+  if (seqlen < 1) return fail(Q2K_ESHAPE, "%s: seqlen = %d < 1", fn, seqlen);
+  if (start_pos < 0 || cache_len < start_pos + seqlen)
+    return fail(Q2K_ESHAPE, "%s: positions %lld..%lld outside the cache of %lld", fn, (long long)start_pos,
+                (long long)(start_pos + seqlen), (long long)cache_len);
+  if ((int64_t)seqlen * n_layers > INT32_MAX) return fail(Q2K_ESHAPE, "%s: seqlen * n_layers too large", fn);
+  if (!aligned(token_map_dev, 8) || !aligned(multipliers_dev, 8) || !aligned(primes_dev, 8) ||
+      !aligned(offsets_dev, 8) || !aligned(cache_dev, 8) || !aligned(out_dev, 8) || !aligned(ids_dev, 4))
+    return fail(Q2K_EALIGN, "%s: 64-bit arrays must be 8-byte aligned, ids 4-byte aligned", fn);
+  const int64_t cols = (int64_t)(max_ngram - 1) * n_heads;
+  const size_t out_bytes = (size_t)n_layers * seqlen * cols * 8;
+  const size_t cache_bytes = (size_t)cache_len * 8;
+  if (overlap(out_dev, out_bytes, cache_dev, cache_bytes) ||
+      overlap(out_dev, out_bytes, token_map_dev, (size_t)vocab * 8) ||
+      overlap(out_dev, out_bytes, ids_dev, (size_t)seqlen * 4) ||
+      overlap(cache_dev, cache_bytes, token_map_dev, (size_t)vocab * 8) ||
+      overlap(cache_dev, cache_bytes, ids_dev, (size_t)seqlen * 4))
+    return fail(Q2K_EINVAL, "%s: out or cache overlaps another argument", fn);
+  return launched(q2k::launch_engram_hash(token_map_dev, vocab, multipliers_dev, primes_dev, offsets_dev,
+                                          n_layers, max_ngram, n_heads, pad_id, cache_dev, ids_dev, seqlen,
+                                          start_pos, out_dev, err_flag_dev, (hipStream_t)stream),
+                  fn);
+}
+
 int32_t q2k_block_dots(const void* w_dev, const void* xq_dev, int32_t* out_dev, int32_t n,
                        int32_t k, int32_t m, void* stream) {
   const char* fn = "q2k_block_dots";

@@ -9,6 +9,10 @@
 // Gate (engram_v41/apply.rs, engram_v41_gate with grid [T, hc]; engram_v41.rs
 // module doc step 4): one 256-thread workgroup per (token, stream) forms
 // three sums over dim in a fixed order, then updates the stream in place.
+//
+// N-gram hash (engram_v41.rs, EngramHasher::hash, which the pages run on the
+// host): one thread per (position, hashed layer), so the row ids are made on
+// the device next to the table they index.
 #include "q2k_device.h"
 #include "q2k_launch.h"
 
@@ -89,6 +93,86 @@ __global__ __launch_bounds__(256) void engram_gate_kernel(float* __restrict__ h,
   const float sg = copysignf(sqrtf(fabsf(s)), s);
   const float g = 1.0f / (1.0f + expf(-sg));
   for (int i = threadIdx.x; i < dim; i += 256) hs[i] = fmaf(g, val[i], hs[i]);
+}
+
+// Row ids of the engram n-gram hash. Thread (s, l): position pos = start_pos + s,
+// hashed layer l. Window token i (i < ng) is the compressed id of position
+// pos - i (position 0 when pos < i): from this call's token ids when that
+// position is >= start_pos, else from the cache; from the first i with
+// pos < i or an unmapped (-1) id on, the token is pad_id. Then
+// rolling = tok[0]*mult[l][0], rolling ^= tok[i]*mult[l][i] (64-bit
+// wrapping), and row id (i, h) = (rolling mod prime, in [0, prime)) + offset.
+// Output layout [n_layers][seqlen][cols]. The thread of layer 0 stores the
+// compressed id of its position into the cache (only positions >= start_pos
+// are written; only positions < start_pos are read from the cache).
+// A token id outside [0, vocab), or a prime <= 0, gives -1 for every row id
+// whose window reads it, -1 in the cache, and *err_flag = 1.
+constexpr int kMaxNgram = 8;
+
+__global__ __launch_bounds__(256) void engram_hash_kernel(
+    const int64_t* __restrict__ token_map, int64_t vocab, const int64_t* __restrict__ mult,
+    const int64_t* __restrict__ primes, const int64_t* __restrict__ offsets, int n_layers, int ng,
+    int n_heads, int64_t pad_id, int64_t* cache, const int32_t* __restrict__ ids, int seqlen,
+    int64_t start_pos, int64_t* __restrict__ out, int32_t* err_flag) {
+  const int tid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= seqlen * n_layers) return;
+  const int s = tid / n_layers;
+  const int l = tid - s * n_layers;
+  const int64_t pos = start_pos + s;
+  const int cols = (ng - 1) * n_heads;
+  bool ok = true;
+  int64_t tok[kMaxNgram];
+  bool blocked = false;
+  for (int i = 0; i < ng; ++i) {
+    const int64_t p = pos >= i ? pos - i : 0;
+    int64_t src;
+    if (p >= start_pos) {
+      const int32_t id = ids[p - start_pos];
+      if (id < 0 || id >= vocab) {
+        ok = false;
+        src = -1;
+      } else {
+        src = token_map[id];
+      }
+    } else {
+      src = cache[p];
+    }
+    if (i == 0 && l == 0) cache[pos] = src;
+    blocked = blocked || pos < i || src == -1;
+    tok[i] = blocked ? pad_id : src;
+  }
+  const int64_t* ml = mult + (int64_t)l * ng;
+  uint64_t rolling = (uint64_t)tok[0] * (uint64_t)ml[0];
+  int64_t* o = out + ((int64_t)l * seqlen + s) * cols;
+  for (int i = 1; i < ng; ++i) {
+    rolling ^= (uint64_t)tok[i] * (uint64_t)ml[i];
+    for (int h = 0; h < n_heads; ++h) {
+      const int col = (i - 1) * n_heads + h;
+      const int64_t pr = primes[((int64_t)l * (ng - 1) + (i - 1)) * n_heads + h];
+      int64_t v = -1;
+      if (ok && pr > 0) {
+        int64_t r = (int64_t)rolling % pr;
+        if (r < 0) r += pr;
+        v = (int64_t)((uint64_t)r + (uint64_t)offsets[(int64_t)l * cols + col]);
+      } else {
+        ok = false;
+      }
+      o[col] = v;
+    }
+  }
+  if (!ok && err_flag != nullptr) *err_flag = 1;
+}
+
+hipError_t launch_engram_hash(const int64_t* token_map, int64_t vocab, const int64_t* mult,
+                              const int64_t* primes, const int64_t* offsets, int n_layers, int ng,
+                              int n_heads, int64_t pad_id, int64_t* cache, const int32_t* ids,
+                              int seqlen, int64_t start_pos, int64_t* out, int32_t* err_flag,
+                              hipStream_t stream) {
+  const int64_t threads = (int64_t)seqlen * n_layers;
+  hipLaunchKernelGGL(engram_hash_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     token_map, vocab, mult, primes, offsets, n_layers, ng, n_heads, pad_id, cache,
+                     ids, seqlen, start_pos, out, err_flag);
+  return hipGetLastError();
 }
 
 hipError_t launch_dequant_rows(const void* table, int64_t n_table_rows, const int64_t* ids,

@@ -55,5 +55,10 @@ hipError_t launch_dequant_rows(const void* table, int64_t n_table_rows, const in
                                int n_rows, void* out, int32_t* err_flag, hipStream_t stream);
 hipError_t launch_engram_gate(float* h, const float* kv, const float* qk, int t, int hc, int dim,
                               float eps, hipStream_t stream);
+hipError_t launch_engram_hash(const int64_t* token_map, int64_t vocab, const int64_t* mult,
+                              const int64_t* primes, const int64_t* offsets, int n_layers, int ng,
+                              int n_heads, int64_t pad_id, int64_t* cache, const int32_t* ids,
+                              int seqlen, int64_t start_pos, int64_t* out, int32_t* err_flag,
+                              hipStream_t stream);
 
 }  // namespace q2k

@@ -146,6 +146,60 @@ def grouped_case(m: int, seed: int = 1005, groups: int = 8, rows: int = 1024,
 
 
 @dataclass
+class EngramHashCase:
+    """Hash tables of the engram n-gram hash and a token sequence."""
+    token_map: np.ndarray      # int64 [vocab]; -1 = unmapped
+    multipliers: np.ndarray    # int64 [n_layers, max_ngram]
+    primes: np.ndarray         # int64 [n_layers, max_ngram - 1, n_heads]
+    offsets: np.ndarray        # int64 [n_layers, (max_ngram - 1) * n_heads]
+    pad_id: int
+    n_heads: int
+    tokens: np.ndarray         # int32 [seqlen]
+
+
+def _primes_from(start: int, count: int) -> list:
+    out, v = [], start
+    while len(out) < count:
+        v += 1
+        if v > 1 and all(v % d for d in range(2, int(v ** 0.5) + 1)):
+            out.append(v)
+    return out
+
+
+def engram_hash_case(seed: int = 1006, vocab: int = 4096, n_layers: int = 2, max_ngram: int = 3,
+                     n_heads: int = 4, seqlen: int = 64, table_rows: int = 500000,
+                     unmapped: float = 0.05) -> EngramHashCase:
+    """Synthetic tables (the real ones ship in the GGUF metadata): compressed
+    ids are a random map of the vocabulary with a share of unmapped (-1)
+    entries; multipliers random non-negative 63-bit values; one distinct
+    prime per (layer, column) near table_rows / (layers * columns); offsets
+    lay the columns' ranges end to end, so every row id falls in
+    [0, table_rows)."""
+    rng = rng_for(seed)
+    cols = (max_ngram - 1) * n_heads
+    compressed = max(2, vocab * 3 // 4)
+    token_map = rng.integers(0, compressed, size=vocab, dtype=np.int64)
+    token_map[rng.random(vocab) < unmapped] = -1
+    pad_token = int(rng.integers(0, vocab))
+    token_map[pad_token] = int(rng.integers(0, compressed))
+    multipliers = rng.integers(1, 1 << 63, size=(n_layers, max_ngram), dtype=np.int64)
+    per = table_rows // (n_layers * cols)
+    plist = _primes_from(per - 2000, n_layers * cols)
+    primes = np.array(plist, dtype=np.int64).reshape(n_layers, max_ngram - 1, n_heads)
+    flat = primes.reshape(n_layers, cols)
+    offsets = np.zeros((n_layers, cols), dtype=np.int64)
+    acc = 0
+    for l in range(n_layers):
+        for c in range(cols):
+            offsets[l, c] = acc
+            acc += int(flat[l, c])
+    tokens = rng.integers(0, vocab, size=seqlen, dtype=np.int64).astype(np.int32)
+    return EngramHashCase(token_map=token_map, multipliers=multipliers, primes=primes,
+                          offsets=offsets, pad_id=int(token_map[pad_token]), n_heads=n_heads,
+                          tokens=tokens)
+
+
+@dataclass
 class ExpertCase:
     """Routed-expert decode batch over a resident expert set."""
     n_experts: int

@@ -95,6 +95,31 @@ def test_grouped_validation(L):
     assert L.q2k_mmvq_grouped(P, Q, P + 64, 8, 1024, 2048, 4, None) == EINVAL    # y inside w
 
 
+def test_engram_hash_validation(L):
+    T = 0x7f0002000000
+
+    def call(**kw):
+        a = dict(tm=T, vocab=4096, mult=T + 0x100000, primes=T + 0x200000, offs=T + 0x300000,
+                 nl=2, ng=3, nh=4, pad=0, cache=T + 0x400000, cache_len=128, ids=T + 0x500000,
+                 seqlen=64, start=0, out=T + 0x600000)
+        a.update(kw)
+        return L.engram_hash(a["tm"], a["vocab"], a["mult"], a["primes"], a["offs"], a["nl"],
+                             a["ng"], a["nh"], a["pad"], a["cache"], a["cache_len"], a["ids"],
+                             a["seqlen"], a["start"], a["out"], None, None)
+    assert call(tm=None) == EINVAL
+    assert call(vocab=0) == ESHAPE
+    assert call(nl=0) == ESHAPE
+    assert call(ng=1) == ESHAPE
+    assert call(ng=9) == ESHAPE
+    assert call(nh=0) == ESHAPE
+    assert call(seqlen=0) == ESHAPE
+    assert call(start=100) == ESHAPE                  # 100 + 64 > 128
+    assert call(start=-1) == ESHAPE
+    assert call(cache=T + 0x400004) == EALIGN
+    assert call(ids=T + 0x500002) == EALIGN
+    assert call(out=T + 0x400000) == EINVAL           # out on the cache
+
+
 def test_experts_validation(L):
     arr = (ctypes.c_void_p * 2)(P, Q)
     ok = dict(stride=1024 * 16 * 84, n_experts=4, ids=0x200000, n_ids=8, xq=0x300000,

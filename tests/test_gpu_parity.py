@@ -506,6 +506,79 @@ def test_engram_step(engram):
     assert_close(hd.cpu().numpy(), orc.engram_gate(e.h, ref_kv, e.qk, e.eps), "gate (end to end)")
 
 
+# ---------------------------------------------------- engram n-gram hash ---
+
+def _hash_tables_dev(hc):
+    return (dev(hc.token_map), dev(hc.multipliers), dev(hc.primes), dev(hc.offsets))
+
+
+def _oracle_hash_layer_major(hc, cache, tokens, start):
+    ids, cache = orc.engram_hash(hc.token_map.tolist(), hc.multipliers.tolist(), hc.primes.tolist(),
+                                 hc.offsets.tolist(), hc.pad_id, hc.n_heads, cache, tokens, start)
+    return np.array(ids, dtype=np.int64).transpose(1, 0, 2), cache
+
+
+def test_engram_hash_prefill_then_decode():
+    """Prefill of 64 positions, then single-token decode steps carrying the
+    device cache: every row id and the cache bit-exact against the oracle."""
+    hc = syn.engram_hash_case(seqlen=80)
+    tm, mu, pr, of = _hash_tables_dev(hc)
+    cache = torch.zeros(128, dtype=torch.int64, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, dev(hc.tokens[:64]), 0, err_flag=flag)
+    want, ocache = _oracle_hash_layer_major(hc, [0] * 128, hc.tokens[:64].tolist(), 0)
+    assert np.array_equal(got.cpu().numpy(), want)
+    for s in range(64, 80):
+        got = q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, dev(hc.tokens[s:s + 1]), s, err_flag=flag)
+        want, ocache = _oracle_hash_layer_major(hc, ocache, [int(hc.tokens[s])], s)
+        assert np.array_equal(got.cpu().numpy(), want), f"decode step {s}"
+    assert np.array_equal(cache.cpu().numpy(), np.array(ocache, dtype=np.int64))
+    assert int(flag.item()) == 0
+
+
+def test_engram_hash_wide_ngram_and_large_ids():
+    """max_ngram 6, 16 heads, compressed ids near 2^62 (products wrap)."""
+    hc = syn.engram_hash_case(seed=8, vocab=512, n_layers=3, max_ngram=6, n_heads=16, seqlen=40)
+    hc.token_map[hc.token_map >= 0] += 1 << 62
+    tm, mu, pr, of = _hash_tables_dev(hc)
+    cache = torch.zeros(40, dtype=torch.int64, device="cuda")
+    got = q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, dev(hc.tokens), 0)
+    want, _ = _oracle_hash_layer_major(hc, [0] * 40, hc.tokens.tolist(), 0)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_engram_hash_bad_token_flags_its_windows():
+    hc = syn.engram_hash_case(seed=9, seqlen=12)
+    toks = hc.tokens.copy()
+    toks[5] = len(hc.token_map) + 3                        # outside the map
+    tm, mu, pr, of = _hash_tables_dev(hc)
+    cache = torch.zeros(12, dtype=torch.int64, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, dev(toks), 0, err_flag=flag).cpu().numpy()
+    assert int(flag.item()) == 1
+    assert np.all(got[:, 5:8] == -1)                       # windows of 3 reading position 5
+    want, _ = _oracle_hash_layer_major(hc, [0] * 12, toks[:5].tolist(), 0)
+    assert np.array_equal(got[:, :5], want)
+    assert int(cache[5].item()) == -1
+
+
+def test_engram_hashed_rows_gather():
+    """Hashed ids of one layer feed the row gather directly (bit-exact)."""
+    hc = syn.engram_hash_case(seqlen=16)
+    table = syn.q2k_blocks(syn.rng_for(1001, 7), 500000, 1)
+    tm, mu, pr, of = _hash_tables_dev(hc)
+    cache = torch.zeros(16, dtype=torch.int64, device="cuda")
+    ids = q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, dev(hc.tokens), 0)
+    layer1 = ids[1].reshape(-1)                           # [tokens * cols]
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rows = q2.q2k_dequant_rows(dev(table.reshape(-1)), 500000, layer1, layer1.numel(), err_flag=flag)
+    want_ids = _oracle_hash_layer_major(hc, [0] * 16, hc.tokens.tolist(), 0)[0][1].reshape(-1)
+    assert np.array_equal(layer1.cpu().numpy(), want_ids)
+    ref = orc.dequant_rows_bf16_bits(table[:, 0], want_ids)
+    assert np.array_equal(rows.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+    assert int(flag.item()) == 0
+
+
 # ------------------------------------------------------- full-size verify ---
 
 @pytest.fixture(scope="module")

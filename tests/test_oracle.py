@@ -394,6 +394,93 @@ def test_grouped_closed_forms():
     assert np.array_equal(y, want)
 
 
+# ------------------------------------------------------- engram n-gram hash --
+
+def _hash_args(hc):
+    return (hc.token_map.tolist(), hc.multipliers.tolist(), hc.primes.tolist(),
+            hc.offsets.tolist(), hc.pad_id, hc.n_heads)
+
+
+def test_engram_hash_hand_example():
+    """max_ngram 2, one head, one layer: mult (3, 5), prime 7, offset 100.
+    Tokens map 0->4, 1->6, 2->-1; pad = 9.
+    pos 0 (id 0): tok = (4, pad 9) -> 12 ^ 45 = 33 -> 33 % 7 = 5 -> 105.
+    pos 1 (id 1): tok = (6, 4) -> 18 ^ 20 = 6 -> 106.
+    pos 2 (id 2): tok[0] = -1 is unmapped, so every tok is pad: 27 ^ 45 = 54 -> 54 % 7 = 5 -> 105.
+    pos 3 (id 0): tok = (4, pad, since cache[2] is -1) -> 105."""
+    args = ([4, 6, -1], [[3, 5]], [[[7]]], [[100]], 9, 1)
+    ids, cache = orc.engram_hash(*args, [0] * 4, [0, 1, 2, 0], 0)
+    assert [r[0][0] for r in ids] == [105, 106, 105, 105]
+    assert cache == [4, 6, -1, 4]
+
+
+def test_engram_hash_wraps_like_int64():
+    """64-bit wrapping products and xor checked against numpy int64."""
+    hc = syn.engram_hash_case(seed=3, vocab=64, seqlen=20)
+    hc.token_map[:] = np.abs(hc.token_map) * (1 << 40) + 12345        # large compressed ids
+    ids, _ = orc.engram_hash(*_hash_args(hc), [0] * 20, hc.tokens.tolist(), 0)
+    mult = hc.multipliers
+    with np.errstate(over="ignore"):
+        for s in range(20):
+            tok = [np.int64(hc.pad_id)] * 3
+            for i in range(3):
+                if s - i < 0:
+                    break
+                tok[i] = np.int64(hc.token_map[hc.tokens[s - i]])
+            for l in range(mult.shape[0]):
+                rolling = tok[0] * mult[l, 0]
+                for i in range(1, 3):
+                    rolling = rolling ^ (tok[i] * mult[l, i])
+                    for h in range(hc.n_heads):
+                        p = int(hc.primes[l, i - 1, h])
+                        want = int(rolling) % p + int(hc.offsets[l, (i - 1) * hc.n_heads + h])
+                        assert ids[s][l][(i - 1) * hc.n_heads + h] == want
+
+
+def test_engram_hash_ranges_and_blocking():
+    hc = syn.engram_hash_case(seed=4, seqlen=200)
+    ids, cache = orc.engram_hash(*_hash_args(hc), [0] * 200, hc.tokens.tolist(), 0)
+    cols = 2 * hc.n_heads
+    for s in range(200):
+        for l in range(2):
+            for c in range(cols):
+                p = int(hc.primes[l].reshape(-1)[c])
+                lo = int(hc.offsets[l, c])
+                assert lo <= ids[s][l][c] < lo + p
+    # An unmapped token U blocks the rest of every window that reaches it:
+    # in [A, U, B, C], position 2 sees (B, pad, pad) like position 0 of [B],
+    # and position 3 sees (C, B, pad) like position 1 of [B, C].
+    mapped = [i for i in range(len(hc.token_map)) if hc.token_map[i] >= 0]
+    unmapped = [i for i in range(len(hc.token_map)) if hc.token_map[i] < 0]
+    A, B, C, U = mapped[0], mapped[1], mapped[2], unmapped[0]
+    args = _hash_args(hc)
+    got, _ = orc.engram_hash(*args, [0] * 4, [A, U, B, C], 0)
+    assert got[2] == orc.engram_hash(*args, [0] * 1, [B], 0)[0][0]
+    assert got[3] == orc.engram_hash(*args, [0] * 2, [B, C], 0)[0][1]
+    # the unmapped position itself hashes as an all-pad window, like [U] alone
+    assert got[1] == orc.engram_hash(*args, [0] * 1, [U], 0)[0][0]
+    with np.errstate(over="ignore"):
+        padv = np.int64(hc.pad_id)
+        rolling = padv * hc.multipliers[0, 0] ^ padv * hc.multipliers[0, 1]
+    assert got[1][0][0] == int(rolling) % int(hc.primes[0, 0, 0]) + int(hc.offsets[0, 0])
+
+
+def test_engram_hash_continues_across_calls():
+    """Prefill then decode steps with the cache carried equal one call."""
+    hc = syn.engram_hash_case(seed=5, seqlen=40)
+    whole, cache_w = orc.engram_hash(*_hash_args(hc), [0] * 40, hc.tokens.tolist(), 0)
+    part, cache = orc.engram_hash(*_hash_args(hc), [0] * 40, hc.tokens[:30].tolist(), 0)
+    for s in range(30, 40):
+        step, cache = orc.engram_hash(*_hash_args(hc), cache, [int(hc.tokens[s])], s)
+        part += step
+    assert part == whole and cache == cache_w
+
+
+def test_engram_hash_rejects_unknown_token():
+    with pytest.raises(ValueError):
+        orc.engram_hash([1, 2], [[3, 5]], [[[7]]], [[0]], 0, 1, [0] * 2, [5], 0)
+
+
 # ----------------------------------------------------------- SwiGLU / gate --
 
 def test_swiglu_against_torch_silu():
