@@ -217,17 +217,32 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
             ev1.synchronize()
         return ev0.elapsed_time(ev1) * 1e3 / (reps * launches)
 
+    def step_bf16(i):
+        q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks[i % 64:i % 64 + 1], 4096 + (i % 64), out=ids)
+        q2.q2k_dequant_rows(table, 500000, ids[1].reshape(-1), 8, out=rows)
+        q2.q2k_gemv_bf16(copies[i % copies_n], rows.view(1, 2048), n_out, 2048, out=kv)
+        q2.engram_gate(h, kv, qk, e.eps)
+
     us_step = timed(step, copies_n)
+    us_step_bf16 = timed(step_bf16, copies_n)
+    us_gemv = timed(lambda i: q2.q2k_gemv_bf16(copies[i % copies_n], rows.view(1, 2048), n_out, 2048,
+                                               out=kv), copies_n)
+    us_mmvq = timed(lambda i: q2.q2k_mmvq(copies[i % copies_n], xq, n_out, 2048, 1, out=kv), copies_n)
     us_hash1 = timed(lambda i: q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks[i % 64:i % 64 + 1],
                                               4096 + (i % 64), out=ids), 16)
     pre = torch.empty((2, 4096, 8), dtype=torch.int64, device=dev)
     us_pre = timed(lambda i: q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks, 0, out=pre), 16)
     wkv_bytes = w0.numel()
     return {"workload": "engram step, one token: hash -> 8-row gather -> q8_1 -> wkv Q2_K "
-                        "[20480, 2048] -> gate [1, 4, 4096]; 80 rotating wkv copies",
+                        "[20480, 2048] -> gate [1, 4, 4096]; 80 rotating wkv copies. The bf16 "
+                        "route skips q8_1: gathered bf16 rows straight into the wkv product",
             "us_per_step": round(us_step, 3), "tokens_per_s": round(1e6 / us_step, 1),
+            "us_per_step_bf16_route": round(us_step_bf16, 3),
             "wkv_bytes": wkv_bytes,
-            "wkv_gbs_at_step_time": round(wkv_bytes / us_step / 1e3, 1),
+            "wkv_q8_1_product_us": round(us_mmvq, 3),
+            "wkv_q8_1_product_gbs": round(wkv_bytes / us_mmvq / 1e3, 1),
+            "wkv_bf16_product_us": round(us_gemv, 3),
+            "wkv_bf16_product_gbs": round(wkv_bytes / us_gemv / 1e3, 1),
             "hash_decode_us": round(us_hash1, 3), "hash_prefill_4096_us": round(us_pre, 3)}
 
 

@@ -156,6 +156,23 @@ Q2K_API int32_t q2k_mmvq_grouped(const void* w_dev, const void* xq_dev, float* y
                          int32_t groups, int32_t rows_per_group, int32_t k, int32_t m,
                          void* stream);
 
+/* Q2_K weights times bf16 activations: the single-token engram projection
+ * read off the raw Q2_K blocks (engram_v41/apply.rs, the
+ * engram_v41_wkv_q2k_gemv launch; engram_v41.rs, EngramLayerWeights::wkv_q2k:
+ * bit for bit the bf16 GEMV over the bf16 expansion of the blocks).
+ *   w_dev        : Q2_K [n, k].
+ *   x_bf16_dev   : bf16 [m, k], row stride x_row_stride elements (a multiple
+ *                  of 8, >= k), 16-byte aligned. Not quantised.
+ *   y_dev        : f32 [m, n].
+ * y[t][r] = f32_rne(sum_e bf16(W[r][e]) * x[t][e]) where bf16(W) is the
+ * expansion q2k_dequant_rows produces (f32 d*sc*q - dmin*m, one rounding,
+ * then bf16 to nearest-even); the bf16 products are exact and are summed in
+ * fp64, so the result is the correctly rounded dot product of the expansion
+ * for any order (to ~2^-53 of the sum). 1 <= m <= Q2K_MAX_M, k % 256 == 0.
+ * Errors as q2k_mmvq (plus Q2K_ESHAPE for a stride < k, Q2K_EALIGN for x). */
+Q2K_API int32_t q2k_gemv_bf16(const void* w_dev, const void* x_bf16_dev, int64_t x_row_stride,
+                         float* y_dev, int32_t n, int32_t k, int32_t m, void* stream);
+
 /* Fused bf16 SwiGLU and q8_1 re-quantisation
  * (kquant_swiglu_q8_1_rows_bf16, moe_v41/init.rs).
  *   g_dev, u_dev : f32 [rows, k] contiguous (gate and up outputs).

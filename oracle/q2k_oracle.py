@@ -28,7 +28,8 @@ rustdoc source views of the metrale engine: ``engram_v41/apply.rs``,
   ``W`` the dequantised weights and ``a = d8 * xq`` the dequantised
   activations, accumulated here in fp64.
 * Row dequantisation to bf16 (``dequant_q2_k_to_bf16``,
-  ``EngramV41::rows_from_q2k``).
+  ``EngramV41::rows_from_q2k``), and the product of that bf16 expansion with
+  bf16 activations (``engram_v41_wkv_q2k_gemv``).
 * SwiGLU then q8_1 re-quantisation (``kquant_swiglu_q8_1_rows_bf16``).
 * The engram n-gram hash (``EngramHasher::hash``): window of compressed
   token ids, rolling xor of wrapping products, Euclidean remainder by a
@@ -319,6 +320,21 @@ def mmvq_grouped(w: np.ndarray, xq: np.ndarray, d8: np.ndarray, groups: int) -> 
     for g in range(groups):
         y[:, g * rows:(g + 1) * rows] = a[:, g * k:(g + 1) * k] @ wf[g * rows:(g + 1) * rows].T
     return y
+
+
+def gemv_bf16(w: np.ndarray, x_bits: np.ndarray) -> np.ndarray:
+    """Q2_K weights times bf16 activations (``engram_v41_wkv_q2k_gemv``,
+    engram_v41/apply.rs; engram_v41.rs ``EngramLayerWeights::wkv_q2k``: the
+    bf16 GEMV over the bf16 expansion of the blocks).
+
+    ``w``: uint8 [n, k/256, 84]; ``x_bits``: uint16 bf16 [m, k]. Each weight
+    is expanded to bf16 exactly as the row dequantisation does; the dot
+    product of the expansion with x is formed in fp64 (every bf16 x bf16
+    product is exact) and rounded to f32. Returns f32 [m, n]."""
+    n, nb = w.shape[0], w.shape[1]
+    wf = bf16_bits_to_f32(q2k_dequant_bf16_bits(w).reshape(n, nb * 256)).astype(np.float64)
+    xf = bf16_bits_to_f32(x_bits).astype(np.float64)
+    return (xf @ wf.T).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------

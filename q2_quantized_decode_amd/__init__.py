@@ -38,6 +38,7 @@ SIGNATURES = {
     "q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP, _I32,
                                 _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP]),
     "q2k_mmvq_grouped": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP]),
+    "q2k_gemv_bf16": (_I32, [_VP, _VP, _I64, _VP, _I32, _I32, _I32, _VP]),
     "swiglu_q8_1_rows": (_I32, [_VP, _VP, _VP, _VP, _SZ, _I32, _I32, _VP]),
     "q2k_dequant_rows": (_I32, [_VP, _I64, _VP, _I32, _VP, _VP, _VP]),
     "engram_gate": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _F32, _VP]),
@@ -176,6 +177,19 @@ def q2k_mmvq_grouped(w: torch.Tensor, xq: torch.Tensor, groups: int, rows_per_gr
     _check("q2k_mmvq_grouped", lib().q2k_mmvq_grouped(
         _contig(w, "w"), _contig(xq, "xq"), _contig(out, "out"), groups, rows_per_group, k, m,
         _stream()))
+    return out
+
+
+def q2k_gemv_bf16(w: torch.Tensor, x: torch.Tensor, n: int, k: int,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """f32 [m, n]: Q2_K [n, k] against bf16 x [m, k] (not quantised)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a bf16 [m, k] tensor with unit column stride")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _check("q2k_gemv_bf16", lib().q2k_gemv_bf16(_contig(w, "w"), _dev(x, "x"), x.stride(0),
+                                                _contig(out, "out"), n, k, m, _stream()))
     return out
 
 

@@ -236,6 +236,26 @@ int32_t q2k_mmvq_grouped(const void* w_dev, const void* xq_dev, float* y_dev, in
   return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
 }
 
+int32_t q2k_gemv_bf16(const void* w_dev, const void* x_bf16_dev, int64_t x_row_stride, float* y_dev,
+                      int32_t n, int32_t k, int32_t m, void* stream) {
+  const char* fn = "q2k_gemv_bf16";
+  if (int32_t r = check_matrix(fn, "w", w_dev, n)) return r;
+  if (int32_t r = check_out(fn, "y", y_dev)) return r;
+  if (!x_bf16_dev) return fail(Q2K_EINVAL, "%s: x is null", fn);
+  if (int32_t r = check_k(fn, k)) return r;
+  if (int32_t r = check_m(fn, m)) return r;
+  if (x_row_stride < k) return fail(Q2K_ESHAPE, "%s: row stride %lld < k = %d", fn, (long long)x_row_stride, k);
+  if (!aligned(x_bf16_dev, 16) || x_row_stride % 8 != 0)
+    return fail(Q2K_EALIGN, "%s: x must be 16-byte aligned with a row stride that is a multiple of 8", fn);
+  if ((int64_t)m * n > (int64_t)1 << 31) return fail(Q2K_ESHAPE, "%s: output larger than 2^31 values", fn);
+  const size_t ybytes = (size_t)m * n * 4;
+  const size_t xbytes = ((size_t)(m - 1) * x_row_stride + k) * 2;
+  if (overlap(y_dev, ybytes, w_dev, q2k_matrix_bytes(n, k)) || overlap(y_dev, ybytes, x_bf16_dev, xbytes))
+    return fail(Q2K_EINVAL, "%s: y overlaps an input", fn);
+  return launched(q2k::launch_gemv_bf16(w_dev, x_bf16_dev, x_row_stride, y_dev, n, k, m, (hipStream_t)stream),
+                  fn);
+}
+
 int32_t swiglu_q8_1_rows(const float* g_dev, const float* u_dev, void* h_bf16_dev, void* hq_dev,
                          size_t hq_bytes, int32_t rows, int32_t k, void* stream) {
   const char* fn = "swiglu_q8_1_rows";

@@ -51,6 +51,9 @@ hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream);
 bool mfma_supports(int k);
 // True when the matrix-core kernel is the faster choice for this launch.
 bool mfma_preferred(const MmvqLaunch& a);
+// Q2_K x bf16 activations (exact expansion, fp64 sums), m = 1..8.
+hipError_t launch_gemv_bf16(const void* w, const void* x, int64_t x_stride, float* y, int n, int k,
+                            int m, hipStream_t stream);
 hipError_t launch_dequant_rows(const void* table, int64_t n_table_rows, const int64_t* ids,
                                int n_rows, void* out, int32_t* err_flag, hipStream_t stream);
 hipError_t launch_engram_gate(float* h, const float* kv, const float* qk, int t, int hc, int dim,

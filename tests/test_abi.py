@@ -120,6 +120,16 @@ def test_engram_hash_validation(L):
     assert call(out=T + 0x400000) == EINVAL           # out on the cache
 
 
+def test_gemv_bf16_validation(L):
+    assert L.q2k_gemv_bf16(None, Q, 1024, 0x100, 256, 1024, 1, None) == EINVAL
+    assert L.q2k_gemv_bf16(P, Q, 1024, 0x100, 256, 1000, 1, None) == ESHAPE
+    assert L.q2k_gemv_bf16(P, Q, 1024, 0x100, 256, 1024, 9, None) == ESHAPE
+    assert L.q2k_gemv_bf16(P, Q, 512, 0x100, 256, 1024, 1, None) == ESHAPE      # stride < k
+    assert L.q2k_gemv_bf16(P, Q + 8, 1024, 0x100, 256, 1024, 1, None) == EALIGN
+    assert L.q2k_gemv_bf16(P, Q, 1028, 0x100, 256, 1024, 2, None) == EALIGN     # stride % 8
+    assert L.q2k_gemv_bf16(P, Q, 1024, P + 64, 256, 1024, 1, None) == EINVAL    # y inside w
+
+
 def test_experts_validation(L):
     arr = (ctypes.c_void_p * 2)(P, Q)
     ok = dict(stride=1024 * 16 * 84, n_experts=4, ids=0x200000, n_ids=8, xq=0x300000,

@@ -506,6 +506,45 @@ def test_engram_step(engram):
     assert_close(hd.cpu().numpy(), orc.engram_gate(e.h, ref_kv, e.qk, e.eps), "gate (end to end)")
 
 
+# ------------------------------------------------- bf16-activation GEMV -----
+
+@pytest.mark.parametrize("n,k,m", [(257, 1024, 1), (100, 2048, 3), (33, 7168, 8), (10, 9216, 2),
+                                   (5, 256, 1), (64, 4096, 5)])
+def test_gemv_bf16_bit_exact(n, k, m):
+    """Exact expansion, exact products, fp64 sums: the f32 bits of the oracle."""
+    case = syn.single_gemv_case(n=n, k=k, m=m, seed=900 + n + k + m)
+    y = q2.q2k_gemv_bf16(dev(case.w.reshape(-1)), bf16_dev(case.x_bits), n, k).cpu().numpy()
+    ref = orc.gemv_bf16(case.w, case.x_bits)
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32)), f"n={n} k={k} m={m}"
+
+
+def test_gemv_bf16_strided_input():
+    case = syn.single_gemv_case(n=70, k=1024, m=3, seed=905)
+    xb = torch.zeros((3, 1024 + 64), dtype=torch.bfloat16, device="cuda")
+    xb[:, :1024] = bf16_dev(case.x_bits)
+    y = q2.q2k_gemv_bf16(dev(case.w.reshape(-1)), xb[:, :1024], 70, 1024).cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), orc.gemv_bf16(case.w, case.x_bits).view(np.uint32))
+
+
+def test_engram_step_bf16_projection(engram):
+    """The pages' single-token route: gathered bf16 rows [1, 2048] straight
+    into the Q2_K wkv [20480, 2048] (no q8_1), then the gate."""
+    e = engram
+    rows = q2.q2k_dequant_rows(dev(e.table.reshape(-1)), e.table.shape[0], dev(e.ids), e.cols)
+    x = rows.view(1, e.cols * 256)
+    n_out = e.dim * (e.hc + 1)
+    kv = q2.q2k_gemv_bf16(dev(e.wkv.reshape(-1)), x, n_out, e.cols * 256)
+    kv_h = kv.cpu().numpy()
+    x_bits = rows.view(torch.int16).cpu().numpy().view(np.uint16).reshape(1, -1)
+    sample = np.unique(np.concatenate([np.arange(0, 256), np.arange(n_out - 256, n_out),
+                                       syn.rng_for(12).choice(n_out, 1024, replace=False)]))
+    ref = orc.gemv_bf16(e.wkv[sample], x_bits)
+    assert np.array_equal(kv_h[:, sample].view(np.uint32), ref.view(np.uint32))
+    hd = dev(e.h)
+    q2.engram_gate(hd, kv, dev(e.qk), e.eps)
+    assert_close(hd.cpu().numpy(), orc.engram_gate(e.h, kv_h, e.qk, e.eps), "gate after bf16 wkv")
+
+
 # ---------------------------------------------------- engram n-gram hash ---
 
 def _hash_tables_dev(hc):

@@ -394,6 +394,53 @@ def test_grouped_closed_forms():
     assert np.array_equal(y, want)
 
 
+# ------------------------------------------------- bf16-activation GEMV -----
+
+def test_gemv_bf16_brute_force_tiny():
+    """Each weight expanded from the raw bytes in plain Python (f32 value,
+    bf16 rounding by the bit rule), times the bf16 x value, summed exactly
+    with fractions, then rounded to f32 once."""
+    from fractions import Fraction
+    case = syn.single_gemv_case(n=3, k=512, m=2, seed=71)
+    y = orc.gemv_bf16(case.w, case.x_bits)
+    xf = orc.bf16_bits_to_f32(case.x_bits)
+    for t in range(2):
+        for r in range(3):
+            acc = Fraction(0)
+            for b in range(2):
+                blk = case.w[r, b]
+                d = np.float32(np.frombuffer(bytes(blk[80:82]), np.float16)[0])
+                dmin = np.float32(np.frombuffer(bytes(blk[82:84]), np.float16)[0])
+                for e in range(256):
+                    h, rest = divmod(e, 128)
+                    j, l = divmod(rest, 32)
+                    q = (int(blk[16 + 32 * h + l]) >> (2 * j)) & 3
+                    sb = 8 * h + 2 * j + (l >= 16)
+                    v = np.float32(d * np.float32(int(blk[sb]) & 15) * np.float32(q)) - \
+                        np.float32(dmin * np.float32(int(blk[sb]) >> 4))
+                    u = int(np.float32(v).view(np.uint32))
+                    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+                    wb = float(np.uint32(u).view(np.float32))
+                    acc += Fraction(wb) * Fraction(float(xf[t, 256 * b + e]))
+            assert y[t, r] == np.float32(float(acc))
+
+
+def test_gemv_bf16_is_the_dense_gemv_over_the_expansion():
+    """Against the row dequantisation (pinned above by hand blocks): a dense
+    f32 GEMV over the expanded rows with exact accumulation gives the same
+    bits; and for integer-valued bf16 x it is exact."""
+    case = syn.single_gemv_case(n=20, k=1024, m=3, seed=72)
+    y = orc.gemv_bf16(case.w, case.x_bits)
+    rows = orc.dequant_rows_bf16_bits(case.w.reshape(-1, 84), None).reshape(20, 1024)
+    wf = orc.bf16_bits_to_f32(rows).astype(np.float64)
+    xf = orc.bf16_bits_to_f32(case.x_bits).astype(np.float64)
+    assert np.array_equal(y, np.array([[np.float32(np.dot(xf[t], wf[r])) for r in range(20)]
+                                       for t in range(3)], dtype=np.float32))
+    w = _const_matrix(4, 2, 0x01, 0xFF, 0x3C00, 0x0000)     # every weight 3.0 exactly
+    x = syn.f32_to_bf16_bits_torch(np.full((1, 512), 2.0, np.float32))
+    assert np.all(orc.gemv_bf16(w, x) == 3.0 * 2.0 * 512)
+
+
 # ------------------------------------------------------- engram n-gram hash --
 
 def _hash_args(hc):
