@@ -108,6 +108,47 @@ def cpu_baseline(case, seconds: float, chunk: int = 4096):
                       f"{wall:.1f} s, fp64 dense oracle"}
 
 
+def bench_mmq(torch, q2, syn, dev, copies, case):
+    """The product past 8 tokens (q2k_mmq) on the large-verify matrix: m =
+    16, 64, 256 tokens ~ N(0,1) with 5% +-20 outliers, over the same rotating
+    copies; graphs of 16 launches, HIP events around the replays."""
+    out = {}
+    for m in (16, 64, 256):
+        x = syn.bf16_bits_to_tensor(syn.bf16_normal(syn.rng_for(1004, m), (m, K), outlier_frac=0.05)).to(dev)
+        xq = q2.q8_1_rows(x)
+        y = torch.empty((m, N), dtype=torch.float32, device=dev)
+        stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for i in range(COPIES):
+                q2.q2k_mmq(copies[i], xq, N, K, m, out=y)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(COPIES):
+                q2.q2k_mmq(copies[i], xq, N, K, m, out=y)
+        reps = max(2, 64 // m)
+        with torch.cuda.stream(stream):
+            g.replay()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            ev1.record(stream)
+            ev1.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / (reps * COPIES)
+        nbytes = mmvq_bytes(m)
+        int8_ops = 2.0 * N * K * m
+        out[f"m{m}"] = {"us_per_launch": round(us, 2), "tokens_per_s": round(m / us * 1e6, 1),
+                        "achieved_gbs": round(nbytes / us / 1e3, 1),
+                        "frac_hbm": round(nbytes / us / 1e3 / PEAK_GBS, 4),
+                        "tops": round(int8_ops / us / 1e6, 1)}
+    out["workload"] = ("q2k_mmq on Q2_K [32768, 7168], m tokens (matrix cores, 8 tokens per "
+                       "workgroup), 16 rotating copies")
+    return out
+
+
 def bench_grouped(torch, q2, syn, dev, copies_n: int = 64):
     """The grouped-input product (wo_a shape: 8 groups x 1024 rows, 2048-wide
     slices of a 16384-wide input) at m = 1 and m = 8 over rotating weight
@@ -384,6 +425,7 @@ def run(args):
                             "bytes_per_launch": mmvq_bytes(8),
                             "us_per_launch": round(r8["launch_s"] * 1e6, 3)}},
     }
+    line["mmq"] = bench_mmq(torch, q2, syn, dev, copies, case)
     del copies
     torch.cuda.synchronize()
     line["grouped"] = bench_grouped(torch, q2, syn, dev)

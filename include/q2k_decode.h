@@ -139,6 +139,20 @@ Q2K_API int32_t q2k_mmvq_experts(const void* const* bases, int32_t n_bases,
                          int32_t n, int32_t k, int32_t m,
                          int32_t* err_flag_dev, void* stream);
 
+/* Q2_K x q8_1 product for any number of tokens (prefill, batched verify):
+ * the pages' route past 8 tokens (moe_v41/init.rs, MoeV41::new: the
+ * metrale_q2_k_mmq128_{nc,wc} kernels and the mmq activation buffers sized
+ * beside the q8_1 rows). Same values as q2k_mmvq for each token:
+ * y[t][r] = sum over the row of d8 * (d*I - dmin*M).
+ *   w_dev  : Q2_K [n, k]; xq_dev : q8_1 rows [m, k]; y_dev : f32 [m, n].
+ *   1 <= m <= Q2K_MMQ_MAX_M, k % 256 == 0; errors as q2k_mmvq.
+ * Rows of 4, 8, 16 or 28 super-blocks run on the matrix cores in groups of
+ * 8 tokens per workgroup; other shapes run the q2k_mmvq kernels on each
+ * group of 8 tokens in turn. */
+#define Q2K_MMQ_MAX_M 4096
+Q2K_API int32_t q2k_mmq(const void* w_dev, const void* xq_dev, float* y_dev, int32_t n,
+                        int32_t k, int32_t m, void* stream);
+
 /* Grouped-input product: the Q2_K route of the attention output projection
  * wo_a (attn_v41/decode.rs, the grouped wo_a step of the decode body, taken
  * when wo_a is Q2_K and m <= 8), where output row g*o_rank + r is the dot of

@@ -38,6 +38,7 @@ SIGNATURES = {
     "q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP, _I32,
                                 _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP]),
     "q2k_mmvq_grouped": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP]),
+    "q2k_mmq": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     "q2k_gemv_bf16": (_I32, [_VP, _VP, _I64, _VP, _I32, _I32, _I32, _VP]),
     "swiglu_q8_1_rows": (_I32, [_VP, _VP, _VP, _VP, _SZ, _I32, _I32, _VP]),
     "q2k_dequant_rows": (_I32, [_VP, _I64, _VP, _I32, _VP, _VP, _VP]),
@@ -165,6 +166,16 @@ def q2k_mmvq_experts(bases: Sequence[torch.Tensor], expert_stride_bytes: int, n_
         arr, len(ptrs), expert_stride_bytes, n_experts, _contig(ids, "ids"), n_ids,
         _contig(xq, "xq"), 1 if x_per_id else 0, _contig(out, "out"), n, k, m, flag or None,
         _stream()))
+    return out
+
+
+def q2k_mmq(w: torch.Tensor, xq: torch.Tensor, n: int, k: int, m: int,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """f32 [m, n] for any number of tokens m (up to 4096)."""
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _check("q2k_mmq", lib().q2k_mmq(_contig(w, "w"), _contig(xq, "xq"), _contig(out, "out"), n, k, m,
+                                    _stream()))
     return out
 
 

@@ -119,6 +119,31 @@ int32_t q2k_mmvq(const void* w_dev, const void* xq_dev, float* y_dev, int32_t n,
   return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
 }
 
+int32_t q2k_mmq(const void* w_dev, const void* xq_dev, float* y_dev, int32_t n, int32_t k, int32_t m,
+                void* stream) {
+  const char* fn = "q2k_mmq";
+  if (int32_t r = check_matrix(fn, "w", w_dev, n)) return r;
+  if (int32_t r = check_out(fn, "y", y_dev)) return r;
+  if (!xq_dev) return fail(Q2K_EINVAL, "%s: xq is null", fn);
+  if (int32_t r = check_k(fn, k)) return r;
+  if (m < 1 || m > Q2K_MMQ_MAX_M) return fail(Q2K_ESHAPE, "%s: m = %d outside 1..%d", fn, m, Q2K_MMQ_MAX_M);
+  if (!aligned(xq_dev, 16)) return fail(Q2K_EALIGN, "%s: xq must be 16-byte aligned", fn);
+  if ((int64_t)m * n > (int64_t)1 << 31) return fail(Q2K_ESHAPE, "%s: output larger than 2^31 values", fn);
+  const size_t ybytes = (size_t)m * n * 4;
+  if (overlap(y_dev, ybytes, w_dev, q2k_matrix_bytes(n, k)) ||
+      overlap(y_dev, ybytes, xq_dev, (size_t)m * q2k::q8_row_bytes(k)))
+    return fail(Q2K_EINVAL, "%s: y overlaps an input", fn);
+  q2k::MmvqLaunch a{};
+  a.w[0] = w_dev;
+  a.y[0] = y_dev;
+  a.n[0] = n;
+  a.njobs = 1;
+  a.xq = xq_dev;
+  a.k = k;
+  a.m = m;
+  return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
+}
+
 int32_t q2k_mmvq_pair(const void* wa_dev, float* ya_dev, int32_t na, const void* wb_dev,
                       float* yb_dev, int32_t nb, const void* xq_dev, int32_t k, int32_t m,
                       void* stream) {

@@ -36,6 +36,7 @@
 // their sums combined through LDS in a fixed order. Four waves per SIMD hide
 // the dependency chains of one tile better than whole-row waves with deeper
 // software pipelining did (measured).
+#include <stdint.h>
 #include <stdlib.h>
 
 #include "q2k_device.h"
@@ -72,7 +73,8 @@ struct MfmaParams {
   int32_t groups;                    // grouped mode when > 0
   int32_t wgs_per_job;               // expert and grouped modes
   int32_t total_wgs;
-  int32_t m;
+  int32_t m;                         // tokens of the launch (any count)
+  int32_t tgroups;                   // groups of kSlots tokens: ceil(m / kSlots)
 };
 
 // LDS layout (bytes) for row length k:
@@ -305,8 +307,20 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const MfmaParams p)
   const int g8 = gridDim.x >> 3;
   const int wgi = (blockIdx.x & 7) * g8 + (blockIdx.x >> 3);   // XCD-major workgroup index
   if (wgi >= p.total_wgs) return;                              // whole workgroup
-  const int m = p.m;
-  const Job J = resolve_job<k>(p, wgi);
+  // Token group tg of a row block: its kSlots tokens (fewer in the last
+  // group). The groups of one block are consecutive workgroups, so they run
+  // together on one XCD and read the block's weights through its L2.
+  const int job_wg = wgi / p.tgroups;
+  const int tg = wgi - job_wg * p.tgroups;
+  Job J = resolve_job<k>(p, job_wg);
+  const int m = min(kSlots, p.m - kSlots * tg);
+  {
+    const int64_t t0 = (int64_t)kSlots * tg;
+    J.X.q += t0 * J.X.stride;
+    J.X.s += t0 * J.X.stride;
+    J.X.m += t0 * J.X.stride;
+    J.Y += t0 * J.ldy;
+  }
 
   const int wiw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int tw = wiw & (kTilesPerWg - 1);
@@ -440,7 +454,9 @@ bool mfma_supports(int k) {
 bool mfma_preferred(const MmvqLaunch& a) {
   // One workgroup per CU at a time (LDS): below a quarter of the chip the
   // packed-dot kernels, which spread a row over more waves, are faster.
-  return a.m >= 2 && a.dots == nullptr && mfma_supports(a.k) && workgroups(a) >= 64;
+  // More than kSlots tokens always go to the matrix cores when they can.
+  if (a.dots != nullptr || !mfma_supports(a.k) || a.m < 2) return false;
+  return a.m > kSlots || workgroups(a) * ((a.m + kSlots - 1) / kSlots) >= 64;
 }
 
 hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream) {
@@ -462,6 +478,7 @@ hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream) {
   p.err_flag = a.err_flag;
   p.groups = a.groups;
   p.m = a.m;
+  p.tgroups = (a.m + kSlots - 1) / kSlots;
 
   // Eight consecutive 16-row tiles per workgroup.
   const int tile_rows = 16 * kTilesPerWg;
@@ -476,6 +493,8 @@ hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream) {
     total_wgs = (int64_t)p.wgs_per_job * a.njobs * a.n_ids;
   }
   if (total_wgs == 0) return hipSuccess;
+  total_wgs *= p.tgroups;
+  if (total_wgs > INT32_MAX - 8) return hipErrorInvalidValue;
   p.total_wgs = (int)total_wgs;
   const dim3 gd((unsigned)((total_wgs + 7) / 8 * 8));
   const size_t shm = lds_bytes(a.k) + kXchgBytes;

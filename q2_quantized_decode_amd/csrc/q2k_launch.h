@@ -9,6 +9,8 @@ namespace q2k {
 
 // Up to this many matrices in one plain (non-expert) product launch.
 constexpr int kMaxPlainJobs = 4;
+// Tokens one packed-dot launch takes (the q2k_mmvq limit); q2k_mmq goes past it.
+constexpr int kMaxM = 8;
 constexpr int kMaxExpertBases = 4;
 
 struct MmvqLaunch {

@@ -130,6 +130,16 @@ def test_gemv_bf16_validation(L):
     assert L.q2k_gemv_bf16(P, Q, 1024, P + 64, 256, 1024, 1, None) == EINVAL    # y inside w
 
 
+def test_mmq_validation(L):
+    assert L.q2k_mmq(None, Q, 0x100, 256, 1024, 16, None) == EINVAL
+    assert L.q2k_mmq(P, Q, 0x100, 256, 1000, 16, None) == ESHAPE
+    assert L.q2k_mmq(P, Q, 0x100, 256, 1024, 0, None) == ESHAPE
+    assert L.q2k_mmq(P, Q, 0x100, 256, 1024, 4097, None) == ESHAPE
+    assert "4096" in _err(L)
+    assert L.q2k_mmq(P, Q + 4, 0x100, 256, 1024, 16, None) == EALIGN
+    assert L.q2k_mmq(P, Q, P + 64, 256, 1024, 16, None) == EINVAL    # y inside w
+
+
 def test_experts_validation(L):
     arr = (ctypes.c_void_p * 2)(P, Q)
     ok = dict(stride=1024 * 16 * 84, n_experts=4, ids=0x200000, n_ids=8, xq=0x300000,

@@ -618,12 +618,49 @@ def test_engram_hashed_rows_gather():
     assert int(flag.item()) == 0
 
 
+# ------------------------------------------------------- m > 8 (MMQ) ------
+
+@pytest.mark.parametrize("n,k,m", [(300, 1024, 9), (1000, 2048, 16), (130, 7168, 33), (257, 4096, 64),
+                                   (100, 1280, 20), (64, 9216, 12), (40, 2048, 200)])
+def test_mmq(n, k, m):
+    """Matrix cores in groups of 8 tokens (k/256 in {4, 8, 16, 28}); other
+    row lengths loop the packed-dot kernels over groups of 8."""
+    rng = syn.rng_for(7100, n, k, m)
+    w = syn.q2k_blocks(rng, n, k // 256)
+    x = syn.bf16_normal(rng, (m, k), outlier_frac=0.05)
+    xq = q2.q8_1_rows(bf16_dev(x))
+    oq, od = assert_q8_equal(xq, x)
+    y = q2.q2k_mmq(dev(w.reshape(-1)), xq, n, k, m).cpu().numpy()
+    assert_close(y, orc.mmvq(w, oq, od), f"mmq n={n} k={k} m={m}")
+
+
+def test_mmq_small_m_is_mmvq():
+    case = syn.single_gemv_case(n=8197, k=2048, m=5, seed=7200)
+    w = dev(case.w.reshape(-1))
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits))
+    a = q2.q2k_mmq(w, xq, 8197, 2048, 5).cpu().numpy()
+    b = q2.q2k_mmvq(w, xq, 8197, 2048, 5).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 # ------------------------------------------------------- full-size verify ---
 
 @pytest.fixture(scope="module")
 def large():
     case = syn.large_verify_case(m=8)
     return case, dev(case.w.reshape(-1))
+
+
+def test_large_mmq_sampled(large):
+    """[32768, 7168] against 64 tokens (8 token groups on the matrix cores)."""
+    case, w = large
+    x = syn.bf16_normal(syn.rng_for(1004, 64), (64, case.k), outlier_frac=0.05)
+    xq = q2.q8_1_rows(bf16_dev(x))
+    oq, od = assert_q8_equal(xq, x)
+    y = q2.q2k_mmq(w, xq, case.n, case.k, 64).cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(case.n - 64, case.n),
+                                     syn.rng_for(5).choice(case.n, 128, replace=False)]))
+    assert_close(y[:, rows], orc.mmvq(case.w[rows], oq, od), "large mmq m=64")
 
 
 @pytest.mark.parametrize("m", [1, 3, 8])
