@@ -425,11 +425,12 @@ def run(args):
                             "bytes_per_launch": mmvq_bytes(8),
                             "us_per_launch": round(r8["launch_s"] * 1e6, 3)}},
     }
-    line["mmq"] = bench_mmq(torch, q2, syn, dev, copies, case)
-    del copies
-    torch.cuda.synchronize()
-    line["grouped"] = bench_grouped(torch, q2, syn, dev)
-    line["engram_step"] = bench_engram(torch, q2, syn, dev)
+    if not args.headline_only:
+        line["mmq"] = bench_mmq(torch, q2, syn, dev, copies, case)
+        del copies
+        torch.cuda.synchronize()
+        line["grouped"] = bench_grouped(torch, q2, syn, dev)
+        line["engram_step"] = bench_engram(torch, q2, syn, dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
@@ -522,6 +523,8 @@ def main():
                     help="wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--pmc-calibration", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the large-verify m = 1 and m = 8 steps (for kernel traces)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic record from two counter runs and exit")
     args = ap.parse_args()
