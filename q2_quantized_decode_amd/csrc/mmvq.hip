@@ -55,7 +55,19 @@ struct MmvqParams {
   int32_t interleave;                // 1: a job's waves take its steps round-robin
   int32_t k;
   int32_t gs_log2;                   // lanes per row group = 1 << gs_log2
+  int32_t g8;                        // workgroups per XCD (grid / 8)
 };
+
+// Touches every field of the argument block at once, so that its scalar
+// loads are issued together and waited for once at the top of the kernel;
+// left to the compiler, the loads of each field go out where it is first
+// needed, and every dependent round costs a memory latency before the first
+// weight load. Later reads of the same fields hit the scalar cache.
+__device__ __forceinline__ void prefetch_args(const MmvqParams& p) {
+  asm volatile("" ::"s"(p.w[0]), "s"(p.y[0]), "s"(p.n[0]), "s"(p.wave_end[0]), "s"(p.wave_end[1]),
+               "s"(p.wave_end[2]), "s"(p.xq), "s"(p.ids), "s"(p.groups), "s"(p.total_waves),
+               "s"(p.k), "s"(p.interleave), "s"(p.chunk), "s"(p.g8));
+}
 
 // The matrix one wave works on, and its run of row steps.
 struct WaveJob {
@@ -416,6 +428,7 @@ constexpr int kStageBytes = 3072;
 // a guarded path with one direct load per step.
 template <int GSL, int R, int CH, bool STAGED>
 __global__ __launch_bounds__(256) void mmvq_m1_kernel(const MmvqParams p) {
+  prefetch_args(p);
   __shared__ __attribute__((aligned(16))) uint8_t stage[STAGED ? 4 : 1][STAGED ? kStageBytes : 16];
   constexpr int GS = 1 << GSL;
   constexpr int P = 64 >> GSL;
@@ -423,7 +436,7 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const MmvqParams p) {
   static_assert(CH % V == 0 && R >= 2, "run and ring shapes");
   const int lane = threadIdx.x & 63;
   const int wiw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int g8 = gridDim.x >> 3;
+  const int g8 = p.g8;
   const int wg = blockIdx.x;
   const int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 + wiw;
   if (wave >= p.total_waves) return;
@@ -569,8 +582,9 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const MmvqParams p) {
 // Narrow rows (2 * k/256 <= 64 half blocks): one half block per lane.
 template <int M, bool CACHE, int DEPTH, bool DOTS>
 __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
+  prefetch_args(p);
   const int lane = threadIdx.x & 63;
-  const int g8 = gridDim.x >> 3;
+  const int g8 = p.g8;
   const int wg = blockIdx.x;
   const int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 +
                    __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -641,8 +655,9 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
 // lane walks half blocks lane, lane + 64, ...; activations come from memory.
 template <int M, bool DOTS>
 __global__ __launch_bounds__(256) void mmvq_wide_kernel(const MmvqParams p) {
+  prefetch_args(p);
   const int lane = threadIdx.x & 63;
-  const int g8 = gridDim.x >> 3;
+  const int g8 = p.g8;
   const int wg = blockIdx.x;
   const int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 +
                    __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -885,6 +900,7 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   p.interleave = tu.interleave;
   int64_t groups = (total_waves + 3) / 4;
   groups = (groups + 7) / 8 * 8;
+  p.g8 = (int)(groups / 8);
   const dim3 grid((unsigned)groups);
   const bool dots = a.dots != nullptr;
 

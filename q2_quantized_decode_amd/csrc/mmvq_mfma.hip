@@ -75,7 +75,17 @@ struct MfmaParams {
   int32_t total_wgs;
   int32_t m;                         // tokens of the launch (any count)
   int32_t tgroups;                   // groups of kSlots tokens: ceil(m / kSlots)
+  int32_t g8;                        // workgroups per XCD (grid / 8)
 };
+
+// Touches the fields the prologue needs at once, so that their scalar loads
+// are issued together and waited for once instead of in dependent rounds
+// (each a memory latency before the first weight load).
+__device__ __forceinline__ void prefetch_args(const MfmaParams& p) {
+  asm volatile("" ::"s"(p.w[0]), "s"(p.y[0]), "s"(p.n[0]), "s"(p.wg_end[0]), "s"(p.wg_end[1]),
+               "s"(p.wg_end[2]), "s"(p.xq), "s"(p.ids), "s"(p.groups), "s"(p.total_wgs),
+               "s"(p.m), "s"(p.tgroups), "s"(p.g8));
+}
 
 // LDS layout (bytes) for row length k:
 //   quants  [kTabSlots][k + 16]   slot stride padded by 16 bytes so the eight
@@ -304,7 +314,8 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const MfmaParams p)
   constexpr int NBH = NB / 2;
   static_assert(NB % 2 == 0, "row split in two halves");
   constexpr uint32_t rowbytes = (uint32_t)NB * kBlockBytes;
-  const int g8 = gridDim.x >> 3;
+  prefetch_args(p);
+  const int g8 = p.g8;
   const int wgi = (blockIdx.x & 7) * g8 + (blockIdx.x >> 3);   // XCD-major workgroup index
   if (wgi >= p.total_wgs) return;                              // whole workgroup
   // Token group tg of a row block: its kSlots tokens (fewer in the last
@@ -497,6 +508,7 @@ hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream) {
   if (total_wgs > INT32_MAX - 8) return hipErrorInvalidValue;
   p.total_wgs = (int)total_wgs;
   const dim3 gd((unsigned)((total_wgs + 7) / 8 * 8));
+  p.g8 = (int)(gd.x / 8);
   const size_t shm = lds_bytes(a.k) + kXchgBytes;
   switch (which) {
     case 0: return launch_nb<4>(p, gd, shm, stream);
