@@ -186,50 +186,70 @@ __device__ __forceinline__ Job resolve_job(const MfmaParams& p, int wgi) {
   return J;
 }
 
-// Stage the activations of m tokens (k wide) in LDS. Every load is issued
-// before the first LDS store, so the staging costs one memory latency.
+// Staging of the activations of m tokens (k wide) in LDS, in two parts: the
+// loads (stage_load), issued before the weight ring so that waiting for them
+// does not wait for the weights (loads complete in issue order), and the LDS
+// stores (stage_store). Every load is issued before the first store, so the
+// staging costs one memory latency.
 template <int k, int THREADS>
-__device__ __forceinline__ void stage_activations(uint8_t* lds, const XView& X, int m) {
-  static_assert(kSlots * (k / 128) <= THREADS, "one scale group per thread");
-  const int tid = threadIdx.x;
-  constexpr int QC = k / 16;  // 16-byte quant chunks per token
-  constexpr int QIT = (kSlots * QC + THREADS - 1) / THREADS;
+struct StageRegs {
+  static constexpr int QC = k / 16;  // 16-byte quant chunks per token
+  static constexpr int QIT = (kSlots * QC + THREADS - 1) / THREADS;
+  static constexpr int C4 = k / 128;
   u32x4 qv[QIT];
+  f32x4 d8v;
+  u32x4 sv;
+};
+
+template <int k, int THREADS>
+__device__ __forceinline__ StageRegs<k, THREADS> stage_load(const XView& X, int m) {
+  using SR = StageRegs<k, THREADS>;
+  static_assert(kSlots * SR::C4 <= THREADS, "one scale group per thread");
+  SR r;
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int it = 0; it < QIT; ++it) {
+  for (int it = 0; it < SR::QIT; ++it) {
     const int idx = tid + it * THREADS;
-    const int t = idx / QC, e = idx - (idx / QC) * QC;
-    qv[it] = u32x4{0, 0, 0, 0};
-    if (idx < kSlots * QC && t < m) qv[it] = gload<u32x4>(X.q + t * X.stride + 16 * e);
+    const int t = idx / SR::QC, e = idx - (idx / SR::QC) * SR::QC;
+    // Unconditional load (slots past m read token 0) and a select after it:
+    // a load under a branch makes the compiler wait for it at the join,
+    // which would serialise the staging loads.
+    const bool ok = idx < kSlots * SR::QC && t < m;
+    r.qv[it] = gload<u32x4>(ok ? X.q + t * X.stride + 16 * e : X.q);
   }
   // Scales and half-block sums: thread (token t2, group c4) takes q8 blocks
   // 4c4..4c4+3, i.e. sub-blocks 8c4..8c4+7.
-  constexpr int C4 = k / 128;
-  const int t2 = tid / C4, c4 = tid - (tid / C4) * C4;
-  const bool sv_ok = tid < kSlots * C4 && t2 < m;
-  f32x4 d8v = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 sv = u32x4{0, 0, 0, 0};
-  if (sv_ok) {
-    d8v = gload<f32x4>(X.s + t2 * X.stride + 16 * c4);
-    sv = gload<u32x4>(X.m + t2 * X.stride + 16 * c4);
-  }
+  const int t2 = tid / SR::C4, c4 = tid - (tid / SR::C4) * SR::C4;
+  const bool sv_ok = tid < kSlots * SR::C4 && t2 < m;
+  r.d8v = gload<f32x4>(sv_ok ? X.s + t2 * X.stride + 16 * c4 : X.s);
+  r.sv = gload<u32x4>(sv_ok ? X.m + t2 * X.stride + 16 * c4 : X.m);
+  return r;
+}
+
+template <int k, int THREADS>
+__device__ __forceinline__ void stage_store(uint8_t* lds, const StageRegs<k, THREADS>& r, int m) {
+  using SR = StageRegs<k, THREADS>;
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int it = 0; it < QIT; ++it) {
+  for (int it = 0; it < SR::QIT; ++it) {
     const int idx = tid + it * THREADS;
-    const int t = idx / QC, e = idx - (idx / QC) * QC;
-    if (idx < kSlots * QC) *reinterpret_cast<u32x4*>(lds + t * q_stride(k) + 16 * e) = qv[it];
+    const int t = idx / SR::QC, e = idx - (idx / SR::QC) * SR::QC;
+    const u32x4 v = t < m ? r.qv[it] : u32x4{0, 0, 0, 0};
+    if (idx < kSlots * SR::QC) *reinterpret_cast<u32x4*>(lds + t * q_stride(k) + 16 * e) = v;
   }
-  for (int e = tid; e < QC; e += THREADS)
+  for (int e = tid; e < SR::QC; e += THREADS)
     *reinterpret_cast<u32x4*>(lds + kSlots * q_stride(k) + 16 * e) = u32x4{0, 0, 0, 0};
-  if (tid < kSlots * C4) {
+  const int t2 = tid / SR::C4, c4 = tid - (tid / SR::C4) * SR::C4;
+  if (tid < kSlots * SR::C4) {
+    const bool live = t2 < m;
     double* d8t = reinterpret_cast<double*>(lds + lds_d8_off(k));
     double* at = reinterpret_cast<double*>(lds + lds_at_off(k));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d8t[(4 * c4 + i) * kSlots + t2] = (double)d8v[i];
+    for (int i = 0; i < 4; ++i) d8t[(4 * c4 + i) * kSlots + t2] = live ? (double)r.d8v[i] : 0.0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int16_t sum = (int16_t)(sv[j >> 1] >> (16 * (j & 1)));
-      at[(8 * c4 + j) * kTabSlots + t2] = (double)d8v[j >> 1] * (double)sum;
+      const int16_t sum = (int16_t)(r.sv[j >> 1] >> (16 * (j & 1)));
+      at[(8 * c4 + j) * kTabSlots + t2] = live ? (double)r.d8v[j >> 1] * (double)sum : 0.0;
     }
   }
   for (int s2 = tid; s2 < k / 16; s2 += THREADS)
@@ -265,10 +285,10 @@ __device__ __forceinline__ Lane lane_consts() {
   L.a_base = opaque_v(a_slot * q_stride(k) + 128u * (g >> 1) + 16u * (g & 1));
   // d8 of the lane's four outputs: tokens 4(g&1) + 0..3 of q8 block 8b + 4(g>>1) + p.
   L.d8_base = opaque_v(lds_d8_off(k) + 8u * (kSlots * 4u * (g >> 1) + 4u * (g & 1)));
-  // M-term A: A-row a = j16 carries token 4(a&1) + (a>>2) when (a&3) < 2,
-  // otherwise zeros; k-index g is sub-block 8(g>>1) + 2i + (g&1).
-  const uint32_t m_slot = (j16 & 3) < 2 ? (uint32_t)(4 * (j16 & 1) + (j16 >> 2)) : (uint32_t)kSlots;
-  L.at_base = opaque_v(lds_at_off(k) + 8u * ((8u * (g >> 1) + (g & 1)) * kTabSlots + m_slot));
+  // M-term A (4x4x4 MFMA, four blocks): lane 16k + 4blk + i holds A[blk][i][k]
+  // = d8*S of token i (+4 for the second MFMA of a pair) and k-index k = g,
+  // which is sub-block 8(g>>1) + 2i' + (g&1) of MFMA pair i'.
+  L.at_base = opaque_v(lds_at_off(k) + 8u * ((8u * (g >> 1) + (g & 1)) * kTabSlots + (uint32_t)(j16 & 3)));
   L.sc_shift = 8u * (g & 1);
   return L;
 }
@@ -284,11 +304,18 @@ __device__ __forceinline__ v4i plane_weights(const u32x4& qs, uint32_t sw, int p
 }
 
 // Final sums of a tile: lanes g and g ^ 2 hold the two q8 halves of the same
-// tokens; the M term sits on lanes g < 2. Gives the row value of token
-// 4g + i on lanes g < 2.
-__device__ __forceinline__ void tile_sums(const double* yI, const v4d& accM, double* yv) {
+// tokens (I term); the M term of token t, row j16 sits on lane 16(t & 3) + j16,
+// in accM0 for t < 4 and accM1 otherwise. Gives the row value of token 4g + i
+// on lanes g < 2.
+__device__ __forceinline__ void tile_sums(const double* yI, double accM0, double accM1, const Lane& L,
+                                          double* yv) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) yv[i] = yI[i] + __shfl_xor(yI[i], 32) - accM[i];
+  for (int i = 0; i < 4; ++i) {
+    const int src = 16 * i + L.j16;
+    const double m0 = __shfl(accM0, src);
+    const double m1 = __shfl(accM1, src);
+    yv[i] = yI[i] + __shfl_xor(yI[i], 32) - (L.g == 0 ? m0 : m1);
+  }
 }
 
 __device__ __forceinline__ void store_tile(const Job& J, int m, int r0, const Lane& L, const double* yv) {
@@ -346,19 +373,25 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const MfmaParams p)
   const uint8_t* Wt = J.W + (size_t)r0 * rowbytes + (size_t)b0 * kBlockBytes;
   const BlkOffsets off{opaque_v(lrow * rowbytes + 16u + 16u * L.g), opaque_v(lrow * rowbytes + 8u * (L.g >> 1)),
                        opaque_v(lrow * rowbytes + 80u)};
+  const StageRegs<k, kThreads> staged = stage_load<k, kThreads>(J.X, m);
   Blk ring[R];
 #pragma unroll
   for (int b = 0; b < R; ++b)
     if (b < NBH) ring[b] = load_blk(Wt + b * kBlockBytes, off);
 
-  stage_activations<k, kThreads>(lds, J.X, m);
+  stage_store<k, kThreads>(lds, staged, m);
   lds_barrier();
 
   double yv[4] = {0.0, 0.0, 0.0, 0.0};
   if (active) {
-    // Two M accumulators (MFMAs i = 0,2 and 1,3) halve the fp64 MFMA
-    // dependency chain.
-    v4d accM0 = v4d{0.0, 0.0, 0.0, 0.0}, accM1 = v4d{0.0, 0.0, 0.0, 0.0};
+    // M term on v_mfma_f64_4x4x4f64 (four 4x4 blocks): block blk = weight rows
+    // 4blk..4blk+3, rows of A = tokens 0..3 (accM0) or 4..7 (accM1), K = four
+    // sub-blocks. B[blk][k][j] sits on lane 16k + 4blk + j = (g, row j16): the
+    // lane's own row and one of its own scale bytes. D[blk][i][j] lands on
+    // lane 16i + 4blk + j: token i (+4), row j16. Unlike the 16x16x4 form it
+    // wastes no rows on absent tokens, and an fp64 MFMA stalls the vector ALU
+    // for its whole duration.
+    double accM0 = 0.0, accM1 = 0.0;
     double yI[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int bb = 0; bb < NBH; ++bb) {
@@ -371,11 +404,12 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const MfmaParams p)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t mb = ((i < 2 ? sw0 : sw1) >> (16 * (i & 1) + 4)) & 15u;
-        const double am = lds_load<double>(lds, L.at_base + 8u * kTabSlots * (16u * b + 2u * i));
-        if (i & 1)
-          accM1 = __builtin_amdgcn_mfma_f64_16x16x4f64(am, dmin * (double)mb, accM1, 0, 0, 0);
-        else
-          accM0 = __builtin_amdgcn_mfma_f64_16x16x4f64(am, dmin * (double)mb, accM0, 0, 0, 0);
+        const uint32_t ao = L.at_base + 8u * kTabSlots * (16u * b + 2u * i);
+        const double a0 = lds_load<double>(lds, ao);
+        const double a1 = lds_load<double>(lds, ao + 32u);
+        const double wm = dmin * (double)mb;
+        accM0 = __builtin_amdgcn_mfma_f64_4x4x4f64(a0, wm, accM0, 0, 0, 0);
+        accM1 = __builtin_amdgcn_mfma_f64_4x4x4f64(a1, wm, accM1, 0, 0, 0);
       }
       double accI[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -396,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const MfmaParams p)
       for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(yI[i]));
       __builtin_amdgcn_sched_barrier(0);
     }
-    tile_sums(yI, accM0 + accM1, yv);
+    tile_sums(yI, accM0, accM1, L, yv);
   }
 
   // Second half -> LDS -> first half. The exchange area follows the tables.
