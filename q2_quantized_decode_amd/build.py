@@ -34,6 +34,13 @@ DEVICE_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+# Per-source extras. mmvq.hip: preload the m = 1 kernel's leading scalar
+# arguments into SGPRs at wave launch (the kernel keeps a fallback entry that
+# loads them, used where the firmware does not preload).
+SOURCE_FLAGS = {
+    "mmvq.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
+}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -44,8 +51,8 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *DEVICE_FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
-           os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-I", os.path.join(ROOT, "include"),
+           "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

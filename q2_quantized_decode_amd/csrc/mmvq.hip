@@ -426,9 +426,16 @@ constexpr int kStageBytes = 3072;
 // A full run is straight-line code, so the hardware wait counters are exact
 // and no wait drains the ring. Runs cut short by the end of the matrix take
 // a guarded path with one direct load per step.
+//
+// The leading scalar arguments describe the whole launch when it is one
+// matrix with interleaved runs (plain != 0): they are preloaded into SGPRs at
+// wave launch (kernel-argument preloading, enabled for this file), so that
+// case issues its first loads without reading the argument block at all.
+// Otherwise the block is fetched and resolved as for the other kernels.
 template <int GSL, int R, int CH, bool STAGED>
-__global__ __launch_bounds__(256) void mmvq_m1_kernel(const MmvqParams p) {
-  prefetch_args(p);
+__global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const uint8_t* xq0, float* y0,
+                                                      int32_t n0, int32_t k0, int32_t total_waves,
+                                                      int32_t g8, int32_t plain, const MmvqParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[STAGED ? 4 : 1][STAGED ? kStageBytes : 16];
   constexpr int GS = 1 << GSL;
   constexpr int P = 64 >> GSL;
@@ -436,14 +443,28 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const MmvqParams p) {
   static_assert(CH % V == 0 && R >= 2, "run and ring shapes");
   const int lane = threadIdx.x & 63;
   const int wiw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int g8 = p.g8;
   const int wg = blockIdx.x;
   const int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 + wiw;
-  if (wave >= p.total_waves) return;
-  const WaveJob J = resolve_wave<1>(p, wave, P);
+  if (wave >= total_waves) return;
+  WaveJob J;
+  if (plain) {
+    // one matrix, runs interleaved: wave w takes steps w, w + W, ...
+    J.w = w0;
+    J.y = y0;
+    J.x = xview(xq0, k0, 0);
+    J.n = n0;
+    J.ldy = n0;
+    J.it = wave;
+    J.it_end = (n0 + P - 1) / P;
+    J.stride = total_waves;
+    J.bad = false;
+  } else {
+    prefetch_args(p);
+    J = resolve_wave<1>(p, wave, P);
+  }
   if (J.it >= J.it_end) return;
 
-  const int k = p.k;
+  const int k = k0;
   const int nb = k >> 8;
   const int hb = lane & (GS - 1);
   const int prow = lane >> GSL;
@@ -761,10 +782,16 @@ void dispatch_narrow(const MmvqParams& p, dim3 grid, bool dots, int depth, hipSt
     const int ring = tuning().ring;
     const int ch = p.chunk;
     const bool staged = tuning().staged;
-#define Q2K_M1(G, R, C)                                                                   \
-  do {                                                                                    \
-    if (staged) hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, true>), grid, dim3(256), 0, s, p); \
-    else hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, false>), grid, dim3(256), 0, s, p);       \
+    // one matrix, interleaved runs: the kernel needs only its scalar arguments
+    const int32_t plain = (p.ids == nullptr && p.groups == 0 && p.wave_end[0] == p.total_waves &&
+                           p.interleave) ? 1 : 0;
+#define Q2K_M1_ARGS p.w[0], p.xq, p.y[0], p.n[0], p.k, p.total_waves, p.g8, plain, p
+#define Q2K_M1(G, R, C)                                                                          \
+  do {                                                                                           \
+    if (staged)                                                                                  \
+      hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, true>), grid, dim3(256), 0, s, Q2K_M1_ARGS);   \
+    else                                                                                         \
+      hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, false>), grid, dim3(256), 0, s, Q2K_M1_ARGS);  \
   } while (0)
 #define Q2K_M1_CH(G, R)                          \
   do {                                           \
@@ -786,8 +813,8 @@ void dispatch_narrow(const MmvqParams& p, dim3 grid, bool dots, int depth, hipSt
     }
 #undef Q2K_M1_RING
 #undef Q2K_M1_CH
-#undef Q2K_M1_RING
 #undef Q2K_M1
+#undef Q2K_M1_ARGS
   }
   if (dots) {
     hipLaunchKernelGGL((mmvq_narrow_kernel<M, false, 1, true>), grid, dim3(256), 0, s, p);
