@@ -34,12 +34,12 @@ DEVICE_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-# Per-source extras. mmvq.hip: preload the m = 1 kernel's leading scalar
-# arguments into SGPRs at wave launch (the kernel keeps a fallback entry that
-# loads them, used where the firmware does not preload).
-SOURCE_FLAGS = {
-    "mmvq.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
-}
+# Kernel-argument preloading: the leading scalar arguments of every kernel
+# (up to 16 SGPRs) are loaded into SGPRs at wave launch instead of by the
+# wave's first scalar loads. The code object keeps a fallback entry that
+# loads them, used where the firmware does not preload.
+DEVICE_FLAGS += ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
+SOURCE_FLAGS: dict = {}
 
 
 def hipcc() -> str:

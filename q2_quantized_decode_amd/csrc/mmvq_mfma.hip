@@ -334,24 +334,43 @@ __device__ __forceinline__ void store_tile(const Job& J, int m, int r0, const La
 // latencies that one tile's dependency chains leave; the second-half sums are
 // added to the first half's through LDS in a fixed order, so the result does
 // not depend on timing.
+//
+// The leading scalar arguments describe the whole launch when it is one
+// matrix (plain != 0); they are preloaded into SGPRs at wave launch
+// (kernel-argument preloading), so that case starts its loads without
+// reading the argument block.
 template <int NB, int R>
-__global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const MfmaParams p) {
+__global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const uint8_t* w0, const uint8_t* xq0,
+                                                             float* y0, int32_t n0, int32_t m_all,
+                                                             int32_t tgroups, int32_t total_wgs,
+                                                             int32_t g8, int32_t plain,
+                                                             const MfmaParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int k = NB * kBlockWeights;
   constexpr int NBH = NB / 2;
   static_assert(NB % 2 == 0, "row split in two halves");
   constexpr uint32_t rowbytes = (uint32_t)NB * kBlockBytes;
-  prefetch_args(p);
-  const int g8 = p.g8;
   const int wgi = (blockIdx.x & 7) * g8 + (blockIdx.x >> 3);   // XCD-major workgroup index
-  if (wgi >= p.total_wgs) return;                              // whole workgroup
+  if (wgi >= total_wgs) return;                                // whole workgroup
   // Token group tg of a row block: its kSlots tokens (fewer in the last
   // group). The groups of one block are consecutive workgroups, so they run
   // together on one XCD and read the block's weights through its L2.
-  const int job_wg = wgi / p.tgroups;
-  const int tg = wgi - job_wg * p.tgroups;
-  Job J = resolve_job<k>(p, job_wg);
-  const int m = min(kSlots, p.m - kSlots * tg);
+  const int job_wg = wgi / tgroups;
+  const int tg = wgi - job_wg * tgroups;
+  Job J;
+  if (plain) {
+    J.W = w0;
+    J.Y = y0;
+    J.X = xview(xq0, k, 0);
+    J.n = n0;
+    J.ldy = n0;
+    J.lwg = job_wg;
+    J.bad = false;
+  } else {
+    prefetch_args(p);
+    J = resolve_job<k>(p, job_wg);
+  }
+  const int m = min(kSlots, m_all - kSlots * tg);
   {
     const int64_t t0 = (int64_t)kSlots * tg;
     J.X.q += t0 * J.X.stride;
@@ -478,7 +497,9 @@ hipError_t launch_nb(const MfmaParams& p, dim3 gd, size_t shm, hipStream_t strea
     if (e != hipSuccess) return e;
     set_for[dev] = true;
   }
-  hipLaunchKernelGGL((mmvq_mfma_kernel<NB, kRing>), gd, dim3(kThreads), shm, stream, p);
+  const int32_t plain = (p.ids == nullptr && p.groups == 0 && p.wg_end[0] * p.tgroups == p.total_wgs) ? 1 : 0;
+  hipLaunchKernelGGL((mmvq_mfma_kernel<NB, kRing>), gd, dim3(kThreads), shm, stream, p.w[0], p.xq, p.y[0],
+                     p.n[0], p.m, p.tgroups, p.total_wgs, p.g8, plain, p);
   return hipGetLastError();
 }
 
