@@ -26,40 +26,64 @@ namespace q2k {
 
 namespace {
 
-struct GemvParams {
-  const uint8_t* w;
-  const uint16_t* x;     // bf16 [m, k], row stride x_stride elements
-  int64_t x_stride;
-  float* y;              // f32 [m, n]
-  int32_t n, k;
-  int32_t gs_log2;       // lanes per row = 1 << gs_log2
-  int32_t total_waves;
+// Kernel arguments (scalars, preloaded into SGPRs at wave launch):
+//   w        Q2_K rows [n, k/256] x 84 bytes
+//   x        bf16 [m, k], row stride x_stride elements
+//   y        f32 [m, n]
+//   gs_log2  lanes per row = 1 << gs_log2
+
+// The four bf16 values one sub-block's 2-bit quants can take, T[q] =
+// bf16_rne(d*sc*q - dmin*m) for q = 0..3 (the same f32 fma and rounding as
+// the per-weight expansion), packed two per dword: lo = T0 | T1 << 16,
+// hi = T2 | T3 << 16.
+struct Table {
+  uint32_t lo, hi;
 };
 
-// bf16 round-to-nearest-even of a finite f32, returned as the f32 it represents.
-__device__ __forceinline__ float bf16_rne_f32(float v) {
-  uint32_t u = __float_as_uint(v);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return __uint_as_float(u & 0xffff0000u);
+__device__ __forceinline__ Table sub_block_table(float dsc, float dmm) {
+  uint32_t t[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t u = __float_as_uint(fmaf(dsc, (float)q, -dmm));
+    t[q] = u + 0x7fffu + ((u >> 16) & 1u);   // bf16 value in the high half
+  }
+  // high halves of t[0], t[1] -> lo; of t[2], t[3] -> hi
+  return Table{__builtin_amdgcn_perm(t[1], t[0], 0x07060302u), __builtin_amdgcn_perm(t[3], t[2], 0x07060302u)};
+}
+
+// f32 values (bf16 in the high half) of the weights whose quants are bytes
+// 2i and 2i + 1 of qm (values 0..3): v_perm picks T[q] out of the packed
+// table with selector bytes (2q, 2q + 1).
+__device__ __forceinline__ void lookup2(const Table& T, uint32_t qm, int i, float& wa, float& wb) {
+  const uint32_t dup = __builtin_amdgcn_perm(qm, qm, i ? 0x03030202u : 0x01010000u);  // qa qa qb qb
+  const uint32_t sel = (dup << 1) + 0x01000100u;                                    // 2qa 2qa+1 2qb 2qb+1
+  const uint32_t pair = __builtin_amdgcn_perm(T.hi, T.lo, sel);                     // T[qa] | T[qb] << 16
+  wa = __uint_as_float(pair << 16);
+  wb = __uint_as_float(pair & 0xffff0000u);
 }
 
 // One plane j (elements 32j .. 32j+31) of a half block: the 32 quants come
 // from qs bytes 0..31 of the half (q0 = bytes 0..15, q1 = 16..31), bits 2j;
-// elements l < 16 use sub-block scale byte s0, the rest s1. xw holds the
-// plane's 32 bf16 activations as 16 dwords (element 2i in the low half).
-__device__ __forceinline__ void plane_dot(const u32x4& q0, const u32x4& q1, uint32_t s0, uint32_t s1,
-                                          float d, float dmin, int j, const uint32_t xw[16],
-                                          double acc[4]) {
-  const float dsc0 = d * (float)(s0 & 15u), dmm0 = dmin * (float)(s0 >> 4);
-  const float dsc1 = d * (float)(s1 & 15u), dmm1 = dmin * (float)(s1 >> 4);
+// elements l < 16 use sub-block table T0, the rest T1. xw holds the plane's
+// 32 bf16 activations as 16 dwords (element 2i in the low half). Every
+// product of two bf16 values is exact in f32 and is summed in fp64.
+__device__ __forceinline__ void plane_dot(const u32x4& q0, const u32x4& q1, const Table& T0,
+                                          const Table& T1, int j, const uint32_t xw[16], double acc[4]) {
 #pragma unroll
-  for (int l = 0; l < 32; ++l) {
-    const uint32_t word = l < 16 ? q0[l >> 2] : q1[(l - 16) >> 2];
-    const uint32_t q = (word >> (8 * (l & 3) + 2 * j)) & 3u;
-    const float wv = bf16_rne_f32(fmaf(l < 16 ? dsc0 : dsc1, (float)q, l < 16 ? -dmm0 : -dmm1));
-    const uint32_t xb = xw[l >> 1];
-    const float xv = __uint_as_float((l & 1) ? (xb & 0xffff0000u) : (xb << 16));
-    acc[l & 3] += (double)(wv * xv);
+  for (int w = 0; w < 8; ++w) {
+    const uint32_t word = w < 4 ? q0[w] : q1[w - 4];
+    const uint32_t qm = (word >> (2 * j)) & 0x03030303u;
+    const Table& T = w < 4 ? T0 : T1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float wa, wb;
+      lookup2(T, qm, i, wa, wb);
+      const uint32_t xb = xw[2 * w + i];
+      const float xa = __uint_as_float(xb << 16);
+      const float xbv = __uint_as_float(xb & 0xffff0000u);
+      acc[2 * i] += (double)(wa * xa);
+      acc[2 * i + 1] += (double)(wb * xbv);
+    }
   }
 }
 
@@ -77,36 +101,38 @@ __device__ __forceinline__ void load_plane_x(const uint16_t* xrow, int e0, uint3
 // M tokens; CACHE_X: one token and one half block per lane, activations kept
 // in VGPRs across steps.
 template <int M, bool CACHE_X>
-__global__ __launch_bounds__(256) void gemv_bf16_kernel(const GemvParams p) {
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint8_t* w, const uint16_t* x, float* y,
+                                                        int64_t x_stride, int32_t n, int32_t k,
+                                                        int32_t gs_log2, int32_t total_waves) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  if (wave >= p.total_waves) return;
-  const int nb = p.k >> 8;
-  const int gs = 1 << p.gs_log2;
-  const int P = 64 >> p.gs_log2;
-  const int prow = lane >> p.gs_log2;
+  if (wave >= total_waves) return;
+  const int nb = k >> 8;
+  const int gs = 1 << gs_log2;
+  const int P = 64 >> gs_log2;
+  const int prow = lane >> gs_log2;
   const int hb0 = lane & (gs - 1);
   const size_t rowbytes = (size_t)nb * kBlockBytes;
-  const int steps = (p.n + P - 1) / P;
+  const int steps = (n + P - 1) / P;
 
   uint32_t xc[CACHE_X ? 4 : 1][CACHE_X ? 16 : 1];
   if constexpr (CACHE_X) {
     const int hb = hb0 < 2 * nb ? hb0 : 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_plane_x(p.x, 128 * hb + 32 * j, xc[j]);
+    for (int j = 0; j < 4; ++j) load_plane_x(x, 128 * hb + 32 * j, xc[j]);
   }
 
-  for (int st = wave; st < steps; st += p.total_waves) {
+  for (int st = wave; st < steps; st += total_waves) {
     const int row = st * P + prow;
     double acc[M][4];
 #pragma unroll
     for (int t = 0; t < M; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[t][i] = 0.0;
-    if (row < p.n) {
+    if (row < n) {
       for (int hb = hb0; hb < 2 * nb; hb += gs) {
         const int b = hb >> 1, h = hb & 1;
-        const uint8_t* blk = p.w + (size_t)row * rowbytes + (size_t)b * kBlockBytes;
+        const uint8_t* blk = w + (size_t)row * rowbytes + (size_t)b * kBlockBytes;
         const u32x4 q0 = gload<u32x4_a4>(blk + 16 + 32 * h);
         const u32x4 q1 = gload<u32x4_a4>(blk + 32 + 32 * h);
         const u32x2 sc = gload<u32x2_a4>(blk + 8 * h);
@@ -118,14 +144,16 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const GemvParams p) {
           // sub-blocks 8h + 2j and 8h + 2j + 1: scale bytes 2j, 2j + 1 of this half
           const uint32_t sw = sc[j >> 1] >> (16 * (j & 1));
           const uint32_t s0 = sw & 0xffu, s1 = (sw >> 8) & 0xffu;
+          const Table T0 = sub_block_table(d * (float)(s0 & 15u), dmin * (float)(s0 >> 4));
+          const Table T1 = sub_block_table(d * (float)(s1 & 15u), dmin * (float)(s1 >> 4));
           if constexpr (CACHE_X) {
-            plane_dot(q0, q1, s0, s1, d, dmin, j, xc[j], acc[0]);
+            plane_dot(q0, q1, T0, T1, j, xc[j], acc[0]);
           } else {
 #pragma unroll
             for (int t = 0; t < M; ++t) {
               uint32_t xw[16];
-              load_plane_x(p.x + (int64_t)t * p.x_stride, 256 * b + 128 * h + 32 * j, xw);
-              plane_dot(q0, q1, s0, s1, d, dmin, j, xw, acc[t]);
+              load_plane_x(x + (int64_t)t * x_stride, 256 * b + 128 * h + 32 * j, xw);
+              plane_dot(q0, q1, T0, T1, j, xw, acc[t]);
             }
           }
         }
@@ -135,7 +163,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const GemvParams p) {
     for (int t = 0; t < M; ++t) {
       double v = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
       for (int off = gs >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
-      if (hb0 == 0 && row < p.n) p.y[(int64_t)t * p.n + row] = (float)v;
+      if (hb0 == 0 && row < n) y[(int64_t)t * n + row] = (float)v;
     }
   }
 }
@@ -153,19 +181,29 @@ int cu_count_gemv() {
   return counts[dev];
 }
 
+struct GemvArgs {
+  const uint8_t* w;
+  const uint16_t* x;
+  float* y;
+  int64_t x_stride;
+  int32_t n, k, gs_log2, total_waves;
+};
+
 template <int M>
-void launch_m(const GemvParams& p, dim3 grid, bool cache_x, hipStream_t s) {
+void launch_m(const GemvArgs& a, dim3 grid, bool cache_x, hipStream_t s) {
   if (M == 1 && cache_x)
-    hipLaunchKernelGGL((gemv_bf16_kernel<1, true>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemv_bf16_kernel<1, true>), grid, dim3(256), 0, s, a.w, a.x, a.y, a.x_stride,
+                       a.n, a.k, a.gs_log2, a.total_waves);
   else
-    hipLaunchKernelGGL((gemv_bf16_kernel<M, false>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemv_bf16_kernel<M, false>), grid, dim3(256), 0, s, a.w, a.x, a.y, a.x_stride,
+                       a.n, a.k, a.gs_log2, a.total_waves);
 }
 
 }  // namespace
 
 hipError_t launch_gemv_bf16(const void* w, const void* x, int64_t x_stride, float* y, int n, int k,
                             int m, hipStream_t stream) {
-  GemvParams p{};
+  GemvArgs p{};
   p.w = static_cast<const uint8_t*>(w);
   p.x = static_cast<const uint16_t*>(x);
   p.x_stride = x_stride;

@@ -284,6 +284,22 @@ def test_pair_attention_inputs(m):
     assert np.array_equal(sb.view(np.uint32), yb.cpu().numpy().view(np.uint32))
 
 
+@pytest.mark.parametrize("n,k", [(1000, 2048), (130, 7168), (4099, 1024)])
+def test_single_token_launch_forms_agree(n, k):
+    """One token: a single-matrix launch (arguments in the leading scalars)
+    and the same matrix as half of a pair (arguments in the block) give the
+    same bits, including waves whose runs end early."""
+    case = syn.single_gemv_case(n=n, k=k, m=1, seed=n + k)
+    w = dev(case.w.reshape(-1))
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits))
+    oq, od = assert_q8_equal(xq, case.x_bits)
+    single = q2.q2k_mmvq(w, xq, n, k, 1).cpu().numpy()
+    ya, yb = q2.q2k_mmvq_pair(w, n, w, n, xq, k, 1)
+    assert np.array_equal(single.view(np.uint32), ya.cpu().numpy().view(np.uint32))
+    assert np.array_equal(single.view(np.uint32), yb.cpu().numpy().view(np.uint32))
+    assert_close(single, orc.mmvq(case.w, oq, od), f"single token n={n} k={k}")
+
+
 def test_pair_ragged():
     pc = syn.attention_pair_case(3, seed=9, na=37, nb=5, k=1280)
     xq = q2.q8_1_rows(bf16_dev(pc.x_bits))
