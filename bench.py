@@ -200,11 +200,12 @@ def bench_grouped(torch, q2, syn, dev, copies_n: int = 64):
 def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
     """The engram step on the device, one token per step: n-gram hash (2
     hashed layers, 3-grams, 4 heads = 8 row ids), gather + dequantisation of
-    8 table rows (500 000-row table), q8_1 of the [1, 2048] row, the wkv
-    product [20480, 2048] (80 rotating copies, 1.1 GB) and the gate on
-    [1, 4, 4096]; graphs of 16 steps, HIP events around the replays. The hash
-    alone is timed the same way, for one decode token and a 4096-token
-    prefill."""
+    8 table rows (500 000-row table) and q8_1 of the [1, 2048] row in one
+    launch, the wkv product [20480, 2048] (80 rotating copies, 1.1 GB) and
+    the gate on [1, 4, 4096]; graphs of 16 steps, HIP events around the
+    replays. The same step with the gather and the q8_1 as two launches, and
+    the hash alone (one decode token, a 4096-token prefill), are timed the
+    same way."""
     e = syn.engram_step_case()
     hc = syn.engram_hash_case(seqlen=4096)
     tm, mu, pr, of = (torch.from_numpy(a).to(dev) for a in
@@ -225,6 +226,12 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
     q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks, 0)
 
     def step(i):
+        q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks[i % 64:i % 64 + 1], 4096 + (i % 64), out=ids)
+        q2.q2k_dequant_rows_q8_1(table, 500000, ids[1].reshape(-1), 8, xq=xq)
+        q2.q2k_mmvq(copies[i % copies_n], xq, n_out, 2048, 1, out=kv)
+        q2.engram_gate(h, kv, qk, e.eps)
+
+    def step_unfused(i):
         q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks[i % 64:i % 64 + 1], 4096 + (i % 64), out=ids)
         q2.q2k_dequant_rows(table, 500000, ids[1].reshape(-1), 8, out=rows)
         q2.q8_1_rows(rows.view(1, 2048), out=xq)
@@ -265,6 +272,7 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
         q2.engram_gate(h, kv, qk, e.eps)
 
     us_step = timed(step, copies_n)
+    us_step_unfused = timed(step_unfused, copies_n)
     us_step_bf16 = timed(step_bf16, copies_n)
     us_gemv = timed(lambda i: q2.q2k_gemv_bf16(copies[i % copies_n], rows.view(1, 2048), n_out, 2048,
                                                out=kv), copies_n)
@@ -274,10 +282,12 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
     pre = torch.empty((2, 4096, 8), dtype=torch.int64, device=dev)
     us_pre = timed(lambda i: q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks, 0, out=pre), 16)
     wkv_bytes = w0.numel()
-    return {"workload": "engram step, one token: hash -> 8-row gather -> q8_1 -> wkv Q2_K "
-                        "[20480, 2048] -> gate [1, 4, 4096]; 80 rotating wkv copies. The bf16 "
-                        "route skips q8_1: gathered bf16 rows straight into the wkv product",
+    return {"workload": "engram step, one token: hash -> 8-row gather + dequant + q8_1 (one "
+                        "launch) -> wkv Q2_K [20480, 2048] -> gate [1, 4, 4096]; 80 rotating wkv "
+                        "copies. The unfused step gathers and quantises in two launches; the "
+                        "bf16 route skips q8_1: gathered bf16 rows straight into the wkv product",
             "us_per_step": round(us_step, 3), "tokens_per_s": round(1e6 / us_step, 1),
+            "us_per_step_unfused": round(us_step_unfused, 3),
             "us_per_step_bf16_route": round(us_step_bf16, 3),
             "wkv_bytes": wkv_bytes,
             "wkv_q8_1_product_us": round(us_mmvq, 3),

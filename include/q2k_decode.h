@@ -61,7 +61,7 @@ extern "C" {
 #define Q2K_API
 #endif
 
-#define Q2K_ABI_VERSION 2
+#define Q2K_ABI_VERSION 3
 
 #define Q2K_OK 0
 #define Q2K_EINVAL (-1)   /* NULL pointer, or pointers that must not overlap do */
@@ -210,6 +210,25 @@ Q2K_API int32_t swiglu_q8_1_rows(const float* g_dev, const float* u_dev, void* h
 Q2K_API int32_t q2k_dequant_rows(const void* table_dev, int64_t n_table_rows,
                          const int64_t* ids_dev, int32_t n_rows, void* out_bf16_dev,
                          int32_t* err_flag_dev, void* stream);
+
+/* Engram rows gathered, dequantised and quantised to q8_1 in one launch:
+ * q2k_dequant_rows followed by q8_1_rows on its output viewed as one row of
+ * 256 * n_rows values (the engram step feeds the gathered rows to the wkv
+ * projection as one [1, 256 * n_rows] activation: engram_v41/apply.rs,
+ * apply; engram_v41.rs module doc steps 2 and 3), with the same bits as
+ * those two calls.
+ *   table_dev, ids_dev, n_rows, err_flag_dev : as q2k_dequant_rows
+ *                  (1 <= n_rows <= 2^20).
+ *   out_bf16_dev : nullable bf16 [n_rows, 256], 16-byte aligned; receives
+ *                  the dequantised rows when non-NULL.
+ *   xq_dev       : one q8_1 row of width 256 * n_rows, 16-byte aligned,
+ *                  xq_bytes >= q8_1_rows_bytes(1, 256 * n_rows).
+ * Errors: Q2K_EINVAL (null table or xq, outputs overlapping the table or
+ * each other), Q2K_ESHAPE, Q2K_ESPACE (xq too small, or contiguous rows past
+ * the table), Q2K_EALIGN. */
+Q2K_API int32_t q2k_dequant_rows_q8_1(const void* table_dev, int64_t n_table_rows,
+                         const int64_t* ids_dev, int32_t n_rows, void* out_bf16_dev,
+                         void* xq_dev, size_t xq_bytes, int32_t* err_flag_dev, void* stream);
 
 /* Engram gate, in place on the f32 stream (engram_v41/apply.rs: grid
  * [T, hc], arguments streams, kv, qk, dim, hc, eps; engram_v41.rs module doc

@@ -42,6 +42,7 @@ SIGNATURES = {
     "q2k_gemv_bf16": (_I32, [_VP, _VP, _I64, _VP, _I32, _I32, _I32, _VP]),
     "swiglu_q8_1_rows": (_I32, [_VP, _VP, _VP, _VP, _SZ, _I32, _I32, _VP]),
     "q2k_dequant_rows": (_I32, [_VP, _I64, _VP, _I32, _VP, _VP, _VP]),
+    "q2k_dequant_rows_q8_1": (_I32, [_VP, _I64, _VP, _I32, _VP, _VP, _SZ, _VP, _VP]),
     "engram_gate": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _F32, _VP]),
     "q2k_block_dots": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     "engram_hash": (_I32, [_VP, _I64, _VP, _VP, _VP, _I32, _I32, _I32, _I64, _VP, _I64, _VP, _I32,
@@ -234,6 +235,28 @@ def q2k_dequant_rows(table: torch.Tensor, n_table_rows: int, ids: Optional[torch
     _check("q2k_dequant_rows", lib().q2k_dequant_rows(
         _contig(table, "table"), n_table_rows, idp, n_rows, _contig(out, "out"), flag, _stream()))
     return out
+
+
+def q2k_dequant_rows_q8_1(table: torch.Tensor, n_table_rows: int, ids: Optional[torch.Tensor],
+                          n_rows: int, xq: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, want_rows: bool = False,
+                          err_flag: Optional[torch.Tensor] = None):
+    """Gathered rows as one q8_1 row of width 256 * n_rows (and, with
+    ``want_rows`` or ``out``, their bf16 [n_rows, 256] values)."""
+    if ids is not None and ids.dtype != torch.int64:
+        raise ValueError("ids must be int64")
+    if out is None and want_rows:
+        out = torch.empty((n_rows, BLOCK_WEIGHTS), dtype=torch.bfloat16, device=table.device)
+    need = q8_1_rows_bytes(1, n_rows * BLOCK_WEIGHTS)
+    if xq is None:
+        xq = torch.empty(max(need, 16), dtype=torch.uint8, device=table.device)
+    idp = _contig(ids, "ids") if ids is not None else None
+    op = _contig(out, "out") if out is not None else None
+    flag = _contig(err_flag, "err_flag") if err_flag is not None else None
+    _check("q2k_dequant_rows_q8_1", lib().q2k_dequant_rows_q8_1(
+        _contig(table, "table"), n_table_rows, idp, n_rows, op, _contig(xq, "xq"), xq.numel(), flag,
+        _stream()))
+    return xq, out
 
 
 def engram_gate(h: torch.Tensor, kv: torch.Tensor, qk: torch.Tensor, eps: float) -> torch.Tensor:

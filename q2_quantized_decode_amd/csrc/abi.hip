@@ -317,6 +317,29 @@ int32_t q2k_dequant_rows(const void* table_dev, int64_t n_table_rows, const int6
                                            err_flag_dev, (hipStream_t)stream), fn);
 }
 
+int32_t q2k_dequant_rows_q8_1(const void* table_dev, int64_t n_table_rows, const int64_t* ids_dev,
+                              int32_t n_rows, void* out_bf16_dev, void* xq_dev, size_t xq_bytes,
+                              int32_t* err_flag_dev, void* stream) {
+  const char* fn = "q2k_dequant_rows_q8_1";
+  if (!table_dev || !xq_dev) return fail(Q2K_EINVAL, "%s: null pointer", fn);
+  if (n_rows < 1 || n_rows > (1 << 20)) return fail(Q2K_ESHAPE, "%s: n_rows = %d outside 1..2^20", fn, n_rows);
+  if (n_table_rows < 1) return fail(Q2K_ESHAPE, "%s: empty table", fn);
+  if (!ids_dev && n_rows > n_table_rows)
+    return fail(Q2K_ESPACE, "%s: %d contiguous rows from a %lld-row table", fn, n_rows, (long long)n_table_rows);
+  if (!aligned(table_dev, 4) || !aligned(xq_dev, 16) || (ids_dev && !aligned(ids_dev, 8)) ||
+      (out_bf16_dev && !aligned(out_bf16_dev, 16)))
+    return fail(Q2K_EALIGN, "%s: table must be 4-byte, ids 8-byte, out and xq 16-byte aligned", fn);
+  const int32_t k = n_rows * 256;
+  const size_t need = q8_1_rows_bytes(1, k);
+  if (xq_bytes < need) return fail(Q2K_ESPACE, "%s: xq holds %zu bytes, %zu needed", fn, xq_bytes, need);
+  const size_t tb = (size_t)n_table_rows * 84, ob = (size_t)k * 2;
+  if (overlap(xq_dev, need, table_dev, tb) ||
+      (out_bf16_dev && (overlap(out_bf16_dev, ob, table_dev, tb) || overlap(out_bf16_dev, ob, xq_dev, need))))
+    return fail(Q2K_EINVAL, "%s: an output overlaps the table or the other output", fn);
+  return launched(q2k::launch_dequant_rows_q8_1(table_dev, n_table_rows, ids_dev, n_rows, out_bf16_dev,
+                                                xq_dev, err_flag_dev, (hipStream_t)stream), fn);
+}
+
 int32_t engram_gate(float* h_dev, const float* kv_dev, const float* qk_dev, int32_t t, int32_t hc,
                     int32_t dim, float eps, void* stream) {
   const char* fn = "engram_gate";

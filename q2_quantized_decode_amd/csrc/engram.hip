@@ -33,26 +33,8 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(const uint8_t* __rest
     if (lane == 0 && err_flag != nullptr) *err_flag = 1;
     return;
   }
-  const uint8_t* blk = table + id * kBlockBytes;
-  const int e = 4 * lane;            // elements e .. e+3 share h, j and sub-block
-  const int h = e >> 7;
-  const int j = (e >> 5) & 3;
-  const int l = e & 31;
-  const uint32_t qw = *reinterpret_cast<const uint32_t*>(blk + 16 + 32 * h + l) >> (2 * j);
-  const uint32_t sb = blk[e >> 4];
-  const uint32_t dd = *reinterpret_cast<const uint32_t*>(blk + 80);
-  const float d = fp16_bits_to_f32(dd & 0xffffu);
-  const float dmin = fp16_bits_to_f32(dd >> 16);
-  const float mterm = dmin * (float)(sb >> 4);   // exact: <= 15 significant bits
   uint32_t bits[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t q = (qw >> (8 * i)) & 3u;
-    // d * (sc*q) is exact in f32, so the subtraction is the only rounding,
-    // whether or not it is fused.
-    const float v = d * (float)((sb & 15u) * q) - mterm;
-    bits[i] = f32_to_bf16_bits(v);
-  }
+  q2k_dequant4(table + id * kBlockBytes, 4 * lane, bits);
   *reinterpret_cast<u32x2*>(o) = u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
 }
 

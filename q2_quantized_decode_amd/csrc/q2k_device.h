@@ -71,4 +71,26 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
 
 __device__ __forceinline__ float quiet_nan() { return __uint_as_float(0x7fc00000u); }
 
+// bf16 bits of elements e..e+3 (e a multiple of 4) of one 84-byte Q2_K block:
+// v = d*sc*q - dmin*m formed in f32 (d*(sc*q) and dmin*m are exact, so the
+// subtraction is the only rounding), then bf16 to nearest-even. The four
+// elements share h = e>>7, plane j = (e>>5)&3 and sub-block e>>4.
+__device__ __forceinline__ void q2k_dequant4(const uint8_t* blk, int e, uint32_t bits[4]) {
+  const int h = e >> 7;
+  const int j = (e >> 5) & 3;
+  const int l = e & 31;
+  const uint32_t qw = *reinterpret_cast<const uint32_t*>(blk + 16 + 32 * h + l) >> (2 * j);
+  const uint32_t sb = blk[e >> 4];
+  const uint32_t dd = *reinterpret_cast<const uint32_t*>(blk + 80);
+  const float d = fp16_bits_to_f32(dd & 0xffffu);
+  const float dmin = fp16_bits_to_f32(dd >> 16);
+  const float mterm = dmin * (float)(sb >> 4);   // exact: <= 15 significant bits
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t q = (qw >> (8 * i)) & 3u;
+    const float v = d * (float)((sb & 15u) * q) - mterm;
+    bits[i] = f32_to_bf16_bits(v);
+  }
+}
+
 }  // namespace q2k

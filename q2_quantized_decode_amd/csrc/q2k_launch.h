@@ -58,6 +58,10 @@ hipError_t launch_gemv_bf16(const void* w, const void* x, int64_t x_stride, floa
                             int m, hipStream_t stream);
 hipError_t launch_dequant_rows(const void* table, int64_t n_table_rows, const int64_t* ids,
                                int n_rows, void* out, int32_t* err_flag, hipStream_t stream);
+// Gathered rows -> optional bf16 copy -> one q8_1 row of width 256 * n_rows.
+hipError_t launch_dequant_rows_q8_1(const void* table, int64_t n_table_rows, const int64_t* ids,
+                                    int n_rows, void* out, void* xq, int32_t* err_flag,
+                                    hipStream_t stream);
 hipError_t launch_engram_gate(float* h, const float* kv, const float* qk, int t, int hc, int dim,
                               float eps, hipStream_t stream);
 hipError_t launch_engram_hash(const int64_t* token_map, int64_t vocab, const int64_t* mult,

@@ -122,6 +122,57 @@ __global__ __launch_bounds__(256) void swiglu_q8_1_rows_kernel(const float* __re
   q8_1_store8(v, hq + row * q8_row_bytes(k), e0, k, active);
 }
 
+// Gathered Q2_K table rows -> bf16 (optional output) -> one q8_1 row of
+// width 256 * n_rows: lane i takes elements 8i..8i+7, i.e. elements
+// e = 8i mod 256 .. +7 of row 8i / 256, dequantised exactly as
+// dequant_rows_kernel does and quantised exactly as q8_1_rows_kernel does
+// (an id outside the table gives that row NaN bf16 values, as there).
+__global__ __launch_bounds__(256) void dequant_rows_q8_1_kernel(const uint8_t* __restrict__ table,
+                                                                int64_t n_table_rows,
+                                                                const int64_t* __restrict__ ids,
+                                                                int n_rows, uint16_t* __restrict__ out,
+                                                                uint8_t* __restrict__ xq,
+                                                                int32_t* err_flag) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int k = n_rows * kBlockWeights;
+  const bool active = gid < k / 8;
+  const int e0 = active ? (int)gid * 8 : 0;
+  const int row = e0 / kBlockWeights, e = e0 % kBlockWeights;
+  const int64_t id = ids ? ids[row] : row;
+  const bool bad = id < 0 || id >= n_table_rows;
+  uint32_t bits[8];
+  if (bad) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bits[i] = 0x7fc0u;
+    if (active && e == 0 && err_flag != nullptr) *err_flag = 1;
+  } else {
+    const uint8_t* blk = table + id * kBlockBytes;
+    q2k_dequant4(blk, e, bits);
+    q2k_dequant4(blk, e + 4, bits + 4);
+  }
+  if (active && out != nullptr) {
+    u32x4 packed;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed[i] = bits[2 * i] | (bits[2 * i + 1] << 16);
+    *reinterpret_cast<u32x4*>(out + e0) = packed;
+  }
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = bf16_bits_to_f32(bits[i]);
+  q8_1_store8(v, xq, e0, k, active);
+}
+
+hipError_t launch_dequant_rows_q8_1(const void* table, int64_t n_table_rows, const int64_t* ids,
+                                    int n_rows, void* out, void* xq, int32_t* err_flag,
+                                    hipStream_t stream) {
+  const int64_t lanes = (int64_t)n_rows * (kBlockWeights / 8);
+  const int64_t blocks = (lanes + 255) / 256;
+  hipLaunchKernelGGL(dequant_rows_q8_1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(table), n_table_rows, ids, n_rows,
+                     static_cast<uint16_t*>(out), static_cast<uint8_t*>(xq), err_flag);
+  return hipGetLastError();
+}
+
 hipError_t launch_q8_1_rows(const void* x, int64_t stride, void* xq, int m, int k,
                             hipStream_t stream) {
   const int64_t lanes = (int64_t)m * (k / 8);

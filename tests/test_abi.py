@@ -38,7 +38,7 @@ def test_header_symbols_exported(L):
 
 
 def test_version_and_sizes(L):
-    assert L.q2k_abi_version() == 2
+    assert L.q2k_abi_version() == 3
     assert L.q8_1_rows_bytes(1, 1024) == 1280
     assert L.q8_1_rows_bytes(8, 7168) == 8 * 8960
     assert L.q8_1_rows_bytes(0, 1024) == 0
@@ -118,6 +118,24 @@ def test_engram_hash_validation(L):
     assert call(cache=T + 0x400004) == EALIGN
     assert call(ids=T + 0x500002) == EALIGN
     assert call(out=T + 0x400000) == EINVAL           # out on the cache
+
+
+def test_dequant_rows_q8_1_validation(L):
+    T, X, O, I = 0x7f0002000000, 0x7f0003000000, 0x7f0004000000, 0x7f0005000000
+    need = L.q8_1_rows_bytes(1, 8 * 256)
+    assert L.q2k_dequant_rows_q8_1(None, 10, I, 8, O, X, need, None, None) == EINVAL
+    assert L.q2k_dequant_rows_q8_1(T, 10, I, 8, O, None, need, None, None) == EINVAL
+    assert L.q2k_dequant_rows_q8_1(T, 10, I, 0, O, X, need, None, None) == ESHAPE
+    assert L.q2k_dequant_rows_q8_1(T, 0, I, 8, O, X, need, None, None) == ESHAPE
+    assert L.q2k_dequant_rows_q8_1(T, 4, None, 8, O, X, need, None, None) == ESPACE   # rows past the table
+    assert L.q2k_dequant_rows_q8_1(T, 10, I, 8, O, X, need - 1, None, None) == ESPACE
+    assert "needed" in _err(L)
+    assert L.q2k_dequant_rows_q8_1(T + 2, 10, I, 8, O, X, need, None, None) == EALIGN
+    assert L.q2k_dequant_rows_q8_1(T, 10, I, 8, O + 8, X, need, None, None) == EALIGN
+    assert L.q2k_dequant_rows_q8_1(T, 10, I, 8, O, X + 8, need, None, None) == EALIGN
+    assert L.q2k_dequant_rows_q8_1(T, 10, I + 4, 8, O, X, need, None, None) == EALIGN
+    assert L.q2k_dequant_rows_q8_1(T, 1000, I, 8, O, T + 256, need, None, None) == EINVAL   # xq in the table
+    assert L.q2k_dequant_rows_q8_1(T, 10, I, 8, X + 1024, X, need, None, None) == EINVAL    # out on xq
 
 
 def test_gemv_bf16_validation(L):

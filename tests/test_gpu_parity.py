@@ -455,6 +455,42 @@ def test_dequant_rows_bit_exact(engram):
     assert np.array_equal(got, orc.dequant_rows_bf16_bits(engram.table[:13], None))
 
 
+@pytest.mark.parametrize("n_rows", [1, 8, 37])
+def test_dequant_rows_q8_1_is_the_composition(engram, n_rows):
+    """One launch gives the bits of q2k_dequant_rows then q8_1_rows on the
+    rows viewed as one [1, 256 n_rows] row, and matches the oracle."""
+    table = dev(engram.table.reshape(-1))
+    nt = engram.table.shape[0]
+    ids_np = syn.rng_for(7300, n_rows).integers(0, nt, size=n_rows, dtype=np.int64)
+    ids = dev(ids_np)
+    rows = q2.q2k_dequant_rows(table, nt, ids, n_rows)
+    xq_ref = q2.q8_1_rows(rows.view(1, n_rows * 256))
+    xq, out = q2.q2k_dequant_rows_q8_1(table, nt, ids, n_rows, want_rows=True)
+    need = q2.q8_1_rows_bytes(1, n_rows * 256)
+    assert torch.equal(xq[:need], xq_ref[:need])
+    assert torch.equal(out.view(torch.int16), rows.view(torch.int16))
+    bits = orc.dequant_rows_bf16_bits(engram.table, ids_np).reshape(1, -1)
+    assert_q8_equal(xq, bits)
+    xq2, none = q2.q2k_dequant_rows_q8_1(table, nt, ids, n_rows)    # no bf16 copy
+    assert none is None and torch.equal(xq2[:need], xq_ref[:need])
+
+
+def test_dequant_rows_q8_1_bad_ids_match_the_composition():
+    table = np.zeros((3, 84), dtype=np.uint8)
+    table[:, 0:16] = 0x25
+    table[:, 16:80] = 0x9C
+    table[:, 80:84] = [0x00, 0x3C, 0x00, 0x38]
+    ids = dev(np.array([0, 5, 2, -1], dtype=np.int64))
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rows = q2.q2k_dequant_rows(dev(table.reshape(-1)), 3, ids, 4)
+    xq_ref = q2.q8_1_rows(rows.view(1, 1024))
+    xq, out = q2.q2k_dequant_rows_q8_1(dev(table.reshape(-1)), 3, ids, 4, want_rows=True, err_flag=flag)
+    need = q2.q8_1_rows_bytes(1, 1024)
+    assert torch.equal(xq[:need], xq_ref[:need])
+    assert torch.equal(out.view(torch.int16), rows.view(torch.int16))
+    assert int(flag.item()) == 1
+
+
 def test_dequant_rows_hand_blocks_and_bad_ids():
     table = np.zeros((3, 84), dtype=np.uint8)
     table[0, 0:16] = [((15 - s) << 4) | s for s in range(16)]
