@@ -405,22 +405,16 @@ __device__ __forceinline__ WHalf load_whalf_at(const uint8_t* base, const LaneOf
   return r;
 }
 
-// Per-wave LDS staging area for one row step (at most 64 half blocks, i.e.
-// 2688 bytes, rounded up to three 1 KB wave-wide 16-byte loads).
-constexpr int kStageBytes = 3072;
-
 // One token, rows of at most 64 half blocks and at least 8 lanes per row
 // (k from 1024 to 8192). Each wave owns a run of CH row steps (CH a multiple
 // of 8, known at compile time), either consecutive or interleaved with the
 // other runs of the matrix (stride S) so that the waves sweep the matrix
 // together. A step is P whole rows (contiguous bytes); lane l works on half
 // block l % GS of row l / GS. Per step:
-//  * direct path (default): each lane loads its half block's fields (32
-//    quant bytes, 8 scale bytes, d/dmin) into a ring of R register sets, R
-//    steps ahead of the arithmetic;
-//  * staged path (STAGED): the step arrives by three wave-wide coalesced
-//    16-byte loads, goes through the wave's own LDS area, and each lane reads
-//    its fields back (measured slower: LDS bank conflicts on the field reads);
+//  * each lane loads its half block's fields (32 quant bytes, 8 scale bytes,
+//    d/dmin) into a ring of R register sets, R steps ahead of the arithmetic
+//    (a variant that brought each step in by coalesced 16-byte loads through
+//    LDS measured slower: bank conflicts on the field reads);
 //  * the activations stay in VGPRs for the whole run; the sums of eight
 //    consecutive steps are reduced together (one transposed butterfly).
 // A full run is straight-line code, so the hardware wait counters are exact
@@ -432,11 +426,10 @@ constexpr int kStageBytes = 3072;
 // wave launch (kernel-argument preloading, enabled for this file), so that
 // case issues its first loads without reading the argument block at all.
 // Otherwise the block is fetched and resolved as for the other kernels.
-template <int GSL, int R, int CH, bool STAGED>
+template <int GSL, int R, int CH>
 __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const uint8_t* xq0, float* y0,
                                                       int32_t n0, int32_t k0, int32_t total_waves,
                                                       int32_t g8, int32_t plain, const MmvqParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage[STAGED ? 4 : 1][STAGED ? kStageBytes : 16];
   constexpr int GS = 1 << GSL;
   constexpr int P = 64 >> GSL;
   constexpr int V = 8;
@@ -488,8 +481,8 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
   const AHalf act = load_ahalf(J.x, 0, b, h);
   double dq[4], dm[4];
 
-  if (full && !STAGED) {
-    // Direct path: each lane loads its own half block's fields.
+  if (full) {
+    // Each lane loads its own half block's fields.
     const LaneOffsets off = lane_offsets((uint32_t)prow * rowbytes + (uint32_t)b * kBlockBytes, h);
     WHalf ws[R];
 #pragma unroll
@@ -508,60 +501,6 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
         const double t = half_block_value_m1(ws[v % R], act, dq, dm);
         if (st + R < CH) ws[v % R] = load_whalf_at(wrun + (size_t)(st + R) * run_stride, off);
         acc[v] = hb_ok ? t : 0.0;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const double tot = reduce8<GSL>(acc, lane);
-      if (writer) J.y[(J.it + (g * V + slot) * S) * P + prow] = J.bad ? quiet_nan() : (float)tot;
-    }
-  } else if (full) {
-    // Staged path. Chunk i of a step is bytes [16 (64 i + lane), +16), clamped to end
-    // inside the step (duplicates re-read and re-write identical bytes).
-    const uint32_t c0 = opaque(min(16u * (uint32_t)lane, step_bytes - 16u));
-    const uint32_t c1 = opaque(min(16u * (uint32_t)(64 + lane), step_bytes - 16u));
-    const uint32_t c2 = opaque(min(16u * (uint32_t)(128 + lane), step_bytes - 16u));
-    uint8_t* lds = stage[STAGED ? wiw : 0];
-    const uint32_t fo = (uint32_t)prow * rowbytes + (uint32_t)b * kBlockBytes;
-    u32x4 raw[R][3];
-    auto fetch = [&](int r, int st) {
-      const uint8_t* base = wrun + (size_t)st * run_stride;
-      raw[r][0] = gload<u32x4_a4>(base + c0);
-      raw[r][1] = gload<u32x4_a4>(base + c1);
-      raw[r][2] = gload<u32x4_a4>(base + c2);
-    };
-    auto stage_step = [&](int r) -> WHalf {
-      *reinterpret_cast<u32x4_a4*>(lds + c0) = raw[r][0];
-      *reinterpret_cast<u32x4_a4*>(lds + c1) = raw[r][1];
-      *reinterpret_cast<u32x4_a4*>(lds + c2) = raw[r][2];
-      WHalf w;
-      w.q0 = *reinterpret_cast<const u32x4_a4*>(lds + fo + 16 + 32 * h);
-      w.q1 = *reinterpret_cast<const u32x4_a4*>(lds + fo + 32 + 32 * h);
-      w.sc = *reinterpret_cast<const u32x2_a4*>(lds + fo + 8 * h);
-      w.dd = *reinterpret_cast<const uint32_t*>(lds + fo + 80);
-      return w;
-    };
-#pragma unroll
-    for (int r = 0; r < R; ++r) fetch(r, r);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dm[j] = (double)act.d8[j];
-      dq[j] = (j & 1) ? 0.25 * dm[j] : dm[j];
-    }
-    WHalf wcur = stage_step(0);
-    if (R < CH) fetch(0, R);
-#pragma unroll
-    for (int g = 0; g < CH / V; ++g) {
-      double acc[V];
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int st = g * V + v;                      // step within the run
-        WHalf wnext = wcur;
-        if (st + 1 < CH) {
-          wnext = stage_step((st + 1) % R);
-          if (st + 1 + R < CH) fetch((st + 1) % R, st + 1 + R);
-        }
-        const double t = half_block_value_m1(wcur, act, dq, dm);
-        acc[v] = hb_ok ? t : 0.0;
-        wcur = wnext;
         __builtin_amdgcn_sched_barrier(0);
       }
       const double tot = reduce8<GSL>(acc, lane);
@@ -724,7 +663,6 @@ struct Tuning {
   int interleave = 1;
   int ring = 4;
   int run = 0;       // m = 1 run length override (8, 16, 32); 0 = from waves_per_cu
-  bool staged = false;
   bool mfma = true;
   int m1_waves_per_cu = 4;
 };
@@ -739,7 +677,6 @@ const Tuning& tuning() {
     }
     if (const char* s = getenv("Q2K_MMVQ_GENERIC_M1")) t.fast_m1 = atoi(s) == 0;
     if (const char* s = getenv("Q2K_MMVQ_INTERLEAVE")) t.interleave = atoi(s) != 0;
-    if (const char* s = getenv("Q2K_MMVQ_STAGED")) t.staged = atoi(s) != 0;
     if (const char* s = getenv("Q2K_MMVQ_NO_MFMA")) t.mfma = atoi(s) == 0;
     if (const char* s = getenv("Q2K_MMVQ_M1_WAVES_PER_CU")) {
       const int v = atoi(s);
@@ -781,18 +718,12 @@ void dispatch_narrow(const MmvqParams& p, dim3 grid, bool dots, int depth, hipSt
   if (M == 1 && !dots && p.gs_log2 >= 3 && fast_m1()) {
     const int ring = tuning().ring;
     const int ch = p.chunk;
-    const bool staged = tuning().staged;
     // one matrix, interleaved runs: the kernel needs only its scalar arguments
     const int32_t plain = (p.ids == nullptr && p.groups == 0 && p.wave_end[0] == p.total_waves &&
                            p.interleave) ? 1 : 0;
 #define Q2K_M1_ARGS p.w[0], p.xq, p.y[0], p.n[0], p.k, p.total_waves, p.g8, plain, p
-#define Q2K_M1(G, R, C)                                                                          \
-  do {                                                                                           \
-    if (staged)                                                                                  \
-      hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, true>), grid, dim3(256), 0, s, Q2K_M1_ARGS);   \
-    else                                                                                         \
-      hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, false>), grid, dim3(256), 0, s, Q2K_M1_ARGS);  \
-  } while (0)
+#define Q2K_M1(G, R, C) \
+  hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C>), grid, dim3(256), 0, s, Q2K_M1_ARGS)
 #define Q2K_M1_CH(G, R)                          \
   do {                                           \
     if (ch == 8) Q2K_M1(G, R, 8);                \
