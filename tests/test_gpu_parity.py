@@ -686,6 +686,18 @@ def test_mmq(n, k, m):
     assert_close(y, orc.mmvq(w, oq, od), f"mmq n={n} k={k} m={m}")
 
 
+def test_mmq_max_tokens():
+    """The largest token count q2k_mmq takes (Q2K_MMQ_MAX_M = 4096), ragged rows."""
+    n, k, m = 37, 1024, 4096
+    rng = syn.rng_for(7150)
+    w = syn.q2k_blocks(rng, n, k // 256)
+    x = syn.bf16_normal(rng, (m, k), outlier_frac=0.05)
+    xq = q2.q8_1_rows(bf16_dev(x))
+    oq, od = assert_q8_equal(xq, x)
+    y = q2.q2k_mmq(dev(w.reshape(-1)), xq, n, k, m).cpu().numpy()
+    assert_close(y, orc.mmvq(w, oq, od), "mmq m=4096")
+
+
 def test_mmq_small_m_is_mmvq():
     case = syn.single_gemv_case(n=8197, k=2048, m=5, seed=7200)
     w = dev(case.w.reshape(-1))
