@@ -48,6 +48,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef double v4d __attribute__((ext_vector_type(4)));
+typedef double v2d __attribute__((ext_vector_type(2)));
 
 constexpr int kSlots = 8;              // token slots of a tile (m <= 8; unused slots are zero)
 constexpr int kTabSlots = kSlots + 1;  // plus one all-zero slot
@@ -90,15 +91,31 @@ __device__ __forceinline__ void prefetch_args(const MfmaParams& p) {
 // LDS layout (bytes) for row length k:
 //   quants  [kTabSlots][k + 16]   slot stride padded by 16 bytes so the eight
 //                                 token slots fall on different banks
-//   d8      [k/32][kSlots] fp64   block-major: a lane's four tokens are adjacent
-//   d8*S    [k/16][kTabSlots] fp64
+//   d8      k/32 x kSlots fp64    in the order of d8_index
+//   d8*S    k/16 x kSlots fp64    in the order of at_index
 __host__ __device__ constexpr uint32_t q_stride(int k) { return (uint32_t)k + 16u; }
 __host__ __device__ constexpr uint32_t lds_d8_off(int k) { return kTabSlots * q_stride(k); }
 __host__ __device__ constexpr uint32_t lds_at_off(int k) {
   return lds_d8_off(k) + (uint32_t)(k / 32) * kSlots * 8u;
 }
 __host__ __device__ constexpr uint32_t lds_bytes(int k) {
-  return lds_at_off(k) + (uint32_t)(k / 16) * kTabSlots * 8u;
+  return lds_at_off(k) + (uint32_t)(k / 16) * kSlots * 8u;
+}
+// Element index (fp64) of d8 of q8 block blk (within the row) of token t:
+// [super-block][plane p][half h][token], so the four 32-byte reads of one
+// plane (K-groups g = 2h + token/4) are 128 consecutive bytes.
+__device__ __forceinline__ uint32_t d8_index(uint32_t blk, uint32_t t) {
+  return (((blk >> 3) * 4u + (blk & 3u)) * 2u + ((blk >> 2) & 1u)) * 8u + t;
+}
+// Element index (fp64) of d8*S of sub-block s (within the row) of token t:
+// [super-block][MFMA i][K-group g][token & 3][token >> 2], where sub-block
+// s = 16b + 8(g>>1) + 2i + (g&1). A lane's two A values of one MFMA pair
+// (tokens j and j + 4) are one 16-byte read, and the sixteen distinct reads
+// of a pair are 256 consecutive bytes.
+__device__ __forceinline__ uint32_t at_index(uint32_t s, uint32_t t) {
+  const uint32_t sl = s & 15u;
+  const uint32_t g = 2u * (sl >> 3) + (sl & 1u), i = (sl & 7u) >> 1;
+  return ((((s >> 4) * 4u + i) * 4u + g) * 4u + (t & 3u)) * 2u + (t >> 2);
 }
 
 template <typename T>
@@ -245,15 +262,13 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, const StageRegs<k, THR
     double* d8t = reinterpret_cast<double*>(lds + lds_d8_off(k));
     double* at = reinterpret_cast<double*>(lds + lds_at_off(k));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d8t[(4 * c4 + i) * kSlots + t2] = live ? (double)r.d8v[i] : 0.0;
+    for (int i = 0; i < 4; ++i) d8t[d8_index(4 * c4 + i, t2)] = live ? (double)r.d8v[i] : 0.0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int16_t sum = (int16_t)(r.sv[j >> 1] >> (16 * (j & 1)));
-      at[(8 * c4 + j) * kTabSlots + t2] = live ? (double)r.d8v[j >> 1] * (double)sum : 0.0;
+      at[at_index(8 * c4 + j, t2)] = live ? (double)r.d8v[j >> 1] * (double)sum : 0.0;
     }
   }
-  for (int s2 = tid; s2 < k / 16; s2 += THREADS)
-    reinterpret_cast<double*>(lds + lds_at_off(k))[s2 * kTabSlots + kSlots] = 0.0;
 }
 
 // Workgroup barrier that orders LDS only: weight loads stay in flight.
@@ -284,11 +299,11 @@ __device__ __forceinline__ Lane lane_consts() {
   const uint32_t a_slot = ((g >> 1) == (j16 >> 3)) ? (uint32_t)(j16 & 7) : (uint32_t)kSlots;
   L.a_base = opaque_v(a_slot * q_stride(k) + 128u * (g >> 1) + 16u * (g & 1));
   // d8 of the lane's four outputs: tokens 4(g&1) + 0..3 of q8 block 8b + 4(g>>1) + p.
-  L.d8_base = opaque_v(lds_d8_off(k) + 8u * (kSlots * 4u * (g >> 1) + 4u * (g & 1)));
+  L.d8_base = opaque_v(lds_d8_off(k) + 32u * (uint32_t)g);
   // M-term A (4x4x4 MFMA, four blocks): lane 16k + 4blk + i holds A[blk][i][k]
   // = d8*S of token i (+4 for the second MFMA of a pair) and k-index k = g,
   // which is sub-block 8(g>>1) + 2i' + (g&1) of MFMA pair i'.
-  L.at_base = opaque_v(lds_at_off(k) + 8u * ((8u * (g >> 1) + (g & 1)) * kTabSlots + (uint32_t)(j16 & 3)));
+  L.at_base = opaque_v(lds_at_off(k) + 16u * (4u * (uint32_t)g + (uint32_t)(j16 & 3)));
   L.sc_shift = 8u * (g & 1);
   return L;
 }
@@ -423,9 +438,8 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const uint8_t* w0, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t mb = ((i < 2 ? sw0 : sw1) >> (16 * (i & 1) + 4)) & 15u;
-        const uint32_t ao = L.at_base + 8u * kTabSlots * (16u * b + 2u * i);
-        const double a0 = lds_load<double>(lds, ao);
-        const double a1 = lds_load<double>(lds, ao + 32u);
+        const v2d a = lds_load<v2d>(lds, L.at_base + 1024u * b + 256u * i);
+        const double a0 = a[0], a1 = a[1];
         const double wm = dmin * (double)mb;
         accM0 = __builtin_amdgcn_mfma_f64_4x4x4f64(a0, wm, accM0, 0, 0, 0);
         accM1 = __builtin_amdgcn_mfma_f64_4x4x4f64(a1, wm, accM1, 0, 0, 0);
@@ -436,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const uint8_t* w0, 
         const v4i aq = lds_load<v4i>(lds, L.a_base + 256u * b + 32u * pl);
         const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, plane_weights(cur.qs, pl < 2 ? sw0 : sw1, pl),
                                                             v4i{0, 0, 0, 0}, 0, 0, 0);
-        const v4d d8 = lds_load<v4d>(lds, L.d8_base + 8u * kSlots * (8u * b + pl));
+        const v4d d8 = lds_load<v4d>(lds, L.d8_base + 512u * b + 128u * pl);
 #pragma unroll
         for (int i = 0; i < 4; ++i) accI[i] = fma(d8[i], (double)c[i], accI[i]);
       }
