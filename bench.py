@@ -108,6 +108,204 @@ def cpu_baseline(case, seconds: float, chunk: int = 4096):
                       f"{wall:.1f} s, fp64 dense oracle"}
 
 
+def graph_us(torch, fn, launches: int, reps: int = 20, chunk: int = 16) -> float:
+    """Average time of fn(i), i = 0..launches-1, in microseconds: the calls
+    are captured in HIP graphs of `chunk` calls each (after one eager pass),
+    and HIP events on the capturing stream bracket `reps` replays of all of
+    them."""
+    stream = torch.cuda.Stream()
+    graphs = []
+    torch.cuda.synchronize()
+    for c0 in range(0, launches, chunk):
+        with torch.cuda.stream(stream):
+            for i in range(c0, min(c0 + chunk, launches)):
+                fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(c0, min(c0 + chunk, launches)):
+                fn(i)
+        graphs.append(g)
+    with torch.cuda.stream(stream):
+        for g in graphs:
+            g.replay()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            for g in graphs:
+                g.replay()
+        ev1.record(stream)
+        ev1.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / (reps * launches)
+
+
+def _roof(nbytes: int, us: float) -> dict:
+    gbs = nbytes / us / 1e3
+    return {"us_per_launch": round(us, 3), "bytes_per_launch": int(nbytes),
+            "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_GBS, 4)}
+
+
+def bench_single(torch, q2, syn, dev, copies_n: int = 4096):
+    """The single small product, Q2_K [256, 1024] at m = 1 (86 016 weight
+    bytes): 4096 copies in one buffer (352 MB, past the Infinity Cache),
+    launch i reads copy i."""
+    case = syn.single_gemv_case()
+    per = case.w.size
+    buf = torch.from_numpy(case.w.reshape(-1)).to(dev).repeat(copies_n)
+    x = syn.bf16_bits_to_tensor(case.x_bits).to(dev)
+    xq = q2.q8_1_rows(x)
+    y = torch.empty((1, case.n), dtype=torch.float32, device=dev)
+    us = graph_us(torch, lambda i: q2.q2k_mmvq(buf[i * per:(i + 1) * per], xq, case.n, case.k, 1,
+                                               out=y), copies_n, reps=5, chunk=256)
+    from oracle import q2k_oracle as orc
+    oq, od, _ = orc.q8_1_from_bf16_bits(case.x_bits)
+    ref = orc.mmvq(case.w, oq, od)
+    if not np.all(np.abs(y.cpu().numpy().astype(np.float64) - ref) <= 1e-4 + 2e-3 * np.abs(ref)):
+        raise SystemExit("bench parity failed: single product")
+    out = _roof(per + q2.q8_1_rows_bytes(1, case.k) + 4 * case.n, us)
+    out["workload"] = (f"single Q2_K product [256, 1024], m = 1, {copies_n} copies in one "
+                       "buffer; launch-bound (86 KB of weights)")
+    return out
+
+
+def bench_pair(torch, q2, syn, dev, copies_n: int = 512):
+    """The attention input pair: q8_1 of x [m, 4096] once, then wq_a [1024,
+    4096] and wkv [512, 4096] against it in one launch, m = 1, 4, 8; 512
+    rotating copies of the two matrices (1.06 GB)."""
+    from oracle import q2k_oracle as orc
+    out = {}
+    for m in (1, 4, 8):
+        pc = syn.attention_pair_case(m)
+        wa0 = torch.from_numpy(pc.wa.reshape(-1)).to(dev)
+        wb0 = torch.from_numpy(pc.wb.reshape(-1)).to(dev)
+        wa = wa0.repeat(copies_n)
+        wb = wb0.repeat(copies_n)
+        pa, pb = wa0.numel(), wb0.numel()
+        x = syn.bf16_bits_to_tensor(pc.x_bits).to(dev)
+        xq = torch.empty(q2.q8_1_rows_bytes(m, pc.k), dtype=torch.uint8, device=dev)
+        ya = torch.empty((m, pc.na), dtype=torch.float32, device=dev)
+        yb = torch.empty((m, pc.nb), dtype=torch.float32, device=dev)
+
+        def prod(i):
+            j = i % copies_n
+            q2.q2k_mmvq_pair(wa[j * pa:(j + 1) * pa], pc.na, wb[j * pb:(j + 1) * pb], pc.nb, xq,
+                             pc.k, m, ya=ya, yb=yb)
+
+        def step(i):
+            q2.q8_1_rows(x, out=xq)
+            prod(i)
+
+        us_step = graph_us(torch, step, copies_n, reps=10, chunk=128)
+        us_prod = graph_us(torch, prod, copies_n, reps=10, chunk=128)
+        oq, od, _ = orc.q8_1_from_bf16_bits(pc.x_bits)
+        ra, rb = orc.mmvq_pair(pc.wa, pc.wb, oq, od)
+        for got, ref in ((ya, ra), (yb, rb)):
+            if not np.all(np.abs(got.cpu().numpy().astype(np.float64) - ref)
+                          <= 1e-4 + 2e-3 * np.abs(ref)):
+                raise SystemExit(f"bench parity failed: attention pair m={m}")
+        r = _roof(pa + pb + q2.q8_1_rows_bytes(m, pc.k) + 4 * m * (pc.na + pc.nb), us_prod)
+        r["us_per_step"] = round(us_step, 3)
+        r["tokens_per_s"] = round(m / us_step * 1e6, 1)
+        out[f"m{m}"] = r
+    out["workload"] = ("attention input pair: x bf16 [m, 4096] -> q8_1 once -> wq_a Q2_K "
+                       "[1024, 4096] and wkv Q2_K [512, 4096] in one launch; 512 rotating copies "
+                       "(1.06 GB); step = q8_1 + pair, product = the pair launch alone")
+    return out
+
+
+def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
+    """The routed-expert decode batch: 256 resident experts of Q2_K gate and
+    up [2048, 4096] and down [4096, 2048] (2.11 GB, all seeded), a fresh
+    set of 8 ids per step (without replacement, seeded). Step: q8_1 of x
+    [1, 4096], gate/up over the 8 ids (one launch), bf16 SwiGLU + q8_1 of
+    the 8 rows, down with one input row per id -> f32 [8, 4096]."""
+    from oracle import q2k_oracle as orc
+    case = syn.expert_batch_case()
+    dim, inter, ne = case.dim, case.inter, case.n_experts
+    per_gu = inter * (dim // 256) * 84
+    per_d = dim * (inter // 256) * 84
+    sets = {}
+    for kind, per in (("gate", per_gu), ("up", per_gu), ("down", per_d)):
+        buf = torch.empty(ne * per, dtype=torch.uint8, device=dev)
+        for e in range(ne):
+            buf[e * per:(e + 1) * per] = torch.from_numpy(case.expert_matrix(e, kind).reshape(-1))
+        sets[kind] = buf
+    rng = syn.rng_for(case.seed, 1 << 20)
+    ids_np = np.stack([rng.choice(ne, size=8, replace=False) for _ in range(steps_n)]).astype(np.int32)
+    ids = torch.from_numpy(ids_np).to(dev)
+    x = syn.bf16_bits_to_tensor(case.x_bits).to(dev)
+    xq = torch.empty(q2.q8_1_rows_bytes(1, dim), dtype=torch.uint8, device=dev)
+    gu = torch.empty((2, 8, 1, inter), dtype=torch.float32, device=dev)
+    hq = torch.empty(q2.q8_1_rows_bytes(8, inter), dtype=torch.uint8, device=dev)
+    yd = torch.empty((1, 8, 1, dim), dtype=torch.float32, device=dev)
+    g, u = gu[0].view(8, inter), gu[1].view(8, inter)
+
+    def gate_up(i):
+        q2.q2k_mmvq_experts([sets["gate"], sets["up"]], per_gu, ne, ids[i % steps_n], xq, False,
+                            inter, dim, 1, out=gu)
+
+    def down(i):
+        q2.q2k_mmvq_experts([sets["down"]], per_d, ne, ids[i % steps_n], hq, True, dim, inter, 1,
+                            out=yd)
+
+    def step(i):
+        q2.q8_1_rows(x, out=xq)
+        gate_up(i)
+        q2.swiglu_q8_1_rows(g, u, hq=hq, want_h=False)
+        down(i)
+
+    us_step = graph_us(torch, step, steps_n)
+    us_gu = graph_us(torch, gate_up, steps_n)
+    us_down = graph_us(torch, down, steps_n)
+    us_q8 = graph_us(torch, lambda i: q2.q8_1_rows(x, out=xq), 16)
+    us_sw = graph_us(torch, lambda i: q2.swiglu_q8_1_rows(g, u, hq=hq, want_h=False), 16)
+    # parity of the last id set, stage by stage: gate/up against the oracle;
+    # h within one bf16 step of the oracle's SwiGLU; then the down product
+    # against the oracle on the oracle's q8_1 of that h
+    i_last = steps_n - 1
+    q2.q8_1_rows(x, out=xq)
+    gate_up(i_last)
+    h, hq_p = q2.swiglu_q8_1_rows(g, u)
+    yp = q2.q2k_mmvq_experts([sets["down"]], per_d, ne, ids[i_last], hq_p, True, dim, inter, 1)
+    torch.cuda.synchronize()
+    sel = ids_np[i_last].tolist()
+    oq, od, _ = orc.q8_1_from_bf16_bits(case.x_bits)
+    gu_h = gu.cpu().numpy()
+    for bi, kind in enumerate(("gate", "up")):
+        ref = orc.mmvq_experts([case.expert_matrix(e, kind) for e in sel], oq, od, x_per_id=False)
+        if not np.all(np.abs(gu_h[bi].astype(np.float64) - ref) <= 1e-4 + 2e-3 * np.abs(ref)):
+            raise SystemExit(f"bench parity failed: experts {kind}")
+    h_bits = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    h_ref = orc.swiglu_bf16_bits(gu_h[0].reshape(8, inter), gu_h[1].reshape(8, inter))
+
+    def ordered(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b)
+
+    if np.abs(ordered(h_bits) - ordered(h_ref)).max() > 1:
+        raise SystemExit("bench parity failed: SwiGLU more than one bf16 step off")
+    hq_o, hd_o, _ = orc.q8_1_from_bf16_bits(h_bits)
+    ref = orc.mmvq_experts([case.expert_matrix(e, "down") for e in sel], hq_o, hd_o, x_per_id=True)
+    if not np.all(np.abs(yp.cpu().numpy()[0].astype(np.float64) - ref) <= 1e-4 + 2e-3 * np.abs(ref)):
+        raise SystemExit("bench parity failed: experts down")
+    b_gu = 16 * per_gu + q2.q8_1_rows_bytes(1, dim) + 4 * 16 * inter + 4 * 8
+    b_d = 8 * per_d + q2.q8_1_rows_bytes(8, inter) + 4 * 8 * dim + 4 * 8
+    step_bytes = b_gu + b_d + (2 * dim + q2.q8_1_rows_bytes(1, dim)) \
+        + (8 * 16 * inter + q2.q8_1_rows_bytes(8, inter))
+    return {"workload": "routed-expert decode batch, m = 1: 256 resident experts (Q2_K gate/up "
+                        "[2048, 4096], down [4096, 2048]; 2.11 GB), 8 ids per step without "
+                        "replacement, 64 id sets; step = q8_1 + gate/up (one launch, 16 matrices) "
+                        "+ bf16 SwiGLU and q8_1 + down (one launch, 8 matrices, one input row "
+                        "per id)",
+            "us_per_step": round(us_step, 3), "tokens_per_s": round(1e6 / us_step, 1),
+            "step_gbs": round(step_bytes / us_step / 1e3, 1),
+            "step_frac": round(step_bytes / us_step / 1e3 / PEAK_GBS, 4),
+            "gate_up": _roof(b_gu, us_gu), "down": _roof(b_d, us_down),
+            "q8_1_us": round(us_q8, 3), "swiglu_q8_1_us": round(us_sw, 3)}
+
+
 def bench_mmq(torch, q2, syn, dev, copies, case):
     """The product past 8 tokens (q2k_mmq) on the large-verify matrix: m =
     16, 64, 256 tokens ~ N(0,1) with 5% +-20 outliers, over the same rotating
@@ -156,9 +354,10 @@ def bench_grouped(torch, q2, syn, dev, copies_n: int = 64):
     out = {}
     gc = syn.grouped_case(8)
     w0 = torch.from_numpy(gc.w.reshape(-1)).to(dev)
-    copies = [w0] + [w0.clone() for _ in range(copies_n - 1)]
-    x8 = syn.bf16_bits_to_tensor(gc.x_bits).to(dev)
     wbytes = w0.numel()
+    buf = w0.repeat(copies_n)            # one allocation, copy i at i * wbytes
+    copies = [buf[i * wbytes:(i + 1) * wbytes] for i in range(copies_n)]
+    x8 = syn.bf16_bits_to_tensor(gc.x_bits).to(dev)
     for m in (1, 8):
         xq = q2.q8_1_rows(x8[:m].contiguous())
         y = torch.empty((m, gc.groups * gc.rows), dtype=torch.float32, device=dev)
@@ -460,6 +659,11 @@ def run(args):
         torch.cuda.synchronize()
         line["grouped"] = bench_grouped(torch, q2, syn, dev)
         line["engram_step"] = bench_engram(torch, q2, syn, dev)
+        torch.cuda.synchronize()
+        line["attention_pair"] = bench_pair(torch, q2, syn, dev)
+        torch.cuda.synchronize()
+        line["expert_batch"] = bench_experts(torch, q2, syn, dev)
+        line["single"] = bench_single(torch, q2, syn, dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -61,7 +61,7 @@ extern "C" {
 #define Q2K_API
 #endif
 
-#define Q2K_ABI_VERSION 3
+#define Q2K_ABI_VERSION 4
 
 #define Q2K_OK 0
 #define Q2K_EINVAL (-1)   /* NULL pointer, or pointers that must not overlap do */
@@ -278,6 +278,26 @@ Q2K_API int32_t engram_hash(const int64_t* token_map_dev, int64_t vocab,
                          int32_t n_heads, int64_t pad_id, int64_t* cache_dev, int64_t cache_len,
                          const int32_t* ids_dev, int32_t seqlen, int64_t start_pos,
                          int64_t* out_dev, int32_t* err_flag_dev, void* stream);
+
+/* Which kernel runs the Q2_K x q8_1 products (q2k_mmvq, its pair, expert
+ * and grouped forms, and q2k_mmq), process-wide. For tests and tuning only:
+ * every kernel forms the same exact int32 block sums and an fp64 epilogue,
+ * so all choices meet the product tolerance; they may differ in the last
+ * bits, since their fp64 sums run in different orders.
+ *   Q2K_KERNEL_AUTO (the default): a cost model measured on MI355X picks
+ *     the matrix-core kernel (2..8 tokens; rows of 4, 8, 16 or 28
+ *     super-blocks) or the packed-dot kernels (tokens split over waves);
+ *   Q2K_KERNEL_MATRIX_CORES: the matrix-core kernel wherever it applies;
+ *   Q2K_KERNEL_PACKED_DOTS: never the matrix-core kernel (more than 8
+ *     tokens then run as groups of 8 on the packed-dot kernels).
+ * The environment variable Q2K_MMVQ_NO_MFMA=1 sets the initial choice to
+ * Q2K_KERNEL_PACKED_DOTS. Returns the previous choice, or Q2K_EINVAL for an
+ * unknown one. Launches already enqueued are unaffected; a thread that
+ * launches while another changes the choice gets either kernel. */
+#define Q2K_KERNEL_AUTO 0
+#define Q2K_KERNEL_MATRIX_CORES 1
+#define Q2K_KERNEL_PACKED_DOTS 2
+Q2K_API int32_t q2k_set_product_kernel(int32_t choice);
 
 /* Integer stage of q2k_mmvq, exported for exact checking (same device
  * code): out_dev int32 [m, n, k/32, 2] receives, per token t, row r and

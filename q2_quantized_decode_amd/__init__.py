@@ -31,6 +31,7 @@ _VP, _I32, _I64, _SZ, _F32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, c
 SIGNATURES = {
     "q2k_abi_version": (_I32, []),
     "q2k_last_error": (ctypes.c_char_p, []),
+    "q2k_set_product_kernel": (_I32, [_I32]),
     "q8_1_rows_bytes": (_SZ, [_I32, _I32]),
     "q8_1_rows": (_I32, [_VP, _I64, _VP, _SZ, _I32, _I32, _VP]),
     "q2k_mmvq": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
@@ -103,6 +104,17 @@ def _contig(t: torch.Tensor, name: str) -> int:
 
 def q2k_abi_version() -> int:
     return int(lib().q2k_abi_version())
+
+
+KERNEL_AUTO, KERNEL_MATRIX_CORES, KERNEL_PACKED_DOTS = 0, 1, 2
+
+
+def q2k_set_product_kernel(choice: int) -> int:
+    """Process-wide product kernel choice (tests and tuning); returns the previous one."""
+    r = int(lib().q2k_set_product_kernel(choice))
+    if r < 0:
+        _check("q2k_set_product_kernel", r)
+    return r
 
 
 def q8_1_rows_bytes(m: int, k: int) -> int:

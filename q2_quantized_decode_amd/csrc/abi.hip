@@ -60,6 +60,13 @@ int32_t q2k_abi_version(void) { return Q2K_ABI_VERSION; }
 
 const char* q2k_last_error(void) { return g_err; }
 
+int32_t q2k_set_product_kernel(int32_t choice) {
+  if (choice != Q2K_KERNEL_AUTO && choice != Q2K_KERNEL_MATRIX_CORES &&
+      choice != Q2K_KERNEL_PACKED_DOTS)
+    return fail(Q2K_EINVAL, "q2k_set_product_kernel: unknown choice %d", choice);
+  return q2k::set_product_kernel(choice);
+}
+
 size_t q8_1_rows_bytes(int32_t m, int32_t k) {
   if (m < 1 || k <= 0 || k % 256 != 0) return 0;
   return (size_t)m * q2k::q8_row_bytes(k);

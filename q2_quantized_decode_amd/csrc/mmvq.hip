@@ -28,6 +28,7 @@
 //   contiguous eighth of the rows through its own L2.
 #include <stdlib.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "q2k_device.h"
@@ -56,6 +57,7 @@ struct MmvqParams {
   int32_t k;
   int32_t gs_log2;                   // lanes per row group = 1 << gs_log2
   int32_t g8;                        // workgroups per XCD (grid / 8)
+  int32_t tsplit;                    // tokens taken by separate waves (1: none)
 };
 
 // Touches every field of the argument block at once, so that its scalar
@@ -66,7 +68,8 @@ struct MmvqParams {
 __device__ __forceinline__ void prefetch_args(const MmvqParams& p) {
   asm volatile("" ::"s"(p.w[0]), "s"(p.y[0]), "s"(p.n[0]), "s"(p.wave_end[0]), "s"(p.wave_end[1]),
                "s"(p.wave_end[2]), "s"(p.xq), "s"(p.ids), "s"(p.groups), "s"(p.total_waves),
-               "s"(p.k), "s"(p.interleave), "s"(p.chunk), "s"(p.g8));
+               "s"(p.k), "s"(p.interleave), "s"(p.chunk), "s"(p.g8),
+               "s"(p.tsplit));
 }
 
 // The matrix one wave works on, and its run of row steps.
@@ -82,8 +85,11 @@ struct WaveJob {
   bool bad;            // expert id out of range
 };
 
+// M is the kernel's token count; a token-split launch (tsplit > 1) runs the
+// one-token kernel, and the launch's own token count sets the layouts.
 template <int M>
 __device__ __forceinline__ WaveJob resolve_wave(const MmvqParams& p, int wave, int P) {
+  const int mt = M == 1 ? p.tsplit : M;
   WaveJob J;
   int lw;
   if (p.ids == nullptr && p.groups == 0) {
@@ -114,8 +120,8 @@ __device__ __forceinline__ WaveJob resolve_wave(const MmvqParams& p, int wave, i
     J.w = p.w[base] + (int64_t)(J.bad ? 0 : id) * p.expert_stride;
     J.n = p.n[0];
     J.ldy = J.n;
-    J.y = p.y[0] + (int64_t)j * M * p.n[0];
-    J.x = xview(p.x_per_id ? p.xq + (int64_t)i * M * (int64_t)q8_row_bytes(p.k) : p.xq, p.k, 0);
+    J.y = p.y[0] + (int64_t)j * mt * p.n[0];
+    J.x = xview(p.x_per_id ? p.xq + (int64_t)i * mt * (int64_t)q8_row_bytes(p.k) : p.xq, p.k, 0);
   }
   const int iters = (J.n + P - 1) / P;
   if (p.interleave) {
@@ -437,9 +443,10 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
   const int lane = threadIdx.x & 63;
   const int wiw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wg = blockIdx.x;
-  const int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 + wiw;
+  int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 + wiw;
   if (wave >= total_waves) return;
   WaveJob J;
+  int tok = 0;
   if (plain) {
     // one matrix, runs interleaved: wave w takes steps w, w + W, ...
     J.w = w0;
@@ -453,7 +460,16 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
     J.bad = false;
   } else {
     prefetch_args(p);
+    // token split: the tsplit waves of one run are consecutive (same or
+    // neighbouring workgroup, same XCD), so they share the run's weights
+    // through that XCD's L2
+    const int ts = p.tsplit;
+    if (ts > 1) {
+      tok = wave % ts;
+      wave /= ts;
+    }
     J = resolve_wave<1>(p, wave, P);
+    J.y += (int64_t)tok * J.ldy;
   }
   if (J.it >= J.it_end) return;
 
@@ -478,7 +494,7 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
   const bool full = last_step < J.it_end && (last_step + 1) * P <= J.n;
 
   // Activations first: the first step waits for them and ring slot 0 only.
-  const AHalf act = load_ahalf(J.x, 0, b, h);
+  const AHalf act = load_ahalf(J.x, tok, b, h);
   double dq[4], dm[4];
 
   if (full) {
@@ -561,7 +577,14 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
   const int h = hb & 1;
   const size_t rowbytes = (size_t)nb * kBlockBytes;
 
-  const WaveJob J = resolve_wave<M>(p, wave, P);
+  // token split (one-token kernel only): as in mmvq_m1_kernel
+  int tok = 0, jw = wave;
+  if (M == 1 && p.tsplit > 1) {
+    tok = wave % p.tsplit;
+    jw = wave / p.tsplit;
+  }
+  WaveJob J = resolve_wave<M>(p, jw, P);
+  J.y += (int64_t)tok * J.ldy;
   if (J.it >= J.it_end) return;
   const uint8_t* wlane = J.w + b * kBlockBytes;
 
@@ -574,7 +597,7 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
                                                  : zero_whalf();
   }
   AHalf act;
-  if constexpr (CACHE) act = hb_ok ? load_ahalf(J.x, 0, b, h) : zero_ahalf();
+  if constexpr (CACHE) act = hb_ok ? load_ahalf(J.x, tok, b, h) : zero_ahalf();
 
   for (int base = J.it; base < J.it_end; base += DEPTH * J.stride) {
 #pragma unroll
@@ -663,8 +686,8 @@ struct Tuning {
   int interleave = 1;
   int ring = 4;
   int run = 0;       // m = 1 run length override (8, 16, 32); 0 = from waves_per_cu
-  bool mfma = true;
   int m1_waves_per_cu = 4;
+  int64_t m1_min_steps = 2048;
 };
 
 const Tuning& tuning() {
@@ -677,7 +700,7 @@ const Tuning& tuning() {
     }
     if (const char* s = getenv("Q2K_MMVQ_GENERIC_M1")) t.fast_m1 = atoi(s) == 0;
     if (const char* s = getenv("Q2K_MMVQ_INTERLEAVE")) t.interleave = atoi(s) != 0;
-    if (const char* s = getenv("Q2K_MMVQ_NO_MFMA")) t.mfma = atoi(s) == 0;
+    if (const char* s = getenv("Q2K_MMVQ_M1_MIN_STEPS")) t.m1_min_steps = atoll(s);
     if (const char* s = getenv("Q2K_MMVQ_M1_WAVES_PER_CU")) {
       const int v = atoi(s);
       if (v >= 1 && v <= 64) t.m1_waves_per_cu = v;
@@ -698,8 +721,6 @@ const Tuning& tuning() {
   return t;
 }
 
-bool fast_m1() { return tuning().fast_m1; }
-
 int cu_count() {
   static int counts[64];
   int dev = 0;
@@ -714,13 +735,14 @@ int cu_count() {
 }
 
 template <int M>
-void dispatch_narrow(const MmvqParams& p, dim3 grid, bool dots, int depth, hipStream_t s) {
-  if (M == 1 && !dots && p.gs_log2 >= 3 && fast_m1()) {
+void dispatch_narrow(const MmvqParams& p, dim3 grid, bool dots, int depth, bool run_kernel,
+                     hipStream_t s) {
+  if (M == 1 && run_kernel) {
     const int ring = tuning().ring;
     const int ch = p.chunk;
     // one matrix, interleaved runs: the kernel needs only its scalar arguments
     const int32_t plain = (p.ids == nullptr && p.groups == 0 && p.wave_end[0] == p.total_waves &&
-                           p.interleave) ? 1 : 0;
+                           p.interleave && p.tsplit == 1) ? 1 : 0;
 #define Q2K_M1_ARGS p.w[0], p.xq, p.y[0], p.n[0], p.k, p.total_waves, p.g8, plain, p
 #define Q2K_M1(G, R, C) \
   hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C>), grid, dim3(256), 0, s, Q2K_M1_ARGS)
@@ -749,15 +771,14 @@ void dispatch_narrow(const MmvqParams& p, dim3 grid, bool dots, int depth, hipSt
   }
   if (dots) {
     hipLaunchKernelGGL((mmvq_narrow_kernel<M, false, 1, true>), grid, dim3(256), 0, s, p);
-  } else if (M == 1) {
+  } else if constexpr (M == 1) {
+    // products take one token per wave (m > 1: token split)
     if (depth == 1)
       hipLaunchKernelGGL((mmvq_narrow_kernel<M, true, 1, false>), grid, dim3(256), 0, s, p);
     else if (depth == 4)
       hipLaunchKernelGGL((mmvq_narrow_kernel<M, true, 4, false>), grid, dim3(256), 0, s, p);
     else
       hipLaunchKernelGGL((mmvq_narrow_kernel<M, true, 2, false>), grid, dim3(256), 0, s, p);
-  } else {
-    hipLaunchKernelGGL((mmvq_narrow_kernel<M, false, 2, false>), grid, dim3(256), 0, s, p);
   }
 }
 
@@ -771,8 +792,34 @@ void dispatch_wide(const MmvqParams& p, dim3 grid, bool dots, hipStream_t s) {
 
 }  // namespace
 
+// Product kernel choice (q2k_set_product_kernel): -1 until first read, then
+// 0 automatic, 1 matrix cores where supported, 2 packed dots only. The
+// variable Q2K_MMVQ_NO_MFMA=1 makes the initial choice 2.
+static std::atomic<int> g_product_kernel{-1};
+
+static int product_kernel() {
+  int c = g_product_kernel.load(std::memory_order_relaxed);
+  if (c < 0) {
+    const char* s = getenv("Q2K_MMVQ_NO_MFMA");
+    int init = (s && atoi(s) != 0) ? 2 : 0;
+    g_product_kernel.compare_exchange_strong(c, init, std::memory_order_relaxed);
+    c = g_product_kernel.load(std::memory_order_relaxed);
+  }
+  return c;
+}
+
+int set_product_kernel(int choice) {
+  const int prev = product_kernel();
+  g_product_kernel.store(choice, std::memory_order_relaxed);
+  return prev;
+}
+
 hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
-  if (tuning().mfma && mfma_preferred(a)) return launch_mmvq_mfma(a, stream);
+  const int choice = product_kernel();
+  const bool mfma = choice == 1   ? (a.dots == nullptr && a.m >= 2 && mfma_supports(a.k))
+                    : choice == 2 ? false
+                                  : mfma_preferred(a);
+  if (mfma) return launch_mmvq_mfma(a, stream);
   if (a.m > kMaxM) {
     // More tokens than the packed-dot kernels take: one launch per group of
     // kMaxM tokens (plain single-matrix launches only).
@@ -834,10 +881,21 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   }
   if (total_iters == 0) return hipSuccess;
   const Tuning& tu = tuning();
-  const bool m1_path = a.m == 1 && a.dots == nullptr && !wide && gs_log2 >= 3 && tu.fast_m1;
+  // m > 1 on the packed-dot path (rows of at most 8192 values): the
+  // one-token kernels with the tokens taken by separate waves, so the
+  // activations stay in registers (a wave that took all m tokens reloaded
+  // them for every token and step: 13 us against 5.9 us on the attention
+  // pair at m = 8)
+  const int tsplit = (a.dots == nullptr && !wide) ? a.m : 1;
+  p.tsplit = tsplit;
+  // The run kernel (runs of 8 to 32 steps per wave) needs enough steps to
+  // fill the chip; smaller launches take one step per wave.
+  const bool m1_path = a.dots == nullptr && !wide && gs_log2 >= 3 && tu.fast_m1 &&
+                       total_iters * tsplit >= tu.m1_min_steps;
   const int64_t target_waves =
       (int64_t)cu_count() * (m1_path ? tu.m1_waves_per_cu : tu.waves_per_cu);
-  int64_t chunk = (total_iters + target_waves - 1) / target_waves;
+  int64_t chunk = (total_iters * tsplit + target_waves - 1) / target_waves;
+  if (tsplit > 1 && !m1_path) chunk = 1;
   if (m1_path) {
     // runs of 8, 16 or 32 steps (compile-time run lengths of the m = 1 kernel)
     chunk = chunk <= 8 ? 8 : chunk <= 16 ? 16 : 32;
@@ -854,6 +912,7 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
     p.waves_per_job = (int)((iters_of[0] + chunk - 1) / chunk);
     total_waves = (int64_t)p.waves_per_job * n_jobs;
   }
+  total_waves *= tsplit;
   p.total_waves = (int)total_waves;
   p.interleave = tu.interleave;
   int64_t groups = (total_waves + 3) / 4;
@@ -873,16 +932,18 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
       case 7: dispatch_wide<7>(p, grid, dots, stream); break;
       default: dispatch_wide<8>(p, grid, dots, stream); break;
     }
+  } else if (tsplit > 1) {
+    dispatch_narrow<1>(p, grid, dots, tu.depth, m1_path, stream);
   } else {
     switch (a.m) {
-      case 1: dispatch_narrow<1>(p, grid, dots, tu.depth, stream); break;
-      case 2: dispatch_narrow<2>(p, grid, dots, tu.depth, stream); break;
-      case 3: dispatch_narrow<3>(p, grid, dots, tu.depth, stream); break;
-      case 4: dispatch_narrow<4>(p, grid, dots, tu.depth, stream); break;
-      case 5: dispatch_narrow<5>(p, grid, dots, tu.depth, stream); break;
-      case 6: dispatch_narrow<6>(p, grid, dots, tu.depth, stream); break;
-      case 7: dispatch_narrow<7>(p, grid, dots, tu.depth, stream); break;
-      default: dispatch_narrow<8>(p, grid, dots, tu.depth, stream); break;
+      case 1: dispatch_narrow<1>(p, grid, dots, tu.depth, m1_path, stream); break;
+      case 2: dispatch_narrow<2>(p, grid, dots, tu.depth, false, stream); break;
+      case 3: dispatch_narrow<3>(p, grid, dots, tu.depth, false, stream); break;
+      case 4: dispatch_narrow<4>(p, grid, dots, tu.depth, false, stream); break;
+      case 5: dispatch_narrow<5>(p, grid, dots, tu.depth, false, stream); break;
+      case 6: dispatch_narrow<6>(p, grid, dots, tu.depth, false, stream); break;
+      case 7: dispatch_narrow<7>(p, grid, dots, tu.depth, false, stream); break;
+      default: dispatch_narrow<8>(p, grid, dots, tu.depth, false, stream); break;
     }
   }
   return hipGetLastError();

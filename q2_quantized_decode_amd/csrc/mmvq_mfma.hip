@@ -532,11 +532,26 @@ bool mfma_supports(int k) {
 }
 
 bool mfma_preferred(const MmvqLaunch& a) {
-  // One workgroup per CU at a time (LDS): below a quarter of the chip the
-  // packed-dot kernels, which spread a row over more waves, are faster.
   // More than kSlots tokens always go to the matrix cores when they can.
+  // Otherwise the faster of two measured cost models (one MI355X, microseconds
+  // over a fixed ~4 us of launch and latency):
+  //  * matrix cores: ~0.75 us per super-block of a row for every round of
+  //    up to 256 workgroups (one workgroup per CU: LDS), whatever m is;
+  //  * packed dots with the tokens split over waves: ~1e-5 us per
+  //    (row, super-block, token), all of it vector-ALU issue.
   if (a.dots != nullptr || !mfma_supports(a.k) || a.m < 2) return false;
-  return a.m > kSlots || workgroups(a) * ((a.m + kSlots - 1) / kSlots) >= 64;
+  if (a.m > kSlots) return true;
+  const int nb = a.k / kBlockWeights;
+  int64_t rows = 0;
+  if (uniform_jobs(a)) {
+    rows = (int64_t)a.n[0] * a.njobs * a.n_ids;
+  } else {
+    for (int j = 0; j < a.njobs; ++j) rows += a.n[j];
+  }
+  const double rounds = (double)((workgroups(a) + 255) / 256);
+  const double t_mfma = 0.75 * nb * rounds;
+  const double t_dots = 1e-5 * (double)rows * nb * a.m;
+  return t_mfma < t_dots;
 }
 
 hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream) {

@@ -48,6 +48,9 @@ hipError_t launch_q8_1_rows(const void* x, int64_t stride, void* xq, int m, int 
 hipError_t launch_swiglu_q8_1_rows(const float* g, const float* u, void* h, void* hq, int rows,
                                    int k, hipStream_t stream);
 hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream);
+// Product kernel choice (0 automatic, 1 matrix cores, 2 packed dots); returns
+// the previous one.
+int set_product_kernel(int choice);
 // 2..8 tokens on the matrix cores, rows of 4, 8, 16 or 28 super-blocks.
 hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream);
 bool mfma_supports(int k);

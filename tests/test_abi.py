@@ -38,12 +38,25 @@ def test_header_symbols_exported(L):
 
 
 def test_version_and_sizes(L):
-    assert L.q2k_abi_version() == 3
+    assert L.q2k_abi_version() == 4
     assert L.q8_1_rows_bytes(1, 1024) == 1280
     assert L.q8_1_rows_bytes(8, 7168) == 8 * 8960
     assert L.q8_1_rows_bytes(0, 1024) == 0
     assert L.q8_1_rows_bytes(1, 100) == 0
     assert L.q8_1_rows_bytes(1, -256) == 0
+
+
+def test_product_kernel_choice(L):
+    """The kernel choice is host state only (no launch): unknown values are
+    refused, valid ones return the previous choice."""
+    prev = L.q2k_set_product_kernel(q2.KERNEL_AUTO)
+    assert prev in (q2.KERNEL_AUTO, q2.KERNEL_PACKED_DOTS)
+    assert L.q2k_set_product_kernel(3) == EINVAL
+    assert "unknown choice" in _err(L)
+    assert L.q2k_set_product_kernel(-1) == EINVAL
+    assert L.q2k_set_product_kernel(q2.KERNEL_MATRIX_CORES) == q2.KERNEL_AUTO
+    assert L.q2k_set_product_kernel(q2.KERNEL_PACKED_DOTS) == q2.KERNEL_MATRIX_CORES
+    assert L.q2k_set_product_kernel(prev) == q2.KERNEL_PACKED_DOTS
 
 
 def _err(L):

@@ -175,6 +175,22 @@ def test_mmvq_deterministic_and_stride_independent():
 
 
 # ------------------------------------------------- matrix-core path ---------
+
+@pytest.fixture
+def matrix_cores():
+    """Runs the test with the matrix-core kernel wherever it applies (the
+    automatic choice takes it only where its cost model says it is faster)."""
+    prev = q2.q2k_set_product_kernel(q2.KERNEL_MATRIX_CORES)
+    yield
+    q2.q2k_set_product_kernel(prev)
+
+
+@pytest.fixture
+def packed_dots():
+    prev = q2.q2k_set_product_kernel(q2.KERNEL_PACKED_DOTS)
+    yield
+    q2.q2k_set_product_kernel(prev)
+
 # 2..8 tokens against matrices of at least 64 workgroups of 128 rows (8192
 # rows) with 4, 8, 16 or 28 super-blocks per row run on the matrix cores.
 
@@ -188,7 +204,7 @@ def _sample_rows(n, seed, extra=256):
 
 
 @pytest.mark.parametrize("k,m", [(1024, 2), (1024, 8), (2048, 3), (4096, 5), (4096, 8), (7168, 4)])
-def test_mfma_mmvq(k, m):
+def test_mfma_mmvq(k, m, matrix_cores):
     n = MFMA_ROWS
     case = syn.single_gemv_case(n=n, k=k, m=m, seed=7000 + k + m)
     w = dev(case.w.reshape(-1))
@@ -211,7 +227,7 @@ def _constant_blocks(n, k, scale_byte, qs_byte, d_bits, dmin_bits):
 
 
 @pytest.mark.parametrize("k", [1024, 7168])
-def test_mfma_closed_forms(k):
+def test_mfma_closed_forms(k, matrix_cores):
     """x = 127 everywhere (d8 = 1, every half sum 16*127). I term: q = 3,
     sc = 1, d = 1, m = 0 gives 3*127*k. M term: sc = 0, m = 5, dmin = 1
     gives -5*127*k."""
@@ -226,7 +242,7 @@ def test_mfma_closed_forms(k):
     assert np.all(y == -5 * 127 * k)
 
 
-def test_mfma_pair():
+def test_mfma_pair(matrix_cores):
     pc = syn.attention_pair_case(4, seed=77, na=4096 + 7, nb=4096 + 100, k=2048)
     xq = q2.q8_1_rows(bf16_dev(pc.x_bits))
     oq, od = assert_q8_equal(xq, pc.x_bits)
@@ -237,10 +253,39 @@ def test_mfma_pair():
     assert_close(yb.cpu().numpy()[:, _sample_rows(pc.nb, 2)], rb, "mfma pair b")
 
 
-@pytest.mark.parametrize("x_per_id", [False, True])
-def test_mfma_experts(x_per_id):
-    """Gate/up-shaped experts (2048 rows) over 8 ids and two bases: 256
-    workgroups; one id out of range gives NaN rows and the flag."""
+def test_pair_token_split_and_matrix_cores_agree():
+    """The pair at m = 8 through the packed-dot kernel (tokens split over
+    waves) and through the matrix cores: both within the tolerance of the
+    oracle on every output."""
+    pc = syn.attention_pair_case(8, seed=78, na=2048 + 3, nb=1024 + 9, k=4096)
+    xq = q2.q8_1_rows(bf16_dev(pc.x_bits))
+    oq, od = assert_q8_equal(xq, pc.x_bits)
+    wa, wb = dev(pc.wa.reshape(-1)), dev(pc.wb.reshape(-1))
+    ra, rb = orc.mmvq_pair(pc.wa, pc.wb, oq, od)
+    for choice in (q2.KERNEL_PACKED_DOTS, q2.KERNEL_MATRIX_CORES):
+        prev = q2.q2k_set_product_kernel(choice)
+        try:
+            ya, yb = q2.q2k_mmvq_pair(wa, pc.na, wb, pc.nb, xq, pc.k, 8)
+        finally:
+            q2.q2k_set_product_kernel(prev)
+        assert_close(ya.cpu().numpy(), ra, f"pair a, kernel {choice}")
+        assert_close(yb.cpu().numpy(), rb, f"pair b, kernel {choice}")
+
+
+@pytest.mark.parametrize("n,k,m", [(1536, 4096, 8), (4103, 2048, 4), (300, 1024, 5),
+                                   (1000, 2048, 2), (77, 512, 3), (64, 7168, 7)])
+def test_token_split(n, k, m, packed_dots):
+    """m > 1 on the packed-dot kernels: each wave takes one token. The first
+    two shapes have enough (row step, token) pairs for the run kernel, the
+    others take one step per wave; k = 512 has fewer than 8 lanes per row."""
+    case = syn.single_gemv_case(n=n, k=k, m=m, seed=7400 + n + m)
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits))
+    oq, od = assert_q8_equal(xq, case.x_bits)
+    y = q2.q2k_mmvq(dev(case.w.reshape(-1)), xq, n, k, m).cpu().numpy()
+    assert_close(y, orc.mmvq(case.w, oq, od), f"token split n={n} k={k} m={m}")
+
+
+def _experts_check(x_per_id):
     rng = syn.rng_for(56, int(x_per_id))
     n, k, m, n_exp = 2048, 1024, 3, 10
     mats = [[syn.q2k_blocks(rng, n, k // 256) for _ in range(n_exp)] for _ in range(2)]
@@ -262,7 +307,21 @@ def test_mfma_experts(x_per_id):
                 continue
             xs = slice(i * m, (i + 1) * m) if x_per_id else slice(0, m)
             ref = orc.mmvq(mats[b][e][rows], oq[xs], od[xs])
-            assert_close(y[b, i][:, rows], ref, f"mfma expert base={b} id={e}")
+            assert_close(y[b, i][:, rows], ref, f"expert base={b} id={e}")
+
+
+@pytest.mark.parametrize("x_per_id", [False, True])
+def test_mfma_experts(x_per_id, matrix_cores):
+    """Gate/up-shaped experts (2048 rows) over 8 ids and two bases: 256
+    workgroups; one id out of range gives NaN rows and the flag."""
+    _experts_check(x_per_id)
+
+
+@pytest.mark.parametrize("x_per_id", [False, True])
+def test_experts_token_split(x_per_id, packed_dots):
+    """The same batch (m = 3) on the packed-dot kernels, tokens split over
+    waves."""
+    _experts_check(x_per_id)
 
 
 # ---------------------------------------------------------------- pair ------
