@@ -110,6 +110,22 @@ Q2K_API int32_t q8_1_rows(const void* x_bf16_dev, int64_t x_row_stride, void* xq
 Q2K_API int32_t q2k_mmvq(const void* w_dev, const void* xq_dev, float* y_dev,
                  int32_t n, int32_t k, int32_t m, void* stream);
 
+/* q8_1_rows and then q2k_mmvq in one call, with the same bytes in xq and
+ * the same bits in y as the two calls (attn_v41/decode.rs and moe_v41/init.rs
+ * quantise an input once and then run its products; here the quantisation
+ * can live inside the product). For one token and rows of 1024..8192
+ * values it is one launch: each workgroup quantises the bf16 row into LDS
+ * while its first weight loads are in flight, and workgroup 0 writes the
+ * q8_1 row to xq; otherwise a q8_1 launch runs ahead of the product.
+ *   w_dev, y_dev, n, k, m : as in q2k_mmvq (m in 1..8).
+ *   x_bf16_dev, x_row_stride : as in q8_1_rows.
+ *   xq_dev, xq_bytes : output, the q8_1 rows (q8_1_rows_bytes(m, k)),
+ *                      16-byte aligned, overlapping no input.
+ * Errors: those of q8_1_rows and q2k_mmvq; y may not overlap w, x or xq. */
+Q2K_API int32_t q8_1_q2k_mmvq(const void* w_dev, const void* x_bf16_dev, int64_t x_row_stride,
+                              void* xq_dev, size_t xq_bytes, float* y_dev, int32_t n, int32_t k,
+                              int32_t m, void* stream);
+
 /* Two Q2_K matrices that read the same q8_1 rows, in one launch
  * (mmvq_q2k_pair_w via kquant_mmvq_pair_w, attn_v41/decode.rs
  * q_kv_projections: wq_a and wkv). ya_dev f32 [m, na], yb_dev f32 [m, nb];

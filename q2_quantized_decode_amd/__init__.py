@@ -35,6 +35,7 @@ SIGNATURES = {
     "q8_1_rows_bytes": (_SZ, [_I32, _I32]),
     "q8_1_rows": (_I32, [_VP, _I64, _VP, _SZ, _I32, _I32, _VP]),
     "q2k_mmvq": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
+    "q8_1_q2k_mmvq": (_I32, [_VP, _VP, _I64, _VP, _SZ, _VP, _I32, _I32, _I32, _VP]),
     "q2k_mmvq_pair": (_I32, [_VP, _VP, _I32, _VP, _VP, _I32, _VP, _I32, _I32, _VP]),
     "q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP, _I32,
                                 _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP]),
@@ -142,6 +143,24 @@ def q2k_mmvq(w: torch.Tensor, xq: torch.Tensor, n: int, k: int, m: int,
     _check("q2k_mmvq", lib().q2k_mmvq(_contig(w, "w"), _contig(xq, "xq"), _contig(out, "out"),
                                       n, k, m, _stream()))
     return out
+
+
+def q8_1_q2k_mmvq(w: torch.Tensor, x: torch.Tensor, n: int, k: int,
+                  xq: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """q8_1 rows of bf16 x [m, k] into xq, then f32 [m, n] = w [n, k] times
+    them: one call (one launch for a single token). Returns (y, xq)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a bf16 [m, k] tensor with unit column stride")
+    m = x.shape[0]
+    need = q8_1_rows_bytes(m, k)
+    if xq is None:
+        xq = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _check("q8_1_q2k_mmvq", lib().q8_1_q2k_mmvq(
+        _contig(w, "w"), _dev(x, "x"), x.stride(0), _contig(xq, "xq"), xq.numel(),
+        _contig(out, "out"), n, k, m, _stream()))
+    return out, xq
 
 
 def q2k_mmvq_pair(wa: torch.Tensor, na: int, wb: torch.Tensor, nb: int, xq: torch.Tensor,

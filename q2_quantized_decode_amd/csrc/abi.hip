@@ -126,6 +126,41 @@ int32_t q2k_mmvq(const void* w_dev, const void* xq_dev, float* y_dev, int32_t n,
   return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
 }
 
+int32_t q8_1_q2k_mmvq(const void* w_dev, const void* x_bf16_dev, int64_t x_row_stride, void* xq_dev,
+                      size_t xq_bytes, float* y_dev, int32_t n, int32_t k, int32_t m, void* stream) {
+  const char* fn = "q8_1_q2k_mmvq";
+  if (int32_t r = check_matrix(fn, "w", w_dev, n)) return r;
+  if (int32_t r = check_out(fn, "y", y_dev)) return r;
+  if (!x_bf16_dev || !xq_dev) return fail(Q2K_EINVAL, "%s: null pointer", fn);
+  if (int32_t r = check_k(fn, k)) return r;
+  if (int32_t r = check_m(fn, m)) return r;
+  if (x_row_stride < k) return fail(Q2K_ESHAPE, "%s: row stride %lld < k = %d", fn, (long long)x_row_stride, k);
+  if (!aligned(x_bf16_dev, 16) || x_row_stride % 8 != 0)
+    return fail(Q2K_EALIGN, "%s: x must be 16-byte aligned with a row stride that is a multiple of 8", fn);
+  if (!aligned(xq_dev, 16)) return fail(Q2K_EALIGN, "%s: xq must be 16-byte aligned", fn);
+  const size_t need = q8_1_rows_bytes(m, k);
+  if (xq_bytes < need) return fail(Q2K_ESPACE, "%s: xq holds %zu bytes, %zu needed", fn, xq_bytes, need);
+  const size_t xbytes = ((size_t)(m - 1) * x_row_stride + k) * 2;
+  const size_t ybytes = (size_t)m * n * 4;
+  const size_t wbytes = q2k_matrix_bytes(n, k);
+  if (overlap(x_bf16_dev, xbytes, xq_dev, need) || overlap(xq_dev, need, w_dev, wbytes))
+    return fail(Q2K_EINVAL, "%s: xq overlaps an input", fn);
+  if (overlap(y_dev, ybytes, w_dev, wbytes) || overlap(y_dev, ybytes, x_bf16_dev, xbytes) ||
+      overlap(y_dev, ybytes, xq_dev, need))
+    return fail(Q2K_EINVAL, "%s: y overlaps an input or xq", fn);
+  q2k::MmvqLaunch a{};
+  a.w[0] = w_dev;
+  a.y[0] = y_dev;
+  a.n[0] = n;
+  a.njobs = 1;
+  a.xq = xq_dev;
+  a.k = k;
+  a.m = m;
+  a.x_bf16 = x_bf16_dev;
+  a.x_stride = x_row_stride;
+  return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
+}
+
 int32_t q2k_mmq(const void* w_dev, const void* xq_dev, float* y_dev, int32_t n, int32_t k, int32_t m,
                 void* stream) {
   const char* fn = "q2k_mmq";

@@ -411,6 +411,67 @@ __device__ __forceinline__ WHalf load_whalf_at(const uint8_t* base, const LaneOf
   return r;
 }
 
+// The lane's activations from a q8_1 row held in LDS (same layout as in
+// device memory: k quants, k/32 scales, k/16 half sums).
+__device__ __forceinline__ AHalf load_ahalf_lds(const uint8_t* xs, int k, int b, int h) {
+  AHalf a;
+  const uint8_t* q = xs + 256 * b + 128 * h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a.x[i] = *reinterpret_cast<const u32x4*>(q + 16 * i);
+  a.d8 = *reinterpret_cast<const f32x4*>(xs + q8_scale_offset(k) + (size_t)(8 * b + 4 * h) * 4);
+  a.s = *reinterpret_cast<const u32x4*>(xs + q8_sum_offset(k) + (size_t)(16 * b + 8 * h) * 2);
+  return a;
+}
+
+// q8_1 of one 32-value block of bf16 (raw: its 64 bytes) into a q8_1 row
+// in LDS and, when gout is non-null, into the same row in device memory.
+// Same arithmetic as q8_1_rows (q8_1_scale, q8_1_quant), so the same bytes.
+__device__ __forceinline__ void q8_1_block_store(uint8_t* xs, uint8_t* gout, const u32x4 raw[4],
+                                                 int blk, int k, bool active) {
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t w = raw[i >> 2][i & 3];
+    v[2 * i] = bf16_bits_to_f32(w & 0xffffu);
+    v[2 * i + 1] = bf16_bits_to_f32(w >> 16);
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+  const float d = q8_1_scale(a);
+  int qv[32];
+  q8_1_quant_lane<32>(v, d, qv);
+  uint32_t qw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int s0 = 0, s1 = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int q = qv[i];
+    if (i < 16) s0 += q; else s1 += q;
+    qw[i >> 2] |= (uint32_t)(q & 0xff) << (8 * (i & 3));
+  }
+  if (!active) return;
+  const u32x4 lo{qw[0], qw[1], qw[2], qw[3]}, hi{qw[4], qw[5], qw[6], qw[7]};
+  const uint32_t sums = ((uint32_t)s0 & 0xffffu) | ((uint32_t)s1 << 16);
+  const size_t so = q8_scale_offset(k) + (size_t)blk * 4, mo = q8_sum_offset(k) + (size_t)blk * 4;
+  *reinterpret_cast<u32x4*>(xs + 32 * blk) = lo;
+  *reinterpret_cast<u32x4*>(xs + 32 * blk + 16) = hi;
+  *reinterpret_cast<float*>(xs + so) = d;
+  *reinterpret_cast<uint32_t*>(xs + mo) = sums;
+  if (gout != nullptr) {
+    *reinterpret_cast<u32x4*>(gout + 32 * blk) = lo;
+    *reinterpret_cast<u32x4*>(gout + 32 * blk + 16) = hi;
+    *reinterpret_cast<float*>(gout + so) = d;
+    *reinterpret_cast<uint32_t*>(gout + mo) = sums;
+  }
+}
+
+// Workgroup barrier that orders LDS only: weight loads stay in flight.
+__device__ __forceinline__ void lds_barrier_m1() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // One token, rows of at most 64 half blocks and at least 8 lanes per row
 // (k from 1024 to 8192). Each wave owns a run of CH row steps (CH a multiple
 // of 8, known at compile time), either consecutive or interleaved with the
@@ -432,10 +493,18 @@ __device__ __forceinline__ WHalf load_whalf_at(const uint8_t* base, const LaneOf
 // wave launch (kernel-argument preloading, enabled for this file), so that
 // case issues its first loads without reading the argument block at all.
 // Otherwise the block is fetched and resolved as for the other kernels.
-template <int GSL, int R, int CH>
+//
+// FQ (fused quantisation, one matrix, one token): xq0 is the bf16 row
+// instead. Each workgroup issues its bf16 loads and then its weight ring,
+// quantises the row into LDS (one thread per 32-value block; workgroup 0
+// also writes it to xq_out), and waits for LDS only, so the quantisation
+// overlaps the weights' memory latency and no separate q8_1 launch is
+// needed.
+template <int GSL, int R, int CH, bool FQ>
 __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const uint8_t* xq0, float* y0,
                                                       int32_t n0, int32_t k0, int32_t total_waves,
-                                                      int32_t g8, int32_t plain, const MmvqParams p) {
+                                                      int32_t g8, int32_t plain, uint8_t* xq_out,
+                                                      const MmvqParams p) {
   constexpr int GS = 1 << GSL;
   constexpr int P = 64 >> GSL;
   constexpr int V = 8;
@@ -444,10 +513,11 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
   const int wiw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wg = blockIdx.x;
   int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 + wiw;
-  if (wave >= total_waves) return;
+  // with FQ every wave of the workgroup takes part in the quantisation
+  if (!FQ && wave >= total_waves) return;
   WaveJob J;
   int tok = 0;
-  if (plain) {
+  if (FQ || plain) {
     // one matrix, runs interleaved: wave w takes steps w, w + W, ...
     J.w = w0;
     J.y = y0;
@@ -471,7 +541,8 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
     J = resolve_wave<1>(p, wave, P);
     J.y += (int64_t)tok * J.ldy;
   }
-  if (J.it >= J.it_end) return;
+  const bool live = wave < total_waves && J.it < J.it_end;
+  if (!FQ && !live) return;
 
   const int k = k0;
   const int nb = k >> 8;
@@ -493,16 +564,44 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
   const int last_step = J.it + (CH - 1) * S;
   const bool full = last_step < J.it_end && (last_step + 1) * P <= J.n;
 
-  // Activations first: the first step waits for them and ring slot 0 only.
-  const AHalf act = load_ahalf(J.x, tok, b, h);
+  // Each lane loads its own half block's fields.
+  const LaneOffsets off = lane_offsets((uint32_t)prow * rowbytes + (uint32_t)b * kBlockBytes, h);
+  WHalf ws[R];
+  AHalf act;
+  if constexpr (FQ) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+    const int tid = threadIdx.x;
+    const int nblk = k >> 5;                 // <= 256 blocks (k <= 8192)
+    const bool qthread = tid < nblk;
+    const uint8_t* xb = xq0 + 64 * (qthread ? tid : 0);
+    u32x4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
+    // The ring goes out before the quantisation waits for the bf16 loads
+    // (loads complete in issue order). Unconditional loads: a wave without
+    // a full run reads row 0 and never uses it.
+    const bool ring_ok = live && full;
+    const LaneOffsets o0 = ring_ok ? off : lane_offsets((uint32_t)b * kBlockBytes, h);
+    const uint8_t* wr = ring_ok ? wrun : J.w;
+    const size_t rs = ring_ok ? run_stride : 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) ws[r] = load_whalf_at(wr + (size_t)r * rs, o0);
+    __builtin_amdgcn_sched_barrier(0);   // keep the ring ahead of the quantisation
+    q8_1_block_store(xs, blockIdx.x == 0 ? xq_out : nullptr, raw, tid, k, qthread);
+    lds_barrier_m1();
+    if (!live) return;
+    act = load_ahalf_lds(xs, k, b, h);
+  } else {
+    // Activations first: the first step waits for them and ring slot 0 only.
+    act = load_ahalf(J.x, tok, b, h);
+  }
   double dq[4], dm[4];
 
   if (full) {
-    // Each lane loads its own half block's fields.
-    const LaneOffsets off = lane_offsets((uint32_t)prow * rowbytes + (uint32_t)b * kBlockBytes, h);
-    WHalf ws[R];
+    if constexpr (!FQ) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) ws[r] = load_whalf_at(wrun + (size_t)r * run_stride, off);
+      for (int r = 0; r < R; ++r) ws[r] = load_whalf_at(wrun + (size_t)r * run_stride, off);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       dm[j] = (double)act.d8[j];
@@ -530,7 +629,6 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
       dm[j] = (double)act.d8[j];
       dq[j] = (j & 1) ? 0.25 * dm[j] : dm[j];
     }
-    const LaneOffsets off = lane_offsets((uint32_t)prow * rowbytes + (uint32_t)b * kBlockBytes, h);
     const LaneOffsets first = lane_offsets((uint32_t)b * kBlockBytes, h);
     for (int g0 = J.it; g0 < J.it_end; g0 += V * S) {
       double acc[V];
@@ -734,18 +832,49 @@ int cu_count() {
   return counts[dev];
 }
 
+// One matrix, one token, interleaved runs: the run kernel needs only its
+// leading scalar arguments (and can take the bf16 row itself).
+bool plain_launch(const MmvqParams& p) {
+  return p.ids == nullptr && p.groups == 0 && p.wave_end[0] == p.total_waves && p.interleave &&
+         p.tsplit == 1;
+}
+
+// The run kernel with fused quantisation: x_bf16 is the token's bf16 row, xq
+// receives its q8_1 row. Only for plain launches with the default ring.
+void dispatch_m1_fused(const MmvqParams& p, dim3 grid, const void* x_bf16, uint8_t* xq,
+                       hipStream_t s) {
+  const int ch = p.chunk;
+  const size_t lds = q8_row_bytes(p.k);
+  const uint8_t* x = static_cast<const uint8_t*>(x_bf16);
+#define Q2K_M1F(G, C)                                                                          \
+  hipLaunchKernelGGL((mmvq_m1_kernel<G, 4, C, true>), grid, dim3(256), lds, s, p.w[0], x,      \
+                     p.y[0], p.n[0], p.k, p.total_waves, p.g8, 1, xq, p)
+#define Q2K_M1F_CH(G)                            \
+  do {                                           \
+    if (ch == 8) Q2K_M1F(G, 8);                  \
+    else if (ch == 16) Q2K_M1F(G, 16);           \
+    else Q2K_M1F(G, 32);                         \
+  } while (0)
+  switch (p.gs_log2) {
+    case 3: Q2K_M1F_CH(3); return;
+    case 4: Q2K_M1F_CH(4); return;
+    case 5: Q2K_M1F_CH(5); return;
+    default: Q2K_M1F_CH(6); return;
+  }
+#undef Q2K_M1F_CH
+#undef Q2K_M1F
+}
+
 template <int M>
 void dispatch_narrow(const MmvqParams& p, dim3 grid, bool dots, int depth, bool run_kernel,
                      hipStream_t s) {
   if (M == 1 && run_kernel) {
     const int ring = tuning().ring;
     const int ch = p.chunk;
-    // one matrix, interleaved runs: the kernel needs only its scalar arguments
-    const int32_t plain = (p.ids == nullptr && p.groups == 0 && p.wave_end[0] == p.total_waves &&
-                           p.interleave && p.tsplit == 1) ? 1 : 0;
-#define Q2K_M1_ARGS p.w[0], p.xq, p.y[0], p.n[0], p.k, p.total_waves, p.g8, plain, p
+    const int32_t plain = plain_launch(p) ? 1 : 0;
+#define Q2K_M1_ARGS p.w[0], p.xq, p.y[0], p.n[0], p.k, p.total_waves, p.g8, plain, nullptr, p
 #define Q2K_M1(G, R, C) \
-  hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C>), grid, dim3(256), 0, s, Q2K_M1_ARGS)
+  hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, false>), grid, dim3(256), 0, s, Q2K_M1_ARGS)
 #define Q2K_M1_CH(G, R)                          \
   do {                                           \
     if (ch == 8) Q2K_M1(G, R, 8);                \
@@ -819,6 +948,15 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   const bool mfma = choice == 1   ? (a.dots == nullptr && a.m >= 2 && mfma_supports(a.k))
                     : choice == 2 ? false
                                   : mfma_preferred(a);
+  if (a.x_bf16 != nullptr && (mfma || a.m > kMaxM)) {
+    // quantisation first, then the product on the q8_1 rows
+    const hipError_t e = launch_q8_1_rows(a.x_bf16, a.x_stride, const_cast<void*>(a.xq), a.m, a.k,
+                                          stream);
+    if (e != hipSuccess) return e;
+    MmvqLaunch b = a;
+    b.x_bf16 = nullptr;
+    return launch_mmvq(b, stream);
+  }
   if (mfma) return launch_mmvq_mfma(a, stream);
   if (a.m > kMaxM) {
     // More tokens than the packed-dot kernels take: one launch per group of
@@ -920,6 +1058,15 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   p.g8 = (int)(groups / 8);
   const dim3 grid((unsigned)groups);
   const bool dots = a.dots != nullptr;
+  if (a.x_bf16 != nullptr) {
+    if (m1_path && a.m == 1 && !dots && plain_launch(p) && tu.ring == 4) {
+      dispatch_m1_fused(p, grid, a.x_bf16, static_cast<uint8_t*>(const_cast<void*>(a.xq)), stream);
+      return hipGetLastError();
+    }
+    const hipError_t e = launch_q8_1_rows(a.x_bf16, a.x_stride, const_cast<void*>(a.xq), a.m, a.k,
+                                          stream);
+    if (e != hipSuccess) return e;
+  }
 
   if (wide) {
     switch (a.m) {

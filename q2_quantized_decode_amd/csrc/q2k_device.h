@@ -71,6 +71,46 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
 
 __device__ __forceinline__ float quiet_nan() { return __uint_as_float(0x7fc00000u); }
 
+// q8_1 of one 32-value block (every quantiser of this library uses these
+// two, so fused and separate quantisation give the same bytes): d = amax/127
+// as a correctly rounded f32 division, and q = round-half-away-from-zero of
+// the correctly rounded quotient v/d, clamped to [-127, 127]; 0 when d == 0.
+__device__ __forceinline__ float q8_1_scale(float amax) { return amax / 127.0f; }
+
+__device__ __forceinline__ int q8_1_quant(float v, float d) {
+  const float r = fminf(fmaxf(roundf(v / d), -127.0f), 127.0f);   // no branch: d == 0 selects 0
+  return d > 0.0f ? (int)r : 0;
+}
+
+// q8_1_quant(v[i], d) for the NV values of one lane (all of one block), with
+// one correctly rounded division rd = 1.0f / d instead of one per value.
+// For a normal d, |v| <= amax = 127.x * d, so a = v * rd is within 2^-16
+// (two roundings of 2^-24 relative) of v / d and within 2^-15.6 of its
+// correctly rounded f32 quotient, and |a| < 127.5. Where a is more than
+// 2^-14 away from the nearest half-integer, both round to the same integer
+// and no tie is involved, so round-to-nearest-even of a (one instruction)
+// equals the half-away rounding of the quotient, already within +-127.
+// A lane with any value closer than that (ties included), a NaN, or a d that
+// is zero or subnormal recomputes its values with the division, in one
+// branch after the loop.
+template <int NV>
+__device__ __forceinline__ void q8_1_quant_lane(const float* v, float d, int* q) {
+  const float rd = 1.0f / d;
+  bool slow = !(d >= 0x1p-126f);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float a = v[i] * rd;
+    const float r = rintf(a);
+    slow = slow || !(fabsf(a - r) < 0.5f - 0x1p-14f);
+    q[i] = (int)r;
+  }
+  if (slow) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) q[i] = q8_1_quant(v[i], d);
+  }
+}
+
+
 // bf16 bits of elements e..e+3 (e a multiple of 4) of one 84-byte Q2_K block:
 // v = d*sc*q - dmin*m formed in f32 (d*(sc*q) and dmin*m are exact, so the
 // subtraction is the only rounding), then bf16 to nearest-even. The four

@@ -38,6 +38,12 @@ struct MmvqLaunch {
   int32_t groups;  // grouped mode when > 0
   int32_t k;
   int32_t m;
+  // Non-null: bf16 rows [m, k] (row stride x_stride elements) that the
+  // launch quantises into xq itself before the product (plain mode): in the
+  // product kernel when it can (one matrix, one token, run kernel), else by
+  // a q8_1 launch ahead of it.
+  const void* x_bf16 = nullptr;
+  int64_t x_stride = 0;
 };
 
 // Expert and grouped launches are n_jobs equal-sized jobs.

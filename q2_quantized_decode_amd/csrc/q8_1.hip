@@ -25,20 +25,12 @@ __device__ __forceinline__ void q8_1_store8(const float v[8], uint8_t* row, int 
   a = fmaxf(a, __shfl_xor(a, 1));
   a = fmaxf(a, __shfl_xor(a, 2));
   // Correctly rounded f32 division (no fast-math reciprocal).
-  const float d = a / 127.0f;
+  const float d = q8_1_scale(a);
   int q[8];
+  q8_1_quant_lane<8>(v, d, q);   // halves away from zero
   int s = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int qi = 0;
-    if (d > 0.0f) {
-      float r = roundf(v[i] / d);   // halves away from zero
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      qi = (int)r;
-    }
-    q[i] = qi;
-    s += qi;
-  }
+  for (int i = 0; i < 8; ++i) s += q[i];
   s += __shfl_xor(s, 1);   // lanes (4i, 4i+1) and (4i+2, 4i+3): one 16-wide half each
   if (!active) return;
   uint32_t lo = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |

@@ -75,6 +75,28 @@ def test_q8_1_rows_validation(L):
     assert L.q8_1_rows(P, 1024, P + 16, 1280, 1, 1024, None) == EINVAL  # overlap
 
 
+def test_fused_q8_1_mmvq_validation(L):
+    """q8_1_q2k_mmvq takes both calls' checks, before any launch."""
+    X, XQ, Y = 0x10000000, 0x20000000, 0x30000000
+    f = L.q8_1_q2k_mmvq
+    assert f(None, X, 1024, XQ, 1280, Y, 256, 1024, 1, None) == EINVAL
+    assert f(P, None, 1024, XQ, 1280, Y, 256, 1024, 1, None) == EINVAL
+    assert f(P, X, 1024, None, 1280, Y, 256, 1024, 1, None) == EINVAL
+    assert f(P, X, 1024, XQ, 1280, None, 256, 1024, 1, None) == EINVAL
+    assert f(P, X, 1000, XQ, 1250, Y, 256, 1000, 1, None) == ESHAPE
+    assert f(P, X, 1024, XQ, 1280 * 9, Y, 256, 1024, 9, None) == ESHAPE
+    assert f(P, X, 1024, XQ, 1280, Y, 0, 1024, 1, None) == ESHAPE
+    assert f(P, X, 512, XQ, 1280, Y, 256, 1024, 1, None) == ESHAPE          # stride < k
+    assert f(P, X + 2, 1024, XQ, 1280, Y, 256, 1024, 1, None) == EALIGN
+    assert f(P, X, 1028, XQ, 2560, Y, 256, 1024, 2, None) == EALIGN         # stride % 8
+    assert f(P, X, 1024, XQ + 4, 1280, Y, 256, 1024, 1, None) == EALIGN
+    assert f(P, X, 1024, XQ, 1279, Y, 256, 1024, 1, None) == ESPACE
+    assert "1280 needed" in _err(L)
+    assert f(P, X, 1024, X + 1024, 1280, Y, 256, 1024, 1, None) == EINVAL  # xq inside x
+    assert f(P, X, 1024, XQ, 1280, XQ + 64, 256, 1024, 1, None) == EINVAL  # y inside xq
+    assert f(P, X, 1024, XQ, 1280, X + 16, 256, 1024, 1, None) == EINVAL   # y inside x
+
+
 def test_mmvq_validation(L):
     assert L.q2k_mmvq(None, Q, P, 256, 1024, 1, None) == EINVAL
     assert L.q2k_mmvq(P, Q, 0x100, 256, 1000, 1, None) == ESHAPE

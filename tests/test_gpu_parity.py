@@ -116,6 +116,56 @@ def test_q8_1_rows_tiny_blocks_keep_subnormal_scales():
     assert_q8_equal(q2.q8_1_rows(bf16_dev(x)), x)
 
 
+def _near_half_blocks():
+    """Blocks [A, x_1..x_31] with every bf16 x in [A/2^20, A] (random signs),
+    for all 128 bf16 mantissas of A at exponents 0, -60, -120 and -125 (the
+    last gives a subnormal d = A/127): every quotient x/d that bf16 inputs can
+    produce near a block maximum, exact ties (x = A/2) included."""
+    rng = syn.rng_for(7777)
+    blocks = []
+    for ea in (0, -60, -120, -125):
+        for ma in range(128):
+            a_bits = ((ea + 127) << 7) | ma
+            xs = []
+            for e in range(ea - 20, ea + 1):
+                if e + 127 <= 0:
+                    continue
+                xs.append(((e + 127) << 7) | np.arange(128))
+            xs = np.concatenate(xs)
+            xs = xs[xs <= a_bits]
+            xs = xs | (rng.integers(0, 2, size=xs.size) << 15)
+            n_blk = -(-xs.size // 31)
+            blk = np.zeros((n_blk, 32), dtype=np.int64)
+            blk[:, 0] = a_bits
+            flat = np.zeros(n_blk * 31, dtype=np.int64)
+            flat[:xs.size] = xs
+            blk[:, 1:] = flat.reshape(n_blk, 31)
+            blocks.append(blk)
+    allb = np.concatenate(blocks)
+    rows = -(-allb.shape[0] // 64)
+    out = np.zeros((rows * 64, 32), dtype=np.int64)
+    out[:allb.shape[0]] = allb
+    return out.reshape(rows, 64 * 32).astype(np.uint16)
+
+
+def test_q8_1_rows_near_half_quotients():
+    """The quantisers divide once per block and take a product per value
+    where that provably rounds alike: bit-exact against the oracle's
+    per-value division on every quotient bf16 inputs give near a block's
+    maximum, and the fused product's q8_1 row equals q8_1_rows on them."""
+    x = _near_half_blocks()
+    xq = q2.q8_1_rows(bf16_dev(x))
+    assert_q8_equal(xq, x)
+    # the fused product (one launch: [8192, 2048] has enough row steps)
+    n, k = 8192, x.shape[1]
+    w = dev(syn.q2k_blocks(syn.rng_for(7778), n, k // 256).reshape(-1))
+    rb = q2.q8_1_rows_bytes(1, k)
+    xd = bf16_dev(x)
+    for r in range(x.shape[0]):
+        _, xq_f = q2.q8_1_q2k_mmvq(w, xd[r:r + 1], n, k)
+        assert torch.equal(xq_f[:rb], xq[r * rb:(r + 1) * rb]), f"row {r}"
+
+
 # ---------------------------------------------------------------- mmvq ------
 
 SHAPES = [
@@ -283,6 +333,34 @@ def test_token_split(n, k, m, packed_dots):
     oq, od = assert_q8_equal(xq, case.x_bits)
     y = q2.q2k_mmvq(dev(case.w.reshape(-1)), xq, n, k, m).cpu().numpy()
     assert_close(y, orc.mmvq(case.w, oq, od), f"token split n={n} k={k} m={m}")
+
+
+@pytest.mark.parametrize("n,k,m", [(20480, 2048, 1), (16384, 1024, 1), (8192, 4096, 1),
+                                   (4099, 8192, 1), (4096, 1024, 1), (300, 4096, 1),
+                                   (1000, 2048, 3), (8197, 7168, 8)])
+def test_fused_q8_1_equals_two_calls(n, k, m):
+    """q8_1_q2k_mmvq gives the bytes of q8_1_rows and the bits of q2k_mmvq on
+    them. The first four shapes run as one launch (quantisation in the
+    product's prologue; k = 8192 has 256 blocks, one per thread), the others
+    as a q8_1 launch ahead of the product (too few row steps for the run
+    kernel, m > 1). Rows are strided on the input for m > 1."""
+    case = syn.single_gemv_case(n=n, k=k, m=m, seed=7600 + n + k + m)
+    w = dev(case.w.reshape(-1))
+    if m == 1:
+        x = bf16_dev(case.x_bits)
+    else:
+        wide = torch.zeros((m, k + 64), dtype=torch.bfloat16, device="cuda")
+        wide[:, :k] = bf16_dev(case.x_bits)
+        x = wide[:, :k]
+    y, xq = q2.q8_1_q2k_mmvq(w, x, n, k)
+    xq2 = q2.q8_1_rows(x)
+    y2 = q2.q2k_mmvq(w, xq2, n, k, m)
+    need = q2.q8_1_rows_bytes(m, k)
+    assert torch.equal(xq[:need], xq2[:need])
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    oq, od = assert_q8_equal(xq, case.x_bits)
+    rows = _sample_rows(n, n + k, extra=64)
+    assert_close(y.cpu().numpy()[:, rows], orc.mmvq(case.w[rows], oq, od), f"fused n={n} k={k} m={m}")
 
 
 def _experts_check(x_per_id):
@@ -772,6 +850,23 @@ def test_mmq_small_m_is_mmvq():
 def large():
     case = syn.large_verify_case(m=8)
     return case, dev(case.w.reshape(-1))
+
+
+def test_fused_q8_1_large_verify(large):
+    """q8_1_q2k_mmvq on the [32768, 7168] matrix, one token (one launch, the
+    quantisation inside the product): the same q8_1 bytes and output bits as
+    q8_1_rows + q2k_mmvq, and within tolerance of the oracle on sampled rows."""
+    case, w = large
+    x = bf16_dev(case.x_bits[:1])
+    y, xq = q2.q8_1_q2k_mmvq(w, x, case.n, case.k)
+    xq2 = q2.q8_1_rows(x)
+    y2 = q2.q2k_mmvq(w, xq2, case.n, case.k, 1)
+    need = q2.q8_1_rows_bytes(1, case.k)
+    assert torch.equal(xq[:need], xq2[:need])
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    oq, od = assert_q8_equal(xq, case.x_bits[:1])
+    rows = _sample_rows(case.n, 77, extra=128)
+    assert_close(y.cpu().numpy()[:, rows], orc.mmvq(case.w[rows], oq, od), "fused large verify")
 
 
 def test_large_mmq_sampled(large):
