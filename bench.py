@@ -4,7 +4,12 @@ Workload: the large batched-verify matrix, Q2_K [32768, 7168] (28
 super-blocks per row, 77 070 336 bytes), seeded synthetic weights and bf16
 activations ~ N(0,1) with 5% +-20 outliers. One step is the whole decode hot
 path for that matrix: q8_1 quantisation of the bf16 token(s), then the
-Q2_K x q8_1 product. The headline runs m = 1; m = 8 is reported beside it.
+Q2_K x q8_1 product, through q8_1_q2k_mmvq (one launch at m = 1: the
+quantisation runs inside the product; the two-call step is timed beside
+it). The headline runs m = 1; m = 8 is reported beside it. Further sections
+time the other workloads (token groups past 8, grouped wo_a, engram step,
+attention pair, routed-expert batch, single small product); --only picks
+workloads for per-workload profiles.
 
 Method:
 * Inputs are resident in HBM before timing. The weights are replicated 16
