@@ -256,12 +256,20 @@ def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
                             out=yd)
 
     def step(i):
+        # q8_1 of x inside the gate/up launch (one launch for the token)
+        q2.q8_1_q2k_mmvq_experts([sets["gate"], sets["up"]], per_gu, ne, ids[i % steps_n], x, inter,
+                                 dim, xq=xq, out=gu)
+        q2.swiglu_q8_1_rows(g, u, hq=hq, want_h=False)
+        down(i)
+
+    def step_unfused(i):
         q2.q8_1_rows(x, out=xq)
         gate_up(i)
         q2.swiglu_q8_1_rows(g, u, hq=hq, want_h=False)
         down(i)
 
     us_step = graph_us(torch, step, steps_n)
+    us_step_unfused = graph_us(torch, step_unfused, steps_n)
     us_gu = graph_us(torch, gate_up, steps_n)
     us_down = graph_us(torch, down, steps_n)
     us_q8 = graph_us(torch, lambda i: q2.q8_1_rows(x, out=xq), 16)
@@ -270,8 +278,14 @@ def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
     # h within one bf16 step of the oracle's SwiGLU; then the down product
     # against the oracle on the oracle's q8_1 of that h
     i_last = steps_n - 1
+    step(i_last)
+    torch.cuda.synchronize()
+    gu_fused = gu.clone()
     q2.q8_1_rows(x, out=xq)
     gate_up(i_last)
+    torch.cuda.synchronize()
+    if not torch.equal(gu_fused.view(torch.int32), gu.view(torch.int32)):
+        raise SystemExit("bench parity failed: fused gate/up differs from q8_1 + gate/up")
     h, hq_p = q2.swiglu_q8_1_rows(g, u)
     yp = q2.q2k_mmvq_experts([sets["down"]], per_d, ne, ids[i_last], hq_p, True, dim, inter, 1)
     torch.cuda.synchronize()
@@ -301,10 +315,11 @@ def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
         + (8 * 16 * inter + q2.q8_1_rows_bytes(8, inter))
     return {"workload": "routed-expert decode batch, m = 1: 256 resident experts (Q2_K gate/up "
                         "[2048, 4096], down [4096, 2048]; 2.11 GB), 8 ids per step without "
-                        "replacement, 64 id sets; step = q8_1 + gate/up (one launch, 16 matrices) "
-                        "+ bf16 SwiGLU and q8_1 + down (one launch, 8 matrices, one input row "
-                        "per id)",
+                        "replacement, 64 id sets; step = q8_1 of x inside gate/up (one launch, 16 "
+                        "matrices) + bf16 SwiGLU and q8_1 + down (one launch, 8 matrices, one "
+                        "input row per id)",
             "us_per_step": round(us_step, 3), "tokens_per_s": round(1e6 / us_step, 1),
+            "us_per_step_separate_q8_1": round(us_step_unfused, 3),
             "step_gbs": round(step_bytes / us_step / 1e3, 1),
             "step_frac": round(step_bytes / us_step / 1e3 / PEAK_GBS, 4),
             "gate_up": _roof(b_gu, us_gu), "down": _roof(b_d, us_down),

@@ -155,6 +155,24 @@ Q2K_API int32_t q2k_mmvq_experts(const void* const* bases, int32_t n_bases,
                          int32_t n, int32_t k, int32_t m,
                          int32_t* err_flag_dev, void* stream);
 
+/* q8_1_rows of one shared input and then q2k_mmvq_experts on it
+ * (x_per_id = 0: the gate/up form of moe_v41/init.rs), in one call with the
+ * same bytes in xq and bits in y as the two calls. For one token on the
+ * run kernel it is one launch (each workgroup quantises x into LDS while
+ * its first weight loads are in flight; workgroup 0 writes xq); otherwise a
+ * q8_1 launch runs ahead of the product.
+ *   bases .. n_ids, y_dev, n, k, m, err_flag_dev : as in q2k_mmvq_experts.
+ *   x_bf16_dev, x_row_stride : bf16 [m, k] as in q8_1_rows.
+ *   xq_dev, xq_bytes : output, q8_1_rows_bytes(m, k) bytes, 16-byte aligned.
+ * Errors: those of q8_1_rows and q2k_mmvq_experts; x, xq, y, ids and the
+ * expert sets may not overlap. */
+Q2K_API int32_t q8_1_q2k_mmvq_experts(const void* const* bases, int32_t n_bases,
+                                      int64_t expert_stride_bytes, int32_t n_experts,
+                                      const int32_t* ids_dev, int32_t n_ids,
+                                      const void* x_bf16_dev, int64_t x_row_stride, void* xq_dev,
+                                      size_t xq_bytes, float* y_dev, int32_t n, int32_t k,
+                                      int32_t m, int32_t* err_flag_dev, void* stream);
+
 /* Q2_K x q8_1 product for any number of tokens (prefill, batched verify):
  * the pages' route past 8 tokens (moe_v41/init.rs, MoeV41::new: the
  * metrale_q2_k_mmq128_{nc,wc} kernels and the mmq activation buffers sized

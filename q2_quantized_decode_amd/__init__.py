@@ -39,6 +39,8 @@ SIGNATURES = {
     "q2k_mmvq_pair": (_I32, [_VP, _VP, _I32, _VP, _VP, _I32, _VP, _I32, _I32, _VP]),
     "q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP, _I32,
                                 _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP]),
+    "q8_1_q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP, _I32,
+                                     _VP, _I64, _VP, _SZ, _VP, _I32, _I32, _I32, _VP, _VP]),
     "q2k_mmvq_grouped": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP]),
     "q2k_mmq": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     "q2k_gemv_bf16": (_I32, [_VP, _VP, _I64, _VP, _I32, _I32, _I32, _VP]),
@@ -199,6 +201,33 @@ def q2k_mmvq_experts(bases: Sequence[torch.Tensor], expert_stride_bytes: int, n_
         _contig(xq, "xq"), 1 if x_per_id else 0, _contig(out, "out"), n, k, m, flag or None,
         _stream()))
     return out
+
+
+def q8_1_q2k_mmvq_experts(bases: Sequence[torch.Tensor], expert_stride_bytes: int, n_experts: int,
+                          ids: torch.Tensor, x: torch.Tensor, n: int, k: int,
+                          xq: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                          err_flag: Optional[torch.Tensor] = None):
+    """q8_1 of the shared bf16 input x [m, k] into xq, then the expert batch
+    on it (x_per_id = 0); one launch for one token. Returns (y, xq)."""
+    if ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a bf16 [m, k] tensor with unit column stride")
+    m = x.shape[0]
+    n_ids = ids.numel()
+    ptrs = [_contig(b, "base") for b in bases]
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    need = q8_1_rows_bytes(m, k)
+    if xq is None:
+        xq = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((len(ptrs), n_ids, m, n), dtype=torch.float32, device=ids.device)
+    flag = 0 if err_flag is None else _contig(err_flag, "err_flag")
+    _check("q8_1_q2k_mmvq_experts", lib().q8_1_q2k_mmvq_experts(
+        arr, len(ptrs), expert_stride_bytes, n_experts, _contig(ids, "ids"), n_ids, _dev(x, "x"),
+        x.stride(0), _contig(xq, "xq"), xq.numel(), _contig(out, "out"), n, k, m, flag or None,
+        _stream()))
+    return out, xq
 
 
 def q2k_mmq(w: torch.Tensor, xq: torch.Tensor, n: int, k: int, m: int,

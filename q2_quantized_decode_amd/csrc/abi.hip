@@ -221,11 +221,13 @@ int32_t q2k_mmvq_pair(const void* wa_dev, float* ya_dev, int32_t na, const void*
   return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
 }
 
-int32_t q2k_mmvq_experts(const void* const* bases, int32_t n_bases, int64_t expert_stride_bytes,
-                         int32_t n_experts, const int32_t* ids_dev, int32_t n_ids,
-                         const void* xq_dev, int32_t x_per_id, float* y_dev, int32_t n, int32_t k,
-                         int32_t m, int32_t* err_flag_dev, void* stream) {
-  const char* fn = "q2k_mmvq_experts";
+// Checks of the expert-batch forms and their launch description (xq is the
+// q8_1 input as the product reads it).
+static int32_t experts_launch(const char* fn, const void* const* bases, int32_t n_bases,
+                              int64_t expert_stride_bytes, int32_t n_experts, const int32_t* ids_dev,
+                              int32_t n_ids, const void* xq_dev, int32_t x_per_id, float* y_dev,
+                              int32_t n, int32_t k, int32_t m, int32_t* err_flag_dev,
+                              q2k::MmvqLaunch* a) {
   if (!bases) return fail(Q2K_EINVAL, "%s: bases is null", fn);
   if (n_bases < 1 || n_bases > q2k::kMaxExpertBases)
     return fail(Q2K_ESHAPE, "%s: n_bases = %d outside 1..%d", fn, n_bases, q2k::kMaxExpertBases);
@@ -252,20 +254,62 @@ int32_t q2k_mmvq_experts(const void* const* bases, int32_t n_bases, int64_t expe
     if (overlap(y_dev, ybytes, bases[i], set_bytes)) return fail(Q2K_EINVAL, "%s: y overlaps a base", fn);
   if (overlap(y_dev, ybytes, xq_dev, q8_1_rows_bytes(x_per_id ? n_ids * m : m, k)))
     return fail(Q2K_EINVAL, "%s: y overlaps xq", fn);
-  q2k::MmvqLaunch a{};
-  for (int i = 0; i < n_bases; ++i) a.w[i] = bases[i];
-  a.y[0] = y_dev;
-  a.n[0] = n;
-  a.njobs = n_bases;
-  a.xq = xq_dev;
-  a.ids = ids_dev;
-  a.n_ids = n_ids;
-  a.n_experts = n_experts;
-  a.x_per_id = x_per_id;
-  a.expert_stride = expert_stride_bytes;
-  a.err_flag = err_flag_dev;
-  a.k = k;
-  a.m = m;
+  *a = q2k::MmvqLaunch{};
+  for (int i = 0; i < n_bases; ++i) a->w[i] = bases[i];
+  a->y[0] = y_dev;
+  a->n[0] = n;
+  a->njobs = n_bases;
+  a->xq = xq_dev;
+  a->ids = ids_dev;
+  a->n_ids = n_ids;
+  a->n_experts = n_experts;
+  a->x_per_id = x_per_id;
+  a->expert_stride = expert_stride_bytes;
+  a->err_flag = err_flag_dev;
+  a->k = k;
+  a->m = m;
+  return Q2K_OK;
+}
+
+int32_t q2k_mmvq_experts(const void* const* bases, int32_t n_bases, int64_t expert_stride_bytes,
+                         int32_t n_experts, const int32_t* ids_dev, int32_t n_ids,
+                         const void* xq_dev, int32_t x_per_id, float* y_dev, int32_t n, int32_t k,
+                         int32_t m, int32_t* err_flag_dev, void* stream) {
+  const char* fn = "q2k_mmvq_experts";
+  q2k::MmvqLaunch a;
+  if (int32_t r = experts_launch(fn, bases, n_bases, expert_stride_bytes, n_experts, ids_dev, n_ids,
+                                 xq_dev, x_per_id, y_dev, n, k, m, err_flag_dev, &a))
+    return r;
+  return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
+}
+
+int32_t q8_1_q2k_mmvq_experts(const void* const* bases, int32_t n_bases, int64_t expert_stride_bytes,
+                              int32_t n_experts, const int32_t* ids_dev, int32_t n_ids,
+                              const void* x_bf16_dev, int64_t x_row_stride, void* xq_dev,
+                              size_t xq_bytes, float* y_dev, int32_t n, int32_t k, int32_t m,
+                              int32_t* err_flag_dev, void* stream) {
+  const char* fn = "q8_1_q2k_mmvq_experts";
+  q2k::MmvqLaunch a;
+  if (int32_t r = experts_launch(fn, bases, n_bases, expert_stride_bytes, n_experts, ids_dev, n_ids,
+                                 xq_dev, 0, y_dev, n, k, m, err_flag_dev, &a))
+    return r;
+  if (!x_bf16_dev) return fail(Q2K_EINVAL, "%s: x is null", fn);
+  if (x_row_stride < k) return fail(Q2K_ESHAPE, "%s: row stride %lld < k = %d", fn, (long long)x_row_stride, k);
+  if (!aligned(x_bf16_dev, 16) || x_row_stride % 8 != 0)
+    return fail(Q2K_EALIGN, "%s: x must be 16-byte aligned with a row stride that is a multiple of 8", fn);
+  const size_t need = q8_1_rows_bytes(m, k);
+  if (xq_bytes < need) return fail(Q2K_ESPACE, "%s: xq holds %zu bytes, %zu needed", fn, xq_bytes, need);
+  const size_t xbytes = ((size_t)(m - 1) * x_row_stride + k) * 2;
+  const size_t ybytes = (size_t)n_bases * n_ids * m * n * 4;
+  const size_t set_bytes = (size_t)expert_stride_bytes * (size_t)(n_experts - 1) + q2k_matrix_bytes(n, k);
+  if (overlap(x_bf16_dev, xbytes, xq_dev, need) || overlap(y_dev, ybytes, x_bf16_dev, xbytes))
+    return fail(Q2K_EINVAL, "%s: x overlaps xq or y", fn);
+  for (int i = 0; i < n_bases; ++i)
+    if (overlap(xq_dev, need, bases[i], set_bytes)) return fail(Q2K_EINVAL, "%s: xq overlaps a base", fn);
+  if (overlap(xq_dev, need, ids_dev, (size_t)n_ids * 4))
+    return fail(Q2K_EINVAL, "%s: xq overlaps ids", fn);
+  a.x_bf16 = x_bf16_dev;
+  a.x_stride = x_row_stride;
   return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
 }
 

@@ -494,8 +494,9 @@ __device__ __forceinline__ void lds_barrier_m1() {
 // case issues its first loads without reading the argument block at all.
 // Otherwise the block is fetched and resolved as for the other kernels.
 //
-// FQ (fused quantisation, one matrix, one token): xq0 is the bf16 row
-// instead. Each workgroup issues its bf16 loads and then its weight ring,
+// FQ (fused quantisation, one token, one input row shared by every matrix
+// of the launch: a single matrix or an expert batch with a shared input):
+// xq0 is the bf16 row instead. Each workgroup issues its bf16 loads and then its weight ring,
 // quantises the row into LDS (one thread per 32-value block; workgroup 0
 // also writes it to xq_out), and waits for LDS only, so the quantisation
 // overlaps the weights' memory latency and no separate q8_1 launch is
@@ -513,11 +514,14 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
   const int wiw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wg = blockIdx.x;
   int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 + wiw;
-  // with FQ every wave of the workgroup takes part in the quantisation
+  // with FQ every wave of the workgroup takes part in the quantisation; a
+  // wave past the end resolves the last wave's job (valid addresses only)
   if (!FQ && wave >= total_waves) return;
+  const bool in_grid = wave < total_waves;
+  if (FQ && !in_grid) wave = total_waves - 1;
   WaveJob J;
   int tok = 0;
-  if (FQ || plain) {
+  if (plain) {
     // one matrix, runs interleaved: wave w takes steps w, w + W, ...
     J.w = w0;
     J.y = y0;
@@ -541,7 +545,7 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
     J = resolve_wave<1>(p, wave, P);
     J.y += (int64_t)tok * J.ldy;
   }
-  const bool live = wave < total_waves && J.it < J.it_end;
+  const bool live = in_grid && J.it < J.it_end;
   if (!FQ && !live) return;
 
   const int k = k0;
@@ -839,16 +843,18 @@ bool plain_launch(const MmvqParams& p) {
          p.tsplit == 1;
 }
 
-// The run kernel with fused quantisation: x_bf16 is the token's bf16 row, xq
-// receives its q8_1 row. Only for plain launches with the default ring.
+// The run kernel with fused quantisation: x_bf16 is the token's bf16 row
+// (shared by every matrix of the launch), xq receives its q8_1 row. One
+// token, default ring.
 void dispatch_m1_fused(const MmvqParams& p, dim3 grid, const void* x_bf16, uint8_t* xq,
                        hipStream_t s) {
   const int ch = p.chunk;
   const size_t lds = q8_row_bytes(p.k);
   const uint8_t* x = static_cast<const uint8_t*>(x_bf16);
+  const int32_t plain = plain_launch(p) ? 1 : 0;
 #define Q2K_M1F(G, C)                                                                          \
   hipLaunchKernelGGL((mmvq_m1_kernel<G, 4, C, true>), grid, dim3(256), lds, s, p.w[0], x,      \
-                     p.y[0], p.n[0], p.k, p.total_waves, p.g8, 1, xq, p)
+                     p.y[0], p.n[0], p.k, p.total_waves, p.g8, plain, xq, p)
 #define Q2K_M1F_CH(G)                            \
   do {                                           \
     if (ch == 8) Q2K_M1F(G, 8);                  \
@@ -1059,7 +1065,8 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   const dim3 grid((unsigned)groups);
   const bool dots = a.dots != nullptr;
   if (a.x_bf16 != nullptr) {
-    if (m1_path && a.m == 1 && !dots && plain_launch(p) && tu.ring == 4) {
+    const bool shared_x = plain_launch(p) || (a.ids != nullptr && a.x_per_id == 0);
+    if (m1_path && a.m == 1 && !dots && shared_x && tu.ring == 4) {
       dispatch_m1_fused(p, grid, a.x_bf16, static_cast<uint8_t*>(const_cast<void*>(a.xq)), stream);
       return hipGetLastError();
     }

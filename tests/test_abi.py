@@ -97,6 +97,32 @@ def test_fused_q8_1_mmvq_validation(L):
     assert f(P, X, 1024, XQ, 1280, X + 16, 256, 1024, 1, None) == EINVAL   # y inside x
 
 
+def test_fused_q8_1_experts_validation(L):
+    import ctypes
+    X, XQ, Y, IDS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+    arr = (ctypes.c_void_p * 2)(P, Q)
+    f = L.q8_1_q2k_mmvq_experts
+    stride = 256 * 4 * 84
+    args = lambda **kw: [kw.get("bases", arr), kw.get("nb", 2), kw.get("stride", stride), 4,
+                         kw.get("ids", IDS), 8, kw.get("x", X), kw.get("xs", 1024), kw.get("xq", XQ),
+                         kw.get("xqb", 1280), kw.get("y", Y), 256, kw.get("k", 1024), kw.get("m", 1),
+                         None, None]
+    assert f(*args(x=None)) == EINVAL
+    assert f(*args(xq=None)) == EINVAL
+    assert f(*args(ids=None)) == EINVAL
+    assert f(*args(nb=5)) == ESHAPE
+    assert f(*args(k=1000, xs=1000)) == ESHAPE
+    assert f(*args(m=9, xqb=1280 * 9)) == ESHAPE
+    assert f(*args(stride=100)) == ESHAPE
+    assert f(*args(xs=512)) == ESHAPE
+    assert f(*args(x=X + 2)) == EALIGN
+    assert f(*args(xq=XQ + 4)) == EALIGN
+    assert f(*args(xqb=1279)) == ESPACE
+    assert f(*args(xq=X + 512)) == EINVAL            # xq inside x
+    assert f(*args(y=X + 16)) == EINVAL             # y inside x
+    assert f(*args(xq=IDS)) == EINVAL               # xq over the ids
+
+
 def test_mmvq_validation(L):
     assert L.q2k_mmvq(None, Q, P, 256, 1024, 1, None) == EINVAL
     assert L.q2k_mmvq(P, Q, 0x100, 256, 1000, 1, None) == ESHAPE

@@ -536,6 +536,49 @@ def test_expert_batch_stagewise(expert_batch):
         assert np.array_equal(s.view(np.uint32), yd.cpu().numpy()[0, i].view(np.uint32))
 
 
+def test_fused_q8_1_experts_equals_two_calls(expert_batch):
+    """q8_1_q2k_mmvq_experts (gate/up form, one launch for one token) gives
+    the bytes of q8_1_rows and the bits of q2k_mmvq_experts on them; an id
+    out of range still NaN-fills its rows and sets the flag."""
+    case, gate, up, down, per_gu, per_d = expert_batch
+    x = bf16_dev(case.x_bits)
+    for ids_np in (case.ids, np.array([case.ids[0], 300, case.ids[2], -4], dtype=np.int32)):
+        ids = dev(ids_np.astype(np.int32))
+        f1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        f2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        y, xq = q2.q8_1_q2k_mmvq_experts([gate, up], per_gu, case.n_experts, ids, x, case.inter,
+                                         case.dim, err_flag=f1)
+        xq2 = q2.q8_1_rows(x)
+        y2 = q2.q2k_mmvq_experts([gate, up], per_gu, case.n_experts, ids, xq2, False, case.inter,
+                                 case.dim, 1, err_flag=f2)
+        need = q2.q8_1_rows_bytes(1, case.dim)
+        assert torch.equal(xq[:need], xq2[:need])
+        assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+        assert int(f1.item()) == int(f2.item()) == int(np.any((ids_np < 0) | (ids_np >= case.n_experts)))
+
+
+def test_fused_q8_1_experts_small_and_multi_token():
+    """Shapes that take a q8_1 launch ahead of the product (few row steps;
+    m = 3): still the bits of the two calls."""
+    rng = syn.rng_for(57)
+    n, k, n_exp = 200, 1024, 6
+    mats = [syn.q2k_blocks(rng, n, k // 256) for _ in range(n_exp)]
+    stride = n * (k // 256) * 84
+    base = dev(np.concatenate([mt.reshape(-1) for mt in mats]))
+    ids = dev(np.array([5, 0, 3], dtype=np.int32))
+    for m in (1, 3):
+        xb = syn.bf16_normal(rng, (m, k))
+        x = bf16_dev(xb)
+        y, xq = q2.q8_1_q2k_mmvq_experts([base], stride, n_exp, ids, x, n, k)
+        xq2 = q2.q8_1_rows(x)
+        y2 = q2.q2k_mmvq_experts([base], stride, n_exp, ids, xq2, False, n, k, m)
+        assert torch.equal(xq[:q2.q8_1_rows_bytes(m, k)], xq2[:q2.q8_1_rows_bytes(m, k)])
+        assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+        oq, od = assert_q8_equal(xq, xb)
+        ref = orc.mmvq_experts([mats[i] for i in (5, 0, 3)], oq, od, x_per_id=False)
+        assert_close(y.cpu().numpy()[0], ref, f"fused experts m={m}")
+
+
 def test_expert_bad_id_flags_and_nans(expert_batch):
     case, gate, up, down, per_gu, per_d = expert_batch
     ids = dev(np.array([case.ids[0], 300, -1, case.ids[1]], dtype=np.int32))
