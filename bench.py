@@ -256,11 +256,12 @@ def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
                             out=yd)
 
     def step(i):
-        # q8_1 of x inside the gate/up launch (one launch for the token)
+        # q8_1 of x inside the gate/up launch, SwiGLU + q8_1 inside the down
+        # launch: two launches for the token
         q2.q8_1_q2k_mmvq_experts([sets["gate"], sets["up"]], per_gu, ne, ids[i % steps_n], x, inter,
                                  dim, xq=xq, out=gu)
-        q2.swiglu_q8_1_rows(g, u, hq=hq, want_h=False)
-        down(i)
+        q2.swiglu_q2k_mmvq_experts([sets["down"]], per_d, ne, ids[i % steps_n], g, u, dim, hq=hq,
+                                   out=yd)
 
     def step_unfused(i):
         q2.q8_1_rows(x, out=xq)
@@ -270,6 +271,8 @@ def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
 
     us_step = graph_us(torch, step, steps_n)
     us_step_unfused = graph_us(torch, step_unfused, steps_n)
+    us_down_fused = graph_us(torch, lambda i: q2.swiglu_q2k_mmvq_experts(
+        [sets["down"]], per_d, ne, ids[i % steps_n], g, u, dim, hq=hq, out=yd), steps_n)
     us_gu = graph_us(torch, gate_up, steps_n)
     us_down = graph_us(torch, down, steps_n)
     us_q8 = graph_us(torch, lambda i: q2.q8_1_rows(x, out=xq), 16)
@@ -280,12 +283,12 @@ def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
     i_last = steps_n - 1
     step(i_last)
     torch.cuda.synchronize()
-    gu_fused = gu.clone()
-    q2.q8_1_rows(x, out=xq)
-    gate_up(i_last)
+    gu_fused, yd_fused = gu.clone(), yd.clone()
+    step_unfused(i_last)
     torch.cuda.synchronize()
-    if not torch.equal(gu_fused.view(torch.int32), gu.view(torch.int32)):
-        raise SystemExit("bench parity failed: fused gate/up differs from q8_1 + gate/up")
+    if not (torch.equal(gu_fused.view(torch.int32), gu.view(torch.int32))
+            and torch.equal(yd_fused.view(torch.int32), yd.view(torch.int32))):
+        raise SystemExit("bench parity failed: the two-launch step differs from the four-launch one")
     h, hq_p = q2.swiglu_q8_1_rows(g, u)
     yp = q2.q2k_mmvq_experts([sets["down"]], per_d, ne, ids[i_last], hq_p, True, dim, inter, 1)
     torch.cuda.synchronize()
@@ -316,10 +319,11 @@ def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
     return {"workload": "routed-expert decode batch, m = 1: 256 resident experts (Q2_K gate/up "
                         "[2048, 4096], down [4096, 2048]; 2.11 GB), 8 ids per step without "
                         "replacement, 64 id sets; step = q8_1 of x inside gate/up (one launch, 16 "
-                        "matrices) + bf16 SwiGLU and q8_1 + down (one launch, 8 matrices, one "
-                        "input row per id)",
+                        "matrices) + bf16 SwiGLU and q8_1 inside down (one launch, 8 matrices, "
+                        "one input row per id)",
             "us_per_step": round(us_step, 3), "tokens_per_s": round(1e6 / us_step, 1),
-            "us_per_step_separate_q8_1": round(us_step_unfused, 3),
+            "us_per_step_four_launches": round(us_step_unfused, 3),
+            "swiglu_down_fused_us": round(us_down_fused, 3),
             "step_gbs": round(step_bytes / us_step / 1e3, 1),
             "step_frac": round(step_bytes / us_step / 1e3 / PEAK_GBS, 4),
             "gate_up": _roof(b_gu, us_gu), "down": _roof(b_d, us_down),

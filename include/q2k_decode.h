@@ -173,6 +173,30 @@ Q2K_API int32_t q8_1_q2k_mmvq_experts(const void* const* bases, int32_t n_bases,
                                       size_t xq_bytes, float* y_dev, int32_t n, int32_t k,
                                       int32_t m, int32_t* err_flag_dev, void* stream);
 
+/* swiglu_q8_1_rows of gate and up rows and then the down product on them
+ * (q2k_mmvq_experts with x_per_id = 1, one token), in one call with the
+ * same bytes in hq and bits in y as the two calls (moe_v41/init.rs:
+ * kquant_swiglu_q8_1_rows_bf16 between the gate/up and down products). For
+ * rows of at most 2048 values on the run kernel, with every workgroup
+ * inside one id's waves, it is one launch: each workgroup forms its id's
+ * bf16 SwiGLU and q8_1 row in LDS while its first weight loads are in
+ * flight; the workgroup holding the id's first wave writes that row to hq.
+ * Otherwise a SwiGLU launch runs ahead of the product.
+ *   bases .. n_ids, y_dev, n, k, err_flag_dev : as in q2k_mmvq_experts
+ *                (y f32 [n_bases, n_ids, n]).
+ *   g_dev, u_dev : f32 [n_ids, k] gate and up rows (row i for the i-th id),
+ *                  16-byte aligned.
+ *   hq_dev, hq_bytes : output, the q8_1 rows of h (q8_1_rows_bytes(n_ids, k)),
+ *                  16-byte aligned.
+ * Errors: those of swiglu_q8_1_rows and q2k_mmvq_experts; hq may not
+ * overlap g, u, ids or the expert sets, nor y overlap g or u. */
+Q2K_API int32_t swiglu_q2k_mmvq_experts(const void* const* bases, int32_t n_bases,
+                                        int64_t expert_stride_bytes, int32_t n_experts,
+                                        const int32_t* ids_dev, int32_t n_ids, const float* g_dev,
+                                        const float* u_dev, void* hq_dev, size_t hq_bytes,
+                                        float* y_dev, int32_t n, int32_t k,
+                                        int32_t* err_flag_dev, void* stream);
+
 /* Q2_K x q8_1 product for any number of tokens (prefill, batched verify):
  * the pages' route past 8 tokens (moe_v41/init.rs, MoeV41::new: the
  * metrale_q2_k_mmq128_{nc,wc} kernels and the mmq activation buffers sized

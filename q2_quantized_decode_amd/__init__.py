@@ -41,6 +41,8 @@ SIGNATURES = {
                                 _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP]),
     "q8_1_q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP, _I32,
                                      _VP, _I64, _VP, _SZ, _VP, _I32, _I32, _I32, _VP, _VP]),
+    "swiglu_q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP,
+                                       _I32, _VP, _VP, _VP, _SZ, _VP, _I32, _I32, _VP, _VP]),
     "q2k_mmvq_grouped": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP]),
     "q2k_mmq": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     "q2k_gemv_bf16": (_I32, [_VP, _VP, _I64, _VP, _I32, _I32, _I32, _VP]),
@@ -228,6 +230,35 @@ def q8_1_q2k_mmvq_experts(bases: Sequence[torch.Tensor], expert_stride_bytes: in
         x.stride(0), _contig(xq, "xq"), xq.numel(), _contig(out, "out"), n, k, m, flag or None,
         _stream()))
     return out, xq
+
+
+def swiglu_q2k_mmvq_experts(bases: Sequence[torch.Tensor], expert_stride_bytes: int, n_experts: int,
+                            ids: torch.Tensor, g: torch.Tensor, u: torch.Tensor, n: int,
+                            hq: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                            err_flag: Optional[torch.Tensor] = None):
+    """h = bf16 SwiGLU of the f32 gate and up rows g, u [n_ids, k], its q8_1
+    rows into hq, then the per-id expert product on them; one launch where
+    the shapes allow. Returns (y [n_bases, n_ids, 1, n], hq)."""
+    if ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    if g.dtype != torch.float32 or u.dtype != torch.float32 or g.shape != u.shape or g.dim() != 2:
+        raise ValueError("g and u must be f32 [n_ids, k] of one shape")
+    n_ids, k = g.shape
+    if n_ids != ids.numel():
+        raise ValueError("g and u need one row per id")
+    ptrs = [_contig(b, "base") for b in bases]
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    need = q8_1_rows_bytes(n_ids, k)
+    if hq is None:
+        hq = torch.empty(max(need, 16), dtype=torch.uint8, device=g.device)
+    if out is None:
+        out = torch.empty((len(ptrs), n_ids, 1, n), dtype=torch.float32, device=g.device)
+    flag = 0 if err_flag is None else _contig(err_flag, "err_flag")
+    _check("swiglu_q2k_mmvq_experts", lib().swiglu_q2k_mmvq_experts(
+        arr, len(ptrs), expert_stride_bytes, n_experts, _contig(ids, "ids"), n_ids,
+        _contig(g, "g"), _contig(u, "u"), _contig(hq, "hq"), hq.numel(), _contig(out, "out"), n, k,
+        flag or None, _stream()))
+    return out, hq
 
 
 def q2k_mmq(w: torch.Tensor, xq: torch.Tensor, n: int, k: int, m: int,

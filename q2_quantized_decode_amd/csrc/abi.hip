@@ -313,6 +313,36 @@ int32_t q8_1_q2k_mmvq_experts(const void* const* bases, int32_t n_bases, int64_t
   return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
 }
 
+int32_t swiglu_q2k_mmvq_experts(const void* const* bases, int32_t n_bases, int64_t expert_stride_bytes,
+                                int32_t n_experts, const int32_t* ids_dev, int32_t n_ids,
+                                const float* g_dev, const float* u_dev, void* hq_dev,
+                                size_t hq_bytes, float* y_dev, int32_t n, int32_t k,
+                                int32_t* err_flag_dev, void* stream) {
+  const char* fn = "swiglu_q2k_mmvq_experts";
+  q2k::MmvqLaunch a;
+  if (int32_t r = experts_launch(fn, bases, n_bases, expert_stride_bytes, n_experts, ids_dev, n_ids,
+                                 hq_dev, 1, y_dev, n, k, 1, err_flag_dev, &a))
+    return r;
+  if (!g_dev || !u_dev) return fail(Q2K_EINVAL, "%s: g or u is null", fn);
+  if (!aligned(g_dev, 16) || !aligned(u_dev, 16))
+    return fail(Q2K_EALIGN, "%s: g and u must be 16-byte aligned", fn);
+  const size_t need = q8_1_rows_bytes(n_ids, k);
+  if (hq_bytes < need) return fail(Q2K_ESPACE, "%s: hq holds %zu bytes, %zu needed", fn, hq_bytes, need);
+  const size_t gbytes = (size_t)n_ids * k * 4;
+  const size_t ybytes = (size_t)n_bases * n_ids * n * 4;
+  const size_t set_bytes = (size_t)expert_stride_bytes * (size_t)(n_experts - 1) + q2k_matrix_bytes(n, k);
+  if (overlap(hq_dev, need, g_dev, gbytes) || overlap(hq_dev, need, u_dev, gbytes) ||
+      overlap(hq_dev, need, ids_dev, (size_t)n_ids * 4))
+    return fail(Q2K_EINVAL, "%s: hq overlaps g, u or ids", fn);
+  for (int i = 0; i < n_bases; ++i)
+    if (overlap(hq_dev, need, bases[i], set_bytes)) return fail(Q2K_EINVAL, "%s: hq overlaps a base", fn);
+  if (overlap(y_dev, ybytes, g_dev, gbytes) || overlap(y_dev, ybytes, u_dev, gbytes))
+    return fail(Q2K_EINVAL, "%s: y overlaps g or u", fn);
+  a.sg = g_dev;
+  a.su = u_dev;
+  return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
+}
+
 int32_t q2k_mmvq_grouped(const void* w_dev, const void* xq_dev, float* y_dev, int32_t groups,
                          int32_t rows_per_group, int32_t k, int32_t m, void* stream) {
   const char* fn = "q2k_mmvq_grouped";

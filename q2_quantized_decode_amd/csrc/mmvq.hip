@@ -58,6 +58,8 @@ struct MmvqParams {
   int32_t gs_log2;                   // lanes per row group = 1 << gs_log2
   int32_t g8;                        // workgroups per XCD (grid / 8)
   int32_t tsplit;                    // tokens taken by separate waves (1: none)
+  const float* sg;                   // SwiGLU prologue: gate rows [n_ids, k]
+  const float* su;                   // and up rows
 };
 
 // Touches every field of the argument block at once, so that its scalar
@@ -83,6 +85,7 @@ struct WaveJob {
   int it_end;          // end of the run
   int stride;          // distance between the wave's consecutive steps
   bool bad;            // expert id out of range
+  int xrow;            // expert mode: position of the id in the list (its input row)
 };
 
 // M is the kernel's token count; a token-split launch (tsplit > 1) runs the
@@ -91,6 +94,7 @@ template <int M>
 __device__ __forceinline__ WaveJob resolve_wave(const MmvqParams& p, int wave, int P) {
   const int mt = M == 1 ? p.tsplit : M;
   WaveJob J;
+  J.xrow = 0;
   int lw;
   if (p.ids == nullptr && p.groups == 0) {
     const int j = (wave >= p.wave_end[0]) + (wave >= p.wave_end[1]) + (wave >= p.wave_end[2]);
@@ -116,6 +120,7 @@ __device__ __forceinline__ WaveJob resolve_wave(const MmvqParams& p, int wave, i
     const int base = j / p.n_ids;
     const int i = j - base * p.n_ids;
     const int id = p.ids[i];
+    J.xrow = i;
     J.bad = id < 0 || id >= p.n_experts;
     J.w = p.w[base] + (int64_t)(J.bad ? 0 : id) * p.expert_stride;
     J.n = p.n[0];
@@ -494,14 +499,18 @@ __device__ __forceinline__ void lds_barrier_m1() {
 // case issues its first loads without reading the argument block at all.
 // Otherwise the block is fetched and resolved as for the other kernels.
 //
-// FQ (fused quantisation, one token, one input row shared by every matrix
-// of the launch: a single matrix or an expert batch with a shared input):
-// xq0 is the bf16 row instead. Each workgroup issues its bf16 loads and then its weight ring,
+// FQ = 1 (fused quantisation, one token, one input row shared by every
+// matrix of the launch: a single matrix or an expert batch with a shared
+// input): xq0 is the bf16 row instead. FQ = 2 (expert batch, one input row
+// per id, every workgroup inside one id's waves): the workgroup forms the
+// bf16 SwiGLU of its id's gate and up rows (p.sg, p.su) and quantises it;
+// the workgroup holding the id's first wave writes that q8_1 row to
+// xq_out + id position * row bytes. Each workgroup issues its bf16 loads and then its weight ring,
 // quantises the row into LDS (one thread per 32-value block; workgroup 0
 // also writes it to xq_out), and waits for LDS only, so the quantisation
 // overlaps the weights' memory latency and no separate q8_1 launch is
 // needed.
-template <int GSL, int R, int CH, bool FQ>
+template <int GSL, int R, int CH, int FQ>
 __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const uint8_t* xq0, float* y0,
                                                       int32_t n0, int32_t k0, int32_t total_waves,
                                                       int32_t g8, int32_t plain, uint8_t* xq_out,
@@ -518,7 +527,25 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
   // wave past the end resolves the last wave's job (valid addresses only)
   if (!FQ && wave >= total_waves) return;
   const bool in_grid = wave < total_waves;
+  // FQ = 2: this workgroup writes its id's q8_1 row (its first wave starts the id)
+  const bool row_writer = FQ == 2 && in_grid && ((wave - wiw) % p.waves_per_job) == 0;
   if (FQ && !in_grid) wave = total_waves - 1;
+  // FQ = 2: the gate and up rows of this id position go out before the id
+  // itself is read (the row is the id's position in the list, not the id)
+  f32x4 gv[2], uv[2];
+  const int k_in = k0;
+  const bool sthread = FQ == 2 && (int)threadIdx.x < (k_in >> 3);   // 8 values per thread
+  const int se0 = sthread ? 8 * (int)threadIdx.x : 0;
+  if constexpr (FQ == 2) {
+    const int srow = (wave / p.waves_per_job) % p.n_ids;
+    const size_t ro = (size_t)srow * (size_t)k_in + (size_t)se0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      gv[i] = gload<f32x4>(p.sg + ro + 4 * i);
+      uv[i] = gload<f32x4>(p.su + ro + 4 * i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
   WaveJob J;
   int tok = 0;
   if (plain) {
@@ -572,18 +599,21 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
   const LaneOffsets off = lane_offsets((uint32_t)prow * rowbytes + (uint32_t)b * kBlockBytes, h);
   WHalf ws[R];
   AHalf act;
-  if constexpr (FQ) {
+  if constexpr (FQ != 0) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
     const int tid = threadIdx.x;
-    const int nblk = k >> 5;                 // <= 256 blocks (k <= 8192)
-    const bool qthread = tid < nblk;
-    const uint8_t* xb = xq0 + 64 * (qthread ? tid : 0);
+    // The input loads go out first, then the ring, so waiting for the input
+    // does not wait for the weights (loads complete in issue order).
+    // Unconditional loads: a wave without a full run reads row 0 and never
+    // uses it.
     u32x4 raw[4];
+    bool qthread = sthread;
+    if constexpr (FQ == 1) {
+      qthread = tid < (k >> 5);                 // one 32-value block per thread (k <= 8192)
+      const uint8_t* xb = xq0 + 64 * (qthread ? tid : 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
-    // The ring goes out before the quantisation waits for the bf16 loads
-    // (loads complete in issue order). Unconditional loads: a wave without
-    // a full run reads row 0 and never uses it.
+      for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
+    }
     const bool ring_ok = live && full;
     const LaneOffsets o0 = ring_ok ? off : lane_offsets((uint32_t)b * kBlockBytes, h);
     const uint8_t* wr = ring_ok ? wrun : J.w;
@@ -591,7 +621,19 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
 #pragma unroll
     for (int r = 0; r < R; ++r) ws[r] = load_whalf_at(wr + (size_t)r * rs, o0);
     __builtin_amdgcn_sched_barrier(0);   // keep the ring ahead of the quantisation
-    q8_1_block_store(xs, blockIdx.x == 0 ? xq_out : nullptr, raw, tid, k, qthread);
+    if constexpr (FQ == 1) {
+      q8_1_block_store(xs, blockIdx.x == 0 ? xq_out : nullptr, raw, tid, k, qthread);
+    } else {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = qthread ? bf16_bits_to_f32(swiglu_bf16_bits(gv[i >> 2][i & 3], uv[i >> 2][i & 3])) : 0.0f;
+      const Q8Lane r8 = q8_1_quant8(v);
+      if (qthread) {
+        q8_1_put8(r8, xs, se0, k);
+        if (row_writer) q8_1_put8(r8, xq_out + (size_t)J.xrow * q8_row_bytes(k), se0, k);
+      }
+    }
     lds_barrier_m1();
     if (!live) return;
     act = load_ahalf_lds(xs, k, b, h);
@@ -602,7 +644,7 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
   double dq[4], dm[4];
 
   if (full) {
-    if constexpr (!FQ) {
+    if constexpr (FQ == 0) {
 #pragma unroll
       for (int r = 0; r < R; ++r) ws[r] = load_whalf_at(wrun + (size_t)r * run_stride, off);
     }
@@ -846,6 +888,7 @@ bool plain_launch(const MmvqParams& p) {
 // The run kernel with fused quantisation: x_bf16 is the token's bf16 row
 // (shared by every matrix of the launch), xq receives its q8_1 row. One
 // token, default ring.
+template <int FQ>
 void dispatch_m1_fused(const MmvqParams& p, dim3 grid, const void* x_bf16, uint8_t* xq,
                        hipStream_t s) {
   const int ch = p.chunk;
@@ -853,7 +896,7 @@ void dispatch_m1_fused(const MmvqParams& p, dim3 grid, const void* x_bf16, uint8
   const uint8_t* x = static_cast<const uint8_t*>(x_bf16);
   const int32_t plain = plain_launch(p) ? 1 : 0;
 #define Q2K_M1F(G, C)                                                                          \
-  hipLaunchKernelGGL((mmvq_m1_kernel<G, 4, C, true>), grid, dim3(256), lds, s, p.w[0], x,      \
+  hipLaunchKernelGGL((mmvq_m1_kernel<G, 4, C, FQ>), grid, dim3(256), lds, s, p.w[0], x,        \
                      p.y[0], p.n[0], p.k, p.total_waves, p.g8, plain, xq, p)
 #define Q2K_M1F_CH(G)                            \
   do {                                           \
@@ -880,7 +923,7 @@ void dispatch_narrow(const MmvqParams& p, dim3 grid, bool dots, int depth, bool 
     const int32_t plain = plain_launch(p) ? 1 : 0;
 #define Q2K_M1_ARGS p.w[0], p.xq, p.y[0], p.n[0], p.k, p.total_waves, p.g8, plain, nullptr, p
 #define Q2K_M1(G, R, C) \
-  hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, false>), grid, dim3(256), 0, s, Q2K_M1_ARGS)
+  hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, 0>), grid, dim3(256), 0, s, Q2K_M1_ARGS)
 #define Q2K_M1_CH(G, R)                          \
   do {                                           \
     if (ch == 8) Q2K_M1(G, R, 8);                \
@@ -954,6 +997,14 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   const bool mfma = choice == 1   ? (a.dots == nullptr && a.m >= 2 && mfma_supports(a.k))
                     : choice == 2 ? false
                                   : mfma_preferred(a);
+  if (a.sg != nullptr && (mfma || a.m > kMaxM)) {
+    const hipError_t e = launch_swiglu_q8_1_rows(a.sg, a.su, nullptr, const_cast<void*>(a.xq),
+                                                 a.n_ids * a.m, a.k, stream);
+    if (e != hipSuccess) return e;
+    MmvqLaunch b = a;
+    b.sg = b.su = nullptr;
+    return launch_mmvq(b, stream);
+  }
   if (a.x_bf16 != nullptr && (mfma || a.m > kMaxM)) {
     // quantisation first, then the product on the q8_1 rows
     const hipError_t e = launch_q8_1_rows(a.x_bf16, a.x_stride, const_cast<void*>(a.xq), a.m, a.k,
@@ -1064,10 +1115,24 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   p.g8 = (int)(groups / 8);
   const dim3 grid((unsigned)groups);
   const bool dots = a.dots != nullptr;
+  if (a.sg != nullptr) {
+    // SwiGLU + q8_1 of each id's row inside the down product when every
+    // workgroup lies inside one id's waves; else the SwiGLU launch first
+    p.sg = a.sg;
+    p.su = a.su;
+    if (m1_path && a.m == 1 && !dots && a.ids != nullptr && a.x_per_id == 1 && a.k <= 2048 &&
+        p.waves_per_job % 4 == 0 && tu.ring == 4) {
+      dispatch_m1_fused<2>(p, grid, nullptr, static_cast<uint8_t*>(const_cast<void*>(a.xq)), stream);
+      return hipGetLastError();
+    }
+    const hipError_t e = launch_swiglu_q8_1_rows(a.sg, a.su, nullptr, const_cast<void*>(a.xq),
+                                                 a.n_ids * a.m, a.k, stream);
+    if (e != hipSuccess) return e;
+  }
   if (a.x_bf16 != nullptr) {
     const bool shared_x = plain_launch(p) || (a.ids != nullptr && a.x_per_id == 0);
     if (m1_path && a.m == 1 && !dots && shared_x && tu.ring == 4) {
-      dispatch_m1_fused(p, grid, a.x_bf16, static_cast<uint8_t*>(const_cast<void*>(a.xq)), stream);
+      dispatch_m1_fused<1>(p, grid, a.x_bf16, static_cast<uint8_t*>(const_cast<void*>(a.xq)), stream);
       return hipGetLastError();
     }
     const hipError_t e = launch_q8_1_rows(a.x_bf16, a.x_stride, const_cast<void*>(a.xq), a.m, a.k,

@@ -111,6 +111,62 @@ __device__ __forceinline__ void q8_1_quant_lane(const float* v, float d, int* q)
 }
 
 
+// q8_1 of 8 values v (elements e0..e0+7 of one row), lanes 4i..4i+3 of the
+// wave holding one 32-block (all lanes call it): the block scale d, the 8
+// quants and the sum of the lane's 16-wide half (lanes 2i and 2i+1).
+struct Q8Lane {
+  float d;
+  uint32_t lo, hi;   // the 8 quants, bytes
+  int s;             // sum of the 16 quants of the lane pair
+};
+
+__device__ __forceinline__ Q8Lane q8_1_quant8(const float* v) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+  a = fmaxf(a, __shfl_xor(a, 1));
+  a = fmaxf(a, __shfl_xor(a, 2));
+  Q8Lane r;
+  r.d = q8_1_scale(a);
+  int q[8];
+  q8_1_quant_lane<8>(v, r.d, q);   // halves away from zero
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += q[i];
+  r.s = s + __shfl_xor(s, 1);
+  r.lo = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
+         ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
+  r.hi = (uint32_t)(q[4] & 0xff) | ((uint32_t)(q[5] & 0xff) << 8) |
+         ((uint32_t)(q[6] & 0xff) << 16) | ((uint32_t)(q[7] & 0xff) << 24);
+  return r;
+}
+
+// Stores a lane's part of a q8_1 row (row base: device memory or LDS).
+__device__ __forceinline__ void q8_1_put8(const Q8Lane& r, uint8_t* row, int e0, int k) {
+  *reinterpret_cast<u32x2*>(row + e0) = u32x2{r.lo, r.hi};
+  const int lane = threadIdx.x & 63;
+  if ((lane & 3) == 0)
+    *reinterpret_cast<float*>(row + q8_scale_offset(k) + (size_t)(e0 / 32) * 4) = r.d;
+  if ((lane & 1) == 0)
+    *reinterpret_cast<int16_t*>(row + q8_sum_offset(k) + (size_t)(e0 / 16) * 2) = (int16_t)r.s;
+}
+
+__device__ __forceinline__ void q8_1_store8(const float* v, uint8_t* row, int e0, int k,
+                                            bool active) {
+  const Q8Lane r = q8_1_quant8(v);
+  if (active) q8_1_put8(r, row, e0, k);
+}
+
+// bf16 bits of silu(g) * u (the bf16 SwiGLU of the expert batch), in f32:
+// silu(g) = g * sigmoid(g), with exp taken of -|g| so it cannot overflow
+// (sigmoid = 1/(1+e) for g >= 0, e/(1+e) for g < 0), then round to nearest
+// even. Every SwiGLU of this library uses it, so they give the same bits.
+__device__ __forceinline__ uint32_t swiglu_bf16_bits(float g, float u) {
+  const float e = expf(-fabsf(g));
+  const float sig = g >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
+  return f32_to_bf16_bits(g * sig * u);
+}
+
 // bf16 bits of elements e..e+3 (e a multiple of 4) of one 84-byte Q2_K block:
 // v = d*sc*q - dmin*m formed in f32 (d*(sc*q) and dmin*m are exact, so the
 // subtraction is the only rounding), then bf16 to nearest-even. The four

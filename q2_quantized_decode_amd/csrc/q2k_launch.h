@@ -44,6 +44,11 @@ struct MmvqLaunch {
   // a q8_1 launch ahead of it.
   const void* x_bf16 = nullptr;
   int64_t x_stride = 0;
+  // Non-null (expert mode, x_per_id): f32 gate and up rows [n_ids * m, k];
+  // the launch forms xq = q8_1(bf16 SwiGLU) of them before the product, in
+  // the product kernel when it can, else by a SwiGLU launch ahead of it.
+  const float* sg = nullptr;
+  const float* su = nullptr;
 };
 
 // Expert and grouped launches are n_jobs equal-sized jobs.

@@ -15,36 +15,6 @@
 
 namespace q2k {
 
-// Quantise the 8 values v (elements e0..e0+7 of one row) and store them.
-// Lanes 4i..4i+3 of the wave must hold one 32-block; all lanes call this.
-__device__ __forceinline__ void q8_1_store8(const float v[8], uint8_t* row, int e0, int k,
-                                            bool active) {
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
-  a = fmaxf(a, __shfl_xor(a, 1));
-  a = fmaxf(a, __shfl_xor(a, 2));
-  // Correctly rounded f32 division (no fast-math reciprocal).
-  const float d = q8_1_scale(a);
-  int q[8];
-  q8_1_quant_lane<8>(v, d, q);   // halves away from zero
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s += q[i];
-  s += __shfl_xor(s, 1);   // lanes (4i, 4i+1) and (4i+2, 4i+3): one 16-wide half each
-  if (!active) return;
-  uint32_t lo = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
-                ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
-  uint32_t hi = (uint32_t)(q[4] & 0xff) | ((uint32_t)(q[5] & 0xff) << 8) |
-                ((uint32_t)(q[6] & 0xff) << 16) | ((uint32_t)(q[7] & 0xff) << 24);
-  *reinterpret_cast<u32x2*>(row + e0) = u32x2{lo, hi};
-  const int lane = threadIdx.x & 63;
-  if ((lane & 3) == 0)
-    *reinterpret_cast<float*>(row + q8_scale_offset(k) + (size_t)(e0 / 32) * 4) = d;
-  if ((lane & 1) == 0)
-    *reinterpret_cast<int16_t*>(row + q8_sum_offset(k) + (size_t)(e0 / 16) * 2) = (int16_t)s;
-}
-
 __global__ __launch_bounds__(256) void q8_1_rows_kernel(const uint16_t* __restrict__ x,
                                                         int64_t stride, uint8_t* __restrict__ xq,
                                                         int m, int k) {
@@ -93,12 +63,7 @@ __global__ __launch_bounds__(256) void swiglu_q8_1_rows_kernel(const float* __re
     const float uu[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // silu(g) = g * sigmoid(g), with exp taken of -|g| so it cannot
-      // overflow: sigmoid = 1/(1+e) for g >= 0 and e/(1+e) for g < 0.
-      const float e = expf(-fabsf(gg[i]));
-      const float sig = gg[i] >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
-      const float silu = gg[i] * sig;
-      hb[i] = f32_to_bf16_bits(silu * uu[i]);
+      hb[i] = swiglu_bf16_bits(gg[i], uu[i]);
       v[i] = bf16_bits_to_f32(hb[i]);
     }
     if (h_out != nullptr) {

@@ -123,6 +123,27 @@ def test_fused_q8_1_experts_validation(L):
     assert f(*args(xq=IDS)) == EINVAL               # xq over the ids
 
 
+def test_fused_swiglu_experts_validation(L):
+    import ctypes
+    G, U, HQ, Y, IDS = 0x10000000, 0x11000000, 0x20000000, 0x30000000, 0x40000000
+    arr = (ctypes.c_void_p * 1)(P,)
+    f = L.swiglu_q2k_mmvq_experts
+    stride = 4096 * 8 * 84
+    args = lambda **kw: [arr, 1, stride, 16, kw.get("ids", IDS), 8, kw.get("g", G), kw.get("u", U),
+                         kw.get("hq", HQ), kw.get("hqb", 8 * 2560), kw.get("y", Y), 4096,
+                         kw.get("k", 2048), None, None]
+    assert f(*args(g=None)) == EINVAL
+    assert f(*args(u=None)) == EINVAL
+    assert f(*args(hq=None)) == EINVAL
+    assert f(*args(k=2000)) == ESHAPE
+    assert f(*args(g=G + 4)) == EALIGN
+    assert f(*args(hq=HQ + 8)) == EALIGN
+    assert f(*args(hqb=8 * 2560 - 1)) == ESPACE
+    assert f(*args(hq=G + 64)) == EINVAL             # hq inside g
+    assert f(*args(y=U + 64)) == EINVAL              # y inside u
+    assert f(*args(hq=IDS)) == EINVAL
+
+
 def test_mmvq_validation(L):
     assert L.q2k_mmvq(None, Q, P, 256, 1024, 1, None) == EINVAL
     assert L.q2k_mmvq(P, Q, 0x100, 256, 1000, 1, None) == ESHAPE

@@ -557,6 +557,58 @@ def test_fused_q8_1_experts_equals_two_calls(expert_batch):
         assert int(f1.item()) == int(f2.item()) == int(np.any((ids_np < 0) | (ids_np >= case.n_experts)))
 
 
+def test_fused_swiglu_down_equals_two_calls(expert_batch):
+    """swiglu_q2k_mmvq_experts on the gate/up outputs of the expert batch
+    (one launch: SwiGLU and q8_1 of each id's row inside the down product)
+    gives the hq bytes of swiglu_q8_1_rows and the y bits of the down
+    product on them; the down output is within tolerance of the oracle on
+    the oracle's q8_1 of that h, and a bad id still NaN-fills and flags."""
+    case, gate, up, down, per_gu, per_d = expert_batch
+    x = bf16_dev(case.x_bits)
+    for ids_np in (case.ids, np.array(list(case.ids[:5]) + [999, case.ids[6], case.ids[7]], dtype=np.int32)):
+        ids = dev(ids_np.astype(np.int32))
+        gu, _ = q2.q8_1_q2k_mmvq_experts([gate, up], per_gu, case.n_experts, ids, x, case.inter, case.dim)
+        g = gu[0].reshape(len(ids_np), case.inter).contiguous()
+        u = gu[1].reshape(len(ids_np), case.inter).contiguous()
+        f1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        f2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        y, hq = q2.swiglu_q2k_mmvq_experts([down], per_d, case.n_experts, ids, g, u, case.dim, err_flag=f1)
+        h2, hq2 = q2.swiglu_q8_1_rows(g, u)
+        y2 = q2.q2k_mmvq_experts([down], per_d, case.n_experts, ids, hq2, True, case.dim, case.inter, 1,
+                                 err_flag=f2)
+        need = q2.q8_1_rows_bytes(len(ids_np), case.inter)
+        assert torch.equal(hq[:need], hq2[:need])
+        assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+        bad = (ids_np < 0) | (ids_np >= case.n_experts)
+        assert int(f1.item()) == int(f2.item()) == int(np.any(bad))
+        if not np.any(bad):
+            h_bits = h2.view(torch.int16).cpu().numpy().view(np.uint16)
+            hq_o, hd_o = assert_q8_equal(hq, h_bits)
+            mats = [case.expert_matrix(e, "down") for e in ids_np.tolist()]
+            ref = orc.mmvq_experts(mats, hq_o, hd_o, x_per_id=True)
+            assert_close(y.cpu().numpy()[0], ref, "fused SwiGLU down")
+
+
+@pytest.mark.parametrize("n,k,n_ids", [(4096, 4096, 3), (200, 1024, 5), (1000, 2048, 3)])
+def test_fused_swiglu_down_fallback_shapes(n, k, n_ids):
+    """Rows over 2048 values, too few row steps, or ids whose waves do not
+    fill whole workgroups: a SwiGLU launch ahead of the product, same bits."""
+    rng = syn.rng_for(58, n, k)
+    n_exp = 6
+    mats = [syn.q2k_blocks(rng, n, k // 256) for _ in range(n_exp)]
+    stride = n * (k // 256) * 84
+    base = dev(np.concatenate([mt.reshape(-1) for mt in mats]))
+    ids = dev(rng.choice(n_exp, n_ids, replace=False).astype(np.int32))
+    g = torch.from_numpy(rng.standard_normal((n_ids, k)).astype(np.float32) * 3).cuda()
+    u = torch.from_numpy(rng.standard_normal((n_ids, k)).astype(np.float32) * 3).cuda()
+    y, hq = q2.swiglu_q2k_mmvq_experts([base], stride, n_exp, ids, g, u, n)
+    _, hq2 = q2.swiglu_q8_1_rows(g, u, want_h=False)
+    y2 = q2.q2k_mmvq_experts([base], stride, n_exp, ids, hq2, True, n, k, 1)
+    need = q2.q8_1_rows_bytes(n_ids, k)
+    assert torch.equal(hq[:need], hq2[:need])
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+
 def test_fused_q8_1_experts_small_and_multi_token():
     """Shapes that take a q8_1 launch ahead of the product (few row steps;
     m = 3): still the bits of the two calls."""
