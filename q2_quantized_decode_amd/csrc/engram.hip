@@ -8,7 +8,9 @@
 //
 // Gate (engram_v41/apply.rs, engram_v41_gate with grid [T, hc]; engram_v41.rs
 // module doc step 4): one 256-thread workgroup per (token, stream) forms
-// three sums over dim in a fixed order, then updates the stream in place.
+// three sums over dim in a fixed order, then updates the stream in place
+// (16-byte loads, all issued at once, when dim % 4 == 0, dim <= 16384 and
+// the pointers are 16-byte aligned; strided scalar loads otherwise).
 //
 // N-gram hash (engram_v41.rs, EngramHasher::hash, which the pages run on the
 // host): one thread per (position, hashed layer), so the row ids are made on
@@ -75,6 +77,66 @@ __global__ __launch_bounds__(256) void engram_gate_kernel(float* __restrict__ h,
   const float sg = copysignf(sqrtf(fabsf(s)), s);
   const float g = 1.0f / (1.0f + expf(-sg));
   for (int i = threadIdx.x; i < dim; i += 256) hs[i] = fmaf(g, val[i], hs[i]);
+}
+
+// The same gate with 16-byte loads: thread i takes float4 elements i, i + 256,
+// ... (NV4 of them per array, dim = 4 * n4 <= 1024 * NV4), and every load of
+// the stream, key, weights and value goes out before the first sum, so the
+// kernel waits for memory once instead of once per strided scalar load.
+// Each thread sums its values in a fixed order, then the same fixed tree.
+template <int NV4>
+__global__ __launch_bounds__(256) void engram_gate_vec_kernel(float* __restrict__ h,
+                                                              const float* __restrict__ kv,
+                                                              const float* __restrict__ qk,
+                                                              int hc, int dim, float eps) {
+  __shared__ float lds[4];
+  const int t = blockIdx.x;
+  const int j = blockIdx.y;
+  const int n4 = dim >> 2;
+  f32x4* hs = reinterpret_cast<f32x4*>(h + ((int64_t)t * hc + j) * dim);
+  const f32x4* key = reinterpret_cast<const f32x4*>(kv + (int64_t)t * (hc + 1) * dim + (int64_t)j * dim);
+  const f32x4* val = reinterpret_cast<const f32x4*>(kv + (int64_t)t * (hc + 1) * dim + (int64_t)hc * dim);
+  const f32x4* w = reinterpret_cast<const f32x4*>(qk + (int64_t)j * dim);
+  f32x4 x[NV4], kk[NV4], ww[NV4], vv[NV4];
+#pragma unroll
+  for (int c = 0; c < NV4; ++c) {
+    const int i = (int)threadIdx.x + 256 * c;
+    const int ic = i < n4 ? i : 0;   // unconditional loads, zeroed below
+    x[c] = hs[ic];
+    kk[c] = key[ic];
+    ww[c] = w[ic];
+    vv[c] = val[ic];
+  }
+  float shh = 0.0f, skk = 0.0f, sqk = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NV4; ++c) {
+    if ((int)threadIdx.x + 256 * c < n4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        shh = fmaf(x[c][e], x[c][e], shh);
+        skk = fmaf(kk[c][e], kk[c][e], skk);
+        sqk = fmaf(ww[c][e] * x[c][e], kk[c][e], sqk);
+      }
+    }
+  }
+  shh = block_sum_256(shh, lds);
+  skk = block_sum_256(skk, lds);
+  sqk = block_sum_256(sqk, lds);
+  const float rh = sqrtf(shh / (float)dim + eps);
+  const float rk = sqrtf(skk / (float)dim + eps);
+  const float s = sqk / (rh * rk * sqrtf((float)dim));
+  const float sg = copysignf(sqrtf(fabsf(s)), s);
+  const float g = 1.0f / (1.0f + expf(-sg));
+#pragma unroll
+  for (int c = 0; c < NV4; ++c) {
+    const int i = (int)threadIdx.x + 256 * c;
+    if (i < n4) {
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = fmaf(g, vv[c][e], x[c][e]);
+      hs[i] = o;
+    }
+  }
 }
 
 // Row ids of the engram n-gram hash. Thread (s, l): position pos = start_pos + s,
@@ -168,8 +230,22 @@ hipError_t launch_dequant_rows(const void* table, int64_t n_table_rows, const in
 
 hipError_t launch_engram_gate(float* h, const float* kv, const float* qk, int t, int hc, int dim,
                               float eps, hipStream_t stream) {
-  hipLaunchKernelGGL(engram_gate_kernel, dim3((unsigned)t, (unsigned)hc), dim3(256), 0, stream, h,
-                     kv, qk, hc, dim, eps);
+  const dim3 grid((unsigned)t, (unsigned)hc);
+  const bool a16 = ((reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(kv) |
+                     reinterpret_cast<uintptr_t>(qk)) & 15u) == 0;
+  if (a16 && dim % 4 == 0 && dim <= 16384) {
+    const int nv4 = (dim / 4 + 255) / 256;
+#define Q2K_GATE_VEC(N) \
+  hipLaunchKernelGGL(engram_gate_vec_kernel<N>, grid, dim3(256), 0, stream, h, kv, qk, hc, dim, eps)
+    if (nv4 <= 1) Q2K_GATE_VEC(1);
+    else if (nv4 <= 2) Q2K_GATE_VEC(2);
+    else if (nv4 <= 4) Q2K_GATE_VEC(4);
+    else if (nv4 <= 8) Q2K_GATE_VEC(8);
+    else Q2K_GATE_VEC(16);
+#undef Q2K_GATE_VEC
+  } else {
+    hipLaunchKernelGGL(engram_gate_kernel, grid, dim3(256), 0, stream, h, kv, qk, hc, dim, eps);
+  }
   return hipGetLastError();
 }
 

@@ -741,12 +741,33 @@ def test_dequant_rows_hand_blocks_and_bad_ids():
     assert np.all(got[3:] == 0x7FC0) and int(flag.item()) == 1
 
 
-@pytest.mark.parametrize("t,hc,dim", [(1, 4, 4096), (2, 1, 4096), (3, 3, 1000), (1, 2, 7), (4, 4, 256)])
+@pytest.mark.parametrize("t,hc,dim", [(1, 4, 4096), (2, 1, 4096), (3, 3, 1000), (1, 2, 7), (4, 4, 256),
+                                      (1, 4, 16384), (2, 2, 6000), (1, 3, 4100)])
 def test_engram_gate(t, hc, dim):
     h, kv, qk, eps = syn.gate_case(11, t, hc, dim)
     hd = dev(h)
     q2.engram_gate(hd, dev(kv), dev(qk), eps)
     assert_close(hd.cpu().numpy(), orc.engram_gate(h, kv, qk, eps), f"gate {t},{hc},{dim}")
+
+
+def test_engram_gate_unaligned_takes_scalar_path():
+    """h, kv and qk 4 bytes past a 16-byte boundary: the strided scalar
+    kernel runs (the 16-byte one needs aligned rows); same tolerance."""
+    t, hc, dim = 1, 4, 4096
+    h, kv, qk, eps = syn.gate_case(12, t, hc, dim)
+    hb = torch.zeros(h.size + 1, dtype=torch.float32, device="cuda")
+    kb = torch.zeros(kv.size + 1, dtype=torch.float32, device="cuda")
+    qb = torch.zeros(qk.size + 1, dtype=torch.float32, device="cuda")
+    hb[1:] = dev(h.reshape(-1))
+    kb[1:] = dev(kv.reshape(-1))
+    qb[1:] = dev(qk.reshape(-1))
+    hv = hb[1:].view(t, hc, dim)
+    q2.engram_gate(hv, kb[1:].view(t, (hc + 1) * dim), qb[1:].view(hc, dim), eps)
+    ref = orc.engram_gate(h, kv, qk, eps)
+    assert_close(hv.cpu().numpy(), ref, "gate, scalar path")
+    ha = dev(h)
+    q2.engram_gate(ha, dev(kv), dev(qk), eps)
+    assert_close(ha.cpu().numpy(), ref, "gate, 16-byte path")
 
 
 def test_engram_gate_closed_forms():
