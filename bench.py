@@ -199,10 +199,17 @@ def bench_pair(torch, q2, syn, dev, copies_n: int = 512):
                              pc.k, m, ya=ya, yb=yb)
 
         def step(i):
+            # q8_1 + pair in one call (two launches at these sizes)
+            j = i % copies_n
+            q2.q8_1_q2k_mmvq_pair(wa[j * pa:(j + 1) * pa], pc.na, wb[j * pb:(j + 1) * pb], pc.nb, x,
+                                  pc.k, xq=xq, ya=ya, yb=yb)
+
+        def step_two_calls(i):
             q2.q8_1_rows(x, out=xq)
             prod(i)
 
         us_step = graph_us(torch, step, copies_n, reps=10, chunk=128)
+        us_step2 = graph_us(torch, step_two_calls, copies_n, reps=10, chunk=128)
         us_prod = graph_us(torch, prod, copies_n, reps=10, chunk=128)
         oq, od, _ = orc.q8_1_from_bf16_bits(pc.x_bits)
         ra, rb = orc.mmvq_pair(pc.wa, pc.wb, oq, od)
@@ -212,11 +219,13 @@ def bench_pair(torch, q2, syn, dev, copies_n: int = 512):
                 raise SystemExit(f"bench parity failed: attention pair m={m}")
         r = _roof(pa + pb + q2.q8_1_rows_bytes(m, pc.k) + 4 * m * (pc.na + pc.nb), us_prod)
         r["us_per_step"] = round(us_step, 3)
+        r["us_per_step_two_calls"] = round(us_step2, 3)
         r["tokens_per_s"] = round(m / us_step * 1e6, 1)
         out[f"m{m}"] = r
     out["workload"] = ("attention input pair: x bf16 [m, 4096] -> q8_1 once -> wq_a Q2_K "
                        "[1024, 4096] and wkv Q2_K [512, 4096] in one launch; 512 rotating copies "
-                       "(1.06 GB); step = q8_1 + pair, product = the pair launch alone")
+                       "(1.06 GB); step = q8_1 + pair (q8_1_q2k_mmvq_pair), product = the pair launch "
+                       "alone")
     return out
 
 

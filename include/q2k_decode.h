@@ -114,9 +114,10 @@ Q2K_API int32_t q2k_mmvq(const void* w_dev, const void* xq_dev, float* y_dev,
  * the same bits in y as the two calls (attn_v41/decode.rs and moe_v41/init.rs
  * quantise an input once and then run its products; here the quantisation
  * can live inside the product). For one token and rows of 1024..8192
- * values it is one launch: each workgroup quantises the bf16 row into LDS
- * while its first weight loads are in flight, and workgroup 0 writes the
- * q8_1 row to xq; otherwise a q8_1 launch runs ahead of the product.
+ * values (at least 2048 row steps) it is one launch: each workgroup
+ * quantises the bf16 row into LDS while its first weight loads are in
+ * flight, and workgroup 0 writes the q8_1 row to xq; otherwise a q8_1
+ * launch runs ahead of the product.
  *   w_dev, y_dev, n, k, m : as in q2k_mmvq (m in 1..8).
  *   x_bf16_dev, x_row_stride : as in q8_1_rows.
  *   xq_dev, xq_bytes : output, the q8_1 rows (q8_1_rows_bytes(m, k)),
@@ -133,6 +134,22 @@ Q2K_API int32_t q8_1_q2k_mmvq(const void* w_dev, const void* x_bf16_dev, int64_t
 Q2K_API int32_t q2k_mmvq_pair(const void* wa_dev, float* ya_dev, int32_t na,
                       const void* wb_dev, float* yb_dev, int32_t nb,
                       const void* xq_dev, int32_t k, int32_t m, void* stream);
+
+/* q8_1_rows and then q2k_mmvq_pair in one call (attn_v41/decode.rs
+ * q_kv_projections quantises the input once for wq_a and wkv), with the same
+ * bytes in xq and bits in ya, yb as the two calls. For one token where the
+ * pair takes the run kernel (at least 2048 row steps, rows of 1024..8192
+ * values) it is one launch, the quantisation inside the product as in
+ * q8_1_q2k_mmvq; otherwise a q8_1 launch runs ahead of the pair.
+ *   wa_dev .. nb, k, m : as in q2k_mmvq_pair.
+ *   x_bf16_dev, x_row_stride : bf16 [m, k] as in q8_1_rows.
+ *   xq_dev, xq_bytes : output, q8_1_rows_bytes(m, k) bytes, 16-byte aligned.
+ * Errors: those of q8_1_rows and q2k_mmvq_pair; xq may not overlap x or the
+ * matrices, nor an output overlap x. */
+Q2K_API int32_t q8_1_q2k_mmvq_pair(const void* wa_dev, float* ya_dev, int32_t na,
+                                   const void* wb_dev, float* yb_dev, int32_t nb,
+                                   const void* x_bf16_dev, int64_t x_row_stride, void* xq_dev,
+                                   size_t xq_bytes, int32_t k, int32_t m, void* stream);
 
 /* Expert-id batch (kquant_mmvq_q2_k_experts_w*, moe_v41/init.rs: gate and
  * up run as one batch of 2*ne matrices, up read at gate_out + ne*inter).

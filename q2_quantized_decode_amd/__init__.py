@@ -37,6 +37,8 @@ SIGNATURES = {
     "q2k_mmvq": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     "q8_1_q2k_mmvq": (_I32, [_VP, _VP, _I64, _VP, _SZ, _VP, _I32, _I32, _I32, _VP]),
     "q2k_mmvq_pair": (_I32, [_VP, _VP, _I32, _VP, _VP, _I32, _VP, _I32, _I32, _VP]),
+    "q8_1_q2k_mmvq_pair": (_I32, [_VP, _VP, _I32, _VP, _VP, _I32, _VP, _I64, _VP, _SZ, _I32, _I32,
+                                  _VP]),
     "q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP, _I32,
                                 _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP]),
     "q8_1_q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP, _I32,
@@ -179,6 +181,27 @@ def q2k_mmvq_pair(wa: torch.Tensor, na: int, wb: torch.Tensor, nb: int, xq: torc
         _contig(wa, "wa"), _contig(ya, "ya"), na, _contig(wb, "wb"), _contig(yb, "yb"), nb,
         _contig(xq, "xq"), k, m, _stream()))
     return ya, yb
+
+
+def q8_1_q2k_mmvq_pair(wa: torch.Tensor, na: int, wb: torch.Tensor, nb: int, x: torch.Tensor, k: int,
+                       xq: Optional[torch.Tensor] = None, ya: Optional[torch.Tensor] = None,
+                       yb: Optional[torch.Tensor] = None):
+    """q8_1 rows of bf16 x [m, k] into xq, then the pair on them in one call.
+    Returns (ya, yb, xq)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a bf16 [m, k] tensor with unit column stride")
+    m = x.shape[0]
+    need = q8_1_rows_bytes(m, k)
+    if xq is None:
+        xq = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if ya is None:
+        ya = torch.empty((m, na), dtype=torch.float32, device=wa.device)
+    if yb is None:
+        yb = torch.empty((m, nb), dtype=torch.float32, device=wb.device)
+    _check("q8_1_q2k_mmvq_pair", lib().q8_1_q2k_mmvq_pair(
+        _contig(wa, "wa"), _contig(ya, "ya"), na, _contig(wb, "wb"), _contig(yb, "yb"), nb,
+        _dev(x, "x"), x.stride(0), _contig(xq, "xq"), xq.numel(), k, m, _stream()))
+    return ya, yb, xq
 
 
 def q2k_mmvq_experts(bases: Sequence[torch.Tensor], expert_stride_bytes: int, n_experts: int,

@@ -186,10 +186,10 @@ int32_t q2k_mmq(const void* w_dev, const void* xq_dev, float* y_dev, int32_t n, 
   return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
 }
 
-int32_t q2k_mmvq_pair(const void* wa_dev, float* ya_dev, int32_t na, const void* wb_dev,
-                      float* yb_dev, int32_t nb, const void* xq_dev, int32_t k, int32_t m,
-                      void* stream) {
-  const char* fn = "q2k_mmvq_pair";
+// Checks of the pair forms and their launch description.
+static int32_t pair_launch(const char* fn, const void* wa_dev, float* ya_dev, int32_t na,
+                           const void* wb_dev, float* yb_dev, int32_t nb, const void* xq_dev,
+                           int32_t k, int32_t m, q2k::MmvqLaunch* out) {
   if (int32_t r = check_matrix(fn, "wa", wa_dev, na)) return r;
   if (int32_t r = check_matrix(fn, "wb", wb_dev, nb)) return r;
   if (int32_t r = check_out(fn, "ya", ya_dev)) return r;
@@ -218,6 +218,41 @@ int32_t q2k_mmvq_pair(const void* wa_dev, float* ya_dev, int32_t na, const void*
   a.xq = xq_dev;
   a.k = k;
   a.m = m;
+  *out = a;
+  return Q2K_OK;
+}
+
+int32_t q2k_mmvq_pair(const void* wa_dev, float* ya_dev, int32_t na, const void* wb_dev,
+                      float* yb_dev, int32_t nb, const void* xq_dev, int32_t k, int32_t m,
+                      void* stream) {
+  const char* fn = "q2k_mmvq_pair";
+  q2k::MmvqLaunch a;
+  if (int32_t r = pair_launch(fn, wa_dev, ya_dev, na, wb_dev, yb_dev, nb, xq_dev, k, m, &a)) return r;
+  return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
+}
+
+int32_t q8_1_q2k_mmvq_pair(const void* wa_dev, float* ya_dev, int32_t na, const void* wb_dev,
+                           float* yb_dev, int32_t nb, const void* x_bf16_dev, int64_t x_row_stride,
+                           void* xq_dev, size_t xq_bytes, int32_t k, int32_t m, void* stream) {
+  const char* fn = "q8_1_q2k_mmvq_pair";
+  q2k::MmvqLaunch a;
+  if (int32_t r = pair_launch(fn, wa_dev, ya_dev, na, wb_dev, yb_dev, nb, xq_dev, k, m, &a)) return r;
+  if (!x_bf16_dev) return fail(Q2K_EINVAL, "%s: x is null", fn);
+  if (x_row_stride < k) return fail(Q2K_ESHAPE, "%s: row stride %lld < k = %d", fn, (long long)x_row_stride, k);
+  if (!aligned(x_bf16_dev, 16) || x_row_stride % 8 != 0)
+    return fail(Q2K_EALIGN, "%s: x must be 16-byte aligned with a row stride that is a multiple of 8", fn);
+  const size_t need = q8_1_rows_bytes(m, k);
+  if (xq_bytes < need) return fail(Q2K_ESPACE, "%s: xq holds %zu bytes, %zu needed", fn, xq_bytes, need);
+  const size_t xbytes = ((size_t)(m - 1) * x_row_stride + k) * 2;
+  if (overlap(x_bf16_dev, xbytes, xq_dev, need) ||
+      overlap(xq_dev, need, wa_dev, q2k_matrix_bytes(na, k)) ||
+      overlap(xq_dev, need, wb_dev, q2k_matrix_bytes(nb, k)))
+    return fail(Q2K_EINVAL, "%s: xq overlaps an input", fn);
+  if (overlap(ya_dev, (size_t)m * na * 4, x_bf16_dev, xbytes) ||
+      overlap(yb_dev, (size_t)m * nb * 4, x_bf16_dev, xbytes))
+    return fail(Q2K_EINVAL, "%s: an output overlaps x", fn);
+  a.x_bf16 = x_bf16_dev;
+  a.x_stride = x_row_stride;
   return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
 }
 

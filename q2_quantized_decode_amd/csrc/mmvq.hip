@@ -1087,6 +1087,14 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   // fill the chip; smaller launches take one step per wave.
   const bool m1_path = a.dots == nullptr && !wide && gs_log2 >= 3 && tu.fast_m1 &&
                        total_iters * tsplit >= tu.m1_min_steps;
+  // A one-token launch that quantises its own input (one bf16 row shared by
+  // every matrix) does it in the run kernel's prologue when the product
+  // takes the run kernel anyway (so the bits are those of the separate
+  // calls). With tokens split over waves a workgroup would quantise four
+  // rows: measured slower than the separate q8_1 launch (attention pair,
+  // m = 4: 12.5 against 8.5 us), so those take the q8_1 launch.
+  const bool fuse_x = a.x_bf16 != nullptr && m1_path && tu.ring == 4 && a.groups == 0 &&
+                      a.m == 1 && (a.ids == nullptr || a.x_per_id == 0);
   const int64_t target_waves =
       (int64_t)cu_count() * (m1_path ? tu.m1_waves_per_cu : tu.waves_per_cu);
   int64_t chunk = (total_iters * tsplit + target_waves - 1) / target_waves;
@@ -1130,8 +1138,7 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (a.x_bf16 != nullptr) {
-    const bool shared_x = plain_launch(p) || (a.ids != nullptr && a.x_per_id == 0);
-    if (m1_path && a.m == 1 && !dots && shared_x && tu.ring == 4) {
+    if (fuse_x) {
       dispatch_m1_fused<1>(p, grid, a.x_bf16, static_cast<uint8_t*>(const_cast<void*>(a.xq)), stream);
       return hipGetLastError();
     }

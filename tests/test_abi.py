@@ -144,6 +144,24 @@ def test_fused_swiglu_experts_validation(L):
     assert f(*args(hq=IDS)) == EINVAL
 
 
+def test_fused_q8_1_pair_validation(L):
+    X, XQ, YA, YB = 0x10000000, 0x20000000, 0x30000000, 0x31000000
+    f = L.q8_1_q2k_mmvq_pair
+    args = lambda **kw: [P, kw.get("ya", YA), 1024, Q, kw.get("yb", YB), 512, kw.get("x", X),
+                         kw.get("xs", 4096), kw.get("xq", XQ), kw.get("xqb", 5120), kw.get("k", 4096),
+                         kw.get("m", 1), None]
+    assert f(*args(x=None)) == EINVAL
+    assert f(*args(xq=None)) == EINVAL
+    assert f(*args(k=4000, xs=4000)) == ESHAPE
+    assert f(*args(m=9)) == ESHAPE
+    assert f(*args(xs=2048)) == ESHAPE
+    assert f(*args(x=X + 8)) == EALIGN
+    assert f(*args(xqb=5119)) == ESPACE
+    assert f(*args(xq=X + 16)) == EINVAL      # xq inside x
+    assert f(*args(ya=X)) == EINVAL           # an output over x
+    assert f(*args(yb=YA + 4)) == EINVAL      # ya and yb overlap
+
+
 def test_mmvq_validation(L):
     assert L.q2k_mmvq(None, Q, P, 256, 1024, 1, None) == EINVAL
     assert L.q2k_mmvq(P, Q, 0x100, 256, 1000, 1, None) == ESHAPE

@@ -303,6 +303,26 @@ def test_mfma_pair(matrix_cores):
     assert_close(yb.cpu().numpy()[:, _sample_rows(pc.nb, 2)], rb, "mfma pair b")
 
 
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+def test_fused_q8_1_pair_equals_two_calls(m):
+    """q8_1_q2k_mmvq_pair on the attention pair shapes gives the xq bytes and
+    output bits of q8_1_rows + q2k_mmvq_pair."""
+    pc = syn.attention_pair_case(m)
+    wa, wb = dev(pc.wa.reshape(-1)), dev(pc.wb.reshape(-1))
+    x = bf16_dev(pc.x_bits)
+    ya, yb, xq = q2.q8_1_q2k_mmvq_pair(wa, pc.na, wb, pc.nb, x, pc.k)
+    xq2 = q2.q8_1_rows(x)
+    ya2, yb2 = q2.q2k_mmvq_pair(wa, pc.na, wb, pc.nb, xq2, pc.k, m)
+    need = q2.q8_1_rows_bytes(m, pc.k)
+    assert torch.equal(xq[:need], xq2[:need])
+    assert torch.equal(ya.view(torch.int32), ya2.view(torch.int32))
+    assert torch.equal(yb.view(torch.int32), yb2.view(torch.int32))
+    oq, od = assert_q8_equal(xq, pc.x_bits)
+    ra, rb = orc.mmvq_pair(pc.wa, pc.wb, oq, od)
+    assert_close(ya.cpu().numpy(), ra, f"fused pair a m={m}")
+    assert_close(yb.cpu().numpy(), rb, f"fused pair b m={m}")
+
+
 def test_pair_token_split_and_matrix_cores_agree():
     """The pair at m = 8 through the packed-dot kernel (tokens split over
     waves) and through the matrix cores: both within the tolerance of the
@@ -336,14 +356,15 @@ def test_token_split(n, k, m, packed_dots):
 
 
 @pytest.mark.parametrize("n,k,m", [(20480, 2048, 1), (16384, 1024, 1), (8192, 4096, 1),
-                                   (4099, 8192, 1), (4096, 1024, 1), (300, 4096, 1),
-                                   (1000, 2048, 3), (8197, 7168, 8)])
+                                   (4099, 8192, 1), (4103, 2048, 4), (2050, 4096, 5),
+                                   (4099, 7168, 3), (513, 8192, 8),
+                                   (4096, 1024, 1), (300, 4096, 1), (1000, 2048, 3), (8197, 7168, 8)])
 def test_fused_q8_1_equals_two_calls(n, k, m):
     """q8_1_q2k_mmvq gives the bytes of q8_1_rows and the bits of q2k_mmvq on
-    them. The first four shapes run as one launch (quantisation in the
-    product's prologue; k = 8192 has 256 blocks, one per thread), the others
-    as a q8_1 launch ahead of the product (too few row steps for the run
-    kernel, m > 1). Rows are strided on the input for m > 1."""
+    them. The first four shapes run as one launch (one token; k = 8192 has
+    256 blocks, one per thread); the others take a q8_1 launch ahead of the
+    product (tokens split over waves, too few row steps for the run kernel,
+    the matrix cores). Rows are strided on the input for m > 1."""
     case = syn.single_gemv_case(n=n, k=k, m=m, seed=7600 + n + k + m)
     w = dev(case.w.reshape(-1))
     if m == 1:
