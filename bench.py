@@ -458,6 +458,13 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
     q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks, 0)
 
     def step(i):
+        # hash (hashed layer 1) + gather + dequant + q8_1 in one launch
+        q2.engram_rows_q8_1(tm, mu, pr, of, hc.pad_id, cache, toks[i % 64:i % 64 + 1], 4096 + (i % 64), 1,
+                            table, 500000, xq=xq)
+        q2.q2k_mmvq(copies[i % copies_n], xq, n_out, 2048, 1, out=kv)
+        q2.engram_gate(h, kv, qk, e.eps)
+
+    def step_hash_apart(i):
         q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks[i % 64:i % 64 + 1], 4096 + (i % 64), out=ids)
         q2.q2k_dequant_rows_q8_1(table, 500000, ids[1].reshape(-1), 8, xq=xq)
         q2.q2k_mmvq(copies[i % copies_n], xq, n_out, 2048, 1, out=kv)
@@ -504,6 +511,7 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
         q2.engram_gate(h, kv, qk, e.eps)
 
     us_step = timed(step, copies_n)
+    us_step_hash_apart = timed(step_hash_apart, copies_n)
     us_step_unfused = timed(step_unfused, copies_n)
     us_step_bf16 = timed(step_bf16, copies_n)
     us_gemv = timed(lambda i: q2.q2k_gemv_bf16(copies[i % copies_n], rows.view(1, 2048), n_out, 2048,
@@ -514,11 +522,13 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
     pre = torch.empty((2, 4096, 8), dtype=torch.int64, device=dev)
     us_pre = timed(lambda i: q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks, 0, out=pre), 16)
     wkv_bytes = w0.numel()
-    return {"workload": "engram step, one token: hash -> 8-row gather + dequant + q8_1 (one "
-                        "launch) -> wkv Q2_K [20480, 2048] -> gate [1, 4, 4096]; 80 rotating wkv "
-                        "copies. The unfused step gathers and quantises in two launches; the "
-                        "bf16 route skips q8_1: gathered bf16 rows straight into the wkv product",
+    return {"workload": "engram step, one token: hash + 8-row gather + dequant + q8_1 (one "
+                        "launch, engram_rows_q8_1) -> wkv Q2_K [20480, 2048] -> gate [1, 4, 4096]; "
+                        "80 rotating wkv copies. hash_apart: the hash as its own launch; unfused: "
+                        "hash, gather and q8_1 as three launches; the bf16 route skips q8_1: "
+                        "gathered bf16 rows straight into the wkv product",
             "us_per_step": round(us_step, 3), "tokens_per_s": round(1e6 / us_step, 1),
+            "us_per_step_hash_apart": round(us_step_hash_apart, 3),
             "us_per_step_unfused": round(us_step_unfused, 3),
             "us_per_step_bf16_route": round(us_step_bf16, 3),
             "wkv_bytes": wkv_bytes,

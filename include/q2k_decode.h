@@ -354,6 +354,31 @@ Q2K_API int32_t engram_hash(const int64_t* token_map_dev, int64_t vocab,
                          const int32_t* ids_dev, int32_t seqlen, int64_t start_pos,
                          int64_t* out_dev, int32_t* err_flag_dev, void* stream);
 
+/* One decode token through the engram row path in one launch: engram_hash
+ * for this token (position pos, ids = token_dev[0]) restricted to hashed
+ * layer `layer`, then q2k_dequant_rows_q8_1 of that layer's row ids
+ * (engram_v41.rs EngramHasher::hash / layer_row_ids, then
+ * EngramV41::rows_from_q2k and the projection's q8_1 input). The same ids,
+ * cache update (cache[pos] = the token's compressed id), rows, q8_1 bytes
+ * and error flag as those two calls.
+ *   token_map_dev .. cache_len : as in engram_hash.
+ *   token_dev : int32 [1], the token at position pos (0 <= pos < cache_len).
+ *   layer : the hashed layer whose row ids are gathered, 0..n_layers-1.
+ *   table_dev, n_table_rows : as in q2k_dequant_rows_q8_1.
+ *   ids_out_dev : nullable int64 [cols] (cols = (max_ngram-1)*n_heads <= 32).
+ *   rows_out_dev : nullable bf16 [cols, 256], 16-byte aligned.
+ *   xq_dev, xq_bytes : output, q8_1_rows_bytes(1, 256*cols), 16-byte aligned.
+ * Errors: those of the two calls; cols > 32 is Q2K_ESHAPE; the outputs may
+ * not overlap each other, the cache or an input. */
+Q2K_API int32_t engram_rows_q8_1(const int64_t* token_map_dev, int64_t vocab,
+                                 const int64_t* multipliers_dev, const int64_t* primes_dev,
+                                 const int64_t* offsets_dev, int32_t n_layers, int32_t max_ngram,
+                                 int32_t n_heads, int64_t pad_id, int64_t* cache_dev,
+                                 int64_t cache_len, const int32_t* token_dev, int64_t pos,
+                                 int32_t layer, const void* table_dev, int64_t n_table_rows,
+                                 int64_t* ids_out_dev, void* rows_out_dev, void* xq_dev,
+                                 size_t xq_bytes, int32_t* err_flag_dev, void* stream);
+
 /* Which kernel runs the Q2_K x q8_1 products (q2k_mmvq, its pair, expert
  * and grouped forms, and q2k_mmq), process-wide. For tests and tuning only:
  * every kernel forms the same exact int32 block sums and an fp64 epilogue,

@@ -52,6 +52,8 @@ SIGNATURES = {
     "q2k_dequant_rows": (_I32, [_VP, _I64, _VP, _I32, _VP, _VP, _VP]),
     "q2k_dequant_rows_q8_1": (_I32, [_VP, _I64, _VP, _I32, _VP, _VP, _SZ, _VP, _VP]),
     "engram_gate": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _F32, _VP]),
+    "engram_rows_q8_1": (_I32, [_VP, _I64, _VP, _VP, _VP, _I32, _I32, _I32, _I64, _VP, _I64, _VP, _I64,
+                                _I32, _VP, _I64, _VP, _VP, _VP, _SZ, _VP, _VP]),
     "q2k_block_dots": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     "engram_hash": (_I32, [_VP, _I64, _VP, _VP, _VP, _I32, _I32, _I32, _I64, _VP, _I64, _VP, _I32,
                            _I64, _VP, _VP, _VP]),
@@ -410,6 +412,37 @@ def engram_hash(token_map: torch.Tensor, multipliers: torch.Tensor, primes: torc
         pad_id, _contig(cache, "cache"), cache.numel(), _contig(ids, "ids"), seqlen, start_pos,
         _contig(out, "out"), flag or None, _stream()))
     return out
+
+
+def engram_rows_q8_1(token_map: torch.Tensor, multipliers: torch.Tensor, primes: torch.Tensor,
+                     offsets: torch.Tensor, pad_id: int, cache: torch.Tensor, token: torch.Tensor,
+                     pos: int, layer: int, table: torch.Tensor, n_table_rows: int,
+                     xq: Optional[torch.Tensor] = None, ids_out: Optional[torch.Tensor] = None,
+                     rows_out: Optional[torch.Tensor] = None,
+                     err_flag: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode token (int32 ``token`` [1] at position ``pos``): hashed layer
+    ``layer``'s row ids, their gather and dequantisation, and q8_1 of the rows
+    viewed as one row, in one launch. Returns xq."""
+    for name, t in (("token_map", token_map), ("multipliers", multipliers), ("primes", primes),
+                    ("offsets", offsets), ("cache", cache)):
+        if t.dtype != torch.int64:
+            raise ValueError(f"{name} must be int64")
+    if token.dtype != torch.int32:
+        raise ValueError("token must be int32")
+    n_layers, max_ngram = multipliers.shape
+    n_heads = primes.shape[-1]
+    cols = (max_ngram - 1) * n_heads
+    need = q8_1_rows_bytes(1, cols * BLOCK_WEIGHTS)
+    if xq is None:
+        xq = torch.empty(max(need, 16), dtype=torch.uint8, device=table.device)
+    opt = lambda t, n: _contig(t, n) if t is not None else None
+    _check("engram_rows_q8_1", lib().engram_rows_q8_1(
+        _contig(token_map, "token_map"), token_map.numel(), _contig(multipliers, "multipliers"),
+        _contig(primes, "primes"), _contig(offsets, "offsets"), n_layers, max_ngram, n_heads, pad_id,
+        _contig(cache, "cache"), cache.numel(), _contig(token, "token"), pos, layer,
+        _contig(table, "table"), n_table_rows, opt(ids_out, "ids_out"), opt(rows_out, "rows_out"),
+        _contig(xq, "xq"), xq.numel(), opt(err_flag, "err_flag"), _stream()))
+    return xq
 
 
 def q2k_block_dots(w: torch.Tensor, xq: torch.Tensor, n: int, k: int, m: int,

@@ -468,6 +468,58 @@ int32_t q2k_dequant_rows(const void* table_dev, int64_t n_table_rows, const int6
                                            err_flag_dev, (hipStream_t)stream), fn);
 }
 
+int32_t engram_rows_q8_1(const int64_t* token_map_dev, int64_t vocab, const int64_t* multipliers_dev,
+                         const int64_t* primes_dev, const int64_t* offsets_dev, int32_t n_layers,
+                         int32_t max_ngram, int32_t n_heads, int64_t pad_id, int64_t* cache_dev,
+                         int64_t cache_len, const int32_t* token_dev, int64_t pos, int32_t layer,
+                         const void* table_dev, int64_t n_table_rows, int64_t* ids_out_dev,
+                         void* rows_out_dev, void* xq_dev, size_t xq_bytes, int32_t* err_flag_dev,
+                         void* stream) {
+  const char* fn = "engram_rows_q8_1";
+  if (!token_map_dev || !multipliers_dev || !primes_dev || !offsets_dev || !cache_dev || !token_dev ||
+      !table_dev || !xq_dev)
+    return fail(Q2K_EINVAL, "%s: null pointer", fn);
+  if (vocab < 1) return fail(Q2K_ESHAPE, "%s: vocab = %lld < 1", fn, (long long)vocab);
+  if (n_layers < 1 || n_layers > 64) return fail(Q2K_ESHAPE, "%s: n_layers = %d outside 1..64", fn, n_layers);
+  if (max_ngram < 2 || max_ngram > 8) return fail(Q2K_ESHAPE, "%s: max_ngram = %d outside 2..8", fn, max_ngram);
+  if (n_heads < 1 || n_heads > 64) return fail(Q2K_ESHAPE, "%s: n_heads = %d outside 1..64", fn, n_heads);
+  if (layer < 0 || layer >= n_layers) return fail(Q2K_ESHAPE, "%s: layer = %d outside 0..%d", fn, layer, n_layers - 1);
+  const int32_t cols = (max_ngram - 1) * n_heads;
+  if (cols > 32) return fail(Q2K_ESHAPE, "%s: %d row ids per token, at most 32 (one workgroup)", fn, cols);
+  if (pos < 0 || cache_len < pos + 1)
+    return fail(Q2K_ESHAPE, "%s: position %lld outside the cache of %lld", fn, (long long)pos, (long long)cache_len);
+  if (n_table_rows < 1) return fail(Q2K_ESHAPE, "%s: empty table", fn);
+  if (!aligned(token_map_dev, 8) || !aligned(multipliers_dev, 8) || !aligned(primes_dev, 8) ||
+      !aligned(offsets_dev, 8) || !aligned(cache_dev, 8) || !aligned(token_dev, 4) ||
+      (ids_out_dev && !aligned(ids_out_dev, 8)) || !aligned(table_dev, 4) || !aligned(xq_dev, 16) ||
+      (rows_out_dev && !aligned(rows_out_dev, 16)))
+    return fail(Q2K_EALIGN, "%s: 64-bit arrays 8-byte, token and table 4-byte, rows and xq 16-byte aligned", fn);
+  const int32_t k = cols * 256;
+  const size_t need = q8_1_rows_bytes(1, k);
+  if (xq_bytes < need) return fail(Q2K_ESPACE, "%s: xq holds %zu bytes, %zu needed", fn, xq_bytes, need);
+  const size_t cache_bytes = (size_t)cache_len * 8, tb = (size_t)n_table_rows * 84, ob = (size_t)k * 2;
+  const size_t ib = (size_t)cols * 8, vb = (size_t)vocab * 8;
+  const void* outs[3] = {xq_dev, rows_out_dev, ids_out_dev};
+  const size_t out_b[3] = {need, ob, ib};
+  for (int a = 0; a < 3; ++a) {
+    if (!outs[a]) continue;
+    if (overlap(outs[a], out_b[a], cache_dev, cache_bytes) || overlap(outs[a], out_b[a], table_dev, tb) ||
+        overlap(outs[a], out_b[a], token_map_dev, vb) || overlap(outs[a], out_b[a], token_dev, 4))
+      return fail(Q2K_EINVAL, "%s: an output overlaps an input or the cache", fn);
+    for (int b = a + 1; b < 3; ++b)
+      if (outs[b] && overlap(outs[a], out_b[a], outs[b], out_b[b]))
+        return fail(Q2K_EINVAL, "%s: two outputs overlap", fn);
+  }
+  if (overlap(cache_dev, cache_bytes, token_map_dev, vb) || overlap(cache_dev, cache_bytes, token_dev, 4) ||
+      overlap(cache_dev, cache_bytes, table_dev, tb))
+    return fail(Q2K_EINVAL, "%s: the cache overlaps an input", fn);
+  return launched(q2k::launch_engram_rows_q8_1(token_map_dev, vocab, multipliers_dev, primes_dev,
+                                               offsets_dev, layer, max_ngram, n_heads, pad_id, cache_dev,
+                                               token_dev, pos, table_dev, n_table_rows, ids_out_dev,
+                                               rows_out_dev, xq_dev, err_flag_dev, (hipStream_t)stream),
+                  fn);
+}
+
 int32_t q2k_dequant_rows_q8_1(const void* table_dev, int64_t n_table_rows, const int64_t* ids_dev,
                               int32_t n_rows, void* out_bf16_dev, void* xq_dev, size_t xq_bytes,
                               int32_t* err_flag_dev, void* stream) {

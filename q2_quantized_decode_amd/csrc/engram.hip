@@ -153,20 +153,17 @@ __global__ __launch_bounds__(256) void engram_gate_vec_kernel(float* __restrict_
 // whose window reads it, -1 in the cache, and *err_flag = 1.
 constexpr int kMaxNgram = 8;
 
-__global__ __launch_bounds__(256) void engram_hash_kernel(
-    const int64_t* __restrict__ token_map, int64_t vocab, const int64_t* __restrict__ mult,
-    const int64_t* __restrict__ primes, const int64_t* __restrict__ offsets, int n_layers, int ng,
-    int n_heads, int64_t pad_id, int64_t* cache, const int32_t* __restrict__ ids, int seqlen,
-    int64_t start_pos, int64_t* __restrict__ out, int32_t* err_flag) {
-  const int tid = blockIdx.x * blockDim.x + threadIdx.x;
-  if (tid >= seqlen * n_layers) return;
-  const int s = tid / n_layers;
-  const int l = tid - s * n_layers;
-  const int64_t pos = start_pos + s;
-  const int cols = (ng - 1) * n_heads;
-  bool ok = true;
-  int64_t tok[kMaxNgram];
+// Window of position pos = start_pos + s for the hash: tok[0..ng-1] and
+// whether every token id it reads is valid. Position p >= start_pos reads
+// this call's ids, earlier positions the cache; from the first i with
+// pos < i or an unmapped (-1) id on, the token is pad_id. Returns the
+// compressed id of pos itself (what the cache keeps for it).
+__device__ __forceinline__ int64_t hash_window(const int64_t* __restrict__ token_map, int64_t vocab,
+                                               int ng, int64_t pad_id, const int64_t* cache,
+                                               const int32_t* __restrict__ ids, int64_t start_pos,
+                                               int64_t pos, int64_t tok[kMaxNgram], bool& ok) {
   bool blocked = false;
+  int64_t own = -1;
   for (int i = 0; i < ng; ++i) {
     const int64_t p = pos >= i ? pos - i : 0;
     int64_t src;
@@ -181,13 +178,25 @@ __global__ __launch_bounds__(256) void engram_hash_kernel(
     } else {
       src = cache[p];
     }
-    if (i == 0 && l == 0) cache[pos] = src;
+    if (i == 0) own = src;
     blocked = blocked || pos < i || src == -1;
     tok[i] = blocked ? pad_id : src;
   }
+  return own;
+}
+
+// Row ids of hashed layer l for a window: rolling = tok[0]*mult[l][0], then
+// rolling ^= tok[i]*mult[l][i] (64-bit wrapping); id (i, h) = (rolling mod
+// prime, in [0, prime)) + offset; -1 once the window is bad or a prime <= 0
+// has been met (in (i, h) order). Writes o[c] for c in [c0, c1) and returns
+// false when any id so far is -1.
+__device__ __forceinline__ bool hash_cols(const int64_t tok[kMaxNgram], const int64_t* __restrict__ mult,
+                                          const int64_t* __restrict__ primes,
+                                          const int64_t* __restrict__ offsets, int l, int ng,
+                                          int n_heads, bool ok, int c0, int c1, int64_t* o) {
+  const int cols = (ng - 1) * n_heads;
   const int64_t* ml = mult + (int64_t)l * ng;
   uint64_t rolling = (uint64_t)tok[0] * (uint64_t)ml[0];
-  int64_t* o = out + ((int64_t)l * seqlen + s) * cols;
   for (int i = 1; i < ng; ++i) {
     rolling ^= (uint64_t)tok[i] * (uint64_t)ml[i];
     for (int h = 0; h < n_heads; ++h) {
@@ -201,10 +210,102 @@ __global__ __launch_bounds__(256) void engram_hash_kernel(
       } else {
         ok = false;
       }
-      o[col] = v;
+      if (col >= c0 && col < c1) o[col - c0] = v;
     }
+    if (i * n_heads >= c1) break;   // later columns are not asked for
   }
+  return ok;
+}
+
+__global__ __launch_bounds__(256) void engram_hash_kernel(
+    const int64_t* __restrict__ token_map, int64_t vocab, const int64_t* __restrict__ mult,
+    const int64_t* __restrict__ primes, const int64_t* __restrict__ offsets, int n_layers, int ng,
+    int n_heads, int64_t pad_id, int64_t* cache, const int32_t* __restrict__ ids, int seqlen,
+    int64_t start_pos, int64_t* __restrict__ out, int32_t* err_flag) {
+  const int tid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= seqlen * n_layers) return;
+  const int s = tid / n_layers;
+  const int l = tid - s * n_layers;
+  const int64_t pos = start_pos + s;
+  const int cols = (ng - 1) * n_heads;
+  bool ok = true;
+  int64_t tok[kMaxNgram];
+  const int64_t own = hash_window(token_map, vocab, ng, pad_id, cache, ids, start_pos, pos, tok, ok);
+  if (l == 0) cache[pos] = own;
+  int64_t* o = out + ((int64_t)l * seqlen + s) * cols;
+  ok = hash_cols(tok, mult, primes, offsets, l, ng, n_heads, ok, 0, cols, o);
   if (!ok && err_flag != nullptr) *err_flag = 1;
+}
+
+// One decode token, one hashed layer, in one workgroup: the layer's row ids
+// (thread c computes column c with hash_window and hash_cols, as the hash
+// kernel would for that position and layer; thread 0 also stores the
+// position's compressed id into the cache), then the gather, dequantisation
+// and q8_1 of those rows viewed as one row, as dequant_rows_q8_1_kernel does
+// (8 values per thread and pass). cols <= 32 (rows of up to 8192 values).
+__global__ __launch_bounds__(256) void engram_rows_q8_1_kernel(
+    const int64_t* __restrict__ token_map, int64_t vocab, const int64_t* __restrict__ mult,
+    const int64_t* __restrict__ primes, const int64_t* __restrict__ offsets, int layer, int ng,
+    int n_heads, int64_t pad_id, int64_t* cache, const int32_t* __restrict__ token, int64_t pos,
+    const uint8_t* __restrict__ table, int64_t n_table_rows, int64_t* __restrict__ ids_out,
+    uint16_t* __restrict__ rows_out, uint8_t* __restrict__ xq, int32_t* err_flag) {
+  __shared__ int64_t rid[32];
+  const int cols = (ng - 1) * n_heads;
+  const int tid = threadIdx.x;
+  if (tid < cols) {
+    bool ok = true;
+    int64_t tok[kMaxNgram];
+    const int64_t own = hash_window(token_map, vocab, ng, pad_id, cache, token, pos, pos, tok, ok);
+    if (tid == 0) cache[pos] = own;
+    int64_t v;
+    ok = hash_cols(tok, mult, primes, offsets, layer, ng, n_heads, ok, tid, tid + 1, &v);
+    rid[tid] = v;
+    if (ids_out != nullptr) ids_out[tid] = v;
+    if (!ok && err_flag != nullptr) *err_flag = 1;
+  }
+  __syncthreads();
+  const int k = cols * kBlockWeights;
+  for (int c0 = 0; c0 < k / 8; c0 += 256) {
+    const int chunk = c0 + tid;
+    const bool active = chunk < k / 8;
+    const int e0 = active ? chunk * 8 : 0;
+    const int row = e0 / kBlockWeights, e = e0 % kBlockWeights;
+    const int64_t id = rid[row];
+    const bool bad = id < 0 || id >= n_table_rows;
+    uint32_t bits[8];
+    if (bad) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bits[i] = 0x7fc0u;
+      if (active && e == 0 && err_flag != nullptr) *err_flag = 1;
+    } else {
+      const uint8_t* blk = table + id * kBlockBytes;
+      q2k_dequant4(blk, e, bits);
+      q2k_dequant4(blk, e + 4, bits + 4);
+    }
+    if (active && rows_out != nullptr) {
+      u32x4 packed;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed[i] = bits[2 * i] | (bits[2 * i + 1] << 16);
+      *reinterpret_cast<u32x4*>(rows_out + e0) = packed;
+    }
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = bf16_bits_to_f32(bits[i]);
+    q8_1_store8(v, xq, e0, k, active);
+  }
+}
+
+hipError_t launch_engram_rows_q8_1(const int64_t* token_map, int64_t vocab, const int64_t* mult,
+                                   const int64_t* primes, const int64_t* offsets, int layer, int ng,
+                                   int n_heads, int64_t pad_id, int64_t* cache, const int32_t* token,
+                                   int64_t pos, const void* table, int64_t n_table_rows,
+                                   int64_t* ids_out, void* rows_out, void* xq, int32_t* err_flag,
+                                   hipStream_t stream) {
+  hipLaunchKernelGGL(engram_rows_q8_1_kernel, dim3(1), dim3(256), 0, stream, token_map, vocab, mult,
+                     primes, offsets, layer, ng, n_heads, pad_id, cache, token, pos,
+                     static_cast<const uint8_t*>(table), n_table_rows, ids_out,
+                     static_cast<uint16_t*>(rows_out), static_cast<uint8_t*>(xq), err_flag);
+  return hipGetLastError();
 }
 
 hipError_t launch_engram_hash(const int64_t* token_map, int64_t vocab, const int64_t* mult,

@@ -78,6 +78,14 @@ hipError_t launch_dequant_rows_q8_1(const void* table, int64_t n_table_rows, con
                                     hipStream_t stream);
 hipError_t launch_engram_gate(float* h, const float* kv, const float* qk, int t, int hc, int dim,
                               float eps, hipStream_t stream);
+// One decode token: hashed layer `layer`'s row ids, then their gather,
+// dequantisation and q8_1 as one row (one workgroup).
+hipError_t launch_engram_rows_q8_1(const int64_t* token_map, int64_t vocab, const int64_t* mult,
+                                   const int64_t* primes, const int64_t* offsets, int layer, int ng,
+                                   int n_heads, int64_t pad_id, int64_t* cache, const int32_t* token,
+                                   int64_t pos, const void* table, int64_t n_table_rows,
+                                   int64_t* ids_out, void* rows_out, void* xq, int32_t* err_flag,
+                                   hipStream_t stream);
 hipError_t launch_engram_hash(const int64_t* token_map, int64_t vocab, const int64_t* mult,
                               const int64_t* primes, const int64_t* offsets, int n_layers, int ng,
                               int n_heads, int64_t pad_id, int64_t* cache, const int32_t* ids,

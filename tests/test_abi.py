@@ -162,6 +162,29 @@ def test_fused_q8_1_pair_validation(L):
     assert f(*args(yb=YA + 4)) == EINVAL      # ya and yb overlap
 
 
+def test_engram_rows_q8_1_validation(L):
+    TM, MU, PR, OF, C, T, TB, XQ = (0x10000000 + 0x1000000 * i for i in range(8))
+    f = L.engram_rows_q8_1
+    args = lambda **kw: [kw.get("tm", TM), 4096, MU, PR, OF, kw.get("nl", 2), kw.get("ng", 3),
+                         kw.get("nh", 4), 0, kw.get("c", C), kw.get("cl", 64), kw.get("t", T),
+                         kw.get("pos", 10), kw.get("layer", 1), kw.get("tb", TB), 500000,
+                         kw.get("ids", None), kw.get("rows", None), kw.get("xq", XQ),
+                         kw.get("xqb", 2560), None, None]
+    assert f(*args(tm=None)) == EINVAL
+    assert f(*args(t=None)) == EINVAL
+    assert f(*args(xq=None)) == EINVAL
+    assert f(*args(layer=2)) == ESHAPE
+    assert f(*args(nh=17)) == ESHAPE                 # 2 * 17 = 34 row ids > 32
+    assert f(*args(pos=64)) == ESHAPE
+    assert f(*args(ng=9)) == ESHAPE
+    assert f(*args(c=C + 4)) == EALIGN
+    assert f(*args(xq=XQ + 8)) == EALIGN
+    assert f(*args(xqb=2559)) == ESPACE
+    assert f(*args(xq=C + 64)) == EINVAL             # xq inside the cache
+    assert f(*args(rows=XQ + 16)) == EINVAL          # rows over xq
+    assert f(*args(ids=TB)) == EINVAL                # ids over the table
+
+
 def test_mmvq_validation(L):
     assert L.q2k_mmvq(None, Q, P, 256, 1024, 1, None) == EINVAL
     assert L.q2k_mmvq(P, Q, 0x100, 256, 1000, 1, None) == ESHAPE

@@ -944,6 +944,64 @@ def test_engram_hashed_rows_gather():
     assert int(flag.item()) == 0
 
 
+def _engram_rows_both_ways(hc, table_np, tokens, start, layer, n_table_rows, bad_prime=False):
+    """Decode tokens one at a time through engram_rows_q8_1 and through
+    engram_hash + q2k_dequant_rows_q8_1 with separate caches; every id, row,
+    q8_1 byte, cache entry and flag must agree."""
+    tm, mu, pr, of = _hash_tables_dev(hc)
+    if bad_prime:
+        pr.view(-1)[3] = 0
+    table = dev(table_np.reshape(-1))
+    cols = (mu.shape[1] - 1) * pr.shape[-1]
+    c1 = torch.zeros(len(tokens) + start + 8, dtype=torch.int64, device="cuda")
+    c2 = c1.clone()
+    # a prefill through the plain hash gives both caches the same history
+    if start > 0:
+        pre = dev(hc.tokens[:start].astype(np.int32))
+        q2.engram_hash(tm, mu, pr, of, hc.pad_id, c1, pre, 0)
+        q2.engram_hash(tm, mu, pr, of, hc.pad_id, c2, pre, 0)
+    need = q2.q8_1_rows_bytes(1, cols * 256)
+    for s, t in enumerate(tokens):
+        pos = start + s
+        tok = dev(np.array([t], dtype=np.int32))
+        f1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        f2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ids1 = torch.empty(cols, dtype=torch.int64, device="cuda")
+        rows1 = torch.empty((cols, 256), dtype=torch.bfloat16, device="cuda")
+        xq1 = q2.engram_rows_q8_1(tm, mu, pr, of, hc.pad_id, c1, tok, pos, layer, table, n_table_rows,
+                                  ids_out=ids1, rows_out=rows1, err_flag=f1)
+        ids2 = q2.engram_hash(tm, mu, pr, of, hc.pad_id, c2, tok, pos, err_flag=f2)[layer].reshape(-1)
+        xq2, rows2 = q2.q2k_dequant_rows_q8_1(table, n_table_rows, ids2, cols, want_rows=True, err_flag=f2)
+        assert torch.equal(ids1, ids2), f"ids, position {pos}"
+        assert torch.equal(rows1.view(torch.int16), rows2.view(torch.int16)), f"rows, position {pos}"
+        assert torch.equal(xq1[:need], xq2[:need]), f"q8_1, position {pos}"
+        assert int(f1.item()) == int(f2.item()), f"flag, position {pos}"
+    assert torch.equal(c1, c2)
+
+
+def test_engram_rows_q8_1_is_the_composition():
+    """One launch for hash (one layer) + gather + dequant + q8_1 of a decode
+    token: the bits of engram_hash then q2k_dequant_rows_q8_1, after a
+    prefill, for both hashed layers."""
+    hc = syn.engram_hash_case(seqlen=48)
+    table = syn.q2k_blocks(syn.rng_for(1001, 8), 500000, 1)
+    for layer in (0, 1):
+        _engram_rows_both_ways(hc, table, hc.tokens[32:48].tolist(), 32, layer, 500000)
+
+
+def test_engram_rows_q8_1_bad_token_prime_and_wide():
+    """A token outside the map (every id -1: NaN rows, flag), a zero prime
+    (ids -1 from its column on), and 16 heads x 2 (32 rows, 8192 values)."""
+    hc = syn.engram_hash_case(seed=9, seqlen=20)
+    table = syn.q2k_blocks(syn.rng_for(1001, 9), 500000, 1)
+    toks = hc.tokens[10:14].tolist()
+    toks[1] = len(hc.token_map) + 5
+    _engram_rows_both_ways(hc, table, toks, 10, 1, 500000)
+    _engram_rows_both_ways(hc, table, hc.tokens[10:13].tolist(), 10, 0, 500000, bad_prime=True)
+    wide = syn.engram_hash_case(seed=10, vocab=512, n_layers=2, max_ngram=3, n_heads=16, seqlen=12)
+    _engram_rows_both_ways(wide, table, wide.tokens[4:12].tolist(), 4, 1, 500000)
+
+
 # ------------------------------------------------------- m > 8 (MMQ) ------
 
 @pytest.mark.parametrize("n,k,m", [(300, 1024, 9), (1000, 2048, 16), (130, 7168, 33), (257, 4096, 64),
