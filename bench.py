@@ -15,11 +15,11 @@ Method:
 * Inputs are resident in HBM before timing. The weights are replicated 16
   times (1.23 GB, over four times the 256 MB Infinity Cache) and step i reads
   copy i % 16, so every step streams its matrix from HBM.
-* The steps are captured once into a HIP graph (16 steps, one per copy) and
+* The steps are captured once into a HIP graph (256 steps, copy i % 16) and
   the graph is replayed; W warm-up steps, then K timed steps between two
   device synchronisations (wall clock).
 * Roofline of the dominant kernel (q2k_mmvq): a second graph holds only the
-  16 products; HIP events on the launching stream bracket its replays, and
+  256 products; HIP events on the launching stream bracket its replays, and
   achieved = algorithmic bytes per launch / average launch time.
 * CPU baseline: the CPU oracle timed on a bounded sample of rows of the
   same matrix and token (about twelve seconds of host work).
@@ -46,6 +46,11 @@ METRIC = "Q2_K mmvq achieved HBM GB/s (% of peak) at m=1 and m=8, 1x MI355X"
 PEAK_GBS = 8000.0          # MI355X HBM3E
 N, K = 32768, 7168
 COPIES = 16
+# Launches per captured HIP graph (copies rotate i % COPIES inside it). Each
+# graph replay costs a few microseconds of its own; a decode step captured as
+# a graph holds hundreds of kernels, so the graphs here hold 256 launches
+# (with 16 the replay overhead added ~0.4 us to every 15 us launch).
+GRAPH = 256
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_large_verify_traffic.json")
 CSRC = os.path.join(ROOT, "q2_quantized_decode_amd", "csrc")
 # The product kernel that runs at each m on this matrix, and its sources.
@@ -113,7 +118,7 @@ def cpu_baseline(case, seconds: float, chunk: int = 4096):
                       f"{wall:.1f} s, fp64 dense oracle"}
 
 
-def graph_us(torch, fn, launches: int, reps: int = 20, chunk: int = 16) -> float:
+def graph_us(torch, fn, launches: int, reps: int = 20, chunk: int = GRAPH) -> float:
     """Average time of fn(i), i = 0..launches-1, in microseconds: the calls
     are captured in HIP graphs of `chunk` calls each (after one eager pass),
     and HIP events on the capturing stream bracket `reps` replays of all of
@@ -208,9 +213,9 @@ def bench_pair(torch, q2, syn, dev, copies_n: int = 512):
             q2.q8_1_rows(x, out=xq)
             prod(i)
 
-        us_step = graph_us(torch, step, copies_n, reps=10, chunk=128)
-        us_step2 = graph_us(torch, step_two_calls, copies_n, reps=10, chunk=128)
-        us_prod = graph_us(torch, prod, copies_n, reps=10, chunk=128)
+        us_step = graph_us(torch, step, copies_n, reps=10)
+        us_step2 = graph_us(torch, step_two_calls, copies_n, reps=10)
+        us_prod = graph_us(torch, prod, copies_n, reps=10)
         oq, od, _ = orc.q8_1_from_bf16_bits(pc.x_bits)
         ra, rb = orc.mmvq_pair(pc.wa, pc.wb, oq, od)
         for got, ref in ((ya, ra), (yb, rb)):
@@ -383,7 +388,7 @@ def bench_mmq(torch, q2, syn, dev, copies, case):
 def bench_grouped(torch, q2, syn, dev, copies_n: int = 64):
     """The grouped-input product (wo_a shape: 8 groups x 1024 rows, 2048-wide
     slices of a 16384-wide input) at m = 1 and m = 8 over rotating weight
-    copies, timed with HIP events around graph replays of 16 launches."""
+    copies, timed with HIP events around graph replays."""
     out = {}
     gc = syn.grouped_case(8)
     w0 = torch.from_numpy(gc.w.reshape(-1)).to(dev)
@@ -394,32 +399,8 @@ def bench_grouped(torch, q2, syn, dev, copies_n: int = 64):
     for m in (1, 8):
         xq = q2.q8_1_rows(x8[:m].contiguous())
         y = torch.empty((m, gc.groups * gc.rows), dtype=torch.float32, device=dev)
-        stream = torch.cuda.Stream()
-        graphs = []
-        torch.cuda.synchronize()
-        for c0 in range(0, copies_n, 16):
-            with torch.cuda.stream(stream):
-                for i in range(16):
-                    q2.q2k_mmvq_grouped(copies[c0 + i], xq, gc.groups, gc.rows, gc.k, m, out=y)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for i in range(16):
-                    q2.q2k_mmvq_grouped(copies[c0 + i], xq, gc.groups, gc.rows, gc.k, m, out=y)
-            graphs.append(g)
-        reps = 20
-        with torch.cuda.stream(stream):
-            for g in graphs:
-                g.replay()
-            ev0 = torch.cuda.Event(enable_timing=True)
-            ev1 = torch.cuda.Event(enable_timing=True)
-            ev0.record(stream)
-            for _ in range(reps):
-                for g in graphs:
-                    g.replay()
-            ev1.record(stream)
-            ev1.synchronize()
-        us = ev0.elapsed_time(ev1) * 1e3 / (reps * copies_n)
+        us = graph_us(torch, lambda i: q2.q2k_mmvq_grouped(copies[i], xq, gc.groups, gc.rows, gc.k, m,
+                                                           out=y), copies_n, reps=20)
         nbytes = wbytes + q2.q8_1_rows_bytes(m, gc.groups * gc.k) + 4 * m * gc.groups * gc.rows
         out[f"m{m}"] = {"us_per_launch": round(us, 3), "bytes_per_launch": nbytes,
                         "achieved": round(nbytes / us / 1e3, 1), "peak": PEAK_GBS, "unit": "GB/s",
@@ -434,7 +415,7 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
     hashed layers, 3-grams, 4 heads = 8 row ids), gather + dequantisation of
     8 table rows (500 000-row table) and q8_1 of the [1, 2048] row in one
     launch, the wkv product [20480, 2048] (80 rotating copies, 1.1 GB) and
-    the gate on [1, 4, 4096]; graphs of 16 steps, HIP events around the
+    the gate on [1, 4, 4096]; HIP graphs of the steps, HIP events around the
     replays. The same step with the gather and the q8_1 as two launches, and
     the hash alone (one decode token, a 4096-token prefill), are timed the
     same way."""
@@ -478,31 +459,7 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
         q2.engram_gate(h, kv, qk, e.eps)
 
     def timed(fn, launches, reps=20):
-        stream = torch.cuda.Stream()
-        graphs = []
-        torch.cuda.synchronize()
-        for c0 in range(0, launches, 16):
-            with torch.cuda.stream(stream):
-                for i in range(16):
-                    fn(c0 + i)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for i in range(16):
-                    fn(c0 + i)
-            graphs.append(g)
-        with torch.cuda.stream(stream):
-            for g in graphs:
-                g.replay()
-            ev0 = torch.cuda.Event(enable_timing=True)
-            ev1 = torch.cuda.Event(enable_timing=True)
-            ev0.record(stream)
-            for _ in range(reps):
-                for g in graphs:
-                    g.replay()
-            ev1.record(stream)
-            ev1.synchronize()
-        return ev0.elapsed_time(ev1) * 1e3 / (reps * launches)
+        return graph_us(torch, fn, launches, reps)
 
     def step_bf16(i):
         q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks[i % 64:i % 64 + 1], 4096 + (i % 64), out=ids)
@@ -607,29 +564,29 @@ def run(args):
 
         g_step = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_step, stream=stream):
-            for i in range(COPIES):
+            for i in range(GRAPH):
                 step(i)
         g_prod = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_prod, stream=stream):
-            for i in range(COPIES):
+            for i in range(GRAPH):
                 product(i)
         # cache-resident reference: the same copy every launch (77 MB fits the
         # 256 MB Infinity Cache); reported beside, never the roofline figure
         g_warm = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_warm, stream=stream):
-            for i in range(COPIES):
+            for i in range(GRAPH):
                 q2.q2k_mmvq(copies[0], xq, N, K, m, out=y)
         torch.cuda.synchronize()
 
-        # exactly args.steps timed steps: whole 16-step replays, then the rest
-        reps, rem = divmod(args.steps, COPIES)
+        # exactly args.steps timed steps: whole GRAPH-step replays, then the rest
+        reps, rem = divmod(args.steps, GRAPH)
         g_rem = None
         if rem:
             g_rem = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g_rem, stream=stream):
                 for i in range(rem):
                     step(i)
-        wreps = max(1, -(-args.warmup // COPIES))
+        wreps = max(1, -(-args.warmup // GRAPH))
         with torch.cuda.stream(stream):
             for _ in range(wreps):
                 g_step.replay()
@@ -662,11 +619,11 @@ def run(args):
                 g_warm.replay()
             ew1.record(stream)
             ew1.synchronize()
-        two_s = graph_us(torch, step_two_calls, COPIES, reps=max(2, reps)) / 1e6
+        two_s = graph_us(torch, step_two_calls, GRAPH, reps=max(2, reps)) / 1e6
         steps = args.steps
-        warm_s = ew0.elapsed_time(ew1) / 1e3 / (preps * COPIES)
+        warm_s = ew0.elapsed_time(ew1) / 1e3 / (preps * GRAPH)
         step_s = (t1 - t0) / steps
-        launch_s = ev0.elapsed_time(ev1) / 1e3 / (preps * COPIES)
+        launch_s = ev0.elapsed_time(ev1) / 1e3 / (preps * GRAPH)
         step_bytes = mmvq_bytes(m) + q8_bytes(m)
         # parity re-check on the benchmarked buffers (sampled rows)
         y_host = y.cpu().numpy()
@@ -687,14 +644,14 @@ def run(args):
             raise SystemExit(f"bench parity failed at m={m}")
 
     r1, r8 = results[1], results[8]
-    wreps_all = max(1, -(-args.warmup // COPIES))
+    wreps_all = max(1, -(-args.warmup // GRAPH))
     line = {
         "metric": METRIC,
         "value": round(r1["step_gbs"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": r1["steps"],
-        "warmup": wreps_all * COPIES,
+        "warmup": wreps_all * GRAPH,
         "ms_per_step": round(r1["step_s"] * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
