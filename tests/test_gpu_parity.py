@@ -1104,3 +1104,88 @@ def test_swiglu_extreme_gates():
     h_bits = h.view(torch.int16).cpu().numpy().view(np.uint16)
     assert bf16_ulp_distance(h_bits, orc.swiglu_bf16_bits(g, u)).max() <= 1
     assert_q8_equal(hq, h_bits)
+
+
+# ------------------------------------------------------------ graphs ------
+
+def test_graph_replays_match_eager():
+    """Every call is enqueue-only, so a decode sequence captured in a HIP
+    graph must give, on each replay, the bits of the same calls run eagerly:
+    the fused single and expert products (quantisation and SwiGLU in their
+    prologues), the pair, and an engram step (hash + gather + q8_1, wkv
+    product, gate on a stream restored inside the graph). Replays alternate
+    with eager work and synchronisations."""
+    rng = syn.rng_for(4242)
+    n, k = 8192, 2048
+    w = dev(syn.q2k_blocks(rng, n, k // 256).reshape(-1))
+    x = bf16_dev(syn.bf16_normal(rng, (1, k)))
+    n_exp, inter, dim = 6, 2048, 2048
+    per_gu = inter * (dim // 256) * 84
+    per_d = dim * (inter // 256) * 84
+    gate = dev(np.concatenate([syn.q2k_blocks(rng, inter, dim // 256).reshape(-1) for _ in range(n_exp)]))
+    up = dev(np.concatenate([syn.q2k_blocks(rng, inter, dim // 256).reshape(-1) for _ in range(n_exp)]))
+    down = dev(np.concatenate([syn.q2k_blocks(rng, dim, inter // 256).reshape(-1) for _ in range(n_exp)]))
+    ids = dev(np.array([4, 1, 5, 2], dtype=np.int32))
+    pc = syn.attention_pair_case(1, seed=4243)
+    wa, wb = dev(pc.wa.reshape(-1)), dev(pc.wb.reshape(-1))
+    xp = bf16_dev(pc.x_bits)
+    e = syn.engram_step_case()
+    hc = syn.engram_hash_case(seqlen=40)
+    tm, mu, pr, of = _hash_tables_dev(hc)
+    cache = torch.zeros(64, dtype=torch.int64, device="cuda")
+    q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, dev(hc.tokens[:32]), 0)
+    table = dev(e.table.reshape(-1))
+    wkv = dev(e.wkv.reshape(-1))
+    h0 = dev(e.h)
+    qk = dev(e.qk)
+    tok = dev(hc.tokens[32:33].astype(np.int32))
+    n_out = e.dim * (e.hc + 1)
+
+    outs = {name: None for name in ("y", "xq", "gu", "xq_gu", "yd", "hq", "ya", "yb", "xq_p",
+                                    "xq_e", "kv", "h")}
+    outs["y"] = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    outs["xq"] = torch.empty(q2.q8_1_rows_bytes(1, k), dtype=torch.uint8, device="cuda")
+    outs["gu"] = torch.empty((2, 4, 1, inter), dtype=torch.float32, device="cuda")
+    outs["xq_gu"] = torch.empty(q2.q8_1_rows_bytes(1, dim), dtype=torch.uint8, device="cuda")
+    outs["yd"] = torch.empty((1, 4, 1, dim), dtype=torch.float32, device="cuda")
+    outs["hq"] = torch.empty(q2.q8_1_rows_bytes(4, inter), dtype=torch.uint8, device="cuda")
+    outs["ya"] = torch.empty((1, pc.na), dtype=torch.float32, device="cuda")
+    outs["yb"] = torch.empty((1, pc.nb), dtype=torch.float32, device="cuda")
+    outs["xq_p"] = torch.empty(q2.q8_1_rows_bytes(1, pc.k), dtype=torch.uint8, device="cuda")
+    outs["xq_e"] = torch.empty(q2.q8_1_rows_bytes(1, 8 * 256), dtype=torch.uint8, device="cuda")
+    outs["kv"] = torch.empty((1, n_out), dtype=torch.float32, device="cuda")
+    outs["h"] = torch.empty_like(h0)
+
+    def seq():
+        q2.q8_1_q2k_mmvq(w, x, n, k, xq=outs["xq"], out=outs["y"])
+        q2.q8_1_q2k_mmvq_experts([gate, up], per_gu, n_exp, ids, x, inter, dim, xq=outs["xq_gu"],
+                                 out=outs["gu"])
+        g = outs["gu"][0].view(4, inter)
+        u = outs["gu"][1].view(4, inter)
+        q2.swiglu_q2k_mmvq_experts([down], per_d, n_exp, ids, g, u, dim, hq=outs["hq"], out=outs["yd"])
+        q2.q8_1_q2k_mmvq_pair(wa, pc.na, wb, pc.nb, xp, pc.k, xq=outs["xq_p"], ya=outs["ya"], yb=outs["yb"])
+        q2.engram_rows_q8_1(tm, mu, pr, of, hc.pad_id, cache, tok, 32, 1, table, 500000, xq=outs["xq_e"])
+        q2.q2k_mmvq(wkv, outs["xq_e"], n_out, 2048, 1, out=outs["kv"])
+        outs["h"].copy_(h0)
+        q2.engram_gate(outs["h"], outs["kv"], qk, e.eps)
+
+    seq()
+    torch.cuda.synchronize()
+    eager = {name: t.clone() for name, t in outs.items()}
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        seq()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        seq()
+    for rep in range(3):
+        for t in outs.values():
+            t.zero_()
+        q2.q2k_mmvq(w, eager["xq"], n, k, 1)          # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t in outs.items():
+            assert torch.equal(t.view(torch.uint8), eager[name].view(torch.uint8)), f"{name}, replay {rep}"
