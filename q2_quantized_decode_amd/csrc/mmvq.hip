@@ -60,6 +60,8 @@ struct MmvqParams {
   int32_t tsplit;                    // tokens taken by separate waves (1: none)
   const float* sg;                   // SwiGLU prologue: gate rows [n_ids, k]
   const float* su;                   // and up rows
+  const uint8_t* xb16;               // narrow kernel with FQ: the token's bf16 row
+  uint8_t* xq_out;                   // narrow kernel with FQ: receives its q8_1 row
 };
 
 // Touches every field of the argument block at once, so that its scalar
@@ -700,15 +702,22 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
 }
 
 // Narrow rows (2 * k/256 <= 64 half blocks): one half block per lane.
-template <int M, bool CACHE, int DEPTH, bool DOTS>
+//
+// FQ (one token, one bf16 row p.xb16 shared by every matrix): the workgroup
+// quantises the row into LDS as mmvq_m1_kernel's FQ = 1 prologue does
+// (workgroup 0 also writes p.xq_out), after issuing its first weight loads.
+template <int M, bool CACHE, int DEPTH, bool DOTS, bool FQ = false>
 __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
+  static_assert(!FQ || (M == 1 && CACHE && !DOTS), "fused quantisation: one token, products only");
   prefetch_args(p);
   const int lane = threadIdx.x & 63;
   const int g8 = p.g8;
   const int wg = blockIdx.x;
-  const int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 +
-                   __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  if (wave >= p.total_waves) return;
+  int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 +
+             __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const bool in_grid = wave < p.total_waves;
+  if (!FQ && !in_grid) return;
+  if (FQ && !in_grid) wave = p.total_waves - 1;   // a valid job; the wave exits after the barrier
 
   const int k = p.k;
   const int nb = k >> 8;
@@ -729,19 +738,50 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
   }
   WaveJob J = resolve_wave<M>(p, jw, P);
   J.y += (int64_t)tok * J.ldy;
-  if (J.it >= J.it_end) return;
+  const bool live = in_grid && J.it < J.it_end;
+  if (!FQ && !live) return;
   const uint8_t* wlane = J.w + b * kBlockBytes;
 
   WHalf ws[DEPTH];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    const int st = J.it + d * J.stride;
-    const int row = st * P + prow;
-    ws[d] = (st < J.it_end && hb_ok && row < J.n) ? load_whalf(wlane + row * rowbytes, h)
-                                                 : zero_whalf();
-  }
   AHalf act;
-  if constexpr (CACHE) act = hb_ok ? load_ahalf(J.x, tok, b, h) : zero_ahalf();
+  if constexpr (FQ) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+    const int tid = threadIdx.x;
+    const bool qthread = tid < (k >> 5);            // one 32-value block per thread
+    const uint8_t* xb = p.xb16 + 64 * (qthread ? tid : 0);
+    u32x4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
+    // first weight loads, unconditional and in bounds (block 0 of row 0
+    // where the lane or the step has nothing to read), zeroed afterwards
+    const uint8_t* wsafe = J.w + (hb_ok ? b : 0) * kBlockBytes;
+    const int hs = hb_ok ? h : 0;
+    bool wok[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int st = J.it + d * J.stride;
+      const int row = st * P + prow;
+      wok[d] = live && st < J.it_end && hb_ok && row < J.n;
+      ws[d] = load_whalf(wsafe + (size_t)(wok[d] ? row : 0) * rowbytes, hs);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the weight loads ahead of the quantisation
+    q8_1_block_store(xs, blockIdx.x == 0 ? p.xq_out : nullptr, raw, tid, k, qthread);
+    lds_barrier_m1();
+    if (!live) return;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+      if (!wok[d]) ws[d] = zero_whalf();
+    act = hb_ok ? load_ahalf_lds(xs, k, b, h) : zero_ahalf();
+  } else {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int st = J.it + d * J.stride;
+      const int row = st * P + prow;
+      ws[d] = (st < J.it_end && hb_ok && row < J.n) ? load_whalf(wlane + row * rowbytes, h)
+                                                   : zero_whalf();
+    }
+    if constexpr (CACHE) act = hb_ok ? load_ahalf(J.x, tok, b, h) : zero_ahalf();
+  }
 
   for (int base = J.it; base < J.it_end; base += DEPTH * J.stride) {
 #pragma unroll
@@ -1140,6 +1180,21 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   if (a.x_bf16 != nullptr) {
     if (fuse_x) {
       dispatch_m1_fused<1>(p, grid, a.x_bf16, static_cast<uint8_t*>(const_cast<void*>(a.xq)), stream);
+      return hipGetLastError();
+    }
+    // the same prologue in the one-step kernel, for the smaller one-token
+    // launches (same kernel as without it, so the same bits)
+    if (!m1_path && !wide && !dots && a.m == 1 && a.groups == 0 &&
+        (a.ids == nullptr || a.x_per_id == 0)) {
+      p.xb16 = static_cast<const uint8_t*>(a.x_bf16);
+      p.xq_out = static_cast<uint8_t*>(const_cast<void*>(a.xq));
+      const size_t lds = q8_row_bytes(a.k);
+      if (tu.depth == 1)
+        hipLaunchKernelGGL((mmvq_narrow_kernel<1, true, 1, false, true>), grid, dim3(256), lds, stream, p);
+      else if (tu.depth == 4)
+        hipLaunchKernelGGL((mmvq_narrow_kernel<1, true, 4, false, true>), grid, dim3(256), lds, stream, p);
+      else
+        hipLaunchKernelGGL((mmvq_narrow_kernel<1, true, 2, false, true>), grid, dim3(256), lds, stream, p);
       return hipGetLastError();
     }
     const hipError_t e = launch_q8_1_rows(a.x_bf16, a.x_stride, const_cast<void*>(a.xq), a.m, a.k,

@@ -358,13 +358,16 @@ def test_token_split(n, k, m, packed_dots):
 @pytest.mark.parametrize("n,k,m", [(20480, 2048, 1), (16384, 1024, 1), (8192, 4096, 1),
                                    (4099, 8192, 1), (4103, 2048, 4), (2050, 4096, 5),
                                    (4099, 7168, 3), (513, 8192, 8),
-                                   (4096, 1024, 1), (300, 4096, 1), (1000, 2048, 3), (8197, 7168, 8)])
+                                   (4096, 1024, 1), (300, 4096, 1), (1, 1280, 1), (3, 256, 1),
+                                   (37, 2560, 1), (1, 8192, 1), (1000, 2048, 3), (8197, 7168, 8)])
 def test_fused_q8_1_equals_two_calls(n, k, m):
     """q8_1_q2k_mmvq gives the bytes of q8_1_rows and the bits of q2k_mmvq on
-    them. The first four shapes run as one launch (one token; k = 8192 has
-    256 blocks, one per thread); the others take a q8_1 launch ahead of the
-    product (tokens split over waves, too few row steps for the run kernel,
-    the matrix cores). Rows are strided on the input for m > 1."""
+    them. One token runs as one launch: the first four shapes on the run
+    kernel (k = 8192 has 256 blocks, one per thread), the next six on the
+    one-step kernel (one row, idle lanes past 2*k/256 half blocks, a single
+    block per row); the last two take a q8_1 launch ahead of the product
+    (tokens split over waves, the matrix cores). Rows are strided on the
+    input for m > 1."""
     case = syn.single_gemv_case(n=n, k=k, m=m, seed=7600 + n + k + m)
     w = dev(case.w.reshape(-1))
     if m == 1:
@@ -380,7 +383,7 @@ def test_fused_q8_1_equals_two_calls(n, k, m):
     assert torch.equal(xq[:need], xq2[:need])
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
     oq, od = assert_q8_equal(xq, case.x_bits)
-    rows = _sample_rows(n, n + k, extra=64)
+    rows = np.arange(n) if n <= 512 else _sample_rows(n, n + k, extra=64)
     assert_close(y.cpu().numpy()[:, rows], orc.mmvq(case.w[rows], oq, od), f"fused n={n} k={k} m={m}")
 
 
