@@ -5,7 +5,7 @@
 // vector dot). With 8 tokens the packed-dot formulation spends two int8 dot
 // instructions per 4 weights on the vector ALUs; here the integer block sums
 // go through v_mfma_i32_16x16x64_i8 and the min term through
-// v_mfma_f64_16x16x4f64, so the vector ALUs only unpack the 2-bit weights and
+// v_mfma_f64_4x4x4f64, so the vector ALUs only unpack the 2-bit weights and
 // scale the per-block integer results.
 //
 // * Tile: one wave computes 16 weight rows x 8 token slots over a range of
@@ -22,11 +22,12 @@
 //   so the output (A-row, weight row) is exactly I = sum sc*q*xq of one
 //   (token, q8 block, row). Each I is scaled by its d8 in fp64 and each
 //   super-block's sum by the row's d.
-// * M term: sum_s dmin*m_s * (d8*S)_s, four fp64 MFMAs per super-block
-//   (K = 4 sub-blocks each: MFMA i, k-index g is sub-block 8(g>>1) + 2i +
-//   (g&1), the scale byte a lane already holds), B = dmin*m (exact), A =
-//   d8*S of the activations (exact), accumulated in the MFMA accumulators.
-//   Its A-rows are arranged so that its output lands on the same lane and
+// * M term: dmin * sum_s m_s * (d8*S)_s per super-block, the sum on two
+//   chains of four fp64 MFMAs (K = 4 sub-blocks each: MFMA i, k-index g is
+//   sub-block 8(g>>1) + 2i + (g&1), the scale byte a lane already holds),
+//   B = m (exact), A = d8*S of the activations (exact); one fp64 fma per
+//   chain then adds dmin times the sum to the row's running M sum. Its
+//   A-rows are arranged so that its output lands on the same lane and
 //   register as the I output of the same token.
 // * Activations of the workgroup's matrix (8 token slots of quants, d8 and
 //   d8*S in fp64, plus an all-zero slot) are staged once in LDS; the waves of
@@ -308,13 +309,39 @@ __device__ __forceinline__ Lane lane_consts() {
   return L;
 }
 
-// B operand of plane pl: sc * q of the lane's 16 weights.
-__device__ __forceinline__ v4i plane_weights(const u32x4& qs, uint32_t sw, int pl) {
-  const uint32_t sc = (sw >> (16 * (pl & 1))) & 15u;
+// Logical right shift of a 64-bit register pair by a constant, as one
+// v_lshrrev_b64: the compiler splits the shift into two 32-bit shifts when it
+// sees that the bits crossing between the halves are masked off afterwards.
+template <int S>
+__device__ __forceinline__ uint64_t lshr64(uint64_t v) {
+  uint64_t r;
+  asm("v_lshrrev_b64 %0, %2, %1" : "=v"(r) : "v"(v), "n"(S));
+  return r;
+}
+
+// B operand of plane pl: sc * q of the lane's 16 weights. scw holds the
+// lane's scale bytes; sc is the 4-bit field at bit off. Two qs dwords are
+// shifted at once: bits crossing from the high dword land in bits 26..31 of
+// the low one (shift <= 6), which the 0x03 byte mask drops.
+template <int PL>
+__device__ __forceinline__ v4i plane_weights(const u32x4& qs, uint32_t scw, uint32_t off) {
+  const uint32_t sc = __builtin_amdgcn_ubfe(scw, off, 4);
   const uint32_t table = mul_u24_030201(sc) << 8;  // bytes 0, sc, 2sc, 3sc
+  uint32_t sel[4];
+  if constexpr (PL == 0) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sel[w] = qs[w];
+  } else {
+    const uint64_t lo = lshr64<2 * PL>(((uint64_t)qs[1] << 32) | qs[0]);
+    const uint64_t hi = lshr64<2 * PL>(((uint64_t)qs[3] << 32) | qs[2]);
+    sel[0] = (uint32_t)lo;
+    sel[1] = (uint32_t)(lo >> 32);
+    sel[2] = (uint32_t)hi;
+    sel[3] = (uint32_t)(hi >> 32);
+  }
   v4i wq;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) wq[w] = (int)__builtin_amdgcn_perm(0u, table, (qs[w] >> (2 * pl)) & 0x03030303u);
+  for (int w = 0; w < 4; ++w) wq[w] = (int)__builtin_amdgcn_perm(0u, table, sel[w] & 0x03030303u);
   return wq;
 }
 
@@ -419,8 +446,8 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const uint8_t* w0, 
   double yv[4] = {0.0, 0.0, 0.0, 0.0};
   if (active) {
     // M term on v_mfma_f64_4x4x4f64 (four 4x4 blocks): block blk = weight rows
-    // 4blk..4blk+3, rows of A = tokens 0..3 (accM0) or 4..7 (accM1), K = four
-    // sub-blocks. B[blk][k][j] sits on lane 16k + 4blk + j = (g, row j16): the
+    // 4blk..4blk+3, rows of A = tokens 0..3 (sM0, then accM0) or 4..7 (sM1,
+    // accM1), K = four sub-blocks. B[blk][k][j] sits on lane 16k + 4blk + j = (g, row j16): the
     // lane's own row and one of its own scale bytes. D[blk][i][j] lands on
     // lane 16i + 4blk + j: token i (+4), row j16. Unlike the 16x16x4 form it
     // wastes no rows on absent tokens, and an fp64 MFMA stalls the vector ALU
@@ -433,23 +460,30 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const uint8_t* w0, 
       const Blk cur = ring[bb % R];
       if (bb + R < NBH) ring[bb % R] = load_blk(Wt + (bb + R) * kBlockBytes, off);
 
-      const uint32_t sw0 = cur.sc[0] >> L.sc_shift, sw1 = cur.sc[1] >> L.sc_shift;
       const double dmin = (double)fp16_bits_to_f32(cur.dd >> 16);
+      // sum_s m_s (d8*S)_s of this super-block (exact terms), then times dmin
+      double sM0 = 0.0, sM1 = 0.0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t mb = ((i < 2 ? sw0 : sw1) >> (16 * (i & 1) + 4)) & 15u;
+        const uint32_t mb = __builtin_amdgcn_ubfe(cur.sc[i >> 1], L.sc_shift + 16u * (i & 1) + 4u, 4);
         const v2d a = lds_load<v2d>(lds, L.at_base + 1024u * b + 256u * i);
         const double a0 = a[0], a1 = a[1];
-        const double wm = dmin * (double)mb;
-        accM0 = __builtin_amdgcn_mfma_f64_4x4x4f64(a0, wm, accM0, 0, 0, 0);
-        accM1 = __builtin_amdgcn_mfma_f64_4x4x4f64(a1, wm, accM1, 0, 0, 0);
+        const double wm = (double)mb;
+        sM0 = __builtin_amdgcn_mfma_f64_4x4x4f64(a0, wm, sM0, 0, 0, 0);
+        sM1 = __builtin_amdgcn_mfma_f64_4x4x4f64(a1, wm, sM1, 0, 0, 0);
       }
+      accM0 = fma(dmin, sM0, accM0);
+      accM1 = fma(dmin, sM1, accM1);
       double accI[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int pl = 0; pl < 4; ++pl) {
         const v4i aq = lds_load<v4i>(lds, L.a_base + 256u * b + 32u * pl);
-        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, plane_weights(cur.qs, pl < 2 ? sw0 : sw1, pl),
-                                                            v4i{0, 0, 0, 0}, 0, 0, 0);
+        const uint32_t scw = cur.sc[pl >> 1], off = L.sc_shift + 16u * (pl & 1);
+        const v4i wq = pl == 0 ? plane_weights<0>(cur.qs, scw, off)
+                     : pl == 1 ? plane_weights<1>(cur.qs, scw, off)
+                     : pl == 2 ? plane_weights<2>(cur.qs, scw, off)
+                               : plane_weights<3>(cur.qs, scw, off);
+        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, wq, v4i{0, 0, 0, 0}, 0, 0, 0);
         const v4d d8 = lds_load<v4d>(lds, L.d8_base + 512u * b + 128u * pl);
 #pragma unroll
         for (int i = 0; i < 4; ++i) accI[i] = fma(d8[i], (double)c[i], accI[i]);
