@@ -15,14 +15,21 @@ Method:
 * Inputs are resident in HBM before timing. The weights are replicated 16
   times (1.23 GB, over four times the 256 MB Infinity Cache) and step i reads
   copy i % 16, so every step streams its matrix from HBM.
-* The steps are captured once into a HIP graph (256 steps, copy i % 16) and
-  the graph is replayed; W warm-up steps, then K timed steps between two
-  device synchronisations (wall clock).
-* Roofline of the dominant kernel (q2k_mmvq): a second graph holds only the
-  256 products; HIP events on the launching stream bracket its replays, and
-  achieved = algorithmic bytes per launch / average launch time.
+* W warm-up steps run first (eagerly). The K timed steps are captured into
+  one HIP graph (copy i % 16); on the launching stream a sleep kernel keeps
+  the GPU busy while the host enqueues a start event, the graph and an end
+  event, so neither the host's launch cost nor the graph's upload lands
+  inside the timed region: ms_per_step = event time / K.
+* Roofline of the dominant kernel (q2k_mmvq): the same method over a graph
+  of products alone (at least 640 launches), achieved = algorithmic bytes
+  per launch / average launch time between the events (gaps between
+  consecutive kernels included). Beside it, the per-dispatch average of the
+  same kernel from the committed rocprofv3 kernel trace
+  (profiles/mmvq_large_verify_rocprof.json), when that record was taken on
+  the current kernel source.
 * CPU baseline: the CPU oracle timed on a bounded sample of rows of the
-  same matrix and token (about twelve seconds of host work).
+  same matrix and token, on one thread and on one thread per available core
+  (median of three runs each; about twenty seconds of host work).
 
 Prints one JSON line.
 """
@@ -52,10 +59,14 @@ COPIES = 16
 # (with 16 the replay overhead added ~0.4 us to every 15 us launch).
 GRAPH = 256
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_large_verify_traffic.json")
+ROCPROF_FILE = os.path.join(ROOT, "profiles", "mmvq_large_verify_rocprof.json")
 CSRC = os.path.join(ROOT, "q2_quantized_decode_amd", "csrc")
 # The product kernel that runs at each m on this matrix, and its sources.
 KERNELS = {1: ("mmvq_m1_kernel", ("mmvq.hip", "q2k_device.h")),
            8: ("mmvq_mfma_kernel", ("mmvq_mfma.hip", "q2k_device.h"))}
+# The exact instantiation the product runs at each m on this matrix, as
+# rocprofv3 names it in its kernel statistics.
+KERNEL_INSTANCES = {1: "mmvq_m1_kernel<6, 4, 32, 0>", 8: "mmvq_mfma_kernel<28, 2, false>"}
 COPY_BYTES = 256 << 20     # size of the calibration copy
 
 
@@ -91,31 +102,72 @@ def measured_traffic(m: int):
     return float(r["bytes_per_launch"])
 
 
-def cpu_baseline(case, seconds: float, chunk: int = 4096):
-    """The oracle's m = 1 product over consecutive row chunks of the matrix
-    (wrapping around) until about `seconds` of wall time have passed."""
+def measured_rocprof(m: int):
+    """Per-dispatch average (us) of the product kernel at m from the committed
+    rocprofv3 kernel statistics, or None when absent or taken on a different
+    kernel source."""
+    try:
+        with open(ROCPROF_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get(f"m{m}")
+    if not r or r.get("kernel_hash") != kernel_hash(m):
+        return None
+    return float(r["avg_us"])
+
+
+def _oracle_rows(orc, case, xq, d8, r0: int, rows: int) -> int:
+    w = case.w[r0:r0 + rows]
+    orc.mmvq(w, xq, d8)
+    return w.nbytes
+
+
+def cpu_baseline(case, chunk: int = 2048, runs: int = 3, max_threads: int = 16):
+    """The oracle's m = 1 product (the plain fp64 dense route) on row chunks
+    of the matrix: one chunk on one thread, and one chunk per thread on one
+    thread per core of this process's affinity mask (at most max_threads;
+    numpy releases the GIL inside its array operations, and BLAS is held to
+    one thread per call so the threads do not oversubscribe). Median of
+    `runs` runs each; GB/s of weight bytes."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from oracle import q2k_oracle as orc
 
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:          # pragma: no cover - threadpoolctl ships with the image
+        threadpool_limits = None
+    affinity = len(os.sched_getaffinity(0))
+    threads = max(1, min(affinity, max_threads))
     xq, d8, _ = orc.q8_1_from_bf16_bits(case.x_bits[:1])
-    done_bytes = 0
-    chunks = 0
-    c0 = time.process_time()
-    t0 = time.perf_counter()
-    while True:
-        r0 = (chunks * chunk) % N
-        w = case.w[r0:r0 + chunk]
-        orc.mmvq(w, xq, d8)
-        done_bytes += w.nbytes
-        chunks += 1
-        wall = time.perf_counter() - t0
-        if wall >= seconds:
-            break
-    cpu = time.process_time() - c0
-    return {"value": round(done_bytes / wall / 1e9, 6), "unit": "GB/s",
-            "cores": max(1, round(cpu / wall)), "kind": "oracle",
-            "sample": f"{chunks} chunks of {chunk} rows of the [32768, 7168] Q2_K matrix "
-                      f"(rows taken in order, wrapping), m=1: {done_bytes} weight bytes in "
-                      f"{wall:.1f} s, fp64 dense oracle"}
+
+    def timed(nthreads: int, run: int) -> float:
+        starts = [((run * nthreads + i) * chunk) % N for i in range(nthreads)]
+        t0 = time.perf_counter()
+        if nthreads == 1:
+            done = _oracle_rows(orc, case, xq, d8, starts[0], chunk)
+        else:
+            with ThreadPoolExecutor(max_workers=nthreads) as ex:
+                done = sum(ex.map(lambda r0: _oracle_rows(orc, case, xq, d8, r0, chunk), starts))
+        return done / (time.perf_counter() - t0) / 1e9
+
+    def median_of(nthreads: int) -> float:
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                return float(np.median([timed(nthreads, r) for r in range(runs)]))
+        return float(np.median([timed(nthreads, r) for r in range(runs)]))
+
+    one = median_of(1)
+    many = median_of(threads) if threads > 1 else one
+    return {"value": round(many, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "affinity_cores": affinity, "threads": threads, "value_1_thread": round(one, 6),
+            "runs": runs,
+            "sample": f"m=1 product of the [32768, 7168] Q2_K matrix on {chunk}-row chunks "
+                      f"({chunk * (K // 256) * 84} weight bytes each): one chunk on 1 thread, and "
+                      f"{threads} chunks on {threads} threads (one per core of the affinity "
+                      f"mask, BLAS at one thread per call); median of {runs} runs each; "
+                      "fp64 dense oracle"}
 
 
 def graph_us(torch, fn, launches: int, reps: int = 20, chunk: int = GRAPH) -> float:
@@ -148,6 +200,45 @@ def graph_us(torch, fn, launches: int, reps: int = 20, chunk: int = GRAPH) -> fl
         ev1.record(stream)
         ev1.synchronize()
     return ev0.elapsed_time(ev1) * 1e3 / (reps * launches)
+
+
+def sleep_cycles_for(torch, stream, us: float) -> int:
+    """GPU sleep-kernel cycles (torch.cuda._sleep) that last about `us`
+    microseconds on this device, measured once with HIP events."""
+    cyc = 1 << 20
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(cyc)      # first launch (module load) untimed
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.cuda._sleep(cyc)
+        e1.record(stream)
+        e1.synchronize()
+    per_us = cyc / max(e0.elapsed_time(e1) * 1e3, 1e-3)
+    return int(per_us * us)
+
+
+def timed_steps(torch, stream, fn, first: int, count: int, busy: int) -> float:
+    """Seconds per call of fn(i), i = first .. first+count-1: the calls are
+    captured into one HIP graph; on `stream` a sleep kernel of `busy` cycles
+    keeps the GPU busy while the host enqueues the start event, the graph and
+    the end event, so the events bracket exactly the `count` calls."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(first, first + count):
+            fn(i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(busy)
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        ev1.synchronize()
+    del g
+    return ev0.elapsed_time(ev1) / 1e3 / count
 
 
 def _roof(nbytes: int, us: float) -> dict:
@@ -539,12 +630,14 @@ def run(args):
     x8 = syn.bf16_bits_to_tensor(case.x_bits).to(dev)
 
     results = {}
+    stream = torch.cuda.Stream()
+    busy = sleep_cycles_for(torch, stream, 3000.0)     # ~3 ms of GPU time ahead of each graph
+    warm, steps = args.warmup, args.steps
+    roof_launches = max(steps, 640)
     for m in (1, 8):
         x = x8[:m].contiguous()
         xq = torch.empty(q2.q8_1_rows_bytes(m, K), dtype=torch.uint8, device=dev)
         y = torch.empty((m, N), dtype=torch.float32, device=dev)
-        stream = torch.cuda.Stream()
-        torch.cuda.synchronize()
 
         def step(i):
             # q8_1 + product in one call (one launch at m = 1)
@@ -557,75 +650,22 @@ def run(args):
         def product(i):
             q2.q2k_mmvq(copies[i % COPIES], xq, N, K, m, out=y)
 
-        with torch.cuda.stream(stream):
-            for i in range(COPIES):          # eager warm-up (and first launches)
-                step(i)
+        def product_same_copy(i):
+            # cache-resident reference: the 77 MB matrix fits the 256 MB
+            # Infinity Cache; reported beside, never the roofline figure
+            q2.q2k_mmvq(copies[0], xq, N, K, m, out=y)
+
         torch.cuda.synchronize()
-
-        g_step = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_step, stream=stream):
-            for i in range(GRAPH):
-                step(i)
-        g_prod = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_prod, stream=stream):
-            for i in range(GRAPH):
-                product(i)
-        # cache-resident reference: the same copy every launch (77 MB fits the
-        # 256 MB Infinity Cache); reported beside, never the roofline figure
-        g_warm = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_warm, stream=stream):
-            for i in range(GRAPH):
-                q2.q2k_mmvq(copies[0], xq, N, K, m, out=y)
-        torch.cuda.synchronize()
-
-        # exactly args.steps timed steps: whole GRAPH-step replays, then the rest
-        reps, rem = divmod(args.steps, GRAPH)
-        g_rem = None
-        if rem:
-            g_rem = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_rem, stream=stream):
-                for i in range(rem):
-                    step(i)
-        wreps = max(1, -(-args.warmup // GRAPH))
         with torch.cuda.stream(stream):
-            for _ in range(wreps):
-                g_step.replay()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(reps):
-                g_step.replay()
-            if g_rem is not None:
-                g_rem.replay()
-            torch.cuda.synchronize()
-            t1 = time.perf_counter()
-
-            # dominant kernel alone, bracketed by events on this stream
-            for _ in range(wreps):
-                g_prod.replay()
-            ev0 = torch.cuda.Event(enable_timing=True)
-            ev1 = torch.cuda.Event(enable_timing=True)
-            preps = max(1, reps)
-            ev0.record(stream)
-            for _ in range(preps):
-                g_prod.replay()
-            ev1.record(stream)
-            ev1.synchronize()
-            for _ in range(wreps):
-                g_warm.replay()
-            ew0 = torch.cuda.Event(enable_timing=True)
-            ew1 = torch.cuda.Event(enable_timing=True)
-            ew0.record(stream)
-            for _ in range(preps):
-                g_warm.replay()
-            ew1.record(stream)
-            ew1.synchronize()
-        two_s = graph_us(torch, step_two_calls, GRAPH, reps=max(2, reps)) / 1e6
-        steps = args.steps
-        warm_s = ew0.elapsed_time(ew1) / 1e3 / (preps * GRAPH)
-        step_s = (t1 - t0) / steps
-        launch_s = ev0.elapsed_time(ev1) / 1e3 / (preps * GRAPH)
+            for i in range(warm):            # the W untimed warm-up steps
+                step(i)
+        step_s = timed_steps(torch, stream, step, warm, steps, busy)
+        two_s = timed_steps(torch, stream, step_two_calls, warm, steps, busy)
+        launch_s = timed_steps(torch, stream, product, warm, roof_launches, busy)
+        warm_s = timed_steps(torch, stream, product_same_copy, 0, 256, busy)
+        step(warm + steps - 1)               # y of the last timed step, for the parity check
+        torch.cuda.synchronize()
         step_bytes = mmvq_bytes(m) + q8_bytes(m)
-        # parity re-check on the benchmarked buffers (sampled rows)
         y_host = y.cpu().numpy()
         results[m] = dict(step_s=step_s, launch_s=launch_s, warm_s=warm_s, steps=steps, y=y_host,
                           two_s=two_s,
@@ -639,19 +679,39 @@ def run(args):
     for m in (1, 8):
         xq_o, d8_o, _ = orc.q8_1_from_bf16_bits(case.x_bits[:m])
         ref = orc.mmvq(case.w[rows], xq_o, d8_o)
-        got = results[m]["y"][:, rows].astype(np.float64)
-        if not np.all(np.abs(got - ref) <= 1e-4 + 2e-3 * np.abs(ref)):
+        got = results[m]["y"][:, rows]
+        if not np.all(np.abs(got.astype(np.float64) - ref) <= 1e-4 + 2e-3 * np.abs(ref)):
             raise SystemExit(f"bench parity failed at m={m}")
+        if not np.array_equal(got.view(np.uint32), orc.mmvq_f32(case.w[rows], xq_o, d8_o).view(np.uint32)):
+            raise SystemExit(f"bench parity failed at m={m}: not the fixed-order bits")
 
     r1, r8 = results[1], results[8]
-    wreps_all = max(1, -(-args.warmup // GRAPH))
+
+    def roofline(m, r):
+        out = {"bound": "hbm", "achieved": round(r["achieved"], 1), "peak": PEAK_GBS,
+               "unit": "GB/s", "frac": round(r["achieved"] / PEAK_GBS, 4),
+               "traffic": measured_traffic(m),
+               "kernel": f"q2k_mmvq ({KERNEL_INSTANCES[m]})",
+               "bytes_per_launch": mmvq_bytes(m),
+               "us_per_launch": round(r["launch_s"] * 1e6, 3),
+               "timing": f"HIP events around {roof_launches} back-to-back launches in one graph "
+                         "(gaps between kernels included)"}
+        rp = measured_rocprof(m)
+        if rp is not None:
+            gbs = mmvq_bytes(m) / rp / 1e3
+            out["rocprof"] = {"us_per_launch": round(rp, 3), "achieved": round(gbs, 1),
+                              "frac": round(gbs / PEAK_GBS, 4),
+                              "source": "profiles/mmvq_large_verify_rocprof.json (kernel trace "
+                                        "average on the current kernel source)"}
+        return out
+
     line = {
         "metric": METRIC,
         "value": round(r1["step_gbs"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": r1["steps"],
-        "warmup": wreps_all * GRAPH,
+        "warmup": warm,
         "ms_per_step": round(r1["step_s"] * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -664,12 +724,7 @@ def run(args):
                    "pct_of_peak": round(100 * r1["step_gbs"] / PEAK_GBS, 2),
                    "tokens_per_s": round(1 / r1["step_s"], 1),
                    "ms_per_step_two_launches": round(r1["two_s"] * 1e3, 5)},
-        "roofline": {"bound": "hbm", "achieved": round(r1["achieved"], 1), "peak": PEAK_GBS,
-                     "unit": "GB/s", "frac": round(r1["achieved"] / PEAK_GBS, 4),
-                     "traffic": measured_traffic(1),
-                     "kernel": f"q2k_mmvq ({KERNELS[1][0]})",
-                     "bytes_per_launch": mmvq_bytes(1),
-                     "us_per_launch": round(r1["launch_s"] * 1e6, 3)},
+        "roofline": roofline(1, r1),
         "cache_resident_us_per_launch": {
             "m1": round(r1["warm_s"] * 1e6, 3), "m8": round(r8["warm_s"] * 1e6, 3),
             "note": "same weight copy every launch (fits the Infinity Cache); not a roofline figure"},
@@ -678,13 +733,7 @@ def run(args):
                "ms_per_step_two_calls": round(r8["two_s"] * 1e3, 5),
                "pct_of_peak": round(100 * r8["step_gbs"] / PEAK_GBS, 2),
                "tokens_per_s": round(8 / r8["step_s"], 1),
-               "roofline": {"bound": "hbm", "achieved": round(r8["achieved"], 1),
-                            "peak": PEAK_GBS, "unit": "GB/s",
-                            "frac": round(r8["achieved"] / PEAK_GBS, 4),
-                            "traffic": measured_traffic(8),
-                            "kernel": f"q2k_mmvq ({KERNELS[8][0]})",
-                            "bytes_per_launch": mmvq_bytes(8),
-                            "us_per_launch": round(r8["launch_s"] * 1e6, 3)}},
+               "roofline": roofline(8, r8)},
     }
     if not args.headline_only and (only is None or "mmq" in only):
         line["mmq"] = bench_mmq(torch, q2, syn, dev, copies, case)
@@ -696,7 +745,7 @@ def run(args):
                 line[SECTION_KEYS[name]] = SECTION_FNS[name](torch, q2, syn, dev)
                 torch.cuda.synchronize()
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(line), flush=True)
 
 
@@ -783,8 +832,6 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3200)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--pmc-calibration", action="store_true")
     ap.add_argument("--only", default="",

@@ -61,7 +61,7 @@ extern "C" {
 #define Q2K_API
 #endif
 
-#define Q2K_ABI_VERSION 4
+#define Q2K_ABI_VERSION 5
 
 #define Q2K_OK 0
 #define Q2K_EINVAL (-1)   /* NULL pointer, or pointers that must not overlap do */
@@ -106,7 +106,19 @@ Q2K_API int32_t q8_1_rows(const void* x_bf16_dev, int64_t x_row_stride, void* xq
  *            overlap w or xq.
  *   1 <= m <= 8, n >= 1, k % 256 == 0.
  * y[t][r] = sum over the row's blocks b and q8 blocks c of
- *           d8[t][c] * (d_b * I - dmin_b * M), I and M exact int32 sums. */
+ *           d8[t][c] * (d_b * I - dmin_b * M), I and M exact int32 sums,
+ * evaluated in one fixed order that every product kernel of this library
+ * follows, so that all of them (and every entry point that computes this
+ * product: pair, expert, grouped, fused and mmq forms) return the same bits:
+ *   - per half block (super-block b, half h, q8 blocks c = 8b+4h+j, j=0..3):
+ *     fI = ((d8_0*I_0 + d8_1*I_1) + d8_2*I_2) + d8_3*I_3 in fp64, one fma per
+ *     term starting from +0 (each product is exact), fM likewise with M, and
+ *     v = RN(d_b*fI) - RN(dmin_b*fM);
+ *   - per half h, a pairwise tree over b = 0..NBP-1 (NBP = k/256 rounded up
+ *     to a power of two; leaves past the row are +0), neighbours first;
+ *   - y = f32(T_0 + T_1), rounded once.
+ * The pages fix no order; this one keeps the result within ~2^-50 relative
+ * of the exact sum and independent of the launch shape. */
 Q2K_API int32_t q2k_mmvq(const void* w_dev, const void* xq_dev, float* y_dev,
                  int32_t n, int32_t k, int32_t m, void* stream);
 
@@ -380,29 +392,37 @@ Q2K_API int32_t engram_rows_q8_1(const int64_t* token_map_dev, int64_t vocab,
                                  size_t xq_bytes, int32_t* err_flag_dev, void* stream);
 
 /* Which kernel runs the Q2_K x q8_1 products (q2k_mmvq, its pair, expert
- * and grouped forms, and q2k_mmq), process-wide. For tests and tuning only:
- * every kernel forms the same exact int32 block sums and an fp64 epilogue,
- * so all choices meet the product tolerance; they may differ in the last
- * bits, since their fp64 sums run in different orders.
+ * and grouped forms, q2k_mmq and q2k_block_dots), process-wide. Every kernel
+ * forms the same exact int32 block sums and follows the fixed summation
+ * order stated at q2k_mmvq, so every choice returns the same bits: the
+ * choice changes speed only.
  *   Q2K_KERNEL_AUTO (the default): a cost model measured on MI355X picks
  *     the matrix-core kernel (2..8 tokens; rows of 4, 8, 16 or 28
  *     super-blocks) or the packed-dot kernels (tokens split over waves);
  *   Q2K_KERNEL_MATRIX_CORES: the matrix-core kernel wherever it applies;
  *   Q2K_KERNEL_PACKED_DOTS: never the matrix-core kernel (more than 8
  *     tokens then run as groups of 8 on the packed-dot kernels).
- * The environment variable Q2K_MMVQ_NO_MFMA=1 sets the initial choice to
- * Q2K_KERNEL_PACKED_DOTS. Returns the previous choice, or Q2K_EINVAL for an
- * unknown one. Launches already enqueued are unaffected; a thread that
- * launches while another changes the choice gets either kernel. */
+ * Returns the previous choice, or Q2K_EINVAL for an unknown one. Launches
+ * already enqueued are unaffected; a thread that launches while another
+ * changes the choice gets either kernel (the same bits). */
 #define Q2K_KERNEL_AUTO 0
 #define Q2K_KERNEL_MATRIX_CORES 1
 #define Q2K_KERNEL_PACKED_DOTS 2
 Q2K_API int32_t q2k_set_product_kernel(int32_t choice);
 
-/* Integer stage of q2k_mmvq, exported for exact checking (same device
- * code): out_dev int32 [m, n, k/32, 2] receives, per token t, row r and
- * q8 block c, I = sum sc*q*xq and M = sum m*xq over the block's 32 values.
- * Arguments as in q2k_mmvq. */
+/* The kernel a single-matrix q2k_mmvq, q2k_block_dots or q2k_mmq of this
+ * shape runs under the current choice: Q2K_KERNEL_MATRIX_CORES or
+ * Q2K_KERNEL_PACKED_DOTS; Q2K_ESHAPE for n < 1, k not a positive multiple
+ * of 256 or m outside 1..Q2K_MMQ_MAX_M. Host only, no device call. */
+Q2K_API int32_t q2k_product_kernel(int32_t n, int32_t k, int32_t m);
+
+/* Integer stage of q2k_mmvq, exported for exact checking: out_dev int32
+ * [m, n, k/32, 2] receives, per token t, row r and q8 block c,
+ * I = sum sc*q*xq and M = sum m*xq over the block's 32 values, as formed by
+ * the kernel the product takes for this shape (q2k_product_kernel): the
+ * matrix-core kernel's own v_mfma_i32_16x16x64_i8 outputs, or the
+ * packed-dot kernels' v_dot4 sums (the device function every packed-dot
+ * product kernel uses). Arguments as in q2k_mmvq. */
 Q2K_API int32_t q2k_block_dots(const void* w_dev, const void* xq_dev, int32_t* out_dev,
                        int32_t n, int32_t k, int32_t m, void* stream);
 

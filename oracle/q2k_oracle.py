@@ -276,6 +276,57 @@ def mmvq_from_block_dots(w: np.ndarray, I: np.ndarray, M: np.ndarray, d8: np.nda
     return np.einsum("tnc,tc->tn", inner, d8.astype(np.float64))
 
 
+def mmvq_f32(w: np.ndarray, xq: np.ndarray, d8: np.ndarray) -> np.ndarray:
+    """The f32 product in the library's fixed summation order, bit for bit.
+
+    The pages fix no order for the fp64 sums of the product. The library fixes
+    one, so that every kernel returns the same bits for the same inputs, and
+    this is that order written out from the integer block sums of
+    ``block_dots`` (the plain definition is ``mmvq``; the two agree to fp64
+    rounding):
+
+    * leaf (token t, row n, super-block b, half h; q8 blocks c = 8b+4h+j):
+      fI = ((0 + d8_0*I_0) + d8_1*I_1) + d8_2*I_2) + d8_3*I_3, each product
+      exact in fp64 (24 + 18 bits), fM likewise with M, and
+      v = RN(d_b * fI) - RN(dmin_b * fM);
+    * for each half h, the pairwise tree over b = 0 .. NBP-1 (NBP the row's
+      block count rounded up to a power of two, leaves past the row +0):
+      (b, b+1) first, then pairs of pairs, and so on;
+    * y = f32(T_0 + T_1), the two halves added and rounded once to f32.
+
+    numpy's fp64 operations are IEEE round-to-nearest and are not fused, so
+    each step above is one rounding. Returns f32 [m, n].
+    """
+    I, M = block_dots(w, xq)
+    return mmvq_f32_from_block_dots(w, I, M, d8)
+
+
+def mmvq_f32_from_block_dots(w: np.ndarray, I: np.ndarray, M: np.ndarray, d8: np.ndarray):
+    """``mmvq_f32`` from integer block sums already formed by ``block_dots``
+    (int [m, n, k/32] each)."""
+    _, _, _, d, dmin = q2k_fields(w)                    # fp64 [n, nb]
+    mt, n, nq = I.shape
+    nb = nq // 8
+    nbp = 1
+    while nbp < nb:
+        nbp *= 2
+    If = I.reshape(mt, n, nb, 2, 4).astype(np.float64)
+    Mf = M.reshape(mt, n, nb, 2, 4).astype(np.float64)
+    d8r = np.asarray(d8, dtype=np.float32).astype(np.float64).reshape(mt, 1, nb, 2, 4)
+    fI = np.zeros((mt, n, nb, 2))
+    fM = np.zeros((mt, n, nb, 2))
+    for j in range(4):
+        fI = fI + d8r[..., j] * If[..., j]
+        fM = fM + d8r[..., j] * Mf[..., j]
+    a = d[None, :, :, None] * fI
+    c = dmin[None, :, :, None] * fM
+    leaves = np.zeros((mt, n, nbp, 2))
+    leaves[:, :, :nb, :] = a - c
+    while leaves.shape[2] > 1:
+        leaves = leaves[:, :, 0::2, :] + leaves[:, :, 1::2, :]
+    return (leaves[:, :, 0, 0] + leaves[:, :, 0, 1]).astype(np.float32)
+
+
 def mmvq_pair(wa, wb, xq, d8):
     """``mmvq_q2k_pair_w`` (attn_v41/decode.rs, q_kv_projections): two
     matrices against the same q8_1 rows."""

@@ -32,6 +32,7 @@ SIGNATURES = {
     "q2k_abi_version": (_I32, []),
     "q2k_last_error": (ctypes.c_char_p, []),
     "q2k_set_product_kernel": (_I32, [_I32]),
+    "q2k_product_kernel": (_I32, [_I32, _I32, _I32]),
     "q8_1_rows_bytes": (_SZ, [_I32, _I32]),
     "q8_1_rows": (_I32, [_VP, _I64, _VP, _SZ, _I32, _I32, _VP]),
     "q2k_mmvq": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
@@ -119,10 +120,20 @@ KERNEL_AUTO, KERNEL_MATRIX_CORES, KERNEL_PACKED_DOTS = 0, 1, 2
 
 
 def q2k_set_product_kernel(choice: int) -> int:
-    """Process-wide product kernel choice (tests and tuning); returns the previous one."""
+    """Process-wide product kernel choice (speed only: every choice returns
+    the same bits); returns the previous one."""
     r = int(lib().q2k_set_product_kernel(choice))
     if r < 0:
         _check("q2k_set_product_kernel", r)
+    return r
+
+
+def q2k_product_kernel(n: int, k: int, m: int) -> int:
+    """KERNEL_MATRIX_CORES or KERNEL_PACKED_DOTS: the kernel a single-matrix
+    product of this shape runs under the current choice."""
+    r = int(lib().q2k_product_kernel(n, k, m))
+    if r < 0:
+        _check("q2k_product_kernel", r)
     return r
 
 

@@ -596,6 +596,19 @@ int32_t engram_hash(const int64_t* token_map_dev, int64_t vocab, const int64_t* 
                   fn);
 }
 
+int32_t q2k_product_kernel(int32_t n, int32_t k, int32_t m) {
+  const char* fn = "q2k_product_kernel";
+  if (n < 1) return fail(Q2K_ESHAPE, "%s: n must be >= 1", fn);
+  if (int32_t r = check_k(fn, k)) return r;
+  if (m < 1 || m > Q2K_MMQ_MAX_M) return fail(Q2K_ESHAPE, "%s: m must be in 1..%d", fn, Q2K_MMQ_MAX_M);
+  q2k::MmvqLaunch a{};
+  a.n[0] = n;
+  a.njobs = 1;
+  a.k = k;
+  a.m = m;
+  return q2k::takes_mfma(a) ? Q2K_KERNEL_MATRIX_CORES : Q2K_KERNEL_PACKED_DOTS;
+}
+
 int32_t q2k_block_dots(const void* w_dev, const void* xq_dev, int32_t* out_dev, int32_t n,
                        int32_t k, int32_t m, void* stream) {
   const char* fn = "q2k_block_dots";

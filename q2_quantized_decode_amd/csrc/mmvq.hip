@@ -26,10 +26,7 @@
 // * Grid: waves take contiguous runs of row steps; workgroup w runs on XCD
 //   w % 8, so runs are numbered XCD-major and each XCD streams one
 //   contiguous eighth of the rows through its own L2.
-#include <stdlib.h>
-
 #include <atomic>
-#include <mutex>
 
 #include "q2k_device.h"
 #include "q2k_launch.h"
@@ -268,11 +265,6 @@ __device__ __forceinline__ void half_block_dots(const WHalf& w, const AHalf& a, 
   I[3] >>= 2;
 }
 
-// The lane's contribution d * sum_j d8_j I_j - dmin * sum_j d8_j M_j, in
-// fp64: d8 (f32) times I (< 2^18) and then times d (fp16) stay within 53
-// bits, so every term is exact and only the sums round (fp64 rounding of
-// terms whose f32 sum would cancel badly: post-SwiGLU activations reach
-// 10^3 while outputs cross zero).
 __device__ __forceinline__ double half_block_value(const WHalf& w, const AHalf& a) {
   int I[4], Mv[4];
   half_block_dots(w, a, I, Mv);
@@ -285,11 +277,15 @@ __device__ __forceinline__ double half_block_value(const WHalf& w, const AHalf& 
   }
   const double d = (double)fp16_bits_to_f32(w.dd & 0xffffu);
   const double dmin = (double)fp16_bits_to_f32(w.dd >> 16);
-  return d * fI - dmin * fM;
+  return half_value(d, dmin, fI, fM);
 }
 
+// Sum over a group of gs lanes holding the half blocks of one row in the
+// order h * gs/2 + b: pairs of neighbours first (the pairwise tree over the
+// row's super-blocks for each half, then the two halves), the same tree as
+// every other product kernel.
 __device__ __forceinline__ double group_sum(double v, int gs) {
-  for (int off = gs >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  for (int off = 1; off < gs; off <<= 1) v += __shfl_xor(v, off);
   return v;
 }
 
@@ -313,22 +309,30 @@ __device__ __forceinline__ double dpp_f64(double v) {
   return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-// DPP controls: the partner of lane l differs from l in bit OFF (and, for
-// the mirrors, in the bits below it): 8 -> row_mirror (l ^ 15 within 16),
-// 4 -> row_half_mirror (l ^ 7 within 8), 2 / 1 -> quad_perm.
+// DPP controls whose partner is exactly lane l ^ OFF: quad_perm [1,0,3,2]
+// and [2,3,0,1] for 1 and 2, row_ror:8 for 8 (a rotation by half of a
+// 16-lane row).
 template <int OFF> struct DppPartner;
-template <> struct DppPartner<8> { static constexpr int ctrl = 0x140; };
-template <> struct DppPartner<4> { static constexpr int ctrl = 0x141; };
-template <> struct DppPartner<2> { static constexpr int ctrl = 0x4E; };   // [2,3,0,1]
-template <> struct DppPartner<1> { static constexpr int ctrl = 0xB1; };   // [1,0,3,2]
+template <> struct DppPartner<8> { static constexpr int ctrl = 0x128; };
+template <> struct DppPartner<2> { static constexpr int ctrl = 0x4E; };
+template <> struct DppPartner<1> { static constexpr int ctrl = 0xB1; };
 
 __device__ __forceinline__ uint64_t bits64(double v) { return __builtin_bit_cast(uint64_t, v); }
 __device__ __forceinline__ double from_bits(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
+// Lane l ^ 4's value (ds_swizzle in xor mode, within 32 lanes).
+__device__ __forceinline__ double xor4_f64(double v) {
+  const uint64_t b = bits64(v);
+  const int lo = __builtin_amdgcn_ds_swizzle((int)(uint32_t)b, 0x101F);
+  const int hi = __builtin_amdgcn_ds_swizzle((int)(uint32_t)(b >> 32), 0x101F);
+  return from_bits((uint32_t)lo, (uint32_t)hi);
+}
+
 // One halving level of a transposed reduction: lanes whose bit OFF is 0 end
-// with X summed over the lane pair, the others with Y summed over the pair.
+// with X summed over the lane pair (l, l ^ OFF), the others with Y summed
+// over the pair.
 template <int OFF>
 __device__ __forceinline__ double halve(double x, double y, int lane) {
   if constexpr (OFF == 32) {
@@ -349,30 +353,37 @@ __device__ __forceinline__ double halve(double x, double y, int lane) {
     const bool up = (lane & OFF) != 0;
     const double send = up ? x : y;
     const double keep = up ? y : x;
-    return keep + dpp_f64<DppPartner<OFF>::ctrl>(send);
+    if constexpr (OFF == 4) {
+      return keep + xor4_f64(send);
+    } else {
+      return keep + dpp_f64<DppPartner<OFF>::ctrl>(send);
+    }
   }
 }
 
-// Sum eight per-lane values a[0..7] over groups of GS = 1 << GSL lanes
-// (GS >= 8) at once: three halving levels leave lane l holding the group
-// total of slot (l & (GS-1)) >> (GSL-3), the remaining levels finish the sum.
+// Sum eight per-lane values a[0..7] (eight row steps) over groups of
+// GS = 1 << GSL lanes (GS >= 8) at once, neighbours first: three halving
+// levels (lane pairs l ^ 1, l ^ 2, l ^ 4) leave lane l holding step l & 7
+// summed over its 8 lanes, and the levels l ^ 8, l ^ 16, l ^ 32 finish the
+// group. With lanes in the order h * GS/2 + b this is the pairwise tree over
+// the super-blocks of each half, then the two halves.
 template <int GSL>
 __device__ __forceinline__ double reduce8(const double a[8], int lane) {
   constexpr int GS = 1 << GSL;
   double b4[4], b2[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) b4[i] = halve<GS / 2>(a[i], a[i + 4], lane);
+  for (int i = 0; i < 4; ++i) b4[i] = halve<1>(a[2 * i], a[2 * i + 1], lane);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) b2[i] = halve<GS / 4>(b4[i], b4[i + 2], lane);
-  double v = halve<GS / 8>(b2[0], b2[1], lane);
-  if constexpr (GS / 16 >= 1) v += dpp_f64<DppPartner<(GS >= 64 ? 4 : GS / 16)>::ctrl>(v);
-  if constexpr (GS / 32 >= 1) v += dpp_f64<DppPartner<(GS >= 64 ? 2 : GS / 32)>::ctrl>(v);
-  if constexpr (GS / 64 >= 1) v += dpp_f64<DppPartner<1>::ctrl>(v);
+  for (int i = 0; i < 2; ++i) b2[i] = halve<2>(b4[2 * i], b4[2 * i + 1], lane);
+  double v = halve<4>(b2[0], b2[1], lane);
+  if constexpr (GS >= 16) v += dpp_f64<DppPartner<8>::ctrl>(v);
+  if constexpr (GS >= 32) v = halve<16>(v, v, lane);
+  if constexpr (GS >= 64) v = halve<32>(v, v, lane);
   return v;
 }
 
-// d*sum_j d8_j I_j - dmin*sum_j d8_j M_j for one lane, fp64 (exact terms).
-// dq holds d8_j with the x4 of planes 1 and 3 folded in (d8/4 is exact).
+// half_block_value for the run kernel: dq holds d8_j with the x4 of planes
+// 1 and 3 folded in (d8/4 is exact, so dq * I4 == d8 * I exactly).
 __device__ __forceinline__ double half_block_value_m1(const WHalf& w, const AHalf& a,
                                                       const double dq[4], const double dm[4]) {
   int I4[4], Mv[4];
@@ -385,7 +396,7 @@ __device__ __forceinline__ double half_block_value_m1(const WHalf& w, const AHal
   }
   const double d = (double)fp16_bits_to_f32(w.dd & 0xffffu);
   const double dmin = (double)fp16_bits_to_f32(w.dd >> 16);
-  return d * fI - dmin * fM;
+  return half_value(d, dmin, fI, fM);
 }
 
 // Weight fields of one lane at fixed 32-bit byte offsets from a uniform
@@ -579,16 +590,19 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
 
   const int k = k0;
   const int nb = k >> 8;
+  // lane l of a row group takes half h = l >> (GSL-1) of super-block
+  // b = l & (GS/2 - 1) (GS/2 is the row's block count rounded up to a power
+  // of two); lanes past the row's blocks read block 0 and add +0
   const int hb = lane & (GS - 1);
   const int prow = lane >> GSL;
-  const bool hb_ok = hb < 2 * nb;
-  const int hbc = hb_ok ? hb : 0;     // idle lanes read a valid half block
-  const int b = hbc >> 1;
-  const int h = hbc & 1;
+  const int braw = hb & (GS / 2 - 1);
+  const bool hb_ok = braw < nb;
+  const int b = hb_ok ? braw : 0;
+  const int h = hb >> (GSL - 1);
   const uint32_t rowbytes = (uint32_t)nb * kBlockBytes;
   const uint32_t step_bytes = (uint32_t)P * rowbytes;
-  const int slot = (lane & (GS - 1)) >> (GSL - 3);
-  const bool writer = (lane & ((GS >> 3) - 1)) == 0;
+  const int slot = lane & 7;                     // the step reduce8 leaves on this lane
+  const bool writer = (lane & (GS - 1)) < 8;
 
   // The run's steps are J.it + st * S, st = 0..CH-1.
   const int S = J.stride;
@@ -724,10 +738,13 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
   const int gs = 1 << p.gs_log2;
   const int P = 64 >> p.gs_log2;
   const int prow = lane >> p.gs_log2;
+  // half h = hb >> (gs_log2 - 1) of super-block hb & (gs/2 - 1), as in
+  // mmvq_m1_kernel (lanes past the row's blocks take block 0 and add +0)
   const int hb = lane & (gs - 1);
-  const bool hb_ok = hb < 2 * nb;
-  const int b = hb >> 1;
-  const int h = hb & 1;
+  const int braw = hb & ((gs >> 1) - 1);
+  const bool hb_ok = braw < nb;
+  const int b = hb_ok ? braw : 0;
+  const int h = hb >> (p.gs_log2 - 1);
   const size_t rowbytes = (size_t)nb * kBlockBytes;
 
   // token split (one-token kernel only): as in mmvq_m1_kernel
@@ -818,8 +835,15 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
   if (J.bad && lane == 0 && p.err_flag != nullptr) *p.err_flag = 1;
 }
 
-// Wide rows (more than 64 half blocks, k > 8192): one row per step, each
-// lane walks half blocks lane, lane + 64, ...; activations come from memory.
+// Wide rows (more than 64 half blocks, k > 8192): one row per step. Lane
+// l takes half h = l >> 5 of super-blocks 32c + (l & 31) for chunks
+// c = 0, 1, ...; each chunk is summed over its 32 lanes neighbours first and
+// the chunk sums are combined pairwise (a binary counter over the chunks, the
+// row's block count rounded up to a power of two), then the two halves: the
+// same tree as every other product kernel. Activations come from memory; the
+// tokens are taken one after the other (each reloads the row, from cache).
+constexpr int kWideLevels = 20;   // chunk tree depth: rows of up to 2^24 blocks
+
 template <int M, bool DOTS>
 __global__ __launch_bounds__(256) void mmvq_wide_kernel(const MmvqParams p) {
   prefetch_args(p);
@@ -831,30 +855,56 @@ __global__ __launch_bounds__(256) void mmvq_wide_kernel(const MmvqParams p) {
   if (wave >= p.total_waves) return;
   const int k = p.k;
   const int nb = k >> 8;
+  int chunks = 1;
+  while (32 * chunks < nb) chunks <<= 1;
+  int top = 0;
+  while ((1 << top) < chunks) ++top;
   const size_t rowbytes = (size_t)nb * kBlockBytes;
+  const int h = lane >> 5;
+  const int jl = lane & 31;
   const WaveJob J = resolve_wave<M>(p, wave, 1);
   for (int row = J.it; row < J.it_end; row += J.stride) {
-    double part[M];
+#pragma unroll 1
+    for (int t = 0; t < M; ++t) {
+      double stk[kWideLevels];
 #pragma unroll
-    for (int t = 0; t < M; ++t) part[t] = 0.0;
-    for (int hb = lane; hb < 2 * nb; hb += 64) {
-      const int b = hb >> 1, h = hb & 1;
-      const WHalf w = load_whalf(J.w + row * rowbytes + b * kBlockBytes, h);
+      for (int l = 0; l < kWideLevels; ++l) stk[l] = 0.0;
+      for (int c = 0; c < chunks; ++c) {
+        const int b = 32 * c + jl;
+        double v = 0.0;
+        if (b < nb) {
+          const WHalf w = load_whalf(J.w + row * rowbytes + b * kBlockBytes, h);
+          const AHalf a = load_ahalf(J.x, t, b, h);
+          if constexpr (DOTS) {
+            store_dots(p.dots, w, a, t, J.n, row, k, b, h);
+          } else {
+            v = half_block_value(w, a);
+          }
+        }
+        if constexpr (!DOTS) {
+          for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off);
+          // binary counter: chunk c closes the subtrees of its trailing ones
+          bool carry = true;
 #pragma unroll
-      for (int t = 0; t < M; ++t) {
-        const AHalf a = load_ahalf(J.x, t, b, h);
-        if constexpr (DOTS) {
-          store_dots(p.dots, w, a, t, J.n, row, k, b, h);
-        } else {
-          part[t] += half_block_value(w, a);
+          for (int l = 0; l < kWideLevels; ++l) {
+            if (carry) {
+              if ((c >> l) & 1) {
+                v = stk[l] + v;
+              } else {
+                stk[l] = v;
+                carry = false;
+              }
+            }
+          }
         }
       }
-    }
-    if constexpr (!DOTS) {
+      if constexpr (!DOTS) {
+        double tot = 0.0;
 #pragma unroll
-      for (int t = 0; t < M; ++t) {
-        const double v = group_sum(part[t], 64);
-        if (lane == 0) J.y[(int64_t)t * J.ldy + row] = J.bad ? quiet_nan() : (float)v;
+        for (int l = 0; l < kWideLevels; ++l)
+          if (l == top) tot = stk[l];
+        tot += __shfl_xor(tot, 32);
+        if (lane == 0) J.y[(int64_t)t * J.ldy + row] = J.bad ? quiet_nan() : (float)tot;
       }
     }
   }
@@ -863,47 +913,21 @@ __global__ __launch_bounds__(256) void mmvq_wide_kernel(const MmvqParams p) {
 
 namespace {
 
+// Launch shapes, fixed at compile time (measured on MI355X). None of them
+// changes a result bit: every kernel's result is independent of its grid,
+// run length and ring depth, and all kernels follow one summation order.
 struct Tuning {
-  int waves_per_cu = 16;
-  int depth = 2;
-  bool fast_m1 = true;
-  int interleave = 1;
-  int ring = 4;
-  int run = 0;       // m = 1 run length override (8, 16, 32); 0 = from waves_per_cu
-  int m1_waves_per_cu = 4;
-  int64_t m1_min_steps = 2048;
+  int waves_per_cu = 16;        // one-step kernel: waves per CU
+  int depth = 2;                // one-step kernel: row steps in flight per wave
+  int interleave = 1;           // a matrix's waves take its row steps round-robin
+  int ring = 4;                 // run kernel: weight steps in flight per wave
+  int m1_waves_per_cu = 4;      // run kernel: waves per CU (one per SIMD)
+  int64_t m1_min_steps = 2048;  // run kernel from this many (row step, token) pairs
 };
 
-const Tuning& tuning() {
-  static Tuning t;
-  static std::once_flag once;
-  std::call_once(once, [] {
-    if (const char* s = getenv("Q2K_MMVQ_WAVES_PER_CU")) {
-      const int v = atoi(s);
-      if (v >= 1 && v <= 64) t.waves_per_cu = v;
-    }
-    if (const char* s = getenv("Q2K_MMVQ_GENERIC_M1")) t.fast_m1 = atoi(s) == 0;
-    if (const char* s = getenv("Q2K_MMVQ_INTERLEAVE")) t.interleave = atoi(s) != 0;
-    if (const char* s = getenv("Q2K_MMVQ_M1_MIN_STEPS")) t.m1_min_steps = atoll(s);
-    if (const char* s = getenv("Q2K_MMVQ_M1_WAVES_PER_CU")) {
-      const int v = atoi(s);
-      if (v >= 1 && v <= 64) t.m1_waves_per_cu = v;
-    }
-    if (const char* s = getenv("Q2K_MMVQ_RUN")) {
-      const int v = atoi(s);
-      if (v == 8 || v == 16 || v == 32) t.run = v;
-    }
-    if (const char* s = getenv("Q2K_MMVQ_RING")) {
-      const int v = atoi(s);
-      if (v == 2 || v == 4 || v == 8) t.ring = v;
-    }
-    if (const char* s = getenv("Q2K_MMVQ_DEPTH")) {
-      const int v = atoi(s);
-      if (v == 1 || v == 2 || v == 4) t.depth = v;
-    }
-  });
-  return t;
-}
+constexpr Tuning kTuning{};
+
+const Tuning& tuning() { return kTuning; }
 
 int cu_count() {
   static int counts[64];
@@ -1010,33 +1034,26 @@ void dispatch_wide(const MmvqParams& p, dim3 grid, bool dots, hipStream_t s) {
 
 }  // namespace
 
-// Product kernel choice (q2k_set_product_kernel): -1 until first read, then
-// 0 automatic, 1 matrix cores where supported, 2 packed dots only. The
-// variable Q2K_MMVQ_NO_MFMA=1 makes the initial choice 2.
-static std::atomic<int> g_product_kernel{-1};
+// Product kernel choice (q2k_set_product_kernel): 0 automatic (the cost
+// model), 1 matrix cores where supported, 2 packed dots only. Every choice
+// returns the same bits (one summation order in every kernel); it only
+// changes which kernel runs.
+static std::atomic<int> g_product_kernel{0};
 
-static int product_kernel() {
-  int c = g_product_kernel.load(std::memory_order_relaxed);
-  if (c < 0) {
-    const char* s = getenv("Q2K_MMVQ_NO_MFMA");
-    int init = (s && atoi(s) != 0) ? 2 : 0;
-    g_product_kernel.compare_exchange_strong(c, init, std::memory_order_relaxed);
-    c = g_product_kernel.load(std::memory_order_relaxed);
-  }
-  return c;
-}
+static int product_kernel() { return g_product_kernel.load(std::memory_order_relaxed); }
 
 int set_product_kernel(int choice) {
-  const int prev = product_kernel();
-  g_product_kernel.store(choice, std::memory_order_relaxed);
-  return prev;
+  return g_product_kernel.exchange(choice, std::memory_order_relaxed);
+}
+
+bool takes_mfma(const MmvqLaunch& a) {
+  const int choice = product_kernel();
+  return choice == 1 ? (a.m >= 2 && mfma_supports(a.k)) : choice == 2 ? false : mfma_preferred(a);
 }
 
 hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
-  const int choice = product_kernel();
-  const bool mfma = choice == 1   ? (a.dots == nullptr && a.m >= 2 && mfma_supports(a.k))
-                    : choice == 2 ? false
-                                  : mfma_preferred(a);
+  // the integer stage (dots) goes to the kernel the product would take
+  const bool mfma = takes_mfma(a);
   if (a.sg != nullptr && (mfma || a.m > kMaxM)) {
     const hipError_t e = launch_swiglu_q8_1_rows(a.sg, a.su, nullptr, const_cast<void*>(a.xq),
                                                  a.n_ids * a.m, a.k, stream);
@@ -1125,7 +1142,7 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   p.tsplit = tsplit;
   // The run kernel (runs of 8 to 32 steps per wave) needs enough steps to
   // fill the chip; smaller launches take one step per wave.
-  const bool m1_path = a.dots == nullptr && !wide && gs_log2 >= 3 && tu.fast_m1 &&
+  const bool m1_path = a.dots == nullptr && !wide && gs_log2 >= 3 &&
                        total_iters * tsplit >= tu.m1_min_steps;
   // A one-token launch that quantises its own input (one bf16 row shared by
   // every matrix) does it in the run kernel's prologue when the product
@@ -1142,7 +1159,6 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   if (m1_path) {
     // runs of 8, 16 or 32 steps (compile-time run lengths of the m = 1 kernel)
     chunk = chunk <= 8 ? 8 : chunk <= 16 ? 16 : 32;
-    if (tu.run > 0) chunk = tu.run;
   }
   p.chunk = (int)chunk;
   int64_t total_waves = 0;

@@ -1,44 +1,47 @@
-// Q2_K x q8_1 product for 2..8 tokens on the CDNA4 matrix cores.
+// Q2_K x q8_1 product for 2..8 tokens (and, by groups of 8, any number of
+// tokens) on the CDNA4 matrix cores.
 //
-// The GGUF Q2_K super-block and the q8_1 block dot it is multiplied with are
-// those of the llama.cpp k-quant pages (block_q2_K layout; the q2_K x q8_1
-// vector dot). With 8 tokens the packed-dot formulation spends two int8 dot
-// instructions per 4 weights on the vector ALUs; here the integer block sums
-// go through v_mfma_i32_16x16x64_i8 and the min term through
-// v_mfma_f64_4x4x4f64, so the vector ALUs only unpack the 2-bit weights and
-// scale the per-block integer results.
+// The weights are GGUF Q2_K super-blocks as the file ships them (engram_v41.rs:
+// ENGRAM_ROW_BYTES = 84 bytes per 256 weights, EngramLayerWeights::wkv_q2k);
+// the activations are this library's q8_1 rows. The pages' own kernels for
+// this product (moe_v41/init.rs: kquant_mmvq_q2_k_w, the experts variants,
+// metrale_q2_k_mmq128_*) are CUDA warp kernels whose source is not shown.
+// With 8 tokens a packed-dot formulation spends two int8 dot instructions per
+// 4 weights on the vector ALUs; here both exact integer block sums go through
+// v_mfma_i32_16x16x64_i8 and the vector ALUs unpack the 2-bit weights and
+// run the fp64 epilogue.
 //
 // * Tile: one wave computes 16 weight rows x 8 token slots over a range of
 //   super-blocks, one 256-weight super-block b at a time. Weights are the B
 //   operand: lane (g = lane/16, j = lane%16) loads only its own row r0 + j
 //   (16 bytes of qs, 8 scale bytes, d/dmin), 28 bytes per super-block.
-// * I term (exact int32): plane p = 0..3 of a super-block is one MFMA with
-//   K = 64 weights; K-group g holds the 16 weights 128(g>>1) + 32p + 16(g&1)
-//   + 0..15, i.e. qs bytes 16g..16g+15, bits 2p..2p+1, all in sub-block
-//   s = 8(g>>1) + 2p + (g&1), so B = sc_s * q (<= 45, a v_perm_b32 lookup of
-//   q in {0, sc, 2sc, 3sc}). The A operand (activations) is block diagonal:
-//   A-row a = token (a&7), half (a>>3) carries that token's quants of q8
-//   block 4(a>>3) + p in the two K-groups of that half and zeros elsewhere,
-//   so the output (A-row, weight row) is exactly I = sum sc*q*xq of one
-//   (token, q8 block, row). Each I is scaled by its d8 in fp64 and each
-//   super-block's sum by the row's d.
-// * M term: dmin * sum_s m_s * (d8*S)_s per super-block, the sum on two
-//   chains of four fp64 MFMAs (K = 4 sub-blocks each: MFMA i, k-index g is
-//   sub-block 8(g>>1) + 2i + (g&1), the scale byte a lane already holds),
-//   B = m (exact), A = d8*S of the activations (exact); one fp64 fma per
-//   chain then adds dmin times the sum to the row's running M sum. Its
-//   A-rows are arranged so that its output lands on the same lane and
-//   register as the I output of the same token.
-// * Activations of the workgroup's matrix (8 token slots of quants, d8 and
-//   d8*S in fp64, plus an all-zero slot) are staged once in LDS; the waves of
-//   a workgroup take eight consecutive tiles of one matrix.
+// * Integer sums: plane p = 0..3 of a super-block is two MFMAs with K = 64
+//   weights; K-group g holds the 16 weights 128(g>>1) + 32p + 16(g&1) + 0..15,
+//   i.e. qs bytes 16g..16g+15 at bits 2p..2p+1, all in sub-block
+//   s = 8(g>>1) + 2p + (g&1). For I the B operand is sc_s * q (<= 45, a
+//   v_perm_b32 lookup of q in {0, sc, 2sc, 3sc}); for M it is m_s in every
+//   byte. The A operand (activations) is block diagonal: A-row a = token
+//   (a&7), half (a>>3) carries that token's quants of q8 block 4(a>>3) + p in
+//   the two K-groups of that half and zeros elsewhere, so each output is
+//   exactly one I (or M) of one (token, q8 block, row).
+// * Epilogue: the library's fixed summation order (q2k_device.h, half_value):
+//   lane (g, j) holds half h = g>>1 of tokens 4(g&1) + 0..3, so the four
+//   planes of a super-block are that half block's four q8 blocks; the leaf
+//   value is formed exactly as in the packed-dot kernels, the leaves of the
+//   wave's super-blocks are combined pairwise, the two waves of a tile meet
+//   through LDS (left + right subtree) and the halves across lanes g, g ^ 2.
+// * Activations of the workgroup's matrix (8 token slots of quants and fp64
+//   d8, plus an all-zero slot) are staged once in LDS; the waves of a
+//   workgroup take eight consecutive tiles of one matrix.
 //
-// A workgroup is sixteen waves: two per tile, each taking half of the row,
-// their sums combined through LDS in a fixed order. Four waves per SIMD hide
-// the dependency chains of one tile better than whole-row waves with deeper
-// software pipelining did (measured).
+// A workgroup is sixteen waves: two per tile, wave 0 taking super-blocks
+// [0, NBP/2) in order and wave 1 the rest [NBP/2, NB) from the end (NBP: NB
+// rounded up to a power of two), so that each 128-byte line shared by two
+// super-blocks (84-byte blocks straddle lines, also at the split and from one
+// row to the next) is read by both waves at about the same time and comes
+// from L2 the second time. Four waves per SIMD hide the dependency chains of
+// one tile.
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "q2k_device.h"
 #include "q2k_launch.h"
@@ -49,16 +52,14 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef double v4d __attribute__((ext_vector_type(4)));
-typedef double v2d __attribute__((ext_vector_type(2)));
 
 constexpr int kSlots = 8;              // token slots of a tile (m <= 8; unused slots are zero)
 constexpr int kTabSlots = kSlots + 1;  // plus one all-zero slot
 constexpr int kTilesPerWg = 8;
 constexpr uint32_t kMfmaMaxLds = 160 * 1024;
 constexpr int kThreads = 2 * kTilesPerWg * kWave;   // two waves per tile
-// The second-half waves hand 4 fp64 partial sums per lane of their tile's
-// lanes g < 2 to the first-half waves.
-constexpr uint32_t kXchgBytes = kTilesPerWg * 32 * 4 * 8;
+// The second waves hand their 4 fp64 subtree sums per lane to the first.
+constexpr uint32_t kXchgBytes = kTilesPerWg * kWave * 4 * 8;
 
 struct MfmaParams {
   const uint8_t* w[kMaxPlainJobs];   // plain: job matrices; expert mode: the bases
@@ -72,6 +73,7 @@ struct MfmaParams {
   int32_t x_per_id;
   int64_t expert_stride;
   int32_t* err_flag;
+  int32_t* dots;                     // DOTS kernel: int32 (I, M) per (token, row, q8 block)
   int32_t groups;                    // grouped mode when > 0
   int32_t wgs_per_job;               // expert and grouped modes
   int32_t total_wgs;
@@ -89,34 +91,29 @@ __device__ __forceinline__ void prefetch_args(const MfmaParams& p) {
                "s"(p.m), "s"(p.tgroups), "s"(p.g8));
 }
 
+// Row blocks rounded up to a power of two (the summation tree's width).
+__host__ __device__ constexpr int pow2_ceil(int v) {
+  int r = 1;
+  while (r < v) r <<= 1;
+  return r;
+}
+
 // LDS layout (bytes) for row length k:
 //   quants  [kTabSlots][k + 16]   slot stride padded by 16 bytes so the eight
 //                                 token slots fall on different banks
 //   d8      k/32 x kSlots fp64    in the order of d8_index
-//   d8*S    k/16 x kSlots fp64    in the order of at_index
+//   xchg    kXchgBytes            the second waves' subtree sums
 __host__ __device__ constexpr uint32_t q_stride(int k) { return (uint32_t)k + 16u; }
 __host__ __device__ constexpr uint32_t lds_d8_off(int k) { return kTabSlots * q_stride(k); }
-__host__ __device__ constexpr uint32_t lds_at_off(int k) {
+__host__ __device__ constexpr uint32_t lds_xchg_off(int k) {
   return lds_d8_off(k) + (uint32_t)(k / 32) * kSlots * 8u;
 }
-__host__ __device__ constexpr uint32_t lds_bytes(int k) {
-  return lds_at_off(k) + (uint32_t)(k / 16) * kSlots * 8u;
-}
+__host__ __device__ constexpr uint32_t lds_bytes(int k) { return lds_xchg_off(k) + kXchgBytes; }
 // Element index (fp64) of d8 of q8 block blk (within the row) of token t:
 // [super-block][plane p][half h][token], so the four 32-byte reads of one
 // plane (K-groups g = 2h + token/4) are 128 consecutive bytes.
 __device__ __forceinline__ uint32_t d8_index(uint32_t blk, uint32_t t) {
   return (((blk >> 3) * 4u + (blk & 3u)) * 2u + ((blk >> 2) & 1u)) * 8u + t;
-}
-// Element index (fp64) of d8*S of sub-block s (within the row) of token t:
-// [super-block][MFMA i][K-group g][token & 3][token >> 2], where sub-block
-// s = 16b + 8(g>>1) + 2i + (g&1). A lane's two A values of one MFMA pair
-// (tokens j and j + 4) are one 16-byte read, and the sixteen distinct reads
-// of a pair are 256 consecutive bytes.
-__device__ __forceinline__ uint32_t at_index(uint32_t s, uint32_t t) {
-  const uint32_t sl = s & 15u;
-  const uint32_t g = 2u * (sl >> 3) + (sl & 1u), i = (sl & 7u) >> 1;
-  return ((((s >> 4) * 4u + i) * 4u + g) * 4u + (t & 3u)) * 2u + (t >> 2);
 }
 
 template <typename T>
@@ -216,7 +213,6 @@ struct StageRegs {
   static constexpr int C4 = k / 128;
   u32x4 qv[QIT];
   f32x4 d8v;
-  u32x4 sv;
 };
 
 template <int k, int THREADS>
@@ -235,12 +231,10 @@ __device__ __forceinline__ StageRegs<k, THREADS> stage_load(const XView& X, int 
     const bool ok = idx < kSlots * SR::QC && t < m;
     r.qv[it] = gload<u32x4>(ok ? X.q + t * X.stride + 16 * e : X.q);
   }
-  // Scales and half-block sums: thread (token t2, group c4) takes q8 blocks
-  // 4c4..4c4+3, i.e. sub-blocks 8c4..8c4+7.
+  // Scales: thread (token t2, group c4) takes q8 blocks 4c4..4c4+3.
   const int t2 = tid / SR::C4, c4 = tid - (tid / SR::C4) * SR::C4;
   const bool sv_ok = tid < kSlots * SR::C4 && t2 < m;
   r.d8v = gload<f32x4>(sv_ok ? X.s + t2 * X.stride + 16 * c4 : X.s);
-  r.sv = gload<u32x4>(sv_ok ? X.m + t2 * X.stride + 16 * c4 : X.m);
   return r;
 }
 
@@ -261,14 +255,8 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, const StageRegs<k, THR
   if (tid < kSlots * SR::C4) {
     const bool live = t2 < m;
     double* d8t = reinterpret_cast<double*>(lds + lds_d8_off(k));
-    double* at = reinterpret_cast<double*>(lds + lds_at_off(k));
 #pragma unroll
     for (int i = 0; i < 4; ++i) d8t[d8_index(4 * c4 + i, t2)] = live ? (double)r.d8v[i] : 0.0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int16_t sum = (int16_t)(r.sv[j >> 1] >> (16 * (j & 1)));
-      at[at_index(8 * c4 + j, t2)] = live ? (double)r.d8v[j >> 1] * (double)sum : 0.0;
-    }
   }
 }
 
@@ -282,9 +270,8 @@ __device__ __forceinline__ void lds_barrier() {
 // Per-lane constants of a tile.
 struct Lane {
   int g, j16;
-  uint32_t a_base;    // I-term A operand (activation quants)
+  uint32_t a_base;    // A operand (activation quants)
   uint32_t d8_base;   // d8 of the lane's four outputs
-  uint32_t at_base;   // M-term A operand (d8*S)
   uint32_t sc_shift;  // 8 * (g & 1)
 };
 
@@ -295,16 +282,12 @@ __device__ __forceinline__ Lane lane_consts() {
   L.g = lane >> 4;
   L.j16 = lane & 15;
   const int g = L.g, j16 = L.j16;
-  // I-term A: A-row j16 = token (j16 & 7), half (j16 >> 3); K-group g is
-  // non-zero only in its own half.
+  // A: A-row j16 = token (j16 & 7), half (j16 >> 3); K-group g is non-zero
+  // only in its own half (other lanes read the all-zero slot).
   const uint32_t a_slot = ((g >> 1) == (j16 >> 3)) ? (uint32_t)(j16 & 7) : (uint32_t)kSlots;
   L.a_base = opaque_v(a_slot * q_stride(k) + 128u * (g >> 1) + 16u * (g & 1));
   // d8 of the lane's four outputs: tokens 4(g&1) + 0..3 of q8 block 8b + 4(g>>1) + p.
   L.d8_base = opaque_v(lds_d8_off(k) + 32u * (uint32_t)g);
-  // M-term A (4x4x4 MFMA, four blocks): lane 16k + 4blk + i holds A[blk][i][k]
-  // = d8*S of token i (+4 for the second MFMA of a pair) and k-index k = g,
-  // which is sub-block 8(g>>1) + 2i' + (g&1) of MFMA pair i'.
-  L.at_base = opaque_v(lds_at_off(k) + 16u * (4u * (uint32_t)g + (uint32_t)(j16 & 3)));
   L.sc_shift = 8u * (g & 1);
   return L;
 }
@@ -345,43 +328,111 @@ __device__ __forceinline__ v4i plane_weights(const u32x4& qs, uint32_t scw, uint
   return wq;
 }
 
-// Final sums of a tile: lanes g and g ^ 2 hold the two q8 halves of the same
-// tokens (I term); the M term of token t, row j16 sits on lane 16(t & 3) + j16,
-// in accM0 for t < 4 and accM1 otherwise. Gives the row value of token 4g + i
-// on lanes g < 2.
-__device__ __forceinline__ void tile_sums(const double* yI, double accM0, double accM1, const Lane& L,
-                                          double* yv) {
+// The subtree sums of one wave of a tile: super-blocks [KH * HB, KH * HB +
+// HB) with HB = NBP/2 leaves, the leaves past the row (wave 1 only) +0.
+// Wave 0 walks its blocks forward, wave 1 backward; a binary counter over
+// the visiting order combines each pair of subtrees as soon as both exist
+// (the same pairwise tree either way: addition is commutative). Writes the
+// four tokens' sums to tot; with DOTS also every (I, M) of the lane.
+template <int NB, int R, int KH, bool DOTS>
+__device__ __forceinline__ void tile_half(const uint8_t* lds, const uint8_t* Wrow,
+                                          const BlkOffsets& off, const Lane& L, Blk (&ring)[R],
+                                          double tot[4], int32_t* dots, int m, int n, int row) {
+  constexpr int NBP = pow2_ceil(NB);
+  constexpr int HB = NBP / 2;
+  constexpr int NR = KH == 0 ? HB : NB - HB;     // real blocks of this wave
+  constexpr int PAD = HB - NR;                   // leading +0 leaves (wave 1)
+  constexpr int LV = __builtin_ctz(HB) + 1;      // counter levels
+  constexpr int k = NB * kBlockWeights;
+  double stk[LV][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int src = 16 * i + L.j16;
-    const double m0 = __shfl(accM0, src);
-    const double m1 = __shfl(accM1, src);
-    yv[i] = yI[i] + __shfl_xor(yI[i], 32) - (L.g == 0 ? m0 : m1);
-  }
-}
-
-__device__ __forceinline__ void store_tile(const Job& J, int m, int r0, const Lane& L, const double* yv) {
+  for (int c = 0; c < HB; ++c) {
+    double v[4];
+    if (c < PAD) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int token = 4 * L.g + i;
-    const int row = r0 + L.j16;
-    if (L.g < 2 && token < m && row < J.n) J.Y[(int64_t)token * J.ldy + row] = J.bad ? quiet_nan() : (float)yv[i];
+      for (int i = 0; i < 4; ++i) v[i] = 0.0;
+    } else {
+      const int q = c - PAD;                               // q-th real block visited
+      const int b = KH == 0 ? q : NB - 1 - q;              // its index in the row
+      const Blk cur = ring[q % R];
+      if (q + R < NR) {
+        const int bn = KH == 0 ? q + R : NB - 1 - (q + R);
+        ring[q % R] = load_blk(Wrow + bn * kBlockBytes, off);
+      }
+      double fI[4] = {0.0, 0.0, 0.0, 0.0}, fM[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int pl = 0; pl < 4; ++pl) {
+        const v4i aq = lds_load<v4i>(lds, L.a_base + 256u * b + 32u * pl);
+        const uint32_t scw = cur.sc[pl >> 1], so = L.sc_shift + 16u * (pl & 1);
+        const v4i wq = pl == 0 ? plane_weights<0>(cur.qs, scw, so)
+                     : pl == 1 ? plane_weights<1>(cur.qs, scw, so)
+                     : pl == 2 ? plane_weights<2>(cur.qs, scw, so)
+                               : plane_weights<3>(cur.qs, scw, so);
+        const int mb = (int)(__builtin_amdgcn_ubfe(scw, so + 4u, 4) * 0x01010101u);
+        const v4i wm = v4i{mb, mb, mb, mb};
+        const v4i cI = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, wq, v4i{0, 0, 0, 0}, 0, 0, 0);
+        const v4i cM = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, wm, v4i{0, 0, 0, 0}, 0, 0, 0);
+        const v4d d8 = lds_load<v4d>(lds, L.d8_base + 512u * b + 128u * pl);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          fI[i] = fma(d8[i], (double)cI[i], fI[i]);
+          fM[i] = fma(d8[i], (double)cM[i], fM[i]);
+        }
+        if constexpr (DOTS) {
+          const int c8 = 8 * b + 4 * (L.g >> 1) + pl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 4 * (L.g & 1) + i;
+            if (t < m && row < n)
+              *reinterpret_cast<u32x2*>(dots + (((int64_t)t * n + row) * (k / 32) + c8) * 2) =
+                  u32x2{(uint32_t)cI[i], (uint32_t)cM[i]};
+          }
+        }
+      }
+      const double d = (double)fp16_bits_to_f32(cur.dd & 0xffffu);
+      const double dmin = (double)fp16_bits_to_f32(cur.dd >> 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = half_value(d, dmin, fI[i], fM[i]);
+    }
+    // binary counter over the visiting order: visit c closes the subtrees
+    // of its trailing one bits
+    int lvl = 0;
+#pragma unroll
+    for (int l = 0; l < LV - 1; ++l) {
+      if (((c >> l) & 1) == 0) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = stk[l][i] + v[i];
+      lvl = l + 1;
+    }
+    // Pin the new subtree sum here: otherwise every super-block's epilogue
+    // is sunk to its first use, keeping the MFMA results live.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(v[i]));
+#pragma unroll
+    for (int l = 0; l < LV; ++l)
+      if (l == lvl) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stk[l][i] = v[i];
+      }
+    __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tot[i] = stk[LV - 1][i];
 }
 
 }  // namespace
 
-// Sixteen waves per workgroup: wave w takes tile w & 7 over super-blocks
-// [(w >> 3) NB/2, ((w >> 3) + 1) NB/2). Four waves per SIMD hide the
-// latencies that one tile's dependency chains leave; the second-half sums are
-// added to the first half's through LDS in a fixed order, so the result does
-// not depend on timing.
+// Sixteen waves per workgroup: wave w takes tile w & 7, super-block half
+// w >> 3 (see tile_half). The first waves add the second waves' subtree sums
+// (received through LDS) to their own, then the two halves are added across
+// lanes g and g ^ 2, so the result does not depend on timing and is the same
+// as the packed-dot kernels'.
 //
 // The leading scalar arguments describe the whole launch when it is one
 // matrix (plain != 0); they are preloaded into SGPRs at wave launch
 // (kernel-argument preloading), so that case starts its loads without
 // reading the argument block.
-template <int NB, int R>
+template <int NB, int R, bool DOTS>
 __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const uint8_t* w0, const uint8_t* xq0,
                                                              float* y0, int32_t n0, int32_t m_all,
                                                              int32_t tgroups, int32_t total_wgs,
@@ -389,8 +440,8 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const uint8_t* w0, 
                                                              const MfmaParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int k = NB * kBlockWeights;
-  constexpr int NBH = NB / 2;
-  static_assert(NB % 2 == 0, "row split in two halves");
+  constexpr int HB = pow2_ceil(NB) / 2;
+  static_assert(NB > HB && NB <= 2 * HB, "two waves per tile");
   constexpr uint32_t rowbytes = (uint32_t)NB * kBlockBytes;
   const int wgi = (blockIdx.x & 7) * g8 + (blockIdx.x >> 3);   // XCD-major workgroup index
   if (wgi >= total_wgs) return;                                // whole workgroup
@@ -430,90 +481,54 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const uint8_t* w0, 
   const int r0 = (active ? tile_raw : tiles - 1) * 16;
   const Lane L = lane_consts<k>();
   const uint32_t lrow = (uint32_t)(min(r0 + L.j16, J.n - 1) - r0);
-  const int b0 = kh * NBH;
-  const uint8_t* Wt = J.W + (size_t)r0 * rowbytes + (size_t)b0 * kBlockBytes;
+  const uint8_t* Wt = J.W + (size_t)r0 * rowbytes;
   const BlkOffsets off{opaque_v(lrow * rowbytes + 16u + 16u * L.g), opaque_v(lrow * rowbytes + 8u * (L.g >> 1)),
                        opaque_v(lrow * rowbytes + 80u)};
   const StageRegs<k, kThreads> staged = stage_load<k, kThreads>(J.X, m);
+  // the first R blocks of this wave's visiting order
   Blk ring[R];
+  if (kh == 0) {
 #pragma unroll
-  for (int b = 0; b < R; ++b)
-    if (b < NBH) ring[b] = load_blk(Wt + b * kBlockBytes, off);
+    for (int q = 0; q < R; ++q) ring[q] = load_blk(Wt + q * kBlockBytes, off);
+  } else {
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+      if (q < NB - HB) ring[q] = load_blk(Wt + (NB - 1 - q) * kBlockBytes, off);
+  }
 
   stage_store<k, kThreads>(lds, staged, m);
   lds_barrier();
 
-  double yv[4] = {0.0, 0.0, 0.0, 0.0};
+  double tot[4] = {0.0, 0.0, 0.0, 0.0};
+  const int row = r0 + L.j16;
   if (active) {
-    // M term on v_mfma_f64_4x4x4f64 (four 4x4 blocks): block blk = weight rows
-    // 4blk..4blk+3, rows of A = tokens 0..3 (sM0, then accM0) or 4..7 (sM1,
-    // accM1), K = four sub-blocks. B[blk][k][j] sits on lane 16k + 4blk + j = (g, row j16): the
-    // lane's own row and one of its own scale bytes. D[blk][i][j] lands on
-    // lane 16i + 4blk + j: token i (+4), row j16. Unlike the 16x16x4 form it
-    // wastes no rows on absent tokens, and an fp64 MFMA stalls the vector ALU
-    // for its whole duration.
-    double accM0 = 0.0, accM1 = 0.0;
-    double yI[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int bb = 0; bb < NBH; ++bb) {
-      const int b = b0 + bb;   // super-block index within the row (LDS operands)
-      const Blk cur = ring[bb % R];
-      if (bb + R < NBH) ring[bb % R] = load_blk(Wt + (bb + R) * kBlockBytes, off);
-
-      const double dmin = (double)fp16_bits_to_f32(cur.dd >> 16);
-      // sum_s m_s (d8*S)_s of this super-block (exact terms), then times dmin
-      double sM0 = 0.0, sM1 = 0.0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t mb = __builtin_amdgcn_ubfe(cur.sc[i >> 1], L.sc_shift + 16u * (i & 1) + 4u, 4);
-        const v2d a = lds_load<v2d>(lds, L.at_base + 1024u * b + 256u * i);
-        const double a0 = a[0], a1 = a[1];
-        const double wm = (double)mb;
-        sM0 = __builtin_amdgcn_mfma_f64_4x4x4f64(a0, wm, sM0, 0, 0, 0);
-        sM1 = __builtin_amdgcn_mfma_f64_4x4x4f64(a1, wm, sM1, 0, 0, 0);
-      }
-      accM0 = fma(dmin, sM0, accM0);
-      accM1 = fma(dmin, sM1, accM1);
-      double accI[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int pl = 0; pl < 4; ++pl) {
-        const v4i aq = lds_load<v4i>(lds, L.a_base + 256u * b + 32u * pl);
-        const uint32_t scw = cur.sc[pl >> 1], off = L.sc_shift + 16u * (pl & 1);
-        const v4i wq = pl == 0 ? plane_weights<0>(cur.qs, scw, off)
-                     : pl == 1 ? plane_weights<1>(cur.qs, scw, off)
-                     : pl == 2 ? plane_weights<2>(cur.qs, scw, off)
-                               : plane_weights<3>(cur.qs, scw, off);
-        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, wq, v4i{0, 0, 0, 0}, 0, 0, 0);
-        const v4d d8 = lds_load<v4d>(lds, L.d8_base + 512u * b + 128u * pl);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) accI[i] = fma(d8[i], (double)c[i], accI[i]);
-      }
-      const double d = (double)fp16_bits_to_f32(cur.dd & 0xffffu);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) yI[i] = fma(d, accI[i], yI[i]);
-      // Pin the running sums here: otherwise every super-block's epilogue is
-      // sunk to the final store, keeping all MFMA results live.
-#pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(yI[i]));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    tile_sums(yI, accM0, accM1, L, yv);
+    if (kh == 0)
+      tile_half<NB, R, 0, DOTS>(lds, Wt, off, L, ring, tot, p.dots, m, J.n, row);
+    else
+      tile_half<NB, R, 1, DOTS>(lds, Wt, off, L, ring, tot, p.dots, m, J.n, row);
   }
 
-  // Second half -> LDS -> first half. The exchange area follows the tables.
-  double* xchg = reinterpret_cast<double*>(lds + lds_bytes(k));
-  const int slot = (tw * 32 + (int)(threadIdx.x & 31)) * 4;
-  if (kh == 1 && active && L.g < 2) {
+  // Second waves -> LDS -> first waves: left + right subtree, then the halves.
+  double* xchg = reinterpret_cast<double*>(lds + lds_xchg_off(k));
+  const int slot = (tw * kWave + (int)(threadIdx.x & 63)) * 4;
+  if (kh == 1 && active) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xchg[slot + i] = yv[i];
+    for (int i = 0; i < 4; ++i) xchg[slot + i] = tot[i];
   }
   lds_barrier();
-  if (kh == 0 && active) {
-    if (L.g < 2) {
+  if (kh == 0 && active && !DOTS) {
+    double yv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) yv[i] += xchg[slot + i];
+    for (int i = 0; i < 4; ++i) {
+      const double t = tot[i] + xchg[slot + i];
+      yv[i] = t + __shfl_xor(t, 32);
     }
-    store_tile(J, m, r0, L, yv);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int token = 4 * L.g + i;
+      if (L.g < 2 && token < m && row < J.n)
+        J.Y[(int64_t)token * J.ldy + row] = J.bad ? quiet_nan() : (float)yv[i];
+    }
   }
   if (J.bad && threadIdx.x == 0 && p.err_flag != nullptr) *p.err_flag = 1;
 }
@@ -532,7 +547,7 @@ int nb_slot(int nb) {
   }
 }
 
-template <int NB>
+template <int NB, bool DOTS>
 hipError_t launch_nb(const MfmaParams& p, dim3 gd, size_t shm, hipStream_t stream) {
   // More than 64 KB of dynamic LDS must be allowed explicitly, once per
   // device and kernel.
@@ -540,14 +555,14 @@ hipError_t launch_nb(const MfmaParams& p, dim3 gd, size_t shm, hipStream_t strea
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!set_for[dev]) {
-    const hipError_t e = hipFuncSetAttribute((const void*)mmvq_mfma_kernel<NB, kRing>,
+    const hipError_t e = hipFuncSetAttribute((const void*)mmvq_mfma_kernel<NB, kRing, DOTS>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaMaxLds);
     if (e != hipSuccess) return e;
     set_for[dev] = true;
   }
   const int32_t plain = (p.ids == nullptr && p.groups == 0 && p.wg_end[0] * p.tgroups == p.total_wgs) ? 1 : 0;
-  hipLaunchKernelGGL((mmvq_mfma_kernel<NB, kRing>), gd, dim3(kThreads), shm, stream, p.w[0], p.xq, p.y[0],
-                     p.n[0], p.m, p.tgroups, p.total_wgs, p.g8, plain, p);
+  hipLaunchKernelGGL((mmvq_mfma_kernel<NB, kRing, DOTS>), gd, dim3(kThreads), shm, stream, p.w[0], p.xq,
+                     p.y[0], p.n[0], p.m, p.tgroups, p.total_wgs, p.g8, plain, p);
   return hipGetLastError();
 }
 
@@ -562,7 +577,7 @@ int64_t workgroups(const MmvqLaunch& a) {
 }  // namespace
 
 bool mfma_supports(int k) {
-  return nb_slot(k / kBlockWeights) >= 0 && lds_bytes(k) + kXchgBytes <= kMfmaMaxLds;
+  return nb_slot(k / kBlockWeights) >= 0 && lds_bytes(k) <= kMfmaMaxLds;
 }
 
 bool mfma_preferred(const MmvqLaunch& a) {
@@ -573,7 +588,8 @@ bool mfma_preferred(const MmvqLaunch& a) {
   //    up to 256 workgroups (one workgroup per CU: LDS), whatever m is;
   //  * packed dots with the tokens split over waves: ~1e-5 us per
   //    (row, super-block, token), all of it vector-ALU issue.
-  if (a.dots != nullptr || !mfma_supports(a.k) || a.m < 2) return false;
+  // The choice changes no result bit (every kernel sums in the same order).
+  if (!mfma_supports(a.k) || a.m < 2) return false;
   if (a.m > kSlots) return true;
   const int nb = a.k / kBlockWeights;
   int64_t rows = 0;
@@ -592,6 +608,8 @@ hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream) {
   const int nb = a.k / kBlockWeights;
   const int which = nb_slot(nb);
   if (which < 0) return hipErrorInvalidValue;
+  const bool dots = a.dots != nullptr;
+  if (dots && (a.m > kSlots || uniform_jobs(a) || a.njobs != 1)) return hipErrorInvalidValue;
   MfmaParams p{};
   for (int j = 0; j < kMaxPlainJobs; ++j) {
     p.w[j] = static_cast<const uint8_t*>(a.w[j]);
@@ -605,6 +623,7 @@ hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream) {
   p.x_per_id = a.x_per_id;
   p.expert_stride = a.expert_stride;
   p.err_flag = a.err_flag;
+  p.dots = a.dots;
   p.groups = a.groups;
   p.m = a.m;
   p.tgroups = (a.m + kSlots - 1) / kSlots;
@@ -627,13 +646,15 @@ hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream) {
   p.total_wgs = (int)total_wgs;
   const dim3 gd((unsigned)((total_wgs + 7) / 8 * 8));
   p.g8 = (int)(gd.x / 8);
-  const size_t shm = lds_bytes(a.k) + kXchgBytes;
+  const size_t shm = lds_bytes(a.k);
+#define Q2K_NB(NBV) (dots ? launch_nb<NBV, true>(p, gd, shm, stream) : launch_nb<NBV, false>(p, gd, shm, stream))
   switch (which) {
-    case 0: return launch_nb<4>(p, gd, shm, stream);
-    case 1: return launch_nb<8>(p, gd, shm, stream);
-    case 2: return launch_nb<16>(p, gd, shm, stream);
-    default: return launch_nb<28>(p, gd, shm, stream);
+    case 0: return Q2K_NB(4);
+    case 1: return Q2K_NB(8);
+    case 2: return Q2K_NB(16);
+    default: return Q2K_NB(28);
   }
+#undef Q2K_NB
 }
 
 }  // namespace q2k

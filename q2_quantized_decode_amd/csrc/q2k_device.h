@@ -69,6 +69,24 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
+// The fixed summation order of every Q2_K x q8_1 product kernel (so that
+// all of them return the same bits for the same inputs):
+//  * leaf, one half block (super-block b, half h: q8 blocks c = 8b+4h+j,
+//    j = 0..3) of one row and token: fI = ((d8_0 I_0 + d8_1 I_1) + d8_2 I_2)
+//    + d8_3 I_3, one fma per term from +0 (every d8 * I is exact in fp64:
+//    24 + 18 bits), fM likewise with M, and v = RN(d * fI) - RN(dmin * fM);
+//  * per half h, the pairwise tree over b = 0 .. NBP-1 (NBP: the row's block
+//    count rounded up to a power of two, leaves past the row are +0),
+//    neighbours first;
+//  * the two halves added, then rounded once to f32.
+// fp64 because post-SwiGLU activations reach 10^3 while outputs cross zero.
+__device__ __forceinline__ double half_value(double d, double dmin, double fI, double fM) {
+#pragma clang fp contract(off)
+  const double a = d * fI;
+  const double c = dmin * fM;
+  return a - c;
+}
+
 __device__ __forceinline__ float quiet_nan() { return __uint_as_float(0x7fc00000u); }
 
 // q8_1 of one 32-value block (every quantiser of this library uses these

@@ -62,6 +62,9 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream);
 // Product kernel choice (0 automatic, 1 matrix cores, 2 packed dots); returns
 // the previous one.
 int set_product_kernel(int choice);
+// True when launch_mmvq runs this launch (product or integer stage) on the
+// matrix-core kernel under the current choice.
+bool takes_mfma(const MmvqLaunch& a);
 // 2..8 tokens on the matrix cores, rows of 4, 8, 16 or 28 super-blocks.
 hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream);
 bool mfma_supports(int k);

@@ -273,3 +273,26 @@ def gate_case(seed: int, tokens: int, hc: int, dim: int, eps: float = 1e-6):
     kv = rng.standard_normal(size=(tokens, (hc + 1) * dim)).astype(np.float32)
     qk = (1.0 + 0.1 * rng.standard_normal(size=(hc, dim))).astype(np.float32)
     return h, kv, qk, eps
+
+
+def summation_order_case(n_rows: int, n_blocks: int, m: int):
+    """Hand-built input whose f32 product depends on the order of the fp64
+    sums (no randomness). Every row: scale nibble 1 and min nibble 0 in each
+    sub-block, d = 1.0, dmin = 0, and quant 1 only at elements 0 and 128 of
+    each super-block (qs[0] and qs[32] = 0x01), 0 elsewhere. Every token:
+    x = 127 * v at element 256b + 128h for the (b, h, v) below, 0 elsewhere,
+    so q8 block 8b + 4h holds one value +-127 with scale |v| and the half
+    block (b, h) of the product is exactly 127 * v:
+        (0, 0): 2^60   (1, 0): 1   (2, 0): -2^60   (3, 0): 2   (0, 1): 1.
+    Returns (w uint8 [n_rows, n_blocks, 84], x bf16 bits [m, 256 * n_blocks]);
+    n_blocks >= 4."""
+    assert n_blocks >= 4
+    w = np.zeros((n_rows, n_blocks, Q2K_BLOCK_BYTES), dtype=np.uint8)
+    w[..., 0:16] = 0x01
+    w[..., 16] = 0x01
+    w[..., 48] = 0x01
+    w[..., 80:82] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
+    x = np.zeros((m, Q2K_BLOCK_WEIGHTS * n_blocks), dtype=np.float32)
+    for b, h, v in ((0, 0, 2.0 ** 60), (1, 0, 1.0), (2, 0, -2.0 ** 60), (3, 0, 2.0), (0, 1, 1.0)):
+        x[:, 256 * b + 128 * h] = 127.0 * v
+    return w, f32_to_bf16_bits_torch(x)

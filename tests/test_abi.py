@@ -38,7 +38,7 @@ def test_header_symbols_exported(L):
 
 
 def test_version_and_sizes(L):
-    assert L.q2k_abi_version() == 4
+    assert L.q2k_abi_version() == 5
     assert L.q8_1_rows_bytes(1, 1024) == 1280
     assert L.q8_1_rows_bytes(8, 7168) == 8 * 8960
     assert L.q8_1_rows_bytes(0, 1024) == 0
@@ -57,6 +57,33 @@ def test_product_kernel_choice(L):
     assert L.q2k_set_product_kernel(q2.KERNEL_MATRIX_CORES) == q2.KERNEL_AUTO
     assert L.q2k_set_product_kernel(q2.KERNEL_PACKED_DOTS) == q2.KERNEL_MATRIX_CORES
     assert L.q2k_set_product_kernel(prev) == q2.KERNEL_PACKED_DOTS
+
+
+def test_product_kernel_query(L):
+    """q2k_product_kernel reports, on the host, which kernel a single-matrix
+    product of a shape runs: the measured cost model under the automatic
+    choice (the large verify matrix: packed dots at one token, the matrix
+    cores at eight; rows of 5 blocks have no matrix-core tile), or the forced
+    choice."""
+    MC, PD = q2.KERNEL_MATRIX_CORES, q2.KERNEL_PACKED_DOTS
+    assert L.q2k_product_kernel(0, 1024, 1) == ESHAPE
+    assert L.q2k_product_kernel(10, 1000, 1) == ESHAPE
+    assert L.q2k_product_kernel(10, 1024, 0) == ESHAPE
+    assert L.q2k_product_kernel(10, 1024, 4097) == ESHAPE
+    prev = L.q2k_set_product_kernel(q2.KERNEL_AUTO)
+    try:
+        assert L.q2k_product_kernel(32768, 7168, 1) == PD
+        assert L.q2k_product_kernel(32768, 7168, 8) == MC
+        assert L.q2k_product_kernel(100, 1280, 8) == PD
+        assert L.q2k_product_kernel(300, 1024, 20) == MC
+        L.q2k_set_product_kernel(PD)
+        assert L.q2k_product_kernel(32768, 7168, 8) == PD
+        L.q2k_set_product_kernel(MC)
+        assert L.q2k_product_kernel(10, 1024, 2) == MC
+        assert L.q2k_product_kernel(10, 1024, 1) == PD
+        assert L.q2k_product_kernel(10, 1280, 3) == PD
+    finally:
+        L.q2k_set_product_kernel(prev)
 
 
 def _err(L):

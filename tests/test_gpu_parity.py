@@ -1,9 +1,13 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
 Bars: q8_1 bytes, integer block sums and dequantised bf16 rows bit-exact;
-f32 products and the gated stream within |gpu - ref| <= 1e-4 + 2e-3 |ref|
-elementwise; the bf16 SwiGLU value within one bf16 ulp (the GPU forms it in
-f32, the oracle in fp64), with its q8_1 bytes bit-exact from the GPU's own h.
+f32 products bit for bit the oracle's evaluation of the library's fixed
+summation order (orc.mmvq_f32) and within |gpu - ref| <= 1e-4 + 2e-3 |ref| of
+the fp64 definition (orc.mmvq, the integer route on every row, the dense
+route on all rows of small matrices and sampled rows of large ones); the
+gated stream within the same tolerance; the bf16 SwiGLU value within one
+bf16 ulp (the GPU forms it in f32, the oracle in fp64), with its q8_1 bytes
+bit-exact from the GPU's own h.
 """
 
 import numpy as np
@@ -73,6 +77,67 @@ def assert_close(got, ref, what=""):
     i = int(np.argmax(excess))
     assert excess.flat[i] <= 0, (f"{what}: element {np.unravel_index(i, got.shape)} "
                                  f"gpu {got.flat[i]!r} ref {ref.flat[i]!r}")
+
+
+# Rows per oracle chunk of a product check, and the largest n * k checked
+# through the dense fp64 route on every row (larger ones: sampled rows there,
+# every row through the integer route and the fixed order).
+CHUNK_ROWS = 4096
+DENSE_ALL_MAX = 1 << 24
+
+
+def assert_bits(got, ref32, what=""):
+    """f32 arrays equal bit for bit."""
+    g = np.ascontiguousarray(np.asarray(got, dtype=np.float32))
+    r = np.ascontiguousarray(np.asarray(ref32, dtype=np.float32))
+    assert g.shape == r.shape, (g.shape, r.shape)
+    bad = np.flatnonzero(g.view(np.uint32) != r.view(np.uint32))
+    assert bad.size == 0, (f"{what}: {bad.size} of {g.size} outputs differ from the fixed-order "
+                           f"oracle; first {np.unravel_index(bad[0], g.shape)}: gpu {g.flat[bad[0]]!r} "
+                           f"oracle {r.flat[bad[0]]!r}")
+
+
+def assert_product(got, w, oq, od, what="", dense_rows=None):
+    """One matrix's product y [m, n] against the oracle: bit for bit the fixed
+    summation order and within tolerance of the integer route on every row
+    (both from one block_dots per CHUNK_ROWS rows), and within tolerance of the
+    dense fp64 definition on every row (small matrices) or on ``dense_rows``."""
+    got = np.asarray(got)
+    n = w.shape[0]
+    for r0 in range(0, n, CHUNK_ROWS):
+        wc = w[r0:r0 + CHUNK_ROWS]
+        I, M = orc.block_dots(wc, oq)
+        gc = got[:, r0:r0 + CHUNK_ROWS]
+        assert_bits(gc, orc.mmvq_f32_from_block_dots(wc, I, M, od), f"{what} rows {r0}..")
+        assert_close(gc, orc.mmvq_from_block_dots(wc, I, M, od), f"{what} rows {r0}.. (integer route)")
+    if dense_rows is None and n * w.shape[1] * 256 > DENSE_ALL_MAX:
+        dense_rows = _sample_rows(n, n + w.shape[1])
+    if dense_rows is None:
+        assert_close(got, orc.mmvq(w, oq, od), what)
+    else:
+        assert_close(got[:, dense_rows], orc.mmvq(w[dense_rows], oq, od), f"{what} (dense, sampled)")
+
+
+def assert_pair(ya, yb, wa, wb, oq, od, what=""):
+    assert_product(ya, wa, oq, od, what + " a")
+    assert_product(yb, wb, oq, od, what + " b")
+
+
+def assert_experts(got, mats, oq, od, x_per_id, what=""):
+    """got [n_ids, m, n]: id i against mats[i], shared input or its own rows."""
+    m_per = oq.shape[0] // len(mats) if x_per_id else oq.shape[0]
+    for i, w in enumerate(mats):
+        sl = slice(i * m_per, (i + 1) * m_per) if x_per_id else slice(0, m_per)
+        assert_product(got[i], w, oq[sl], od[sl], f"{what} id #{i}")
+
+
+def assert_grouped(got, w, oq, od, groups, what=""):
+    """got [m, groups * R]: group g's rows against the g-th input slice."""
+    rows = w.shape[0] // groups
+    k = w.shape[1] * 256
+    for g in range(groups):
+        assert_product(got[:, g * rows:(g + 1) * rows], w[g * rows:(g + 1) * rows],
+                       oq[:, g * k:(g + 1) * k], od[:, g * k // 32:(g + 1) * k // 32], f"{what} group {g}")
 
 
 # ----------------------------------------------------------------- q8_1 -----
@@ -188,7 +253,7 @@ def test_mmvq_and_block_dots(n, k, m):
     got = dots.cpu().numpy().astype(np.int64)
     assert np.array_equal(got[..., 0], I), "I sums differ"
     assert np.array_equal(got[..., 1], M), "M sums differ"
-    assert_close(y.cpu().numpy(), orc.mmvq(case.w, oq, od), f"mmvq n={n} k={k} m={m}")
+    assert_product(y.cpu().numpy(), case.w, oq, od, f"mmvq n={n} k={k} m={m}")
 
 
 def test_mmvq_single_gemv_workload():
@@ -197,7 +262,7 @@ def test_mmvq_single_gemv_workload():
     xq = q2.q8_1_rows(bf16_dev(case.x_bits))
     oq, od = assert_q8_equal(xq, case.x_bits)
     y = q2.q2k_mmvq(dev(case.w.reshape(-1)), xq, 256, 1024, 1)
-    assert_close(y.cpu().numpy(), orc.mmvq(case.w, oq, od), "single gemv")
+    assert_product(y.cpu().numpy(), case.w, oq, od, "single gemv")
 
 
 def test_mmvq_exact_closed_form():
@@ -222,6 +287,142 @@ def test_mmvq_deterministic_and_stride_independent():
     # the first 1000 rows alone give the same bytes as inside the bigger launch
     c = q2.q2k_mmvq(w[: 1000 * 16 * 84], xq, 1000, 4096, 4).cpu().numpy()
     assert np.array_equal(c.view(np.uint32), a[:, :1000].view(np.uint32))
+
+
+# ------------------------------------------------- fixed summation order ---
+
+MC, PD, AUTO = q2.KERNEL_MATRIX_CORES, q2.KERNEL_PACKED_DOTS, q2.KERNEL_AUTO
+
+
+class kernel_choice:
+    """with kernel_choice(c): products run with q2k_set_product_kernel(c)."""
+
+    def __init__(self, choice):
+        self.choice = choice
+
+    def __enter__(self):
+        self.prev = q2.q2k_set_product_kernel(self.choice)
+
+    def __exit__(self, *exc):
+        q2.q2k_set_product_kernel(self.prev)
+
+
+# (rows, blocks per row, tokens, choice, kernel the product takes)
+HAND_CASES = [
+    (16384, 4, 1, AUTO, PD),      # run kernel, 8 rows per row step
+    (4096, 28, 1, AUTO, PD),      # run kernel, one row per step, idle lanes
+    (37, 4, 1, AUTO, PD),         # one-step kernel
+    (37, 5, 2, AUTO, PD),         # one-step kernel, tokens split, padded tree
+    (8197, 4, 2, MC, MC), (8197, 4, 2, PD, PD),
+    (8197, 8, 5, MC, MC), (4099, 16, 3, MC, MC), (4099, 16, 3, PD, PD),
+    (8197, 28, 8, MC, MC), (8197, 28, 8, PD, PD),
+    (64, 36, 1, AUTO, PD), (64, 36, 3, AUTO, PD),   # wide kernel (k > 8192)
+]
+
+
+@pytest.mark.parametrize("n,nb,m,choice,kernel", HAND_CASES)
+def test_fixed_order_hand_case_every_kernel(n, nb, m, choice, kernel):
+    """The hand-built input of synthetic.summation_order_case, whose f32
+    result depends on the order of the fp64 sums (the oracle's derivation:
+    127 where the exact sum is 508), gives exactly 127 on every kernel:
+    every row and token, through q2k_mmvq, the pair form and, for one token,
+    the fused quantisation."""
+    k = 256 * nb
+    w_np, x = syn.summation_order_case(n, nb, m)
+    w = dev(w_np.reshape(-1))
+    xq = q2.q8_1_rows(bf16_dev(x))
+    assert_q8_equal(xq, x)
+    with kernel_choice(choice):
+        assert q2.q2k_product_kernel(n, k, m) == kernel
+        y = q2.q2k_mmvq(w, xq, n, k, m).cpu().numpy()
+        ya, yb = q2.q2k_mmvq_pair(w, n, w[: 5 * nb * 84], 5, xq, k, m)
+        outs = [y, ya.cpu().numpy(), yb.cpu().numpy()]
+        if m == 1:
+            outs.append(q2.q8_1_q2k_mmvq(w, bf16_dev(x), n, k)[0].cpu().numpy())
+    for o in outs:
+        assert np.all(o == 127.0), np.unique(o)
+
+
+def test_fixed_order_hand_case_mmq_grouped_experts():
+    """The same input through q2k_mmq (20 tokens: matrix-core groups and the
+    packed-dot group loop), the grouped form and the expert batch."""
+    nb, k = 4, 1024
+    w_np, x = syn.summation_order_case(300, nb, 20)
+    w = dev(w_np.reshape(-1))
+    xq = q2.q8_1_rows(bf16_dev(x))
+    for choice in (MC, PD):
+        with kernel_choice(choice):
+            assert np.all(q2.q2k_mmq(w, xq, 300, k, 20).cpu().numpy() == 127.0)
+    _, x2 = syn.summation_order_case(1, nb, 3)
+    xg = np.concatenate([x2, x2], axis=1)                     # two groups of 1024
+    yg = q2.q2k_mmvq_grouped(w[: 2 * 150 * nb * 84], q2.q8_1_rows(bf16_dev(xg)), 2, 150, k, 3)
+    assert np.all(yg.cpu().numpy() == 127.0)
+    ids = dev(np.array([1, 0, 1], dtype=np.int32))
+    ye = q2.q2k_mmvq_experts([w], 150 * nb * 84, 2, ids, q2.q8_1_rows(bf16_dev(x2)), False, 150, k, 3)
+    assert np.all(ye.cpu().numpy() == 127.0)
+
+
+@pytest.mark.parametrize("choice", [MC, PD])
+def test_block_dots_of_the_kernel_taken(choice):
+    """q2k_block_dots returns the integer sums of the kernel the product
+    takes: on the matrix cores the v_mfma_i32_16x16x64_i8 outputs (I and M),
+    else the packed-dot sums; all rows of [8197, 1024] at m = 5, bit-exact."""
+    n, k, m = 8197, 1024, 5
+    case = syn.single_gemv_case(n=n, k=k, m=m, seed=7300)
+    w = dev(case.w.reshape(-1))
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits))
+    oq, _ = assert_q8_equal(xq, case.x_bits)
+    with kernel_choice(choice):
+        assert q2.q2k_product_kernel(n, k, m) == choice
+        dots = q2.q2k_block_dots(w, xq, n, k, m).cpu().numpy().astype(np.int64)
+    I, M = orc.block_dots(case.w, oq)
+    assert np.array_equal(dots[..., 0], I), "I sums differ"
+    assert np.array_equal(dots[..., 1], M), "M sums differ"
+
+
+def test_block_dots_large_verify_matrix_cores(large):
+    """The [32768, 7168] matrix at m = 8 (the product's automatic choice is
+    the matrix cores): their integer sums on sampled rows, bit-exact."""
+    case, w = large
+    m = 8
+    assert q2.q2k_product_kernel(case.n, case.k, m) == MC
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits[:m]))
+    oq, _ = assert_q8_equal(xq, case.x_bits[:m])
+    dots = q2.q2k_block_dots(w, xq, case.n, case.k, m)
+    rows = _sample_rows(case.n, 91, extra=256)
+    got = dots[:, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.int64)
+    del dots
+    I, M = orc.block_dots(case.w[rows], oq)
+    assert np.array_equal(got[..., 0], I), "I sums differ"
+    assert np.array_equal(got[..., 1], M), "M sums differ"
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_every_kernel_choice_same_bits_attention_pair(m):
+    """The attention pair (wq_a [1024, 4096], wkv [512, 4096]) under every
+    product kernel choice: identical bits."""
+    pc = syn.attention_pair_case(m)
+    wa, wb = dev(pc.wa.reshape(-1)), dev(pc.wb.reshape(-1))
+    x = bf16_dev(pc.x_bits)
+    outs = []
+    for choice in (AUTO, MC, PD):
+        with kernel_choice(choice):
+            ya, yb, _ = q2.q8_1_q2k_mmvq_pair(wa, pc.na, wb, pc.nb, x, pc.k)
+            outs.append(torch.cat([ya.reshape(-1), yb.reshape(-1)]).cpu().numpy())
+    for o in outs[1:]:
+        assert_bits(o, outs[0], f"attention pair m={m}")
+
+
+def test_every_kernel_choice_same_bits_large_verify(large):
+    """[32768, 7168] at m = 8: the matrix cores (automatic) and the packed
+    dots (tokens split over waves) return identical bits."""
+    case, w = large
+    xq = q2.q8_1_rows(bf16_dev(case.x_bits[:8]))
+    outs = []
+    for choice in (AUTO, PD):
+        with kernel_choice(choice):
+            outs.append(q2.q2k_mmvq(w, xq, case.n, case.k, 8).cpu().numpy())
+    assert_bits(outs[1], outs[0], "large verify m=8: packed dots vs matrix cores")
 
 
 # ------------------------------------------------- matrix-core path ---------
@@ -261,8 +462,7 @@ def test_mfma_mmvq(k, m, matrix_cores):
     xq = q2.q8_1_rows(bf16_dev(case.x_bits))
     oq, od = assert_q8_equal(xq, case.x_bits)
     y = q2.q2k_mmvq(w, xq, n, k, m).cpu().numpy()
-    rows = np.arange(n) if k == 1024 else _sample_rows(n, k + m)
-    assert_close(y[:, rows], orc.mmvq(case.w[rows], oq, od), f"mfma n={n} k={k} m={m}")
+    assert_product(y, case.w, oq, od, f"mfma n={n} k={k} m={m}")
     again = q2.q2k_mmvq(w, xq, n, k, m).cpu().numpy()
     assert np.array_equal(again.view(np.uint32), y.view(np.uint32)), "not deterministic"
 
@@ -297,10 +497,7 @@ def test_mfma_pair(matrix_cores):
     xq = q2.q8_1_rows(bf16_dev(pc.x_bits))
     oq, od = assert_q8_equal(xq, pc.x_bits)
     ya, yb = q2.q2k_mmvq_pair(dev(pc.wa.reshape(-1)), pc.na, dev(pc.wb.reshape(-1)), pc.nb, xq, pc.k, 4)
-    ra = orc.mmvq(pc.wa[_sample_rows(pc.na, 1)], oq, od)
-    rb = orc.mmvq(pc.wb[_sample_rows(pc.nb, 2)], oq, od)
-    assert_close(ya.cpu().numpy()[:, _sample_rows(pc.na, 1)], ra, "mfma pair a")
-    assert_close(yb.cpu().numpy()[:, _sample_rows(pc.nb, 2)], rb, "mfma pair b")
+    assert_pair(ya.cpu().numpy(), yb.cpu().numpy(), pc.wa, pc.wb, oq, od, "mfma pair")
 
 
 @pytest.mark.parametrize("m", [1, 2, 4, 8])
@@ -318,28 +515,27 @@ def test_fused_q8_1_pair_equals_two_calls(m):
     assert torch.equal(ya.view(torch.int32), ya2.view(torch.int32))
     assert torch.equal(yb.view(torch.int32), yb2.view(torch.int32))
     oq, od = assert_q8_equal(xq, pc.x_bits)
-    ra, rb = orc.mmvq_pair(pc.wa, pc.wb, oq, od)
-    assert_close(ya.cpu().numpy(), ra, f"fused pair a m={m}")
-    assert_close(yb.cpu().numpy(), rb, f"fused pair b m={m}")
+    assert_pair(ya.cpu().numpy(), yb.cpu().numpy(), pc.wa, pc.wb, oq, od, f"fused pair m={m}")
 
 
 def test_pair_token_split_and_matrix_cores_agree():
     """The pair at m = 8 through the packed-dot kernel (tokens split over
-    waves) and through the matrix cores: both within the tolerance of the
-    oracle on every output."""
+    waves) and through the matrix cores: the same bits, the oracle's."""
     pc = syn.attention_pair_case(8, seed=78, na=2048 + 3, nb=1024 + 9, k=4096)
     xq = q2.q8_1_rows(bf16_dev(pc.x_bits))
     oq, od = assert_q8_equal(xq, pc.x_bits)
     wa, wb = dev(pc.wa.reshape(-1)), dev(pc.wb.reshape(-1))
-    ra, rb = orc.mmvq_pair(pc.wa, pc.wb, oq, od)
+    outs = []
     for choice in (q2.KERNEL_PACKED_DOTS, q2.KERNEL_MATRIX_CORES):
         prev = q2.q2k_set_product_kernel(choice)
         try:
             ya, yb = q2.q2k_mmvq_pair(wa, pc.na, wb, pc.nb, xq, pc.k, 8)
         finally:
             q2.q2k_set_product_kernel(prev)
-        assert_close(ya.cpu().numpy(), ra, f"pair a, kernel {choice}")
-        assert_close(yb.cpu().numpy(), rb, f"pair b, kernel {choice}")
+        outs.append((ya.cpu().numpy(), yb.cpu().numpy()))
+        assert_pair(outs[-1][0], outs[-1][1], pc.wa, pc.wb, oq, od, f"pair, kernel {choice}")
+    assert_bits(outs[0][0], outs[1][0], "pair a: packed dots vs matrix cores")
+    assert_bits(outs[0][1], outs[1][1], "pair b: packed dots vs matrix cores")
 
 
 @pytest.mark.parametrize("n,k,m", [(1536, 4096, 8), (4103, 2048, 4), (300, 1024, 5),
@@ -352,7 +548,7 @@ def test_token_split(n, k, m, packed_dots):
     xq = q2.q8_1_rows(bf16_dev(case.x_bits))
     oq, od = assert_q8_equal(xq, case.x_bits)
     y = q2.q2k_mmvq(dev(case.w.reshape(-1)), xq, n, k, m).cpu().numpy()
-    assert_close(y, orc.mmvq(case.w, oq, od), f"token split n={n} k={k} m={m}")
+    assert_product(y, case.w, oq, od, f"token split n={n} k={k} m={m}")
 
 
 @pytest.mark.parametrize("n,k,m", [(20480, 2048, 1), (16384, 1024, 1), (8192, 4096, 1),
@@ -383,8 +579,7 @@ def test_fused_q8_1_equals_two_calls(n, k, m):
     assert torch.equal(xq[:need], xq2[:need])
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
     oq, od = assert_q8_equal(xq, case.x_bits)
-    rows = np.arange(n) if n <= 512 else _sample_rows(n, n + k, extra=64)
-    assert_close(y.cpu().numpy()[:, rows], orc.mmvq(case.w[rows], oq, od), f"fused n={n} k={k} m={m}")
+    assert_product(y.cpu().numpy(), case.w, oq, od, f"fused n={n} k={k} m={m}")
 
 
 def _experts_check(x_per_id):
@@ -401,15 +596,13 @@ def _experts_check(x_per_id):
     y = q2.q2k_mmvq_experts(bases, stride, n_exp, dev(ids_np), xq, x_per_id, n, k, m,
                             err_flag=flag).cpu().numpy()
     assert int(flag.item()) == 1
-    rows = _sample_rows(n, 3, extra=128)
     for b in range(2):
         for i, e in enumerate(ids_np.tolist()):
             if e >= n_exp:
                 assert np.all(np.isnan(y[b, i]))
                 continue
             xs = slice(i * m, (i + 1) * m) if x_per_id else slice(0, m)
-            ref = orc.mmvq(mats[b][e][rows], oq[xs], od[xs])
-            assert_close(y[b, i][:, rows], ref, f"expert base={b} id={e}")
+            assert_product(y[b, i], mats[b][e], oq[xs], od[xs], f"expert base={b} id={e}")
 
 
 @pytest.mark.parametrize("x_per_id", [False, True])
@@ -436,9 +629,7 @@ def test_pair_attention_inputs(m):
     oq, od = assert_q8_equal(xq, pc.x_bits)
     wa, wb = dev(pc.wa.reshape(-1)), dev(pc.wb.reshape(-1))
     ya, yb = q2.q2k_mmvq_pair(wa, pc.na, wb, pc.nb, xq, pc.k, m)
-    ra, rb = orc.mmvq_pair(pc.wa, pc.wb, oq, od)
-    assert_close(ya.cpu().numpy(), ra, "pair a")
-    assert_close(yb.cpu().numpy(), rb, "pair b")
+    assert_pair(ya.cpu().numpy(), yb.cpu().numpy(), pc.wa, pc.wb, oq, od, "pair")
     sa = q2.q2k_mmvq(wa, xq, pc.na, pc.k, m).cpu().numpy()
     sb = q2.q2k_mmvq(wb, xq, pc.nb, pc.k, m).cpu().numpy()
     assert np.array_equal(sa.view(np.uint32), ya.cpu().numpy().view(np.uint32))
@@ -458,7 +649,7 @@ def test_single_token_launch_forms_agree(n, k):
     ya, yb = q2.q2k_mmvq_pair(w, n, w, n, xq, k, 1)
     assert np.array_equal(single.view(np.uint32), ya.cpu().numpy().view(np.uint32))
     assert np.array_equal(single.view(np.uint32), yb.cpu().numpy().view(np.uint32))
-    assert_close(single, orc.mmvq(case.w, oq, od), f"single token n={n} k={k}")
+    assert_product(single, case.w, oq, od, f"single token n={n} k={k}")
 
 
 def test_pair_ragged():
@@ -466,9 +657,7 @@ def test_pair_ragged():
     xq = q2.q8_1_rows(bf16_dev(pc.x_bits))
     oq, od = assert_q8_equal(xq, pc.x_bits)
     ya, yb = q2.q2k_mmvq_pair(dev(pc.wa.reshape(-1)), 37, dev(pc.wb.reshape(-1)), 5, xq, 1280, 3)
-    ra, rb = orc.mmvq_pair(pc.wa, pc.wb, oq, od)
-    assert_close(ya.cpu().numpy(), ra, "ragged pair a")
-    assert_close(yb.cpu().numpy(), rb, "ragged pair b")
+    assert_pair(ya.cpu().numpy(), yb.cpu().numpy(), pc.wa, pc.wb, oq, od, "ragged pair")
 
 
 # -------------------------------------------------------------- grouped -----
@@ -482,6 +671,7 @@ def test_grouped_wo_a(m):
     oq, od = assert_q8_equal(xq, gc.x_bits)
     y = q2.q2k_mmvq_grouped(dev(gc.w.reshape(-1)), xq, gc.groups, gc.rows, gc.k, m).cpu().numpy()
     assert_close(y, orc.mmvq_grouped(gc.w, oq, od, gc.groups), f"grouped m={m}")
+    assert_grouped(y, gc.w, oq, od, gc.groups, f"grouped m={m}")
 
 
 @pytest.mark.parametrize("groups,rows,k,m", [(3, 37, 1280, 3), (5, 16, 256, 1), (2, 130, 9216, 2)])
@@ -495,6 +685,7 @@ def test_grouped_ragged_equals_slices(groups, rows, k, m):
     oq, od = assert_q8_equal(xq, gc.x_bits)
     y = q2.q2k_mmvq_grouped(w, xq, groups, rows, k, m).cpu().numpy()
     assert_close(y, orc.mmvq_grouped(gc.w, oq, od, groups), "grouped ragged")
+    assert_grouped(y, gc.w, oq, od, groups, "grouped ragged")
     per = rows * (k // 256) * 84
     for g in range(groups):
         xs = q2.q8_1_rows(bf16_dev(np.ascontiguousarray(gc.x_bits[:, g * k:(g + 1) * k])))
@@ -538,8 +729,7 @@ def test_expert_batch_stagewise(expert_batch):
     gu_h = gu.cpu().numpy()
     for bi, kind in enumerate(("gate", "up")):
         mats = [case.expert_matrix(e, kind) for e in case.ids.tolist()]
-        ref = orc.mmvq_experts(mats, oq, od, x_per_id=False)
-        assert_close(gu_h[bi], ref, kind)
+        assert_experts(gu_h[bi], mats, oq, od, False, kind)
     g = gu[0].reshape(len(case.ids), case.inter).contiguous()
     u = gu[1].reshape(len(case.ids), case.inter).contiguous()
     h, hq = q2.swiglu_q8_1_rows(g, u)
@@ -550,8 +740,7 @@ def test_expert_batch_stagewise(expert_batch):
     yd = q2.q2k_mmvq_experts([down], per_d, case.n_experts, ids, hq, True, case.dim,
                              case.inter, 1, err_flag=flag)
     mats = [case.expert_matrix(e, "down") for e in case.ids.tolist()]
-    ref_d = orc.mmvq_experts(mats, hq_o, hd_o, x_per_id=True)
-    assert_close(yd.cpu().numpy()[0], ref_d, "down")
+    assert_experts(yd.cpu().numpy()[0], mats, hq_o, hd_o, True, "down")
     assert int(flag.item()) == 0
     # experts == per-expert singles, bit for bit
     for i, e in enumerate(case.ids.tolist()):
@@ -609,8 +798,7 @@ def test_fused_swiglu_down_equals_two_calls(expert_batch):
             h_bits = h2.view(torch.int16).cpu().numpy().view(np.uint16)
             hq_o, hd_o = assert_q8_equal(hq, h_bits)
             mats = [case.expert_matrix(e, "down") for e in ids_np.tolist()]
-            ref = orc.mmvq_experts(mats, hq_o, hd_o, x_per_id=True)
-            assert_close(y.cpu().numpy()[0], ref, "fused SwiGLU down")
+            assert_experts(y.cpu().numpy()[0], mats, hq_o, hd_o, True, "fused SwiGLU down")
 
 
 @pytest.mark.parametrize("n,k,n_ids", [(4096, 4096, 3), (200, 1024, 5), (1000, 2048, 3)])
@@ -651,8 +839,8 @@ def test_fused_q8_1_experts_small_and_multi_token():
         assert torch.equal(xq[:q2.q8_1_rows_bytes(m, k)], xq2[:q2.q8_1_rows_bytes(m, k)])
         assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
         oq, od = assert_q8_equal(xq, xb)
-        ref = orc.mmvq_experts([mats[i] for i in (5, 0, 3)], oq, od, x_per_id=False)
-        assert_close(y.cpu().numpy()[0], ref, f"fused experts m={m}")
+        assert_experts(y.cpu().numpy()[0], [mats[i] for i in (5, 0, 3)], oq, od, False,
+                       f"fused experts m={m}")
 
 
 def test_expert_bad_id_flags_and_nans(expert_batch):
@@ -680,11 +868,9 @@ def test_experts_multi_token_shared_and_per_id():
     xq = q2.q8_1_rows(bf16_dev(x))
     oq, od = assert_q8_equal(xq, x)
     y = q2.q2k_mmvq_experts([dev(buf)], stride, n_exp, dev(ids_np), xq, True, n, k, m).cpu().numpy()
-    ref = orc.mmvq_experts([mats[i] for i in ids_np], oq, od, x_per_id=True)
-    assert_close(y[0], ref, "per-id experts")
+    assert_experts(y[0], [mats[i] for i in ids_np], oq, od, True, "per-id experts")
     ys = q2.q2k_mmvq_experts([dev(buf)], stride, n_exp, dev(ids_np), xq, False, n, k, m).cpu().numpy()
-    refs = orc.mmvq_experts([mats[i] for i in ids_np], oq[:m], od[:m], x_per_id=False)
-    assert_close(ys[0], refs, "shared-input experts")
+    assert_experts(ys[0], [mats[i] for i in ids_np], oq[:m], od[:m], False, "shared-input experts")
 
 
 # --------------------------------------------------------------- engram -----
@@ -813,6 +999,25 @@ def test_engram_gate_closed_forms():
     assert np.array_equal(hd.cpu().numpy(), h)                # v = 0: unchanged
 
 
+@pytest.mark.parametrize("dim", [4, 4096])
+def test_engram_gate_small_vectors_eps(dim):
+    """Constant vectors small enough that eps = 1e-6 matters (h = 1e-3,
+    keys 2e-3, value 1): the oracle's eps-inside-each-rms reading, and for
+    dim = 4 its closed form s = 4/sqrt(10)."""
+    a, b, eps, hc = 1e-3, 2e-3, 1e-6, 2
+    h = np.full((1, hc, dim), a, np.float32)
+    kv = np.concatenate([np.full(hc * dim, b, np.float32), np.ones(dim, np.float32)])[None]
+    qk = np.ones((hc, dim), np.float32)
+    hd = dev(h)
+    q2.engram_gate(hd, dev(kv), dev(qk), eps)
+    got = hd.cpu().numpy()
+    ref = orc.engram_gate(h, kv, qk, eps)
+    assert_close(got, ref, f"gate small vectors dim={dim}")
+    if dim == 4:
+        g = 1.0 / (1.0 + np.exp(-np.sqrt(4.0 / np.sqrt(10.0))))
+        assert_close(got, np.full_like(ref, a + g), "closed form")
+
+
 def test_engram_step(engram):
     """Row gather [8 x 256] -> [1, 2048] -> q8_1 -> wkv [20480, 2048] -> gate on [1, 4, 4096]."""
     e = engram
@@ -826,8 +1031,9 @@ def test_engram_step(engram):
     oq, od = assert_q8_equal(xq, ref_rows.reshape(1, -1))
     n_out = e.dim * (e.hc + 1)
     kv = q2.q2k_mmvq(dev(e.wkv.reshape(-1)), xq, n_out, e.cols * 256, 1)
-    ref_kv = orc.mmvq(e.wkv, oq, od)
-    assert_close(kv.cpu().numpy(), ref_kv, "wkv")
+    assert_product(kv.cpu().numpy(), e.wkv, oq, od, "wkv")
+    I, M = orc.block_dots(e.wkv, oq)
+    ref_kv = orc.mmvq_from_block_dots(e.wkv, I, M, od)[0][None]
     hd = dev(e.h)
     q2.engram_gate(hd, kv, dev(e.qk), e.eps)
     kv_h = kv.cpu().numpy()
@@ -1018,7 +1224,7 @@ def test_mmq(n, k, m):
     xq = q2.q8_1_rows(bf16_dev(x))
     oq, od = assert_q8_equal(xq, x)
     y = q2.q2k_mmq(dev(w.reshape(-1)), xq, n, k, m).cpu().numpy()
-    assert_close(y, orc.mmvq(w, oq, od), f"mmq n={n} k={k} m={m}")
+    assert_product(y, w, oq, od, f"mmq n={n} k={k} m={m}")
 
 
 def test_mmq_max_tokens():
@@ -1030,7 +1236,7 @@ def test_mmq_max_tokens():
     xq = q2.q8_1_rows(bf16_dev(x))
     oq, od = assert_q8_equal(xq, x)
     y = q2.q2k_mmq(dev(w.reshape(-1)), xq, n, k, m).cpu().numpy()
-    assert_close(y, orc.mmvq(w, oq, od), "mmq m=4096")
+    assert_product(y, w, oq, od, "mmq m=4096")
 
 
 def test_mmq_small_m_is_mmvq():
@@ -1063,12 +1269,13 @@ def test_fused_q8_1_large_verify(large):
     assert torch.equal(xq[:need], xq2[:need])
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
     oq, od = assert_q8_equal(xq, case.x_bits[:1])
-    rows = _sample_rows(case.n, 77, extra=128)
-    assert_close(y.cpu().numpy()[:, rows], orc.mmvq(case.w[rows], oq, od), "fused large verify")
+    assert_product(y.cpu().numpy(), case.w, oq, od, "fused large verify",
+                   dense_rows=_sample_rows(case.n, 77, extra=128))
 
 
 def test_large_mmq_sampled(large):
-    """[32768, 7168] against 64 tokens (8 token groups on the matrix cores)."""
+    """[32768, 7168] against 64 tokens (8 token groups on the matrix cores):
+    sampled rows (every token) bit for bit the fixed order."""
     case, w = large
     x = syn.bf16_normal(syn.rng_for(1004, 64), (64, case.k), outlier_frac=0.05)
     xq = q2.q8_1_rows(bf16_dev(x))
@@ -1076,13 +1283,15 @@ def test_large_mmq_sampled(large):
     y = q2.q2k_mmq(w, xq, case.n, case.k, 64).cpu().numpy()
     rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(case.n - 64, case.n),
                                      syn.rng_for(5).choice(case.n, 128, replace=False)]))
-    assert_close(y[:, rows], orc.mmvq(case.w[rows], oq, od), "large mmq m=64")
+    assert_product(y[:, rows], case.w[rows], oq, od, "large mmq m=64")
 
 
 @pytest.mark.parametrize("m", [1, 3, 8])
-def test_large_verify_sampled(large, m):
+def test_large_verify_all_rows(large, m):
     """[32768, 7168] Q2_K against m bf16 tokens with 5% +-20 outliers, in the
-    launch configuration the benchmark times; sampled rows vs the oracle."""
+    launch configuration the benchmark times: all 32768 rows bit for bit the
+    fixed order and within tolerance of the integer route (in 4096-row
+    chunks), sampled rows of the dense fp64 definition."""
     case, w = large
     x = case.x_bits[:m]
     xq = q2.q8_1_rows(bf16_dev(x))
@@ -1091,9 +1300,7 @@ def test_large_verify_sampled(large, m):
     rows = np.unique(np.concatenate([
         np.arange(0, 64), np.arange(case.n - 64, case.n),
         syn.rng_for(4, m).choice(case.n, 384, replace=False)]))
-    ref = orc.mmvq(case.w[rows], oq, od)
-    assert_close(y[:, rows], ref, f"large m={m}")
-    assert np.all(np.isfinite(y))
+    assert_product(y, case.w, oq, od, f"large m={m}", dense_rows=rows)
 
 
 def test_swiglu_extreme_gates():

@@ -347,6 +347,84 @@ def test_mmvq_linearity_under_power_of_two_scaling():
     assert np.array_equal(orc.mmvq(case.w, xq2, d2), 2.0 * orc.mmvq(case.w, xq1, d1))
 
 
+def test_fixed_order_hand_case():
+    """mmvq_f32 (the library's fixed summation order) on a hand-built input
+    whose f32 result depends on the order. Each half block (b, h) contributes
+    exactly 127 * v (one q8 value +-127 with scale |v|, sc = q = d = 1, no min
+    term): half 0 has v = 2^60, 1, -2^60, 2 for b = 0..3, half 1 has v = 1 at
+    b = 0. In fp64, 127 * 2^60 has an ulp of 2^14, so 127*2^60 + 127 and
+    -127*2^60 + 254 round back to +-127*2^60: the pairwise tree of half 0 is
+    0, half 1 gives 127, y = 127. The exact sum is 127 * 4 = 508; summing the
+    half blocks in element order would give 254, pairing the halves of each
+    super-block first would give 0."""
+    w, x = syn.summation_order_case(n_rows=3, n_blocks=4, m=2)
+    xq, d8, _ = orc.q8_1_from_bf16_bits(x)
+    assert d8[0, 0] == 2.0 ** 60 and xq[0, 0] == 127
+    assert d8[0, 16] == 2.0 ** 60 and xq[0, 512] == -127
+    assert d8[0, 24] == 2.0 and xq[0, 3 * 256] == 127
+    y = orc.mmvq_f32(w, xq, d8)
+    assert y.dtype == np.float32 and np.all(y == 127.0)
+    exact = sum(Fraction(int(xq[0, e])) * Fraction(float(d8[0, e // 32])) for e in (0, 128, 256, 512, 768))
+    assert exact == 508
+    # more blocks past the hand-set ones only add +0 leaves (nbp 8 and 64)
+    for nb in (5, 36):
+        w2, x2 = syn.summation_order_case(n_rows=1, n_blocks=nb, m=1)
+        xq2, d82, _ = orc.q8_1_from_bf16_bits(x2)
+        assert np.all(orc.mmvq_f32(w2, xq2, d82) == 127.0)
+
+
+def _exact_y(w, xq, d8, t, r):
+    """The product of one token and row as an exact rational from the bytes."""
+    acc = Fraction(0)
+    for b in range(w.shape[1]):
+        blk = w[r, b]
+        d = Fraction(float(np.frombuffer(bytes(blk[80:82]), np.float16)[0]))
+        dmin = Fraction(float(np.frombuffer(bytes(blk[82:84]), np.float16)[0]))
+        for e in range(256):
+            h, j, l = e // 128, (e % 128) // 32, e % 32
+            q = (int(blk[16 + 32 * h + l]) >> (2 * j)) & 3
+            sb = 8 * h + 2 * j + (l >= 16)
+            wv = d * (int(blk[sb]) & 15) * q - dmin * (int(blk[sb]) >> 4)
+            c = 256 * b + e
+            acc += wv * Fraction(float(d8[t, c // 32])) * int(xq[t, c])
+    return acc
+
+
+@pytest.mark.parametrize("n,k,m", [(3, 256, 2), (2, 1280, 2), (2, 768, 1)])
+def test_fixed_order_is_the_rounded_exact_sum(n, k, m):
+    """mmvq_f32 is within one f32 ulp of the exact rational product (k/256
+    = 1, 5 and 3 blocks: padded trees of 1, 8 and 4 leaves)."""
+    case = syn.single_gemv_case(n=n, k=k, m=m, seed=300 + n + k + m)
+    xq, d8, _ = orc.q8_1_from_bf16_bits(case.x_bits)
+    y = orc.mmvq_f32(case.w, xq, d8)
+    for t in range(m):
+        for r in range(n):
+            ex = float(_exact_y(case.w, xq, d8, t, r))
+            ulp = float(np.spacing(np.float32(abs(ex))))
+            assert abs(float(y[t, r]) - ex) <= ulp, (t, r, float(y[t, r]), ex)
+
+
+def test_fixed_order_closed_forms_and_agreement():
+    k = 512
+    xq = np.full((1, k), 127, dtype=np.int64)
+    d8 = np.ones((1, k // 32), dtype=np.float32)
+    w = _const_matrix(2, 2, 0x01, 0xFF, 0x3C00, 0x0000)        # W = 3
+    assert orc.mmvq_f32(w, xq, d8).tolist() == [[195072.0, 195072.0]]
+    w = _const_matrix(1, 2, 0x32, 0x55, 0x3C00, 0x3C00)        # W = -1 (min term)
+    assert orc.mmvq_f32(w, xq, d8).tolist() == [[-65024.0]]
+    # random blocks, 5% outliers: the f32 rounding of the fp64 dense route
+    # except where the two fp64 sums straddle an f32 rounding boundary
+    rng = syn.rng_for(301)
+    for nb in (1, 3, 4, 7, 28, 36):
+        w = syn.q2k_blocks(rng, 64, nb)
+        x = syn.bf16_normal(rng, (3, 256 * nb), outlier_frac=0.05)
+        xq, d8, _ = orc.q8_1_from_bf16_bits(x)
+        y = orc.mmvq_f32(w, xq, d8)
+        ref = orc.mmvq(w, xq, d8)
+        assert np.all(np.abs(y - ref) <= np.spacing(np.abs(ref).astype(np.float32)))
+        assert np.count_nonzero(y != ref.astype(np.float32)) <= 2
+
+
 def test_pair_and_experts_compose_single():
     pc = syn.attention_pair_case(m=2, na=8, nb=4, k=512)
     xq, d8, _ = orc.q8_1_from_bf16_bits(pc.x_bits)
@@ -579,6 +657,26 @@ def test_gate_constant_vectors_closed_form():
     sig2 = 0.8807970779778823       # 1 / (1 + e^-2): s = 4, sqrt(s) = 2
     assert np.allclose(out[0, 0], 3.0 + sig2, rtol=0, atol=1e-15)
     assert np.allclose(out[0, 1], -0.25 + (1 - sig2), rtol=0, atol=1e-15)
+
+
+def test_gate_eps_enters_each_rms():
+    """Small constant vectors, where eps matters: h = a, k = b, qk = 1, v = 1,
+    dim = 4. With eps inside each root, s = dim*a*b / (sqrt(a^2 + eps) *
+    sqrt(b^2 + eps) * sqrt(dim)) = 2ab / sqrt((a^2 + eps)(b^2 + eps)); for
+    a = 1e-3, b = 2e-3, eps = 1e-6 that is 4e-6 / sqrt(1e-11) = 4 / sqrt(10).
+    Other placements give other values: eps added after each root
+    (2ab / ((a + eps)(b + eps)) = 1.997), to the product of the two norms
+    (2ab / (ab + eps) = 4/3), inside one common root (0.004), or no eps (2)."""
+    a, b, eps, dim = 1e-3, 2e-3, 1e-6, 4
+    h = np.full((1, 1, dim), a)
+    kv = np.concatenate([np.full(dim, b), np.ones(dim)])[None]
+    qk = np.ones((1, dim))
+    out = orc.engram_gate(h, kv, qk, eps)
+    s = 4.0 / math.sqrt(10.0)
+    g = 1.0 / (1.0 + math.exp(-math.sqrt(s)))
+    assert np.allclose(out[0, 0], a + g, rtol=0, atol=1e-12)
+    for wrong in (1.997, 4.0 / 3.0, 0.004, 2.0):
+        assert abs((1.0 / (1.0 + math.exp(-math.sqrt(wrong)))) - g) > 1e-3
 
 
 def test_gate_sign_flip_gives_complement():
