@@ -15,13 +15,16 @@ Method:
 * Inputs are resident in HBM before timing. The weights are replicated 16
   times (1.23 GB, over four times the 256 MB Infinity Cache) and step i reads
   copy i % 16, so every step streams its matrix from HBM.
-* W warm-up steps run first (eagerly). The K timed steps are captured into
-  one HIP graph (copy i % 16); on the launching stream a sleep kernel keeps
-  the GPU busy while the host enqueues a start event, the graph and an end
-  event, so neither the host's launch cost nor the graph's upload lands
-  inside the timed region: ms_per_step = event time / K.
-* Roofline of the dominant kernel (q2k_mmvq): the same method over a graph
-  of products alone (at least 640 launches), achieved = algorithmic bytes
+* The W warm-up steps and the K timed steps are captured into two HIP
+  graphs (copy i % 16) and uploaded. On the launching stream a short sleep
+  kernel covers the host's enqueueing, then the warm-up graph runs, then a
+  start event, the timed graph and an end event: the GPU is busy when the
+  start event is reached and the events bracket exactly the K steps;
+  ms_per_step = event time / K.
+* Roofline of the dominant kernel (q2k_mmvq), timed first for each m:
+  products alone, a graph of 128 launches replayed 4 times untimed (the
+  GPU's clocks settle during the first milliseconds of streaming) and then
+  5 times between HIP events, achieved = algorithmic bytes
   per launch / average launch time between the events (gaps between
   consecutive kernels included). Beside it, the per-dispatch average of the
   same kernel from the committed rocprofv3 kernel trace
@@ -218,27 +221,101 @@ def sleep_cycles_for(torch, stream, us: float) -> int:
     return int(per_us * us)
 
 
-def timed_steps(torch, stream, fn, first: int, count: int, busy: int) -> float:
-    """Seconds per call of fn(i), i = first .. first+count-1: the calls are
-    captured into one HIP graph; on `stream` a sleep kernel of `busy` cycles
-    keeps the GPU busy while the host enqueues the start event, the graph and
-    the end event, so the events bracket exactly the `count` calls."""
+_HIP = None
+
+
+def graph_upload(g, stream) -> None:
+    """hipGraphUpload of a captured graph's executable on `stream`, so that its
+    first replay costs the host no upload (torch does not expose the call)."""
+    global _HIP
+    import ctypes
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        _HIP.hipGraphUpload.restype = ctypes.c_int
+    rc = _HIP.hipGraphUpload(ctypes.c_void_p(g.raw_cuda_graph_exec()),
+                             ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"hipGraphUpload failed ({rc})")
+
+
+def capture(torch, stream, fn, first: int, count: int):
+    """fn(i), i = first .. first+count-1, captured into one uploaded HIP graph
+    (None when count is 0)."""
+    if count <= 0:
+        return None
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for i in range(first, first + count):
             fn(i)
+    graph_upload(g, stream)
     torch.cuda.synchronize()
+    return g
+
+
+def timed_steps(torch, stream, fn, warm: int, count: int, busy: int, reps: int = 1) -> float:
+    """Seconds per call of fn(i) over `count` calls i = warm .. warm+count-1,
+    after `warm` untimed calls i = 0 .. warm-1. Both runs are captured into
+    uploaded HIP graphs; on `stream` a short sleep kernel (`busy` cycles)
+    covers the host's enqueueing, then the warm-up graph, the start event,
+    `reps` replays of the timed graph and the end event: the events bracket
+    exactly reps * count calls, with the GPU busy up to the start event."""
+    g_warm = capture(torch, stream, fn, 0, warm)
+    g = capture(torch, stream, fn, warm, count)
     with torch.cuda.stream(stream):
+        torch.cuda._sleep(busy)
+        if g_warm is not None:
+            g_warm.replay()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(busy)
         ev0.record(stream)
-        g.replay()
+        for _ in range(reps):
+            g.replay()
+        ev1.record(stream)
+        ev1.synchronize()
+    del g, g_warm
+    return ev0.elapsed_time(ev1) / 1e3 / (count * reps)
+
+
+def replay_timed(torch, stream, fn, count: int, reps: int, warm_reps: int = 1) -> float:
+    """Seconds per call of fn(i), i = 0 .. count-1, captured into one HIP
+    graph: `warm_reps` untimed replays (they also keep the GPU busy while the
+    host enqueues the rest), then `reps` replays between HIP events."""
+    g = capture(torch, stream, fn, 0, count)
+    with torch.cuda.stream(stream):
+        for _ in range(warm_reps):
+            g.replay()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            g.replay()
         ev1.record(stream)
         ev1.synchronize()
     del g
-    return ev0.elapsed_time(ev1) / 1e3 / count
+    return ev0.elapsed_time(ev1) / 1e3 / (count * reps)
+
+
+ROOF_GRAPH, ROOF_WARM_REPS, ROOF_REPS = 128, 4, 5
+
+
+def product_roofline(torch, q2, stream, copies, x8, m: int, same_copy: bool = True):
+    """Average time of one q2k_mmvq launch on the large verify matrix: a
+    graph of 128 launches (copy i % 16), 4 untimed replays (~7 ms: after an
+    idle GPU the first few ms of streaming run slower, up to ~18 us per
+    launch, before the clocks settle), then 5 replays (640 launches) between
+    HIP events; with same_copy also the same with one weight copy for every
+    launch (cache-resident reference). Replaying one graph matters: a
+    second graph of the same launches measured ~0.6 us per launch slower."""
+    xq = q2.q8_1_rows(x8[:m].contiguous())
+    y = torch.empty((m, N), dtype=torch.float32, device=x8.device)
+    launch_s = replay_timed(torch, stream, lambda i: q2.q2k_mmvq(copies[i % COPIES], xq, N, K, m, out=y),
+                            ROOF_GRAPH, ROOF_REPS, ROOF_WARM_REPS)
+    warm_s = None
+    if same_copy:
+        warm_s = replay_timed(torch, stream, lambda i: q2.q2k_mmvq(copies[0], xq, N, K, m, out=y), 128, 2)
+    return launch_s, warm_s
 
 
 def _roof(nbytes: int, us: float) -> dict:
@@ -628,12 +705,23 @@ def run(args):
     w0 = torch.from_numpy(case.w.reshape(-1)).to(dev)
     copies = [w0] + [w0.clone() for _ in range(COPIES - 1)]
     x8 = syn.bf16_bits_to_tensor(case.x_bits).to(dev)
+    if args.roofline_only:
+        # only the product launches behind `roofline` (for kernel traces)
+        stream = torch.cuda.Stream()
+        out = {}
+        for m in (1, 8):
+            launch_s, _ = product_roofline(torch, q2, stream, copies, x8, m, same_copy=False)
+            out[f"m{m}"] = {"us_per_launch": round(launch_s * 1e6, 3),
+                            "achieved_gbs": round(mmvq_bytes(m) / launch_s / 1e9, 1),
+                            "frac": round(mmvq_bytes(m) / launch_s / 1e9 / PEAK_GBS, 4)}
+        print(json.dumps({"roofline_only": out}), flush=True)
+        return
 
     results = {}
     stream = torch.cuda.Stream()
-    busy = sleep_cycles_for(torch, stream, 3000.0)     # ~3 ms of GPU time ahead of each graph
+    busy = sleep_cycles_for(torch, stream, 500.0)      # ~0.5 ms of GPU time ahead of each run
     warm, steps = args.warmup, args.steps
-    roof_launches = max(steps, 640)
+    roof_launches = ROOF_GRAPH * ROOF_REPS
     for m in (1, 8):
         x = x8[:m].contiguous()
         xq = torch.empty(q2.q8_1_rows_bytes(m, K), dtype=torch.uint8, device=dev)
@@ -647,22 +735,13 @@ def run(args):
             q2.q8_1_rows(x, out=xq)
             q2.q2k_mmvq(copies[i % COPIES], xq, N, K, m, out=y)
 
-        def product(i):
-            q2.q2k_mmvq(copies[i % COPIES], xq, N, K, m, out=y)
-
-        def product_same_copy(i):
-            # cache-resident reference: the 77 MB matrix fits the 256 MB
-            # Infinity Cache; reported beside, never the roofline figure
-            q2.q2k_mmvq(copies[0], xq, N, K, m, out=y)
-
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            for i in range(warm):            # the W untimed warm-up steps
-                step(i)
+        # the dominant kernel alone first (its warm-up also brings the GPU to
+        # its sustained clocks); the same-copy figure is cache-resident (the
+        # 77 MB matrix fits the 256 MB Infinity Cache): reported beside, never
+        # the roofline figure
+        launch_s, warm_s = product_roofline(torch, q2, stream, copies, x8, m)
         step_s = timed_steps(torch, stream, step, warm, steps, busy)
         two_s = timed_steps(torch, stream, step_two_calls, warm, steps, busy)
-        launch_s = timed_steps(torch, stream, product, warm, roof_launches, busy)
-        warm_s = timed_steps(torch, stream, product_same_copy, 0, 256, busy)
         step(warm + steps - 1)               # y of the last timed step, for the parity check
         torch.cuda.synchronize()
         step_bytes = mmvq_bytes(m) + q8_bytes(m)
@@ -694,8 +773,9 @@ def run(args):
                "kernel": f"q2k_mmvq ({KERNEL_INSTANCES[m]})",
                "bytes_per_launch": mmvq_bytes(m),
                "us_per_launch": round(r["launch_s"] * 1e6, 3),
-               "timing": f"HIP events around {roof_launches} back-to-back launches in one graph "
-                         "(gaps between kernels included)"}
+               "timing": f"HIP events around {roof_launches} back-to-back launches (5 replays "
+                         "of a 128-launch graph after 4 untimed replays; gaps between kernels "
+                         "included)"}
         rp = measured_rocprof(m)
         if rp is not None:
             gbs = mmvq_bytes(m) / rp / 1e3
@@ -827,6 +907,44 @@ def traffic_from(fetch_csv: str, write_csv: str, out: str):
     print(json.dumps(rec))
 
 
+def rocprof_from(trace_csv: str, out: str):
+    """The product kernel's average duration at m = 1 and m = 8 over exactly
+    the dispatches the roofline's HIP events bracket (the last 640 of each
+    instantiation in a rocprofv3 --kernel-trace run of --roofline-only),
+    with the hash of each kernel's source, so that bench.py reports it only
+    while the kernel is unchanged."""
+    import csv
+    with open(trace_csv, newline="") as f:
+        rows = list(csv.DictReader(f))
+    timed = ROOF_GRAPH * ROOF_REPS
+    rec = {"command": ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d <out> -o prof "
+                       "--output-format csv -- python3 /root/repo/bench.py --roofline-only; "
+                       "python3 bench.py --rocprof-from <out>/prof_kernel_trace.csv"),
+           "dispatches": f"per m: {ROOF_WARM_REPS} untimed and {ROOF_REPS} timed replays of a "
+                         f"{ROOF_GRAPH}-launch graph over 16 rotating weight copies; the average is "
+                         f"over the {timed} timed dispatches (the last {timed} of the kernel)"}
+    for m, inst in KERNEL_INSTANCES.items():
+        hit = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+                     if inst in r["Kernel_Name"])
+        if len(hit) < timed:
+            raise SystemExit(f"{trace_csv}: {len(hit)} dispatches of {inst}, need {timed}")
+        d = np.array([(e - s_) / 1e3 for s_, e in hit[-timed:]])
+        avg_us = float(d.mean())
+        span_us = (hit[-1][1] - hit[-timed][0]) / 1e3 / timed
+        rec[f"m{m}"] = {"kernel": inst, "kernel_hash": kernel_hash(m), "dispatches": timed,
+                        "avg_us": round(avg_us, 4), "median_us": round(float(np.median(d)), 3),
+                        "p10_us": round(float(np.percentile(d, 10)), 3),
+                        "p90_us": round(float(np.percentile(d, 90)), 3),
+                        "span_per_dispatch_us": round(span_us, 4),
+                        "algorithmic_bytes": mmvq_bytes(m),
+                        "achieved_gbs": round(mmvq_bytes(m) / avg_us / 1e3, 1),
+                        "frac": round(mmvq_bytes(m) / avg_us / 1e3 / PEAK_GBS, 4)}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -839,11 +957,19 @@ def main():
                          "'headline' only their JSON is printed (profiling runs)")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the large-verify m = 1 and m = 8 steps (for kernel traces)")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the product launches the roofline figures time (for kernel traces)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic record from two counter runs and exit")
+    ap.add_argument("--rocprof-from", metavar="KERNEL_TRACE_CSV",
+                    help="write the product kernels' rocprofv3 averages from the kernel trace of "
+                         "a --roofline-only run and exit")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from, TRAFFIC_FILE)
+        return
+    if args.rocprof_from:
+        rocprof_from(args.rocprof_from, ROCPROF_FILE)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

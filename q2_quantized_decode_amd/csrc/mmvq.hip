@@ -281,12 +281,12 @@ __device__ __forceinline__ double half_block_value(const WHalf& w, const AHalf& 
 }
 
 // Sum over a group of gs lanes holding the half blocks of one row in the
-// order h * gs/2 + b: pairs of neighbours first (the pairwise tree over the
-// row's super-blocks for each half, then the two halves), the same tree as
-// every other product kernel.
+// order 2b + h: lane offsets 2, 4, .., gs/2 first (the pairwise tree over
+// the row's super-blocks for each half), then 1 (the two halves), the same
+// tree as every other product kernel.
 __device__ __forceinline__ double group_sum(double v, int gs) {
-  for (int off = 1; off < gs; off <<= 1) v += __shfl_xor(v, off);
-  return v;
+  for (int off = 2; off < gs; off <<= 1) v += __shfl_xor(v, off);
+  return v + __shfl_xor(v, 1);
 }
 
 __device__ __forceinline__ void store_dots(int32_t* dots, const WHalf& w, const AHalf& a, int t,
@@ -362,24 +362,40 @@ __device__ __forceinline__ double halve(double x, double y, int lane) {
 }
 
 // Sum eight per-lane values a[0..7] (eight row steps) over groups of
-// GS = 1 << GSL lanes (GS >= 8) at once, neighbours first: three halving
-// levels (lane pairs l ^ 1, l ^ 2, l ^ 4) leave lane l holding step l & 7
-// summed over its 8 lanes, and the levels l ^ 8, l ^ 16, l ^ 32 finish the
-// group. With lanes in the order h * GS/2 + b this is the pairwise tree over
-// the super-blocks of each half, then the two halves.
+// GS = 1 << GSL lanes (GS >= 8) at once. Lanes hold half blocks in the order
+// 2b + h, so the pairwise tree over the super-blocks takes the lane offsets
+// 2, 4, .., GS/2 and the two halves offset 1, last. Three halving levels
+// (offsets 2, 4, 8; for GS = 8: 2, 4, 1) leave lane l holding step
+// reduce8_slot(l) summed over its 8 lanes; the remaining offsets finish the
+// group.
 template <int GSL>
 __device__ __forceinline__ double reduce8(const double a[8], int lane) {
   constexpr int GS = 1 << GSL;
+  constexpr int O3 = GS >= 16 ? 8 : 1;
   double b4[4], b2[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) b4[i] = halve<1>(a[2 * i], a[2 * i + 1], lane);
+  for (int i = 0; i < 4; ++i) b4[i] = halve<2>(a[2 * i], a[2 * i + 1], lane);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) b2[i] = halve<2>(b4[2 * i], b4[2 * i + 1], lane);
-  double v = halve<4>(b2[0], b2[1], lane);
-  if constexpr (GS >= 16) v += dpp_f64<DppPartner<8>::ctrl>(v);
+  for (int i = 0; i < 2; ++i) b2[i] = halve<4>(b4[2 * i], b4[2 * i + 1], lane);
+  double v = halve<O3>(b2[0], b2[1], lane);
   if constexpr (GS >= 32) v = halve<16>(v, v, lane);
   if constexpr (GS >= 64) v = halve<32>(v, v, lane);
+  if constexpr (GS >= 16) v += dpp_f64<DppPartner<1>::ctrl>(v);
   return v;
+}
+
+// The step (0..7) that reduce8 leaves on lane l, and whether l is the one
+// lane of its row group that writes it.
+template <int GSL>
+__device__ __forceinline__ int reduce8_slot(int lane) {
+  if constexpr (GSL >= 4) return (lane >> 1) & 7;
+  return ((lane >> 1) & 3) | ((lane & 1) << 2);
+}
+
+template <int GSL>
+__device__ __forceinline__ bool reduce8_writer(int lane) {
+  if constexpr (GSL >= 4) return (lane & ((1 << GSL) - 1) & ~0xE) == 0;
+  return true;
 }
 
 // half_block_value for the run kernel: dq holds d8_j with the x4 of planes
@@ -590,19 +606,19 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
 
   const int k = k0;
   const int nb = k >> 8;
-  // lane l of a row group takes half h = l >> (GSL-1) of super-block
-  // b = l & (GS/2 - 1) (GS/2 is the row's block count rounded up to a power
-  // of two); lanes past the row's blocks read block 0 and add +0
+  // lane l of a row group takes half h = l & 1 of super-block b = (l & (GS-1))
+  // >> 1 (GS/2 is the row's block count rounded up to a power of two);
+  // lanes past the row's blocks read block 0 and add +0
   const int hb = lane & (GS - 1);
   const int prow = lane >> GSL;
-  const int braw = hb & (GS / 2 - 1);
+  const int braw = hb >> 1;
   const bool hb_ok = braw < nb;
   const int b = hb_ok ? braw : 0;
-  const int h = hb >> (GSL - 1);
+  const int h = hb & 1;
   const uint32_t rowbytes = (uint32_t)nb * kBlockBytes;
   const uint32_t step_bytes = (uint32_t)P * rowbytes;
-  const int slot = lane & 7;                     // the step reduce8 leaves on this lane
-  const bool writer = (lane & (GS - 1)) < 8;
+  const int slot = reduce8_slot<GSL>(lane);      // the step reduce8 leaves on this lane
+  const bool writer = reduce8_writer<GSL>(lane);
 
   // The run's steps are J.it + st * S, st = 0..CH-1.
   const int S = J.stride;
@@ -738,13 +754,13 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
   const int gs = 1 << p.gs_log2;
   const int P = 64 >> p.gs_log2;
   const int prow = lane >> p.gs_log2;
-  // half h = hb >> (gs_log2 - 1) of super-block hb & (gs/2 - 1), as in
-  // mmvq_m1_kernel (lanes past the row's blocks take block 0 and add +0)
+  // half h = hb & 1 of super-block hb >> 1, as in mmvq_m1_kernel (lanes
+  // past the row's blocks take block 0 and add +0)
   const int hb = lane & (gs - 1);
-  const int braw = hb & ((gs >> 1) - 1);
+  const int braw = hb >> 1;
   const bool hb_ok = braw < nb;
   const int b = hb_ok ? braw : 0;
-  const int h = hb >> (p.gs_log2 - 1);
+  const int h = hb & 1;
   const size_t rowbytes = (size_t)nb * kBlockBytes;
 
   // token split (one-token kernel only): as in mmvq_m1_kernel

@@ -368,7 +368,8 @@ __device__ __forceinline__ void tile_half(const uint8_t* lds, const uint8_t* Wro
                      : pl == 1 ? plane_weights<1>(cur.qs, scw, so)
                      : pl == 2 ? plane_weights<2>(cur.qs, scw, so)
                                : plane_weights<3>(cur.qs, scw, so);
-        const int mb = (int)(__builtin_amdgcn_ubfe(scw, so + 4u, 4) * 0x01010101u);
+        // the min nibble in all four bytes (byte 0 of the field, selected four times)
+        const int mb = (int)__builtin_amdgcn_perm(0u, __builtin_amdgcn_ubfe(scw, so + 4u, 4), 0u);
         const v4i wm = v4i{mb, mb, mb, mb};
         const v4i cI = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, wq, v4i{0, 0, 0, 0}, 0, 0, 0);
         const v4i cM = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, wm, v4i{0, 0, 0, 0}, 0, 0, 0);

@@ -98,3 +98,33 @@ def test_more_than_one_gpu_is_refused():
     assert res.returncode == 2
     assert "one GPU" in res.stderr
     assert res.stdout.strip() == ""
+
+
+def test_rocprof_record_from_kernel_trace(tmp_path, monkeypatch):
+    """--rocprof-from averages the last 640 dispatches of each product
+    instantiation in a kernel trace (the ones the roofline's events bracket);
+    bench.py reports the average only while the kernel source hash matches."""
+    timed = bench.ROOF_GRAPH * bench.ROOF_REPS
+    header = '"Kind","Kernel_Name","Start_Timestamp","End_Timestamp"'
+    lines = [header]
+    t = 1000
+    for m, warm_us, timed_us in ((1, 18.0, 13.5), (8, 30.0, 20.0)):
+        name = f"void q2k::{bench.KERNEL_INSTANCES[m]}(unsigned char const*, float*)"
+        for i in range(bench.ROOF_GRAPH * bench.ROOF_WARM_REPS + timed):
+            dur = warm_us if i < bench.ROOF_GRAPH * bench.ROOF_WARM_REPS else timed_us
+            lines.append(f'"KERNEL_DISPATCH","{name}",{t},{t + int(dur * 1000)}')
+            t += int(dur * 1000) + 100
+    lines.append(f'"KERNEL_DISPATCH","void q2k::mmvq_m1_kernel<6, 4, 32, 1>(x)",{t},{t + 5000}')
+    csv_path = tmp_path / "prof_kernel_trace.csv"
+    csv_path.write_text("\n".join(lines) + "\n")
+    out = tmp_path / "rec.json"
+    bench.rocprof_from(str(csv_path), str(out))
+    rec = json.loads(out.read_text())
+    assert rec["m1"]["avg_us"] == 13.5 and rec["m8"]["avg_us"] == 20.0
+    assert rec["m1"]["dispatches"] == timed
+    assert rec["m1"]["frac"] == round(bench.mmvq_bytes(1) / 13.5 / 1e3 / 8000.0, 4)
+    monkeypatch.setattr(bench, "ROCPROF_FILE", str(out))
+    assert bench.measured_rocprof(1) == 13.5
+    rec["m1"]["kernel_hash"] = "0" * 16
+    out.write_text(json.dumps(rec))
+    assert bench.measured_rocprof(1) is None
