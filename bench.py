@@ -606,8 +606,16 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
     # prefill positions 0..4095 once so the decode steps see a real look-back
     q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks, 0)
 
+    ws = torch.empty(q2.engram_step_workspace_bytes(3, 4, e.hc, e.dim), dtype=torch.uint8, device=dev)
+
     def step(i):
-        # hash (hashed layer 1) + gather + dequant + q8_1 in one launch
+        # one call: hash (hashed layer 1), gather, dequant and q8_1 in the wkv
+        # product's prologue (one launch), then the gate
+        q2.engram_step(tm, mu, pr, of, hc.pad_id, cache, toks[i % 64:i % 64 + 1], 4096 + (i % 64), 1,
+                       table, 500000, copies[i % copies_n], qk, h, e.eps, workspace=ws)
+
+    def step_rows_apart(i):
+        # hash + gather + dequant + q8_1 in one launch of their own
         q2.engram_rows_q8_1(tm, mu, pr, of, hc.pad_id, cache, toks[i % 64:i % 64 + 1], 4096 + (i % 64), 1,
                             table, 500000, xq=xq)
         q2.q2k_mmvq(copies[i % copies_n], xq, n_out, 2048, 1, out=kv)
@@ -636,6 +644,7 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
         q2.engram_gate(h, kv, qk, e.eps)
 
     us_step = timed(step, copies_n)
+    us_step_rows_apart = timed(step_rows_apart, copies_n)
     us_step_hash_apart = timed(step_hash_apart, copies_n)
     us_step_unfused = timed(step_unfused, copies_n)
     us_step_bf16 = timed(step_bf16, copies_n)
@@ -647,12 +656,15 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
     pre = torch.empty((2, 4096, 8), dtype=torch.int64, device=dev)
     us_pre = timed(lambda i: q2.engram_hash(tm, mu, pr, of, hc.pad_id, cache, toks, 0, out=pre), 16)
     wkv_bytes = w0.numel()
-    return {"workload": "engram step, one token: hash + 8-row gather + dequant + q8_1 (one "
-                        "launch, engram_rows_q8_1) -> wkv Q2_K [20480, 2048] -> gate [1, 4, 4096]; "
-                        "80 rotating wkv copies. hash_apart: the hash as its own launch; unfused: "
-                        "hash, gather and q8_1 as three launches; the bf16 route skips q8_1: "
-                        "gathered bf16 rows straight into the wkv product",
+    return {"workload": "engram step, one token (engram_step): hash + 8-row gather + dequant + "
+                        "q8_1 in the prologue of the wkv Q2_K [20480, 2048] product (one launch) -> "
+                        "gate [1, 4, 4096]; 80 rotating wkv copies. rows_apart: hash, gather, "
+                        "dequant and q8_1 as one launch of their own (engram_rows_q8_1); "
+                        "hash_apart: the hash as its own launch as well; unfused: hash, gather and "
+                        "q8_1 as three launches; the bf16 route skips q8_1: gathered bf16 rows "
+                        "straight into the wkv product",
             "us_per_step": round(us_step, 3), "tokens_per_s": round(1e6 / us_step, 1),
+            "us_per_step_rows_apart": round(us_step_rows_apart, 3),
             "us_per_step_hash_apart": round(us_step_hash_apart, 3),
             "us_per_step_unfused": round(us_step_unfused, 3),
             "us_per_step_bf16_route": round(us_step_bf16, 3),

@@ -391,6 +391,46 @@ Q2K_API int32_t engram_rows_q8_1(const int64_t* token_map_dev, int64_t vocab,
                                  int64_t* ids_out_dev, void* rows_out_dev, void* xq_dev,
                                  size_t xq_bytes, int32_t* err_flag_dev, void* stream);
 
+/* One decode token through the whole engram layer step (engram_v41.rs module
+ * doc steps 1-4; engram_v41/apply.rs, EngramV41::apply with one token and
+ * the Q2_K projection): the token's row ids of hashed layer `layer`
+ * (engram_hash), the gather, dequantisation and q8_1 of those rows viewed as
+ * one row (q2k_dequant_rows_q8_1), the wkv projection of that row (q2k_mmvq,
+ * m = 1) into kv, and the gate on h (engram_gate). The same bits in h, the
+ * cache and the error flag as engram_rows_q8_1 + q2k_mmvq + engram_gate.
+ * When the projection takes the run kernel (at least 2048 row steps) the
+ * first three stages are one launch: every workgroup of the product forms
+ * the q8_1 row in its prologue while its first weight loads are in flight;
+ * then the gate launch.
+ *   token_map_dev .. layer : as in engram_rows_q8_1 (cols = (max_ngram-1) *
+ *                  n_heads <= 32 row ids, so the projection's input width is
+ *                  k = 256 * cols).
+ *   table_dev, n_table_rows : as in q2k_dequant_rows.
+ *   wkv_dev      : Q2_K [(hc+1)*dim, 256*cols].
+ *   qk_dev, h_dev, hc, dim, eps : as in engram_gate with t = 1 (h updated in
+ *                  place).
+ *   workspace_dev, workspace_bytes : device memory the step may overwrite
+ *                  (the pages keep kv in a workspace of EngramV41: its kv
+ *                  buffer): kv f32 [(hc+1)*dim] then the q8_1 row, at least
+ *                  engram_step_workspace_bytes(max_ngram, n_heads, hc, dim)
+ *                  bytes, 256-byte aligned; its contents after the call are
+ *                  kv (rounded up to 256 bytes) and the q8_1 row.
+ *   err_flag_dev : nullable, as in engram_rows_q8_1.
+ * Errors: Q2K_EINVAL (null pointers; h, the cache or the workspace
+ * overlapping each other or an input), Q2K_ESHAPE (as the calls it
+ * replaces), Q2K_ESPACE (workspace too small), Q2K_EALIGN. */
+Q2K_API size_t engram_step_workspace_bytes(int32_t max_ngram, int32_t n_heads, int32_t hc,
+                                           int32_t dim);
+Q2K_API int32_t engram_step(const int64_t* token_map_dev, int64_t vocab,
+                            const int64_t* multipliers_dev, const int64_t* primes_dev,
+                            const int64_t* offsets_dev, int32_t n_layers, int32_t max_ngram,
+                            int32_t n_heads, int64_t pad_id, int64_t* cache_dev, int64_t cache_len,
+                            const int32_t* token_dev, int64_t pos, int32_t layer,
+                            const void* table_dev, int64_t n_table_rows, const void* wkv_dev,
+                            const float* qk_dev, float* h_dev, int32_t hc, int32_t dim, float eps,
+                            void* workspace_dev, size_t workspace_bytes, int32_t* err_flag_dev,
+                            void* stream);
+
 /* Which kernel runs the Q2_K x q8_1 products (q2k_mmvq, its pair, expert
  * and grouped forms, q2k_mmq and q2k_block_dots), process-wide. Every kernel
  * forms the same exact int32 block sums and follows the fixed summation

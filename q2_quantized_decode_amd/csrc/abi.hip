@@ -38,6 +38,12 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return na > 0 && nb > 0 && x < y + nb && y < x + na;
 }
 
+// The engram step's kv rows in its workspace, rounded to 256 bytes; the
+// q8_1 row of the gathered rows follows them.
+size_t engram_kv_bytes(int32_t hc, int32_t dim) {
+  return ((size_t)(hc + 1) * (size_t)dim * 4 + 255) / 256 * 256;
+}
+
 size_t q2k_matrix_bytes(int64_t n, int64_t k) { return (size_t)n * (size_t)(k / 256) * 84; }
 
 int32_t check_k(const char* fn, int32_t k) {
@@ -520,6 +526,108 @@ int32_t engram_rows_q8_1(const int64_t* token_map_dev, int64_t vocab, const int6
                   fn);
 }
 
+}  // extern "C"
+
+namespace {
+
+// engram_step on a workspace ws of ws_bytes bytes (the caller's, or the
+// library's own scratch array for engram_step_noalloc).
+int32_t engram_step_on(const char* fn, const int64_t* token_map_dev, int64_t vocab,
+                       const int64_t* multipliers_dev, const int64_t* primes_dev,
+                       const int64_t* offsets_dev, int32_t n_layers, int32_t max_ngram, int32_t n_heads,
+                       int64_t pad_id, int64_t* cache_dev, int64_t cache_len, const int32_t* token_dev,
+                       int64_t pos, int32_t layer, const void* table_dev, int64_t n_table_rows,
+                       const void* wkv_dev, const float* qk_dev, float* h_dev, int32_t hc, int32_t dim,
+                       float eps, void* ws, size_t ws_bytes, int32_t* err_flag_dev, void* stream) {
+  if (!token_map_dev || !multipliers_dev || !primes_dev || !offsets_dev || !cache_dev || !token_dev ||
+      !table_dev || !wkv_dev || !qk_dev || !h_dev || !ws)
+    return fail(Q2K_EINVAL, "%s: null pointer", fn);
+  if (vocab < 1) return fail(Q2K_ESHAPE, "%s: vocab = %lld < 1", fn, (long long)vocab);
+  if (n_layers < 1 || n_layers > 64) return fail(Q2K_ESHAPE, "%s: n_layers = %d outside 1..64", fn, n_layers);
+  if (max_ngram < 2 || max_ngram > 8) return fail(Q2K_ESHAPE, "%s: max_ngram = %d outside 2..8", fn, max_ngram);
+  if (n_heads < 1 || n_heads > 64) return fail(Q2K_ESHAPE, "%s: n_heads = %d outside 1..64", fn, n_heads);
+  if (layer < 0 || layer >= n_layers) return fail(Q2K_ESHAPE, "%s: layer = %d outside 0..%d", fn, layer, n_layers - 1);
+  const int32_t cols = (max_ngram - 1) * n_heads;
+  if (cols > 32) return fail(Q2K_ESHAPE, "%s: %d row ids per token, at most 32", fn, cols);
+  if (pos < 0 || cache_len < pos + 1)
+    return fail(Q2K_ESHAPE, "%s: position %lld outside the cache of %lld", fn, (long long)pos, (long long)cache_len);
+  if (n_table_rows < 1) return fail(Q2K_ESHAPE, "%s: empty table", fn);
+  if (hc < 1 || hc > 4) return fail(Q2K_ESHAPE, "%s: hc = %d outside 1..4", fn, hc);
+  if (dim < 1 || (int64_t)(hc + 1) * dim > INT32_MAX / 4)
+    return fail(Q2K_ESHAPE, "%s: dim = %d outside 1..(2^31/4)/(hc+1)", fn, dim);
+  if (!(eps >= 0.0f)) return fail(Q2K_ESHAPE, "%s: eps must be >= 0", fn);
+  if (!aligned(token_map_dev, 8) || !aligned(multipliers_dev, 8) || !aligned(primes_dev, 8) ||
+      !aligned(offsets_dev, 8) || !aligned(cache_dev, 8) || !aligned(token_dev, 4) ||
+      !aligned(table_dev, 4) || !aligned(wkv_dev, 4) || !aligned(qk_dev, 4) || !aligned(h_dev, 4) ||
+      !aligned(ws, 256))
+    return fail(Q2K_EALIGN, "%s: 64-bit arrays 8-byte, token, table, wkv, qk and h 4-byte, the "
+                "workspace 256-byte aligned", fn);
+  const int32_t n = (hc + 1) * dim, k = cols * 256;
+  const size_t kvb = engram_kv_bytes(hc, dim);
+  const size_t need = kvb + q8_1_rows_bytes(1, k);
+  if (ws_bytes < need) return fail(Q2K_ESPACE, "%s: workspace holds %zu bytes, %zu needed", fn, ws_bytes, need);
+  // written: h, cache, workspace; read: everything else
+  const void* wr[3] = {h_dev, cache_dev, ws};
+  const size_t wr_b[3] = {(size_t)hc * dim * 4, (size_t)cache_len * 8, need};
+  const void* rd[8] = {token_map_dev, multipliers_dev, primes_dev, offsets_dev, token_dev, table_dev,
+                       wkv_dev, qk_dev};
+  const size_t rd_b[8] = {(size_t)vocab * 8, (size_t)n_layers * max_ngram * 8,
+                          (size_t)n_layers * (max_ngram - 1) * n_heads * 8, (size_t)n_layers * cols * 8, 4,
+                          (size_t)n_table_rows * 84, q2k_matrix_bytes(n, k), (size_t)hc * dim * 4};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(wr[a], wr_b[a], wr[b], wr_b[b])) return fail(Q2K_EINVAL, "%s: h, the cache and the workspace must not overlap", fn);
+    for (int b = 0; b < 8; ++b)
+      if (overlap(wr[a], wr_b[a], rd[b], rd_b[b])) return fail(Q2K_EINVAL, "%s: h, the cache or the workspace overlaps an input", fn);
+  }
+  q2k::EngramRows E;
+  E.token_map = token_map_dev;
+  E.vocab = vocab;
+  E.mult = multipliers_dev;
+  E.primes = primes_dev;
+  E.offsets = offsets_dev;
+  E.layer = layer;
+  E.ng = max_ngram;
+  E.n_heads = n_heads;
+  E.pad_id = pad_id;
+  E.cache = cache_dev;
+  E.token = token_dev;
+  E.pos = pos;
+  E.table = static_cast<const uint8_t*>(table_dev);
+  E.n_table_rows = n_table_rows;
+  E.err_flag = err_flag_dev;
+  float* kv = static_cast<float*>(ws);
+  q2k::MmvqLaunch a{};
+  a.w[0] = wkv_dev;
+  a.y[0] = kv;
+  a.n[0] = n;
+  a.njobs = 1;
+  a.xq = static_cast<uint8_t*>(ws) + kvb;
+  a.k = k;
+  a.m = 1;
+  a.eg = &E;
+  const hipStream_t st = (hipStream_t)stream;
+  if (int32_t r = launched(q2k::launch_mmvq(a, st), fn)) return r;
+  return launched(q2k::launch_engram_gate(h_dev, kv, qk_dev, 1, hc, dim, eps, st), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t engram_step(const int64_t* token_map_dev, int64_t vocab, const int64_t* multipliers_dev,
+                    const int64_t* primes_dev, const int64_t* offsets_dev, int32_t n_layers,
+                    int32_t max_ngram, int32_t n_heads, int64_t pad_id, int64_t* cache_dev,
+                    int64_t cache_len, const int32_t* token_dev, int64_t pos, int32_t layer,
+                    const void* table_dev, int64_t n_table_rows, const void* wkv_dev,
+                    const float* qk_dev, float* h_dev, int32_t hc, int32_t dim, float eps,
+                    void* workspace_dev, size_t workspace_bytes, int32_t* err_flag_dev, void* stream) {
+  return engram_step_on("engram_step", token_map_dev, vocab, multipliers_dev, primes_dev, offsets_dev,
+                        n_layers, max_ngram, n_heads, pad_id, cache_dev, cache_len, token_dev, pos, layer,
+                        table_dev, n_table_rows, wkv_dev, qk_dev, h_dev, hc, dim, eps, workspace_dev,
+                        workspace_bytes, err_flag_dev, stream);
+}
+
 int32_t q2k_dequant_rows_q8_1(const void* table_dev, int64_t n_table_rows, const int64_t* ids_dev,
                               int32_t n_rows, void* out_bf16_dev, void* xq_dev, size_t xq_bytes,
                               int32_t* err_flag_dev, void* stream) {
@@ -594,6 +702,14 @@ int32_t engram_hash(const int64_t* token_map_dev, int64_t vocab, const int64_t* 
                                           n_layers, max_ngram, n_heads, pad_id, cache_dev, ids_dev, seqlen,
                                           start_pos, out_dev, err_flag_dev, (hipStream_t)stream),
                   fn);
+}
+
+size_t engram_step_workspace_bytes(int32_t max_ngram, int32_t n_heads, int32_t hc, int32_t dim) {
+  if (max_ngram < 2 || max_ngram > 8 || n_heads < 1 || n_heads > 64 || hc < 1 || hc > 4 || dim < 1)
+    return 0;
+  const int32_t cols = (max_ngram - 1) * n_heads;
+  if (cols > 32) return 0;
+  return engram_kv_bytes(hc, dim) + q8_1_rows_bytes(1, cols * 256);
 }
 
 int32_t q2k_product_kernel(int32_t n, int32_t k, int32_t m) {

@@ -151,72 +151,6 @@ __global__ __launch_bounds__(256) void engram_gate_vec_kernel(float* __restrict_
 // are written; only positions < start_pos are read from the cache).
 // A token id outside [0, vocab), or a prime <= 0, gives -1 for every row id
 // whose window reads it, -1 in the cache, and *err_flag = 1.
-constexpr int kMaxNgram = 8;
-
-// Window of position pos = start_pos + s for the hash: tok[0..ng-1] and
-// whether every token id it reads is valid. Position p >= start_pos reads
-// this call's ids, earlier positions the cache; from the first i with
-// pos < i or an unmapped (-1) id on, the token is pad_id. Returns the
-// compressed id of pos itself (what the cache keeps for it).
-__device__ __forceinline__ int64_t hash_window(const int64_t* __restrict__ token_map, int64_t vocab,
-                                               int ng, int64_t pad_id, const int64_t* cache,
-                                               const int32_t* __restrict__ ids, int64_t start_pos,
-                                               int64_t pos, int64_t tok[kMaxNgram], bool& ok) {
-  bool blocked = false;
-  int64_t own = -1;
-  for (int i = 0; i < ng; ++i) {
-    const int64_t p = pos >= i ? pos - i : 0;
-    int64_t src;
-    if (p >= start_pos) {
-      const int32_t id = ids[p - start_pos];
-      if (id < 0 || id >= vocab) {
-        ok = false;
-        src = -1;
-      } else {
-        src = token_map[id];
-      }
-    } else {
-      src = cache[p];
-    }
-    if (i == 0) own = src;
-    blocked = blocked || pos < i || src == -1;
-    tok[i] = blocked ? pad_id : src;
-  }
-  return own;
-}
-
-// Row ids of hashed layer l for a window: rolling = tok[0]*mult[l][0], then
-// rolling ^= tok[i]*mult[l][i] (64-bit wrapping); id (i, h) = (rolling mod
-// prime, in [0, prime)) + offset; -1 once the window is bad or a prime <= 0
-// has been met (in (i, h) order). Writes o[c] for c in [c0, c1) and returns
-// false when any id so far is -1.
-__device__ __forceinline__ bool hash_cols(const int64_t tok[kMaxNgram], const int64_t* __restrict__ mult,
-                                          const int64_t* __restrict__ primes,
-                                          const int64_t* __restrict__ offsets, int l, int ng,
-                                          int n_heads, bool ok, int c0, int c1, int64_t* o) {
-  const int cols = (ng - 1) * n_heads;
-  const int64_t* ml = mult + (int64_t)l * ng;
-  uint64_t rolling = (uint64_t)tok[0] * (uint64_t)ml[0];
-  for (int i = 1; i < ng; ++i) {
-    rolling ^= (uint64_t)tok[i] * (uint64_t)ml[i];
-    for (int h = 0; h < n_heads; ++h) {
-      const int col = (i - 1) * n_heads + h;
-      const int64_t pr = primes[((int64_t)l * (ng - 1) + (i - 1)) * n_heads + h];
-      int64_t v = -1;
-      if (ok && pr > 0) {
-        int64_t r = (int64_t)rolling % pr;
-        if (r < 0) r += pr;
-        v = (int64_t)((uint64_t)r + (uint64_t)offsets[(int64_t)l * cols + col]);
-      } else {
-        ok = false;
-      }
-      if (col >= c0 && col < c1) o[col - c0] = v;
-    }
-    if (i * n_heads >= c1) break;   // later columns are not asked for
-  }
-  return ok;
-}
-
 __global__ __launch_bounds__(256) void engram_hash_kernel(
     const int64_t* __restrict__ token_map, int64_t vocab, const int64_t* __restrict__ mult,
     const int64_t* __restrict__ primes, const int64_t* __restrict__ offsets, int n_layers, int ng,

@@ -59,6 +59,7 @@ struct MmvqParams {
   const float* su;                   // and up rows
   const uint8_t* xb16;               // narrow kernel with FQ: the token's bf16 row
   uint8_t* xq_out;                   // narrow kernel with FQ: receives its q8_1 row
+  EngramRows eg;                     // run kernel with FQ = 3: the engram rows of the input
 };
 
 // Touches every field of the argument block at once, so that its scalar
@@ -530,7 +531,13 @@ __device__ __forceinline__ void lds_barrier_m1() {
 //
 // FQ = 1 (fused quantisation, one token, one input row shared by every
 // matrix of the launch: a single matrix or an expert batch with a shared
-// input): xq0 is the bf16 row instead. FQ = 2 (expert batch, one input row
+// input): xq0 is the bf16 row instead. FQ = 3 (one matrix, one token): the
+// input row is a decode token's engram rows (p.eg): threads 0..cols-1 of
+// each workgroup compute the token's row ids of one hashed layer with the
+// hash kernels' device functions (workgroup 0 also stores the position's
+// compressed id into the cache and raises the error flag), then every
+// thread gathers, dequantises and quantises 8 values per pass into the LDS
+// row (workgroup 0 also writes it to xq_out), as engram_rows_q8_1 does. FQ = 2 (expert batch, one input row
 // per id, every workgroup inside one id's waves): the workgroup forms the
 // bf16 SwiGLU of its id's gate and up rows (p.sg, p.su) and quantises it;
 // the workgroup holding the id's first wave writes that q8_1 row to
@@ -655,6 +662,86 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
     __builtin_amdgcn_sched_barrier(0);   // keep the ring ahead of the quantisation
     if constexpr (FQ == 1) {
       q8_1_block_store(xs, blockIdx.x == 0 ? xq_out : nullptr, raw, tid, k, qthread);
+    } else if constexpr (FQ == 3) {
+      __shared__ int64_t rid[32];
+      const EngramRows& E = p.eg;
+      const int cols = k >> 8;
+      // Thread c < cols computes row id c with the hash kernels' rules
+      // (hash_window, hash_cols), every independent load issued at once:
+      // the token, the window's cached ids, the layer's multipliers and the
+      // column's prime and offset; then token -> token_map; the ids' table
+      // rows are the third and last dependent round.
+      const bool hthread = tid < cols;
+      const int c = hthread ? tid : 0;
+      const int ng = E.ng, nh = E.n_heads;
+      const int64_t pos = E.pos;
+      const int32_t t0 = E.token[0];
+      int64_t cw[kMaxNgram], mu[kMaxNgram];
+#pragma unroll
+      for (int i = 0; i < kMaxNgram; ++i) {
+        const int ii = i < ng ? i : ng - 1;
+        cw[i] = E.cache[pos >= ii ? pos - ii : 0];
+        mu[i] = E.mult[(int64_t)E.layer * ng + ii];
+      }
+      const int64_t pr = E.primes[(int64_t)E.layer * cols + c];
+      const int64_t of = E.offsets[(int64_t)E.layer * cols + c];
+      const bool tok_ok = t0 >= 0 && (int64_t)t0 < E.vocab;
+      const int64_t own = tok_ok ? E.token_map[tok_ok ? t0 : 0] : -1;
+      int64_t tk[kMaxNgram];
+      bool blocked = own == -1;
+      tk[0] = blocked ? E.pad_id : own;
+#pragma unroll
+      for (int i = 1; i < kMaxNgram; ++i) {
+        blocked = blocked || pos < i || cw[i] == -1;
+        tk[i] = blocked ? E.pad_id : cw[i];
+      }
+      const int ic = c / nh + 1;                   // the window length of column c
+      uint64_t rolling = (uint64_t)tk[0] * (uint64_t)mu[0];
+#pragma unroll
+      for (int i = 1; i < kMaxNgram; ++i)
+        if (i <= ic) rolling ^= (uint64_t)tk[i] * (uint64_t)mu[i];
+      // a prime <= 0 makes its column and every later one -1 (column order)
+      const uint64_t badp = __ballot(hthread && pr <= 0);
+      const bool ok = tok_ok && (badp & ((2ull << c) - 1ull)) == 0;
+      int64_t v = -1;
+      if (ok) {
+        int64_t r = (int64_t)rolling % pr;
+        if (r < 0) r += pr;
+        v = (int64_t)((uint64_t)r + (uint64_t)of);
+      }
+      if (hthread) {
+        rid[tid] = v;
+        if (blockIdx.x == 0) {
+          if (tid == 0) E.cache[pos] = own;
+          if (!ok && E.err_flag != nullptr) *E.err_flag = 1;
+        }
+      }
+      lds_barrier_m1();
+      for (int c0 = 0; c0 < (k >> 3); c0 += 256) {
+        const int chunk = c0 + tid;
+        const bool active = chunk < (k >> 3);
+        const int e0 = active ? chunk * 8 : 0;
+        const int64_t id = rid[e0 >> 8];
+        const int e = e0 & 255;
+        uint32_t bits[8];
+        if (id < 0 || id >= E.n_table_rows) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bits[i] = 0x7fc0u;
+          if (blockIdx.x == 0 && active && e == 0 && E.err_flag != nullptr) *E.err_flag = 1;
+        } else {
+          const uint8_t* blk = E.table + id * kBlockBytes;
+          q2k_dequant4(blk, e, bits);
+          q2k_dequant4(blk, e + 4, bits + 4);
+        }
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = bf16_bits_to_f32(bits[i]);
+        const Q8Lane r8 = q8_1_quant8(v);
+        if (active) {
+          q8_1_put8(r8, xs, e0, k);
+          if (blockIdx.x == 0 && xq_out != nullptr) q8_1_put8(r8, xq_out, e0, k);
+        }
+      }
     } else {
       float v[8];
 #pragma unroll
@@ -1207,6 +1294,22 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
     }
     const hipError_t e = launch_swiglu_q8_1_rows(a.sg, a.su, nullptr, const_cast<void*>(a.xq),
                                                  a.n_ids * a.m, a.k, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (a.eg != nullptr) {
+    // the input row is a decode token's engram rows: formed in the run
+    // kernel's prologue when the product takes it, else by the rows launch
+    p.eg = *a.eg;
+    if (m1_path && a.m == 1 && a.njobs == 1 && a.ids == nullptr && a.groups == 0 && !dots &&
+        a.k <= 8192 && tu.ring == 4) {
+      dispatch_m1_fused<3>(p, grid, nullptr, static_cast<uint8_t*>(const_cast<void*>(a.xq)), stream);
+      return hipGetLastError();
+    }
+    const EngramRows& E = *a.eg;
+    const hipError_t e = launch_engram_rows_q8_1(E.token_map, E.vocab, E.mult, E.primes, E.offsets,
+                                                 E.layer, E.ng, E.n_heads, E.pad_id, E.cache, E.token,
+                                                 E.pos, E.table, E.n_table_rows, nullptr, nullptr,
+                                                 const_cast<void*>(a.xq), E.err_flag, stream);
     if (e != hipSuccess) return e;
   }
   if (a.x_bf16 != nullptr) {

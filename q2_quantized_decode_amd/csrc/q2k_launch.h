@@ -13,6 +13,28 @@ constexpr int kMaxPlainJobs = 4;
 constexpr int kMaxM = 8;
 constexpr int kMaxExpertBases = 4;
 
+// One decode token's engram rows as the input of a product: the token's
+// hashed row ids of one hashed layer, the gathered table rows, dequantised
+// and quantised to one q8_1 row (engram_rows_q8_1 in the product's
+// prologue).
+struct EngramRows {
+  const int64_t* token_map = nullptr;
+  int64_t vocab = 0;
+  const int64_t* mult = nullptr;
+  const int64_t* primes = nullptr;
+  const int64_t* offsets = nullptr;
+  int32_t layer = 0;
+  int32_t ng = 0;
+  int32_t n_heads = 0;
+  int64_t pad_id = 0;
+  int64_t* cache = nullptr;
+  const int32_t* token = nullptr;
+  int64_t pos = 0;
+  const uint8_t* table = nullptr;
+  int64_t n_table_rows = 0;
+  int32_t* err_flag = nullptr;
+};
+
 struct MmvqLaunch {
   // Plain mode (ids == nullptr, groups == 0): job j multiplies w[j] [n[j], k]
   // by xq.
@@ -49,6 +71,10 @@ struct MmvqLaunch {
   // the product kernel when it can, else by a SwiGLU launch ahead of it.
   const float* sg = nullptr;
   const float* su = nullptr;
+  // Non-null (plain mode, one matrix, m = 1): the input row is this decode
+  // token's engram rows; xq receives their q8_1 row. In the product kernel
+  // when it can (run kernel), else by an engram_rows_q8_1 launch ahead of it.
+  const EngramRows* eg = nullptr;
 };
 
 // Expert and grouped launches are n_jobs equal-sized jobs.

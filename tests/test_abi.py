@@ -212,6 +212,39 @@ def test_engram_rows_q8_1_validation(L):
     assert f(*args(ids=TB)) == EINVAL                # ids over the table
 
 
+def test_engram_step_validation(L):
+    """engram_step refuses bad arguments on the host before any launch; the
+    workspace is sized by engram_step_workspace_bytes (kv rounded to 256
+    bytes, then the q8_1 row of 256 * cols values)."""
+    TM, MU, PR, OF, C, T, TB, W, QK, H, WS = (0x10000000 + 0x1000000 * i for i in range(11))
+    need = L.engram_step_workspace_bytes(3, 4, 4, 4096)
+    assert need == (5 * 4096 * 4 + 255) // 256 * 256 + 2048 * 5 // 4
+    assert L.engram_step_workspace_bytes(3, 17, 4, 4096) == 0        # 34 row ids
+    assert L.engram_step_workspace_bytes(3, 4, 5, 4096) == 0
+    f = L.engram_step
+    args = lambda **kw: [kw.get("tm", TM), 4096, MU, PR, OF, kw.get("nl", 2), kw.get("ng", 3),
+                         kw.get("nh", 4), 0, kw.get("c", C), kw.get("cl", 64), kw.get("t", T),
+                         kw.get("pos", 10), kw.get("layer", 1), kw.get("tb", TB), 500000,
+                         kw.get("w", W), kw.get("qk", QK), kw.get("h", H), kw.get("hc", 4),
+                         kw.get("dim", 4096), kw.get("eps", 1e-6), kw.get("ws", WS),
+                         kw.get("wsb", need), None, None]
+    assert f(*args(tm=None)) == EINVAL
+    assert f(*args(w=None)) == EINVAL
+    assert f(*args(ws=None)) == EINVAL
+    assert f(*args(layer=2)) == ESHAPE
+    assert f(*args(nh=17)) == ESHAPE
+    assert f(*args(pos=64)) == ESHAPE
+    assert f(*args(hc=5)) == ESHAPE
+    assert f(*args(dim=0)) == ESHAPE
+    assert f(*args(eps=-1.0)) == ESHAPE
+    assert f(*args(ws=WS + 16)) == EALIGN
+    assert f(*args(w=W + 2)) == EALIGN
+    assert f(*args(wsb=need - 1)) == ESPACE
+    assert f(*args(ws=C + 256)) == EINVAL              # workspace inside the cache
+    assert f(*args(h=W + 64)) == EINVAL                # h inside wkv
+    assert f(*args(ws=H + 256)) == EINVAL              # workspace over h
+
+
 def test_mmvq_validation(L):
     assert L.q2k_mmvq(None, Q, P, 256, 1024, 1, None) == EINVAL
     assert L.q2k_mmvq(P, Q, 0x100, 256, 1000, 1, None) == ESHAPE

@@ -1211,6 +1211,93 @@ def test_engram_rows_q8_1_bad_token_prime_and_wide():
     _engram_rows_both_ways(wide, table, wide.tokens[4:12].tolist(), 4, 1, 500000)
 
 
+def _engram_step_both_ways(hc, table_np, wkv_np, h_np, qk_np, eps, tokens, start, layer,
+                           n_table_rows, hcs, dim):
+    """Decode tokens through engram_step and through engram_rows_q8_1 +
+    q2k_mmvq + engram_gate with separate caches and streams h: the h bits,
+    cache, kv, q8_1 row and flag must agree at every position; returns the
+    last q8_1 row (oracle side) and the last h."""
+    tm, mu, pr, of = _hash_tables_dev(hc)
+    table = dev(table_np.reshape(-1))
+    wkv = dev(wkv_np.reshape(-1))
+    qk = dev(qk_np)
+    cols = (mu.shape[1] - 1) * pr.shape[-1]
+    n_out = (hcs + 1) * dim
+    c1 = torch.zeros(len(tokens) + start + 8, dtype=torch.int64, device="cuda")
+    c2 = c1.clone()
+    if start > 0:
+        pre = dev(hc.tokens[:start].astype(np.int32))
+        q2.engram_hash(tm, mu, pr, of, hc.pad_id, c1, pre, 0)
+        q2.engram_hash(tm, mu, pr, of, hc.pad_id, c2, pre, 0)
+    h1, h2 = dev(h_np), dev(h_np)
+    need_ws = q2.engram_step_workspace_bytes(mu.shape[1], pr.shape[-1], hcs, dim)
+    kv_bytes = (n_out * 4 + 255) // 256 * 256
+    need_q8 = q2.q8_1_rows_bytes(1, cols * 256)
+    assert need_ws == kv_bytes + need_q8
+    ws = torch.full((need_ws + 512,), 0x55, dtype=torch.uint8, device="cuda")
+    kv2 = torch.empty((1, n_out), dtype=torch.float32, device="cuda")
+    for s_, t in enumerate(tokens):
+        pos = start + s_
+        tok = dev(np.array([t], dtype=np.int32))
+        f1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        f2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        q2.engram_step(tm, mu, pr, of, hc.pad_id, c1, tok, pos, layer, table, n_table_rows, wkv, qk, h1,
+                       eps, workspace=ws, err_flag=f1)
+        xq2 = q2.engram_rows_q8_1(tm, mu, pr, of, hc.pad_id, c2, tok, pos, layer, table, n_table_rows,
+                                  err_flag=f2)
+        q2.q2k_mmvq(wkv, xq2, n_out, cols * 256, 1, out=kv2)
+        q2.engram_gate(h2, kv2, qk, eps)
+        assert torch.equal(h1.view(torch.int32), h2.view(torch.int32)), f"h, position {pos}"
+        assert torch.equal(ws[:n_out * 4].view(torch.int32), kv2.view(-1).view(torch.int32)), f"kv, position {pos}"
+        assert torch.equal(ws[kv_bytes:kv_bytes + need_q8], xq2[:need_q8]), f"q8_1, position {pos}"
+        assert int(f1.item()) == int(f2.item()), f"flag, position {pos}"
+    assert torch.equal(c1, c2)
+    assert torch.all(ws[need_ws:] == 0x55), "wrote past its workspace"
+    return xq2, h1
+
+
+def test_engram_step_is_the_composition():
+    """engram_step on the engram workload (wkv [20480, 2048], hc = 4, dim =
+    4096: the rows formed in the run kernel's prologue) after a prefill, both
+    hashed layers: every bit of the three calls it replaces; the last token
+    also against the oracle end to end (hash, rows, q8_1, the fixed-order
+    projection, the gate)."""
+    e = syn.engram_step_case()
+    hc = syn.engram_hash_case(seqlen=40)
+    assert q2.q2k_product_kernel(20480, 2048, 1) == PD
+    for layer in (0, 1):
+        xq2, h1 = _engram_step_both_ways(hc, e.table, e.wkv, e.h, e.qk, e.eps, hc.tokens[32:40].tolist(), 32,
+                                         layer, e.table.shape[0], e.hc, e.dim)
+    # the oracle: the hash of the last position, its rows and q8_1, kv, the
+    # gate applied once per decoded token to the stream (layer 1 run)
+    ids, _ = orc.engram_hash(hc.token_map.tolist(), hc.multipliers.tolist(), hc.primes.tolist(),
+                             hc.offsets.tolist(), hc.pad_id, hc.n_heads, [0] * 48, hc.tokens[:40].tolist(), 0)
+    h_ref = e.h.astype(np.float64)
+    for pos in range(32, 40):
+        rows = orc.dequant_rows_bf16_bits(e.table, ids[pos][1])
+        oq, od, _ = orc.q8_1_from_bf16_bits(rows.reshape(1, -1))
+        kv = orc.mmvq_f32(e.wkv, oq, od).astype(np.float64)
+        h_ref = orc.engram_gate(h_ref.astype(np.float32), kv, e.qk, e.eps)
+    assert_q8_equal(xq2, rows.reshape(1, -1))
+    assert_close(h1.cpu().numpy(), h_ref, "engram step, 8 tokens end to end")
+
+
+def test_engram_step_small_and_bad_token():
+    """A projection too small for the run kernel (dim 256: the rows launch
+    ahead of the product) and a token outside the vocabulary (NaN rows, the
+    flag): still the bits of the composition."""
+    hc = syn.engram_hash_case(seqlen=24, vocab=512, n_heads=2)
+    rng = syn.rng_for(1011)
+    table = syn.q2k_blocks(rng, 500000, 1)
+    dim, hcs = 256, 2
+    wkv = syn.q2k_blocks(rng, (hcs + 1) * dim, 4)
+    h, _, qk, eps = syn.gate_case(1011, 1, hcs, dim)
+    assert q2.q2k_product_kernel((hcs + 1) * dim, 1024, 1) == PD
+    toks = hc.tokens[16:24].tolist()
+    toks[3] = 100000                                    # outside the vocabulary
+    _engram_step_both_ways(hc, table, wkv, h, qk, eps, toks, 16, 1, 500000, hcs, dim)
+
+
 # ------------------------------------------------------- m > 8 (MMQ) ------
 
 @pytest.mark.parametrize("n,k,m", [(300, 1024, 9), (1000, 2048, 16), (130, 7168, 33), (257, 4096, 64),
