@@ -431,6 +431,32 @@ Q2K_API int32_t engram_step(const int64_t* token_map_dev, int64_t vocab,
                             void* workspace_dev, size_t workspace_bytes, int32_t* err_flag_dev,
                             void* stream);
 
+/* engram_step without the workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same launches and the same bits as
+ * engram_step, with kv and the q8_1 row kept in a device array of the
+ * library (Q2K_ENGRAM_SCRATCH_BYTES, one per GPU, held until the process
+ * ends; its address is looked up once per device). Calls no allocator.
+ * Limit: engram_step_workspace_bytes(max_ngram, n_heads, hc, dim) <=
+ * Q2K_ENGRAM_SCRATCH_BYTES (hc + 1 = 5 streams of dim 8192 with 32 row
+ * ids fit), else Q2K_ESPACE before any launch. Every call on one GPU uses
+ * the same array and overwrites what it reads (kv and the q8_1 row are
+ * written whole before they are read), so nothing needs clearing between
+ * calls; calls that overlap on one GPU (other streams, other threads) race.
+ * Arguments and other errors as engram_step; Q2K_EDEVICE when the array's
+ * device address cannot be looked up. */
+#define Q2K_ENGRAM_SCRATCH_BYTES (176 * 1024)
+Q2K_API int32_t engram_step_noalloc(const int64_t* token_map_dev, int64_t vocab,
+                                    const int64_t* multipliers_dev, const int64_t* primes_dev,
+                                    const int64_t* offsets_dev, int32_t n_layers,
+                                    int32_t max_ngram, int32_t n_heads, int64_t pad_id,
+                                    int64_t* cache_dev, int64_t cache_len,
+                                    const int32_t* token_dev, int64_t pos, int32_t layer,
+                                    const void* table_dev, int64_t n_table_rows,
+                                    const void* wkv_dev, const float* qk_dev, float* h_dev,
+                                    int32_t hc, int32_t dim, float eps, int32_t* err_flag_dev,
+                                    void* stream);
+
 /* Which kernel runs the Q2_K x q8_1 products (q2k_mmvq, its pair, expert
  * and grouped forms, q2k_mmq and q2k_block_dots), process-wide. Every kernel
  * forms the same exact int32 block sums and follows the fixed summation

@@ -57,6 +57,8 @@ SIGNATURES = {
                                 _I32, _VP, _I64, _VP, _VP, _VP, _SZ, _VP, _VP]),
     "q2k_block_dots": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     "engram_step_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "engram_step_noalloc": (_I32, [_VP, _I64, _VP, _VP, _VP, _I32, _I32, _I32, _I64, _VP, _I64, _VP, _I64,
+                                   _I32, _VP, _I64, _VP, _VP, _VP, _I32, _I32, _F32, _VP, _VP]),
     "engram_step": (_I32, [_VP, _I64, _VP, _VP, _VP, _I32, _I32, _I32, _I64, _VP, _I64, _VP, _I64, _I32,
                            _VP, _I64, _VP, _VP, _VP, _I32, _I32, _F32, _VP, _SZ, _VP, _VP]),
     "engram_hash": (_I32, [_VP, _I64, _VP, _VP, _VP, _I32, _I32, _I32, _I64, _VP, _I64, _VP, _I32,
@@ -504,3 +506,31 @@ def engram_step(token_map: torch.Tensor, multipliers: torch.Tensor, primes: torc
         _contig(table, "table"), n_table_rows, _contig(wkv, "wkv"), _contig(qk, "qk"), _contig(h, "h"),
         hc, dim, float(eps), _contig(workspace, "workspace"), workspace.numel(), flag, _stream()))
     return h, workspace
+
+
+def engram_step_noalloc(token_map: torch.Tensor, multipliers: torch.Tensor, primes: torch.Tensor,
+                        offsets: torch.Tensor, pad_id: int, cache: torch.Tensor, token: torch.Tensor,
+                        pos: int, layer: int, table: torch.Tensor, n_table_rows: int, wkv: torch.Tensor,
+                        qk: torch.Tensor, h: torch.Tensor, eps: float,
+                        err_flag: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """engram_step with the library's own device array as its workspace (no
+    allocation anywhere in the call); h [1, hc, dim] updated in place."""
+    for name, t in (("token_map", token_map), ("multipliers", multipliers), ("primes", primes),
+                    ("offsets", offsets), ("cache", cache)):
+        if t.dtype != torch.int64:
+            raise ValueError(f"{name} must be int64")
+    if token.dtype != torch.int32:
+        raise ValueError("token must be int32")
+    if h.dtype != torch.float32 or h.dim() != 3 or h.shape[0] != 1:
+        raise ValueError("h must be f32 [1, hc, dim]")
+    n_layers, max_ngram = multipliers.shape
+    n_heads = primes.shape[-1]
+    _, hc, dim = h.shape
+    flag = _contig(err_flag, "err_flag") if err_flag is not None else None
+    _check("engram_step_noalloc", lib().engram_step_noalloc(
+        _contig(token_map, "token_map"), token_map.numel(), _contig(multipliers, "multipliers"),
+        _contig(primes, "primes"), _contig(offsets, "offsets"), n_layers, max_ngram, n_heads, pad_id,
+        _contig(cache, "cache"), cache.numel(), _contig(token, "token"), pos, layer,
+        _contig(table, "table"), n_table_rows, _contig(wkv, "wkv"), _contig(qk, "qk"), _contig(h, "h"),
+        hc, dim, float(eps), flag, _stream()))
+    return h

@@ -9,6 +9,8 @@
 #include <string.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/q2k_decode.h"
 #include "q2k_device.h"
 #include "q2k_launch.h"
@@ -531,8 +533,10 @@ int32_t engram_rows_q8_1(const int64_t* token_map_dev, int64_t vocab, const int6
 namespace {
 
 // engram_step on a workspace ws of ws_bytes bytes (the caller's, or the
-// library's own scratch array for engram_step_noalloc).
-int32_t engram_step_on(const char* fn, const int64_t* token_map_dev, int64_t vocab,
+// library's own scratch array for engram_step_noalloc: ws_is_scratch, when
+// ws is null during the checks and the pointer is fetched afterwards).
+// check_only: run every argument check, launch nothing (no HIP call).
+int32_t engram_step_on(const char* fn, bool check_only, bool ws_is_scratch, const int64_t* token_map_dev, int64_t vocab,
                        const int64_t* multipliers_dev, const int64_t* primes_dev,
                        const int64_t* offsets_dev, int32_t n_layers, int32_t max_ngram, int32_t n_heads,
                        int64_t pad_id, int64_t* cache_dev, int64_t cache_len, const int32_t* token_dev,
@@ -540,7 +544,7 @@ int32_t engram_step_on(const char* fn, const int64_t* token_map_dev, int64_t voc
                        const void* wkv_dev, const float* qk_dev, float* h_dev, int32_t hc, int32_t dim,
                        float eps, void* ws, size_t ws_bytes, int32_t* err_flag_dev, void* stream) {
   if (!token_map_dev || !multipliers_dev || !primes_dev || !offsets_dev || !cache_dev || !token_dev ||
-      !table_dev || !wkv_dev || !qk_dev || !h_dev || !ws)
+      !table_dev || !wkv_dev || !qk_dev || !h_dev || (!ws && !ws_is_scratch))
     return fail(Q2K_EINVAL, "%s: null pointer", fn);
   if (vocab < 1) return fail(Q2K_ESHAPE, "%s: vocab = %lld < 1", fn, (long long)vocab);
   if (n_layers < 1 || n_layers > 64) return fail(Q2K_ESHAPE, "%s: n_layers = %d outside 1..64", fn, n_layers);
@@ -559,13 +563,15 @@ int32_t engram_step_on(const char* fn, const int64_t* token_map_dev, int64_t voc
   if (!aligned(token_map_dev, 8) || !aligned(multipliers_dev, 8) || !aligned(primes_dev, 8) ||
       !aligned(offsets_dev, 8) || !aligned(cache_dev, 8) || !aligned(token_dev, 4) ||
       !aligned(table_dev, 4) || !aligned(wkv_dev, 4) || !aligned(qk_dev, 4) || !aligned(h_dev, 4) ||
-      !aligned(ws, 256))
+      (!ws_is_scratch && !aligned(ws, 256)))
     return fail(Q2K_EALIGN, "%s: 64-bit arrays 8-byte, token, table, wkv, qk and h 4-byte, the "
                 "workspace 256-byte aligned", fn);
   const int32_t n = (hc + 1) * dim, k = cols * 256;
   const size_t kvb = engram_kv_bytes(hc, dim);
   const size_t need = kvb + q8_1_rows_bytes(1, k);
-  if (ws_bytes < need) return fail(Q2K_ESPACE, "%s: workspace holds %zu bytes, %zu needed", fn, ws_bytes, need);
+  if (ws_bytes < need)
+    return fail(Q2K_ESPACE, "%s: %s holds %zu bytes, %zu needed", fn,
+                ws_is_scratch ? "the library's scratch array" : "the workspace", ws_bytes, need);
   // written: h, cache, workspace; read: everything else
   const void* wr[3] = {h_dev, cache_dev, ws};
   const size_t wr_b[3] = {(size_t)hc * dim * 4, (size_t)cache_len * 8, need};
@@ -575,11 +581,14 @@ int32_t engram_step_on(const char* fn, const int64_t* token_map_dev, int64_t voc
                           (size_t)n_layers * (max_ngram - 1) * n_heads * 8, (size_t)n_layers * cols * 8, 4,
                           (size_t)n_table_rows * 84, q2k_matrix_bytes(n, k), (size_t)hc * dim * 4};
   for (int a = 0; a < 3; ++a) {
+    if (a == 2 && ws_is_scratch) continue;   // the library's own array overlaps nothing of the caller's
     for (int b = a + 1; b < 3; ++b)
-      if (overlap(wr[a], wr_b[a], wr[b], wr_b[b])) return fail(Q2K_EINVAL, "%s: h, the cache and the workspace must not overlap", fn);
+      if (!(b == 2 && ws_is_scratch) && overlap(wr[a], wr_b[a], wr[b], wr_b[b]))
+        return fail(Q2K_EINVAL, "%s: h, the cache and the workspace must not overlap", fn);
     for (int b = 0; b < 8; ++b)
       if (overlap(wr[a], wr_b[a], rd[b], rd_b[b])) return fail(Q2K_EINVAL, "%s: h, the cache or the workspace overlaps an input", fn);
   }
+  if (check_only) return Q2K_OK;
   q2k::EngramRows E;
   E.token_map = token_map_dev;
   E.vocab = vocab;
@@ -611,6 +620,37 @@ int32_t engram_step_on(const char* fn, const int64_t* token_map_dev, int64_t voc
   return launched(q2k::launch_engram_gate(h_dev, kv, qk_dev, 1, hc, dim, eps, st), fn);
 }
 
+
+// The engram step's workspace for engram_step_noalloc, for callers that
+// cannot allocate: kv of up to 40960 values (hc + 1 = 5 streams of 8192)
+// and the q8_1 row of up to 32 gathered rows (8192 values), 163840 + 10240
+// bytes, rounded to 176 KiB. Each GPU the library runs on holds its own copy
+// until the process ends. In host code `scratch` names a host-side stand-in:
+// only the per-device address from hipGetSymbolAddress is handed to kernels.
+__device__ __align__(256) uint8_t scratch[Q2K_ENGRAM_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64];   // per device: the device address of its `scratch`
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.
+int32_t scratch_address(const char* fn, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(Q2K_EDEVICE, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(Q2K_EDEVICE, "%s: device %d, at most 64 are tracked", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(Q2K_EDEVICE, "%s: hipGetSymbolAddress(scratch) failed: %s", fn, hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return Q2K_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -622,10 +662,32 @@ int32_t engram_step(const int64_t* token_map_dev, int64_t vocab, const int64_t* 
                     const void* table_dev, int64_t n_table_rows, const void* wkv_dev,
                     const float* qk_dev, float* h_dev, int32_t hc, int32_t dim, float eps,
                     void* workspace_dev, size_t workspace_bytes, int32_t* err_flag_dev, void* stream) {
-  return engram_step_on("engram_step", token_map_dev, vocab, multipliers_dev, primes_dev, offsets_dev,
+  return engram_step_on("engram_step", false, false, token_map_dev, vocab, multipliers_dev, primes_dev, offsets_dev,
                         n_layers, max_ngram, n_heads, pad_id, cache_dev, cache_len, token_dev, pos, layer,
                         table_dev, n_table_rows, wkv_dev, qk_dev, h_dev, hc, dim, eps, workspace_dev,
                         workspace_bytes, err_flag_dev, stream);
+}
+
+int32_t engram_step_noalloc(const int64_t* token_map_dev, int64_t vocab, const int64_t* multipliers_dev,
+                            const int64_t* primes_dev, const int64_t* offsets_dev, int32_t n_layers,
+                            int32_t max_ngram, int32_t n_heads, int64_t pad_id, int64_t* cache_dev,
+                            int64_t cache_len, const int32_t* token_dev, int64_t pos, int32_t layer,
+                            const void* table_dev, int64_t n_table_rows, const void* wkv_dev,
+                            const float* qk_dev, float* h_dev, int32_t hc, int32_t dim, float eps,
+                            int32_t* err_flag_dev, void* stream) {
+  const char* fn = "engram_step_noalloc";
+  // every check first (no HIP call), then the scratch address, then the launches
+  if (int32_t r = engram_step_on(fn, true, true, token_map_dev, vocab, multipliers_dev, primes_dev,
+                                 offsets_dev, n_layers, max_ngram, n_heads, pad_id, cache_dev, cache_len,
+                                 token_dev, pos, layer, table_dev, n_table_rows, wkv_dev, qk_dev, h_dev, hc,
+                                 dim, eps, nullptr, Q2K_ENGRAM_SCRATCH_BYTES, err_flag_dev, stream))
+    return r;
+  void* ws = nullptr;
+  if (int32_t r = scratch_address(fn, &ws)) return r;
+  return engram_step_on(fn, false, true, token_map_dev, vocab, multipliers_dev, primes_dev, offsets_dev,
+                        n_layers, max_ngram, n_heads, pad_id, cache_dev, cache_len, token_dev, pos, layer,
+                        table_dev, n_table_rows, wkv_dev, qk_dev, h_dev, hc, dim, eps, ws,
+                        Q2K_ENGRAM_SCRATCH_BYTES, err_flag_dev, stream);
 }
 
 int32_t q2k_dequant_rows_q8_1(const void* table_dev, int64_t n_table_rows, const int64_t* ids_dev,

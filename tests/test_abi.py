@@ -245,6 +245,22 @@ def test_engram_step_validation(L):
     assert f(*args(ws=H + 256)) == EINVAL              # workspace over h
 
 
+def test_engram_step_noalloc_checks_before_any_hip_call(L):
+    """engram_step_noalloc runs every argument check before it looks up its
+    array's device address (a HIP call; none here, there is no GPU), and
+    refuses steps whose workspace would pass Q2K_ENGRAM_SCRATCH_BYTES."""
+    TM, MU, PR, OF, C, T, TB, W, QK, H = (0x10000000 + 0x1000000 * i for i in range(10))
+    f = L.engram_step_noalloc
+    args = lambda **kw: [kw.get("tm", TM), 4096, MU, PR, OF, 2, 3, 4, 0, C, 64, T, 10, 1, TB, 500000,
+                         W, QK, kw.get("h", H), kw.get("hc", 4), kw.get("dim", 4096), 1e-6, None, None]
+    assert f(*args(tm=None)) == EINVAL
+    assert f(*args(hc=5)) == ESHAPE
+    assert f(*args(dim=16384)) == ESPACE
+    assert "scratch array" in _err(L)
+    assert f(*args(h=W + 64)) == EINVAL
+    assert L.engram_step_workspace_bytes(3, 16, 4, 8192) <= 176 * 1024   # the stated limit fits
+
+
 def test_mmvq_validation(L):
     assert L.q2k_mmvq(None, Q, P, 256, 1024, 1, None) == EINVAL
     assert L.q2k_mmvq(P, Q, 0x100, 256, 1000, 1, None) == ESHAPE
