@@ -984,7 +984,7 @@ def main():
         rocprof_from(args.rocprof_from, ROCPROF_FILE)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         raise SystemExit(2)
     if args.pmc_calibration:

@@ -16,7 +16,21 @@
 // for rows of more than 64 half blocks) of row l / group; P = 64 / group rows
 // per wave step; wave w takes steps w, w + W, ... With one token and at most
 // 64 half blocks per row, a lane's 128 activations stay in VGPRs for all its
-// steps; otherwise they are read per half block and plane.
+// steps; otherwise they are read per half block and plane. One token and at
+// most 32 half blocks per row (k <= 4096, the engram projection's 2048
+// among them): a quarter of a half block per lane, its 64 activations kept
+// as f64, so each weight costs one f64 fma instead of an f32 product, a
+// widening and an f64 add.
+//
+// Per weight the arithmetic is the table lookup (a selector and a v_perm
+// per two weights, then the split of the pair), the widening of the weight
+// to f64 and one f64 fma: about 6 VALU instructions, at one wave64
+// instruction per 4 clocks per SIMD about 6.4 us for the 41.9 M weights of
+// a [20480, 2048] matrix on 256 CUs at 2.4 GHz. The kernel is bound by that
+// arithmetic, not by its 13.8 MB of weights (1.7 us at 8 TB/s).
+//
+// Each wave requests its next row step's weights before computing the
+// current one.
 #include <stdlib.h>
 
 #include "q2k_device.h"
@@ -32,6 +46,9 @@ namespace {
 //   y        f32 [m, n]
 //   gs_log2  lanes per row = 1 << gs_log2
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 // The four bf16 values one sub-block's 2-bit quants can take, T[q] =
 // bf16_rne(d*sc*q - dmin*m) for q = 0..3 (the same f32 fma and rounding as
 // the per-weight expansion), packed two per dword: lo = T0 | T1 << 16,
@@ -41,23 +58,29 @@ struct Table {
 };
 
 __device__ __forceinline__ Table sub_block_table(float dsc, float dmm) {
-  uint32_t t[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t u = __float_as_uint(fmaf(dsc, (float)q, -dmm));
-    t[q] = u + 0x7fffu + ((u >> 16) & 1u);   // bf16 value in the high half
-  }
-  // high halves of t[0], t[1] -> lo; of t[2], t[3] -> hi
-  return Table{__builtin_amdgcn_perm(t[1], t[0], 0x07060302u), __builtin_amdgcn_perm(t[3], t[2], 0x07060302u)};
+  // v_cvt_pk_bf16_f32 rounds two f32 values to bf16, nearest-even (the
+  // values here are never f32 subnormals: both products are multiples of
+  // 2^-24); element 0 lands in the low half
+  const f32x2_t t01 = {fmaf(dsc, 0.0f, -dmm), fmaf(dsc, 1.0f, -dmm)};
+  const f32x2_t t23 = {fmaf(dsc, 2.0f, -dmm), fmaf(dsc, 3.0f, -dmm)};
+  return Table{__builtin_bit_cast(uint32_t, __builtin_convertvector(t01, bf16x2_t)),
+               __builtin_bit_cast(uint32_t, __builtin_convertvector(t23, bf16x2_t))};
 }
 
-// f32 values (bf16 in the high half) of the weights whose quants are bytes
-// 2i and 2i + 1 of qm (values 0..3): v_perm picks T[q] out of the packed
-// table with selector bytes (2q, 2q + 1).
-__device__ __forceinline__ void lookup2(const Table& T, uint32_t qm, int i, float& wa, float& wb) {
-  const uint32_t dup = __builtin_amdgcn_perm(qm, qm, i ? 0x03030202u : 0x01010000u);  // qa qa qb qb
-  const uint32_t sel = (dup << 1) + 0x01000100u;                                    // 2qa 2qa+1 2qb 2qb+1
-  const uint32_t pair = __builtin_amdgcn_perm(T.hi, T.lo, sel);                     // T[qa] | T[qb] << 16
+// Lookup selectors of the four weights whose quants are bytes 0..3 of
+// word >> 2j (bits 0..1 of each byte): selector bytes (2q, 2q + 1) pick
+// T[q] out of the packed table. s01 serves weights 0 and 1, s23 weights 2
+// and 3.
+__device__ __forceinline__ void lookup_selectors(uint32_t word, int j, uint32_t& s01, uint32_t& s23) {
+  const uint32_t q2 = (j == 0 ? word << 1 : word >> (2 * j - 1)) & 0x06060606u;   // 2q per byte
+  const uint32_t q2p = q2 | 0x01010101u;                                            // 2q + 1
+  s01 = __builtin_amdgcn_perm(q2p, q2, 0x05010400u);
+  s23 = __builtin_amdgcn_perm(q2p, q2, 0x07030602u);
+}
+
+// f32 values (bf16 in the high half) of the two weights a selector serves.
+__device__ __forceinline__ void lookup_pair(const Table& T, uint32_t sel, float& wa, float& wb) {
+  const uint32_t pair = __builtin_amdgcn_perm(T.hi, T.lo, sel);   // T[qa] | T[qb] << 16
   wa = __uint_as_float(pair << 16);
   wb = __uint_as_float(pair & 0xffff0000u);
 }
@@ -71,18 +94,37 @@ __device__ __forceinline__ void plane_dot(const u32x4& q0, const u32x4& q1, cons
                                           const Table& T1, int j, const uint32_t xw[16], double acc[4]) {
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
-    const uint32_t word = w < 4 ? q0[w] : q1[w - 4];
-    const uint32_t qm = (word >> (2 * j)) & 0x03030303u;
+    uint32_t sel[2];
+    lookup_selectors(w < 4 ? q0[w] : q1[w - 4], j, sel[0], sel[1]);
     const Table& T = w < 4 ? T0 : T1;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       float wa, wb;
-      lookup2(T, qm, i, wa, wb);
+      lookup_pair(T, sel[i], wa, wb);
       const uint32_t xb = xw[2 * w + i];
       const float xa = __uint_as_float(xb << 16);
       const float xbv = __uint_as_float(xb & 0xffff0000u);
       acc[2 * i] += (double)(wa * xa);
       acc[2 * i + 1] += (double)(wb * xbv);
+    }
+  }
+}
+
+// The same with the plane's activations already widened to f32 (xf[l] is
+// element l of the plane).
+__device__ __forceinline__ void plane_dot_f(const u32x4& q0, const u32x4& q1, const Table& T0,
+                                            const Table& T1, int j, const float xf[32], double acc[4]) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t sel[2];
+    lookup_selectors(w < 4 ? q0[w] : q1[w - 4], j, sel[0], sel[1]);
+    const Table& T = w < 4 ? T0 : T1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float wa, wb;
+      lookup_pair(T, sel[i], wa, wb);
+      acc[2 * i] += (double)(wa * xf[4 * w + 2 * i]);
+      acc[2 * i + 1] += (double)(wb * xf[4 * w + 2 * i + 1]);
     }
   }
 }
@@ -115,13 +157,45 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint8_t* w, const 
   const size_t rowbytes = (size_t)nb * kBlockBytes;
   const int steps = (n + P - 1) / P;
 
-  uint32_t xc[CACHE_X ? 4 : 1][CACHE_X ? 16 : 1];
+  // CACHE_X: the lane's 128 activations as f32, widened once
+  float xc[CACHE_X ? 4 : 1][CACHE_X ? 32 : 1];
   if constexpr (CACHE_X) {
     const int hb = hb0 < 2 * nb ? hb0 : 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_plane_x(x, 128 * hb + 32 * j, xc[j]);
+    for (int j = 0; j < 4; ++j) {
+      uint32_t xw[16];
+      load_plane_x(x, 128 * hb + 32 * j, xw);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        xc[j][2 * i] = __uint_as_float(xw[i] << 16);
+        xc[j][2 * i + 1] = __uint_as_float(xw[i] & 0xffff0000u);
+      }
+    }
   }
 
+  // The weights of the wave's next row step are requested before the
+  // current one is computed (a ring of two).
+  struct HalfW {
+    u32x4 q0, q1;
+    u32x2 sc;
+    uint32_t dd;
+  };
+  auto load_half = [&](int st, int hb) {
+    HalfW r;
+    const int row = min(st * P + prow, n - 1);
+    const int b = hb >> 1, h = hb & 1;
+    const uint8_t* blk = w + (size_t)row * rowbytes + (size_t)b * kBlockBytes;
+    r.q0 = gload<u32x4_a4>(blk + 16 + 32 * h);
+    r.q1 = gload<u32x4_a4>(blk + 32 + 32 * h);
+    r.sc = gload<u32x2_a4>(blk + 8 * h);
+    r.dd = gload<uint32_t>(blk + 80);
+    return r;
+  };
+  const int hbl = hb0 < 2 * nb ? hb0 : 0;   // CACHE_X: the lane's one half block
+  HalfW nxt{};
+  if constexpr (CACHE_X) {
+    if (wave < steps) nxt = load_half(wave, hbl);
+  }
   for (int st = wave; st < steps; st += total_waves) {
     const int row = st * P + prow;
     double acc[M][4];
@@ -129,14 +203,18 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint8_t* w, const 
     for (int t = 0; t < M; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[t][i] = 0.0;
+    HalfW cur{};
+    if constexpr (CACHE_X) {
+      cur = nxt;
+      if (st + total_waves < steps) nxt = load_half(st + total_waves, hbl);
+    }
     if (row < n) {
       for (int hb = hb0; hb < 2 * nb; hb += gs) {
         const int b = hb >> 1, h = hb & 1;
-        const uint8_t* blk = w + (size_t)row * rowbytes + (size_t)b * kBlockBytes;
-        const u32x4 q0 = gload<u32x4_a4>(blk + 16 + 32 * h);
-        const u32x4 q1 = gload<u32x4_a4>(blk + 32 + 32 * h);
-        const u32x2 sc = gload<u32x2_a4>(blk + 8 * h);
-        const uint32_t dd = gload<uint32_t>(blk + 80);
+        if constexpr (!CACHE_X) cur = load_half(st, hb);
+        const u32x4 q0 = cur.q0, q1 = cur.q1;
+        const u32x2 sc = cur.sc;
+        const uint32_t dd = cur.dd;
         const float d = fp16_bits_to_f32(dd & 0xffffu);
         const float dmin = fp16_bits_to_f32(dd >> 16);
 #pragma unroll
@@ -147,7 +225,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint8_t* w, const 
           const Table T0 = sub_block_table(d * (float)(s0 & 15u), dmin * (float)(s0 >> 4));
           const Table T1 = sub_block_table(d * (float)(s1 & 15u), dmin * (float)(s1 >> 4));
           if constexpr (CACHE_X) {
-            plane_dot(q0, q1, T0, T1, j, xc[j], acc[0]);
+            plane_dot_f(q0, q1, T0, T1, j, xc[j], acc[0]);
           } else {
 #pragma unroll
             for (int t = 0; t < M; ++t) {
@@ -157,6 +235,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint8_t* w, const 
             }
           }
         }
+        if constexpr (CACHE_X) break;       // one half block per lane
       }
     }
 #pragma unroll
@@ -165,6 +244,93 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint8_t* w, const 
       for (int off = gs >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
       if (hb0 == 0 && row < n) y[(int64_t)t * n + row] = (float)v;
     }
+  }
+}
+
+// One token, rows of at most 32 half blocks (k <= 4096): lane l of a row's
+// group (4 k/256 lanes, rounded up to a power of two) takes quarter l of the
+// row: quant bytes 16 (l & 1) .. 16 (l & 1) + 15 of half block l >> 1, i.e.
+// the first or the second 16 elements of each of the half's four planes
+// (sub-blocks 8h + 2j + (l & 1), j = 0..3), 64 weights per step. Its 64
+// activations stay in VGPRs as f64 for all its steps, so a weight costs one
+// f64 fma, acc + w * x: the product is exact, so this rounds exactly as
+// adding the exact f32 product does.
+__global__ __launch_bounds__(256) void gemv_bf16_quarter_kernel(const uint8_t* w, const uint16_t* x,
+                                                                float* y, int32_t n, int32_t k,
+                                                                int32_t gs_log2, int32_t total_waves) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (wave >= total_waves) return;
+  const int nb = k >> 8;
+  const int gs = 1 << gs_log2;
+  const int P = 64 >> gs_log2;
+  const int prow = lane >> gs_log2;
+  const int ql = lane & (gs - 1);
+  const bool q_ok = ql < 4 * nb;          // lanes past the row's quarters add +0
+  const int qq = q_ok ? ql : 0;
+  const int hb = qq >> 1, part = qq & 1;
+  const int b = hb >> 1, h = hb & 1;
+  const size_t rowbytes = (size_t)nb * kBlockBytes;
+  const int steps = (n + P - 1) / P;
+
+  double xd[4][16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint16_t* xp = x + 256 * b + 128 * h + 32 * j + 16 * part;
+    const u32x4 a0 = gload<u32x4>(xp);
+    const u32x4 a1 = gload<u32x4>(xp + 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t v = i < 4 ? a0[i] : a1[i - 4];
+      xd[j][2 * i] = q_ok ? (double)__uint_as_float(v << 16) : 0.0;
+      xd[j][2 * i + 1] = q_ok ? (double)__uint_as_float(v & 0xffff0000u) : 0.0;
+    }
+  }
+
+  struct QuarterW {
+    u32x4 q;
+    u32x2 sc;
+    uint32_t dd;
+  };
+  // the next step's weights are requested before the current step is computed
+  auto load_quarter = [&](int st) {
+    QuarterW r;
+    const int row = min(st * P + prow, n - 1);
+    const uint8_t* blk = w + (size_t)row * rowbytes + (size_t)b * kBlockBytes;
+    r.q = gload<u32x4_a4>(blk + 16 + 32 * h + 16 * part);
+    r.sc = gload<u32x2_a4>(blk + 8 * h);
+    r.dd = gload<uint32_t>(blk + 80);
+    return r;
+  };
+  QuarterW nxt = load_quarter(wave);
+  for (int st = wave; st < steps; st += total_waves) {
+    const int row = st * P + prow;
+    const QuarterW cur = nxt;
+    if (st + total_waves < steps) nxt = load_quarter(st + total_waves);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    const float d = fp16_bits_to_f32(cur.dd & 0xffffu);
+    const float dmin = fp16_bits_to_f32(cur.dd >> 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // sub-block 8h + 2j + part: scale byte 2j + part of this half
+      const uint32_t sv = (cur.sc[j >> 1] >> (16 * (j & 1) + 8 * part)) & 0xffu;
+      const Table T = sub_block_table(d * (float)(sv & 15u), dmin * (float)(sv >> 4));
+#pragma unroll
+      for (int wi = 0; wi < 4; ++wi) {
+        uint32_t sel[2];
+        lookup_selectors(cur.q[wi], j, sel[0], sel[1]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          float wa, wb;
+          lookup_pair(T, sel[i], wa, wb);
+          acc[2 * i] = fma((double)wa, xd[j][4 * wi + 2 * i], acc[2 * i]);
+          acc[2 * i + 1] = fma((double)wb, xd[j][4 * wi + 2 * i + 1], acc[2 * i + 1]);
+        }
+      }
+    }
+    double v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    for (int off = gs >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (ql == 0 && row < n) y[row] = (float)v;
   }
 }
 
@@ -211,13 +377,25 @@ hipError_t launch_gemv_bf16(const void* w, const void* x, int64_t x_stride, floa
   p.n = n;
   p.k = k;
   const int half_blocks = 2 * (k / kBlockWeights);
+  if (m == 1 && half_blocks <= 32) {
+    // one token, k <= 4096: a quarter of a half block per lane
+    int gsl = 0;
+    while ((1 << gsl) < 2 * half_blocks) ++gsl;
+    const int P = 64 >> gsl;
+    const int64_t steps = ((int64_t)n + P - 1) / P;
+    const int64_t waves = steps < (int64_t)cu_count_gemv() * 8 ? steps : (int64_t)cu_count_gemv() * 8;
+    hipLaunchKernelGGL(gemv_bf16_quarter_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
+                       p.w, p.x, y, n, k, gsl, (int32_t)waves);
+    return hipGetLastError();
+  }
   int gsl = 0;
   while ((1 << gsl) < half_blocks && gsl < 6) ++gsl;
   p.gs_log2 = gsl;
   const int P = 64 >> gsl;
   const int64_t steps = ((int64_t)n + P - 1) / P;
-  // About 16 waves per CU, each taking every W-th step.
-  const int64_t waves = steps < (int64_t)cu_count_gemv() * 16 ? steps : (int64_t)cu_count_gemv() * 16;
+  // About 8 waves per CU, each taking every W-th step (with the next
+  // step's weights in flight).
+  const int64_t waves = steps < (int64_t)cu_count_gemv() * 8 ? steps : (int64_t)cu_count_gemv() * 8;
   p.total_waves = (int)waves;
   const dim3 grid((unsigned)((waves + 3) / 4));
   const bool cache_x = half_blocks <= 64;

@@ -1062,14 +1062,14 @@ void dispatch_m1_fused(const MmvqParams& p, dim3 grid, const void* x_bf16, uint8
   const size_t lds = q8_row_bytes(p.k);
   const uint8_t* x = static_cast<const uint8_t*>(x_bf16);
   const int32_t plain = plain_launch(p) ? 1 : 0;
-#define Q2K_M1F(G, C)                                                                          \
-  hipLaunchKernelGGL((mmvq_m1_kernel<G, 4, C, FQ>), grid, dim3(256), lds, s, p.w[0], x,        \
+#define Q2K_M1F(G, R, C)                                                                       \
+  hipLaunchKernelGGL((mmvq_m1_kernel<G, R, C, FQ>), grid, dim3(256), lds, s, p.w[0], x,        \
                      p.y[0], p.n[0], p.k, p.total_waves, p.g8, plain, xq, p)
 #define Q2K_M1F_CH(G)                            \
   do {                                           \
-    if (ch == 8) Q2K_M1F(G, 8);                  \
-    else if (ch == 16) Q2K_M1F(G, 16);           \
-    else Q2K_M1F(G, 32);                         \
+    if (ch == 8) Q2K_M1F(G, 4, 8);               \
+    else if (ch == 16) Q2K_M1F(G, 4, 16);        \
+    else Q2K_M1F(G, 4, 32);                      \
   } while (0)
   switch (p.gs_log2) {
     case 3: Q2K_M1F_CH(3); return;
