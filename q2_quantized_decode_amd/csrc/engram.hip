@@ -40,20 +40,32 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(const uint8_t* __rest
   *reinterpret_cast<u32x2*>(o) = u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
 }
 
-__device__ __forceinline__ float block_sum_256(float v, float* lds) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+// The three gate sums over a 256-thread workgroup at once: each wave folds
+// its 64 lanes (xor tree), then the four wave sums are added as
+// (w0 + w1) + (w2 + w3). One barrier for all three.
+__device__ __forceinline__ void block_sum3_256(float& a, float& b, float& c, float* lds) {
+  for (int off = 32; off > 0; off >>= 1) {
+    a += __shfl_xor(a, off);
+    b += __shfl_xor(b, off);
+    c += __shfl_xor(c, off);
+  }
   const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    lds[wave] = a;
+    lds[4 + wave] = b;
+    lds[8 + wave] = c;
+  }
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds[wave] = v;
-  __syncthreads();
-  return (lds[0] + lds[1]) + (lds[2] + lds[3]);
+  a = (lds[0] + lds[1]) + (lds[2] + lds[3]);
+  b = (lds[4] + lds[5]) + (lds[6] + lds[7]);
+  c = (lds[8] + lds[9]) + (lds[10] + lds[11]);
 }
 
 __global__ __launch_bounds__(256) void engram_gate_kernel(float* __restrict__ h,
                                                           const float* __restrict__ kv,
                                                           const float* __restrict__ qk, int hc,
                                                           int dim, float eps) {
-  __shared__ float lds[4];
+  __shared__ float lds[12];
   const int t = blockIdx.x;
   const int j = blockIdx.y;
   float* hs = h + ((int64_t)t * hc + j) * dim;
@@ -68,9 +80,7 @@ __global__ __launch_bounds__(256) void engram_gate_kernel(float* __restrict__ h,
     skk = fmaf(kk, kk, skk);
     sqk = fmaf(w[i] * x, kk, sqk);
   }
-  shh = block_sum_256(shh, lds);
-  skk = block_sum_256(skk, lds);
-  sqk = block_sum_256(sqk, lds);
+  block_sum3_256(shh, skk, sqk, lds);
   const float rh = sqrtf(shh / (float)dim + eps);
   const float rk = sqrtf(skk / (float)dim + eps);
   const float s = sqk / (rh * rk * sqrtf((float)dim));
@@ -89,7 +99,7 @@ __global__ __launch_bounds__(256) void engram_gate_vec_kernel(float* __restrict_
                                                               const float* __restrict__ kv,
                                                               const float* __restrict__ qk,
                                                               int hc, int dim, float eps) {
-  __shared__ float lds[4];
+  __shared__ float lds[12];
   const int t = blockIdx.x;
   const int j = blockIdx.y;
   const int n4 = dim >> 2;
@@ -119,9 +129,7 @@ __global__ __launch_bounds__(256) void engram_gate_vec_kernel(float* __restrict_
       }
     }
   }
-  shh = block_sum_256(shh, lds);
-  skk = block_sum_256(skk, lds);
-  sqk = block_sum_256(sqk, lds);
+  block_sum3_256(shh, skk, sqk, lds);
   const float rh = sqrtf(shh / (float)dim + eps);
   const float rk = sqrtf(skk / (float)dim + eps);
   const float s = sqk / (rh * rk * sqrtf((float)dim));
