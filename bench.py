@@ -677,11 +677,57 @@ def bench_engram(torch, q2, syn, dev, copies_n: int = 80):
 
 
 # Workloads in run order; "headline" is the large verify at m = 1 and 8.
-SECTIONS = ["headline", "mmq", "grouped", "engram", "pair", "experts", "single"]
+# Single-matrix shapes of the workloads above (rows, k), for the product
+# kernel sweep.
+KERNEL_SWEEP_SHAPES = [(32768, 7168), (20480, 2048), (1024, 4096), (512, 4096), (2048, 4096),
+                       (4096, 2048), (1024, 2048)]
+
+
+def bench_kernels(torch, q2, syn, dev):
+    """The two product kernels at m = 2..8 on each workload matrix shape:
+    matrix cores (q2k_set_product_kernel(1)) and packed dots (2), same bits
+    either way; each over rotating weight copies of >= 1 GiB, graphs of 16
+    launches, HIP events around the replays. Reports both times and the
+    kernel the default choice takes."""
+    out = {}
+    prev = q2.q2k_set_product_kernel(q2.KERNEL_AUTO)
+    try:
+        for (n, k) in KERNEL_SWEEP_SHAPES:
+            w = syn.q2k_blocks(syn.rng_for(5, n, k), n, k // 256)
+            per = w.size
+            ncopy = max(2, min(1024, -(-(1 << 30) // per)))
+            buf = torch.from_numpy(w.reshape(-1)).to(dev).repeat(ncopy)
+            for m in range(2, 9):
+                x = syn.bf16_bits_to_tensor(syn.bf16_normal(syn.rng_for(6, m), (m, k))).to(dev)
+                xq = q2.q8_1_rows(x)
+                y = torch.empty((m, n), dtype=torch.float32, device=dev)
+                rec = {"auto": "mfma" if q2.q2k_product_kernel(n, k, m) == q2.KERNEL_MATRIX_CORES
+                       else "dots"}
+                for name, choice in (("mfma", q2.KERNEL_MATRIX_CORES), ("dots", q2.KERNEL_PACKED_DOTS)):
+                    q2.q2k_set_product_kernel(choice)
+                    launches = min(ncopy, 128)
+                    rec[name + "_us"] = round(graph_us(
+                        torch, lambda i: q2.q2k_mmvq(buf[i * per:(i + 1) * per], xq, n, k, m, out=y),
+                        launches, reps=max(2, 1024 // launches), chunk=16), 3)
+                    q2.q2k_set_product_kernel(q2.KERNEL_AUTO)
+                rec["auto_is_faster"] = rec[rec["auto"] + "_us"] <= min(rec["mfma_us"], rec["dots_us"]) * 1.02
+                out[f"{n}x{k}_m{m}"] = rec
+            del buf
+            torch.cuda.empty_cache()
+    finally:
+        q2.q2k_set_product_kernel(prev)
+    out["workload"] = ("q2k_mmvq at m = 2..8 on the workloads' matrix shapes, both product "
+                       "kernels (same bits), >= 1 GiB of rotating weight copies per shape")
+    return out
+
+
+SECTIONS = ["headline", "mmq", "grouped", "engram", "pair", "experts", "single", "kernels"]
+ON_REQUEST = {"kernels"}     # run only when named in --only
 SECTION_KEYS = {"mmq": "mmq", "grouped": "grouped", "engram": "engram_step",
-                "pair": "attention_pair", "experts": "expert_batch", "single": "single"}
+                "pair": "attention_pair", "experts": "expert_batch", "single": "single",
+                "kernels": "product_kernels"}
 SECTION_FNS = {"grouped": bench_grouped, "engram": bench_engram, "pair": bench_pair,
-               "experts": bench_experts, "single": bench_single}
+               "experts": bench_experts, "single": bench_single, "kernels": bench_kernels}
 
 
 def run(args):
@@ -833,7 +879,7 @@ def run(args):
     torch.cuda.synchronize()
     if not args.headline_only:
         for name in SECTIONS[2:]:
-            if only is None or name in only:
+            if (only is None and name not in ON_REQUEST) or (only is not None and name in only):
                 line[SECTION_KEYS[name]] = SECTION_FNS[name](torch, q2, syn, dev)
                 torch.cuda.synchronize()
     if not args.no_cpu:
@@ -957,6 +1003,45 @@ def rocprof_from(trace_csv: str, out: str):
     print(json.dumps(rec))
 
 
+def kernel_sweep_from(trace_csv: str, sweep_json: str) -> None:
+    """Markdown table of a kernel trace of `--only kernels`: the product
+    dispatches, in launch order, split per (shape, m, kernel) exactly as
+    bench_kernels issues them (per configuration: one eager pass, one untimed
+    replay, then the timed replays of `launches` captured calls); the averages
+    are over the timed replays only."""
+    import csv
+    import statistics
+
+    rec = json.loads(open(sweep_json).read().strip().split("\n")[-1])["product_kernels"]
+    with open(trace_csv, newline="") as f:
+        rows = [r for r in csv.DictReader(f) if "mmvq_" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    i = 0
+    print("| shape | m | matrix cores: kernel | avg (us) | packed dots: kernel | avg (us) "
+          "| events: matrix cores / packed dots (us) | default choice |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (n, k) in KERNEL_SWEEP_SHAPES:
+        per = n * (k // 256) * 84
+        ncopy = max(2, min(1024, -(-(1 << 30) // per)))
+        launches = min(ncopy, 128)
+        reps = max(2, 1024 // launches)
+        for m in range(2, 9):
+            cells = []
+            for _ in ("mfma", "dots"):
+                seg = rows[i:i + launches * (2 + reps)]
+                i += launches * (2 + reps)
+                names = sorted({r["Kernel_Name"].split("(")[0].replace("void ", "").replace("q2k::", "")
+                                for r in seg})
+                d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in seg[2 * launches:]]
+                cells.append((", ".join(names), statistics.mean(d)))
+            r = rec[f"{n}x{k}_m{m}"]
+            print(f"| [{n}, {k}] | {m} | `{cells[0][0]}` | {cells[0][1]:.3f} | `{cells[1][0]}` | "
+                  f"{cells[1][1]:.3f} | {r['mfma_us']} / {r['dots_us']} | "
+                  f"{'matrix cores' if r['auto'] == 'mfma' else 'packed dots'} |")
+    if i != len(rows):
+        raise SystemExit(f"trace has {len(rows)} product dispatches, the sweep issues {i}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -973,6 +1058,9 @@ def main():
                     help="only the product launches the roofline figures time (for kernel traces)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic record from two counter runs and exit")
+    ap.add_argument("--kernel-sweep-from", nargs=2, metavar=("KERNEL_TRACE_CSV", "SWEEP_JSON"),
+                    help="print the per-configuration table of a kernel trace of --only kernels "
+                         "and exit")
     ap.add_argument("--rocprof-from", metavar="KERNEL_TRACE_CSV",
                     help="write the product kernels' rocprofv3 averages from the kernel trace of "
                          "a --roofline-only run and exit")
@@ -982,6 +1070,9 @@ def main():
         return
     if args.rocprof_from:
         rocprof_from(args.rocprof_from, ROCPROF_FILE)
+        return
+    if args.kernel_sweep_from:
+        kernel_sweep_from(*args.kernel_sweep_from)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
