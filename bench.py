@@ -1003,6 +1003,36 @@ def rocprof_from(trace_csv: str, out: str):
     print(json.dumps(rec))
 
 
+def trace_summary(trace_csv: str) -> None:
+    """Markdown table of this library's dispatches in a rocprofv3 kernel
+    trace, grouped by kernel and workgroup count: dispatches, average and
+    10th/50th/90th percentile durations (warm-up and capture included)."""
+    import csv
+    import re
+    import statistics
+
+    groups: dict = {}
+    with open(trace_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            if "q2k::" not in r["Kernel_Name"]:
+                continue
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+            name = re.sub(r"\(.*", "", name).replace("void ", "")
+            wgs = 1
+            for ax in "XYZ":
+                wgs *= int(r[f"Grid_Size_{ax}"]) // max(1, int(r[f"Workgroup_Size_{ax}"]))
+            groups.setdefault((name, wgs), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | workgroups | dispatches | avg (us) | p10 | median | p90 |")
+    print("|---|---|---|---|---|---|---|")
+    for (name, wgs), d in sorted(groups.items(), key=lambda kv: -len(kv[1])):
+        d.sort()
+        def q(fr, d=d):
+            return d[min(len(d) - 1, int(fr * len(d)))]
+        print(f"| `{name}` | {wgs} | {len(d)} | {statistics.mean(d):.2f} | {q(0.1):.2f} | "
+              f"{q(0.5):.2f} | {q(0.9):.2f} |")
+
+
 def kernel_sweep_from(trace_csv: str, sweep_json: str) -> None:
     """Markdown table of a kernel trace of `--only kernels`: the product
     dispatches, in launch order, split per (shape, m, kernel) exactly as
@@ -1058,6 +1088,8 @@ def main():
                     help="only the product launches the roofline figures time (for kernel traces)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic record from two counter runs and exit")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print the per-kernel table of a rocprofv3 kernel trace and exit")
     ap.add_argument("--kernel-sweep-from", nargs=2, metavar=("KERNEL_TRACE_CSV", "SWEEP_JSON"),
                     help="print the per-configuration table of a kernel trace of --only kernels "
                          "and exit")
@@ -1070,6 +1102,9 @@ def main():
         return
     if args.rocprof_from:
         rocprof_from(args.rocprof_from, ROCPROF_FILE)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.kernel_sweep_from:
         kernel_sweep_from(*args.kernel_sweep_from)
