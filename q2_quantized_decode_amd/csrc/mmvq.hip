@@ -501,6 +501,15 @@ __device__ __forceinline__ void q8_1_block_store(uint8_t* xs, uint8_t* gout, con
 }
 
 // Workgroup barrier that orders LDS only: weight loads stay in flight.
+// A wave-uniform 8-byte load through the scalar data cache, waited for
+// inside the same asm statement. It counts on the scalar memory counter, so
+// waiting for it does not wait for the vector loads the wave has in flight.
+__device__ __forceinline__ int64_t scalar_load_i64(const int64_t* p) {
+  int64_t v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  return v;
+}
+
 __device__ __forceinline__ void lds_barrier_m1() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -653,6 +662,31 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
 #pragma unroll
       for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
     }
+    // FQ = 3: the hash's independent loads (the token, the window's cached
+    // ids, the layer's multipliers, the column's prime and offset) also go
+    // out before the ring
+    constexpr int NG3 = FQ == 3 ? kMaxNgram : 1;
+    int32_t h_t0 = 0;
+    int64_t h_cw[NG3], h_mu[NG3], h_pr = 0, h_of = 0;
+    if constexpr (FQ == 3) {
+      const EngramRows& E = p.eg;
+      // every argument field the prologue reads, fetched in one round now
+      asm volatile("" ::"s"(E.token_map), "s"(E.vocab), "s"(E.mult), "s"(E.primes), "s"(E.offsets),
+                   "s"(E.layer), "s"(E.ng), "s"(E.n_heads), "s"(E.pad_id), "s"(E.cache), "s"(E.token),
+                   "s"(E.pos), "s"(E.table), "s"(E.n_table_rows), "s"(E.err_flag));
+      const int cols = k >> 8;
+      const int c = tid < cols ? tid : 0;
+      h_t0 = E.token[0];
+#pragma unroll
+      for (int i = 0; i < kMaxNgram; ++i) {
+        const int ii = i < E.ng ? i : E.ng - 1;
+        h_cw[i] = E.cache[E.pos >= ii ? E.pos - ii : 0];
+        h_mu[i] = E.mult[(int64_t)E.layer * E.ng + ii];
+      }
+      h_pr = E.primes[(int64_t)E.layer * cols + c];
+      h_of = E.offsets[(int64_t)E.layer * cols + c];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const bool ring_ok = live && full;
     const LaneOffsets o0 = ring_ok ? off : lane_offsets((uint32_t)b * kBlockBytes, h);
     const uint8_t* wr = ring_ok ? wrun : J.w;
@@ -667,26 +701,27 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
       const EngramRows& E = p.eg;
       const int cols = k >> 8;
       // Thread c < cols computes row id c with the hash kernels' rules
-      // (hash_window, hash_cols), every independent load issued at once:
-      // the token, the window's cached ids, the layer's multipliers and the
-      // column's prime and offset; then token -> token_map; the ids' table
-      // rows are the third and last dependent round.
+      // (hash_window, hash_cols) from the loads issued before the ring; the
+      // token -> compressed id lookup is a scalar load (it waits on the
+      // scalar counter only, not behind the ring); the ids' table rows are
+      // the third and last dependent round.
       const bool hthread = tid < cols;
       const int c = hthread ? tid : 0;
       const int ng = E.ng, nh = E.n_heads;
       const int64_t pos = E.pos;
-      const int32_t t0 = E.token[0];
-      int64_t cw[kMaxNgram], mu[kMaxNgram];
+      // The loaded values enter through empty asm statements, as opaque VGPR
+      // values: otherwise the compiler, seeing uniform values, moves them to
+      // scalar registers right after their loads, which means waiting for
+      // the loads before the ring can go out.
 #pragma unroll
-      for (int i = 0; i < kMaxNgram; ++i) {
-        const int ii = i < ng ? i : ng - 1;
-        cw[i] = E.cache[pos >= ii ? pos - ii : 0];
-        mu[i] = E.mult[(int64_t)E.layer * ng + ii];
-      }
-      const int64_t pr = E.primes[(int64_t)E.layer * cols + c];
-      const int64_t of = E.offsets[(int64_t)E.layer * cols + c];
+      for (int i = 0; i < kMaxNgram; ++i) asm volatile("" : "+v"(h_cw[i]), "+v"(h_mu[i]));
+      asm volatile("" : "+v"(h_t0), "+v"(h_pr), "+v"(h_of));
+      const int32_t t0 = __builtin_amdgcn_readfirstlane(h_t0);
+      const int64_t* cw = h_cw;
+      const int64_t* mu = h_mu;
+      const int64_t pr = h_pr, of = h_of;
       const bool tok_ok = t0 >= 0 && (int64_t)t0 < E.vocab;
-      const int64_t own = tok_ok ? E.token_map[tok_ok ? t0 : 0] : -1;
+      const int64_t own = tok_ok ? scalar_load_i64(E.token_map + t0) : -1;
       int64_t tk[kMaxNgram];
       bool blocked = own == -1;
       tk[0] = blocked ? E.pad_id : own;
