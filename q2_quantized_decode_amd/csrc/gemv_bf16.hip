@@ -255,16 +255,17 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint8_t* w, const 
 // activations stay in VGPRs as f64 for all its steps, so a weight costs one
 // f64 fma, acc + w * x: the product is exact, so this rounds exactly as
 // adding the exact f32 product does.
+template <int GSL>
 __global__ __launch_bounds__(256) void gemv_bf16_quarter_kernel(const uint8_t* w, const uint16_t* x,
                                                                 float* y, int32_t n, int32_t k,
-                                                                int32_t gs_log2, int32_t total_waves) {
+                                                                int32_t total_waves) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (wave >= total_waves) return;
   const int nb = k >> 8;
-  const int gs = 1 << gs_log2;
-  const int P = 64 >> gs_log2;
-  const int prow = lane >> gs_log2;
+  constexpr int gs = 1 << GSL;
+  constexpr int P = 64 >> GSL;
+  const int prow = lane >> GSL;
   const int ql = lane & (gs - 1);
   const bool q_ok = ql < 4 * nb;          // lanes past the row's quarters add +0
   const int qq = q_ok ? ql : 0;
@@ -328,8 +329,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_quarter_kernel(const uint8_t* w
         }
       }
     }
-    double v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    for (int off = gs >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    const double v = group_sum_f64<GSL>((acc[0] + acc[1]) + (acc[2] + acc[3]), lane);
     if (ql == 0 && row < n) y[row] = (float)v;
   }
 }
@@ -384,8 +384,17 @@ hipError_t launch_gemv_bf16(const void* w, const void* x, int64_t x_stride, floa
     const int P = 64 >> gsl;
     const int64_t steps = ((int64_t)n + P - 1) / P;
     const int64_t waves = steps < (int64_t)cu_count_gemv() * 8 ? steps : (int64_t)cu_count_gemv() * 8;
-    hipLaunchKernelGGL(gemv_bf16_quarter_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
-                       p.w, p.x, y, n, k, gsl, (int32_t)waves);
+    const dim3 grid((unsigned)((waves + 3) / 4));
+#define Q2K_GEMV_Q(G) \
+  hipLaunchKernelGGL(gemv_bf16_quarter_kernel<G>, grid, dim3(256), 0, stream, p.w, p.x, y, n, k, (int32_t)waves)
+    switch (gsl) {
+      case 2: Q2K_GEMV_Q(2); break;
+      case 3: Q2K_GEMV_Q(3); break;
+      case 4: Q2K_GEMV_Q(4); break;
+      case 5: Q2K_GEMV_Q(5); break;
+      default: Q2K_GEMV_Q(6); break;
+    }
+#undef Q2K_GEMV_Q
     return hipGetLastError();
   }
   int gsl = 0;

@@ -299,69 +299,6 @@ __device__ __forceinline__ void store_dots(int32_t* dots, const WHalf& w, const 
   *reinterpret_cast<u32x4*>(o + 4) = u32x4{(uint32_t)I[2], (uint32_t)Mv[2], (uint32_t)I[3], (uint32_t)Mv[3]};
 }
 
-// ---------------------------------------------------------------------------
-// Cross-lane helpers on fp64 values (moved as two dwords).
-
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
-  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
-
-// DPP controls whose partner is exactly lane l ^ OFF: quad_perm [1,0,3,2]
-// and [2,3,0,1] for 1 and 2, row_ror:8 for 8 (a rotation by half of a
-// 16-lane row).
-template <int OFF> struct DppPartner;
-template <> struct DppPartner<8> { static constexpr int ctrl = 0x128; };
-template <> struct DppPartner<2> { static constexpr int ctrl = 0x4E; };
-template <> struct DppPartner<1> { static constexpr int ctrl = 0xB1; };
-
-__device__ __forceinline__ uint64_t bits64(double v) { return __builtin_bit_cast(uint64_t, v); }
-__device__ __forceinline__ double from_bits(uint32_t lo, uint32_t hi) {
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
-// Lane l ^ 4's value (ds_swizzle in xor mode, within 32 lanes).
-__device__ __forceinline__ double xor4_f64(double v) {
-  const uint64_t b = bits64(v);
-  const int lo = __builtin_amdgcn_ds_swizzle((int)(uint32_t)b, 0x101F);
-  const int hi = __builtin_amdgcn_ds_swizzle((int)(uint32_t)(b >> 32), 0x101F);
-  return from_bits((uint32_t)lo, (uint32_t)hi);
-}
-
-// One halving level of a transposed reduction: lanes whose bit OFF is 0 end
-// with X summed over the lane pair (l, l ^ OFF), the others with Y summed
-// over the pair.
-template <int OFF>
-__device__ __forceinline__ double halve(double x, double y, int lane) {
-  if constexpr (OFF == 32) {
-    // swaps lanes 32..63 of the first operand with lanes 0..31 of the second
-    const uint64_t bx = bits64(x), by = bits64(y);
-    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)bx, (uint32_t)by, false, false);
-    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(bx >> 32), (uint32_t)(by >> 32),
-                                                     false, false);
-    return from_bits(lo[0], hi[0]) + from_bits(lo[1], hi[1]);
-  } else if constexpr (OFF == 16) {
-    // swaps the odd 16-lane rows of the first operand with the even rows of the second
-    const uint64_t bx = bits64(x), by = bits64(y);
-    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)bx, (uint32_t)by, false, false);
-    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(bx >> 32), (uint32_t)(by >> 32),
-                                                     false, false);
-    return from_bits(lo[0], hi[0]) + from_bits(lo[1], hi[1]);
-  } else {
-    const bool up = (lane & OFF) != 0;
-    const double send = up ? x : y;
-    const double keep = up ? y : x;
-    if constexpr (OFF == 4) {
-      return keep + xor4_f64(send);
-    } else {
-      return keep + dpp_f64<DppPartner<OFF>::ctrl>(send);
-    }
-  }
-}
-
 // Sum eight per-lane values a[0..7] (eight row steps) over groups of
 // GS = 1 << GSL lanes (GS >= 8) at once. Lanes hold half blocks in the order
 // 2b + h, so the pairwise tree over the super-blocks takes the lane offsets
