@@ -41,14 +41,12 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(const uint8_t* __rest
 }
 
 // The three gate sums over a 256-thread workgroup at once: each wave folds
-// its 64 lanes (xor tree), then the four wave sums are added as
-// (w0 + w1) + (w2 + w3). One barrier for all three.
+// its 64 lanes (wave_sum_f32: partners l ^ 1 .. l ^ 32), then the four wave
+// sums are added as (w0 + w1) + (w2 + w3). One barrier for all three.
 __device__ __forceinline__ void block_sum3_256(float& a, float& b, float& c, float* lds) {
-  for (int off = 32; off > 0; off >>= 1) {
-    a += __shfl_xor(a, off);
-    b += __shfl_xor(b, off);
-    c += __shfl_xor(c, off);
-  }
+  a = wave_sum_f32(a);
+  b = wave_sum_f32(b);
+  c = wave_sum_f32(c);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     lds[wave] = a;

@@ -241,7 +241,15 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint8_t* w, const 
 #pragma unroll
     for (int t = 0; t < M; ++t) {
       double v = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
-      for (int off = gs >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      switch (gs_log2) {
+        case 0: break;
+        case 1: v = group_sum_f64<1>(v, lane); break;
+        case 2: v = group_sum_f64<2>(v, lane); break;
+        case 3: v = group_sum_f64<3>(v, lane); break;
+        case 4: v = group_sum_f64<4>(v, lane); break;
+        case 5: v = group_sum_f64<5>(v, lane); break;
+        default: v = group_sum_f64<6>(v, lane); break;
+      }
       if (hb0 == 0 && row < n) y[(int64_t)t * n + row] = (float)v;
     }
   }

@@ -285,9 +285,25 @@ __device__ __forceinline__ double half_block_value(const WHalf& w, const AHalf& 
 // order 2b + h: lane offsets 2, 4, .., gs/2 first (the pairwise tree over
 // the row's super-blocks for each half), then 1 (the two halves), the same
 // tree as every other product kernel.
-__device__ __forceinline__ double group_sum(double v, int gs) {
-  for (int off = 2; off < gs; off <<= 1) v += __shfl_xor(v, off);
-  return v + __shfl_xor(v, 1);
+template <int GSL>
+__device__ __forceinline__ double group_sum_t(double v, int lane) {
+  if constexpr (GSL >= 2) v += dpp_f64<DppPartner<2>::ctrl>(v);
+  if constexpr (GSL >= 3) v += xor4_f64(v);
+  if constexpr (GSL >= 4) v += dpp_f64<DppPartner<8>::ctrl>(v);
+  if constexpr (GSL >= 5) v = halve<16>(v, v, lane);
+  if constexpr (GSL >= 6) v = halve<32>(v, v, lane);
+  return v + dpp_f64<DppPartner<1>::ctrl>(v);
+}
+
+__device__ __forceinline__ double group_sum(double v, int gs, int lane) {
+  switch (gs) {
+    case 2: return group_sum_t<1>(v, lane);
+    case 4: return group_sum_t<2>(v, lane);
+    case 8: return group_sum_t<3>(v, lane);
+    case 16: return group_sum_t<4>(v, lane);
+    case 32: return group_sum_t<5>(v, lane);
+    default: return group_sum_t<6>(v, lane);
+  }
 }
 
 __device__ __forceinline__ void store_dots(int32_t* dots, const WHalf& w, const AHalf& a, int t,
@@ -899,7 +915,7 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
             if (live) store_dots(p.dots, w, a, t, J.n, row, k, b, h);
           } else {
             double part = live ? half_block_value(w, a) : 0.0;
-            part = group_sum(part, gs);
+            part = group_sum(part, gs, lane);
             if (hb == 0 && row < J.n)
               J.y[(int64_t)t * J.ldy + row] = J.bad ? quiet_nan() : (float)part;
           }
@@ -957,7 +973,12 @@ __global__ __launch_bounds__(256) void mmvq_wide_kernel(const MmvqParams p) {
           }
         }
         if constexpr (!DOTS) {
-          for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off);
+          // the chunk's 32 leaves, neighbours first (partners l ^ 1 .. l ^ 16)
+          v += dpp_f64<DppPartner<1>::ctrl>(v);
+          v += dpp_f64<DppPartner<2>::ctrl>(v);
+          v += xor4_f64(v);
+          v += dpp_f64<DppPartner<8>::ctrl>(v);
+          v = halve<16>(v, v, lane);
           // binary counter: chunk c closes the subtrees of its trailing ones
           bool carry = true;
 #pragma unroll
@@ -978,7 +999,7 @@ __global__ __launch_bounds__(256) void mmvq_wide_kernel(const MmvqParams p) {
 #pragma unroll
         for (int l = 0; l < kWideLevels; ++l)
           if (l == top) tot = stk[l];
-        tot += __shfl_xor(tot, 32);
+        tot = halve<32>(tot, tot, lane);   // the two halves
         if (lane == 0) J.y[(int64_t)t * J.ldy + row] = J.bad ? quiet_nan() : (float)tot;
       }
     }

@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const uint8_t* w0, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const double t = tot[i] + xchg[slot + i];
-      yv[i] = t + __shfl_xor(t, 32);
+      yv[i] = halve<32>(t, t, (int)(threadIdx.x & 63));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -49,6 +49,116 @@ __device__ __forceinline__ T gload(const void* p) {
   return *(const __attribute__((address_space(1))) T*)(p);
 }
 
+// ---------------------------------------------------------------------------
+// Cross-lane helpers on fp64 values (moved as two dwords).
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// DPP controls whose partner is exactly lane l ^ OFF: quad_perm [1,0,3,2]
+// and [2,3,0,1] for 1 and 2, row_ror:8 for 8 (a rotation by half of a
+// 16-lane row).
+template <int OFF> struct DppPartner;
+template <> struct DppPartner<8> { static constexpr int ctrl = 0x128; };
+template <> struct DppPartner<2> { static constexpr int ctrl = 0x4E; };
+template <> struct DppPartner<1> { static constexpr int ctrl = 0xB1; };
+
+__device__ __forceinline__ uint64_t bits64(double v) { return __builtin_bit_cast(uint64_t, v); }
+__device__ __forceinline__ double from_bits(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Lane l ^ 4's value (ds_swizzle in xor mode, within 32 lanes).
+__device__ __forceinline__ double xor4_f64(double v) {
+  const uint64_t b = bits64(v);
+  const int lo = __builtin_amdgcn_ds_swizzle((int)(uint32_t)b, 0x101F);
+  const int hi = __builtin_amdgcn_ds_swizzle((int)(uint32_t)(b >> 32), 0x101F);
+  return from_bits((uint32_t)lo, (uint32_t)hi);
+}
+
+// One halving level of a transposed reduction: lanes whose bit OFF is 0 end
+// with X summed over the lane pair (l, l ^ OFF), the others with Y summed
+// over the pair.
+template <int OFF>
+__device__ __forceinline__ double halve(double x, double y, int lane) {
+  if constexpr (OFF == 32) {
+    // swaps lanes 32..63 of the first operand with lanes 0..31 of the second
+    const uint64_t bx = bits64(x), by = bits64(y);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)bx, (uint32_t)by, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(bx >> 32), (uint32_t)(by >> 32),
+                                                     false, false);
+    return from_bits(lo[0], hi[0]) + from_bits(lo[1], hi[1]);
+  } else if constexpr (OFF == 16) {
+    // swaps the odd 16-lane rows of the first operand with the even rows of the second
+    const uint64_t bx = bits64(x), by = bits64(y);
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)bx, (uint32_t)by, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(bx >> 32), (uint32_t)(by >> 32),
+                                                     false, false);
+    return from_bits(lo[0], hi[0]) + from_bits(lo[1], hi[1]);
+  } else {
+    const bool up = (lane & OFF) != 0;
+    const double send = up ? x : y;
+    const double keep = up ? y : x;
+    if constexpr (OFF == 4) {
+      return keep + xor4_f64(send);
+    } else {
+      return keep + dpp_f64<DppPartner<OFF>::ctrl>(send);
+    }
+  }
+}
+
+
+// 32-bit cross-lane partners: DPP for l ^ 1, l ^ 2 and l ^ 8, ds_swizzle in
+// xor mode for l ^ 4, and the permlane swaps for the sums with l ^ 16 and
+// l ^ 32 (each lane gets its own value plus its partner's).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t xor4_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);
+}
+__device__ __forceinline__ float sum_xor16_f32(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32_f32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// f32 sum over all 64 lanes, left on every lane: partners l ^ 1, l ^ 2, ..,
+// l ^ 32 in that order.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v)));
+  v += __uint_as_float(xor4_u32(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x128>(__float_as_uint(v)));
+  v = sum_xor16_f32(v);
+  return sum_xor32_f32(v);
+}
+
+// The sum of v over each aligned group of 1 << GSL lanes (GSL <= 6), left on
+// every lane of the group: partners l ^ 1, l ^ 2, l ^ 4, l ^ 8, l ^ 16, l ^ 32
+// in that order, each level one exchange and one add (DPP, ds_swizzle or
+// permlane swaps: no LDS round trip).
+template <int GSL>
+__device__ __forceinline__ double group_sum_f64(double v, int lane) {
+  static_assert(GSL >= 0 && GSL <= 6, "at most one wave");
+  if constexpr (GSL >= 1) v += dpp_f64<DppPartner<1>::ctrl>(v);
+  if constexpr (GSL >= 2) v += dpp_f64<DppPartner<2>::ctrl>(v);
+  if constexpr (GSL >= 3) v += xor4_f64(v);
+  if constexpr (GSL >= 4) v += dpp_f64<DppPartner<8>::ctrl>(v);
+  if constexpr (GSL >= 5) v = halve<16>(v, v, lane);
+  if constexpr (GSL >= 6) v = halve<32>(v, v, lane);
+  return v;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // f32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
@@ -142,8 +252,8 @@ __device__ __forceinline__ Q8Lane q8_1_quant8(const float* v) {
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
-  a = fmaxf(a, __shfl_xor(a, 1));
-  a = fmaxf(a, __shfl_xor(a, 2));
+  a = fmaxf(a, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(a))));
+  a = fmaxf(a, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(a))));
   Q8Lane r;
   r.d = q8_1_scale(a);
   int q[8];
@@ -151,7 +261,7 @@ __device__ __forceinline__ Q8Lane q8_1_quant8(const float* v) {
   int s = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) s += q[i];
-  r.s = s + __shfl_xor(s, 1);
+  r.s = s + (int)dpp_u32<0xB1>((uint32_t)s);
   r.lo = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
          ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
   r.hi = (uint32_t)(q[4] & 0xff) | ((uint32_t)(q[5] & 0xff) << 8) |
@@ -275,84 +385,5 @@ __device__ __forceinline__ bool hash_cols(const int64_t tok[kMaxNgram], const in
   return ok;
 }
 
-// ---------------------------------------------------------------------------
-// Cross-lane helpers on fp64 values (moved as two dwords).
-
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
-  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
-
-// DPP controls whose partner is exactly lane l ^ OFF: quad_perm [1,0,3,2]
-// and [2,3,0,1] for 1 and 2, row_ror:8 for 8 (a rotation by half of a
-// 16-lane row).
-template <int OFF> struct DppPartner;
-template <> struct DppPartner<8> { static constexpr int ctrl = 0x128; };
-template <> struct DppPartner<2> { static constexpr int ctrl = 0x4E; };
-template <> struct DppPartner<1> { static constexpr int ctrl = 0xB1; };
-
-__device__ __forceinline__ uint64_t bits64(double v) { return __builtin_bit_cast(uint64_t, v); }
-__device__ __forceinline__ double from_bits(uint32_t lo, uint32_t hi) {
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
-// Lane l ^ 4's value (ds_swizzle in xor mode, within 32 lanes).
-__device__ __forceinline__ double xor4_f64(double v) {
-  const uint64_t b = bits64(v);
-  const int lo = __builtin_amdgcn_ds_swizzle((int)(uint32_t)b, 0x101F);
-  const int hi = __builtin_amdgcn_ds_swizzle((int)(uint32_t)(b >> 32), 0x101F);
-  return from_bits((uint32_t)lo, (uint32_t)hi);
-}
-
-// One halving level of a transposed reduction: lanes whose bit OFF is 0 end
-// with X summed over the lane pair (l, l ^ OFF), the others with Y summed
-// over the pair.
-template <int OFF>
-__device__ __forceinline__ double halve(double x, double y, int lane) {
-  if constexpr (OFF == 32) {
-    // swaps lanes 32..63 of the first operand with lanes 0..31 of the second
-    const uint64_t bx = bits64(x), by = bits64(y);
-    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)bx, (uint32_t)by, false, false);
-    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(bx >> 32), (uint32_t)(by >> 32),
-                                                     false, false);
-    return from_bits(lo[0], hi[0]) + from_bits(lo[1], hi[1]);
-  } else if constexpr (OFF == 16) {
-    // swaps the odd 16-lane rows of the first operand with the even rows of the second
-    const uint64_t bx = bits64(x), by = bits64(y);
-    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)bx, (uint32_t)by, false, false);
-    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(bx >> 32), (uint32_t)(by >> 32),
-                                                     false, false);
-    return from_bits(lo[0], hi[0]) + from_bits(lo[1], hi[1]);
-  } else {
-    const bool up = (lane & OFF) != 0;
-    const double send = up ? x : y;
-    const double keep = up ? y : x;
-    if constexpr (OFF == 4) {
-      return keep + xor4_f64(send);
-    } else {
-      return keep + dpp_f64<DppPartner<OFF>::ctrl>(send);
-    }
-  }
-}
-
-
-// The sum of v over each aligned group of 1 << GSL lanes (GSL <= 6), left on
-// every lane of the group: partners l ^ 1, l ^ 2, l ^ 4, l ^ 8, l ^ 16, l ^ 32
-// in that order, each level one exchange and one add (DPP, ds_swizzle or
-// permlane swaps: no LDS round trip).
-template <int GSL>
-__device__ __forceinline__ double group_sum_f64(double v, int lane) {
-  static_assert(GSL >= 0 && GSL <= 6, "at most one wave");
-  if constexpr (GSL >= 1) v += dpp_f64<DppPartner<1>::ctrl>(v);
-  if constexpr (GSL >= 2) v += dpp_f64<DppPartner<2>::ctrl>(v);
-  if constexpr (GSL >= 3) v += xor4_f64(v);
-  if constexpr (GSL >= 4) v += dpp_f64<DppPartner<8>::ctrl>(v);
-  if constexpr (GSL >= 5) v = halve<16>(v, v, lane);
-  if constexpr (GSL >= 6) v = halve<32>(v, v, lane);
-  return v;
-}
 
 }  // namespace q2k
