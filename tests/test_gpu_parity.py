@@ -1283,6 +1283,25 @@ def test_engram_step_is_the_composition():
     assert_close(h1.cpu().numpy(), h_ref, "engram step, 8 tokens end to end")
 
 
+@pytest.mark.parametrize("start", [0, 32])
+def test_engram_step_longest_window(start):
+    """The longest n-gram window (8 tokens: 7 cached ids per column), two
+    heads (14 row ids, k = 3584) and a projection large enough for the rows
+    to be formed in the product's prologue ([4096, 3584]: 2048 row steps):
+    every bit of the separate calls, from the first positions (windows that
+    reach before the sequence) and after a prefill."""
+    hc = syn.engram_hash_case(seqlen=48, max_ngram=8, n_heads=2)
+    rng = syn.rng_for(1012)
+    table = syn.q2k_blocks(rng, 500000, 1)
+    dim, hcs = 1024, 3
+    wkv = syn.q2k_blocks(rng, (hcs + 1) * dim, 14)
+    h, _, qk, eps = syn.gate_case(1012, 1, hcs, dim)
+    assert q2.q2k_product_kernel((hcs + 1) * dim, 14 * 256, 1) == PD
+    for layer in (0, 1):
+        _engram_step_both_ways(hc, table, wkv, h, qk, eps, hc.tokens[start:start + 8].tolist(), start,
+                               layer, 500000, hcs, dim)
+
+
 def test_engram_step_small_and_bad_token():
     """A projection too small for the run kernel (dim 256: the rows launch
     ahead of the product) and a token outside the vocabulary (NaN rows, the
