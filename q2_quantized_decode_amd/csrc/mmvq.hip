@@ -660,7 +660,7 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
       // the third and last dependent round.
       const bool hthread = tid < cols;
       const int c = hthread ? tid : 0;
-      const int ng = E.ng, nh = E.n_heads;
+      const int nh = E.n_heads;
       const int64_t pos = E.pos;
       // The loaded values enter through empty asm statements, as opaque VGPR
       // values: otherwise the compiler, seeing uniform values, moves them to
