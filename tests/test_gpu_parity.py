@@ -1045,7 +1045,8 @@ def test_engram_step(engram):
 
 @pytest.mark.parametrize("n,k,m", [(257, 1024, 1), (100, 2048, 3), (33, 7168, 8), (10, 9216, 2),
                                    (5, 256, 1), (64, 4096, 5), (300, 768, 1), (70, 4096, 1),
-                                   (70001, 256, 1), (901, 6144, 1)])
+                                   (70001, 256, 1), (901, 6144, 1), (333, 512, 1), (40, 256, 2),
+                                   (40, 512, 3), (40, 1024, 4)])
 def test_gemv_bf16_bit_exact(n, k, m):
     """Exact expansion, exact products, fp64 sums: the f32 bits of the oracle."""
     case = syn.single_gemv_case(n=n, k=k, m=m, seed=900 + n + k + m)
