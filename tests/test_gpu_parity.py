@@ -1065,7 +1065,8 @@ def test_gemv_bf16_strided_input():
 
 def test_engram_step_bf16_projection(engram):
     """The pages' single-token route: gathered bf16 rows [1, 2048] straight
-    into the Q2_K wkv [20480, 2048] (no q8_1), then the gate."""
+    into the Q2_K wkv [20480, 2048] (no q8_1; every row bit for bit against
+    the oracle, in chunks), then the gate."""
     e = engram
     rows = q2.q2k_dequant_rows(dev(e.table.reshape(-1)), e.table.shape[0], dev(e.ids), e.cols)
     x = rows.view(1, e.cols * 256)
@@ -1073,10 +1074,10 @@ def test_engram_step_bf16_projection(engram):
     kv = q2.q2k_gemv_bf16(dev(e.wkv.reshape(-1)), x, n_out, e.cols * 256)
     kv_h = kv.cpu().numpy()
     x_bits = rows.view(torch.int16).cpu().numpy().view(np.uint16).reshape(1, -1)
-    sample = np.unique(np.concatenate([np.arange(0, 256), np.arange(n_out - 256, n_out),
-                                       syn.rng_for(12).choice(n_out, 1024, replace=False)]))
-    ref = orc.gemv_bf16(e.wkv[sample], x_bits)
-    assert np.array_equal(kv_h[:, sample].view(np.uint32), ref.view(np.uint32))
+    for r0 in range(0, n_out, CHUNK_ROWS):
+        r1 = min(n_out, r0 + CHUNK_ROWS)
+        ref = orc.gemv_bf16(e.wkv[r0:r1], x_bits)
+        assert np.array_equal(kv_h[:, r0:r1].view(np.uint32), ref.view(np.uint32)), f"rows {r0}..{r1}"
     hd = dev(e.h)
     q2.engram_gate(hd, kv, dev(e.qk), e.eps)
     assert_close(hd.cpu().numpy(), orc.engram_gate(e.h, kv_h, e.qk, e.eps), "gate after bf16 wkv")
