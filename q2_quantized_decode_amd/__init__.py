@@ -403,20 +403,57 @@ def engram_gate(h: torch.Tensor, kv: torch.Tensor, qk: torch.Tensor, eps: float)
     return h
 
 
+def _hash_tables(token_map: torch.Tensor, multipliers: torch.Tensor, primes: torch.Tensor,
+                 offsets: torch.Tensor, cache: torch.Tensor):
+    """Dtypes and shapes of the engram hash tables: multipliers int64
+    [n_layers, max_ngram], primes int64 [n_layers, max_ngram - 1, n_heads],
+    offsets int64 with one entry per prime. The kernels index these arrays
+    from (n_layers, max_ngram, n_heads), so a mis-shaped table would read
+    past its allocation: refused here. Returns (n_layers, max_ngram, n_heads)."""
+    for name, t in (("token_map", token_map), ("multipliers", multipliers), ("primes", primes),
+                    ("offsets", offsets), ("cache", cache)):
+        if t.dtype != torch.int64:
+            raise ValueError(f"{name} must be int64")
+    if multipliers.dim() != 2 or primes.dim() != 3:
+        raise ValueError("multipliers must be [n_layers, max_ngram] and primes "
+                         "[n_layers, max_ngram - 1, n_heads]")
+    n_layers, max_ngram = multipliers.shape
+    if primes.shape[0] != n_layers or primes.shape[1] != max_ngram - 1:
+        raise ValueError(f"primes {tuple(primes.shape)} does not match multipliers "
+                         f"{tuple(multipliers.shape)}")
+    if offsets.numel() != primes.numel():
+        raise ValueError("offsets must hold one entry per prime")
+    return n_layers, max_ngram, primes.shape[2]
+
+
+def _engram_step_buffers(table: torch.Tensor, n_table_rows: int, wkv: torch.Tensor, qk: torch.Tensor,
+                         h: torch.Tensor, token: torch.Tensor, cols: int):
+    """Sizes of the engram step's buffers against its shapes (the kernels
+    read table rows below n_table_rows, the whole wkv [(hc+1)*dim, cols*256]
+    and qk [hc, dim])."""
+    if token.dtype != torch.int32 or token.numel() < 1:
+        raise ValueError("token must be int32 with one element")
+    if h.dtype != torch.float32 or h.dim() != 3 or h.shape[0] != 1:
+        raise ValueError("h must be f32 [1, hc, dim]")
+    _, hc, dim = h.shape
+    if table.numel() * table.element_size() < n_table_rows * BLOCK_BYTES:
+        raise ValueError(f"table holds fewer than n_table_rows = {n_table_rows} blocks")
+    if wkv.numel() * wkv.element_size() != (hc + 1) * dim * cols * BLOCK_BYTES:
+        raise ValueError(f"wkv must be Q2_K [(hc+1)*dim, {cols * BLOCK_WEIGHTS}] for hc = {hc}, dim = {dim}")
+    if qk.dtype != torch.float32 or qk.numel() != hc * dim:
+        raise ValueError("qk must be f32 [hc, dim]")
+    return hc, dim
+
+
 def engram_hash(token_map: torch.Tensor, multipliers: torch.Tensor, primes: torch.Tensor,
                 offsets: torch.Tensor, pad_id: int, cache: torch.Tensor, ids: torch.Tensor,
                 start_pos: int, out: Optional[torch.Tensor] = None,
                 err_flag: Optional[torch.Tensor] = None) -> torch.Tensor:
     """int64 [n_layers, seqlen, (max_ngram-1)*n_heads] engram row ids for the
     int32 token ids at positions start_pos.. (the int64 ``cache`` is updated)."""
-    for name, t in (("token_map", token_map), ("multipliers", multipliers), ("primes", primes),
-                    ("offsets", offsets), ("cache", cache)):
-        if t.dtype != torch.int64:
-            raise ValueError(f"{name} must be int64")
+    n_layers, max_ngram, n_heads = _hash_tables(token_map, multipliers, primes, offsets, cache)
     if ids.dtype != torch.int32:
         raise ValueError("ids must be int32")
-    n_layers, max_ngram = multipliers.shape
-    n_heads = primes.shape[-1]
     cols = (max_ngram - 1) * n_heads
     seqlen = ids.numel()
     if out is None:
@@ -439,15 +476,12 @@ def engram_rows_q8_1(token_map: torch.Tensor, multipliers: torch.Tensor, primes:
     """One decode token (int32 ``token`` [1] at position ``pos``): hashed layer
     ``layer``'s row ids, their gather and dequantisation, and q8_1 of the rows
     viewed as one row, in one launch. Returns xq."""
-    for name, t in (("token_map", token_map), ("multipliers", multipliers), ("primes", primes),
-                    ("offsets", offsets), ("cache", cache)):
-        if t.dtype != torch.int64:
-            raise ValueError(f"{name} must be int64")
+    n_layers, max_ngram, n_heads = _hash_tables(token_map, multipliers, primes, offsets, cache)
     if token.dtype != torch.int32:
         raise ValueError("token must be int32")
-    n_layers, max_ngram = multipliers.shape
-    n_heads = primes.shape[-1]
     cols = (max_ngram - 1) * n_heads
+    if table.numel() * table.element_size() < n_table_rows * BLOCK_BYTES:
+        raise ValueError(f"table holds fewer than n_table_rows = {n_table_rows} blocks")
     need = q8_1_rows_bytes(1, cols * BLOCK_WEIGHTS)
     if xq is None:
         xq = torch.empty(max(need, 16), dtype=torch.uint8, device=table.device)
@@ -484,17 +518,8 @@ def engram_step(token_map: torch.Tensor, multipliers: torch.Tensor, primes: torc
     ``layer``, gather + dequant + q8_1, the wkv projection into kv and the
     gate on h [1, hc, dim] in place. Returns (h, workspace); the workspace
     starts with kv f32 [(hc+1)*dim]."""
-    for name, t in (("token_map", token_map), ("multipliers", multipliers), ("primes", primes),
-                    ("offsets", offsets), ("cache", cache)):
-        if t.dtype != torch.int64:
-            raise ValueError(f"{name} must be int64")
-    if token.dtype != torch.int32:
-        raise ValueError("token must be int32")
-    if h.dtype != torch.float32 or h.dim() != 3 or h.shape[0] != 1:
-        raise ValueError("h must be f32 [1, hc, dim]")
-    n_layers, max_ngram = multipliers.shape
-    n_heads = primes.shape[-1]
-    _, hc, dim = h.shape
+    n_layers, max_ngram, n_heads = _hash_tables(token_map, multipliers, primes, offsets, cache)
+    hc, dim = _engram_step_buffers(table, n_table_rows, wkv, qk, h, token, (max_ngram - 1) * n_heads)
     need = engram_step_workspace_bytes(max_ngram, n_heads, hc, dim)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=h.device)
@@ -515,17 +540,8 @@ def engram_step_noalloc(token_map: torch.Tensor, multipliers: torch.Tensor, prim
                         err_flag: Optional[torch.Tensor] = None) -> torch.Tensor:
     """engram_step with the library's own device array as its workspace (no
     allocation anywhere in the call); h [1, hc, dim] updated in place."""
-    for name, t in (("token_map", token_map), ("multipliers", multipliers), ("primes", primes),
-                    ("offsets", offsets), ("cache", cache)):
-        if t.dtype != torch.int64:
-            raise ValueError(f"{name} must be int64")
-    if token.dtype != torch.int32:
-        raise ValueError("token must be int32")
-    if h.dtype != torch.float32 or h.dim() != 3 or h.shape[0] != 1:
-        raise ValueError("h must be f32 [1, hc, dim]")
-    n_layers, max_ngram = multipliers.shape
-    n_heads = primes.shape[-1]
-    _, hc, dim = h.shape
+    n_layers, max_ngram, n_heads = _hash_tables(token_map, multipliers, primes, offsets, cache)
+    hc, dim = _engram_step_buffers(table, n_table_rows, wkv, qk, h, token, (max_ngram - 1) * n_heads)
     flag = _contig(err_flag, "err_flag") if err_flag is not None else None
     _check("engram_step_noalloc", lib().engram_step_noalloc(
         _contig(token_map, "token_map"), token_map.numel(), _contig(multipliers, "multipliers"),

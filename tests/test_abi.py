@@ -405,3 +405,34 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros((1, 256), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         q2.q8_1_rows(x)
+
+
+def test_engram_bindings_refuse_mis_shaped_tables():
+    """The kernels index the hash tables and the wkv matrix from the shapes
+    the binding derives (n_layers, max_ngram, n_heads, hc, dim): tables of
+    another shape, or a wkv of another size, are refused before any call."""
+    import numpy as np
+    import torch
+
+    from q2_quantized_decode_amd import synthetic as syn
+    hc = syn.engram_hash_case(seqlen=8)
+    e = syn.engram_step_case()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    cache = torch.zeros(16, dtype=torch.int64)
+    tok = torch.zeros(1, dtype=torch.int32)
+    good = (t(hc.token_map), t(hc.multipliers), t(hc.primes), t(hc.offsets))
+    flat = (good[0], good[1], t(hc.primes.reshape(hc.primes.shape[0], -1)), good[3])
+    for fn in (q2.engram_step, q2.engram_step_noalloc):
+        with pytest.raises(ValueError, match="primes"):
+            fn(*flat, hc.pad_id, cache, tok, 3, 0, t(e.table.reshape(-1)), e.table.shape[0],
+               t(e.wkv.reshape(-1)), t(e.qk), t(e.h), 1e-6)
+        with pytest.raises(ValueError, match="wkv"):
+            fn(*good, hc.pad_id, cache, tok, 3, 0, t(e.table.reshape(-1)), e.table.shape[0],
+               t(e.wkv.reshape(-1)[: 84 * 1000]), t(e.qk), t(e.h), 1e-6)
+        with pytest.raises(ValueError, match="table"):
+            fn(*good, hc.pad_id, cache, tok, 3, 0, t(e.table.reshape(-1)[:84]), e.table.shape[0],
+               t(e.wkv.reshape(-1)), t(e.qk), t(e.h), 1e-6)
+    with pytest.raises(ValueError, match="primes"):
+        q2.engram_hash(*flat, hc.pad_id, cache, t(hc.tokens[:4].astype(np.int32)), 0)
+    with pytest.raises(ValueError, match="primes"):
+        q2.engram_rows_q8_1(*flat, hc.pad_id, cache, tok, 3, 0, t(e.table.reshape(-1)), e.table.shape[0])

@@ -64,6 +64,6 @@ def test_engram_step_noalloc_refuses_steps_past_its_array():
                                torch.zeros(16, dtype=torch.int64, device="cuda"),
                                d(np.array([1], dtype=np.int32)), 3, 0,
                                torch.zeros(84 * 16, dtype=torch.uint8, device="cuda"), 16,
-                               torch.zeros(84, dtype=torch.uint8, device="cuda"),
+                               torch.zeros(5 * dim * 8 * 84, dtype=torch.uint8, device="cuda"),
                                torch.zeros((4, dim), dtype=torch.float32, device="cuda"), h, 1e-6)
     assert e.value.code == -3 and "scratch array" in str(e.value)
