@@ -680,23 +680,24 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
       tk[0] = blocked ? E.pad_id : own;
 #pragma unroll
       for (int i = 1; i < kMaxNgram; ++i) {
-        blocked = blocked || pos < i || cw[i] == -1;
+        blocked = blocked | (pos < i) | (cw[i] == -1);   // no short-circuit branches
         tk[i] = blocked ? E.pad_id : cw[i];
       }
       const int ic = c / nh + 1;                   // the window length of column c
-      uint64_t rolling = (uint64_t)tk[0] * (uint64_t)mu[0];
+      // rolling xor of the window's products: the running xor over i, then
+      // column c's value at i = ic picked without branches
+      uint64_t acc = (uint64_t)tk[0] * (uint64_t)mu[0];
+      uint64_t rolling = acc;
 #pragma unroll
-      for (int i = 1; i < kMaxNgram; ++i)
-        if (i <= ic) rolling ^= (uint64_t)tk[i] * (uint64_t)mu[i];
+      for (int i = 1; i < kMaxNgram; ++i) {
+        acc ^= (uint64_t)tk[i] * (uint64_t)mu[i];
+        rolling = i == ic ? acc : rolling;
+      }
       // a prime <= 0 makes its column and every later one -1 (column order)
       const uint64_t badp = __ballot(hthread && pr <= 0);
       const bool ok = tok_ok && (badp & ((2ull << c) - 1ull)) == 0;
-      int64_t v = -1;
-      if (ok) {
-        int64_t r = (int64_t)rolling % pr;
-        if (r < 0) r += pr;
-        v = (int64_t)((uint64_t)r + (uint64_t)of);
-      }
+      const int64_t r = mod_euclid_i64((int64_t)rolling, ok ? pr : 1);
+      const int64_t v = ok ? (int64_t)((uint64_t)r + (uint64_t)of) : -1;
       if (hthread) {
         rid[tid] = v;
         if (blockIdx.x == 0) {

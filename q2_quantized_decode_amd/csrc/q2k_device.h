@@ -317,6 +317,35 @@ __device__ __forceinline__ void q2k_dequant4(const uint8_t* blk, int e, uint32_t
   }
 }
 
+// x mod p in [0, p) for p > 0 (the Euclidean remainder: C's % then + p when
+// negative). For p < 2^32 the unsigned remainder is taken 16 bits at a time
+// in fp64: every partial dividend is below p * 2^16 < 2^48, so it, the
+// quotient estimate's product and the difference are exact, and the
+// estimate floor(D * (1/p)) is off by at most one, which one compare each
+// way corrects. Larger p take the integer division.
+__device__ __forceinline__ int64_t mod_euclid_i64(int64_t x, int64_t p) {
+  const bool neg = x < 0;
+  const uint64_t u = neg ? 0ull - (uint64_t)x : (uint64_t)x;
+  uint64_t r;
+  if ((uint64_t)p >> 32 == 0) {
+    const double pd = (double)p;
+    const double inv = 1.0 / pd;
+    double rr = 0.0;
+#pragma unroll
+    for (int k = 3; k >= 0; --k) {
+      const double dv = fma(rr, 65536.0, (double)((u >> (16 * k)) & 0xffffull));
+      const double q = floor(dv * inv);
+      double t = fma(-q, pd, dv);
+      t = t < 0.0 ? t + pd : t;
+      rr = t >= pd ? t - pd : t;
+    }
+    r = (uint64_t)rr;
+  } else {
+    r = u % (uint64_t)p;
+  }
+  return (int64_t)(neg && r != 0 ? (uint64_t)p - r : r);
+}
+
 // Engram n-gram hash helpers (engram_v41.rs, EngramHasher::hash), shared by
 // the hash kernels and the product's engram prologue.
 constexpr int kMaxNgram = 8;
@@ -372,8 +401,7 @@ __device__ __forceinline__ bool hash_cols(const int64_t tok[kMaxNgram], const in
       const int64_t pr = primes[((int64_t)l * (ng - 1) + (i - 1)) * n_heads + h];
       int64_t v = -1;
       if (ok && pr > 0) {
-        int64_t r = (int64_t)rolling % pr;
-        if (r < 0) r += pr;
+        const int64_t r = mod_euclid_i64((int64_t)rolling, pr);
         v = (int64_t)((uint64_t)r + (uint64_t)offsets[(int64_t)l * cols + col]);
       } else {
         ok = false;

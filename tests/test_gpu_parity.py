@@ -10,6 +10,8 @@ bf16 ulp (the GPU forms it in f32, the oracle in fp64), with its q8_1 bytes
 bit-exact from the GPU's own h.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -1111,6 +1113,25 @@ def test_engram_hash_prefill_then_decode():
         assert np.array_equal(got.cpu().numpy(), want), f"decode step {s}"
     assert np.array_equal(cache.cpu().numpy(), np.array(ocache, dtype=np.int64))
     assert int(flag.item()) == 0
+
+
+def test_engram_hash_moduli_across_the_range():
+    """Row ids for moduli from 1 to 2^62, both sides of 2^32 (the kernels take
+    the remainder 16 bits at a time in fp64 below 2^32, by integer division
+    above): every id bit for bit against the oracle's Python remainder, over
+    rolling hashes of both signs."""
+    hc = syn.engram_hash_case(seed=14, seqlen=48)
+    mods = [(1 << 32) - 5, (1 << 32) - 1, (1 << 31) + 11, 1, 2, 65537, 1 << 32, (1 << 32) + 15,
+            (1 << 40) + 7, (1 << 62) + 3, 3, 1234567891, 999999937, (1 << 33) - 9, 7, 65521]
+    primes = np.array(mods, dtype=np.int64).reshape(hc.primes.shape)
+    offsets = np.zeros_like(hc.offsets)
+    big = dataclasses.replace(hc, primes=primes, offsets=offsets)
+    tm, mu, pr, of = _hash_tables_dev(big)
+    cache = torch.zeros(64, dtype=torch.int64, device="cuda")
+    got = q2.engram_hash(tm, mu, pr, of, big.pad_id, cache, dev(big.tokens[:48]), 0)
+    want, _ = _oracle_hash_layer_major(big, [0] * 64, big.tokens[:48].tolist(), 0)
+    assert np.array_equal(got.cpu().numpy(), want)
+    assert (want < 0).sum() < want.size // 4        # mostly real ids, not blocked columns
 
 
 def test_engram_hash_wide_ngram_and_large_ids():
