@@ -16,15 +16,16 @@ Method:
   times (1.23 GB, over four times the 256 MB Infinity Cache) and step i reads
   copy i % 16, so every step streams its matrix from HBM.
 * The W warm-up steps and the K timed steps are captured into two HIP
-  graphs (copy i % 16) and uploaded. On the launching stream a short sleep
-  kernel covers the host's enqueueing, then the warm-up graph runs, then a
-  start event, the timed graph and an end event: the GPU is busy when the
-  start event is reached and the events bracket exactly the K steps;
-  ms_per_step = event time / K.
+  graphs (copy i % 16) and uploaded. On the launching stream about 40 ms of
+  untimed load (the m = 1 product over the copies) settles the clocks and
+  covers the host's enqueueing, then the warm-up graph runs, then a start
+  event, the timed graph and an end event: the GPU is busy when the start
+  event is reached and the events bracket exactly the K steps;
+  ms_per_step = event time / K. (After an idle GPU the shader clock runs at
+  1.5-1.9 GHz for the first ~15 ms of streaming and at 2.0-2.25 GHz after.)
 * Roofline of the dominant kernel (q2k_mmvq), timed first for each m:
-  products alone, a graph of 128 launches replayed 4 times untimed (the
-  GPU's clocks settle during the first milliseconds of streaming) and then
-  5 times between HIP events, achieved = algorithmic bytes
+  products alone, a graph of 128 launches replayed untimed for about 40 ms
+  and then 5 times between HIP events, achieved = algorithmic bytes
   per launch / average launch time between the events (gaps between
   consecutive kernels included). Beside it, the per-dispatch average of the
   same kernel from the committed rocprofv3 kernel trace
@@ -191,34 +192,49 @@ def graph_us(torch, fn, launches: int, reps: int = 20, chunk: int = GRAPH) -> fl
             for i in range(c0, min(c0 + chunk, launches)):
                 fn(i)
         graphs.append(g)
-    with torch.cuda.stream(stream):
+    def one_pass():
         for g in graphs:
             g.replay()
+
+    settle(torch, stream, one_pass)
+    with torch.cuda.stream(stream):
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
         for _ in range(reps):
-            for g in graphs:
-                g.replay()
+            one_pass()
         ev1.record(stream)
         ev1.synchronize()
     return ev0.elapsed_time(ev1) * 1e3 / (reps * launches)
 
 
-def sleep_cycles_for(torch, stream, us: float) -> int:
-    """GPU sleep-kernel cycles (torch.cuda._sleep) that last about `us`
-    microseconds on this device, measured once with HIP events."""
-    cyc = 1 << 20
+# Untimed load ahead of every timed region, in milliseconds of GPU time.
+# Measured with a copy of the m = 1 product kernel that reads the shader-clock
+# and the constant 100 MHz counters at the start and end of each wave: after
+# an idle GPU the clock runs at 1.5-1.9 GHz for the first ~15 ms of
+# streaming, then at 2.0-2.25 GHz; the same launches take 14.8-18 us per
+# launch in the first milliseconds and 13.9-14.5 us once settled.
+SETTLE_MS = 40.0
+
+
+def settle(torch, stream, replay) -> int:
+    """Enqueues on `stream` untimed passes of `replay` (a callable that
+    enqueues one pass of a workload) covering about SETTLE_MS of GPU time, so
+    that the clocks have settled and the GPU is still busy when the caller
+    records its start event. One pass is timed first to size the count.
+    Returns the number of untimed passes enqueued after it."""
     with torch.cuda.stream(stream):
-        torch.cuda._sleep(cyc)      # first launch (module load) untimed
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        torch.cuda._sleep(cyc)
+        replay()
         e1.record(stream)
-        e1.synchronize()
-    per_us = cyc / max(e0.elapsed_time(e1) * 1e3, 1e-3)
-    return int(per_us * us)
+    e1.synchronize()
+    n = max(1, int(-(-SETTLE_MS // max(e0.elapsed_time(e1), 1e-3))))
+    with torch.cuda.stream(stream):
+        for _ in range(n):
+            replay()
+    return n
 
 
 _HIP = None
@@ -254,17 +270,19 @@ def capture(torch, stream, fn, first: int, count: int):
     return g
 
 
-def timed_steps(torch, stream, fn, warm: int, count: int, busy: int, reps: int = 1) -> float:
+def timed_steps(torch, stream, fn, warm: int, count: int, load, reps: int = 1) -> float:
     """Seconds per call of fn(i) over `count` calls i = warm .. warm+count-1,
     after `warm` untimed calls i = 0 .. warm-1. Both runs are captured into
-    uploaded HIP graphs; on `stream` a short sleep kernel (`busy` cycles)
-    covers the host's enqueueing, then the warm-up graph, the start event,
-    `reps` replays of the timed graph and the end event: the events bracket
-    exactly reps * count calls, with the GPU busy up to the start event."""
+    uploaded HIP graphs; on `stream` about SETTLE_MS of untimed load (passes
+    of `load`, a callable enqueueing one pass of another workload) settles
+    the clocks and covers the host's enqueueing, then the warm-up graph, the
+    start event, `reps` replays of the timed graph and the end event: the
+    events bracket exactly reps * count calls, with the GPU busy up to the
+    start event."""
     g_warm = capture(torch, stream, fn, 0, warm)
     g = capture(torch, stream, fn, warm, count)
+    settle(torch, stream, load)
     with torch.cuda.stream(stream):
-        torch.cuda._sleep(busy)
         if g_warm is not None:
             g_warm.replay()
         ev0 = torch.cuda.Event(enable_timing=True)
@@ -278,14 +296,14 @@ def timed_steps(torch, stream, fn, warm: int, count: int, busy: int, reps: int =
     return ev0.elapsed_time(ev1) / 1e3 / (count * reps)
 
 
-def replay_timed(torch, stream, fn, count: int, reps: int, warm_reps: int = 1) -> float:
+def replay_timed(torch, stream, fn, count: int, reps: int) -> float:
     """Seconds per call of fn(i), i = 0 .. count-1, captured into one HIP
-    graph: `warm_reps` untimed replays (they also keep the GPU busy while the
-    host enqueues the rest), then `reps` replays between HIP events."""
+    graph: untimed replays for about SETTLE_MS (they also keep the GPU busy
+    while the host enqueues the rest), then `reps` replays between HIP
+    events."""
     g = capture(torch, stream, fn, 0, count)
+    settle(torch, stream, g.replay)
     with torch.cuda.stream(stream):
-        for _ in range(warm_reps):
-            g.replay()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
@@ -297,21 +315,21 @@ def replay_timed(torch, stream, fn, count: int, reps: int, warm_reps: int = 1) -
     return ev0.elapsed_time(ev1) / 1e3 / (count * reps)
 
 
-ROOF_GRAPH, ROOF_WARM_REPS, ROOF_REPS = 128, 4, 5
+ROOF_GRAPH, ROOF_REPS = 128, 5
 
 
 def product_roofline(torch, q2, stream, copies, x8, m: int, same_copy: bool = True):
     """Average time of one q2k_mmvq launch on the large verify matrix: a
-    graph of 128 launches (copy i % 16), 4 untimed replays (~7 ms: after an
-    idle GPU the first few ms of streaming run slower, up to ~18 us per
-    launch, before the clocks settle), then 5 replays (640 launches) between
-    HIP events; with same_copy also the same with one weight copy for every
+    graph of 128 launches (copy i % 16), untimed replays for about SETTLE_MS
+    (after an idle GPU the first ~15 ms of streaming run at lower clocks, up
+    to ~18 us per launch), then 5 replays (640 launches) between HIP
+    events; with same_copy also the same with one weight copy for every
     launch (cache-resident reference). Replaying one graph matters: a
     second graph of the same launches measured ~0.6 us per launch slower."""
     xq = q2.q8_1_rows(x8[:m].contiguous())
     y = torch.empty((m, N), dtype=torch.float32, device=x8.device)
     launch_s = replay_timed(torch, stream, lambda i: q2.q2k_mmvq(copies[i % COPIES], xq, N, K, m, out=y),
-                            ROOF_GRAPH, ROOF_REPS, ROOF_WARM_REPS)
+                            ROOF_GRAPH, ROOF_REPS)
     warm_s = None
     if same_copy:
         warm_s = replay_timed(torch, stream, lambda i: q2.q2k_mmvq(copies[0], xq, N, K, m, out=y), 128, 2)
@@ -532,8 +550,8 @@ def bench_mmq(torch, q2, syn, dev, copies, case):
             for i in range(COPIES):
                 q2.q2k_mmq(copies[i], xq, N, K, m, out=y)
         reps = max(2, 64 // m)
+        settle(torch, stream, g.replay)
         with torch.cuda.stream(stream):
-            g.replay()
             ev0 = torch.cuda.Event(enable_timing=True)
             ev1 = torch.cuda.Event(enable_timing=True)
             ev0.record(stream)
@@ -777,7 +795,12 @@ def run(args):
 
     results = {}
     stream = torch.cuda.Stream()
-    busy = sleep_cycles_for(torch, stream, 500.0)      # ~0.5 ms of GPU time ahead of each run
+    # the untimed load ahead of each timed step run: the m = 1 product over
+    # the rotating copies (see SETTLE_MS)
+    xq_load = q2.q8_1_rows(x8[:1].contiguous())
+    y_load = torch.empty((1, N), dtype=torch.float32, device=dev)
+    g_load = capture(torch, stream, lambda i: q2.q2k_mmvq(copies[i % COPIES], xq_load, N, K, 1, out=y_load),
+                     0, ROOF_GRAPH)
     warm, steps = args.warmup, args.steps
     roof_launches = ROOF_GRAPH * ROOF_REPS
     for m in (1, 8):
@@ -798,8 +821,8 @@ def run(args):
         # 77 MB matrix fits the 256 MB Infinity Cache): reported beside, never
         # the roofline figure
         launch_s, warm_s = product_roofline(torch, q2, stream, copies, x8, m)
-        step_s = timed_steps(torch, stream, step, warm, steps, busy)
-        two_s = timed_steps(torch, stream, step_two_calls, warm, steps, busy)
+        step_s = timed_steps(torch, stream, step, warm, steps, g_load.replay)
+        two_s = timed_steps(torch, stream, step_two_calls, warm, steps, g_load.replay)
         step(warm + steps - 1)               # y of the last timed step, for the parity check
         torch.cuda.synchronize()
         step_bytes = mmvq_bytes(m) + q8_bytes(m)
@@ -863,6 +886,10 @@ def run(args):
                    "tokens_per_s": round(1 / r1["step_s"], 1),
                    "ms_per_step_two_launches": round(r1["two_s"] * 1e3, 5)},
         "roofline": roofline(1, r1),
+        "settle": {"ms": SETTLE_MS,
+                   "note": "untimed load run before each timed region (the m = 1 product over the "
+                           "rotating copies ahead of the warm-up steps; the region's own launches "
+                           "elsewhere) so that the clocks have left their idle state"},
         "cache_resident_us_per_launch": {
             "m1": round(r1["warm_s"] * 1e6, 3), "m8": round(r8["warm_s"] * 1e6, 3),
             "note": "same weight copy every launch (fits the Infinity Cache); not a roofline figure"},
@@ -978,8 +1005,9 @@ def rocprof_from(trace_csv: str, out: str):
     rec = {"command": ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d <out> -o prof "
                        "--output-format csv -- python3 /root/repo/bench.py --roofline-only; "
                        "python3 bench.py --rocprof-from <out>/prof_kernel_trace.csv"),
-           "dispatches": f"per m: {ROOF_WARM_REPS} untimed and {ROOF_REPS} timed replays of a "
-                         f"{ROOF_GRAPH}-launch graph over 16 rotating weight copies; the average is "
+           "dispatches": f"per m: untimed replays for about {SETTLE_MS:g} ms, then {ROOF_REPS} timed "
+                         f"replays of a {ROOF_GRAPH}-launch graph over 16 rotating weight copies; the "
+                         f"average is "
                          f"over the {timed} timed dispatches (the last {timed} of the kernel)"}
     for m, inst in KERNEL_INSTANCES.items():
         hit = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
@@ -1073,12 +1101,15 @@ def kernel_sweep_from(trace_csv: str, sweep_json: str) -> None:
 
 
 def main():
+    global SETTLE_MS
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3200)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--pmc-calibration", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed load ahead of every timed region, ms of GPU time")
     ap.add_argument("--only", default="",
                     help="comma list of workloads to run (" + ",".join(SECTIONS) + "); without "
                          "'headline' only their JSON is printed (profiling runs)")
@@ -1097,6 +1128,7 @@ def main():
                     help="write the product kernels' rocprofv3 averages from the kernel trace of "
                          "a --roofline-only run and exit")
     args = ap.parse_args()
+    SETTLE_MS = args.settle_ms
     if args.traffic_from:
         traffic_from(*args.traffic_from, TRAFFIC_FILE)
         return
