@@ -15,13 +15,14 @@ Method:
 * Inputs are resident in HBM before timing. The weights are replicated 16
   times (1.23 GB, over four times the 256 MB Infinity Cache) and step i reads
   copy i % 16, so every step streams its matrix from HBM.
-* The W warm-up steps and the K timed steps are captured into two HIP
-  graphs (copy i % 16) and uploaded. On the launching stream about 40 ms of
-  untimed load (the m = 1 product over the copies) settles the clocks and
-  covers the host's enqueueing, then the warm-up graph runs, then a start
-  event, the timed graph and an end event: the GPU is busy when the start
-  event is reached and the events bracket exactly the K steps;
-  ms_per_step = event time / K. (After an idle GPU the shader clock runs at
+* On the launching stream about 40 ms of untimed load (the m = 1 product
+  over the copies) settles the clocks and covers the host's enqueueing,
+  then the W warm-up steps, a start event, the K timed steps (copy i % 16)
+  and an end event: the GPU is busy when the start event is reached and the
+  events bracket exactly the K steps; ms_per_step = event time / K. Runs of
+  up to 512 launches are launched directly (the host enqueues them while
+  the load runs), longer ones as two uploaded HIP graphs (warm-up, timed):
+  a graph launch adds ~10 us on the GPU, which 20 steps would feel. (After an idle GPU the shader clock runs at
   1.5-1.9 GHz for the first ~15 ms of streaming and at 2.0-2.25 GHz after.)
 * Roofline of the dominant kernel (q2k_mmvq), timed first for each m:
   products alone, a graph of 128 launches replayed untimed for about 40 ms
@@ -270,15 +271,39 @@ def capture(torch, stream, fn, first: int, count: int):
     return g
 
 
-def timed_steps(torch, stream, fn, warm: int, count: int, load, reps: int = 1) -> float:
+# Step runs of at most this many launches (warm-up included) are launched
+# directly on the busy stream instead of as graphs: the host enqueues them
+# (~10 us per launch) while the settle load still runs, and no graph boundary
+# falls inside the timed region. A graph launch adds ~10 us on the GPU (20
+# steps measured 3-8 % slower as a graph than launched directly; 3200 steps
+# agree within 0.2 %), while longer runs launched directly would outpace the
+# host.
+DIRECT_MAX_LAUNCHES = 512
+
+
+def timed_steps(torch, stream, fn, warm: int, count: int, load, launches_per_step: int = 1):
     """Seconds per call of fn(i) over `count` calls i = warm .. warm+count-1,
-    after `warm` untimed calls i = 0 .. warm-1. Both runs are captured into
-    uploaded HIP graphs; on `stream` about SETTLE_MS of untimed load (passes
-    of `load`, a callable enqueueing one pass of another workload) settles
-    the clocks and covers the host's enqueueing, then the warm-up graph, the
-    start event, `reps` replays of the timed graph and the end event: the
-    events bracket exactly reps * count calls, with the GPU busy up to the
-    start event."""
+    after `warm` untimed calls i = 0 .. warm-1, and how they were launched.
+    On `stream` about SETTLE_MS of untimed load (passes of `load`, a callable
+    enqueueing one pass of another workload) settles the clocks and covers
+    the host's enqueueing; then the warm-up calls, the start event, the
+    timed calls and the end event, so the events bracket exactly `count`
+    calls with the GPU busy up to the start event. Short runs are launched
+    directly (see DIRECT_MAX_LAUNCHES); longer ones are captured into two
+    uploaded HIP graphs (warm-up and timed)."""
+    if (warm + count) * launches_per_step <= DIRECT_MAX_LAUNCHES:
+        settle(torch, stream, load)
+        with torch.cuda.stream(stream):
+            for i in range(warm):
+                fn(i)
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for i in range(warm, warm + count):
+                fn(i)
+            ev1.record(stream)
+        ev1.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3 / count, "direct"
     g_warm = capture(torch, stream, fn, 0, warm)
     g = capture(torch, stream, fn, warm, count)
     settle(torch, stream, load)
@@ -288,12 +313,11 @@ def timed_steps(torch, stream, fn, warm: int, count: int, load, reps: int = 1) -
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        for _ in range(reps):
-            g.replay()
+        g.replay()
         ev1.record(stream)
         ev1.synchronize()
     del g, g_warm
-    return ev0.elapsed_time(ev1) / 1e3 / (count * reps)
+    return ev0.elapsed_time(ev1) / 1e3 / count, "graph"
 
 
 def replay_timed(torch, stream, fn, count: int, reps: int) -> float:
@@ -821,14 +845,15 @@ def run(args):
         # 77 MB matrix fits the 256 MB Infinity Cache): reported beside, never
         # the roofline figure
         launch_s, warm_s = product_roofline(torch, q2, stream, copies, x8, m)
-        step_s = timed_steps(torch, stream, step, warm, steps, g_load.replay)
-        two_s = timed_steps(torch, stream, step_two_calls, warm, steps, g_load.replay)
+        step_s, launch_mode = timed_steps(torch, stream, step, warm, steps, g_load.replay,
+                                          1 if m == 1 else 2)
+        two_s, _ = timed_steps(torch, stream, step_two_calls, warm, steps, g_load.replay, 2)
         step(warm + steps - 1)               # y of the last timed step, for the parity check
         torch.cuda.synchronize()
         step_bytes = mmvq_bytes(m) + q8_bytes(m)
         y_host = y.cpu().numpy()
         results[m] = dict(step_s=step_s, launch_s=launch_s, warm_s=warm_s, steps=steps, y=y_host,
-                          two_s=two_s,
+                          two_s=two_s, launch_mode=launch_mode,
                           step_gbs=step_bytes / step_s / 1e9,
                           achieved=mmvq_bytes(m) / launch_s / 1e9)
 
@@ -886,6 +911,8 @@ def run(args):
                    "tokens_per_s": round(1 / r1["step_s"], 1),
                    "ms_per_step_two_launches": round(r1["two_s"] * 1e3, 5)},
         "roofline": roofline(1, r1),
+        "step_launches": ("direct (no graph boundary inside the timed region)"
+                          if r1["launch_mode"] == "direct" else "one captured HIP graph of the timed steps"),
         "settle": {"ms": SETTLE_MS,
                    "note": "untimed load run before each timed region (the m = 1 product over the "
                            "rotating copies ahead of the warm-up steps; the region's own launches "
