@@ -301,15 +301,13 @@ def mmvq_f32(w: np.ndarray, xq: np.ndarray, d8: np.ndarray) -> np.ndarray:
     return mmvq_f32_from_block_dots(w, I, M, d8)
 
 
-def mmvq_f32_from_block_dots(w: np.ndarray, I: np.ndarray, M: np.ndarray, d8: np.ndarray):
-    """``mmvq_f32`` from integer block sums already formed by ``block_dots``
-    (int [m, n, k/32] each)."""
+def fixed_order_leaves(w: np.ndarray, I: np.ndarray, M: np.ndarray, d8: np.ndarray):
+    """The leaf values of the fixed summation orders, fp64 [m, n, nb, 2]
+    (token, row, super-block b, half h): fI and fM chained over the four q8
+    blocks 8b+4h+j from +0, then RN(d_b * fI) - RN(dmin_b * fM)."""
     _, _, _, d, dmin = q2k_fields(w)                    # fp64 [n, nb]
     mt, n, nq = I.shape
     nb = nq // 8
-    nbp = 1
-    while nbp < nb:
-        nbp *= 2
     If = I.reshape(mt, n, nb, 2, 4).astype(np.float64)
     Mf = M.reshape(mt, n, nb, 2, 4).astype(np.float64)
     d8r = np.asarray(d8, dtype=np.float32).astype(np.float64).reshape(mt, 1, nb, 2, 4)
@@ -318,13 +316,44 @@ def mmvq_f32_from_block_dots(w: np.ndarray, I: np.ndarray, M: np.ndarray, d8: np
     for j in range(4):
         fI = fI + d8r[..., j] * If[..., j]
         fM = fM + d8r[..., j] * Mf[..., j]
-    a = d[None, :, :, None] * fI
-    c = dmin[None, :, :, None] * fM
+    return d[None, :, :, None] * fI - dmin[None, :, :, None] * fM
+
+
+def mmvq_f32_from_block_dots(w: np.ndarray, I: np.ndarray, M: np.ndarray, d8: np.ndarray):
+    """``mmvq_f32`` from integer block sums already formed by ``block_dots``
+    (int [m, n, k/32] each)."""
+    v = fixed_order_leaves(w, I, M, d8)
+    mt, n, nb, _ = v.shape
+    nbp = 1
+    while nbp < nb:
+        nbp *= 2
     leaves = np.zeros((mt, n, nbp, 2))
-    leaves[:, :, :nb, :] = a - c
+    leaves[:, :, :nb, :] = v
     while leaves.shape[2] > 1:
         leaves = leaves[:, :, 0::2, :] + leaves[:, :, 1::2, :]
     return (leaves[:, :, 0, 0] + leaves[:, :, 0, 1]).astype(np.float32)
+
+
+def mmq_f32(w: np.ndarray, xq: np.ndarray, d8: np.ndarray) -> np.ndarray:
+    """The f32 product past 8 tokens (``q2k_mmq``) in its fixed order, bit for
+    bit: the leaves of ``mmvq_f32``, summed per half h in row order from +0,
+    T_h = ((0 + v_0) + v_1) + ... + v_{nb-1} (no padding), then
+    y = f32(T_0 + T_1). The order differs from ``mmvq_f32`` only in how the
+    leaves of a half are added (a running sum instead of the pairwise tree),
+    which a kernel that walks the row block by block for many tokens at once
+    can keep in one register per output. Returns f32 [m, n]."""
+    I, M = block_dots(w, xq)
+    return mmq_f32_from_block_dots(w, I, M, d8)
+
+
+def mmq_f32_from_block_dots(w: np.ndarray, I: np.ndarray, M: np.ndarray, d8: np.ndarray):
+    """``mmq_f32`` from integer block sums already formed by ``block_dots``."""
+    v = fixed_order_leaves(w, I, M, d8)
+    mt, n, nb, _ = v.shape
+    t = np.zeros((mt, n, 2))
+    for b in range(nb):
+        t = t + v[:, :, b, :]
+    return (t[:, :, 0] + t[:, :, 1]).astype(np.float32)
 
 
 def mmvq_pair(wa, wb, xq, d8):
