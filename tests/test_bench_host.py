@@ -110,8 +110,9 @@ def test_rocprof_record_from_kernel_trace(tmp_path, monkeypatch):
     t = 1000
     for m, warm_us, timed_us in ((1, 18.0, 13.5), (8, 30.0, 20.0)):
         name = f"void q2k::{bench.KERNEL_INSTANCES[m]}(unsigned char const*, float*)"
-        for i in range(bench.ROOF_GRAPH * bench.ROOF_WARM_REPS + timed):
-            dur = warm_us if i < bench.ROOF_GRAPH * bench.ROOF_WARM_REPS else timed_us
+        warm = bench.ROOF_GRAPH * 21            # the untimed settle replays
+        for i in range(warm + timed):
+            dur = warm_us if i < warm else timed_us
             lines.append(f'"KERNEL_DISPATCH","{name}",{t},{t + int(dur * 1000)}')
             t += int(dur * 1000) + 100
     lines.append(f'"KERNEL_DISPATCH","void q2k::mmvq_m1_kernel<6, 4, 32, 1>(x)",{t},{t + 5000}')
