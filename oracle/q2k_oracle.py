@@ -336,12 +336,12 @@ def mmvq_f32_from_block_dots(w: np.ndarray, I: np.ndarray, M: np.ndarray, d8: np
 
 def mmq_f32(w: np.ndarray, xq: np.ndarray, d8: np.ndarray) -> np.ndarray:
     """The f32 product past 8 tokens (``q2k_mmq``) in its fixed order, bit for
-    bit: the leaves of ``mmvq_f32``, summed per half h in row order from +0,
-    T_h = ((0 + v_0) + v_1) + ... + v_{nb-1} (no padding), then
-    y = f32(T_0 + T_1). The order differs from ``mmvq_f32`` only in how the
-    leaves of a half are added (a running sum instead of the pairwise tree),
+    bit: the leaves of ``mmvq_f32`` added to one running fp64 sum from +0 in
+    row order, (b, h) = (0, 0), (0, 1), (1, 0), ..., (nb-1, 1) (no padding),
+    then y = f32(T). The order differs from ``mmvq_f32`` only in how the
+    leaves are added (a running sum instead of the pairwise tree per half),
     which a kernel that walks the row block by block for many tokens at once
-    can keep in one register per output. Returns f32 [m, n]."""
+    can keep in one register pair per output. Returns f32 [m, n]."""
     I, M = block_dots(w, xq)
     return mmq_f32_from_block_dots(w, I, M, d8)
 
@@ -350,10 +350,11 @@ def mmq_f32_from_block_dots(w: np.ndarray, I: np.ndarray, M: np.ndarray, d8: np.
     """``mmq_f32`` from integer block sums already formed by ``block_dots``."""
     v = fixed_order_leaves(w, I, M, d8)
     mt, n, nb, _ = v.shape
-    t = np.zeros((mt, n, 2))
+    t = np.zeros((mt, n))
     for b in range(nb):
-        t = t + v[:, :, b, :]
-    return (t[:, :, 0] + t[:, :, 1]).astype(np.float32)
+        for h in range(2):
+            t = t + v[:, :, b, h]
+    return t.astype(np.float32)
 
 
 def mmvq_pair(wa, wb, xq, d8):
