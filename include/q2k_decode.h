@@ -229,13 +229,19 @@ Q2K_API int32_t swiglu_q2k_mmvq_experts(const void* const* bases, int32_t n_base
 /* Q2_K x q8_1 product for any number of tokens (prefill, batched verify):
  * the pages' route past 8 tokens (moe_v41/init.rs, MoeV41::new: the
  * metrale_q2_k_mmq128_{nc,wc} kernels and the mmq activation buffers sized
- * beside the q8_1 rows). Same values as q2k_mmvq for each token:
- * y[t][r] = sum over the row of d8 * (d*I - dmin*M).
+ * beside the q8_1 rows). The same sum as q2k_mmvq for each token,
+ * y[t][r] = sum over the row of d8 * (d*I - dmin*M), with the same exact
+ * int32 block sums and the same fp64 value per half block, in one of two
+ * fixed orders:
+ *   m <= 16: the q2k_mmvq kernels on groups of 8 tokens (the pairwise tree
+ *            stated at q2k_mmvq; the same bits as q2k_mmvq per group);
+ *   m >= 17: the tile kernel (matrix cores, 32 tokens x 64 rows per
+ *            workgroup, any row length), whose half-block values are added
+ *            to one running fp64 sum in row order, (b, h) = (0,0), (0,1),
+ *            (1,0), ..., then rounded to f32.
  *   w_dev  : Q2_K [n, k]; xq_dev : q8_1 rows [m, k]; y_dev : f32 [m, n].
- *   1 <= m <= Q2K_MMQ_MAX_M, k % 256 == 0; errors as q2k_mmvq.
- * Rows of 4, 8, 16 or 28 super-blocks run on the matrix cores in groups of
- * 8 tokens per workgroup; other shapes run the q2k_mmvq kernels on each
- * group of 8 tokens in turn. */
+ *   1 <= m <= Q2K_MMQ_MAX_M, k % 256 == 0, m * n <= 2^31; errors as
+ *   q2k_mmvq. */
 #define Q2K_MMQ_MAX_M 4096
 Q2K_API int32_t q2k_mmq(const void* w_dev, const void* xq_dev, float* y_dev, int32_t n,
                         int32_t k, int32_t m, void* stream);
@@ -458,16 +464,17 @@ Q2K_API int32_t engram_step_noalloc(const int64_t* token_map_dev, int64_t vocab,
                                     void* stream);
 
 /* Which kernel runs the Q2_K x q8_1 products (q2k_mmvq, its pair, expert
- * and grouped forms, q2k_mmq and q2k_block_dots), process-wide. Every kernel
- * forms the same exact int32 block sums and follows the fixed summation
- * order stated at q2k_mmvq, so every choice returns the same bits: the
- * choice changes speed only.
+ * and grouped forms, q2k_mmq up to 16 tokens and q2k_block_dots),
+ * process-wide. Every kernel forms the same exact int32 block sums and
+ * follows the fixed summation order stated at q2k_mmvq, so every choice
+ * returns the same bits: the choice changes speed only. (q2k_mmq from 17
+ * tokens always runs its tile kernel and order.)
  *   Q2K_KERNEL_AUTO (the default): a cost model measured on MI355X picks
  *     the matrix-core kernel (2..8 tokens; rows of 4, 8, 16 or 28
  *     super-blocks) or the packed-dot kernels (tokens split over waves);
  *   Q2K_KERNEL_MATRIX_CORES: the matrix-core kernel wherever it applies;
- *   Q2K_KERNEL_PACKED_DOTS: never the matrix-core kernel (more than 8
- *     tokens then run as groups of 8 on the packed-dot kernels).
+ *   Q2K_KERNEL_PACKED_DOTS: never the matrix-core kernel (9..16 tokens
+ *     then run as groups of 8 on the packed-dot kernels).
  * Returns the previous choice, or Q2K_EINVAL for an unknown one. Launches
  * already enqueued are unaffected; a thread that launches while another
  * changes the choice gets either kernel (the same bits). */
@@ -478,17 +485,21 @@ Q2K_API int32_t q2k_set_product_kernel(int32_t choice);
 
 /* The kernel a single-matrix q2k_mmvq, q2k_block_dots or q2k_mmq of this
  * shape runs under the current choice: Q2K_KERNEL_MATRIX_CORES or
- * Q2K_KERNEL_PACKED_DOTS; Q2K_ESHAPE for n < 1, k not a positive multiple
+ * Q2K_KERNEL_PACKED_DOTS (always the matrix cores from 17 tokens, where the
+ * choice does not apply); Q2K_ESHAPE for n < 1, k not a positive multiple
  * of 256 or m outside 1..Q2K_MMQ_MAX_M. Host only, no device call. */
 Q2K_API int32_t q2k_product_kernel(int32_t n, int32_t k, int32_t m);
 
-/* Integer stage of q2k_mmvq, exported for exact checking: out_dev int32
- * [m, n, k/32, 2] receives, per token t, row r and q8 block c,
- * I = sum sc*q*xq and M = sum m*xq over the block's 32 values, as formed by
- * the kernel the product takes for this shape (q2k_product_kernel): the
- * matrix-core kernel's own v_mfma_i32_16x16x64_i8 outputs, or the
- * packed-dot kernels' v_dot4 sums (the device function every packed-dot
- * product kernel uses). Arguments as in q2k_mmvq. */
+/* Integer stage of the product of m tokens (q2k_mmvq, and q2k_mmq past 8
+ * tokens), exported for exact checking: out_dev int32 [m, n, k/32, 2]
+ * receives, per token t, row r and q8 block c, I = sum sc*q*xq and
+ * M = sum m*xq over the block's 32 values, as formed by the kernel the
+ * product takes for this shape (q2k_product_kernel): the matrix-core
+ * kernels' own v_mfma_i32_16x16x64_i8 (up to 16 tokens) or
+ * v_mfma_i32_16x16x32_i8 (from 17) outputs, or the packed-dot kernels'
+ * v_dot4 sums (the device function every packed-dot product kernel uses).
+ * 1 <= m <= Q2K_MMQ_MAX_M, m * n * k/32 * 2 <= 2^31; out may not overlap
+ * w or xq; other arguments and errors as in q2k_mmvq. */
 Q2K_API int32_t q2k_block_dots(const void* w_dev, const void* xq_dev, int32_t* out_dev,
                        int32_t n, int32_t k, int32_t m, void* stream);
 

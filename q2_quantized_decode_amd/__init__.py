@@ -497,7 +497,8 @@ def engram_rows_q8_1(token_map: torch.Tensor, multipliers: torch.Tensor, primes:
 
 def q2k_block_dots(w: torch.Tensor, xq: torch.Tensor, n: int, k: int, m: int,
                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """int32 [m, n, k/32, 2]: the exact (I, M) sums of q2k_mmvq's integer stage."""
+    """int32 [m, n, k/32, 2]: the exact (I, M) sums of the integer stage of the
+    product of m tokens (q2k_mmvq up to 8 tokens, q2k_mmq past 8)."""
     if out is None:
         out = torch.empty((m, n, k // 32, 2), dtype=torch.int32, device=w.device)
     _check("q2k_block_dots", lib().q2k_block_dots(_contig(w, "w"), _contig(xq, "xq"),

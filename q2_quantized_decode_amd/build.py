@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq2kdecode.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "mmvq.hip", "mmvq_mfma.hip", "gemv_bf16.hip", "q8_1.hip", "engram.hip"]
+SOURCES = ["abi.hip", "mmvq.hip", "mmvq_mfma.hip", "mmq.hip", "gemv_bf16.hip", "q8_1.hip", "engram.hip"]
 
 DEVICE_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -183,6 +183,8 @@ int32_t q2k_mmq(const void* w_dev, const void* xq_dev, float* y_dev, int32_t n, 
   if (overlap(y_dev, ybytes, w_dev, q2k_matrix_bytes(n, k)) ||
       overlap(y_dev, ybytes, xq_dev, (size_t)m * q2k::q8_row_bytes(k)))
     return fail(Q2K_EINVAL, "%s: y overlaps an input", fn);
+  if (m >= q2k::kMmqTileMinM)
+    return launched(q2k::launch_mmq(w_dev, xq_dev, y_dev, nullptr, n, k, m, (hipStream_t)stream), fn);
   q2k::MmvqLaunch a{};
   a.w[0] = w_dev;
   a.y[0] = y_dev;
@@ -779,6 +781,7 @@ int32_t q2k_product_kernel(int32_t n, int32_t k, int32_t m) {
   if (n < 1) return fail(Q2K_ESHAPE, "%s: n must be >= 1", fn);
   if (int32_t r = check_k(fn, k)) return r;
   if (m < 1 || m > Q2K_MMQ_MAX_M) return fail(Q2K_ESHAPE, "%s: m must be in 1..%d", fn, Q2K_MMQ_MAX_M);
+  if (m >= q2k::kMmqTileMinM) return Q2K_KERNEL_MATRIX_CORES;   // q2k_mmq's tile kernel, any choice
   q2k::MmvqLaunch a{};
   a.n[0] = n;
   a.njobs = 1;
@@ -793,11 +796,16 @@ int32_t q2k_block_dots(const void* w_dev, const void* xq_dev, int32_t* out_dev, 
   if (int32_t r = check_matrix(fn, "w", w_dev, n)) return r;
   if (!xq_dev || !out_dev) return fail(Q2K_EINVAL, "%s: null pointer", fn);
   if (int32_t r = check_k(fn, k)) return r;
-  if (int32_t r = check_m(fn, m)) return r;
+  if (m < 1 || m > Q2K_MMQ_MAX_M) return fail(Q2K_ESHAPE, "%s: m = %d outside 1..%d", fn, m, Q2K_MMQ_MAX_M);
   if (!aligned(xq_dev, 16) || !aligned(out_dev, 16))
     return fail(Q2K_EALIGN, "%s: xq and out must be 16-byte aligned", fn);
   if ((int64_t)m * n * (k / 32) * 2 > (int64_t)1 << 31)
     return fail(Q2K_ESHAPE, "%s: output larger than 2^31 values", fn);
+  if (overlap(out_dev, (size_t)m * n * (k / 32) * 8, w_dev, q2k_matrix_bytes(n, k)) ||
+      overlap(out_dev, (size_t)m * n * (k / 32) * 8, xq_dev, (size_t)m * q2k::q8_row_bytes(k)))
+    return fail(Q2K_EINVAL, "%s: out overlaps an input", fn);
+  if (m >= q2k::kMmqTileMinM)
+    return launched(q2k::launch_mmq(w_dev, xq_dev, nullptr, out_dev, n, k, m, (hipStream_t)stream), fn);
   q2k::MmvqLaunch a{};
   a.w[0] = w_dev;
   a.n[0] = n;

@@ -1172,13 +1172,14 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   if (a.m > kMaxM) {
     // More tokens than the packed-dot kernels take: one launch per group of
     // kMaxM tokens (plain single-matrix launches only).
-    if (a.ids != nullptr || a.groups > 0 || a.njobs != 1 || a.dots != nullptr) return hipErrorInvalidValue;
+    if (a.ids != nullptr || a.groups > 0 || a.njobs != 1) return hipErrorInvalidValue;
     const size_t rb = q8_row_bytes(a.k);
     for (int t0 = 0; t0 < a.m; t0 += kMaxM) {
       MmvqLaunch g = a;
       g.m = a.m - t0 < kMaxM ? a.m - t0 : kMaxM;
       g.xq = static_cast<const uint8_t*>(a.xq) + (size_t)t0 * rb;
-      g.y[0] = a.y[0] + (size_t)t0 * a.n[0];
+      if (a.dots != nullptr) g.dots = a.dots + (size_t)t0 * a.n[0] * (a.k / 32) * 2;
+      else g.y[0] = a.y[0] + (size_t)t0 * a.n[0];
       const hipError_t e = launch_mmvq(g, stream);
       if (e != hipSuccess) return e;
     }

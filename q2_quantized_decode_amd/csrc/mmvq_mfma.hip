@@ -502,11 +502,13 @@ __global__ __launch_bounds__(kThreads) void mmvq_mfma_kernel(const uint8_t* w0, 
 
   double tot[4] = {0.0, 0.0, 0.0, 0.0};
   const int row = r0 + L.j16;
+  // DOTS (one matrix): this token group's (I, M) start kSlots * tg tokens in
+  int32_t* const dots = DOTS ? p.dots + (int64_t)kSlots * tg * J.n * (k / 32) * 2 : nullptr;
   if (active) {
     if (kh == 0)
-      tile_half<NB, R, 0, DOTS>(lds, Wt, off, L, ring, tot, p.dots, m, J.n, row);
+      tile_half<NB, R, 0, DOTS>(lds, Wt, off, L, ring, tot, dots, m, J.n, row);
     else
-      tile_half<NB, R, 1, DOTS>(lds, Wt, off, L, ring, tot, p.dots, m, J.n, row);
+      tile_half<NB, R, 1, DOTS>(lds, Wt, off, L, ring, tot, dots, m, J.n, row);
   }
 
   // Second waves -> LDS -> first waves: left + right subtree, then the halves.
@@ -610,7 +612,7 @@ hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream) {
   const int which = nb_slot(nb);
   if (which < 0) return hipErrorInvalidValue;
   const bool dots = a.dots != nullptr;
-  if (dots && (a.m > kSlots || uniform_jobs(a) || a.njobs != 1)) return hipErrorInvalidValue;
+  if (dots && (uniform_jobs(a) || a.njobs != 1)) return hipErrorInvalidValue;
   MfmaParams p{};
   for (int j = 0; j < kMaxPlainJobs; ++j) {
     p.w[j] = static_cast<const uint8_t*>(a.w[j]);

@@ -11,6 +11,10 @@ namespace q2k {
 constexpr int kMaxPlainJobs = 4;
 // Tokens one packed-dot launch takes (the q2k_mmvq limit); q2k_mmq goes past it.
 constexpr int kMaxM = 8;
+// q2k_mmq from this many tokens runs the tile kernel (launch_mmq, its own
+// summation order); up to 16 tokens it runs the q2k_mmvq kernels on groups
+// of 8 (their order), which keep more waves busy on so few tokens.
+constexpr int kMmqTileMinM = 17;
 constexpr int kMaxExpertBases = 4;
 
 // One decode token's engram rows as the input of a product: the token's
@@ -96,6 +100,11 @@ hipError_t launch_mmvq_mfma(const MmvqLaunch& a, hipStream_t stream);
 bool mfma_supports(int k);
 // True when the matrix-core kernel is the faster choice for this launch.
 bool mfma_preferred(const MmvqLaunch& a);
+// More than 8 tokens on the matrix cores (q2k_mmq; its own summation order:
+// the leaves of each half added in row order). With dots non-null the
+// launch writes the int32 (I, M) block sums instead of y.
+hipError_t launch_mmq(const void* w, const void* xq, float* y, int32_t* dots, int n, int k, int m,
+                      hipStream_t stream);
 // Q2_K x bf16 activations (exact expansion, fp64 sums), m = 1..8.
 hipError_t launch_gemv_bf16(const void* w, const void* x, int64_t x_stride, float* y, int n, int k,
                             int m, hipStream_t stream);

@@ -396,7 +396,8 @@ def test_swiglu_dequant_gate_dots_validation(L):
     assert L.engram_gate(P, Q, 0x10000000, 0, 4, 4096, 1e-6, None) == ESHAPE
     assert L.engram_gate(P, P + 64, 0x10000000, 1, 4, 4096, 1e-6, None) == EINVAL
     assert L.engram_gate(P, Q, 0x10000000, 1, 4, 4096, -1.0, None) == ESHAPE
-    assert L.q2k_block_dots(P, Q, 0x10000000, 256, 1024, 9, None) == ESHAPE
+    assert L.q2k_block_dots(P, Q, 0x10000000, 256, 1024, 4097, None) == ESHAPE
+    assert L.q2k_block_dots(P, Q, 0x10000000, 256, 1024, 0, None) == ESHAPE
     assert L.q2k_block_dots(P, Q, 0x10000004, 256, 1024, 1, None) == EALIGN
 
 

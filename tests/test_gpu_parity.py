@@ -99,18 +99,21 @@ def assert_bits(got, ref32, what=""):
                            f"oracle {r.flat[bad[0]]!r}")
 
 
-def assert_product(got, w, oq, od, what="", dense_rows=None):
+def assert_product(got, w, oq, od, what="", dense_rows=None, order="tree"):
     """One matrix's product y [m, n] against the oracle: bit for bit the fixed
-    summation order and within tolerance of the integer route on every row
-    (both from one block_dots per CHUNK_ROWS rows), and within tolerance of the
-    dense fp64 definition on every row (small matrices) or on ``dense_rows``."""
+    summation order (``order``: "tree", the one-to-eight-token products'
+    pairwise tree, or "running", q2k_mmq's running sum past 8 tokens) and
+    within tolerance of the integer route on every row (both from one
+    block_dots per CHUNK_ROWS rows), and within tolerance of the dense fp64
+    definition on every row (small matrices) or on ``dense_rows``."""
     got = np.asarray(got)
     n = w.shape[0]
+    bits = {"tree": orc.mmvq_f32_from_block_dots, "running": orc.mmq_f32_from_block_dots}[order]
     for r0 in range(0, n, CHUNK_ROWS):
         wc = w[r0:r0 + CHUNK_ROWS]
         I, M = orc.block_dots(wc, oq)
         gc = got[:, r0:r0 + CHUNK_ROWS]
-        assert_bits(gc, orc.mmvq_f32_from_block_dots(wc, I, M, od), f"{what} rows {r0}..")
+        assert_bits(gc, bits(wc, I, M, od), f"{what} rows {r0}..")
         assert_close(gc, orc.mmvq_from_block_dots(wc, I, M, od), f"{what} rows {r0}.. (integer route)")
     if dense_rows is None and n * w.shape[1] * 256 > DENSE_ALL_MAX:
         dense_rows = _sample_rows(n, n + w.shape[1])
@@ -346,15 +349,19 @@ def test_fixed_order_hand_case_every_kernel(n, nb, m, choice, kernel):
 
 
 def test_fixed_order_hand_case_mmq_grouped_experts():
-    """The same input through q2k_mmq (20 tokens: matrix-core groups and the
-    packed-dot group loop), the grouped form and the expert batch."""
+    """The same input through q2k_mmq (20 tokens: the tile kernel's running
+    sum gives 254, the oracle's derivation, whatever the kernel choice; 16
+    and 8 tokens: groups of 8 on the q2k_mmvq kernels, the tree's 127), the
+    grouped form and the expert batch."""
     nb, k = 4, 1024
     w_np, x = syn.summation_order_case(300, nb, 20)
     w = dev(w_np.reshape(-1))
     xq = q2.q8_1_rows(bf16_dev(x))
     for choice in (MC, PD):
         with kernel_choice(choice):
-            assert np.all(q2.q2k_mmq(w, xq, 300, k, 20).cpu().numpy() == 127.0)
+            assert np.all(q2.q2k_mmq(w, xq, 300, k, 20).cpu().numpy() == 254.0)
+            assert np.all(q2.q2k_mmq(w, xq, 300, k, 16).cpu().numpy() == 127.0)
+            assert np.all(q2.q2k_mmq(w, xq, 300, k, 8).cpu().numpy() == 127.0)
     _, x2 = syn.summation_order_case(1, nb, 3)
     xg = np.concatenate([x2, x2], axis=1)                     # two groups of 1024
     yg = q2.q2k_mmvq_grouped(w[: 2 * 150 * nb * 84], q2.q8_1_rows(bf16_dev(xg)), 2, 150, k, 3)
@@ -1343,18 +1350,66 @@ def test_engram_step_small_and_bad_token():
 
 # ------------------------------------------------------- m > 8 (MMQ) ------
 
-@pytest.mark.parametrize("n,k,m", [(300, 1024, 9), (1000, 2048, 16), (130, 7168, 33), (257, 4096, 64),
-                                   (100, 1280, 20), (64, 9216, 12), (40, 2048, 200)])
+MMQ_SHAPES = [(300, 1024, 9), (1000, 2048, 16), (130, 7168, 33), (257, 4096, 64), (100, 1280, 20),
+              (64, 9216, 12), (40, 2048, 200), (65, 256, 17), (129, 2304, 31), (191, 512, 65),
+              (70, 7168, 130)]
+
+
+def mmq_order(m):
+    return "running" if m >= 17 else "tree"
+
+
+@pytest.mark.parametrize("n,k,m", MMQ_SHAPES)
 def test_mmq(n, k, m):
-    """Matrix cores in groups of 8 tokens (k/256 in {4, 8, 16, 28}); other
-    row lengths loop the packed-dot kernels over groups of 8."""
+    """Past 8 tokens: up to 16 tokens the q2k_mmvq kernels on groups of 8
+    (matrix cores for k/256 in {4, 8, 16, 28}, else the packed dots; the
+    tree order), from 17 the tile kernel (32 tokens and 64 rows per
+    workgroup, any row length; the running-sum order), ragged in rows and
+    tokens; bit for bit."""
     rng = syn.rng_for(7100, n, k, m)
     w = syn.q2k_blocks(rng, n, k // 256)
     x = syn.bf16_normal(rng, (m, k), outlier_frac=0.05)
     xq = q2.q8_1_rows(bf16_dev(x))
     oq, od = assert_q8_equal(xq, x)
     y = q2.q2k_mmq(dev(w.reshape(-1)), xq, n, k, m).cpu().numpy()
-    assert_product(y, w, oq, od, f"mmq n={n} k={k} m={m}")
+    assert_product(y, w, oq, od, f"mmq n={n} k={k} m={m}", order=mmq_order(m))
+
+
+@pytest.mark.parametrize("n,k,m", [(300, 1024, 9), (300, 1024, 16), (100, 1280, 12), (129, 2304, 31),
+                                   (191, 512, 65), (70, 7168, 40)])
+def test_mmq_block_dots(n, k, m):
+    """q2k_block_dots past 8 tokens, the integer sums of the kernel
+    q2k_mmq takes, every (token, row, block) bit-exact: groups of 8 on the
+    matrix-core kernel (k = 1024) or the packed dots (k = 1280) up to 16
+    tokens, the tile kernel's own v_mfma_i32_16x16x32_i8 outputs from 17."""
+    rng = syn.rng_for(7110, n, k, m)
+    w = syn.q2k_blocks(rng, n, k // 256)
+    x = syn.bf16_normal(rng, (m, k), outlier_frac=0.05)
+    xq = q2.q8_1_rows(bf16_dev(x))
+    oq, _ = assert_q8_equal(xq, x)
+    assert q2.q2k_product_kernel(n, k, m) == (PD if k == 1280 else MC)
+    dots = q2.q2k_block_dots(dev(w.reshape(-1)), xq, n, k, m).cpu().numpy().astype(np.int64)
+    I, M = orc.block_dots(w, oq)
+    assert np.array_equal(dots[..., 0], I), "I sums differ"
+    assert np.array_equal(dots[..., 1], M), "M sums differ"
+
+
+@pytest.mark.parametrize("m", [12, 24])
+def test_mmq_same_bits_for_every_kernel_choice(m):
+    """Every kernel choice gives the same bits past 8 tokens: up to 16 the
+    choice picks the kernel and all kernels keep the tree order; from 17 it
+    does not apply (the query names the matrix cores whatever the choice)."""
+    n, k = 200, 2048
+    rng = syn.rng_for(7120, m)
+    w = dev(syn.q2k_blocks(rng, n, k // 256).reshape(-1))
+    xq = q2.q8_1_rows(bf16_dev(syn.bf16_normal(rng, (m, k), outlier_frac=0.05)))
+    outs = []
+    for choice in (AUTO, MC, PD):
+        with kernel_choice(choice):
+            if m >= 17:
+                assert q2.q2k_product_kernel(n, k, m) == MC
+            outs.append(q2.q2k_mmq(w, xq, n, k, m).cpu().numpy().view(np.uint32))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
 def test_mmq_max_tokens():
@@ -1366,7 +1421,7 @@ def test_mmq_max_tokens():
     xq = q2.q8_1_rows(bf16_dev(x))
     oq, od = assert_q8_equal(xq, x)
     y = q2.q2k_mmq(dev(w.reshape(-1)), xq, n, k, m).cpu().numpy()
-    assert_product(y, w, oq, od, "mmq m=4096")
+    assert_product(y, w, oq, od, "mmq m=4096", order="running")
 
 
 def test_mmq_small_m_is_mmvq():
@@ -1404,8 +1459,8 @@ def test_fused_q8_1_large_verify(large):
 
 
 def test_large_mmq_sampled(large):
-    """[32768, 7168] against 64 tokens (8 token groups on the matrix cores):
-    sampled rows (every token) bit for bit the fixed order."""
+    """[32768, 7168] against 64 tokens (one 64-token tile per 64 rows):
+    sampled rows (every token) bit for bit the running-sum order."""
     case, w = large
     x = syn.bf16_normal(syn.rng_for(1004, 64), (64, case.k), outlier_frac=0.05)
     xq = q2.q8_1_rows(bf16_dev(x))
@@ -1413,7 +1468,7 @@ def test_large_mmq_sampled(large):
     y = q2.q2k_mmq(w, xq, case.n, case.k, 64).cpu().numpy()
     rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(case.n - 64, case.n),
                                      syn.rng_for(5).choice(case.n, 128, replace=False)]))
-    assert_product(y[:, rows], case.w[rows], oq, od, "large mmq m=64")
+    assert_product(y[:, rows], case.w[rows], oq, od, "large mmq m=64", order="running")
 
 
 @pytest.mark.parametrize("m", [1, 3, 8])
