@@ -590,7 +590,8 @@ def bench_mmq(torch, q2, syn, dev, copies, case):
                         "achieved_gbs": round(nbytes / us / 1e3, 1),
                         "frac_hbm": round(nbytes / us / 1e3 / PEAK_GBS, 4),
                         "tops": round(int8_ops / us / 1e6, 1)}
-    out["workload"] = ("q2k_mmq on Q2_K [32768, 7168], m tokens (matrix cores, 8 tokens per "
+    out["workload"] = ("q2k_mmq on Q2_K [32768, 7168], m tokens (m = 16: the matrix-core kernel "
+                       "on groups of 8; from 17: the tile kernel, 32 tokens x 64 rows per "
                        "workgroup), 16 rotating copies")
     return out
 
