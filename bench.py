@@ -175,7 +175,7 @@ def cpu_baseline(case, chunk: int = 2048, runs: int = 3, max_threads: int = 16):
                       "fp64 dense oracle"}
 
 
-def graph_us(torch, fn, launches: int, reps: int = 20, chunk: int = GRAPH) -> float:
+def graph_us(torch, fn, launches: int, reps: int = 20, chunk: int = GRAPH, info: dict = None) -> float:
     """Average time of fn(i), i = 0..launches-1, in microseconds: the calls
     are captured in HIP graphs of `chunk` calls each (after one eager pass),
     and HIP events on the capturing stream bracket `reps` replays of all of
@@ -197,7 +197,10 @@ def graph_us(torch, fn, launches: int, reps: int = 20, chunk: int = GRAPH) -> fl
         for g in graphs:
             g.replay()
 
-    settle(torch, stream, one_pass)
+    n_settle = settle(torch, stream, one_pass)
+    if info is not None:
+        # passes over the launches ahead of the timed ones: eager, sizing, settle
+        info["untimed_passes"] = 2 + n_settle
     with torch.cuda.stream(stream):
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
@@ -749,9 +752,11 @@ def bench_kernels(torch, q2, syn, dev):
                 for name, choice in (("mfma", q2.KERNEL_MATRIX_CORES), ("dots", q2.KERNEL_PACKED_DOTS)):
                     q2.q2k_set_product_kernel(choice)
                     launches = min(ncopy, 128)
+                    info = {}
                     rec[name + "_us"] = round(graph_us(
                         torch, lambda i: q2.q2k_mmvq(buf[i * per:(i + 1) * per], xq, n, k, m, out=y),
-                        launches, reps=max(2, 1024 // launches), chunk=16), 3)
+                        launches, reps=max(2, 1024 // launches), chunk=16, info=info), 3)
+                    rec[name + "_untimed_passes"] = info["untimed_passes"]
                     q2.q2k_set_product_kernel(q2.KERNEL_AUTO)
                 rec["auto_is_faster"] = rec[rec["auto"] + "_us"] <= min(rec["mfma_us"], rec["dots_us"]) * 1.02
                 out[f"{n}x{k}_m{m}"] = rec
@@ -1090,11 +1095,12 @@ def trace_summary(trace_csv: str) -> None:
 
 
 def kernel_sweep_from(trace_csv: str, sweep_json: str) -> None:
-    """Markdown table of a kernel trace of `--only kernels`: the product
-    dispatches, in launch order, split per (shape, m, kernel) exactly as
-    bench_kernels issues them (per configuration: one eager pass, one untimed
-    replay, then the timed replays of `launches` captured calls); the averages
-    are over the timed replays only."""
+    """Markdown table of a kernel trace of `--only kernels`, with the JSON
+    line that same traced run printed: the product dispatches, in launch
+    order, split per (shape, m, kernel) exactly as bench_kernels issues them
+    (per configuration: the untimed passes the JSON records, then the timed
+    replays of `launches` captured calls); the averages are over the timed
+    replays only."""
     import csv
     import statistics
 
@@ -1113,14 +1119,16 @@ def kernel_sweep_from(trace_csv: str, sweep_json: str) -> None:
         reps = max(2, 1024 // launches)
         for m in range(2, 9):
             cells = []
-            for _ in ("mfma", "dots"):
-                seg = rows[i:i + launches * (2 + reps)]
-                i += launches * (2 + reps)
-                names = sorted({r["Kernel_Name"].split("(")[0].replace("void ", "").replace("q2k::", "")
-                                for r in seg})
-                d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in seg[2 * launches:]]
-                cells.append((", ".join(names), statistics.mean(d)))
             r = rec[f"{n}x{k}_m{m}"]
+            for name in ("mfma", "dots"):
+                untimed = r[name + "_untimed_passes"]
+                seg = rows[i:i + launches * (untimed + reps)]
+                i += launches * (untimed + reps)
+                names = sorted({x["Kernel_Name"].split("(")[0].replace("void ", "").replace("q2k::", "")
+                                for x in seg})
+                d = [(int(x["End_Timestamp"]) - int(x["Start_Timestamp"])) / 1e3
+                     for x in seg[untimed * launches:]]
+                cells.append((", ".join(names), statistics.mean(d)))
             print(f"| [{n}, {k}] | {m} | `{cells[0][0]}` | {cells[0][1]:.3f} | `{cells[1][0]}` | "
                   f"{cells[1][1]:.3f} | {r['mfma_us']} / {r['dots_us']} | "
                   f"{'matrix cores' if r['auto'] == 'mfma' else 'packed dots'} |")

@@ -129,3 +129,36 @@ def test_rocprof_record_from_kernel_trace(tmp_path, monkeypatch):
     rec["m1"]["kernel_hash"] = "0" * 16
     out.write_text(json.dumps(rec))
     assert bench.measured_rocprof(1) is None
+
+
+def test_kernel_sweep_table_from_trace(tmp_path, capsys, monkeypatch):
+    """--kernel-sweep-from splits the trace per configuration by the untimed
+    passes the run recorded (eager, sizing and settle passes differ from one
+    configuration to the next) and averages the timed replays only."""
+    monkeypatch.setattr(bench, "KERNEL_SWEEP_SHAPES", [(8192, 2048)])
+    n, k = 8192, 2048
+    per = n * (k // 256) * 84
+    launches = min(max(2, min(1024, -(-(1 << 30) // per))), 128)
+    reps = max(2, 1024 // launches)
+    rec = {}
+    lines = ['"Kind","Kernel_Name","Start_Timestamp","End_Timestamp"']
+    t = 1000
+    for m in range(2, 9):
+        r = {"auto": "mfma", "mfma_us": 1.0, "dots_us": 2.0}
+        for name, kern, untimed in (("mfma", "mmvq_mfma_kernel<8, 2, false>", 3 + m),
+                                    ("dots", "mmvq_m1_kernel<5, 4, 16, 0>", 4 + m)):
+            r[name + "_untimed_passes"] = untimed
+            for i in range(launches * (untimed + reps)):
+                dur = 50.0 if i < launches * untimed else (10.0 if name == "mfma" else 20.0) + m
+                lines.append(f'"KERNEL_DISPATCH","void q2k::{kern}(x)",{t},{t + int(dur * 1000)}')
+                t += int(dur * 1000) + 100
+        rec[f"{n}x{k}_m{m}"] = r
+    csv_path = tmp_path / "k.csv"
+    csv_path.write_text("\n".join(lines) + "\n")
+    js = tmp_path / "k.json"
+    js.write_text(json.dumps({"product_kernels": rec}) + "\n")
+    bench.kernel_sweep_from(str(csv_path), str(js))
+    out = capsys.readouterr().out.strip().split("\n")
+    assert len(out) == 2 + 7
+    row4 = out[2 + 2]
+    assert "| 4 |" in row4 and "14.000" in row4 and "24.000" in row4 and "mmvq_mfma_kernel<8, 2, false>" in row4
