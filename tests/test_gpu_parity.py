@@ -1352,7 +1352,7 @@ def test_engram_step_small_and_bad_token():
 
 MMQ_SHAPES = [(300, 1024, 9), (1000, 2048, 16), (130, 7168, 33), (257, 4096, 64), (100, 1280, 20),
               (64, 9216, 12), (40, 2048, 200), (65, 256, 17), (129, 2304, 31), (191, 512, 65),
-              (70, 7168, 130)]
+              (70, 7168, 130), (1, 256, 17), (63, 8192, 47), (64, 10240, 32)]
 
 
 def mmq_order(m):
