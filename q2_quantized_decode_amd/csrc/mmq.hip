@@ -11,8 +11,8 @@
 //   plane p) is one v_mfma_i32_16x16x32_i8 per sum: the weights are the A
 //   operand (row i; lane (g, i) holds K = 8g..8g+7 of the block, i.e. qs
 //   bytes 32h + 8g .. +7 at bits 2p..2p+1, all in sub-block 8h + 2p + (g>>1)),
-//   the activations the B operand (K x 16 tokens). A = sc*q (a v_perm_b32
-//   lookup of q in {0, sc, 2sc, 3sc}) gives I, A = m gives M: every output is
+//   the activations the B operand (K x 16 tokens). A = sc*q (one 32-bit
+//   multiply per four quants) gives I, A = m gives M: every output is
 //   exactly one I (or M) of one (row, token, block).
 // * Epilogue: lane (g, j) holds rows 4g..4g+3 of token j. The leaf of (row,
 //   token, b, h) is formed as in every product kernel of the library (fI, fM
@@ -42,21 +42,22 @@ constexpr int kMmqThreads = kMmqWaves * kWave;
 constexpr int kMmqRows = 16 * kMmqWaves;   // weight rows per workgroup
 
 // LDS of one staged super-block for T tokens:
-//   quants [8 blocks][4 K-slices][T tokens][8 bytes]: the B operand of one
-//          (block, token group) is 512 consecutive bytes in lane order
-//   d8     [T tokens][8 blocks] fp64
+//   quants [8 blocks][4 K-slices] slices of [T tokens][8 bytes], each slice
+//          padded by 8 bytes: the B operand of one (block, token group) is
+//          four runs of 128 consecutive bytes in lane order, and the 16
+//          lanes that store one token's 16-byte chunks write 16 different
+//          slices, which the padding puts on different banks (unpadded they
+//          all hit the same two banks)
+//   d8     [pair: blocks 4h + {0, 1} or {2, 3}][half h][T tokens] of 16
+//          bytes (two fp64): the 16 lanes of a read take 16 consecutive
+//          16-byte entries
 template <int T>
 struct MmqLds {
-  static constexpr uint32_t kQuant = 8u * 4u * T * 8u;
+  static constexpr uint32_t kSlice = (uint32_t)T * 8u + 8u;
+  static constexpr uint32_t kQuant = 8u * 4u * kSlice;
   static constexpr uint32_t kBuf = kQuant + (uint32_t)T * 64u;
   static constexpr uint32_t kBytes = 2u * kBuf;
 };
-
-__device__ __forceinline__ uint32_t mul_u24_030201(uint32_t sc) {
-  uint32_t r;
-  asm("v_mul_u32_u24_e32 %0, 0x30201, %1" : "=v"(r) : "v"(sc));
-  return r;
-}
 
 // One lane's weight fields of one super-block: qs[32h + 8g .. +7] for both
 // halves, the 16 scale bytes, d and dmin.
@@ -77,6 +78,8 @@ __device__ __forceinline__ MmqW mmq_load_w(const uint8_t* blk, uint32_t qoff) {
 
 // A operands of the lane's row for the 8 q8 blocks of a super-block:
 // ai = sc*q (8 int8); mb = m in all 4 bytes (the M operand is mb twice).
+// Four 2-bit quants q in the bytes of a word times sc <= 15 is sc*q in every
+// byte (each product <= 45 stays inside its byte), one 32-bit multiply.
 struct MmqA {
   int64_t ai[2][4];
   uint32_t mb[2][4];
@@ -93,13 +96,12 @@ __device__ __forceinline__ MmqA mmq_unpack(const MmqW& w, uint32_t soff) {
       const uint32_t off = soff + 16u * (p & 1);
       const uint32_t sc = __builtin_amdgcn_ubfe(scw, off, 4);
       const uint32_t mv = __builtin_amdgcn_ubfe(scw, off + 4u, 4);
-      const uint32_t table = mul_u24_030201(sc) << 8;   // bytes 0, sc, 2sc, 3sc
       const uint32_t s0 = (w.q[h][0] >> (2 * p)) & 0x03030303u;
       const uint32_t s1 = (w.q[h][1] >> (2 * p)) & 0x03030303u;
-      const uint32_t lo = __builtin_amdgcn_perm(0u, table, s0);
-      const uint32_t hi = __builtin_amdgcn_perm(0u, table, s1);
+      const uint32_t lo = s0 * sc;
+      const uint32_t hi = s1 * sc;
       a.ai[h][p] = (int64_t)(((uint64_t)hi << 32) | lo);
-      a.mb[h][p] = __builtin_amdgcn_perm(0u, mv, 0u);
+      a.mb[h][p] = mv * 0x01010101u;
     }
   }
   return a;
@@ -140,15 +142,17 @@ __device__ __forceinline__ void mmq_stage_store(uint8_t* buf, const MmqStage<T>&
     const int tl = c / 16, e = c % 16;       // 16 bytes = K-slices 2(e&1), +1 of block e/2
     const u32x4 v = t0 + tl < m ? s.q[it] : u32x4{0, 0, 0, 0};
     const uint32_t blk = (uint32_t)(e >> 1), g0 = 2u * (uint32_t)(e & 1);
-    *reinterpret_cast<u32x2*>(buf + ((blk * 4u + g0) * T + tl) * 8u) = u32x2{v[0], v[1]};
-    *reinterpret_cast<u32x2*>(buf + ((blk * 4u + g0 + 1u) * T + tl) * 8u) = u32x2{v[2], v[3]};
+    *reinterpret_cast<u32x2*>(buf + (blk * 4u + g0) * MmqLds<T>::kSlice + tl * 8u) = u32x2{v[0], v[1]};
+    *reinterpret_cast<u32x2*>(buf + (blk * 4u + g0 + 1u) * MmqLds<T>::kSlice + tl * 8u) = u32x2{v[2], v[3]};
   }
   if (tid < 2 * T) {
     const int tl = tid >> 1;
     const bool live = t0 + tl < m;
-    double* d = reinterpret_cast<double*>(buf + MmqLds<T>::kQuant) + tl * 8 + 4 * (tid & 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = live ? (double)s.d8[i] : 0.0;
+    const uint32_t h = (uint32_t)(tid & 1);   // the thread's blocks 4h .. 4h + 3
+    uint8_t* dq = buf + MmqLds<T>::kQuant + (h * T + (uint32_t)tl) * 16u;
+    const f64x2 zero{0.0, 0.0};
+    *reinterpret_cast<f64x2*>(dq) = live ? f64x2{(double)s.d8[0], (double)s.d8[1]} : zero;
+    *reinterpret_cast<f64x2*>(dq + 2u * T * 16u) = live ? f64x2{(double)s.d8[2], (double)s.d8[3]} : zero;
   }
 }
 
@@ -249,15 +253,15 @@ __global__ __launch_bounds__(kMmqThreads, mmq_wgs_per_cu<G>()) void mmq_kernel(c
           else
             asm volatile("" : "+v"(ofs));
         }
-        const double* d8p = reinterpret_cast<const double*>(buf + L::kQuant + ofs * 8u) + 4 * h;
+        const uint8_t* d8p = buf + L::kQuant + (uint32_t)h * T * 16u + ofs * 2u;
         const f64x2 d8a = *reinterpret_cast<const f64x2*>(d8p);
-        const f64x2 d8b = *reinterpret_cast<const f64x2*>(d8p + 2);
+        const f64x2 d8b = *reinterpret_cast<const f64x2*>(d8p + 2u * T * 16u);
         const double d8[4] = {d8a[0], d8a[1], d8b[0], d8b[1]};
         double fI[4] = {0.0, 0.0, 0.0, 0.0}, fM[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const uint32_t blk = 4u * h + p;
-          const int64_t bx = *reinterpret_cast<const int64_t*>(buf + (blk * 4u + (uint32_t)g) * T * 8u + ofs);
+          const int64_t bx = *reinterpret_cast<const int64_t*>(buf + (blk * 4u + (uint32_t)g) * L::kSlice + ofs);
           const v4i ci = __builtin_amdgcn_mfma_i32_16x16x32_i8(a.ai[h][p], bx, v4i{0, 0, 0, 0}, 0, 0, 0);
           const int64_t am = (int64_t)(((uint64_t)a.mb[h][p] << 32) | a.mb[h][p]);
           const v4i cm = __builtin_amdgcn_mfma_i32_16x16x32_i8(am, bx, v4i{0, 0, 0, 0}, 0, 0, 0);
