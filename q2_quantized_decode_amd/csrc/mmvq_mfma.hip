@@ -18,9 +18,9 @@
 // * Integer sums: plane p = 0..3 of a super-block is two MFMAs with K = 64
 //   weights; K-group g holds the 16 weights 128(g>>1) + 32p + 16(g&1) + 0..15,
 //   i.e. qs bytes 16g..16g+15 at bits 2p..2p+1, all in sub-block
-//   s = 8(g>>1) + 2p + (g&1). For I the B operand is sc_s * q (<= 45, a
-//   v_perm_b32 lookup of q in {0, sc, 2sc, 3sc}); for M it is m_s in every
-//   byte. The A operand (activations) is block diagonal: A-row a = token
+//   s = 8(g>>1) + 2p + (g&1). For I the B operand is sc_s * q (<= 45, so
+//   four masked quants times sc in one 32-bit multiply); for M it is m_s in
+//   every byte. The A operand (activations) is block diagonal: A-row a = token
 //   (a&7), half (a>>3) carries that token's quants of q8 block 4(a>>3) + p in
 //   the two K-groups of that half and zeros elsewhere, so each output is
 //   exactly one I (or M) of one (token, q8 block, row).
@@ -124,15 +124,6 @@ __device__ __forceinline__ T lds_load(const uint8_t* base, uint32_t off) {
 __device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
   asm volatile("" : "+v"(v));
   return v;
-}
-
-// sc * 0x030201 as one full-rate 24-bit multiply. Written as asm because the
-// compiler otherwise merges the following shift into a 32-bit constant and
-// emits the quarter-rate v_mul_lo_u32.
-__device__ __forceinline__ uint32_t mul_u24_030201(uint32_t sc) {
-  uint32_t r;
-  asm("v_mul_u32_u24_e32 %0, 0x30201, %1" : "=v"(r) : "v"(sc));
-  return r;
 }
 
 // Weight fields of one lane for one super-block.
@@ -305,11 +296,12 @@ __device__ __forceinline__ uint64_t lshr64(uint64_t v) {
 // B operand of plane pl: sc * q of the lane's 16 weights. scw holds the
 // lane's scale bytes; sc is the 4-bit field at bit off. Two qs dwords are
 // shifted at once: bits crossing from the high dword land in bits 26..31 of
-// the low one (shift <= 6), which the 0x03 byte mask drops.
+// the low one (shift <= 6), which the 0x03 byte mask drops. Four masked
+// quants times sc is sc * q in every byte (each at most 45, no carry), one
+// v_mul_lo_u32 (a full-rate instruction on gfx950) per four weights.
 template <int PL>
 __device__ __forceinline__ v4i plane_weights(const u32x4& qs, uint32_t scw, uint32_t off) {
   const uint32_t sc = __builtin_amdgcn_ubfe(scw, off, 4);
-  const uint32_t table = mul_u24_030201(sc) << 8;  // bytes 0, sc, 2sc, 3sc
   uint32_t sel[4];
   if constexpr (PL == 0) {
 #pragma unroll
@@ -324,7 +316,7 @@ __device__ __forceinline__ v4i plane_weights(const u32x4& qs, uint32_t scw, uint
   }
   v4i wq;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) wq[w] = (int)__builtin_amdgcn_perm(0u, table, sel[w] & 0x03030303u);
+  for (int w = 0; w < 4; ++w) wq[w] = (int)((sel[w] & 0x03030303u) * sc);
   return wq;
 }
 
@@ -368,8 +360,8 @@ __device__ __forceinline__ void tile_half(const uint8_t* lds, const uint8_t* Wro
                      : pl == 1 ? plane_weights<1>(cur.qs, scw, so)
                      : pl == 2 ? plane_weights<2>(cur.qs, scw, so)
                                : plane_weights<3>(cur.qs, scw, so);
-        // the min nibble in all four bytes (byte 0 of the field, selected four times)
-        const int mb = (int)__builtin_amdgcn_perm(0u, __builtin_amdgcn_ubfe(scw, so + 4u, 4), 0u);
+        // the min nibble in all four bytes
+        const int mb = (int)(__builtin_amdgcn_ubfe(scw, so + 4u, 4) * 0x01010101u);
         const v4i wm = v4i{mb, mb, mb, mb};
         const v4i cI = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, wq, v4i{0, 0, 0, 0}, 0, 0, 0);
         const v4i cM = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, wm, v4i{0, 0, 0, 0}, 0, 0, 0);
