@@ -483,6 +483,13 @@ def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
                             out=yd)
 
     def step(i):
+        # q8_1 of x in the gate/up launch's prologue, the SwiGLU and its q8_1
+        # in its epilogue, then the down launch: two launches for the token
+        q2.q8_1_q2k_mmvq_experts_swiglu([sets["gate"], sets["up"]], per_gu, ne, ids[i % steps_n], x,
+                                        inter, dim, xq=xq, out=gu, hq=hq)
+        down(i)
+
+    def step_swiglu_in_down(i):
         # q8_1 of x inside the gate/up launch, SwiGLU + q8_1 inside the down
         # launch: two launches for the token
         q2.q8_1_q2k_mmvq_experts([sets["gate"], sets["up"]], per_gu, ne, ids[i % steps_n], x, inter,
@@ -497,7 +504,11 @@ def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
         down(i)
 
     us_step = graph_us(torch, step, steps_n)
+    us_step_sw_down = graph_us(torch, step_swiglu_in_down, steps_n)
     us_step_unfused = graph_us(torch, step_unfused, steps_n)
+    us_gu_sw = graph_us(torch, lambda i: q2.q8_1_q2k_mmvq_experts_swiglu(
+        [sets["gate"], sets["up"]], per_gu, ne, ids[i % steps_n], x, inter, dim, xq=xq, out=gu, hq=hq),
+        steps_n)
     us_down_fused = graph_us(torch, lambda i: q2.swiglu_q2k_mmvq_experts(
         [sets["down"]], per_d, ne, ids[i % steps_n], g, u, dim, hq=hq, out=yd), steps_n)
     us_gu = graph_us(torch, gate_up, steps_n)
@@ -511,11 +522,13 @@ def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
     step(i_last)
     torch.cuda.synchronize()
     gu_fused, yd_fused = gu.clone(), yd.clone()
-    step_unfused(i_last)
-    torch.cuda.synchronize()
-    if not (torch.equal(gu_fused.view(torch.int32), gu.view(torch.int32))
-            and torch.equal(yd_fused.view(torch.int32), yd.view(torch.int32))):
-        raise SystemExit("bench parity failed: the two-launch step differs from the four-launch one")
+    for other in (step_swiglu_in_down, step_unfused):
+        other(i_last)
+        torch.cuda.synchronize()
+        if not (torch.equal(gu_fused.view(torch.int32), gu.view(torch.int32))
+                and torch.equal(yd_fused.view(torch.int32), yd.view(torch.int32))):
+            raise SystemExit("bench parity failed: the two-launch step differs from "
+                             f"{other.__name__}")
     h, hq_p = q2.swiglu_q8_1_rows(g, u)
     yp = q2.q2k_mmvq_experts([sets["down"]], per_d, ne, ids[i_last], hq_p, True, dim, inter, 1)
     torch.cuda.synchronize()
@@ -545,11 +558,14 @@ def bench_experts(torch, q2, syn, dev, steps_n: int = 64):
         + (8 * 16 * inter + q2.q8_1_rows_bytes(8, inter))
     return {"workload": "routed-expert decode batch, m = 1: 256 resident experts (Q2_K gate/up "
                         "[2048, 4096], down [4096, 2048]; 2.11 GB), 8 ids per step without "
-                        "replacement, 64 id sets; step = q8_1 of x inside gate/up (one launch, 16 "
-                        "matrices) + bf16 SwiGLU and q8_1 inside down (one launch, 8 matrices, "
-                        "one input row per id)",
+                        "replacement, 64 id sets; step = gate/up with q8_1 of x in its prologue "
+                        "and the bf16 SwiGLU + q8_1 of h in its epilogue (one launch, 16 "
+                        "matrices) + down on those q8_1 rows (one launch, 8 matrices, one input "
+                        "row per id)",
             "us_per_step": round(us_step, 3), "tokens_per_s": round(1e6 / us_step, 1),
+            "us_per_step_swiglu_in_down": round(us_step_sw_down, 3),
             "us_per_step_four_launches": round(us_step_unfused, 3),
+            "gate_up_swiglu_us": round(us_gu_sw, 3),
             "swiglu_down_fused_us": round(us_down_fused, 3),
             "step_gbs": round(step_bytes / us_step / 1e3, 1),
             "step_frac": round(step_bytes / us_step / 1e3 / PEAK_GBS, 4),

@@ -202,6 +202,34 @@ Q2K_API int32_t q8_1_q2k_mmvq_experts(const void* const* bases, int32_t n_bases,
                                       size_t xq_bytes, float* y_dev, int32_t n, int32_t k,
                                       int32_t m, int32_t* err_flag_dev, void* stream);
 
+/* q8_1_q2k_mmvq_experts on the gate and up sets of one token followed by
+ * swiglu_q8_1_rows of its two result sets (moe_v41/init.rs: the gate/up
+ * product, then kquant_swiglu_q8_1_rows_bf16 ahead of the down product),
+ * in one call with the same bits in y and bytes in xq, h and hq as those
+ * calls in sequence. For rows of 2048 to 8192 values and n a multiple of 64
+ * on the run kernel it is one launch: each workgroup takes 64 rows of one
+ * id in both sets (its waves 32 consecutive rows each) and, after its
+ * product, forms their bf16 SwiGLU and the two q8_1 blocks of h in its
+ * epilogue. Otherwise the SwiGLU launch follows the product.
+ *   bases[0], bases[1] : the gate and up expert sets, as in q2k_mmvq_experts.
+ *   expert_stride_bytes, n_experts, ids_dev, n_ids, err_flag_dev : as there.
+ *   x_bf16_dev : bf16 [1, k], 16-byte aligned; xq_dev, xq_bytes : output,
+ *                its q8_1 row (q8_1_rows_bytes(1, k)), 16-byte aligned.
+ *   y_dev      : output, f32 [2, n_ids, n] (gate rows, then up rows).
+ *   h_bf16_dev : nullable output, bf16 [n_ids, n], 16-byte aligned.
+ *   hq_dev, hq_bytes : output, the q8_1 rows of h (q8_1_rows_bytes(n_ids, n)),
+ *                16-byte aligned: the input of the down product
+ *                (q2k_mmvq_experts with x_per_id = 1).
+ *   n % 256 == 0 (h is a q8_1 row of n values), k % 256 == 0.
+ * Errors: those of q8_1_q2k_mmvq_experts and swiglu_q8_1_rows; no output
+ * may overlap another buffer of the call. */
+Q2K_API int32_t q8_1_q2k_mmvq_experts_swiglu(const void* const* bases, int64_t expert_stride_bytes,
+                                             int32_t n_experts, const int32_t* ids_dev,
+                                             int32_t n_ids, const void* x_bf16_dev, void* xq_dev,
+                                             size_t xq_bytes, float* y_dev, void* h_bf16_dev,
+                                             void* hq_dev, size_t hq_bytes, int32_t n, int32_t k,
+                                             int32_t* err_flag_dev, void* stream);
+
 /* swiglu_q8_1_rows of gate and up rows and then the down product on them
  * (q2k_mmvq_experts with x_per_id = 1, one token), in one call with the
  * same bytes in hq and bits in y as the two calls (moe_v41/init.rs:

@@ -44,6 +44,8 @@ SIGNATURES = {
                                 _VP, _I32, _VP, _I32, _I32, _I32, _VP, _VP]),
     "q8_1_q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP, _I32,
                                      _VP, _I64, _VP, _SZ, _VP, _I32, _I32, _I32, _VP, _VP]),
+    "q8_1_q2k_mmvq_experts_swiglu": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I64, _I32, _VP, _I32,
+                                            _VP, _VP, _SZ, _VP, _VP, _VP, _SZ, _I32, _I32, _VP, _VP]),
     "swiglu_q2k_mmvq_experts": (_I32, [ctypes.POINTER(ctypes.c_void_p), _I32, _I64, _I32, _VP,
                                        _I32, _VP, _VP, _VP, _SZ, _VP, _I32, _I32, _VP, _VP]),
     "q2k_mmvq_grouped": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP]),
@@ -271,6 +273,42 @@ def q8_1_q2k_mmvq_experts(bases: Sequence[torch.Tensor], expert_stride_bytes: in
         x.stride(0), _contig(xq, "xq"), xq.numel(), _contig(out, "out"), n, k, m, flag or None,
         _stream()))
     return out, xq
+
+
+def q8_1_q2k_mmvq_experts_swiglu(bases: Sequence[torch.Tensor], expert_stride_bytes: int,
+                                 n_experts: int, ids: torch.Tensor, x: torch.Tensor, n: int, k: int,
+                                 xq: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                                 h: Optional[torch.Tensor] = None, hq: Optional[torch.Tensor] = None,
+                                 want_h: bool = False, err_flag: Optional[torch.Tensor] = None):
+    """Gate and up (bases = [gate set, up set]) of one bf16 token x [1, k],
+    then the bf16 SwiGLU of the two result sets and its q8_1 rows: one
+    launch where the shapes allow. Returns (y [2, n_ids, 1, n], xq, h or
+    None, hq); hq feeds q2k_mmvq_experts(..., x_per_id=True)."""
+    if ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    if len(bases) != 2:
+        raise ValueError("bases must be the gate and up expert sets")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[0] != 1 or x.stride(1) != 1:
+        raise ValueError("x must be a bf16 [1, k] tensor with unit column stride")
+    n_ids = ids.numel()
+    ptrs = [_contig(b, "base") for b in bases]
+    arr = (ctypes.c_void_p * 2)(*ptrs)
+    need = q8_1_rows_bytes(1, k)
+    if xq is None:
+        xq = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((2, n_ids, 1, n), dtype=torch.float32, device=ids.device)
+    if h is None and want_h:
+        h = torch.empty((n_ids, n), dtype=torch.bfloat16, device=ids.device)
+    hneed = q8_1_rows_bytes(n_ids, n)
+    if hq is None:
+        hq = torch.empty(max(hneed, 16), dtype=torch.uint8, device=ids.device)
+    flag = 0 if err_flag is None else _contig(err_flag, "err_flag")
+    _check("q8_1_q2k_mmvq_experts_swiglu", lib().q8_1_q2k_mmvq_experts_swiglu(
+        arr, expert_stride_bytes, n_experts, _contig(ids, "ids"), n_ids, _dev(x, "x"),
+        _contig(xq, "xq"), xq.numel(), _contig(out, "out"), _contig(h, "h") if h is not None else None,
+        _contig(hq, "hq"), hq.numel(), n, k, flag or None, _stream()))
+    return out, xq, h, hq
 
 
 def swiglu_q2k_mmvq_experts(bases: Sequence[torch.Tensor], expert_stride_bytes: int, n_experts: int,

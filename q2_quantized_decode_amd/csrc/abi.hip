@@ -358,6 +358,48 @@ int32_t q8_1_q2k_mmvq_experts(const void* const* bases, int32_t n_bases, int64_t
   return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
 }
 
+int32_t q8_1_q2k_mmvq_experts_swiglu(const void* const* bases, int64_t expert_stride_bytes,
+                                     int32_t n_experts, const int32_t* ids_dev, int32_t n_ids,
+                                     const void* x_bf16_dev, void* xq_dev, size_t xq_bytes,
+                                     float* y_dev, void* h_bf16_dev, void* hq_dev, size_t hq_bytes,
+                                     int32_t n, int32_t k, int32_t* err_flag_dev, void* stream) {
+  const char* fn = "q8_1_q2k_mmvq_experts_swiglu";
+  q2k::MmvqLaunch a;
+  if (int32_t r = experts_launch(fn, bases, 2, expert_stride_bytes, n_experts, ids_dev, n_ids,
+                                 xq_dev, 0, y_dev, n, k, 1, err_flag_dev, &a))
+    return r;
+  if (n % 256 != 0)
+    return fail(Q2K_ESHAPE, "%s: n = %d is not a multiple of 256 (h is the down product's input)", fn, n);
+  if (!x_bf16_dev || !hq_dev) return fail(Q2K_EINVAL, "%s: x or hq is null", fn);
+  if (!aligned(x_bf16_dev, 16) || !aligned(hq_dev, 16) || (h_bf16_dev && !aligned(h_bf16_dev, 16)))
+    return fail(Q2K_EALIGN, "%s: x, h and hq must be 16-byte aligned", fn);
+  const size_t need = q8_1_rows_bytes(1, k);
+  if (xq_bytes < need) return fail(Q2K_ESPACE, "%s: xq holds %zu bytes, %zu needed", fn, xq_bytes, need);
+  const size_t hneed = q8_1_rows_bytes(n_ids, n);
+  if (hq_bytes < hneed) return fail(Q2K_ESPACE, "%s: hq holds %zu bytes, %zu needed", fn, hq_bytes, hneed);
+  const size_t xbytes = (size_t)k * 2;
+  const size_t ybytes = (size_t)2 * n_ids * n * 4;
+  const size_t hbytes = (size_t)n_ids * n * 2;
+  const size_t set_bytes = (size_t)expert_stride_bytes * (size_t)(n_experts - 1) + q2k_matrix_bytes(n, k);
+  // every output against every other buffer of the call
+  const struct { const void* p; size_t n; } out[3] = {{xq_dev, need}, {hq_dev, hneed}, {h_bf16_dev, hbytes}};
+  const struct { const void* p; size_t n; } all[8] = {
+      {x_bf16_dev, xbytes}, {ids_dev, (size_t)n_ids * 4}, {bases[0], set_bytes}, {bases[1], set_bytes},
+      {y_dev, ybytes},      {xq_dev, need},               {hq_dev, hneed},       {h_bf16_dev, hbytes}};
+  for (int i = 0; i < 3; ++i) {
+    if (!out[i].p) continue;
+    for (int j = 0; j < 8; ++j)   // all[5 + i] is out[i] itself
+      if (j != 5 + i && all[j].p && overlap(out[i].p, out[i].n, all[j].p, all[j].n))
+        return fail(Q2K_EINVAL, "%s: an output overlaps another buffer of the call", fn);
+  }
+  if (overlap(y_dev, ybytes, x_bf16_dev, xbytes)) return fail(Q2K_EINVAL, "%s: y overlaps x", fn);
+  a.x_bf16 = x_bf16_dev;
+  a.x_stride = k;
+  a.sw_hq = hq_dev;
+  a.sw_h = h_bf16_dev;
+  return launched(q2k::launch_mmvq(a, (hipStream_t)stream), fn);
+}
+
 int32_t swiglu_q2k_mmvq_experts(const void* const* bases, int32_t n_bases, int64_t expert_stride_bytes,
                                 int32_t n_experts, const int32_t* ids_dev, int32_t n_ids,
                                 const float* g_dev, const float* u_dev, void* hq_dev,

@@ -60,6 +60,9 @@ struct MmvqParams {
   const uint8_t* xb16;               // narrow kernel with FQ: the token's bf16 row
   uint8_t* xq_out;                   // narrow kernel with FQ: receives its q8_1 row
   EngramRows eg;                     // run kernel with FQ = 3: the engram rows of the input
+  uint8_t* sw_hq;                    // run kernel with FQ = 4: q8_1 rows of the SwiGLU
+  uint16_t* sw_h;                    // and (nullable) its bf16 rows, [n_ids, n]
+  int32_t pair_blocks;               // FQ = 4: 64-row blocks per matrix
 };
 
 // Touches every field of the argument block at once, so that its scalar
@@ -145,6 +148,30 @@ __device__ __forceinline__ WaveJob resolve_wave(const MmvqParams& p, int wave, i
     J.it_end = min(J.it + p.chunk, iters);
     J.stride = 1;
   }
+  return J;
+}
+
+// FQ = 4 (gate and up with their SwiGLU): workgroup q takes id i = q /
+// pair_blocks and rows 64 * (q % pair_blocks) .. +63 of both matrices; its
+// wave w runs 32 consecutive rows, 32 * (w >> 1) .. +31 of the block, of
+// matrix w & 1 (0 gate, 1 up).
+__device__ __forceinline__ WaveJob resolve_pair(const MmvqParams& p, int wave, int P) {
+  const int q = wave >> 2, w = wave & 3;
+  const int i = q / p.pair_blocks;
+  const int rb = q - i * p.pair_blocks;
+  const int base = w & 1;
+  const int id = p.ids[i];
+  WaveJob J;
+  J.xrow = i;
+  J.bad = id < 0 || id >= p.n_experts;
+  J.w = p.w[base] + (int64_t)(J.bad ? 0 : id) * p.expert_stride;
+  J.n = p.n[0];
+  J.ldy = J.n;
+  J.y = p.y[0] + (int64_t)(base * p.n_ids + i) * p.n[0];
+  J.x = xview(p.xq, p.k, 0);
+  J.it = (64 * rb + 32 * (w >> 1)) / P;
+  J.it_end = min(J.it + 32 / P, (J.n + P - 1) / P);
+  J.stride = 1;
   return J;
 }
 
@@ -503,7 +530,12 @@ __device__ __forceinline__ void lds_barrier_m1() {
 // per id, every workgroup inside one id's waves): the workgroup forms the
 // bf16 SwiGLU of its id's gate and up rows (p.sg, p.su) and quantises it;
 // the workgroup holding the id's first wave writes that q8_1 row to
-// xq_out + id position * row bytes. Each workgroup issues its bf16 loads and then its weight ring,
+// xq_out + id position * row bytes. FQ = 4 (expert batch of two bases, gate
+// and up, one shared bf16 row): the FQ = 1 prologue, the rows of each
+// workgroup paired as resolve_pair states, and an epilogue in which the
+// workgroup forms the bf16 SwiGLU of its 64 gate and up outputs and their two
+// q8_1 blocks (p.sw_hq, p.sw_h), as swiglu_q8_1_rows does.
+// Each workgroup issues its bf16 loads and then its weight ring,
 // quantises the row into LDS (one thread per 32-value block; workgroup 0
 // also writes it to xq_out), and waits for LDS only, so the quantisation
 // overlaps the weights' memory latency and no separate q8_1 launch is
@@ -517,6 +549,9 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
   constexpr int P = 64 >> GSL;
   constexpr int V = 8;
   static_assert(CH % V == 0 && R >= 2, "run and ring shapes");
+  static_assert(FQ != 4 || P * CH == 32, "FQ = 4: 32 rows per wave");
+  // FQ = 4: the workgroup's gate (0) and up (1) outputs, rows of its block
+  __shared__ float ysw[2][64];
   const int lane = threadIdx.x & 63;
   const int wiw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wg = blockIdx.x;
@@ -559,16 +594,20 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
     J.bad = false;
   } else {
     prefetch_args(p);
-    // token split: the tsplit waves of one run are consecutive (same or
-    // neighbouring workgroup, same XCD), so they share the run's weights
-    // through that XCD's L2
-    const int ts = p.tsplit;
-    if (ts > 1) {
-      tok = wave % ts;
-      wave /= ts;
+    if constexpr (FQ == 4) {
+      J = resolve_pair(p, wave, P);
+    } else {
+      // token split: the tsplit waves of one run are consecutive (same or
+      // neighbouring workgroup, same XCD), so they share the run's weights
+      // through that XCD's L2
+      const int ts = p.tsplit;
+      if (ts > 1) {
+        tok = wave % ts;
+        wave /= ts;
+      }
+      J = resolve_wave<1>(p, wave, P);
+      J.y += (int64_t)tok * J.ldy;
     }
-    J = resolve_wave<1>(p, wave, P);
-    J.y += (int64_t)tok * J.ldy;
   }
   const bool live = in_grid && J.it < J.it_end;
   if (!FQ && !live) return;
@@ -609,7 +648,7 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
     // uses it.
     u32x4 raw[4];
     bool qthread = sthread;
-    if constexpr (FQ == 1) {
+    if constexpr (FQ == 1 || FQ == 4) {
       qthread = tid < (k >> 5);                 // one 32-value block per thread (k <= 8192)
       const uint8_t* xb = xq0 + 64 * (qthread ? tid : 0);
 #pragma unroll
@@ -647,7 +686,7 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
 #pragma unroll
     for (int r = 0; r < R; ++r) ws[r] = load_whalf_at(wr + (size_t)r * rs, o0);
     __builtin_amdgcn_sched_barrier(0);   // keep the ring ahead of the quantisation
-    if constexpr (FQ == 1) {
+    if constexpr (FQ == 1 || FQ == 4) {
       q8_1_block_store(xs, blockIdx.x == 0 ? xq_out : nullptr, raw, tid, k, qthread);
     } else if constexpr (FQ == 3) {
       __shared__ int64_t rid[32];
@@ -773,7 +812,16 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
         __builtin_amdgcn_sched_barrier(0);
       }
       const double tot = reduce8<GSL>(acc, lane);
-      if (writer) J.y[(J.it + (g * V + slot) * S) * P + prow] = J.bad ? quiet_nan() : (float)tot;
+      if constexpr (FQ == 4) {
+        const int row = (J.it + (g * V + slot) * S) * P + prow;
+        const float yv = J.bad ? quiet_nan() : (float)tot;
+        if (writer) {
+          J.y[row] = yv;
+          ysw[wiw & 1][row & 63] = yv;
+        }
+      } else {
+        if (writer) J.y[(J.it + (g * V + slot) * S) * P + prow] = J.bad ? quiet_nan() : (float)tot;
+      }
     }
   } else {
     // Guarded path: one direct load per step, rows past n read the step's
@@ -801,7 +849,55 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
       const double tot = reduce8<GSL>(acc, lane);
       const int step = g0 + slot * S;
       const int row = step * P + prow;
-      if (writer && step < J.it_end && row < J.n) J.y[row] = J.bad ? quiet_nan() : (float)tot;
+      if constexpr (FQ == 4) {
+        if (writer && step < J.it_end && row < J.n) {
+          const float yv = J.bad ? quiet_nan() : (float)tot;
+          J.y[row] = yv;
+          ysw[wiw & 1][row & 63] = yv;
+        }
+      } else {
+        if (writer && step < J.it_end && row < J.n) J.y[row] = J.bad ? quiet_nan() : (float)tot;
+      }
+    }
+  }
+  if constexpr (FQ == 4) {
+    // The workgroup's 64 (gate, up) pairs -> bf16 SwiGLU -> two q8_1
+    // blocks, one element per lane of wave 0: lane r forms h of row r; the
+    // block maximum, the 16-wide sums and the packing of four quants per
+    // word are cross-lane steps within the lane's 32-lane block.
+    const int q = wave >> 2;
+    const int i = q / p.pair_blocks;
+    const int e = 64 * (q - i * p.pair_blocks) + lane;   // element of h's row
+    lds_barrier_m1();
+    if (wiw == 0) {
+      const uint32_t hb = swiglu_bf16_bits(ysw[0][lane], ysw[1][lane]);
+      if (p.sw_h != nullptr) p.sw_h[(size_t)i * J.n + e] = (uint16_t)hb;
+      const float v = bf16_bits_to_f32(hb);
+      float a = fmaxf(0.0f, fabsf(v));   // a NaN counts as 0, as in q8_1_quant8
+      a = fmaxf(a, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(a))));
+      a = fmaxf(a, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(a))));
+      a = fmaxf(a, __uint_as_float(xor4_u32(__float_as_uint(a))));
+      a = fmaxf(a, __uint_as_float(dpp_u32<0x128>(__float_as_uint(a))));
+      {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+        a = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
+      const float d = q8_1_scale(a);
+      int qv;
+      q8_1_quant_lane<1>(&v, d, &qv);   // halves away from zero
+      int sum = qv;
+      sum += (int)dpp_u32<0xB1>((uint32_t)sum);
+      sum += (int)dpp_u32<0x4E>((uint32_t)sum);
+      sum += (int)xor4_u32((uint32_t)sum);
+      sum += (int)dpp_u32<0x128>((uint32_t)sum);
+      uint32_t word = ((uint32_t)qv & 0xffu) << (8 * (lane & 3));
+      word |= dpp_u32<0xB1>(word);
+      word |= dpp_u32<0x4E>(word);
+      uint8_t* row = p.sw_hq + (size_t)i * q8_row_bytes(J.n);
+      if ((lane & 3) == 0) *reinterpret_cast<uint32_t*>(row + e) = word;
+      if ((lane & 31) == 0) *reinterpret_cast<float*>(row + q8_scale_offset(J.n) + (size_t)(e / 32) * 4) = d;
+      if ((lane & 15) == 0)
+        *reinterpret_cast<int16_t*>(row + q8_sum_offset(J.n) + (size_t)(e / 16) * 2) = (int16_t)sum;
     }
   }
   if (J.bad && lane == 0 && p.err_flag != nullptr) *p.err_flag = 1;
@@ -1075,6 +1171,20 @@ void dispatch_m1_fused(const MmvqParams& p, dim3 grid, const void* x_bf16, uint8
 #undef Q2K_M1F
 }
 
+// FQ = 4: 32 rows per wave, so the run length follows the row group size.
+void dispatch_m1_swiglu(const MmvqParams& p, dim3 grid, const void* x_bf16, uint8_t* xq,
+                        hipStream_t s) {
+  const size_t lds = q8_row_bytes(p.k);
+  const uint8_t* x = static_cast<const uint8_t*>(x_bf16);
+#define Q2K_M1S(G, C)                                                                          \
+  hipLaunchKernelGGL((mmvq_m1_kernel<G, 4, C, 4>), grid, dim3(256), lds, s, p.w[0], x, p.y[0], \
+                     p.n[0], p.k, p.total_waves, p.g8, 0, xq, p)
+  if (p.gs_log2 == 4) Q2K_M1S(4, 8);
+  else if (p.gs_log2 == 5) Q2K_M1S(5, 16);
+  else Q2K_M1S(6, 32);
+#undef Q2K_M1S
+}
+
 template <int M>
 void dispatch_narrow(const MmvqParams& p, dim3 grid, bool dots, int depth, bool run_kernel,
                      hipStream_t s) {
@@ -1148,9 +1258,28 @@ bool takes_mfma(const MmvqLaunch& a) {
   return choice == 1 ? (a.m >= 2 && mfma_supports(a.k)) : choice == 2 ? false : mfma_preferred(a);
 }
 
+// The SwiGLU epilogue (FQ = 4) takes gate and up of one token, one shared
+// bf16 row, rows of 2048 to 8192 values on the run kernel's ring of 4, and
+// whole 64-row blocks.
+static bool swiglu_epilogue_fits(const MmvqLaunch& a, bool mfma) {
+  return a.ids != nullptr && a.njobs == 2 && a.m == 1 && a.x_per_id == 0 && a.x_bf16 != nullptr &&
+         a.dots == nullptr && a.sg == nullptr && !mfma && a.k >= 2048 && a.k <= 8192 &&
+         a.n[0] % 64 == 0 && tuning().ring == 4;
+}
+
 hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   // the integer stage (dots) goes to the kernel the product would take
   const bool mfma = takes_mfma(a);
+  if (a.sw_hq != nullptr && !swiglu_epilogue_fits(a, mfma)) {
+    // the product, then the SwiGLU launch on its two result sets
+    MmvqLaunch b = a;
+    b.sw_hq = b.sw_h = nullptr;
+    const hipError_t e = launch_mmvq(b, stream);
+    if (e != hipSuccess) return e;
+    const float* yg = a.y[0];
+    const float* yu = a.y[0] + (size_t)a.n_ids * a.n[0];
+    return launch_swiglu_q8_1_rows(yg, yu, a.sw_h, a.sw_hq, a.n_ids, a.n[0], stream);
+  }
   if (a.sg != nullptr && (mfma || a.m > kMaxM)) {
     const hipError_t e = launch_swiglu_q8_1_rows(a.sg, a.su, nullptr, const_cast<void*>(a.xq),
                                                  a.n_ids * a.m, a.k, stream);
@@ -1306,6 +1435,21 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
                                                  E.pos, E.table, E.n_table_rows, nullptr, nullptr,
                                                  const_cast<void*>(a.xq), E.err_flag, stream);
     if (e != hipSuccess) return e;
+  }
+  if (a.sw_hq != nullptr) {
+    // gate and up with their SwiGLU in the epilogue: workgroups of 64 rows
+    // of one id, both matrices (resolve_pair)
+    p.pair_blocks = a.n[0] / 64;
+    p.chunk = 32 / P;
+    p.interleave = 0;
+    p.total_waves = a.n_ids * p.pair_blocks * 4;
+    const int64_t wgs = ((int64_t)a.n_ids * p.pair_blocks + 7) / 8 * 8;
+    p.g8 = (int)(wgs / 8);
+    p.sw_hq = static_cast<uint8_t*>(a.sw_hq);
+    p.sw_h = static_cast<uint16_t*>(a.sw_h);
+    dispatch_m1_swiglu(p, dim3((unsigned)wgs), a.x_bf16,
+                       static_cast<uint8_t*>(const_cast<void*>(a.xq)), stream);
+    return hipGetLastError();
   }
   if (a.x_bf16 != nullptr) {
     if (fuse_x) {

@@ -79,6 +79,12 @@ struct MmvqLaunch {
   // token's engram rows; xq receives their q8_1 row. In the product kernel
   // when it can (run kernel), else by an engram_rows_q8_1 launch ahead of it.
   const EngramRows* eg = nullptr;
+  // Non-null (expert mode with two bases, gate and up, x_bf16 shared, one
+  // token): after the product, sw_hq receives the q8_1 rows [n_ids, n] of
+  // h = bf16 SwiGLU(gate rows, up rows) and sw_h (nullable) h itself; in the
+  // product kernel's epilogue when it can, else by a SwiGLU launch after it.
+  void* sw_hq = nullptr;
+  void* sw_h = nullptr;
 };
 
 // Expert and grouped launches are n_jobs equal-sized jobs.

@@ -150,6 +150,36 @@ def test_fused_q8_1_experts_validation(L):
     assert f(*args(xq=IDS)) == EINVAL               # xq over the ids
 
 
+def test_fused_gate_up_swiglu_validation(L):
+    import ctypes
+    X, XQ, Y, IDS, H, HQ = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, 0x60000000
+    arr = (ctypes.c_void_p * 2)(P, Q)
+    f = L.q8_1_q2k_mmvq_experts_swiglu
+    stride = 256 * 4 * 84
+    args = lambda **kw: [kw.get("bases", arr), kw.get("stride", stride), 4, kw.get("ids", IDS), 8,
+                         kw.get("x", X), kw.get("xq", XQ), kw.get("xqb", 1280), kw.get("y", Y),
+                         kw.get("h", H), kw.get("hq", HQ), kw.get("hqb", 8 * 320), kw.get("n", 256),
+                         kw.get("k", 1024), None, None]
+    assert f(*args(x=None)) == EINVAL
+    assert f(*args(xq=None)) == EINVAL
+    assert f(*args(hq=None)) == EINVAL
+    assert f(*args(ids=None)) == EINVAL
+    assert f(*args(k=1000)) == ESHAPE
+    assert f(*args(n=320)) == ESHAPE                # h is a Q2_K product's input
+    assert f(*args(stride=100)) == ESHAPE
+    assert f(*args(x=X + 2)) == EALIGN
+    assert f(*args(hq=HQ + 8)) == EALIGN
+    assert f(*args(h=H + 2)) == EALIGN
+    assert f(*args(xqb=1279)) == ESPACE
+    assert f(*args(hqb=8 * 320 - 1)) == ESPACE
+    assert f(*args(hq=X + 64)) == EINVAL             # hq inside x
+    assert f(*args(h=Y + 64)) == EINVAL              # h inside y
+    assert f(*args(hq=IDS)) == EINVAL                # hq over the ids
+    assert f(*args(xq=HQ + 256)) == EINVAL           # xq inside hq
+    assert f(*args(h=P + 64)) == EINVAL              # h inside the gate set
+    assert f(*args(y=X + 16)) == EINVAL              # y inside x
+
+
 def test_fused_swiglu_experts_validation(L):
     import ctypes
     G, U, HQ, Y, IDS = 0x10000000, 0x11000000, 0x20000000, 0x30000000, 0x40000000

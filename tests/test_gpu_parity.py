@@ -810,6 +810,95 @@ def test_fused_swiglu_down_equals_two_calls(expert_batch):
             assert_experts(y.cpu().numpy()[0], mats, hq_o, hd_o, True, "fused SwiGLU down")
 
 
+def _gate_up_swiglu_two_calls(gate, up, stride, n_experts, ids, x, n, k, n_ids):
+    """The calls q8_1_q2k_mmvq_experts_swiglu stands for: gate/up with x's
+    q8_1 in the product, then swiglu_q8_1_rows of the two result sets."""
+    f = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y, xq = q2.q8_1_q2k_mmvq_experts([gate, up], stride, n_experts, ids, x, n, k, err_flag=f)
+    g = y[0].reshape(n_ids, n).contiguous()
+    u = y[1].reshape(n_ids, n).contiguous()
+    h, hq = q2.swiglu_q8_1_rows(g, u)
+    return y, xq, h, hq, f
+
+
+def test_fused_gate_up_swiglu_equals_calls(expert_batch):
+    """q8_1_q2k_mmvq_experts_swiglu (one launch: gate and up rows of one id
+    per workgroup, SwiGLU and q8_1 in its epilogue) gives the bits of y and
+    the bytes of xq, h and hq of the separate calls; a bad id NaN-fills its
+    rows and sets the flag as there; the whole chain through the down
+    product matches the oracle."""
+    case, gate, up, down, per_gu, per_d = expert_batch
+    x = bf16_dev(case.x_bits)
+    n, k = case.inter, case.dim
+    for ids_np in (case.ids, np.array([case.ids[0], 300, case.ids[2], -4], dtype=np.int32)):
+        ids = dev(ids_np.astype(np.int32))
+        n_ids = len(ids_np)
+        for want_h in (True, False):
+            f1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+            y, xq, h, hq = q2.q8_1_q2k_mmvq_experts_swiglu([gate, up], per_gu, case.n_experts, ids, x,
+                                                           n, k, want_h=want_h, err_flag=f1)
+            y2, xq2, h2, hq2, f2 = _gate_up_swiglu_two_calls(gate, up, per_gu, case.n_experts, ids, x,
+                                                             n, k, n_ids)
+            need = q2.q8_1_rows_bytes(1, k)
+            assert torch.equal(xq[:need], xq2[:need])
+            assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+            hneed = q2.q8_1_rows_bytes(n_ids, n)
+            assert torch.equal(hq[:hneed], hq2[:hneed])
+            if want_h:
+                assert torch.equal(h.view(torch.int16), h2.view(torch.int16))
+            else:
+                assert h is None
+            bad = (ids_np < 0) | (ids_np >= case.n_experts)
+            assert int(f1.item()) == int(f2.item()) == int(np.any(bad))
+    # the chain against the oracle: gate/up, the SwiGLU within one bf16 step,
+    # q8_1 of the GPU's h exact, then the down product
+    ids = dev(case.ids)
+    y, xq, h, hq = q2.q8_1_q2k_mmvq_experts_swiglu([gate, up], per_gu, case.n_experts, ids, x, n, k,
+                                                   want_h=True)
+    oq, od = assert_q8_equal(xq, case.x_bits)
+    gu_h = y.cpu().numpy()
+    for bi, kind in enumerate(("gate", "up")):
+        mats = [case.expert_matrix(e, kind) for e in case.ids.tolist()]
+        assert_experts(gu_h[bi], mats, oq, od, False, f"fused {kind}")
+    h_bits = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref_h = orc.swiglu_bf16_bits(gu_h[0].reshape(-1, n), gu_h[1].reshape(-1, n))
+    assert bf16_ulp_distance(h_bits, ref_h).max() <= 1, "SwiGLU more than one bf16 ulp off"
+    hq_o, hd_o = assert_q8_equal(hq, h_bits)
+    yd = q2.q2k_mmvq_experts([down], per_d, case.n_experts, ids, hq, True, case.dim, n, 1)
+    mats = [case.expert_matrix(e, "down") for e in case.ids.tolist()]
+    assert_experts(yd.cpu().numpy()[0], mats, hq_o, hd_o, True, "down after the fused SwiGLU")
+
+
+@pytest.mark.parametrize("n,k,n_ids", [(256, 2048, 1), (512, 8192, 3), (1280, 2304, 2),
+                                       (512, 1024, 3), (256, 12288, 2), (320 * 8, 4096, 5)])
+def test_fused_gate_up_swiglu_shapes(n, k, n_ids):
+    """Row lengths of 2048 to 8192 values (16, 32 or 64 lanes per row, so
+    8, 16 or 32 row steps per wave) in one launch; k = 1024 and the wide
+    rows past 8192 values take the SwiGLU launch after the product; the
+    same bits as the separate calls either way."""
+    rng = syn.rng_for(59, n, k)
+    n_exp = 6
+    gm = [syn.q2k_blocks(rng, n, k // 256) for _ in range(n_exp)]
+    um = [syn.q2k_blocks(rng, n, k // 256) for _ in range(n_exp)]
+    stride = n * (k // 256) * 84
+    gate = dev(np.concatenate([mt.reshape(-1) for mt in gm]))
+    up = dev(np.concatenate([mt.reshape(-1) for mt in um]))
+    ids = dev(rng.choice(n_exp, n_ids, replace=False).astype(np.int32))
+    xb = syn.bf16_normal(rng, (1, k))
+    x = bf16_dev(xb)
+    y, xq, h, hq = q2.q8_1_q2k_mmvq_experts_swiglu([gate, up], stride, n_exp, ids, x, n, k, want_h=True)
+    y2, xq2, h2, hq2, _ = _gate_up_swiglu_two_calls(gate, up, stride, n_exp, ids, x, n, k, n_ids)
+    assert torch.equal(xq[:q2.q8_1_rows_bytes(1, k)], xq2[:q2.q8_1_rows_bytes(1, k)])
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    assert torch.equal(h.view(torch.int16), h2.view(torch.int16))
+    hneed = q2.q8_1_rows_bytes(n_ids, n)
+    assert torch.equal(hq[:hneed], hq2[:hneed])
+    oq, od = assert_q8_equal(xq, xb)
+    sel = ids.cpu().numpy().tolist()
+    assert_experts(y.cpu().numpy()[0], [gm[i] for i in sel], oq, od, False, "fused gate")
+    assert_experts(y.cpu().numpy()[1], [um[i] for i in sel], oq, od, False, "fused up")
+
+
 @pytest.mark.parametrize("n,k,n_ids", [(4096, 4096, 3), (200, 1024, 5), (1000, 2048, 3)])
 def test_fused_swiglu_down_fallback_shapes(n, k, n_ids):
     """Rows over 2048 values, too few row steps, or ids whose waves do not
