@@ -125,11 +125,13 @@ Q2K_API int32_t q2k_mmvq(const void* w_dev, const void* xq_dev, float* y_dev,
 /* q8_1_rows and then q2k_mmvq in one call, with the same bytes in xq and
  * the same bits in y as the two calls (attn_v41/decode.rs and moe_v41/init.rs
  * quantise an input once and then run its products; here the quantisation
- * can live inside the product). For one token and rows of 1024..8192
- * values (at least 2048 row steps) it is one launch: each workgroup
- * quantises the bf16 row into LDS while its first weight loads are in
- * flight, and workgroup 0 writes the q8_1 row to xq; otherwise a q8_1
- * launch runs ahead of the product.
+ * can live inside the product). For rows of 1024..8192 values on the
+ * packed-dot run kernel (at least 2048 row steps x tokens) it is one
+ * launch: each workgroup quantises the bf16 row of its token into LDS while
+ * its first weight loads are in flight (with 2..8 tokens each workgroup
+ * takes one token), and one workgroup per token writes its q8_1 row to xq;
+ * otherwise (fewer row steps, the matrix cores) a q8_1 launch runs ahead of
+ * the product.
  *   w_dev, y_dev, n, k, m : as in q2k_mmvq (m in 1..8).
  *   x_bf16_dev, x_row_stride : as in q8_1_rows.
  *   xq_dev, xq_bytes : output, the q8_1 rows (q8_1_rows_bytes(m, k)),
@@ -149,10 +151,10 @@ Q2K_API int32_t q2k_mmvq_pair(const void* wa_dev, float* ya_dev, int32_t na,
 
 /* q8_1_rows and then q2k_mmvq_pair in one call (attn_v41/decode.rs
  * q_kv_projections quantises the input once for wq_a and wkv), with the same
- * bytes in xq and bits in ya, yb as the two calls. For one token where the
- * pair takes the run kernel (at least 2048 row steps, rows of 1024..8192
- * values) it is one launch, the quantisation inside the product as in
- * q8_1_q2k_mmvq; otherwise a q8_1 launch runs ahead of the pair.
+ * bytes in xq and bits in ya, yb as the two calls. Where the pair takes the
+ * packed-dot run kernel (at least 2048 row steps x tokens, rows of
+ * 1024..8192 values) it is one launch, the quantisation inside the product
+ * as in q8_1_q2k_mmvq; otherwise a q8_1 launch runs ahead of the pair.
  *   wa_dev .. nb, k, m : as in q2k_mmvq_pair.
  *   x_bf16_dev, x_row_stride : bf16 [m, k] as in q8_1_rows.
  *   xq_dev, xq_bytes : output, q8_1_rows_bytes(m, k) bytes, 16-byte aligned.

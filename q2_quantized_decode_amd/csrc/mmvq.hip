@@ -63,6 +63,7 @@ struct MmvqParams {
   uint8_t* sw_hq;                    // run kernel with FQ = 4: q8_1 rows of the SwiGLU
   uint16_t* sw_h;                    // and (nullable) its bf16 rows, [n_ids, n]
   int32_t pair_blocks;               // FQ = 4: 64-row blocks per matrix
+  int64_t x_row_bytes;               // FQ = 5: row stride of the bf16 input, bytes
 };
 
 // Touches every field of the argument block at once, so that its scalar
@@ -534,7 +535,12 @@ __device__ __forceinline__ void lds_barrier_m1() {
 // and up, one shared bf16 row): the FQ = 1 prologue, the rows of each
 // workgroup paired as resolve_pair states, and an epilogue in which the
 // workgroup forms the bf16 SwiGLU of its 64 gate and up outputs and their two
-// q8_1 blocks (p.sw_hq, p.sw_h), as swiglu_q8_1_rows does.
+// q8_1 blocks (p.sw_hq, p.sw_h), as swiglu_q8_1_rows does. FQ = 5 (one
+// matrix or several with plain jobs, m = p.tsplit tokens, bf16 rows x0 with
+// stride p.x_row_bytes): workgroup q takes token q % m and that token's
+// waves 4 (q / m) .. +3 (total_waves is the count per token), quantises
+// that token's row into LDS as FQ = 1 does, and the token's first
+// workgroup writes it to row q of xq_out.
 // Each workgroup issues its bf16 loads and then its weight ring,
 // quantises the row into LDS (one thread per 32-value block; workgroup 0
 // also writes it to xq_out), and waits for LDS only, so the quantisation
@@ -556,6 +562,14 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
   const int wiw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wg = blockIdx.x;
   int wave = (((wg & 7) * g8) + (wg >> 3)) * 4 + wiw;
+  int tok5 = 0;
+  bool xq_writer5 = false;
+  if constexpr (FQ == 5) {
+    const int q = wave >> 2;
+    tok5 = q % p.tsplit;
+    xq_writer5 = q < p.tsplit;
+    wave = (q / p.tsplit) * 4 + wiw;
+  }
   // with FQ every wave of the workgroup takes part in the quantisation; a
   // wave past the end resolves the last wave's job (valid addresses only)
   if (!FQ && wave >= total_waves) return;
@@ -596,6 +610,9 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
     prefetch_args(p);
     if constexpr (FQ == 4) {
       J = resolve_pair(p, wave, P);
+    } else if constexpr (FQ == 5) {
+      J = resolve_wave<1>(p, wave, P);
+      J.y += (int64_t)tok5 * J.ldy;
     } else {
       // token split: the tsplit waves of one run are consecutive (same or
       // neighbouring workgroup, same XCD), so they share the run's weights
@@ -653,6 +670,11 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
       const uint8_t* xb = xq0 + 64 * (qthread ? tid : 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
+    } else if constexpr (FQ == 5) {
+      qthread = tid < (k >> 5);
+      const uint8_t* xb = xq0 + (size_t)tok5 * (size_t)p.x_row_bytes + 64 * (qthread ? tid : 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
     }
     // FQ = 3: the hash's independent loads (the token, the window's cached
     // ids, the layer's multipliers, the column's prime and offset) also go
@@ -688,6 +710,9 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
     __builtin_amdgcn_sched_barrier(0);   // keep the ring ahead of the quantisation
     if constexpr (FQ == 1 || FQ == 4) {
       q8_1_block_store(xs, blockIdx.x == 0 ? xq_out : nullptr, raw, tid, k, qthread);
+    } else if constexpr (FQ == 5) {
+      q8_1_block_store(xs, xq_writer5 ? xq_out + (size_t)tok5 * q8_row_bytes(k) : nullptr, raw, tid, k,
+                       qthread);
     } else if constexpr (FQ == 3) {
       __shared__ int64_t rid[32];
       const EngramRows& E = p.eg;
@@ -1374,11 +1399,17 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   // A one-token launch that quantises its own input (one bf16 row shared by
   // every matrix) does it in the run kernel's prologue when the product
   // takes the run kernel anyway (so the bits are those of the separate
-  // calls). With tokens split over waves a workgroup would quantise four
-  // rows: measured slower than the separate q8_1 launch (attention pair,
-  // m = 4: 12.5 against 8.5 us), so those take the q8_1 launch.
+  // calls).
   const bool fuse_x = a.x_bf16 != nullptr && m1_path && tu.ring == 4 && a.groups == 0 &&
                       a.m == 1 && (a.ids == nullptr || a.x_per_id == 0);
+  // Several tokens that quantise their own rows (plain jobs): one token per
+  // workgroup in the run kernel (FQ = 5), each workgroup quantising only its
+  // token's row in its prologue (with the tokens split over the waves of a
+  // workgroup it would quantise four rows: 12.5 against 8.5 us for the q8_1
+  // launch and the product on the attention pair at m = 4; one row per
+  // workgroup: 8.42 against 8.50 us, m = 8: 8.35 against 8.57 us).
+  const bool fuse_xs = a.x_bf16 != nullptr && m1_path && tu.ring == 4 && a.groups == 0 &&
+                       a.ids == nullptr && a.m > 1 && tsplit == a.m && a.k <= 8192;
   const int64_t target_waves =
       (int64_t)cu_count() * (m1_path ? tu.m1_waves_per_cu : tu.waves_per_cu);
   int64_t chunk = (total_iters * tsplit + target_waves - 1) / target_waves;
@@ -1398,6 +1429,7 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
     p.waves_per_job = (int)((iters_of[0] + chunk - 1) / chunk);
     total_waves = (int64_t)p.waves_per_job * n_jobs;
   }
+  const int64_t waves_per_token = total_waves;
   total_waves *= tsplit;
   p.total_waves = (int)total_waves;
   p.interleave = tu.interleave;
@@ -1454,6 +1486,15 @@ hipError_t launch_mmvq(const MmvqLaunch& a, hipStream_t stream) {
   if (a.x_bf16 != nullptr) {
     if (fuse_x) {
       dispatch_m1_fused<1>(p, grid, a.x_bf16, static_cast<uint8_t*>(const_cast<void*>(a.xq)), stream);
+      return hipGetLastError();
+    }
+    if (fuse_xs) {
+      const int64_t wgs = ((waves_per_token + 3) / 4 * tsplit + 7) / 8 * 8;
+      p.total_waves = (int)waves_per_token;
+      p.g8 = (int)(wgs / 8);
+      p.x_row_bytes = a.x_stride * 2;
+      dispatch_m1_fused<5>(p, dim3((unsigned)wgs), a.x_bf16,
+                           static_cast<uint8_t*>(const_cast<void*>(a.xq)), stream);
       return hipGetLastError();
     }
     // the same prologue in the one-step kernel, for the smaller one-token
