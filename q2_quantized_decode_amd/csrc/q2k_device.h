@@ -218,13 +218,17 @@ __device__ __forceinline__ int q8_1_quant(float v, float d) {
 // 2^-14 away from the nearest half-integer, both round to the same integer
 // and no tie is involved, so round-to-nearest-even of a (one instruction)
 // equals the half-away rounding of the quotient, already within +-127.
-// A lane with any value closer than that (ties included), a NaN, or a d that
-// is zero or subnormal recomputes its values with the division, in one
-// branch after the loop.
+// A value closer than that (ties included), a NaN, or a d that is zero or
+// subnormal is recomputed with the division, after the loop and only where
+// some lane of the wave needs it: exact ties are common (any element equal
+// to half its block's maximum gives v/d = 63.5), so redoing a whole lane's
+// values whenever one of them is near a tie had most waves take every
+// division.
 template <int NV>
 __device__ __forceinline__ void q8_1_quant_lane(const float* v, float d, int* q) {
   const float rd = 1.0f / d;
-  bool slow = !(d >= 0x1p-126f);
+  const bool dslow = !(d >= 0x1p-126f);
+  bool slow = dslow;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const float a = v[i] * rd;
@@ -234,7 +238,10 @@ __device__ __forceinline__ void q8_1_quant_lane(const float* v, float d, int* q)
   }
   if (slow) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) q[i] = q8_1_quant(v[i], d);
+    for (int i = 0; i < NV; ++i) {
+      const float a = v[i] * rd;
+      if (dslow || !(fabsf(a - rintf(a)) < 0.5f - 0x1p-14f)) q[i] = q8_1_quant(v[i], d);
+    }
   }
 }
 
