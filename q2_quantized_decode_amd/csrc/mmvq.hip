@@ -481,6 +481,48 @@ __device__ __forceinline__ void q8_1_block_store(uint8_t* xs, uint8_t* gout, con
   }
 }
 
+// The same for one half (16 values, raw: their 32 bytes) of a 32-value
+// block, the lane pair 2j, 2j + 1 holding block j (halves 0 and 1): the
+// block maximum is one exchange between the pair, each lane quantises and
+// sums its own 16 values. Rows of k <= 4096 (at most 256 halves) take one
+// half per thread, so the prologue's quantisation is half as long.
+__device__ __forceinline__ void q8_1_half_store(uint8_t* xs, uint8_t* gout, const u32x4 raw[2], int hb,
+                                                int k, bool active) {
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = raw[i >> 2][i & 3];
+    v[2 * i] = bf16_bits_to_f32(w & 0xffffu);
+    v[2 * i + 1] = bf16_bits_to_f32(w >> 16);
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+  a = fmaxf(a, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(a))));
+  const float d = q8_1_scale(a);
+  int qv[16];
+  q8_1_quant_lane<16>(v, d, qv);
+  uint32_t qw[4] = {0, 0, 0, 0};
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sum += qv[i];
+    qw[i >> 2] |= (uint32_t)(qv[i] & 0xff) << (8 * (i & 3));
+  }
+  if (!active) return;
+  const int blk = hb >> 1, h = hb & 1;
+  const u32x4 q4{qw[0], qw[1], qw[2], qw[3]};
+  const size_t so = q8_scale_offset(k) + (size_t)blk * 4, mo = q8_sum_offset(k) + (size_t)blk * 4 + 2 * h;
+  *reinterpret_cast<u32x4*>(xs + 32 * blk + 16 * h) = q4;
+  if (h == 0) *reinterpret_cast<float*>(xs + so) = d;
+  *reinterpret_cast<int16_t*>(xs + mo) = (int16_t)sum;
+  if (gout != nullptr) {
+    *reinterpret_cast<u32x4*>(gout + 32 * blk + 16 * h) = q4;
+    if (h == 0) *reinterpret_cast<float*>(gout + so) = d;
+    *reinterpret_cast<int16_t*>(gout + mo) = (int16_t)sum;
+  }
+}
+
 // Workgroup barrier that orders LDS only: weight loads stay in flight.
 // A wave-uniform 8-byte load through the scalar data cache, waited for
 // inside the same asm statement. It counts on the scalar memory counter, so
@@ -665,16 +707,22 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
     // uses it.
     u32x4 raw[4];
     bool qthread = sthread;
-    if constexpr (FQ == 1 || FQ == 4) {
-      qthread = tid < (k >> 5);                 // one 32-value block per thread (k <= 8192)
-      const uint8_t* xb = xq0 + 64 * (qthread ? tid : 0);
+    // k <= 4096 (GSL <= 5): one 16-value half block per thread
+    constexpr bool HALVES = (FQ == 4 || FQ == 5 || FQ == 1) && GSL <= 5;
+    if constexpr (FQ == 1 || FQ == 4 || FQ == 5) {
+      const uint8_t* xrow = xq0;
+      if constexpr (FQ == 5) xrow += (size_t)tok5 * (size_t)p.x_row_bytes;
+      if constexpr (HALVES) {
+        qthread = tid < (k >> 4);
+        const uint8_t* xb = xrow + 32 * (qthread ? tid : 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
-    } else if constexpr (FQ == 5) {
-      qthread = tid < (k >> 5);
-      const uint8_t* xb = xq0 + (size_t)tok5 * (size_t)p.x_row_bytes + 64 * (qthread ? tid : 0);
+        for (int i = 0; i < 2; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
+      } else {
+        qthread = tid < (k >> 5);               // one 32-value block per thread (k <= 8192)
+        const uint8_t* xb = xrow + 64 * (qthread ? tid : 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
+        for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
+      }
     }
     // FQ = 3: the hash's independent loads (the token, the window's cached
     // ids, the layer's multipliers, the column's prime and offset) also go
@@ -708,11 +756,15 @@ __global__ __launch_bounds__(256) void mmvq_m1_kernel(const uint8_t* w0, const u
 #pragma unroll
     for (int r = 0; r < R; ++r) ws[r] = load_whalf_at(wr + (size_t)r * rs, o0);
     __builtin_amdgcn_sched_barrier(0);   // keep the ring ahead of the quantisation
-    if constexpr (FQ == 1 || FQ == 4) {
-      q8_1_block_store(xs, blockIdx.x == 0 ? xq_out : nullptr, raw, tid, k, qthread);
-    } else if constexpr (FQ == 5) {
-      q8_1_block_store(xs, xq_writer5 ? xq_out + (size_t)tok5 * q8_row_bytes(k) : nullptr, raw, tid, k,
-                       qthread);
+    if constexpr (FQ == 1 || FQ == 4 || FQ == 5) {
+      uint8_t* gout = nullptr;
+      if constexpr (FQ == 5) {
+        if (xq_writer5) gout = xq_out + (size_t)tok5 * q8_row_bytes(k);
+      } else {
+        if (blockIdx.x == 0) gout = xq_out;
+      }
+      if constexpr (HALVES) q8_1_half_store(xs, gout, raw, tid, k, qthread);
+      else q8_1_block_store(xs, gout, raw, tid, k, qthread);
     } else if constexpr (FQ == 3) {
       __shared__ int64_t rid[32];
       const EngramRows& E = p.eg;
@@ -977,11 +1029,14 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
   if constexpr (FQ) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
     const int tid = threadIdx.x;
-    const bool qthread = tid < (k >> 5);            // one 32-value block per thread
-    const uint8_t* xb = p.xb16 + 64 * (qthread ? tid : 0);
+    // one 32-value block per thread, or one 16-value half for k <= 4096
+    // (the last two loads of a half then re-read its first, unused)
+    const bool halves = k <= 4096;
+    const bool qthread = tid < (halves ? (k >> 4) : (k >> 5));
+    const uint8_t* xb = p.xb16 + (halves ? 32 : 64) * (qthread ? tid : 0);
     u32x4 raw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + 16 * i);
+    for (int i = 0; i < 4; ++i) raw[i] = gload<u32x4>(xb + ((halves && i >= 2) ? 0 : 16 * i));
     // first weight loads, unconditional and in bounds (block 0 of row 0
     // where the lane or the step has nothing to read), zeroed afterwards
     const uint8_t* wsafe = J.w + (hb_ok ? b : 0) * kBlockBytes;
@@ -995,7 +1050,8 @@ __global__ __launch_bounds__(256) void mmvq_narrow_kernel(const MmvqParams p) {
       ws[d] = load_whalf(wsafe + (size_t)(wok[d] ? row : 0) * rowbytes, hs);
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the weight loads ahead of the quantisation
-    q8_1_block_store(xs, blockIdx.x == 0 ? p.xq_out : nullptr, raw, tid, k, qthread);
+    if (halves) q8_1_half_store(xs, blockIdx.x == 0 ? p.xq_out : nullptr, raw, tid, k, qthread);
+    else q8_1_block_store(xs, blockIdx.x == 0 ? p.xq_out : nullptr, raw, tid, k, qthread);
     lds_barrier_m1();
     if (!live) return;
 #pragma unroll
