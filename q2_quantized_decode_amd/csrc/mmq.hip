@@ -124,7 +124,7 @@ __device__ __forceinline__ MmqStage<T> mmq_stage_load(const uint8_t* xq, int64_t
 #pragma unroll
   for (int it = 0; it < MmqStage<T>::QC; ++it) {
     const int c = tid + it * kMmqThreads;   // chunk: token c / 16, bytes 16 * (c % 16)
-    const int t = min(t0 + c / 16, m - 1);  // past the last token: a valid row, zeroed at the store
+    const int t = min(t0 + c / 16, m - 1);  // past the last token: the last token's row
     s.q[it] = gload<u32x4>(xq + (int64_t)t * rowb + 256 * b + 16 * (c % 16));
   }
   // d8: thread (token tid / 2, blocks 4 (tid & 1) .. +3)
@@ -133,26 +133,27 @@ __device__ __forceinline__ MmqStage<T> mmq_stage_load(const uint8_t* xq, int64_t
   return s;
 }
 
+// Token slots past m hold the last token's activations (the loads clamp
+// the token): every output depends on its own token's column only, and the
+// outputs of those slots are never stored, so nothing needs zeroing.
 template <int T>
-__device__ __forceinline__ void mmq_stage_store(uint8_t* buf, const MmqStage<T>& s, int t0, int m) {
+__device__ __forceinline__ void mmq_stage_store(uint8_t* buf, const MmqStage<T>& s) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int it = 0; it < MmqStage<T>::QC; ++it) {
     const int c = tid + it * kMmqThreads;
     const int tl = c / 16, e = c % 16;       // 16 bytes = K-slices 2(e&1), +1 of block e/2
-    const u32x4 v = t0 + tl < m ? s.q[it] : u32x4{0, 0, 0, 0};
+    const u32x4 v = s.q[it];
     const uint32_t blk = (uint32_t)(e >> 1), g0 = 2u * (uint32_t)(e & 1);
     *reinterpret_cast<u32x2*>(buf + (blk * 4u + g0) * MmqLds<T>::kSlice + tl * 8u) = u32x2{v[0], v[1]};
     *reinterpret_cast<u32x2*>(buf + (blk * 4u + g0 + 1u) * MmqLds<T>::kSlice + tl * 8u) = u32x2{v[2], v[3]};
   }
   if (tid < 2 * T) {
     const int tl = tid >> 1;
-    const bool live = t0 + tl < m;
     const uint32_t h = (uint32_t)(tid & 1);   // the thread's blocks 4h .. 4h + 3
     uint8_t* dq = buf + MmqLds<T>::kQuant + (h * T + (uint32_t)tl) * 16u;
-    const f64x2 zero{0.0, 0.0};
-    *reinterpret_cast<f64x2*>(dq) = live ? f64x2{(double)s.d8[0], (double)s.d8[1]} : zero;
-    *reinterpret_cast<f64x2*>(dq + 2u * T * 16u) = live ? f64x2{(double)s.d8[2], (double)s.d8[3]} : zero;
+    *reinterpret_cast<f64x2*>(dq) = f64x2{(double)s.d8[0], (double)s.d8[1]};
+    *reinterpret_cast<f64x2*>(dq + 2u * T * 16u) = f64x2{(double)s.d8[2], (double)s.d8[3]};
   }
 }
 
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kMmqThreads, mmq_wgs_per_cu<G>()) void mmq_kernel(c
   MmqW wcur = mmq_load_w(wl, qoff);
   {
     const MmqStage<T> s0 = mmq_stage_load<T>(xq, rowb, k, t0, m, 0);
-    mmq_stage_store<T>(lds, s0, t0, m);
+    mmq_stage_store<T>(lds, s0);
   }
   mmq_barrier();
 
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(kMmqThreads, mmq_wgs_per_cu<G>()) void mmq_kernel(c
         }
       }
     }
-    mmq_stage_store<T>(lds + (uint32_t)((b + 1) & 1) * L::kBuf, snext, t0, m);
+    mmq_stage_store<T>(lds + (uint32_t)((b + 1) & 1) * L::kBuf, snext);
     mmq_barrier();
   }
 
