@@ -1596,13 +1596,16 @@ def test_graph_replays_match_eager():
     """Every call is enqueue-only, so a decode sequence captured in a HIP
     graph must give, on each replay, the bits of the same calls run eagerly:
     the fused single and expert products (quantisation and SwiGLU in their
-    prologues), the pair, and an engram step (hash + gather + q8_1, wkv
+    prologues, the SwiGLU in the gate/up epilogue, 4 tokens quantised one
+    per workgroup), the pair, and an engram step (hash + gather + q8_1, wkv
     product, gate on a stream restored inside the graph). Replays alternate
     with eager work and synchronisations."""
     rng = syn.rng_for(4242)
     n, k = 8192, 2048
     w = dev(syn.q2k_blocks(rng, n, k // 256).reshape(-1))
-    x = bf16_dev(syn.bf16_normal(rng, (1, k)))
+    xb = syn.bf16_normal(rng, (1, k))
+    x = bf16_dev(xb)
+    x4 = bf16_dev(np.concatenate([xb, syn.bf16_normal(rng, (3, k))]))   # token 0 is x
     n_exp, inter, dim = 6, 2048, 2048
     per_gu = inter * (dim // 256) * 84
     per_d = dim * (inter // 256) * 84
@@ -1626,7 +1629,8 @@ def test_graph_replays_match_eager():
     n_out = e.dim * (e.hc + 1)
 
     outs = {name: None for name in ("y", "xq", "gu", "xq_gu", "yd", "hq", "ya", "yb", "xq_p",
-                                    "xq_e", "kv", "h")}
+                                    "xq_e", "kv", "h", "y4", "xq4", "gu2", "xq_gu2", "h2", "hq2",
+                                    "yd2")}
     outs["y"] = torch.empty((1, n), dtype=torch.float32, device="cuda")
     outs["xq"] = torch.empty(q2.q8_1_rows_bytes(1, k), dtype=torch.uint8, device="cuda")
     outs["gu"] = torch.empty((2, 4, 1, inter), dtype=torch.float32, device="cuda")
@@ -1639,6 +1643,13 @@ def test_graph_replays_match_eager():
     outs["xq_e"] = torch.empty(q2.q8_1_rows_bytes(1, 8 * 256), dtype=torch.uint8, device="cuda")
     outs["kv"] = torch.empty((1, n_out), dtype=torch.float32, device="cuda")
     outs["h"] = torch.empty_like(h0)
+    outs["y4"] = torch.empty((4, n), dtype=torch.float32, device="cuda")
+    outs["xq4"] = torch.empty(q2.q8_1_rows_bytes(4, k), dtype=torch.uint8, device="cuda")
+    outs["gu2"] = torch.empty((2, 4, 1, inter), dtype=torch.float32, device="cuda")
+    outs["xq_gu2"] = torch.empty(q2.q8_1_rows_bytes(1, dim), dtype=torch.uint8, device="cuda")
+    outs["h2"] = torch.empty((4, inter), dtype=torch.bfloat16, device="cuda")
+    outs["hq2"] = torch.empty(q2.q8_1_rows_bytes(4, inter), dtype=torch.uint8, device="cuda")
+    outs["yd2"] = torch.empty((1, 4, 1, dim), dtype=torch.float32, device="cuda")
 
     def seq():
         q2.q8_1_q2k_mmvq(w, x, n, k, xq=outs["xq"], out=outs["y"])
@@ -1652,6 +1663,10 @@ def test_graph_replays_match_eager():
         q2.q2k_mmvq(wkv, outs["xq_e"], n_out, 2048, 1, out=outs["kv"])
         outs["h"].copy_(h0)
         q2.engram_gate(outs["h"], outs["kv"], qk, e.eps)
+        q2.q8_1_q2k_mmvq(w, x4, n, k, xq=outs["xq4"], out=outs["y4"])
+        q2.q8_1_q2k_mmvq_experts_swiglu([gate, up], per_gu, n_exp, ids, x, inter, dim, xq=outs["xq_gu2"],
+                                        out=outs["gu2"], h=outs["h2"], hq=outs["hq2"])
+        q2.q2k_mmvq_experts([down], per_d, n_exp, ids, outs["hq2"], True, dim, inter, 1, out=outs["yd2"])
 
     seq()
     torch.cuda.synchronize()
@@ -1673,3 +1688,8 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for name, t in outs.items():
             assert torch.equal(t.view(torch.uint8), eager[name].view(torch.uint8)), f"{name}, replay {rep}"
+    # the two expert routes and the token-per-workgroup quantisation agree
+    assert torch.equal(eager["gu2"], eager["gu"]) and torch.equal(eager["yd2"], eager["yd"])
+    assert torch.equal(eager["hq2"], eager["hq"])
+    assert torch.equal(eager["y4"][:1], eager["y"])
+    assert torch.equal(eager["xq4"][:q2.q8_1_rows_bytes(1, k)], eager["xq"])
