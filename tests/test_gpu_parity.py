@@ -1144,9 +1144,13 @@ def test_engram_step(engram):
 @pytest.mark.parametrize("n,k,m", [(257, 1024, 1), (100, 2048, 3), (33, 7168, 8), (10, 9216, 2),
                                    (5, 256, 1), (64, 4096, 5), (300, 768, 1), (70, 4096, 1),
                                    (70001, 256, 1), (901, 6144, 1), (333, 512, 1), (40, 256, 2),
-                                   (40, 512, 3), (40, 1024, 4)])
+                                   (40, 512, 3), (40, 1024, 4), (65832, 512, 1)])
 def test_gemv_bf16_bit_exact(n, k, m):
-    """Exact expansion, exact products, fp64 sums: the f32 bits of the oracle."""
+    """Exact expansion, exact products, fp64 sums: the f32 bits of the oracle.
+    One-token shapes with k <= 4096 run the quarter kernel, whose waves keep
+    a ring of three row steps: [70001, 256] gives its 2048 waves two or three
+    steps, [65832, 512] four or five (a second pass through the ring that
+    stops after one or two slots), the engram projection five."""
     case = syn.single_gemv_case(n=n, k=k, m=m, seed=900 + n + k + m)
     y = q2.q2k_gemv_bf16(dev(case.w.reshape(-1)), bf16_dev(case.x_bits), n, k).cpu().numpy()
     ref = orc.gemv_bf16(case.w, case.x_bits)
